@@ -1,0 +1,166 @@
+/*
+ * mk.h — C ABI of the persistent decode megakernel for MI355X (gfx950).
+ *
+ * One call of mk_decode_step runs one autoregressive decode step of a
+ * Llama-style decoder (optionally with a sparse mixture-of-experts FFN) for a
+ * fixed batch of independent sequences, as ONE kernel launch.  Inside that
+ * launch every CU runs an interpreter over a queue of tile tasks built ahead
+ * of time on the host (the on-GPU interpreter and per-SM instruction queues of
+ * the koas-w.github.io megakernel notes, "on-GPU interpreter / persistent
+ * kernel" and "static and dynamic scheduling"; the Hazy Research megakernel
+ * news page, section 4, "fusion big bang": instruction sequences built once in
+ * Python and reused for hundreds of forward passes).  Tasks order themselves
+ * through integer counters in global memory (same page, section 4,
+ * "synchronisation"; MPK news page, part 2: a task increments its trigger
+ * event, an event fires at a threshold) and prefetch the next tasks' weights
+ * into paged LDS (same Hazy page, section 4, "shared memory to remove memory
+ * bubbles").
+ *
+ * Conventions for every entry point:
+ *   - (dev) marks device memory, (host) host memory.
+ *   - No call prints, throws or exits; failures are reported by the status.
+ *   - A handle is not thread-safe; steps on one handle must be issued in order
+ *     on one stream.
+ *   - All weights are bf16 bit patterns (uint16), row-major [out][in].
+ */
+#ifndef MK_H
+#define MK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct mk_handle mk_handle;
+
+typedef enum {
+    MK_OK = 0,
+    MK_E_INVALID = 1,      /* bad argument or unsupported shape (host-side check) */
+    MK_E_UNSUPPORTED = 2,  /* valid request this build does not implement */
+    MK_E_NOMEM = 3,        /* device or host allocation failed */
+    MK_E_HIP = 4,          /* a HIP runtime call failed */
+    MK_E_NOT_RESIDENT = 5, /* the persistent grid cannot be co-resident on the device */
+    MK_E_DEVICE = 6,       /* the kernel recorded an error (see mk_check_device_error) */
+    MK_E_NO_DEVICE = 7     /* no usable GPU */
+} mk_status;
+
+/* Per-layer weights (dev, bf16, [out][in]); the caller keeps ownership.
+ * attn_norm, ffn_norm: [hidden].  wq [n_q*d][hidden], wk/wv [n_kv*d][hidden],
+ * wo [hidden][n_q*d]; dense FFN: w_gate/w_up [ffn][hidden], w_down [hidden][ffn].
+ * MoE FFN (n_experts > 0): router [n_experts][hidden], exp_gate/exp_up
+ * [n_experts][expert_ffn][hidden], exp_down [n_experts][hidden][expert_ffn]. */
+typedef struct {
+    const void *attn_norm, *wq, *wk, *wv, *wo, *ffn_norm, *w_gate, *w_up, *w_down;
+    const void *router, *exp_gate, *exp_up, *exp_down;
+} mk_layer_weights;
+
+/* Model description.  head_dim must be 64 or 128; n_q a multiple of n_kv.
+ * RMSNorm: x * g / sqrt(mean(x^2) + rms_eps).  RoPE pairs (j, j + d/2) of each
+ * head at angle position * rope_theta^(-2j/d).  tok_embed [vocab][hidden];
+ * lm_head [vocab][hidden] or NULL when tied_lm_head (then tok_embed is used);
+ * final_norm [hidden].  layers: (host) array of n_layers entries. */
+typedef struct {
+    int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn_dim, vocab;
+    int32_t n_experts, top_k, expert_ffn_dim; /* n_experts == 0: dense SwiGLU FFN */
+    float rms_eps, rope_theta;
+    int32_t tied_lm_head;
+    const void *tok_embed, *lm_head, *final_norm;
+    const mk_layer_weights *layers;
+} mk_model_desc;
+
+/* Build options; pass NULL for the defaults (all fields 0 / -1 as noted). */
+typedef struct {
+    int32_t sched;             /* 0 static per-CU queues (default), 1 dynamic global queue (atomic pop) */
+    int32_t n_workgroups;      /* persistent workgroups; 0 = one per CU of the device */
+    int32_t policy;            /* static assignment: 0 round-robin, 1 least-loaded (bytes) first */
+    int32_t attn_splits;       /* KV chunks per (sequence, KV head); 0 = automatic */
+    int32_t debug_timeout_ms;  /* bound on every in-kernel wait; 0 = 2000 ms */
+    int32_t debug_drop_signal; /* >= 0: the task with this index skips its signal (tests); -1 = off */
+    int32_t trace;             /* 1: record per-task timestamps (mk_read_trace) */
+    int32_t reserved[9];
+} mk_options;
+
+/* Validates the description, copies the weights into a handle-owned packed
+ * layout (the caller may free its copies afterwards), builds the task graph,
+ * the event targets and the queues, and uploads them to the current device.
+ * batch >= 1 sequences; max_ctx >= 1 positions per sequence in the KV cache.
+ * Errors: MK_E_INVALID (NULL pointers, unsupported shapes), MK_E_NO_DEVICE,
+ * MK_E_NOMEM, MK_E_HIP.  On success *out receives the handle. */
+mk_status mk_build_graph(const mk_model_desc *desc, int32_t batch, int32_t max_ctx, const mk_options *opt,
+                         mk_handle **out);
+
+/* Host-only planning: builds the task graph and queues exactly as
+ * mk_build_graph would for `n_workgroups` workgroups (weight pointers in desc
+ * are ignored and may be NULL) and writes the export image (format as
+ * mk_export_graph) into buf (host) of capacity cap; *need receives the size.
+ * Touches no GPU.  Returns MK_E_INVALID when cap is too small (need is set). */
+mk_status mk_plan_graph(const mk_model_desc *desc, int32_t batch, int32_t max_ctx, const mk_options *opt,
+                        int32_t n_workgroups, void *buf, size_t cap, size_t *need);
+
+/* Bytes of the KV cache the caller allocates for this handle: K then V, each
+ * bf16 [n_layers][batch][n_kv][max_ctx][head_dim]. */
+size_t mk_kv_cache_bytes(const mk_handle *h);
+
+/* One decode step, asynchronous on `stream` (a hipStream_t; NULL = the null
+ * stream); enqueues exactly one kernel.  tokens (dev) int32 [batch]: the token
+ * fed at this step; positions (dev) int32 [batch]: its position, i.e. the
+ * number of tokens already in the cache; the step writes K/V slot
+ * positions[b] of every layer of kv_cache (dev, layout of mk_kv_cache_bytes)
+ * and reads slots 0..positions[b].  logits (dev) float [batch][vocab] or NULL.
+ * tokens may be the pointer returned by mk_next_tokens (greedy chaining).
+ * Device-side checks (token outside [0, vocab), position outside
+ * [0, max_ctx), a wait exceeding debug_timeout_ms) record an error that
+ * mk_check_device_error reports; outputs are then unspecified.
+ * Errors: MK_E_INVALID (NULL handle/tokens/positions/kv_cache), MK_E_HIP,
+ * MK_E_NOT_RESIDENT. */
+mk_status mk_decode_step(mk_handle *h, const int32_t *tokens, const int32_t *positions, void *kv_cache,
+                         float *logits, void *stream);
+
+/* (dev) int32 [batch]: greedy next token of the last step (lowest index among
+ * equal maximal logits).  Owned by the handle, valid until mk_destroy. */
+const int32_t *mk_next_tokens(const mk_handle *h);
+
+/* (dev) float [batch][hidden]: the final residual (before the final norm) of
+ * the last step.  Owned by the handle. */
+const float *mk_hidden_out(const mk_handle *h);
+
+/* (dev) int32 [n_layers][batch][top_k]: experts chosen in the last step (MoE
+ * models only; NULL otherwise).  Owned by the handle. */
+const int32_t *mk_expert_ids(const mk_handle *h);
+
+/* Synchronises the device, then reports a device-side error of the last
+ * steps: MK_OK if none, MK_E_DEVICE with a message in msg (host, cap bytes)
+ * otherwise.  Clears the record and re-arms the counters so the handle can be
+ * used again. */
+mk_status mk_check_device_error(mk_handle *h, char *msg, size_t cap);
+
+/* Writes the task graph of the handle (records, event targets, queues) into
+ * buf (host, cap bytes) in the export format of mk_plan_graph; *need gets the
+ * size.  MK_E_INVALID if cap is too small. */
+mk_status mk_export_graph(const mk_handle *h, void *buf, size_t cap, size_t *need);
+
+/* Test hook: synchronises the device and copies the event counters (summed
+ * over their sub-counters) into host (n entries) and the step epoch into
+ * *epoch.  After k steps from a fresh handle, counter e equals k * target(e). */
+mk_status mk_read_counters(mk_handle *h, uint32_t *host, size_t n, uint32_t *epoch);
+
+/* Test hook: synchronises and copies per-task execution counts (n_tasks
+ * entries, host) — each task runs exactly once per step. */
+mk_status mk_read_task_counts(mk_handle *h, uint32_t *host, size_t n);
+
+/* Trace (when built with trace=1): per task of the last step, four uint64
+ * values {workgroup, t_start, t_ready, t_end} in ticks of the 100 MHz device
+ * clock; n_tasks * 4 entries into host. */
+mk_status mk_read_trace(mk_handle *h, uint64_t *host, size_t n);
+
+void mk_destroy(mk_handle *h);
+
+const char *mk_status_str(mk_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MK_H */

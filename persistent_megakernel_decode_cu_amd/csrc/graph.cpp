@@ -1,0 +1,325 @@
+// Host task-graph builder and queue scheduler (pure C++, no GPU calls).
+//
+// The graph follows the SM-level task graph of the pages (koas-w.github.io
+// megakernel notes, "SM-level task graph": nodes are tasks that run on one
+// SM/CU, edges are tile-level dependencies; MPK news page, part 1: tasks and
+// events, a trigger edge from each task to the event it completes, a
+// dependency edge from an event to the tasks it releases).  Events are integer
+// counters: a task adds one to its event when done, and a task waits until the
+// counter of its event reaches the number of producers (Hazy Research
+// megakernel news page, section 4, "synchronisation").
+//
+// Static scheduling gives every workgroup a private queue fixed before launch;
+// dynamic scheduling lets workgroups claim tasks from one global queue
+// (koas-w.github.io notes, "static and dynamic scheduling").  Both queue kinds
+// are subsequences of one topological order, so the task that is lowest in
+// that order among the unfinished ones can always run: no deadlock.
+#include "graph.h"
+
+#include <algorithm>
+#include <cstring>
+#include <numeric>
+
+namespace mk {
+
+static bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+static int64_t pow2_floor(int64_t x) {
+    int64_t p = 1;
+    while (p * 2 <= x) p *= 2;
+    return p;
+}
+static int64_t pow2_ceil(int64_t x) {
+    int64_t p = 1;
+    while (p < x) p *= 2;
+    return p;
+}
+static uint64_t pad256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
+
+// A GEMV tile whose rows have KT bf16 columns is consumed from 16 KiB LDS
+// pages: rows must not straddle pages and a 1 KiB wave load must hold whole
+// rows or whole fractions of a row.
+static bool gemv_k_ok(int64_t kt) { return is_pow2(kt) && kt >= 64 && kt <= 8192; }
+
+int plan_tiling(const Dims& dm, int B, int C, int W, const PlanOptions& o, Tiling* t, std::string* err) {
+    auto fail = [&](const char* m) {
+        if (err) *err = m;
+        return -1;
+    };
+    if (dm.L < 0 || dm.h <= 0 || dm.nq <= 0 || dm.nkv <= 0 || dm.d <= 0 || dm.V <= 0) return fail("non-positive model dimension");
+    if (B < 1 || C < 1 || W < 1) return fail("batch, max_ctx and workgroups must be >= 1");
+    if (dm.d != 64 && dm.d != 128) return fail("head_dim must be 64 or 128");
+    if (dm.nq % dm.nkv) return fail("n_q_heads must be a multiple of n_kv_heads");
+    if (dm.n_experts != 0) return fail("mixture-of-experts FFN is not implemented by this build");
+    if (B != 1) return fail("batch > 1 is not implemented by this build");
+    if (dm.f <= 0) return fail("ffn_dim must be positive");
+    if (!gemv_k_ok(dm.h) || dm.h > MAX_ACT) return fail("hidden must be a power of two in [64, 4096]");
+    const int grp = dm.nq / dm.nkv;
+    if (grp > 16) return fail("more than 16 query heads per KV head");
+    if (!gemv_k_ok((int64_t)grp * dm.d)) return fail("query heads per KV head times head_dim must be a power of two");
+    Tiling& T = *t;
+    memset(&T, 0, sizeof(T));
+    T.L = dm.L; T.h = dm.h; T.nq = dm.nq; T.nkv = dm.nkv; T.d = dm.d; T.f = dm.f; T.V = dm.V;
+    T.B = B; T.C = C; T.W = W; T.grp = grp;
+    T.qkv_pairs = 8;
+    T.n_qkv_tiles = (dm.nq + 2 * dm.nkv) * (dm.d / 2) / T.qkv_pairs;
+    int S = o.attn_splits;
+    if (S <= 0) S = (int)std::max<int64_t>(1, std::min<int64_t>(16, (C + 255) / 256));
+    if (S > C) S = C;
+    T.attn_splits = S;
+    T.n_attn_tiles = B * dm.nkv * S;
+    // O-proj: tiles (KV group g, rows) with K = grp*d columns; about W tiles per layer
+    T.o_rows = (int)std::min<int64_t>(std::min<int64_t>(dm.h, MAX_TILE_ROWS),
+                                      std::max<int64_t>(8, pow2_floor((int64_t)dm.h * dm.nkv / W)));
+    T.n_o_tiles = dm.nkv * (dm.h / T.o_rows);
+    // down-proj K blocks of kd columns of m; gate/up tiles feed whole K blocks
+    T.kd = (int)std::min<int64_t>(1024, dm.f);
+    if (dm.f % T.kd || !gemv_k_ok(T.kd)) return fail("ffn_dim must be a multiple of 1024 (or a power of two below it)");
+    const int64_t n_kb = dm.f / T.kd;
+    T.d_rows = (int)std::min<int64_t>(std::min<int64_t>(dm.h, MAX_TILE_ROWS),
+                                      std::max<int64_t>(8, pow2_floor((int64_t)dm.h * n_kb / W)));
+    T.n_down_tiles = (int)(n_kb * (dm.h / T.d_rows));
+    T.g_rows = (int)std::max<int64_t>(4, pow2_ceil((dm.f + W - 1) / W));
+    if (T.g_rows > T.kd) T.g_rows = T.kd;
+    if (T.g_rows > MAX_TILE_ROWS / 2) T.g_rows = MAX_TILE_ROWS / 2;
+    if (T.kd % T.g_rows) return fail("gate/up tile does not divide the down-proj K block");
+    T.n_gu_tiles = dm.f / T.g_rows;
+    T.lm_rows = (int)std::min<int64_t>(MAX_TILE_ROWS, (dm.V + W - 1) / W);
+    T.n_lm_tiles = (dm.V + T.lm_rows - 1) / T.lm_rows;
+    return 0;
+}
+
+void plan_layout(const Tiling& T, bool tied, Layout* out) {
+    Layout& Ly = *out;
+    memset(&Ly, 0, sizeof(Ly));
+    const uint64_t h = T.h;
+    uint64_t at = 0;
+    Ly.gains = at;
+    at = pad256(at + (uint64_t)(2 * T.L + 1) * h * 2);
+    Ly.embed = at;
+    at = pad256(at + (uint64_t)T.V * h * 2);
+    if (tied) {
+        Ly.lm = Ly.embed;
+    } else {
+        Ly.lm = at;
+        at = pad256(at + (uint64_t)T.V * h * 2);
+    }
+    Ly.layer0 = at;
+    uint64_t l = 0;
+    Ly.qkv = l;
+    l = pad256(l + (uint64_t)(T.nq + 2 * T.nkv) * T.d * h * 2);
+    Ly.o = l;
+    l = pad256(l + h * (uint64_t)T.nq * T.d * 2);
+    Ly.gu = l;
+    l = pad256(l + 2ull * T.f * h * 2);
+    Ly.down = l;
+    l = pad256(l + h * (uint64_t)T.f * 2);
+    Ly.layer_bytes = l;
+    Ly.total = Ly.layer0 + (uint64_t)T.L * l;
+}
+
+uint32_t Graph::new_event() {
+    target.push_back(0);
+    nsub.push_back(1);
+    return (uint32_t)target.size() - 1;
+}
+
+static uint64_t task_cost(const Task& k) { return (uint64_t)k.wbytes + 8192; }
+
+int build_graph(const Tiling& T, const Layout& Ly, int sched, int policy, Graph* G) {
+    Graph& g = *G;
+    g.T = T;
+    g.lay = Ly;
+    g.sched = (uint32_t)sched;
+    g.tasks.clear();
+    g.target.clear();
+    g.nsub.clear();
+    const uint64_t h = T.h;
+    const int L = T.L, grp = T.grp, half = T.d / 2;
+    const int pair_blocks = half / T.qkv_pairs;
+    const int n_kb = T.f / T.kd;
+
+    auto add = [&](Task k) {
+        k.id = (uint32_t)g.tasks.size();
+        g.tasks.push_back(k);
+        if (k.sig_ev != NONE) g.target[k.sig_ev] += 1;
+    };
+    auto blank = [](uint8_t op, int layer) {
+        Task k;
+        memset(&k, 0, sizeof(k));
+        k.op = op;
+        k.layer = (uint16_t)layer;
+        k.wait_ev = NONE;
+        k.sig_ev = NONE;
+        k.wait_nsub = 1;
+        k.sig_nsub = 1;
+        return k;
+    };
+
+    uint32_t ev_x = NONE;  // residual stream ready for the current layer (NONE for layer 0: embedding)
+    for (int l = 0; l < L; ++l) {
+        const uint64_t lbase = Ly.layer0 + (uint64_t)l * Ly.layer_bytes;
+        std::vector<uint32_t> ev_qkv(T.nkv), ev_attn(T.nkv), ev_m(n_kb);
+        for (int gi = 0; gi < T.nkv; ++gi) ev_qkv[gi] = g.new_event();
+        for (int gi = 0; gi < T.nkv; ++gi) ev_attn[gi] = g.new_event();
+        const uint32_t ev_xb = g.new_event();
+        for (int kb = 0; kb < n_kb; ++kb) ev_m[kb] = g.new_event();
+        const uint32_t ev_next = g.new_event();
+
+        // fused RMSNorm + QKV + RoPE tiles, grouped by KV head: q heads of the group, then its k and v head
+        uint64_t tile = 0;
+        for (int gi = 0; gi < T.nkv; ++gi) {
+            for (int s = 0; s < grp + 2; ++s) {
+                int slot = s < grp ? gi * grp + s : (s == grp ? T.nq + gi : T.nq + T.nkv + gi);
+                for (int pb = 0; pb < pair_blocks; ++pb, ++tile) {
+                    Task k = blank(OP_QKV, l);
+                    k.part = (uint16_t)slot;
+                    k.row0 = (uint32_t)(pb * T.qkv_pairs);
+                    k.nrows = (uint32_t)T.qkv_pairs;
+                    k.wait_ev = ev_x;
+                    k.sig_ev = ev_qkv[gi];
+                    k.wbytes = (uint32_t)(2 * T.qkv_pairs * h * 2);
+                    k.wofs = lbase + Ly.qkv + tile * k.wbytes;
+                    add(k);
+                }
+            }
+        }
+        // attention chunks per (sequence, KV group, chunk)
+        for (int b = 0; b < T.B; ++b)
+            for (int gi = 0; gi < T.nkv; ++gi)
+                for (int c = 0; c < T.attn_splits; ++c) {
+                    Task k = blank(OP_ATTN, l);
+                    k.part = (uint16_t)gi;
+                    k.row0 = (uint32_t)c;
+                    k.nrows = (uint32_t)grp;
+                    k.seq = (uint32_t)b;
+                    k.wait_ev = ev_qkv[gi];
+                    k.sig_ev = ev_attn[gi];
+                    add(k);
+                }
+        // O-proj K slices: tile (group, row block)
+        const int o_kt = grp * T.d;
+        for (int gi = 0; gi < T.nkv; ++gi)
+            for (int rb = 0; rb < T.h / T.o_rows; ++rb) {
+                Task k = blank(OP_OPROJ, l);
+                k.part = (uint16_t)gi;
+                k.row0 = (uint32_t)(rb * T.o_rows);
+                k.nrows = (uint32_t)T.o_rows;
+                k.flags = gi == 0 ? TF_RESID : 0;
+                k.wait_ev = ev_attn[gi];
+                k.sig_ev = ev_xb;
+                k.wbytes = (uint32_t)((uint64_t)T.o_rows * o_kt * 2);
+                k.wofs = lbase + Ly.o + ((uint64_t)gi * (T.h / T.o_rows) + rb) * k.wbytes;
+                add(k);
+            }
+        // RMSNorm + gate/up + SiLU tiles
+        for (int t = 0; t < T.n_gu_tiles; ++t) {
+            Task k = blank(OP_GATEUP, l);
+            k.row0 = (uint32_t)(t * T.g_rows);
+            k.nrows = (uint32_t)T.g_rows;
+            k.wait_ev = ev_xb;
+            k.sig_ev = ev_m[(t * T.g_rows) / T.kd];
+            k.wbytes = (uint32_t)(2ull * T.g_rows * h * 2);
+            k.wofs = lbase + Ly.gu + (uint64_t)t * k.wbytes;
+            add(k);
+        }
+        // down-proj K slices: tile (K block, row block)
+        for (int kb = 0; kb < n_kb; ++kb)
+            for (int rb = 0; rb < T.h / T.d_rows; ++rb) {
+                Task k = blank(OP_DOWN, l);
+                k.part = (uint16_t)kb;
+                k.row0 = (uint32_t)(rb * T.d_rows);
+                k.nrows = (uint32_t)T.d_rows;
+                k.flags = kb == 0 ? TF_RESID : 0;
+                k.wait_ev = ev_m[kb];
+                k.sig_ev = ev_next;
+                k.wbytes = (uint32_t)((uint64_t)T.d_rows * T.kd * 2);
+                k.wofs = lbase + Ly.down + ((uint64_t)kb * (T.h / T.d_rows) + rb) * k.wbytes;
+                add(k);
+            }
+        ev_x = ev_next;
+    }
+    // final RMSNorm + LM head + argmax
+    for (int t = 0; t < T.n_lm_tiles; ++t) {
+        Task k = blank(OP_LMHEAD, L);
+        k.row0 = (uint32_t)(t * T.lm_rows);
+        k.nrows = (uint32_t)std::min<int64_t>(T.lm_rows, (int64_t)T.V - (int64_t)t * T.lm_rows);
+        k.wait_ev = ev_x;
+        k.wbytes = (uint32_t)((uint64_t)k.nrows * h * 2);
+        k.wofs = Ly.lm + (uint64_t)k.row0 * h * 2;
+        add(k);
+    }
+    // sub-counters: events with many producers spread their increments over 8 counters
+    for (size_t e = 0; e < g.target.size(); ++e) g.nsub[e] = g.target[e] > 32 ? 8 : 1;
+    for (auto& k : g.tasks) {
+        if (k.wait_ev != NONE) {
+            k.wait_target = g.target[k.wait_ev];
+            k.wait_nsub = (uint8_t)g.nsub[k.wait_ev];
+        }
+        if (k.sig_ev != NONE) k.sig_nsub = (uint8_t)g.nsub[k.sig_ev];
+    }
+    // queues
+    const int W = T.W;
+    const size_t n = g.tasks.size();
+    g.order.resize(n);
+    std::iota(g.order.begin(), g.order.end(), 0u);
+    std::vector<std::vector<uint32_t>> per(W);
+    if (policy == 0) {
+        for (size_t i = 0; i < n; ++i) per[i % W].push_back((uint32_t)i);
+    } else {
+        std::vector<uint64_t> load(W, 0);
+        for (size_t i = 0; i < n; ++i) {
+            int best = 0;
+            for (int w = 1; w < W; ++w)
+                if (load[w] < load[best]) best = w;
+            load[best] += task_cost(g.tasks[i]);
+            per[best].push_back((uint32_t)i);
+        }
+    }
+    g.queue_off.assign(W + 1, 0);
+    g.queue.clear();
+    for (int w = 0; w < W; ++w) {
+        g.queue_off[w] = (uint32_t)g.queue.size();
+        g.queue.insert(g.queue.end(), per[w].begin(), per[w].end());
+    }
+    g.queue_off[W] = (uint32_t)g.queue.size();
+    return 0;
+}
+
+size_t export_size(const Graph& g) {
+    return sizeof(ExportHeader) + g.tasks.size() * sizeof(Task) + g.target.size() * 8 + g.queue_off.size() * 4 +
+           g.queue.size() * 4 + g.order.size() * 4;
+}
+
+size_t export_graph(const Graph& g, void* buf, size_t cap) {
+    size_t need = export_size(g);
+    if (!buf || cap < need) return need;
+    ExportHeader hd;
+    memset(&hd, 0, sizeof(hd));
+    hd.magic = EXPORT_MAGIC;
+    hd.version = 1;
+    hd.n_tasks = (uint32_t)g.tasks.size();
+    hd.n_events = (uint32_t)g.target.size();
+    hd.W = (uint32_t)g.T.W;
+    hd.sched = g.sched;
+    const Tiling& T = g.T;
+    hd.L = T.L; hd.h = T.h; hd.nq = T.nq; hd.nkv = T.nkv; hd.d = T.d; hd.f = T.f; hd.V = T.V; hd.B = T.B; hd.C = T.C;
+    hd.grp = T.grp; hd.qkv_pairs = T.qkv_pairs; hd.attn_splits = T.attn_splits; hd.o_rows = T.o_rows;
+    hd.g_rows = T.g_rows; hd.kd = T.kd; hd.d_rows = T.d_rows; hd.lm_rows = T.lm_rows;
+    hd.record_bytes = sizeof(Task);
+    uint8_t* p = (uint8_t*)buf;
+    memcpy(p, &hd, sizeof(hd));
+    p += sizeof(hd);
+    auto put = [&](const void* src, size_t bytes) {
+        if (bytes) memcpy(p, src, bytes);
+        p += bytes;
+    };
+    put(g.tasks.data(), g.tasks.size() * sizeof(Task));
+    put(g.target.data(), g.target.size() * 4);
+    put(g.nsub.data(), g.nsub.size() * 4);
+    put(g.queue_off.data(), g.queue_off.size() * 4);
+    put(g.queue.data(), g.queue.size() * 4);
+    put(g.order.data(), g.order.size() * 4);
+    return need;
+}
+
+}  // namespace mk

@@ -1,0 +1,969 @@
+// Persistent decode megakernel for gfx950 (MI355X).
+//
+// One launch runs one decode step.  Each workgroup owns one CU (the ~150 KiB of
+// LDS it declares leaves room for no second one) and runs an interpreter over
+// a queue of tile tasks (koas-w.github.io megakernel notes, "on-GPU
+// interpreter / persistent kernel"; Hazy Research megakernel news page,
+// section 4, "fusion big bang").  The workgroup has five waves:
+//
+//   wave 4 (loader): fetches task records (static: its own queue; dynamic: an
+//     atomic pop from one global queue, koas-w.github.io notes, "static and
+//     dynamic scheduling") into an LDS FIFO, and streams every task's weights
+//     (attention: its KV-cache chunk) into a ring of 16 KiB LDS pages with
+//     global_load_lds_dwordx4.  Weights never depend on activations, so the
+//     loader runs ahead of the compute waves as far as free pages allow: the
+//     next tasks' weights arrive while the current task still waits on its
+//     inputs (Hazy page, section 4, "shared memory to remove memory bubbles":
+//     paged shared memory; pages released by one instruction are handed to the
+//     next one so it can start its loads early).  The loader keeps its vector
+//     memory counter for the page loads alone: task records and parameters are
+//     read with scalar loads, control words through LDS.
+//   waves 0-3 (compute): wait for the task's event counter, stage its
+//     activations into LDS, run the op out of the LDS pages, store results and
+//     add one to the event the task completes (Hazy page, section 4,
+//     "synchronisation"; MPK news page, part 2: fetch, execute, trigger event).
+//
+// Cross-CU data (activations, partial sums, counters) is written with
+// device-scope (sc1) stores or atomics, waited for with s_waitcnt, and read
+// with device-scope loads; no L2 write-back or invalidate is issued inside the
+// step.  Weights and the KV-cache prefix come from earlier launches and use
+// ordinary (LDS-DMA) loads.
+#include <hip/hip_runtime.h>
+
+#include "mk_internal.h"
+#include "runtime.h"
+
+namespace mk {
+
+constexpr int NCW = 4;                 // compute waves
+constexpr int NTHREADS = (NCW + 1) * 64;
+constexpr int PAGE = 16384;            // LDS page (bytes)
+constexpr int NPAGES = 8;              // ring of 8 pages = 128 KiB
+constexpr int FIFO = 16;               // task records in flight in LDS
+constexpr int XS = MAX_ACT;            // activation staging (floats)
+constexpr int ROWRES = MAX_TILE_ROWS;  // per-task row results (floats)
+constexpr int MAX_INFLIGHT = 3;        // pages in flight (3 * 16 loads < 64 = vmcnt range)
+constexpr int MAXB = 64;               // sequences per step held in LDS
+
+struct __attribute__((aligned(16))) Smem {
+    float xs[XS];
+    float rowres[ROWRES];
+    Task fifo[FIFO];
+    float wsc[NCW][64];
+    int32_t pos[MAXB];
+    int32_t tok[MAXB];
+    StepArgs args;
+    uint32_t fifo_first_page[FIFO];
+    uint32_t fifo_ready[FIFO];
+    uint32_t fifo_free[FIFO];
+    uint32_t page_ready[NPAGES];
+    uint32_t page_free[NPAGES];
+    uint32_t go, cbar, done, abort;
+};
+
+__shared__ Smem S;
+// The page ring is its own LDS object so that LDS accesses of the loader to the
+// control words can be told apart from its in-flight LDS-DMA writes.
+__shared__ __attribute__((aligned(16))) uint8_t ring[NPAGES][PAGE];
+
+typedef const __attribute__((address_space(4))) Params CParams;
+typedef __attribute__((address_space(3))) volatile uint32_t lds_u32;
+typedef __attribute__((address_space(1))) uint32_t g_u32;
+typedef __attribute__((address_space(1))) float g_f32;
+typedef __attribute__((address_space(1))) unsigned long long g_u64;
+
+// ---- small device helpers -----------------------------------------------------
+
+__device__ __forceinline__ uint64_t rtc() { return __builtin_amdgcn_s_memrealtime(); }
+__device__ __forceinline__ uint32_t xcc_id() { return __builtin_amdgcn_s_getreg(20 | (3 << 11)) & 7u; }
+__device__ __forceinline__ uint32_t uni(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Params are read through the constant address space with a wave-uniform pointer: scalar loads.
+__device__ __forceinline__ CParams& P(const Params* pp) {
+    uint64_t v = (uint64_t)pp;
+    uint32_t lo = uni((uint32_t)v), hi = uni((uint32_t)(v >> 32));
+    return *(CParams*)(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ uint32_t lds_ld(const uint32_t& x) { return *(lds_u32*)&x; }
+__device__ __forceinline__ void lds_st(uint32_t& x, uint32_t v) { *(lds_u32*)&x = v; }
+__device__ __forceinline__ void lds_add(uint32_t& x, uint32_t v) {
+    __hip_atomic_fetch_add(&x, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+__device__ __forceinline__ uint32_t ld_dev(const uint32_t* p) {
+    return __hip_atomic_load((g_u32*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ldf_dev(const float* p) { return __uint_as_float(ld_dev((const uint32_t*)p)); }
+__device__ __forceinline__ void st_dev(uint32_t* p, uint32_t v) {
+    __hip_atomic_store((g_u32*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void stf_dev(float* p, float v) { st_dev((uint32_t*)p, __float_as_uint(v)); }
+__device__ __forceinline__ void addf_dev(float* p, float v) {
+    __hip_atomic_fetch_add((g_f32*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t addu_dev(uint32_t* p, uint32_t v) {
+    return __hip_atomic_fetch_add((g_u32*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// 16-bit device-scope store through a buffer resource whose base is wave-uniform
+__device__ __forceinline__ void st16_dev(uint16_t* base, uint32_t idx, uint16_t v) {
+    __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7ffffff0, 0x00020000);
+    __builtin_amdgcn_raw_buffer_store_b16(v, r, idx * 2, 0, 16 /* sc1 */);
+}
+__device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void lgkm_wait_all() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+__device__ __forceinline__ uint16_t f2bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float dot8(uint4 w, const float* x, float a) {
+    a = fmaf(bf16lo(w.x), x[0], a);
+    a = fmaf(bf16hi(w.x), x[1], a);
+    a = fmaf(bf16lo(w.y), x[2], a);
+    a = fmaf(bf16hi(w.y), x[3], a);
+    a = fmaf(bf16lo(w.z), x[4], a);
+    a = fmaf(bf16hi(w.z), x[5], a);
+    a = fmaf(bf16lo(w.w), x[6], a);
+    a = fmaf(bf16hi(w.w), x[7], a);
+    return a;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+template <int W>
+__device__ __forceinline__ float seg_sum(float v) {
+#pragma unroll
+    for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+__device__ __forceinline__ uint32_t ctr_index(uint32_t ev, uint32_t sub) { return (ev * 8u + sub) * 32u; }
+
+// ---- error path -------------------------------------------------------------------
+
+__device__ __noinline__ void raise_error(const Params* pp, uint32_t code, uint32_t task, uint32_t ev, uint32_t seen,
+                                         uint32_t target) {
+    CParams& p = P(pp);
+    uint32_t* st = p.state;
+    uint32_t expected = 0u;
+    if (__hip_atomic_compare_exchange_strong((g_u32*)&st[ST_ERR], &expected, code, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT)) {
+        st_dev(&st[ST_ERR + 1], blockIdx.x);
+        st_dev(&st[ST_ERR + 2], task);
+        st_dev(&st[ST_ERR + 3], ev);
+        st_dev(&st[ST_ERR + 4], seen);
+        st_dev(&st[ST_ERR + 5], target);
+    }
+    st_dev(&st[ST_ABORT], 1u);
+    lds_st(S.abort, 1u);
+}
+
+// Spin until an LDS word reaches v.  Returns false on abort or timeout.
+__device__ __noinline__ bool lds_wait_ge(const uint32_t& w, uint32_t v, const Params* pp, uint32_t task) {
+    uint64_t t0 = 0;
+    uint32_t it = 0;
+    while (lds_ld(w) < v) {
+        if (lds_ld(S.abort)) return false;
+        if ((++it & 255u) == 0u) {
+            CParams& p = P(pp);
+            const uint64_t now = rtc();
+            if (t0 == 0) {
+                t0 = now;
+            } else if (now - t0 > p.timeout) {
+                raise_error(pp, ERR_TIMEOUT_LDS, task, NONE, lds_ld(w), v);
+                return false;
+            }
+            if (ld_dev(&p.state[ST_ABORT])) {
+                lds_st(S.abort, 1u);
+                return false;
+            }
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    return true;
+}
+
+// Compute wave 0: wait until the event's sub-counters sum to `want`.
+__device__ __noinline__ bool wait_event(const Params* pp, uint32_t ev, uint32_t nsub, uint32_t want, uint32_t task) {
+    CParams& p = P(pp);
+    const int lane = threadIdx.x & 63;
+    const uint64_t t0 = rtc();
+    uint32_t it = 0;
+    const uint32_t* ctr = p.ctr;
+    for (;;) {
+        uint32_t v = (uint32_t)lane < nsub ? ld_dev(&ctr[ctr_index(ev, lane)]) : 0u;
+        v += __shfl_xor(v, 1, 64);
+        v += __shfl_xor(v, 2, 64);
+        v += __shfl_xor(v, 4, 64);
+        const uint32_t sum = uni(v);
+        if (sum >= want) return true;
+        if (lds_ld(S.abort)) return false;
+        if ((++it & 63u) == 0u) {
+            if (ld_dev(&p.state[ST_ABORT])) {
+                lds_st(S.abort, 1u);
+                return false;
+            }
+            if (rtc() - t0 > p.timeout) {
+                raise_error(pp, ERR_TIMEOUT_EVENT, task, ev, sum, want);
+                return false;
+            }
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
+// ---- geometry shared by loader and compute -------------------------------------------
+
+struct Chunk {
+    int32_t c0, c1, P;  // chunk positions [c0, c1) of 0..P; prefix rows in LDS are [c0, min(c1, P))
+};
+__device__ __forceinline__ Chunk attn_chunk(int32_t splits, int32_t P, uint32_t c) {
+    const int32_t n = P + 1;
+    const int32_t lc = (n + splits - 1) / splits;
+    Chunk ch;
+    ch.P = P;
+    ch.c0 = min(n, (int32_t)c * lc);
+    ch.c1 = min(n, ch.c0 + lc);
+    return ch;
+}
+// one page holds 8 KiB of K rows then 8 KiB of V rows of consecutive positions
+__device__ __forceinline__ int32_t attn_block_rows(int32_t d) { return 4096 / d; }
+
+__device__ __forceinline__ int32_t seq_pos(uint32_t b) { return (int32_t)lds_ld(*(const uint32_t*)&S.pos[b]); }
+
+__device__ __forceinline__ uint32_t task_pages(const Task& k, int32_t splits, int32_t d) {
+    if (k.op == OP_ATTN) {
+        const Chunk ch = attn_chunk(splits, seq_pos(k.seq), k.row0);
+        const int32_t npre = max(0, min(ch.c1, ch.P) - ch.c0);
+        const int32_t pb = attn_block_rows(d);
+        return (uint32_t)((npre + pb - 1) / pb);
+    }
+    return (k.wbytes + PAGE - 1) / PAGE;
+}
+
+// ---- loader wave ---------------------------------------------------------------------
+
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_off) {
+    __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)((uint8_t*)&ring[0][0] + lds_off), 16, 0,
+                                     0);
+}
+
+__device__ __forceinline__ void issue_page(CParams& p, const Task& k, uint32_t kp, uint32_t slot, int lane) {
+    const uint32_t dst = slot * PAGE;
+    if (k.op == OP_ATTN) {
+        const int32_t d = p.T.d;
+        const Chunk ch = attn_chunk(p.T.attn_splits, seq_pos(k.seq), k.row0);
+        const int32_t pb = attn_block_rows(d);
+        const int32_t p0 = ch.c0 + (int32_t)kp * pb;
+        const int32_t rows = min(pb, min(ch.c1, ch.P) - p0);
+        const uint32_t valid = (uint32_t)rows * (uint32_t)d * 2u;
+        const uint64_t row = (((uint64_t)k.layer * p.T.B + k.seq) * p.T.nkv + k.part) * (uint64_t)p.T.C + (uint64_t)p0;
+        const uint8_t* kb = (const uint8_t*)S.args.kc + row * d * 2;
+        const uint8_t* vb = (const uint8_t*)S.args.vc + row * d * 2;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t off = min((uint32_t)(j * 1024 + lane * 16), valid - 16u);
+            dma16(kb + off, dst + j * 1024);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t off = min((uint32_t)(j * 1024 + lane * 16), valid - 16u);
+            dma16(vb + off, dst + 8192 + j * 1024);
+        }
+    } else {
+        const uint8_t* base = p.w + k.wofs + (uint64_t)kp * PAGE;
+        const uint32_t valid = min((uint32_t)PAGE, k.wbytes - kp * PAGE);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const uint32_t off = min((uint32_t)(j * 1024 + lane * 16), valid - 16u);
+            dma16(base + off, dst + j * 1024);
+        }
+    }
+}
+
+typedef const __attribute__((address_space(4))) uint32_t c_u32;
+typedef const __attribute__((address_space(4))) Task c_task;
+
+__device__ __noinline__ void loader(const Params* pp, uint32_t epoch) {
+    CParams& p = P(pp);
+    const int lane = threadIdx.x & 63;
+    const uint32_t W = gridDim.x;
+    c_u32* qoff = (c_u32*)p.queue_off;
+    c_u32* queue = (c_u32*)p.queue;
+    c_task* tasks = (c_task*)p.tasks;
+    const uint32_t sched = p.sched;
+    const uint32_t n_tasks = p.n_tasks;
+    const int32_t splits = p.T.attn_splits, hd = p.T.d;
+    uint32_t qbeg = 0, qend = 0;
+    if (sched == 0) {
+        qbeg = qoff[blockIdx.x];
+        qend = qoff[blockIdx.x + 1];
+    }
+    uint32_t pseq = 0, pub = 0;  // next page to issue / to publish
+
+    auto publish_one = [&]() {
+        if (lane == 0) lds_st(S.page_ready[pub % NPAGES], pub + 1);
+        ++pub;
+    };
+    auto drain = [&]() {
+        vm_wait_all();
+        while (pub < pseq) publish_one();
+    };
+
+    for (uint32_t t = 0;; ++t) {
+        bool end;
+        uint32_t ti;
+        if (sched == 0) {
+            end = qbeg + t >= qend;
+            ti = end ? 0u : queue[qbeg + t];
+        } else {
+            drain();
+            uint32_t old = 0;
+            if (lane == 0) old = addu_dev(&p.state[ST_HEAD], 1u);
+            old = uni(old);
+            const uint32_t rel = old - (epoch - 1u) * (n_tasks + W);
+            end = rel >= n_tasks;
+            ti = end ? 0u : rel;
+        }
+        const uint32_t slot = t % FIFO;
+        if (lds_ld(S.fifo_free[slot]) < t / FIFO) {
+            drain();
+            if (!uni(lds_wait_ge(S.fifo_free[slot], t / FIFO, pp, ti))) break;
+        }
+        Task k;
+        ti = uni(ti);
+        if (!end) {
+            c_u32* src = (c_u32*)&tasks[ti];
+#pragma unroll
+            for (int i = 0; i < 12; ++i) ((uint32_t*)&k)[i] = src[i];
+        } else {
+            k = Task();
+            k.op = OP_END;
+        }
+        if (lane == 0) {
+#pragma unroll
+            for (int i = 0; i < 12; ++i) lds_st(((uint32_t*)&S.fifo[slot])[i], ((const uint32_t*)&k)[i]);
+            lds_st(S.fifo_first_page[slot], pseq);
+        }
+        lgkm_wait_all();
+        if (lane == 0) lds_st(S.fifo_ready[slot], t + 1);
+        if (end) break;
+        const uint32_t np = task_pages(k, splits, hd);
+        for (uint32_t kp = 0; kp < np; ++kp) {
+            const uint32_t ps = pseq % NPAGES;
+            const uint32_t need = NCW * (pseq / NPAGES);
+            if (lds_ld(S.page_free[ps]) < need) {
+                drain();
+                if (!uni(lds_wait_ge(S.page_free[ps], need, pp, ti))) goto out;
+            }
+            issue_page(p, k, kp, ps, lane);
+            ++pseq;
+            if (pseq - pub == MAX_INFLIGHT) {
+                vm_wait<16 * (MAX_INFLIGHT - 1)>();
+                publish_one();
+            }
+        }
+    }
+out:
+    drain();
+}
+
+// ---- compute-wave primitives -------------------------------------------------------
+
+__device__ __forceinline__ bool cbarrier(const Params* pp, uint32_t& cgen, int lane, uint32_t task) {
+    cgen += NCW;
+    lgkm_wait_all();
+    if (lane == 0) lds_add(S.cbar, 1u);
+    return lds_wait_ge(S.cbar, cgen, pp, task);
+}
+
+__device__ __forceinline__ bool page_acquire(const Params* pp, uint32_t seq, uint32_t task) {
+    return lds_wait_ge(S.page_ready[seq % NPAGES], seq + 1, pp, task);
+}
+__device__ __forceinline__ void page_release(uint32_t seq, int lane) {
+    lgkm_wait_all();
+    if (lane == 0) lds_add(S.page_free[seq % NPAGES], 1u);
+}
+
+// This lane's slice of the staged activation vector (LDS xs[xo + column]) times
+// scale and the bf16 gains g (null: 1), in the order the GEMV consumes it.
+template <int KT>
+__device__ __forceinline__ void load_x(int xo, int lane, float scale, const uint16_t* g, float* x) {
+    if constexpr (KT >= 512) {
+#pragma unroll
+        for (int j = 0; j < KT / 512; ++j)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int c = j * 512 + lane * 8 + i;
+                x[j * 8 + i] = S.xs[xo + c] * scale * (g ? bf16f(g[c]) : 1.0f);
+            }
+    } else {
+        constexpr int LPROW = KT / 8;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int c = (lane % LPROW) * 8 + i;
+            x[i] = S.xs[xo + c] * scale * (g ? bf16f(g[c]) : 1.0f);
+        }
+    }
+}
+
+// y[r] = W[r, :] . x over the task's rows; weights in consecutive LDS pages from
+// page sequence `page0`; results in S.rowres[r].  Every compute wave releases
+// every page of the task exactly once.
+template <int KT>
+__device__ __noinline__ bool gemv_tile(const Params* pp, int wave, uint32_t page0, uint32_t nrows, uint32_t wbytes,
+                                       int xo, float scale, const uint16_t* g, uint32_t task) {
+    const int lane = threadIdx.x & 63;
+    float x[KT >= 512 ? KT / 64 : 8];
+    load_x<KT>(xo, lane, scale, g, x);
+    const uint32_t npages = (wbytes + PAGE - 1) / PAGE;
+    if constexpr (KT >= 512) {
+        constexpr int RB = 2 * KT;      // bytes per row
+        constexpr int RPP = PAGE / RB;  // rows per page (>= 1)
+        constexpr int LPR = KT / 512;   // 1 KiB wave loads per row
+        for (uint32_t pg = 0; pg < npages; ++pg) {
+            if (!page_acquire(pp, page0 + pg, task)) return false;
+            const uint32_t slot = (page0 + pg) % NPAGES;
+            const uint32_t r_lo = pg * RPP;
+            const uint32_t r_hi = min(nrows, r_lo + RPP);
+            uint32_t r = r_lo + ((uint32_t)(wave - (int)(r_lo % NCW)) + NCW) % NCW;
+            for (; r < r_hi; r += NCW) {
+                const uint32_t off = (r - r_lo) * RB + lane * 16;
+                float a = 0.f;
+#pragma unroll
+                for (int j = 0; j < LPR; ++j) {
+                    const uint4 w = *(const uint4*)&ring[slot][off + j * 1024];
+                    a = dot8(w, x + j * 8, a);
+                }
+                a = wave_sum(a);
+                if (lane == 0) S.rowres[r] = a;
+            }
+            page_release(page0 + pg, lane);
+        }
+    } else {
+        constexpr int RB = 2 * KT;
+        constexpr int RPL = 1024 / RB;   // rows per 1 KiB load
+        constexpr int LPROW = 64 / RPL;  // lanes per row
+        for (uint32_t pg = 0; pg < npages; ++pg) {
+            if (!page_acquire(pp, page0 + pg, task)) return false;
+            const uint32_t slot = (page0 + pg) % NPAGES;
+#pragma unroll
+            for (int uu = 0; uu < 16 / NCW; ++uu) {
+                const uint32_t u = (uint32_t)(uu * NCW + wave);  // 1 KiB unit within the page
+                const uint32_t r = (pg * 16 + u) * RPL + lane / LPROW;
+                const uint4 w = *(const uint4*)&ring[slot][u * 1024 + lane * 16];
+                const float a = seg_sum<LPROW>(dot8(w, x, 0.f));
+                if ((lane % LPROW) == 0 && r < nrows) S.rowres[r] = a;
+            }
+            page_release(page0 + pg, lane);
+        }
+    }
+    return true;
+}
+
+__device__ bool gemv(int kt, const Params* pp, int wave, uint32_t page0, uint32_t nrows, uint32_t wbytes, int xo,
+                     float scale, const uint16_t* g, uint32_t task) {
+    switch (kt) {
+        case 64: return gemv_tile<64>(pp, wave, page0, nrows, wbytes, xo, scale, g, task);
+        case 128: return gemv_tile<128>(pp, wave, page0, nrows, wbytes, xo, scale, g, task);
+        case 256: return gemv_tile<256>(pp, wave, page0, nrows, wbytes, xo, scale, g, task);
+        case 512: return gemv_tile<512>(pp, wave, page0, nrows, wbytes, xo, scale, g, task);
+        case 1024: return gemv_tile<1024>(pp, wave, page0, nrows, wbytes, xo, scale, g, task);
+        case 2048: return gemv_tile<2048>(pp, wave, page0, nrows, wbytes, xo, scale, g, task);
+        default: return gemv_tile<4096>(pp, wave, page0, nrows, wbytes, xo, scale, g, task);
+    }
+}
+
+// RMS scale 1/sqrt(mean(xs^2) + eps) of xs[0..n), computed by one wave
+__device__ __forceinline__ float rms_scale(int n, float eps, int lane) {
+    float ss = 0.f;
+    for (int i = lane; i < n; i += 64) ss = fmaf(S.xs[i], S.xs[i], ss);
+    ss = wave_sum(ss);
+    return 1.0f / sqrtf(ss / (float)n + eps);
+}
+
+__device__ __forceinline__ float* acc_buf(CParams& p, uint32_t parity, int idx, int b) {
+    return p.acc + (((size_t)parity * (2 * p.T.L + 1) + idx) * p.T.B + b) * p.T.h;
+}
+__device__ __forceinline__ const uint16_t* gains(CParams& p, int idx) {
+    return (const uint16_t*)(p.w + p.lay.gains) + (size_t)idx * p.T.h;
+}
+__device__ __forceinline__ const uint16_t* embed_row(CParams& p, int b) {
+    return (const uint16_t*)(p.w + p.lay.embed) + (size_t)S.tok[b] * p.T.h;
+}
+
+// ---- staging (compute wave 0, after the event) -----------------------------------------
+
+__device__ __noinline__ void stage(const Params* pp, const Task& k, uint32_t parity) {
+    CParams& p = P(pp);
+    const int lane = threadIdx.x & 63;
+    const int h = p.T.h;
+    switch (k.op) {
+        case OP_QKV:
+        case OP_LMHEAD: {
+            const int l = k.op == OP_QKV ? (int)k.layer : p.T.L;
+            if (l == 0) {
+                const uint16_t* e = embed_row(p, 0);
+                for (int i = lane; i < h; i += 64) S.xs[i] = bf16f(e[i]);
+            } else {
+                const float* src = acc_buf(p, parity, 2 * l - 1, 0);
+                for (int i = lane; i < h; i += 64) S.xs[i] = ldf_dev(src + i);
+            }
+            break;
+        }
+        case OP_GATEUP: {
+            const float* src = acc_buf(p, parity, 2 * k.layer, 0);
+            for (int i = lane; i < h; i += 64) S.xs[i] = ldf_dev(src + i);
+            break;
+        }
+        case OP_DOWN: {
+            const float* src = p.m + (size_t)k.part * p.T.kd;
+            for (int i = lane; i < p.T.kd; i += 64) S.xs[i] = ldf_dev(src + i);
+            break;
+        }
+        case OP_ATTN: {
+            const float* q = p.q + (size_t)k.seq * p.T.nq * p.T.d + (size_t)k.part * p.T.grp * p.T.d;
+            for (int i = lane; i < p.T.grp * p.T.d; i += 64) S.xs[i] = ldf_dev(q + i);
+            break;
+        }
+        case OP_OPROJ: {
+            // a = sum_c e^(m_c - M) o_c / sum_c e^(m_c - M) l_c over the chunks c of every head of the group
+            const int D = p.T.d, Sp = p.T.attn_splits, G = p.T.grp;
+            const size_t hstride = (size_t)(D + 2), cstride = (size_t)G * (D + 2);
+            for (int hw = 0; hw < G; ++hw) {
+                const float* src = p.part + ((size_t)k.part * Sp * G + hw) * hstride;
+                float Mx = -INFINITY;
+                for (int c = 0; c < Sp; ++c) Mx = fmaxf(Mx, ldf_dev(src + c * cstride));
+                float den = 0.f, num0 = 0.f, num1 = 0.f;
+                for (int c = 0; c < Sp; ++c) {
+                    const float* pc = src + c * cstride;
+                    const float mc = ldf_dev(pc);
+                    const float sc = mc == -INFINITY ? 0.f : __expf(mc - Mx);
+                    den = fmaf(sc, ldf_dev(pc + 1), den);
+                    num0 = fmaf(sc, ldf_dev(pc + 2 + lane), num0);
+                    if (D == 128) num1 = fmaf(sc, ldf_dev(pc + 2 + 64 + lane), num1);
+                }
+                S.xs[hw * D + lane] = num0 / den;
+                if (D == 128) S.xs[hw * D + 64 + lane] = num1 / den;
+            }
+            break;
+        }
+        default: break;
+    }
+}
+
+// ---- ops ---------------------------------------------------------------------------------
+
+__device__ __noinline__ bool op_qkv(const Params* pp, int wave, uint32_t& cgen, const Task& k, uint32_t page0) {
+    CParams& p = P(pp);
+    const int lane = threadIdx.x & 63;
+    const float r = rms_scale(p.T.h, p.eps, lane);
+    if (!gemv(p.T.h, pp, wave, page0, 2 * k.nrows, k.wbytes, 0, r, gains(p, 2 * k.layer), k.id)) return false;
+    if (!cbarrier(pp, cgen, lane, k.id)) return false;
+    // one lane per RoPE pair; rows [0, n) of the tile are first halves, [n, 2n) second halves
+    const int tid = wave * 64 + lane;
+    const uint32_t n = k.nrows;
+    const int half = p.T.d / 2;
+    const uint32_t slot = k.part;
+    const int nq = p.T.nq, nkv = p.T.nkv;
+    const int32_t P0 = S.pos[0];
+    if ((uint32_t)tid < n) {
+        const int j = (int)k.row0 + tid;
+        float lo = S.rowres[tid], hi = S.rowres[n + tid];
+        if (slot < (uint32_t)(nq + nkv)) {
+            const float2 cs = p.rope[(size_t)P0 * half + j];
+            const float a = lo * cs.x - hi * cs.y;
+            const float c = lo * cs.y + hi * cs.x;
+            lo = a;
+            hi = c;
+        }
+        if (slot < (uint32_t)nq) {
+            float* q = p.q + (size_t)slot * p.T.d;
+            stf_dev(q + j, lo);
+            stf_dev(q + j + half, hi);
+        }
+    }
+    if (slot >= (uint32_t)nq) {
+        const bool is_k = slot < (uint32_t)(nq + nkv);
+        const int g = is_k ? (int)slot - nq : (int)slot - nq - nkv;
+        uint16_t* base = (is_k ? S.args.kc : S.args.vc) +
+                         (((size_t)k.layer * p.T.B + 0) * nkv + g) * (size_t)p.T.C * p.T.d + (size_t)P0 * p.T.d;
+        if ((uint32_t)tid < n) {
+            const int j = (int)k.row0 + tid;
+            float lo = S.rowres[tid], hi = S.rowres[n + tid];
+            if (is_k) {
+                const float2 cs = p.rope[(size_t)P0 * half + j];
+                const float a = lo * cs.x - hi * cs.y;
+                const float c = lo * cs.y + hi * cs.x;
+                lo = a;
+                hi = c;
+            }
+            st16_dev(base, (uint32_t)j, f2bf16(lo));
+            st16_dev(base, (uint32_t)(j + half), f2bf16(hi));
+        }
+    }
+    return true;
+}
+
+// Attention over one chunk of the context of (sequence, KV group): one wave per query head.
+template <int D>
+__device__ __noinline__ bool op_attn(const Params* pp, int wave, const Task& k, uint32_t page0) {
+    CParams& p = P(pp);
+    const int lane = threadIdx.x & 63;
+    const int b = (int)k.seq, g = k.part;
+    const Chunk ch = attn_chunk(p.T.attn_splits, S.pos[b], k.row0);
+    const int32_t pb = attn_block_rows(D);
+    const int32_t pre_end = min(ch.c1, ch.P);
+    const int32_t npre = max(0, pre_end - ch.c0);
+    const uint32_t npages = (uint32_t)((npre + pb - 1) / pb);
+    const float scale = 1.0f / sqrtf((float)D);
+    constexpr int DL = D / 64;  // dimensions per lane
+    const int G = p.T.grp;
+    const int nh = (G - wave + NCW - 1) / NCW;  // heads of this wave: wave, wave + NCW, ...
+    float M[4], Ls[4], o[4][DL];
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh) {
+        M[hh] = -INFINITY;
+        Ls[hh] = 0.f;
+#pragma unroll
+        for (int e = 0; e < DL; ++e) o[hh][e] = 0.f;
+    }
+    for (uint32_t pg = 0; pg < npages; ++pg) {
+        if (!page_acquire(pp, page0 + pg, k.id)) return false;
+        const uint32_t slot = (page0 + pg) % NPAGES;
+        const int32_t rows = min(pb, pre_end - (ch.c0 + (int32_t)pg * pb));
+#pragma unroll
+        for (int hh = 0; hh < 4; ++hh) {
+            if (hh >= nh) break;
+            const int hw = wave + hh * NCW;
+            // scores: lane = position within the block
+            float s = -INFINITY;
+            if (lane < rows) {
+                float a = 0.f;
+#pragma unroll
+                for (int c = 0; c < D / 8; ++c) {
+                    const uint4 w = *(const uint4*)&ring[slot][lane * (2 * D) + c * 16];
+                    a = dot8(w, &S.xs[hw * D + c * 8], a);
+                }
+                s = a * scale;
+            }
+            const float mn = fmaxf(M[hh], wave_max(s));
+            const float corr = __expf(M[hh] - mn);
+            const float e = lane < rows ? __expf(s - mn) : 0.f;
+            Ls[hh] = Ls[hh] * corr + wave_sum(e);
+            M[hh] = mn;
+            S.wsc[wave][lane] = e;
+            lgkm_wait_all();
+            // o[t] += sum_p e_p V[p][t]: lane = dimension
+#pragma unroll
+            for (int ee = 0; ee < DL; ++ee) o[hh][ee] *= corr;
+            for (int r = 0; r < rows; ++r) {
+                const float wgt = S.wsc[wave][r];
+#pragma unroll
+                for (int ee = 0; ee < DL; ++ee) {
+                    const uint16_t vv = *(const uint16_t*)&ring[slot][8192 + r * (2 * D) + (lane + 64 * ee) * 2];
+                    o[hh][ee] = fmaf(wgt, bf16f(vv), o[hh][ee]);
+                }
+            }
+        }
+        page_release(page0 + pg, lane);
+    }
+    // the current token (position P) if it falls in this chunk: read back from the cache (bf16)
+    if (ch.c0 <= ch.P && ch.P < ch.c1) {
+        const size_t row = (((size_t)k.layer * p.T.B + b) * p.T.nkv + g) * (size_t)p.T.C + (size_t)ch.P;
+        const uint16_t* kr = S.args.kc + row * D;
+        const uint16_t* vr = S.args.vc + row * D;
+        float kv[DL], vv[DL];
+#pragma unroll
+        for (int ee = 0; ee < DL; ++ee) {
+            const int t = lane + 64 * ee;
+            const uint32_t wk = ld_dev((const uint32_t*)(kr + (t & ~1)));
+            const uint32_t wv = ld_dev((const uint32_t*)(vr + (t & ~1)));
+            kv[ee] = (t & 1) ? bf16hi(wk) : bf16lo(wk);
+            vv[ee] = (t & 1) ? bf16hi(wv) : bf16lo(wv);
+        }
+#pragma unroll
+        for (int hh = 0; hh < 4; ++hh) {
+            if (hh >= nh) break;
+            const int hw = wave + hh * NCW;
+            float a = 0.f;
+#pragma unroll
+            for (int ee = 0; ee < DL; ++ee) a = fmaf(S.xs[hw * D + lane + 64 * ee], kv[ee], a);
+            const float s = wave_sum(a) * scale;
+            const float mn = fmaxf(M[hh], s);
+            const float corr = __expf(M[hh] - mn);
+            const float e = __expf(s - mn);
+            Ls[hh] = Ls[hh] * corr + e;
+            M[hh] = mn;
+#pragma unroll
+            for (int ee = 0; ee < DL; ++ee) o[hh][ee] = fmaf(e, vv[ee], o[hh][ee] * corr);
+        }
+    }
+    // partials (m, l, o) -> part[b][g][chunk][head][D + 2]
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh) {
+        if (hh >= nh) break;
+        const int hw = wave + hh * NCW;
+        float* dst = p.part + ((((size_t)b * p.T.nkv + g) * p.T.attn_splits + k.row0) * G + hw) * (D + 2);
+        if (lane == 0) {
+            stf_dev(dst, M[hh]);
+            stf_dev(dst + 1, Ls[hh]);
+        }
+#pragma unroll
+        for (int ee = 0; ee < DL; ++ee) stf_dev(dst + 2 + lane + 64 * ee, o[hh][ee]);
+    }
+    return true;
+}
+
+__device__ __noinline__ bool op_oproj(const Params* pp, int wave, uint32_t& cgen, const Task& k, uint32_t page0,
+                                      uint32_t parity) {
+    CParams& p = P(pp);
+    const int lane = threadIdx.x & 63;
+    if (!gemv(p.T.grp * p.T.d, pp, wave, page0, k.nrows, k.wbytes, 0, 1.0f, nullptr, k.id)) return false;
+    if (!cbarrier(pp, cgen, lane, k.id)) return false;
+    float* dst = acc_buf(p, parity, 2 * k.layer, 0);
+    for (uint32_t i = (uint32_t)(wave * 64 + lane); i < k.nrows; i += NCW * 64) {
+        const uint32_t row = k.row0 + i;
+        float val = S.rowres[i];
+        if (k.flags & TF_RESID)
+            val += k.layer == 0 ? bf16f(embed_row(p, 0)[row]) : ldf_dev(acc_buf(p, parity, 2 * k.layer - 1, 0) + row);
+        addf_dev(dst + row, val);
+    }
+    return true;
+}
+
+__device__ __noinline__ bool op_gateup(const Params* pp, int wave, uint32_t& cgen, const Task& k, uint32_t page0) {
+    CParams& p = P(pp);
+    const int lane = threadIdx.x & 63;
+    const float r = rms_scale(p.T.h, p.eps, lane);
+    if (!gemv(p.T.h, pp, wave, page0, 2 * k.nrows, k.wbytes, 0, r, gains(p, 2 * k.layer + 1), k.id)) return false;
+    if (!cbarrier(pp, cgen, lane, k.id)) return false;
+    for (uint32_t i = (uint32_t)(wave * 64 + lane); i < k.nrows; i += NCW * 64) {
+        const float gt = S.rowres[i], up = S.rowres[k.nrows + i];
+        stf_dev(p.m + k.row0 + i, gt / (1.0f + __expf(-gt)) * up);
+    }
+    return true;
+}
+
+__device__ __noinline__ bool op_down(const Params* pp, int wave, uint32_t& cgen, const Task& k, uint32_t page0,
+                                     uint32_t parity) {
+    CParams& p = P(pp);
+    const int lane = threadIdx.x & 63;
+    if (!gemv(p.T.kd, pp, wave, page0, k.nrows, k.wbytes, 0, 1.0f, nullptr, k.id)) return false;
+    if (!cbarrier(pp, cgen, lane, k.id)) return false;
+    float* dst = acc_buf(p, parity, 2 * k.layer + 1, 0);
+    for (uint32_t i = (uint32_t)(wave * 64 + lane); i < k.nrows; i += NCW * 64) {
+        const uint32_t row = k.row0 + i;
+        float val = S.rowres[i];
+        if (k.flags & TF_RESID) val += ldf_dev(acc_buf(p, parity, 2 * k.layer, 0) + row);
+        addf_dev(dst + row, val);
+    }
+    return true;
+}
+
+__device__ __noinline__ bool op_lmhead(const Params* pp, int wave, uint32_t& cgen, const Task& k, uint32_t page0,
+                                       uint32_t parity) {
+    CParams& p = P(pp);
+    const int lane = threadIdx.x & 63;
+    const float r = rms_scale(p.T.h, p.eps, lane);
+    if (!gemv(p.T.h, pp, wave, page0, k.nrows, k.wbytes, 0, r, gains(p, 2 * p.T.L), k.id)) return false;
+    if (!cbarrier(pp, cgen, lane, k.id)) return false;
+    float bv = -INFINITY;
+    uint32_t bi = 0xffffffffu;
+    float* logits = S.args.logits;
+    for (uint32_t i = (uint32_t)(wave * 64 + lane); i < k.nrows; i += NCW * 64) {
+        const float val = S.rowres[i];
+        if (logits) logits[k.row0 + i] = val;
+        if (val > bv) {  // rows visited in increasing order: the first maximum is kept
+            bv = val;
+            bi = k.row0 + i;
+        }
+    }
+    // pack (order-preserving value bits, inverted index): the largest key is the
+    // largest value at the lowest index
+    const uint32_t ub = __float_as_uint(bv);
+    const uint32_t ord = (ub & 0x80000000u) ? ~ub : (ub | 0x80000000u);
+    unsigned long long key = bi == 0xffffffffu ? 0ull : (((unsigned long long)ord << 32) | (0xffffffffu - bi));
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const unsigned long long other = __shfl_xor(key, o, 64);
+        key = other > key ? other : key;
+    }
+    if (lane == 0 && key)
+        __hip_atomic_fetch_max((g_u64*)&p.key[parity * p.T.B + 0], key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return true;
+}
+
+// After the last LM-head tile of the step: publish the argmax and the final residual.
+__device__ __noinline__ void finish_step(const Params* pp, uint32_t epoch, uint32_t parity) {
+    CParams& p = P(pp);
+    const int lane = threadIdx.x & 63;
+    uint32_t old = 0;
+    if (lane == 0) old = addu_dev(&p.ticket[0], 1u);
+    old = uni(old);
+    if (old + 1u != epoch * (uint32_t)p.T.n_lm_tiles) return;
+    const unsigned long long key =
+        __hip_atomic_load((g_u64*)&p.key[parity * p.T.B + 0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0) p.next[0] = (int32_t)(0xffffffffu - (uint32_t)(key & 0xffffffffu));
+    const int h = p.T.h;
+    if (p.T.L == 0) {
+        const uint16_t* e = embed_row(p, 0);
+        for (int i = lane; i < h; i += 64) p.hidden[i] = bf16f(e[i]);
+    } else {
+        const float* src = acc_buf(p, parity, 2 * p.T.L - 1, 0);
+        for (int i = lane; i < h; i += 64) p.hidden[i] = ldf_dev(src + i);
+    }
+}
+
+// ---- compute-wave main loop ---------------------------------------------------------------
+
+__device__ __noinline__ void compute(const Params* pp, uint32_t epoch, int wave) {
+    const int lane = threadIdx.x & 63;
+    const uint32_t parity = epoch & 1u;
+    uint32_t cgen = 0;
+    for (uint32_t t = 0;; ++t) {
+        const uint32_t slot = t % FIFO;
+        if (!lds_wait_ge(S.fifo_ready[slot], t + 1, pp, NONE)) return;
+        Task k;
+#pragma unroll
+        for (int i = 0; i < 12; ++i) ((uint32_t*)&k)[i] = uni(lds_ld(((const uint32_t*)&S.fifo[slot])[i]));
+        const uint32_t page0 = uni(lds_ld(S.fifo_first_page[slot]));
+        if (k.op == OP_END) return;
+        const uint64_t t_fetch = rtc();
+        uint64_t t_ready = 0;
+        // ---- wait for the inputs and stage them (wave 0) ----
+        if (wave == 0) {
+            if (k.wait_ev != NONE && !wait_event(pp, k.wait_ev, k.wait_nsub, epoch * k.wait_target, k.id)) return;
+            t_ready = rtc();
+            stage(pp, k, parity);
+            lgkm_wait_all();
+            if (lane == 0) lds_st(S.go, t + 1);
+        } else {
+            if (!lds_wait_ge(S.go, t + 1, pp, k.id)) return;
+        }
+        // ---- execute ----
+        bool ok = true;
+        switch (k.op) {
+            case OP_QKV: ok = op_qkv(pp, wave, cgen, k, page0); break;
+            case OP_ATTN: ok = P(pp).T.d == 64 ? op_attn<64>(pp, wave, k, page0) : op_attn<128>(pp, wave, k, page0); break;
+            case OP_OPROJ: ok = op_oproj(pp, wave, cgen, k, page0, parity); break;
+            case OP_GATEUP: ok = op_gateup(pp, wave, cgen, k, page0); break;
+            case OP_DOWN: ok = op_down(pp, wave, cgen, k, page0, parity); break;
+            case OP_LMHEAD: ok = op_lmhead(pp, wave, cgen, k, page0, parity); break;
+            default: break;
+        }
+        if (!ok) return;
+        // ---- completion: every wave's stores are done, then wave 0 signals ----
+        vm_wait_all();
+        lgkm_wait_all();
+        if (lane == 0) lds_add(S.done, 1u);
+        if (wave == 0) {
+            if (!lds_wait_ge(S.done, NCW * (t + 1), pp, k.id)) return;
+            CParams& p = P(pp);
+            if (k.sig_ev != NONE && k.id != p.drop_task && lane == 0) {
+                const uint32_t sub = k.sig_nsub == 8 ? xcc_id() : 0u;
+                addu_dev(&p.ctr[ctr_index(k.sig_ev, sub)], 1u);
+            }
+            if (k.op == OP_LMHEAD) finish_step(pp, epoch, parity);
+            if (p.task_count && lane == 0) addu_dev(&p.task_count[k.id], 1u);
+            if (p.trace && lane == 0) {
+                unsigned long long* tr = p.trace + (size_t)k.id * 4;
+                tr[0] = blockIdx.x;
+                tr[1] = t_fetch;
+                tr[2] = t_ready;
+                tr[3] = rtc();
+            }
+            vm_wait_all();
+            if (lane == 0) lds_add(S.fifo_free[slot], 1u);
+        }
+    }
+}
+
+// ---- the kernel --------------------------------------------------------------------------
+
+__global__ void __launch_bounds__(NTHREADS, 1) mk_step_kernel(const Params* pp, StepArgs a) {
+    const int wave = threadIdx.x >> 6;
+    CParams& p = P(pp);
+    if (threadIdx.x < FIFO) {
+        S.fifo_ready[threadIdx.x] = 0;
+        S.fifo_free[threadIdx.x] = 0;
+    }
+    if (threadIdx.x < NPAGES) {
+        S.page_ready[threadIdx.x] = 0;
+        S.page_free[threadIdx.x] = 0;
+    }
+    if (threadIdx.x == 0) {
+        S.go = 0;
+        S.cbar = 0;
+        S.done = 0;
+        S.abort = 0;
+        S.args = a;
+    }
+    const uint32_t epoch = p.state[ST_EPOCH];
+    const uint32_t parity = epoch & 1u;
+    const int B = p.T.B;
+    for (int b = threadIdx.x; b < B; b += NTHREADS) {
+        S.tok[b] = a.tokens[b];
+        S.pos[b] = a.positions[b];
+    }
+    __syncthreads();
+    bool bad = false;
+    for (int b = 0; b < B; ++b) {
+        if (S.tok[b] < 0 || S.tok[b] >= p.T.V) bad = true;
+        if (S.pos[b] < 0 || S.pos[b] >= p.T.C) bad = true;
+    }
+    if (bad) {
+        if (blockIdx.x == 0 && threadIdx.x == 0) raise_error(pp, ERR_INPUT, 0, 0, 0, 0);
+    } else {
+        // clear the other parity's accumulators and argmax keys for the next step (read only after this launch)
+        const size_t nacc = (size_t)(2 * p.T.L + 1) * B * p.T.h;
+        float* other = p.acc + (size_t)(parity ^ 1u) * nacc;
+        for (size_t i = (size_t)blockIdx.x * NTHREADS + threadIdx.x; i < nacc; i += (size_t)gridDim.x * NTHREADS)
+            other[i] = 0.f;
+        if (blockIdx.x == 0 && (int)threadIdx.x < B) p.key[(parity ^ 1u) * B + threadIdx.x] = 0ull;
+        if (wave == NCW) loader(pp, epoch);
+        else compute(pp, epoch, wave);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t old = addu_dev(&p.state[ST_EXIT], 1u);
+        if (old + 1u == epoch * gridDim.x) st_dev(&p.state[ST_EPOCH], epoch + 1u);
+    }
+}
+
+hipError_t launch_step(const Params* dparams, const StepArgs& a, uint32_t grid, hipStream_t stream, bool cooperative) {
+    if (cooperative) {
+        StepArgs ac = a;
+        const Params* pc = dparams;
+        void* args[] = {(void*)&pc, (void*)&ac};
+        return hipLaunchCooperativeKernel((const void*)mk_step_kernel, dim3(grid), dim3(NTHREADS), args, 0, stream);
+    }
+    hipLaunchKernelGGL(mk_step_kernel, dim3(grid), dim3(NTHREADS), 0, stream, dparams, a);
+    return hipGetLastError();
+}
+
+int step_threads() { return NTHREADS; }
+size_t step_lds_bytes() { return sizeof(Smem); }
+const void* step_kernel_ptr() { return (const void*)mk_step_kernel; }
+
+}  // namespace mk

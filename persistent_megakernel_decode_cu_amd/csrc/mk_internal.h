@@ -1,0 +1,90 @@
+// Internal definitions shared by the host task-graph builder, the runtime and
+// the device interpreter.  Not part of the public ABI (include/mk.h is).
+#pragma once
+#include <stdint.h>
+
+namespace mk {
+
+// ---- opcodes of the on-GPU interpreter ----------------------------------------
+enum Op : uint8_t {
+    OP_END = 0,       // end of a queue
+    OP_QKV = 1,       // RMSNorm + fused QKV GEMV tile + RoPE + KV-cache append
+    OP_ATTN = 2,      // GQA decode attention over one KV chunk -> (m, l, o) partials
+    OP_OPROJ = 3,     // merge attention partials of one KV group + O-proj K-slice + residual (atomic)
+    OP_GATEUP = 4,    // RMSNorm + gate/up GEMV tile + SiLU * up
+    OP_DOWN = 5,      // down-proj K-slice tile + residual (atomic)
+    OP_LMHEAD = 6,    // final RMSNorm + LM-head tile + argmax (packed 64-bit atomic max)
+    OP_COUNT = 7
+};
+
+constexpr uint32_t NONE = 0xFFFFFFFFu;
+
+// Device-side capacities the tiling must respect.
+constexpr int MAX_TILE_ROWS = 1024;  // rows of one GEMV tile (LDS row-result buffer)
+constexpr int MAX_ACT = 4096;        // floats of one staged activation vector (LDS)
+
+// One instruction of the interpreter: 48 bytes, read by the loader wave into LDS.
+struct Task {
+    uint8_t op;
+    uint8_t wait_nsub;     // sub-counters of the awaited event (1 or 8)
+    uint8_t sig_nsub;      // sub-counters of the signalled event (1 or 8)
+    uint8_t flags;         // op-specific (OPROJ/DOWN: add the residual)
+    uint16_t layer;
+    uint16_t part;         // QKV: head slot; ATTN/OPROJ: KV group; DOWN: K block; others 0
+    uint32_t row0;         // first output row (QKV: first RoPE pair; ATTN: chunk index)
+    uint32_t nrows;        // output rows of the tile (QKV: pairs)
+    uint32_t wait_ev;      // awaited event or NONE
+    uint32_t wait_target;  // producers of the awaited event (per step)
+    uint32_t sig_ev;       // signalled event or NONE
+    uint32_t wbytes;       // bytes of weights streamed into LDS pages for this task
+    uint64_t wofs;         // byte offset of those weights in the packed weight buffer
+    uint32_t seq;          // sequence (batch index) for ATTN; 0 otherwise
+    uint32_t id;           // global task index (topological order)
+};
+static_assert(sizeof(Task) == 48, "task record is 48 bytes");
+
+enum TaskFlags : uint8_t {
+    TF_RESID = 1,   // OPROJ / DOWN: this tile also adds the residual input
+    TF_ZEROKEY = 2  // reserved
+};
+
+// Tiling of one model on W workgroups (computed once on the host).
+struct Tiling {
+    int32_t L, h, nq, nkv, d, f, V, B, C, W;
+    int32_t grp;          // query heads per KV head
+    int32_t qkv_pairs;    // RoPE pairs per QKV tile (rows = 2 * pairs)
+    int32_t attn_splits;  // KV chunks per (sequence, KV group)
+    int32_t o_rows;       // O-proj tile rows (tile columns = grp * d)
+    int32_t g_rows;       // gate rows per gate/up tile (same number of up rows)
+    int32_t kd;           // down-proj K block (columns of m per tile)
+    int32_t d_rows;       // down-proj tile rows
+    int32_t lm_rows;      // LM-head rows per tile
+    int32_t n_qkv_tiles, n_attn_tiles, n_o_tiles, n_gu_tiles, n_down_tiles, n_lm_tiles;  // per layer / total LM
+};
+
+// Byte layout of the handle-owned packed weight buffer.
+struct Layout {
+    uint64_t gains;       // (2L+1) x h bf16: attn_norm[l], ffn_norm[l] (l = 0..L-1), final
+    uint64_t embed;       // V x h
+    uint64_t lm;          // V x h (== embed when tied)
+    uint64_t layer0;      // start of layer 0
+    uint64_t layer_bytes; // bytes per layer
+    uint64_t qkv, o, gu, down;  // offsets within a layer
+    uint64_t total;
+};
+
+// Export image (mk_export_graph / mk_plan_graph): header, then
+// Task[n_tasks], uint32 target[n_events], uint32 nsub[n_events],
+// uint32 queue_off[W+1], uint32 queue[n_tasks], uint32 order[n_tasks].
+struct ExportHeader {
+    uint32_t magic;       // 'MKG1'
+    uint32_t version;     // 1
+    uint32_t n_tasks, n_events, W, sched;
+    int32_t L, h, nq, nkv, d, f, V, B, C;
+    int32_t grp, qkv_pairs, attn_splits, o_rows, g_rows, kd, d_rows, lm_rows;
+    uint32_t record_bytes;
+    uint32_t reserved[7];
+};
+constexpr uint32_t EXPORT_MAGIC = 0x31474B4Du;
+
+}  // namespace mk

@@ -1,0 +1,425 @@
+// C ABI of the megakernel library: handle lifecycle, weight repacking, graph
+// upload and the one-launch decode step (declarations in include/mk.h).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/mk.h"
+#include "graph.h"
+#include "runtime.h"
+
+using namespace mk;
+
+struct mk_handle {
+    int device = 0;
+    int W = 0;
+    bool cooperative = true;
+    bool tied = true;
+    Graph g;
+    Params p;           // host copy
+    Params* dparams = nullptr;  // device copy read by the kernel
+    size_t n_events = 0;
+    size_t acc_bytes = 0;
+    // device allocations owned by the handle
+    std::vector<void*> allocs;
+};
+
+namespace {
+
+mk_status hip_fail(hipError_t e) {
+    (void)e;
+    return e == hipErrorOutOfMemory ? MK_E_NOMEM : MK_E_HIP;
+}
+
+#define HIPCHK(x)                                        \
+    do {                                                 \
+        hipError_t e_ = (x);                             \
+        if (e_ != hipSuccess) return hip_fail(e_);       \
+    } while (0)
+
+template <typename T>
+mk_status dalloc(mk_handle* h, T** out, size_t bytes, bool zero) {
+    void* p = nullptr;
+    if (bytes == 0) bytes = 256;
+    HIPCHK(hipMalloc(&p, bytes));
+    h->allocs.push_back(p);
+    if (zero) HIPCHK(hipMemset(p, 0, bytes));
+    *out = (T*)p;
+    return MK_OK;
+}
+
+Dims dims_of(const mk_model_desc* d) {
+    Dims dm;
+    dm.L = d->n_layers;
+    dm.h = d->hidden;
+    dm.nq = d->n_q_heads;
+    dm.nkv = d->n_kv_heads;
+    dm.d = d->head_dim;
+    dm.f = d->ffn_dim;
+    dm.V = d->vocab;
+    dm.n_experts = d->n_experts;
+    dm.top_k = d->top_k;
+    dm.fe = d->expert_ffn_dim;
+    return dm;
+}
+
+mk_status plan(const mk_model_desc* desc, int32_t batch, int32_t max_ctx, const mk_options* opt, int W, Graph* g,
+               bool* tied) {
+    if (!desc) return MK_E_INVALID;
+    mk_options o;
+    memset(&o, 0, sizeof(o));
+    o.debug_drop_signal = -1;
+    if (opt) o = *opt;
+    if (o.sched < 0 || o.sched > 1 || o.policy < 0 || o.policy > 1) return MK_E_INVALID;
+    PlanOptions po;
+    po.attn_splits = o.attn_splits;
+    Tiling T;
+    std::string err;
+    Dims dm = dims_of(desc);
+    if (dm.n_experts != 0 || batch != 1) {
+        if (dm.n_experts < 0 || batch < 1) return MK_E_INVALID;
+        return MK_E_UNSUPPORTED;
+    }
+    if (plan_tiling(dm, batch, max_ctx, W, po, &T, &err) != 0) return MK_E_INVALID;
+    Layout Ly;
+    *tied = desc->tied_lm_head != 0;
+    plan_layout(T, *tied, &Ly);
+    build_graph(T, Ly, o.sched, o.policy, g);
+    return MK_OK;
+}
+
+// Copy the caller's weights into the packed layout: gains, embedding (+ LM head),
+// then per layer the QKV, O, gate/up and down tiles in task order.
+mk_status repack(mk_handle* h, const mk_model_desc* d, uint8_t* wd) {
+    const Tiling& T = h->g.T;
+    const Layout& Ly = h->g.lay;
+    const size_t H = (size_t)T.h;
+    const size_t rowb = H * 2;
+    hipStream_t s = nullptr;
+    for (int l = 0; l < T.L; ++l) {
+        HIPCHK(hipMemcpyAsync(wd + Ly.gains + (size_t)(2 * l) * rowb, d->layers[l].attn_norm, rowb, hipMemcpyDeviceToDevice, s));
+        HIPCHK(hipMemcpyAsync(wd + Ly.gains + (size_t)(2 * l + 1) * rowb, d->layers[l].ffn_norm, rowb, hipMemcpyDeviceToDevice, s));
+    }
+    HIPCHK(hipMemcpyAsync(wd + Ly.gains + (size_t)(2 * T.L) * rowb, d->final_norm, rowb, hipMemcpyDeviceToDevice, s));
+    HIPCHK(hipMemcpyAsync(wd + Ly.embed, d->tok_embed, (size_t)T.V * rowb, hipMemcpyDeviceToDevice, s));
+    if (!h->tied) HIPCHK(hipMemcpyAsync(wd + Ly.lm, d->lm_head, (size_t)T.V * rowb, hipMemcpyDeviceToDevice, s));
+    const int half = T.d / 2, P = T.qkv_pairs;
+    for (const Task& k : h->g.tasks) {
+        if (k.op == OP_QKV) {
+            const mk_layer_weights& lw = d->layers[k.layer];
+            const uint8_t* src;
+            int hrow;
+            if (k.part < T.nq) {
+                src = (const uint8_t*)lw.wq;
+                hrow = k.part * T.d;
+            } else if (k.part < T.nq + T.nkv) {
+                src = (const uint8_t*)lw.wk;
+                hrow = (k.part - T.nq) * T.d;
+            } else {
+                src = (const uint8_t*)lw.wv;
+                hrow = (k.part - T.nq - T.nkv) * T.d;
+            }
+            uint8_t* dst = wd + k.wofs;
+            HIPCHK(hipMemcpyAsync(dst, src + (size_t)(hrow + k.row0) * rowb, (size_t)P * rowb, hipMemcpyDeviceToDevice, s));
+            HIPCHK(hipMemcpyAsync(dst + (size_t)P * rowb, src + (size_t)(hrow + k.row0 + half) * rowb, (size_t)P * rowb,
+                                  hipMemcpyDeviceToDevice, s));
+        } else if (k.op == OP_OPROJ) {
+            const size_t kt = (size_t)T.grp * T.d;
+            const uint8_t* src = (const uint8_t*)d->layers[k.layer].wo + ((size_t)k.row0 * T.nq * T.d + k.part * kt) * 2;
+            HIPCHK(hipMemcpy2DAsync(wd + k.wofs, kt * 2, src, (size_t)T.nq * T.d * 2, kt * 2, k.nrows,
+                                    hipMemcpyDeviceToDevice, s));
+        } else if (k.op == OP_GATEUP) {
+            const mk_layer_weights& lw = d->layers[k.layer];
+            const size_t nb = (size_t)k.nrows * rowb;
+            HIPCHK(hipMemcpyAsync(wd + k.wofs, (const uint8_t*)lw.w_gate + (size_t)k.row0 * rowb, nb, hipMemcpyDeviceToDevice, s));
+            HIPCHK(hipMemcpyAsync(wd + k.wofs + nb, (const uint8_t*)lw.w_up + (size_t)k.row0 * rowb, nb, hipMemcpyDeviceToDevice, s));
+        } else if (k.op == OP_DOWN) {
+            const size_t kd = (size_t)T.kd;
+            const uint8_t* src = (const uint8_t*)d->layers[k.layer].w_down + ((size_t)k.row0 * T.f + (size_t)k.part * kd) * 2;
+            HIPCHK(hipMemcpy2DAsync(wd + k.wofs, kd * 2, src, (size_t)T.f * 2, kd * 2, k.nrows, hipMemcpyDeviceToDevice, s));
+        }
+    }
+    HIPCHK(hipStreamSynchronize(s));
+    return MK_OK;
+}
+
+mk_status rearm(mk_handle* h) {
+    const Tiling& T = h->g.T;
+    Params& p = h->p;
+    HIPCHK(hipMemset(p.ctr, 0, h->n_events * 8 * 32 * 4));
+    std::vector<uint32_t> st(ST_WORDS, 0);
+    st[ST_EPOCH] = 1;
+    HIPCHK(hipMemcpy(p.state, st.data(), ST_WORDS * 4, hipMemcpyHostToDevice));
+    HIPCHK(hipMemset(p.acc, 0, h->acc_bytes));
+    HIPCHK(hipMemset(p.key, 0, sizeof(unsigned long long) * 2 * T.B));
+    HIPCHK(hipMemset(p.ticket, 0, 4 * T.B));
+    HIPCHK(hipDeviceSynchronize());
+    return MK_OK;
+}
+
+bool desc_ok(const mk_model_desc* d) {
+    if (!d || !d->tok_embed || !d->final_norm || (!d->tied_lm_head && !d->lm_head)) return false;
+    if (d->n_layers > 0 && !d->layers) return false;
+    for (int l = 0; l < d->n_layers; ++l) {
+        const mk_layer_weights& w = d->layers[l];
+        if (!w.attn_norm || !w.wq || !w.wk || !w.wv || !w.wo || !w.ffn_norm) return false;
+        if (d->n_experts == 0 && (!w.w_gate || !w.w_up || !w.w_down)) return false;
+    }
+    return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mk_status_str(mk_status s) {
+    switch (s) {
+        case MK_OK: return "ok";
+        case MK_E_INVALID: return "invalid argument";
+        case MK_E_UNSUPPORTED: return "unsupported";
+        case MK_E_NOMEM: return "out of memory";
+        case MK_E_HIP: return "HIP runtime error";
+        case MK_E_NOT_RESIDENT: return "persistent grid cannot be co-resident";
+        case MK_E_DEVICE: return "device-side error";
+        case MK_E_NO_DEVICE: return "no GPU";
+    }
+    return "unknown status";
+}
+
+mk_status mk_plan_graph(const mk_model_desc* desc, int32_t batch, int32_t max_ctx, const mk_options* opt,
+                        int32_t n_workgroups, void* buf, size_t cap, size_t* need) {
+    if (!desc || n_workgroups < 1) return MK_E_INVALID;
+    Graph g;
+    bool tied;
+    mk_status st = plan(desc, batch, max_ctx, opt, n_workgroups, &g, &tied);
+    if (st != MK_OK) return st;
+    size_t n = export_size(g);
+    if (need) *need = n;
+    if (!buf || cap < n) return MK_E_INVALID;
+    export_graph(g, buf, cap);
+    return MK_OK;
+}
+
+mk_status mk_build_graph(const mk_model_desc* desc, int32_t batch, int32_t max_ctx, const mk_options* opt,
+                         mk_handle** out) {
+    if (!out) return MK_E_INVALID;
+    *out = nullptr;
+    if (!desc_ok(desc)) return MK_E_INVALID;
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) return MK_E_NO_DEVICE;
+    mk_options o;
+    memset(&o, 0, sizeof(o));
+    o.debug_drop_signal = -1;
+    if (opt) o = *opt;
+    mk_handle* h = new mk_handle();
+    HIPCHK(hipGetDevice(&h->device));
+    hipDeviceProp_t prop;
+    HIPCHK(hipGetDeviceProperties(&prop, h->device));
+    int per_cu = 0;
+    HIPCHK(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, step_kernel_ptr(), step_threads(), 0));
+    const int max_resident = per_cu * prop.multiProcessorCount;
+    h->W = o.n_workgroups > 0 ? o.n_workgroups : prop.multiProcessorCount;
+    if (h->W > max_resident) {
+        delete h;
+        return MK_E_NOT_RESIDENT;
+    }
+    mk_status st = plan(desc, batch, max_ctx, &o, h->W, &h->g, &h->tied);
+    if (st != MK_OK) {
+        delete h;
+        return st;
+    }
+    const Tiling& T = h->g.T;
+    Params& p = h->p;
+    memset(&p, 0, sizeof(p));
+    p.T = T;
+    p.lay = h->g.lay;
+    p.eps = desc->rms_eps;
+    p.sched = (uint32_t)o.sched;
+    p.n_tasks = (uint32_t)h->g.tasks.size();
+    p.drop_task = o.debug_drop_signal >= 0 ? (uint32_t)o.debug_drop_signal : NONE;
+    const double ms = o.debug_timeout_ms > 0 ? o.debug_timeout_ms : 2000.0;
+    p.timeout = (unsigned long long)(ms * 1e5);  // 100 MHz clock
+    h->n_events = h->g.target.size();
+#define ALLOC(ptr, bytes, zero)                                   \
+    do {                                                          \
+        mk_status s_ = dalloc(h, &(ptr), (bytes), (zero));        \
+        if (s_ != MK_OK) {                                        \
+            mk_destroy(h);                                        \
+            return s_;                                            \
+        }                                                         \
+    } while (0)
+#define ALLOC2(ptr, bytes) ALLOC(ptr, bytes, false)
+    uint8_t* wd;
+    ALLOC(wd, h->g.lay.total, false);
+    p.w = wd;
+    st = repack(h, desc, wd);
+    if (st != MK_OK) {
+        mk_destroy(h);
+        return st;
+    }
+    Task* td;
+    ALLOC(td, h->g.tasks.size() * sizeof(Task), false);
+    p.tasks = td;
+    uint32_t *qo, *qq;
+    ALLOC(qo, h->g.queue_off.size() * 4, false);
+    ALLOC(qq, h->g.queue.size() * 4, false);
+    p.queue_off = qo;
+    p.queue = qq;
+    ALLOC(p.ctr, h->n_events * 8 * 32 * 4, true);
+    ALLOC(p.state, ST_WORDS * 4, true);
+    float2* rope;
+    const int half = T.d / 2;
+    ALLOC(rope, (size_t)T.C * half * sizeof(float2), false);
+    p.rope = rope;
+    ALLOC(p.q, (size_t)T.B * T.nq * T.d * 4, true);
+    ALLOC(p.part, (size_t)T.B * T.nkv * T.attn_splits * T.grp * (T.d + 2) * 4, true);
+    ALLOC(p.m, (size_t)T.B * T.f * 4, true);
+    h->acc_bytes = (size_t)2 * (2 * T.L + 1) * T.B * T.h * 4;
+    ALLOC(p.acc, h->acc_bytes, true);
+    ALLOC(p.hidden, (size_t)T.B * T.h * 4, true);
+    ALLOC(p.key, sizeof(unsigned long long) * 2 * T.B, true);
+    ALLOC(p.ticket, 4 * T.B, true);
+    ALLOC(p.next, 4 * T.B, true);
+    if (o.trace) {
+        ALLOC(p.task_count, h->g.tasks.size() * 4, true);
+        ALLOC(p.trace, h->g.tasks.size() * 32, true);
+    }
+    auto up = [&](void* dst, const void* src, size_t n) { return hipMemcpy(dst, src, n, hipMemcpyHostToDevice); };
+    if (up(td, h->g.tasks.data(), h->g.tasks.size() * sizeof(Task)) != hipSuccess ||
+        up(qo, h->g.queue_off.data(), h->g.queue_off.size() * 4) != hipSuccess ||
+        up(qq, h->g.queue.data(), h->g.queue.size() * 4) != hipSuccess) {
+        mk_destroy(h);
+        return MK_E_HIP;
+    }
+    // RoPE table: angle = pos * theta^(-2j/d), evaluated in double, stored as float (cos, sin)
+    std::vector<float2> tab((size_t)T.C * half);
+    for (int pos = 0; pos < T.C; ++pos)
+        for (int j = 0; j < half; ++j) {
+            double a = (double)pos * std::pow((double)desc->rope_theta, -2.0 * j / (double)T.d);
+            tab[(size_t)pos * half + j] = make_float2((float)std::cos(a), (float)std::sin(a));
+        }
+    if (up(rope, tab.data(), tab.size() * sizeof(float2)) != hipSuccess) {
+        mk_destroy(h);
+        return MK_E_HIP;
+    }
+    Params* dp;
+    ALLOC2(dp, sizeof(Params));
+    h->dparams = dp;
+    if (up(dp, &p, sizeof(Params)) != hipSuccess) {
+        mk_destroy(h);
+        return MK_E_HIP;
+    }
+    st = rearm(h);
+    if (st != MK_OK) {
+        mk_destroy(h);
+        return st;
+    }
+    *out = h;
+    return MK_OK;
+#undef ALLOC2
+#undef ALLOC
+}
+
+size_t mk_kv_cache_bytes(const mk_handle* h) {
+    if (!h) return 0;
+    const Tiling& T = h->g.T;
+    return (size_t)2 * T.L * T.B * T.nkv * (size_t)T.C * T.d * 2;
+}
+
+mk_status mk_decode_step(mk_handle* h, const int32_t* tokens, const int32_t* positions, void* kv_cache, float* logits,
+                         void* stream) {
+    if (!h || !tokens || !positions || (!kv_cache && h->g.T.L > 0)) return MK_E_INVALID;
+    const Tiling& T = h->g.T;
+    StepArgs a;
+    a.tokens = tokens;
+    a.positions = positions;
+    a.kc = (uint16_t*)kv_cache;
+    a.vc = (uint16_t*)kv_cache + (size_t)T.L * T.B * T.nkv * (size_t)T.C * T.d;
+    a.logits = logits;
+    hipError_t e = launch_step(h->dparams, a, (uint32_t)h->W, (hipStream_t)stream, h->cooperative);
+    if (e == hipErrorCooperativeLaunchTooLarge) return MK_E_NOT_RESIDENT;
+    return e == hipSuccess ? MK_OK : MK_E_HIP;
+}
+
+const int32_t* mk_next_tokens(const mk_handle* h) { return h ? h->p.next : nullptr; }
+const float* mk_hidden_out(const mk_handle* h) { return h ? h->p.hidden : nullptr; }
+const int32_t* mk_expert_ids(const mk_handle* h) {
+    (void)h;
+    return nullptr;
+}
+
+mk_status mk_check_device_error(mk_handle* h, char* msg, size_t cap) {
+    if (!h) return MK_E_INVALID;
+    HIPCHK(hipDeviceSynchronize());
+    uint32_t rec[8];
+    HIPCHK(hipMemcpy(rec, h->p.state + ST_ERR, sizeof(rec), hipMemcpyDeviceToHost));
+    if (rec[0] == ERR_NONE) return MK_OK;
+    if (msg && cap) {
+        const char* what = rec[0] == ERR_TIMEOUT_EVENT ? "timeout waiting for an event counter"
+                           : rec[0] == ERR_TIMEOUT_LDS ? "timeout waiting inside a workgroup"
+                           : rec[0] == ERR_INPUT     ? "token or position out of range"
+                                                     : "unknown device error";
+        snprintf(msg, cap, "%s (workgroup %u, task %u, event %u, seen %u, target %u)", what, rec[1], rec[2], rec[3],
+                 rec[4], rec[5]);
+    }
+    mk_status st = rearm(h);
+    return st == MK_OK ? MK_E_DEVICE : st;
+}
+
+mk_status mk_export_graph(const mk_handle* h, void* buf, size_t cap, size_t* need) {
+    if (!h) return MK_E_INVALID;
+    size_t n = export_size(h->g);
+    if (need) *need = n;
+    if (!buf || cap < n) return MK_E_INVALID;
+    export_graph(h->g, buf, cap);
+    return MK_OK;
+}
+
+mk_status mk_read_counters(mk_handle* h, uint32_t* host, size_t n, uint32_t* epoch) {
+    if (!h || (!host && n)) return MK_E_INVALID;
+    HIPCHK(hipDeviceSynchronize());
+    std::vector<uint32_t> raw(h->n_events * 8 * 32);
+    HIPCHK(hipMemcpy(raw.data(), h->p.ctr, raw.size() * 4, hipMemcpyDeviceToHost));
+    for (size_t e = 0; e < n && e < h->n_events; ++e) {
+        uint32_t s = 0;
+        for (int k = 0; k < 8; ++k) s += raw[(e * 8 + k) * 32];
+        host[e] = s;
+    }
+    if (epoch) {
+        uint32_t ep;
+        HIPCHK(hipMemcpy(&ep, h->p.state + ST_EPOCH, 4, hipMemcpyDeviceToHost));
+        *epoch = ep - 1;  // steps completed since the last re-arm
+    }
+    return MK_OK;
+}
+
+mk_status mk_read_task_counts(mk_handle* h, uint32_t* host, size_t n) {
+    if (!h || !host) return MK_E_INVALID;
+    if (!h->p.task_count) return MK_E_UNSUPPORTED;
+    HIPCHK(hipDeviceSynchronize());
+    size_t m = n < h->g.tasks.size() ? n : h->g.tasks.size();
+    HIPCHK(hipMemcpy(host, h->p.task_count, m * 4, hipMemcpyDeviceToHost));
+    return MK_OK;
+}
+
+mk_status mk_read_trace(mk_handle* h, uint64_t* host, size_t n) {
+    if (!h || !host) return MK_E_INVALID;
+    if (!h->p.trace) return MK_E_UNSUPPORTED;
+    HIPCHK(hipDeviceSynchronize());
+    size_t m = n < h->g.tasks.size() * 4 ? n : h->g.tasks.size() * 4;
+    HIPCHK(hipMemcpy(host, h->p.trace, m * 8, hipMemcpyDeviceToHost));
+    return MK_OK;
+}
+
+void mk_destroy(mk_handle* h) {
+    if (!h) return;
+    (void)hipDeviceSynchronize();
+    for (void* a : h->allocs) (void)hipFree(a);
+    delete h;
+}
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// Kernel parameter block and launch glue shared by the runtime (host) and the
+// megakernel (device).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mk_internal.h"
+
+namespace mk {
+
+// control words in Params::state (uint32 index; each on its own 128-byte line)
+constexpr uint32_t ST_EPOCH = 0;    // step number of the next launch (starts at 1)
+constexpr uint32_t ST_EXIT = 32;    // workgroups that finished (monotonic)
+constexpr uint32_t ST_HEAD = 64;    // dynamic queue head (monotonic)
+constexpr uint32_t ST_ABORT = 96;   // set when any wave gives up
+constexpr uint32_t ST_ERR = 128;    // error record: code, workgroup, task, event, seen, target
+constexpr uint32_t ST_WORDS = 160;
+
+enum ErrCode : uint32_t { ERR_NONE = 0, ERR_TIMEOUT_EVENT = 1, ERR_TIMEOUT_LDS = 2, ERR_INPUT = 3 };
+
+// Per-step pointers, passed by value with every launch.
+struct StepArgs {
+    const int32_t* tokens;    // [B]
+    const int32_t* positions; // [B]
+    uint16_t* kc;             // K cache [L][B][n_kv][C][d]
+    uint16_t* vc;             // V cache
+    float* logits;            // [B][V] or null
+};
+
+// Everything else the kernel reads, resident in device memory for the life of the handle.
+struct Params {
+    const Task* tasks;
+    const uint32_t* queue_off;
+    const uint32_t* queue;
+    uint32_t n_tasks;
+    uint32_t sched;
+    uint32_t* ctr;            // event counters [n_events][8 sub-counters][32 words]
+    uint32_t* state;          // control words
+    const uint8_t* w;         // packed weights
+    const float2* rope;       // [max_ctx][head_dim/2] (cos, sin)
+    float* q;                 // [B][n_q*d]
+    float* part;              // [B][n_kv][S][grp][d+2]
+    float* m;                 // [B][f]
+    float* acc;               // [2][2L+1][B][h] residual accumulators (by step parity)
+    float* hidden;            // [B][h]
+    unsigned long long* key;  // [2][B] packed argmax keys
+    uint32_t* ticket;         // [B]
+    int32_t* next;            // [B]
+    uint32_t* task_count;     // [n_tasks] or null
+    unsigned long long* trace;  // [n_tasks][4] or null
+    Tiling T;
+    Layout lay;
+    float eps;
+    uint32_t drop_task;
+    unsigned long long timeout;  // ticks of the 100 MHz device clock
+};
+
+hipError_t launch_step(const Params* dparams, const StepArgs& a, uint32_t grid, hipStream_t stream, bool cooperative);
+int step_threads();
+size_t step_lds_bytes();
+const void* step_kernel_ptr();
+
+}  // namespace mk
