@@ -1,0 +1,173 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the MI355X persistent megakernel.
+
+Workload: Llama-3.2-1B-shaped decoder (16 layers, hidden 2048, 32 Q / 8 KV
+heads of 64, SwiGLU 8192, vocab 128256, tied LM head, RoPE theta 5e5), bf16
+synthetic weights ~N(0, 0.02), bf16 KV cache prefilled with N(0, 1) to
+context 1024, batch 1; K greedy decode steps at positions 1024, 1025, ...
+with the next token chained on the device.  One step = one kernel launch.
+
+Prints one JSON line: steps/s (value), ms and us per step, the roofline of the
+megakernel (algorithmic bytes = weights + KV read per step, against the 8 TB/s
+HBM peak), the one-kernel-per-op HIP baseline on the same inputs, and the
+oracle's CPU time on a bounded sample.
+
+  python bench.py [--gpus 1] [--steps 256] [--warmup 10] [--sched static|dynamic]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode µs/step (steps/s) at batch 1, Llama-1B shape; achieved HBM GB/s vs peak"
+HBM_PEAK_GBS = 8000.0
+
+
+def step_bytes(cfg, positions):
+    """Algorithmic bytes of one decode step: every weight once + K and V rows 0..P of every layer."""
+    kv = 4 * cfg.n_layers * cfg.n_kv * cfg.head_dim * (np.asarray(positions, np.int64) + 1)
+    return cfg.weight_bytes() + int(kv.sum())
+
+
+def cpu_baseline(cfg, w, kc, vc, tok, P0, budget_s=10.0):
+    """The oracle (plain C, double precision, OpenMP over output rows) on the same inputs."""
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    k2, v2 = kc.copy(), vc.copy()
+    t = np.array(tok, np.int32)
+    first = None
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        r = oracle.decode_step(cfg, w, t, [P0 + n], k2, v2)
+        if first is None:
+            first = r
+        t = r["next"].copy()
+        n += 1
+        if time.perf_counter() - t0 > budget_s and n >= 2:
+            break
+    dt = time.perf_counter() - t0
+    return dict(value=n / dt, unit="steps/s", cores=threads, kind="oracle",
+                sample=f"{n} greedy decode steps of the same workload from position {P0} ({dt:.1f} s)"), first
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--sched", choices=["static", "dynamic"], default="static")
+    ap.add_argument("--policy", choices=["rr", "lpt"], default="rr")
+    ap.add_argument("--attn-splits", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-baseline", action="store_true", help="skip the one-kernel-per-op baseline")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; multi-GPU runs are not part of this "
+                                   "build (see DESIGN.md for how the path would shard)", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import synth
+    import persistent_megakernel_decode_cu_amd as mk
+
+    cfg = synth.configs.LLAMA_1B
+    P0, C, K, W = 1024, 2048, args.steps, args.warmup
+    if P0 + max(K, W) > C:
+        raise SystemExit("steps exceed the KV cache")
+    t_gen = time.perf_counter()
+    w = synth.make_weights(cfg)
+    kc, vc = synth.make_kv(cfg, 1, C)
+    tok = synth.make_tokens(cfg, 1)
+    t_gen = time.perf_counter() - t_gen
+
+    dev = {k: torch.from_numpy(v.view(np.int16)).cuda() for k, v in w.items()}
+    model = mk.Model(cfg, dev)
+    opt = mk.options(sched=0 if args.sched == "static" else 1, policy=0 if args.policy == "rr" else 1,
+                     attn_splits=args.attn_splits)
+    h = mk.mk_build_graph(model.desc, 1, C, opt)
+    graph = mk.parse_export(mk.mk_export_graph(h))
+    kv = torch.from_numpy(np.concatenate([kc.reshape(-1), vc.reshape(-1)]).view(np.int16)).cuda()
+    logits = torch.empty(cfg.vocab, dtype=torch.float32, device="cuda")
+    positions = torch.arange(P0, P0 + max(K, W), dtype=torch.int32, device="cuda")
+    tok0 = torch.tensor(tok, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    nxt = mk.mk_next_tokens(h)
+
+    def run(n):
+        for s in range(n):
+            tptr = tok0.data_ptr() if s == 0 else nxt
+            mk.mk_decode_step(h, tptr, positions[s:s + 1].data_ptr(), kv.data_ptr(), logits.data_ptr(), sp)
+
+    # first step alone: parity sanity check against the oracle below
+    run(1)
+    torch.cuda.synchronize()
+    err = mk.mk_check_device_error(h)
+    if err:
+        raise SystemExit(f"device error: {err}")
+    first_logits = logits.cpu().numpy().copy()
+    # warmup (the KV slots it writes are rewritten by the timed steps)
+    run(W)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    run(K)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = e0.elapsed_time(e1)
+    err = mk.mk_check_device_error(h)
+    if err:
+        raise SystemExit(f"device error: {err}")
+    ms = ms_total / K
+    pos_list = list(range(P0, P0 + K))
+    bytes_mean = np.mean([step_bytes(cfg, [p]) for p in pos_list])
+    achieved = bytes_mean / (ms * 1e-3) / 1e9
+
+    out = {
+        "metric": METRIC,
+        "value": round(1000.0 / ms, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms, 5),
+        "us_per_step": round(ms * 1000.0, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name} greedy decode, batch 1, positions {P0}..{P0 + K - 1}, bf16 weights "
+                               f"and KV cache, one kernel launch per step",
+                   "batch": 1, "first_position": P0, "max_ctx": C, "sched": args.sched, "policy": args.policy,
+                   "workgroups": int(graph["header"]["W"]), "tasks_per_step": int(graph["header"]["n_tasks"]),
+                   "attn_splits": int(graph["header"]["attn_splits"])},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_step": int(bytes_mean)},
+    }
+    mk.mk_destroy(h)
+    del dev, model
+
+    if not args.no_cpu_baseline:
+        cb, first = cpu_baseline(cfg, w, kc, vc, tok, P0)
+        out["cpu_baseline"] = cb
+        out["parity_first_step"] = {
+            "max_abs_dlogit": float(np.abs(first_logits.astype(np.float64) - first["logits"][0]).max()),
+            "argmax_equal": bool(int(np.argmax(first_logits)) == int(first["next"][0]))}
+    out["input_generation_s"] = round(t_gen, 1)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -193,8 +193,11 @@ def mk_read_task_counts(h, n_tasks):
     return out
 
 
+TRACE_WORDS = 8
+
+
 def mk_read_trace(h, n_tasks):
-    out = np.zeros((n_tasks, 4), dtype=np.uint64)
+    out = np.zeros((n_tasks, TRACE_WORDS), dtype=np.uint64)
     _check(load().mk_read_trace(h, out.ctypes.data, out.size), "mk_read_trace")
     return out
 

@@ -36,13 +36,16 @@
 namespace mk {
 
 constexpr int NCW = 4;                 // compute waves
-constexpr int NTHREADS = (NCW + 1) * 64;
+constexpr int NLW = 2;                 // loader waves; each issues every NLW-th 1 KiB load of every page
+constexpr int NTHREADS = (NCW + NLW) * 64;
 constexpr int PAGE = 16384;            // LDS page (bytes)
 constexpr int NPAGES = 8;              // ring of 8 pages = 128 KiB
 constexpr int FIFO = 16;               // task records in flight in LDS
 constexpr int XS = MAX_ACT;            // activation staging (floats)
 constexpr int ROWRES = MAX_TILE_ROWS;  // per-task row results (floats)
-constexpr int MAX_INFLIGHT = 3;        // pages in flight (3 * 16 loads < 64 = vmcnt range)
+constexpr int LPP = 16 / NLW;          // loads per page per loader wave
+constexpr int MAX_INFLIGHT = 6;        // pages in flight per loader wave (6 * 8 loads < 64 = vmcnt range)
+constexpr int DYNQ = 64;               // popped task ids shared between the loader waves (dynamic queue)
 constexpr int MAXB = 64;               // sequences per step held in LDS
 
 struct __attribute__((aligned(16))) Smem {
@@ -56,9 +59,13 @@ struct __attribute__((aligned(16))) Smem {
     uint32_t fifo_first_page[FIFO];
     uint32_t fifo_ready[FIFO];
     uint32_t fifo_free[FIFO];
-    uint32_t page_ready[NPAGES];
-    uint32_t page_free[NPAGES];
+    uint32_t page_ready[NLW][NPAGES];  // per loader wave: uses of the slot it has published
+    uint32_t page_free[NPAGES];   // compute-wave releases (NCW per use of the slot)
+    uint32_t dyn_tid[DYNQ];
+    uint32_t dyn_ready, dyn_ack;
     uint32_t go, cbar, done, abort;
+    uint32_t t_ready_lo, t_ready_hi;
+    uint32_t tm[4];  // trace: low 32 bits of the clock after staging / after the GEMV
 };
 
 __shared__ Smem S;
@@ -139,20 +146,37 @@ __device__ __forceinline__ float dot8(uint4 w, const float* x, float a) {
     return a;
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+// Sum over each row of 16 lanes with DPP (every lane of the row gets the row sum).
+__device__ __forceinline__ float row16_sum(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true));  // quad_perm [1,0,3,2]
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, true));  // quad_perm [2,3,0,1]
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, true)); // row_ror:4
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, true)); // row_ror:8
     return v;
+}
+// Sum over the wave, returned wave-uniform.
+__device__ __forceinline__ float wave_sum(float v) {
+    v = row16_sum(v);
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)) +
+           __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16)) +
+           __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32)) +
+           __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
 }
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
     return v;
 }
+// Sum over aligned segments of W lanes (W = 8, 16, 32); every lane gets its segment's sum.
 template <int W>
 __device__ __forceinline__ float seg_sum(float v) {
+    if constexpr (W >= 16) {
+        v = row16_sum(v);
+        if constexpr (W == 32) v += __shfl_xor(v, 16, 64);
+    } else {
 #pragma unroll
-    for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+        for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    }
     return v;
 }
 
@@ -178,7 +202,7 @@ __device__ __noinline__ void raise_error(const Params* pp, uint32_t code, uint32
 }
 
 // Spin until an LDS word reaches v.  Returns false on abort or timeout.
-__device__ __noinline__ bool lds_wait_ge(const uint32_t& w, uint32_t v, const Params* pp, uint32_t task) {
+__device__ __noinline__ bool lds_wait_slow(const uint32_t& w, uint32_t v, const Params* pp, uint32_t task) {
     uint64_t t0 = 0;
     uint32_t it = 0;
     while (lds_ld(w) < v) {
@@ -200,6 +224,11 @@ __device__ __noinline__ bool lds_wait_ge(const uint32_t& w, uint32_t v, const Pa
         __builtin_amdgcn_s_sleep(1);
     }
     return true;
+}
+
+__device__ __forceinline__ bool lds_wait_ge(const uint32_t& w, uint32_t v, const Params* pp, uint32_t task) {
+    if (lds_ld(w) >= v) return true;
+    return uni(lds_wait_slow(w, v, pp, task)) != 0;
 }
 
 // Compute wave 0: wait until the event's sub-counters sum to `want`.
@@ -268,7 +297,7 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_off) {
                                      0);
 }
 
-__device__ __forceinline__ void issue_page(CParams& p, const Task& k, uint32_t kp, uint32_t slot, int lane) {
+__device__ __forceinline__ void issue_page(CParams& p, const Task& k, uint32_t kp, uint32_t slot, int lane, int lw) {
     const uint32_t dst = slot * PAGE;
     if (k.op == OP_ATTN) {
         const int32_t d = p.T.d;
@@ -281,20 +310,18 @@ __device__ __forceinline__ void issue_page(CParams& p, const Task& k, uint32_t k
         const uint8_t* kb = (const uint8_t*)S.args.kc + row * d * 2;
         const uint8_t* vb = (const uint8_t*)S.args.vc + row * d * 2;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const uint32_t off = min((uint32_t)(j * 1024 + lane * 16), valid - 16u);
-            dma16(kb + off, dst + j * 1024);
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const uint32_t off = min((uint32_t)(j * 1024 + lane * 16), valid - 16u);
-            dma16(vb + off, dst + 8192 + j * 1024);
+        for (int i = 0; i < LPP; ++i) {
+            const int j = i * NLW + lw;  // 1 KiB load j of the page: K rows for j < 8, V rows after
+            const uint8_t* src = j < 8 ? kb : vb;
+            const uint32_t off = min((uint32_t)((j & 7) * 1024 + lane * 16), valid - 16u);
+            dma16(src + off, dst + j * 1024);
         }
     } else {
         const uint8_t* base = p.w + k.wofs + (uint64_t)kp * PAGE;
         const uint32_t valid = min((uint32_t)PAGE, k.wbytes - kp * PAGE);
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
+        for (int i = 0; i < LPP; ++i) {
+            const int j = i * NLW + lw;
             const uint32_t off = min((uint32_t)(j * 1024 + lane * 16), valid - 16u);
             dma16(base + off, dst + j * 1024);
         }
@@ -304,8 +331,15 @@ __device__ __forceinline__ void issue_page(CParams& p, const Task& k, uint32_t k
 typedef const __attribute__((address_space(4))) uint32_t c_u32;
 typedef const __attribute__((address_space(4))) Task c_task;
 
-__device__ __noinline__ void loader(const Params* pp, uint32_t epoch) {
+// Loader wave lw of NLW.  All loader waves walk the same task sequence and the
+// same page sequence; each issues its share of every page and publishes it with
+// an LDS add.  Wave 0 also feeds the compute waves' task FIFO and, for the
+// dynamic queue, pops task ids and hands them to the other loader waves.  Every
+// wait first drains and publishes the loads in flight, so a page a consumer
+// waits for is never held back by a waiting loader.
+__device__ __noinline__ void loader(const Params* pp, uint32_t epoch, int lw) {
     CParams& p = P(pp);
+    lw = (int)uni((uint32_t)lw);
     const int lane = threadIdx.x & 63;
     const uint32_t W = gridDim.x;
     c_u32* qoff = (c_u32*)p.queue_off;
@@ -322,7 +356,7 @@ __device__ __noinline__ void loader(const Params* pp, uint32_t epoch) {
     uint32_t pseq = 0, pub = 0;  // next page to issue / to publish
 
     auto publish_one = [&]() {
-        if (lane == 0) lds_st(S.page_ready[pub % NPAGES], pub + 1);
+        if (lane == 0) lds_st(S.page_ready[lw][pub % NPAGES], pub / NPAGES + 1);
         ++pub;
     };
     auto drain = [&]() {
@@ -336,22 +370,34 @@ __device__ __noinline__ void loader(const Params* pp, uint32_t epoch) {
         if (sched == 0) {
             end = qbeg + t >= qend;
             ti = end ? 0u : queue[qbeg + t];
-        } else {
+        } else if (lw == 0) {
             drain();
             uint32_t old = 0;
             if (lane == 0) old = addu_dev(&p.state[ST_HEAD], 1u);
             old = uni(old);
             const uint32_t rel = old - (epoch - 1u) * (n_tasks + W);
             end = rel >= n_tasks;
-            ti = end ? 0u : rel;
+            ti = end ? NONE : rel;
+            if (NLW > 1) {
+                if (lds_ld(S.dyn_ack) + DYNQ < t + 1 && !uni(lds_wait_ge(S.dyn_ack, t + 1 - DYNQ, pp, ti))) break;
+                if (lane == 0) lds_st(S.dyn_tid[t % DYNQ], ti);
+                lgkm_wait_all();
+                if (lane == 0) lds_st(S.dyn_ready, t + 1);
+            }
+            if (end) ti = 0u;
+        } else {
+            if (lds_ld(S.dyn_ready) < t + 1) {
+                drain();
+                if (!uni(lds_wait_ge(S.dyn_ready, t + 1, pp, NONE))) break;
+            }
+            ti = uni(lds_ld(S.dyn_tid[t % DYNQ]));
+            lgkm_wait_all();
+            if (lane == 0 && lw == 1) lds_st(S.dyn_ack, t + 1);
+            end = ti == NONE;
+            if (end) ti = 0u;
         }
-        const uint32_t slot = t % FIFO;
-        if (lds_ld(S.fifo_free[slot]) < t / FIFO) {
-            drain();
-            if (!uni(lds_wait_ge(S.fifo_free[slot], t / FIFO, pp, ti))) break;
-        }
-        Task k;
         ti = uni(ti);
+        Task k;
         if (!end) {
             c_u32* src = (c_u32*)&tasks[ti];
 #pragma unroll
@@ -360,13 +406,20 @@ __device__ __noinline__ void loader(const Params* pp, uint32_t epoch) {
             k = Task();
             k.op = OP_END;
         }
-        if (lane == 0) {
+        if (lw == 0) {
+            const uint32_t slot = t % FIFO;
+            if (lds_ld(S.fifo_free[slot]) < t / FIFO) {
+                drain();
+                if (!uni(lds_wait_ge(S.fifo_free[slot], t / FIFO, pp, ti))) break;
+            }
+            if (lane == 0) {
 #pragma unroll
-            for (int i = 0; i < 12; ++i) lds_st(((uint32_t*)&S.fifo[slot])[i], ((const uint32_t*)&k)[i]);
-            lds_st(S.fifo_first_page[slot], pseq);
+                for (int i = 0; i < 12; ++i) lds_st(((uint32_t*)&S.fifo[slot])[i], ((const uint32_t*)&k)[i]);
+                lds_st(S.fifo_first_page[slot], pseq);
+            }
+            lgkm_wait_all();
+            if (lane == 0) lds_st(S.fifo_ready[slot], t + 1);
         }
-        lgkm_wait_all();
-        if (lane == 0) lds_st(S.fifo_ready[slot], t + 1);
         if (end) break;
         const uint32_t np = task_pages(k, splits, hd);
         for (uint32_t kp = 0; kp < np; ++kp) {
@@ -376,10 +429,10 @@ __device__ __noinline__ void loader(const Params* pp, uint32_t epoch) {
                 drain();
                 if (!uni(lds_wait_ge(S.page_free[ps], need, pp, ti))) goto out;
             }
-            issue_page(p, k, kp, ps, lane);
+            issue_page(p, k, kp, ps, lane, lw);
             ++pseq;
             if (pseq - pub == MAX_INFLIGHT) {
-                vm_wait<16 * (MAX_INFLIGHT - 1)>();
+                vm_wait<LPP * (MAX_INFLIGHT - 1)>();
                 publish_one();
             }
         }
@@ -390,116 +443,203 @@ out:
 
 // ---- compute-wave primitives -------------------------------------------------------
 
-__device__ __forceinline__ bool cbarrier(const Params* pp, uint32_t& cgen, int lane, uint32_t task) {
-    cgen += NCW;
+constexpr uint32_t RSRC_FLAGS = 0x00020000;  // raw buffer, 32-bit data format
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+
+struct Ctx {
+    int wave, lane, tid;  // compute wave, lane, thread index among the compute lanes
+    uint32_t t;           // task sequence number of this workgroup
+    uint32_t epoch, parity;
+    uint32_t* cgen;       // compute-wave barrier generation
+};
+
+__device__ __forceinline__ bool cbarrier(const Params* pp, Ctx& c, uint32_t task) {
+    *c.cgen += NCW;
     lgkm_wait_all();
-    if (lane == 0) lds_add(S.cbar, 1u);
-    return lds_wait_ge(S.cbar, cgen, pp, task);
+    if (c.lane == 0) lds_add(S.cbar, 1u);
+    return lds_wait_ge(S.cbar, *c.cgen, pp, task);
 }
 
 __device__ __forceinline__ bool page_acquire(const Params* pp, uint32_t seq, uint32_t task) {
-    return lds_wait_ge(S.page_ready[seq % NPAGES], seq + 1, pp, task);
+#pragma unroll
+    for (int lw = 0; lw < NLW; ++lw)
+        if (!lds_wait_ge(S.page_ready[lw][seq % NPAGES], seq / NPAGES + 1, pp, task)) return false;
+    return true;
 }
 __device__ __forceinline__ void page_release(uint32_t seq, int lane) {
     lgkm_wait_all();
     if (lane == 0) lds_add(S.page_free[seq % NPAGES], 1u);
 }
+__device__ __forceinline__ void page_skip(uint32_t seq, int lane) {
+    if (lane == 0) lds_add(S.page_free[seq % NPAGES], 1u);
+}
 
-// This lane's slice of the staged activation vector (LDS xs[xo + column]) times
-// scale and the bf16 gains g (null: 1), in the order the GEMV consumes it.
-template <int KT>
-__device__ __forceinline__ void load_x(int xo, int lane, float scale, const uint16_t* g, float* x) {
-    if constexpr (KT >= 512) {
+__device__ __forceinline__ void tmark(const Ctx& c, int i) {
+    if (c.wave == 0 && c.lane == 0) lds_st(S.tm[i], (uint32_t)rtc());
+}
+
+// One poll of an event: do its sub-counters sum to `want`?
+__device__ __forceinline__ bool event_ready(CParams& p, uint32_t ev, uint32_t nsub, uint32_t want, int lane) {
+    uint32_t v = (uint32_t)lane < nsub ? ld_dev(&p.ctr[ctr_index(ev, lane)]) : 0u;
+    v += __shfl_xor(v, 1, 64);
+    v += __shfl_xor(v, 2, 64);
+    v += __shfl_xor(v, 4, 64);
+    return uni(v) >= want;
+}
+
+// Compute wave 0 waits for the task's event and releases the other compute waves.
+__device__ __forceinline__ bool await_inputs(const Params* pp, const Task& k, Ctx& c) {
+    if (c.wave == 0) {
+        if (k.wait_ev != NONE) {
+            CParams& p = P(pp);
+            const uint32_t want = c.epoch * k.wait_target;
+            if (!event_ready(p, k.wait_ev, k.wait_nsub, want, c.lane) &&
+                !uni(wait_event(pp, k.wait_ev, k.wait_nsub, want, k.id)))
+                return false;
+        }
+        const uint64_t tr = rtc();
+        if (c.lane == 0) {
+            lds_st(S.t_ready_lo, (uint32_t)tr);
+            lds_st(S.t_ready_hi, (uint32_t)(tr >> 32));
+            lds_st(S.go, c.t + 1);
+        }
+        return true;
+    }
+    return lds_wait_ge(S.go, c.t + 1, pp, k.id);
+}
+
+// n floats (n a multiple of 4) from src, read with device-scope 16-byte loads spread
+// over the compute lanes (all issued before any is used), into LDS xs[dst + i].
+template <int MAXQ>
+__device__ __forceinline__ void stage_f32(int dst, const float* src, int n, int tid) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, n * 4, RSRC_FLAGS);
+    u32x4 v[MAXQ];
 #pragma unroll
-        for (int j = 0; j < KT / 512; ++j)
+    for (int q = 0; q < MAXQ; ++q) v[q] = __builtin_amdgcn_raw_buffer_load_b128(r, (tid + q * NCW * 64) * 16, 0, 16);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int c = j * 512 + lane * 8 + i;
-                x[j * 8 + i] = S.xs[xo + c] * scale * (g ? bf16f(g[c]) : 1.0f);
-            }
-    } else {
-        constexpr int LPROW = KT / 8;
+    for (int q = 0; q < MAXQ; ++q) {
+        const int i = (tid + q * NCW * 64) * 4;
+        if (i < n) *(u32x4*)&S.xs[dst + i] = v[q];
+    }
+}
+// n bf16 values (n a multiple of 8) from src (ordinary loads) into LDS xs[dst + i] as floats
+__device__ __forceinline__ void stage_bf16(int dst, const uint16_t* src, int n, int tid) {
+    uint4 v[2];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int c = (lane % LPROW) * 8 + i;
-            x[i] = S.xs[xo + c] * scale * (g ? bf16f(g[c]) : 1.0f);
+    for (int q = 0; q < 2; ++q) {
+        const int i = (tid + q * NCW * 64) * 8;
+        v[q] = i < n ? *(const uint4*)(src + i) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int i = (tid + q * NCW * 64) * 8;
+        if (i < n) {
+            *(float4*)&S.xs[dst + i] = make_float4(bf16lo(v[q].x), bf16hi(v[q].x), bf16lo(v[q].y), bf16hi(v[q].y));
+            *(float4*)&S.xs[dst + i + 4] = make_float4(bf16lo(v[q].z), bf16hi(v[q].z), bf16lo(v[q].w), bf16hi(v[q].w));
         }
     }
+}
+
+// This lane's slice of xs[xo + column] in GEMV order, times `scale` and the bf16
+// gains gw (already loaded: KT/512 words of 8 gains; null = no gains).
+template <int KT>
+__device__ __forceinline__ void load_x(int xo, int lane, float scale, const uint4* gw, float* x) {
+    if constexpr (KT >= 512) {
+#pragma unroll
+        for (int j = 0; j < KT / 512; ++j) {
+            const float4 a = *(const float4*)&S.xs[xo + j * 512 + lane * 8];
+            const float4 b = *(const float4*)&S.xs[xo + j * 512 + lane * 8 + 4];
+            float g[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
+            if (gw) {
+                g[0] = bf16lo(gw[j].x); g[1] = bf16hi(gw[j].x); g[2] = bf16lo(gw[j].y); g[3] = bf16hi(gw[j].y);
+                g[4] = bf16lo(gw[j].z); g[5] = bf16hi(gw[j].z); g[6] = bf16lo(gw[j].w); g[7] = bf16hi(gw[j].w);
+            }
+            x[j * 8 + 0] = a.x * scale * g[0]; x[j * 8 + 1] = a.y * scale * g[1];
+            x[j * 8 + 2] = a.z * scale * g[2]; x[j * 8 + 3] = a.w * scale * g[3];
+            x[j * 8 + 4] = b.x * scale * g[4]; x[j * 8 + 5] = b.y * scale * g[5];
+            x[j * 8 + 6] = b.z * scale * g[6]; x[j * 8 + 7] = b.w * scale * g[7];
+        }
+    } else {
+        constexpr int LPROW = KT / 8;
+        const float4 a = *(const float4*)&S.xs[xo + (lane % LPROW) * 8];
+        const float4 b = *(const float4*)&S.xs[xo + (lane % LPROW) * 8 + 4];
+        x[0] = a.x * scale; x[1] = a.y * scale; x[2] = a.z * scale; x[3] = a.w * scale;
+        x[4] = b.x * scale; x[5] = b.y * scale; x[6] = b.z * scale; x[7] = b.w * scale;
+    }
+}
+// gains of this lane's GEMV columns (KT >= 512 only)
+template <int KT>
+__device__ __forceinline__ void load_gains(const uint16_t* g, int lane, uint4* gw) {
+#pragma unroll
+    for (int j = 0; j < KT / 512; ++j) gw[j] = *(const uint4*)(g + j * 512 + lane * 8);
+}
+
+// 1/sqrt(mean(xs[0..n)^2) + eps), computed by each wave from LDS
+__device__ __forceinline__ float rms_scale(int n, float eps, int lane) {
+    float ss = 0.f;
+    for (int i = lane * 4; i < n; i += 256) {
+        const float4 a = *(const float4*)&S.xs[i];
+        ss += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w;
+    }
+    return 1.0f / sqrtf(wave_sum(ss) / (float)n + eps);
 }
 
 // y[r] = W[r, :] . x over the task's rows; weights in consecutive LDS pages from
-// page sequence `page0`; results in S.rowres[r].  Every compute wave releases
-// every page of the task exactly once.
+// page sequence `page0`; results in S.rowres[r].  Wave w computes the pages
+// pg = w (mod NCW) and releases the others untouched: every compute wave
+// releases every page of the task exactly once.
 template <int KT>
-__device__ __noinline__ bool gemv_tile(const Params* pp, int wave, uint32_t page0, uint32_t nrows, uint32_t wbytes,
-                                       int xo, float scale, const uint16_t* g, uint32_t task) {
-    const int lane = threadIdx.x & 63;
-    float x[KT >= 512 ? KT / 64 : 8];
-    load_x<KT>(xo, lane, scale, g, x);
+__device__ __forceinline__ bool gemv_pages(const Params* pp, int wave, int lane, uint32_t page0, uint32_t nrows,
+                                           uint32_t wbytes, const float* x, uint32_t task) {
     const uint32_t npages = (wbytes + PAGE - 1) / PAGE;
-    if constexpr (KT >= 512) {
-        constexpr int RB = 2 * KT;      // bytes per row
-        constexpr int RPP = PAGE / RB;  // rows per page (>= 1)
-        constexpr int LPR = KT / 512;   // 1 KiB wave loads per row
-        for (uint32_t pg = 0; pg < npages; ++pg) {
-            if (!page_acquire(pp, page0 + pg, task)) return false;
-            const uint32_t slot = (page0 + pg) % NPAGES;
+    for (uint32_t pg = 0; pg < npages; ++pg) {
+        if ((int)(pg % NCW) != wave) {
+            page_skip(page0 + pg, lane);
+            continue;
+        }
+        if (!page_acquire(pp, page0 + pg, task)) return false;
+        const uint32_t slot = (page0 + pg) % NPAGES;
+        if constexpr (KT >= 512) {
+            constexpr int RB = 2 * KT;      // bytes per row
+            constexpr int RPP = PAGE / RB;  // rows per page
+            constexpr int LPR = KT / 512;   // 1 KiB wave loads per row
             const uint32_t r_lo = pg * RPP;
-            const uint32_t r_hi = min(nrows, r_lo + RPP);
-            uint32_t r = r_lo + ((uint32_t)(wave - (int)(r_lo % NCW)) + NCW) % NCW;
-            for (; r < r_hi; r += NCW) {
-                const uint32_t off = (r - r_lo) * RB + lane * 16;
+            // the whole page goes to registers first, so the page is handed back to
+            // the loader before the arithmetic
+            uint4 wv[RPP * LPR];
+#pragma unroll
+            for (int i = 0; i < RPP * LPR; ++i) wv[i] = *(const uint4*)&ring[slot][i * 1024 + lane * 16];
+            page_release(page0 + pg, lane);
+            float acc[RPP];
+#pragma unroll
+            for (int rr = 0; rr < RPP; ++rr) {
                 float a = 0.f;
 #pragma unroll
-                for (int j = 0; j < LPR; ++j) {
-                    const uint4 w = *(const uint4*)&ring[slot][off + j * 1024];
-                    a = dot8(w, x + j * 8, a);
-                }
-                a = wave_sum(a);
-                if (lane == 0) S.rowres[r] = a;
+                for (int j = 0; j < LPR; ++j) a = dot8(wv[rr * LPR + j], x + j * 8, a);
+                acc[rr] = a;
             }
-            page_release(page0 + pg, lane);
-        }
-    } else {
-        constexpr int RB = 2 * KT;
-        constexpr int RPL = 1024 / RB;   // rows per 1 KiB load
-        constexpr int LPROW = 64 / RPL;  // lanes per row
-        for (uint32_t pg = 0; pg < npages; ++pg) {
-            if (!page_acquire(pp, page0 + pg, task)) return false;
-            const uint32_t slot = (page0 + pg) % NPAGES;
 #pragma unroll
-            for (int uu = 0; uu < 16 / NCW; ++uu) {
-                const uint32_t u = (uint32_t)(uu * NCW + wave);  // 1 KiB unit within the page
+            for (int rr = 0; rr < RPP; ++rr) {
+                const float a = wave_sum(acc[rr]);
+                if (lane == 0 && r_lo + rr < nrows) S.rowres[r_lo + rr] = a;
+            }
+        } else {
+            constexpr int RB = 2 * KT;
+            constexpr int RPL = 1024 / RB;   // rows per 1 KiB load
+            constexpr int LPROW = 64 / RPL;  // lanes per row
+            uint4 wv[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) wv[u] = *(const uint4*)&ring[slot][u * 1024 + lane * 16];
+            page_release(page0 + pg, lane);
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const float a = seg_sum<LPROW>(dot8(wv[u], x, 0.f));
                 const uint32_t r = (pg * 16 + u) * RPL + lane / LPROW;
-                const uint4 w = *(const uint4*)&ring[slot][u * 1024 + lane * 16];
-                const float a = seg_sum<LPROW>(dot8(w, x, 0.f));
                 if ((lane % LPROW) == 0 && r < nrows) S.rowres[r] = a;
             }
-            page_release(page0 + pg, lane);
         }
     }
     return true;
-}
-
-__device__ bool gemv(int kt, const Params* pp, int wave, uint32_t page0, uint32_t nrows, uint32_t wbytes, int xo,
-                     float scale, const uint16_t* g, uint32_t task) {
-    switch (kt) {
-        case 64: return gemv_tile<64>(pp, wave, page0, nrows, wbytes, xo, scale, g, task);
-        case 128: return gemv_tile<128>(pp, wave, page0, nrows, wbytes, xo, scale, g, task);
-        case 256: return gemv_tile<256>(pp, wave, page0, nrows, wbytes, xo, scale, g, task);
-        case 512: return gemv_tile<512>(pp, wave, page0, nrows, wbytes, xo, scale, g, task);
-        case 1024: return gemv_tile<1024>(pp, wave, page0, nrows, wbytes, xo, scale, g, task);
-        case 2048: return gemv_tile<2048>(pp, wave, page0, nrows, wbytes, xo, scale, g, task);
-        default: return gemv_tile<4096>(pp, wave, page0, nrows, wbytes, xo, scale, g, task);
-    }
-}
-
-// RMS scale 1/sqrt(mean(xs^2) + eps) of xs[0..n), computed by one wave
-__device__ __forceinline__ float rms_scale(int n, float eps, int lane) {
-    float ss = 0.f;
-    for (int i = lane; i < n; i += 64) ss = fmaf(S.xs[i], S.xs[i], ss);
-    ss = wave_sum(ss);
-    return 1.0f / sqrtf(ss / (float)n + eps);
 }
 
 __device__ __forceinline__ float* acc_buf(CParams& p, uint32_t parity, int idx, int b) {
@@ -512,90 +652,57 @@ __device__ __forceinline__ const uint16_t* embed_row(CParams& p, int b) {
     return (const uint16_t*)(p.w + p.lay.embed) + (size_t)S.tok[b] * p.T.h;
 }
 
-// ---- staging (compute wave 0, after the event) -----------------------------------------
-
-__device__ __noinline__ void stage(const Params* pp, const Task& k, uint32_t parity) {
-    CParams& p = P(pp);
-    const int lane = threadIdx.x & 63;
-    const int h = p.T.h;
-    switch (k.op) {
-        case OP_QKV:
-        case OP_LMHEAD: {
-            const int l = k.op == OP_QKV ? (int)k.layer : p.T.L;
-            if (l == 0) {
-                const uint16_t* e = embed_row(p, 0);
-                for (int i = lane; i < h; i += 64) S.xs[i] = bf16f(e[i]);
-            } else {
-                const float* src = acc_buf(p, parity, 2 * l - 1, 0);
-                for (int i = lane; i < h; i += 64) S.xs[i] = ldf_dev(src + i);
-            }
-            break;
-        }
-        case OP_GATEUP: {
-            const float* src = acc_buf(p, parity, 2 * k.layer, 0);
-            for (int i = lane; i < h; i += 64) S.xs[i] = ldf_dev(src + i);
-            break;
-        }
-        case OP_DOWN: {
-            const float* src = p.m + (size_t)k.part * p.T.kd;
-            for (int i = lane; i < p.T.kd; i += 64) S.xs[i] = ldf_dev(src + i);
-            break;
-        }
-        case OP_ATTN: {
-            const float* q = p.q + (size_t)k.seq * p.T.nq * p.T.d + (size_t)k.part * p.T.grp * p.T.d;
-            for (int i = lane; i < p.T.grp * p.T.d; i += 64) S.xs[i] = ldf_dev(q + i);
-            break;
-        }
-        case OP_OPROJ: {
-            // a = sum_c e^(m_c - M) o_c / sum_c e^(m_c - M) l_c over the chunks c of every head of the group
-            const int D = p.T.d, Sp = p.T.attn_splits, G = p.T.grp;
-            const size_t hstride = (size_t)(D + 2), cstride = (size_t)G * (D + 2);
-            for (int hw = 0; hw < G; ++hw) {
-                const float* src = p.part + ((size_t)k.part * Sp * G + hw) * hstride;
-                float Mx = -INFINITY;
-                for (int c = 0; c < Sp; ++c) Mx = fmaxf(Mx, ldf_dev(src + c * cstride));
-                float den = 0.f, num0 = 0.f, num1 = 0.f;
-                for (int c = 0; c < Sp; ++c) {
-                    const float* pc = src + c * cstride;
-                    const float mc = ldf_dev(pc);
-                    const float sc = mc == -INFINITY ? 0.f : __expf(mc - Mx);
-                    den = fmaf(sc, ldf_dev(pc + 1), den);
-                    num0 = fmaf(sc, ldf_dev(pc + 2 + lane), num0);
-                    if (D == 128) num1 = fmaf(sc, ldf_dev(pc + 2 + 64 + lane), num1);
-                }
-                S.xs[hw * D + lane] = num0 / den;
-                if (D == 128) S.xs[hw * D + 64 + lane] = num1 / den;
-            }
-            break;
-        }
-        default: break;
-    }
+// Residual stream entering layer l (l == L: the final one) into xs[0..h)
+template <int H4>
+__device__ __forceinline__ void stage_x(CParams& p, int l, uint32_t parity, int tid) {
+    if (l == 0) stage_bf16(0, embed_row(p, 0), p.T.h, tid);
+    else stage_f32<H4>(0, acc_buf(p, parity, 2 * l - 1, 0), p.T.h, tid);
 }
 
 // ---- ops ---------------------------------------------------------------------------------
 
-__device__ __noinline__ bool op_qkv(const Params* pp, int wave, uint32_t& cgen, const Task& k, uint32_t page0) {
+// RMSNorm + QKV tile + RoPE + K/V append.  Tile rows [0, n) are the first halves
+// (j0 + i) of n RoPE pairs of one head, rows [n, 2n) the second halves (j0 + i + d/2).
+template <int KT>
+__device__ __noinline__ bool op_qkv(const Params* pp, const Task& k, uint32_t page0, Ctx c) {
     CParams& p = P(pp);
-    const int lane = threadIdx.x & 63;
-    const float r = rms_scale(p.T.h, p.eps, lane);
-    if (!gemv(p.T.h, pp, wave, page0, 2 * k.nrows, k.wbytes, 0, r, gains(p, 2 * k.layer), k.id)) return false;
-    if (!cbarrier(pp, cgen, lane, k.id)) return false;
-    // one lane per RoPE pair; rows [0, n) of the tile are first halves, [n, 2n) second halves
-    const int tid = wave * 64 + lane;
-    const uint32_t n = k.nrows;
-    const int half = p.T.d / 2;
-    const uint32_t slot = k.part;
-    const int nq = p.T.nq, nkv = p.T.nkv;
+    const int lane = c.lane, tid = c.tid;
+    const uint32_t n = k.nrows, slot = k.part;
+    const int half = p.T.d / 2, nq = p.T.nq, nkv = p.T.nkv;
     const int32_t P0 = S.pos[0];
+    uint4 gw[KT / 512 > 0 ? KT / 512 : 1];
+    if constexpr (KT >= 512) load_gains<KT>(gains(p, 2 * k.layer), lane, gw);
+    float2 cs = make_float2(1.f, 0.f);
+    if ((uint32_t)tid < n && slot < (uint32_t)(nq + nkv)) cs = p.rope[(size_t)P0 * half + k.row0 + tid];
+    if (!await_inputs(pp, k, c)) return false;
+    stage_x<(MAX_ACT + 1023) / 1024>(p, k.layer, c.parity, tid);
+    if (!cbarrier(pp, c, k.id)) return false;
+    tmark(c, 0);
+    {
+        float x[KT >= 512 ? KT / 64 : 8];
+        const float r = rms_scale(KT, p.eps, lane);
+        if constexpr (KT >= 512) {
+            load_x<KT>(0, lane, r, gw, x);
+        } else {
+            // small hidden sizes: apply the gains from LDS-staged activations directly
+            const uint16_t* g = gains(p, 2 * k.layer);
+            constexpr int LPROW = KT / 8;
+            load_x<KT>(0, lane, r, nullptr, x);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] *= bf16f(g[(lane % LPROW) * 8 + i]);
+        }
+        if (!gemv_pages<KT>(pp, c.wave, lane, page0, 2 * n, k.wbytes, x, k.id)) return false;
+    }
+    if (!cbarrier(pp, c, k.id)) return false;
+    tmark(c, 1);
     if ((uint32_t)tid < n) {
         const int j = (int)k.row0 + tid;
         float lo = S.rowres[tid], hi = S.rowres[n + tid];
         if (slot < (uint32_t)(nq + nkv)) {
-            const float2 cs = p.rope[(size_t)P0 * half + j];
             const float a = lo * cs.x - hi * cs.y;
-            const float c = lo * cs.y + hi * cs.x;
+            const float b = lo * cs.y + hi * cs.x;
             lo = a;
-            hi = c;
+            hi = b;
         }
         if (slot < (uint32_t)nq) {
             float* q = p.q + (size_t)slot * p.T.d;
@@ -612,11 +719,10 @@ __device__ __noinline__ bool op_qkv(const Params* pp, int wave, uint32_t& cgen, 
             const int j = (int)k.row0 + tid;
             float lo = S.rowres[tid], hi = S.rowres[n + tid];
             if (is_k) {
-                const float2 cs = p.rope[(size_t)P0 * half + j];
                 const float a = lo * cs.x - hi * cs.y;
-                const float c = lo * cs.y + hi * cs.x;
+                const float b = lo * cs.y + hi * cs.x;
                 lo = a;
-                hi = c;
+                hi = b;
             }
             st16_dev(base, (uint32_t)j, f2bf16(lo));
             st16_dev(base, (uint32_t)(j + half), f2bf16(hi));
@@ -627,9 +733,9 @@ __device__ __noinline__ bool op_qkv(const Params* pp, int wave, uint32_t& cgen, 
 
 // Attention over one chunk of the context of (sequence, KV group): one wave per query head.
 template <int D>
-__device__ __noinline__ bool op_attn(const Params* pp, int wave, const Task& k, uint32_t page0) {
+__device__ __noinline__ bool op_attn(const Params* pp, const Task& k, uint32_t page0, Ctx c) {
     CParams& p = P(pp);
-    const int lane = threadIdx.x & 63;
+    const int lane = c.lane, wave = c.wave;
     const int b = (int)k.seq, g = k.part;
     const Chunk ch = attn_chunk(p.T.attn_splits, S.pos[b], k.row0);
     const int32_t pb = attn_block_rows(D);
@@ -640,6 +746,38 @@ __device__ __noinline__ bool op_attn(const Params* pp, int wave, const Task& k, 
     constexpr int DL = D / 64;  // dimensions per lane
     const int G = p.T.grp;
     const int nh = (G - wave + NCW - 1) / NCW;  // heads of this wave: wave, wave + NCW, ...
+    const bool has_cur = ch.c0 <= ch.P && ch.P < ch.c1;
+    if (!await_inputs(pp, k, c)) return false;
+    // each wave stages the query rows of its own heads, and the current token's K/V row
+    float kv[DL], vv[DL];
+    {
+        const float* qg = p.q + (size_t)b * p.T.nq * D + (size_t)g * G * D;
+        float qv[4][DL];
+#pragma unroll
+        for (int hh = 0; hh < 4; ++hh)
+#pragma unroll
+            for (int ee = 0; ee < DL; ++ee)
+                qv[hh][ee] = hh < nh ? ldf_dev(qg + (wave + hh * NCW) * D + lane + 64 * ee) : 0.f;
+        if (has_cur) {
+            const size_t row = (((size_t)k.layer * p.T.B + b) * p.T.nkv + g) * (size_t)p.T.C + (size_t)ch.P;
+            const uint16_t* kr = S.args.kc + row * D;
+            const uint16_t* vr = S.args.vc + row * D;
+#pragma unroll
+            for (int ee = 0; ee < DL; ++ee) {
+                const int t = lane + 64 * ee;
+                const uint32_t wk = ld_dev((const uint32_t*)(kr + (t & ~1)));
+                const uint32_t wv = ld_dev((const uint32_t*)(vr + (t & ~1)));
+                kv[ee] = (t & 1) ? bf16hi(wk) : bf16lo(wk);
+                vv[ee] = (t & 1) ? bf16hi(wv) : bf16lo(wv);
+            }
+        }
+#pragma unroll
+        for (int hh = 0; hh < 4; ++hh)
+#pragma unroll
+            for (int ee = 0; ee < DL; ++ee)
+                if (hh < nh) S.xs[(wave + hh * NCW) * D + lane + 64 * ee] = qv[hh][ee];
+        lgkm_wait_all();
+    }
     float M[4], Ls[4], o[4][DL];
 #pragma unroll
     for (int hh = 0; hh < 4; ++hh) {
@@ -661,9 +799,9 @@ __device__ __noinline__ bool op_attn(const Params* pp, int wave, const Task& k, 
             if (lane < rows) {
                 float a = 0.f;
 #pragma unroll
-                for (int c = 0; c < D / 8; ++c) {
-                    const uint4 w = *(const uint4*)&ring[slot][lane * (2 * D) + c * 16];
-                    a = dot8(w, &S.xs[hw * D + c * 8], a);
+                for (int cc = 0; cc < D / 8; ++cc) {
+                    const uint4 w = *(const uint4*)&ring[slot][lane * (2 * D) + cc * 16];
+                    a = dot8(w, &S.xs[hw * D + cc * 8], a);
                 }
                 s = a * scale;
             }
@@ -681,27 +819,14 @@ __device__ __noinline__ bool op_attn(const Params* pp, int wave, const Task& k, 
                 const float wgt = S.wsc[wave][r];
 #pragma unroll
                 for (int ee = 0; ee < DL; ++ee) {
-                    const uint16_t vv = *(const uint16_t*)&ring[slot][8192 + r * (2 * D) + (lane + 64 * ee) * 2];
-                    o[hh][ee] = fmaf(wgt, bf16f(vv), o[hh][ee]);
+                    const uint16_t vvv = *(const uint16_t*)&ring[slot][8192 + r * (2 * D) + (lane + 64 * ee) * 2];
+                    o[hh][ee] = fmaf(wgt, bf16f(vvv), o[hh][ee]);
                 }
             }
         }
         page_release(page0 + pg, lane);
     }
-    // the current token (position P) if it falls in this chunk: read back from the cache (bf16)
-    if (ch.c0 <= ch.P && ch.P < ch.c1) {
-        const size_t row = (((size_t)k.layer * p.T.B + b) * p.T.nkv + g) * (size_t)p.T.C + (size_t)ch.P;
-        const uint16_t* kr = S.args.kc + row * D;
-        const uint16_t* vr = S.args.vc + row * D;
-        float kv[DL], vv[DL];
-#pragma unroll
-        for (int ee = 0; ee < DL; ++ee) {
-            const int t = lane + 64 * ee;
-            const uint32_t wk = ld_dev((const uint32_t*)(kr + (t & ~1)));
-            const uint32_t wv = ld_dev((const uint32_t*)(vr + (t & ~1)));
-            kv[ee] = (t & 1) ? bf16hi(wk) : bf16lo(wk);
-            vv[ee] = (t & 1) ? bf16hi(wv) : bf16lo(wv);
-        }
+    if (has_cur) {
 #pragma unroll
         for (int hh = 0; hh < 4; ++hh) {
             if (hh >= nh) break;
@@ -735,63 +860,169 @@ __device__ __noinline__ bool op_attn(const Params* pp, int wave, const Task& k, 
     return true;
 }
 
-__device__ __noinline__ bool op_oproj(const Params* pp, int wave, uint32_t& cgen, const Task& k, uint32_t page0,
-                                      uint32_t parity) {
+// Merge of the attention partials of one KV group, O-proj K-slice, residual (atomic add).
+template <int KT>
+__device__ __noinline__ bool op_oproj(const Params* pp, const Task& k, uint32_t page0, Ctx c) {
     CParams& p = P(pp);
-    const int lane = threadIdx.x & 63;
-    if (!gemv(p.T.grp * p.T.d, pp, wave, page0, k.nrows, k.wbytes, 0, 1.0f, nullptr, k.id)) return false;
-    if (!cbarrier(pp, cgen, lane, k.id)) return false;
-    float* dst = acc_buf(p, parity, 2 * k.layer, 0);
-    for (uint32_t i = (uint32_t)(wave * 64 + lane); i < k.nrows; i += NCW * 64) {
-        const uint32_t row = k.row0 + i;
-        float val = S.rowres[i];
-        if (k.flags & TF_RESID)
-            val += k.layer == 0 ? bf16f(embed_row(p, 0)[row]) : ldf_dev(acc_buf(p, parity, 2 * k.layer - 1, 0) + row);
-        addf_dev(dst + row, val);
+    const int lane = c.lane, tid = c.tid, wave = c.wave;
+    if (!await_inputs(pp, k, c)) return false;
+    const int D = p.T.d, Sp = p.T.attn_splits, G = p.T.grp;
+    // residual rows of this lane's epilogue (loaded now, used after the GEMV)
+    float res[MAX_TILE_ROWS / (NCW * 64)];
+#pragma unroll
+    for (int q = 0; q < MAX_TILE_ROWS / (NCW * 64); ++q) {
+        const uint32_t i = (uint32_t)(tid + q * NCW * 64);
+        res[q] = 0.f;
+        if ((k.flags & TF_RESID) && i < k.nrows) {
+            const uint32_t row = k.row0 + i;
+            res[q] = k.layer == 0 ? bf16f(embed_row(p, 0)[row]) : ldf_dev(acc_buf(p, c.parity, 2 * k.layer - 1, 0) + row);
+        }
+    }
+    // a = sum_c e^(m_c - M) o_c / sum_c e^(m_c - M) l_c, one wave per query head
+    for (int hw = wave; hw < G; hw += NCW) {
+        const float* src = p.part + ((size_t)k.part * Sp * G + hw) * (D + 2);
+        const size_t cs = (size_t)G * (D + 2);
+        float mc[16], lc[16], oc[16][2];
+#pragma unroll
+        for (int cc = 0; cc < 16; ++cc) {
+            if (cc < Sp) {
+                mc[cc] = ldf_dev(src + cc * cs);
+                lc[cc] = ldf_dev(src + cc * cs + 1);
+                oc[cc][0] = ldf_dev(src + cc * cs + 2 + lane);
+                oc[cc][1] = D == 128 ? ldf_dev(src + cc * cs + 2 + 64 + lane) : 0.f;
+            }
+        }
+        float Mx = -INFINITY;
+#pragma unroll
+        for (int cc = 0; cc < 16; ++cc)
+            if (cc < Sp) Mx = fmaxf(Mx, mc[cc]);
+        float den = 0.f, n0 = 0.f, n1 = 0.f;
+#pragma unroll
+        for (int cc = 0; cc < 16; ++cc) {
+            if (cc < Sp) {
+                const float sc = mc[cc] == -INFINITY ? 0.f : __expf(mc[cc] - Mx);
+                den = fmaf(sc, lc[cc], den);
+                n0 = fmaf(sc, oc[cc][0], n0);
+                n1 = fmaf(sc, oc[cc][1], n1);
+            }
+        }
+        S.xs[hw * D + lane] = n0 / den;
+        if (D == 128) S.xs[hw * D + 64 + lane] = n1 / den;
+    }
+    if (!cbarrier(pp, c, k.id)) return false;
+    tmark(c, 0);
+    {
+        float x[KT >= 512 ? KT / 64 : 8];
+        load_x<KT>(0, lane, 1.0f, nullptr, x);
+        if (!gemv_pages<KT>(pp, wave, lane, page0, k.nrows, k.wbytes, x, k.id)) return false;
+    }
+    if (!cbarrier(pp, c, k.id)) return false;
+    tmark(c, 1);
+    float* dst = acc_buf(p, c.parity, 2 * k.layer, 0);
+#pragma unroll
+    for (int q = 0; q < MAX_TILE_ROWS / (NCW * 64); ++q) {
+        const uint32_t i = (uint32_t)(tid + q * NCW * 64);
+        if (i < k.nrows) addf_dev(dst + k.row0 + i, S.rowres[i] + res[q]);
     }
     return true;
 }
 
-__device__ __noinline__ bool op_gateup(const Params* pp, int wave, uint32_t& cgen, const Task& k, uint32_t page0) {
+// RMSNorm + gate/up tile + SiLU(gate) * up.  Tile rows [0, n) gate, [n, 2n) up.
+template <int KT>
+__device__ __noinline__ bool op_gateup(const Params* pp, const Task& k, uint32_t page0, Ctx c) {
     CParams& p = P(pp);
-    const int lane = threadIdx.x & 63;
-    const float r = rms_scale(p.T.h, p.eps, lane);
-    if (!gemv(p.T.h, pp, wave, page0, 2 * k.nrows, k.wbytes, 0, r, gains(p, 2 * k.layer + 1), k.id)) return false;
-    if (!cbarrier(pp, cgen, lane, k.id)) return false;
-    for (uint32_t i = (uint32_t)(wave * 64 + lane); i < k.nrows; i += NCW * 64) {
+    const int lane = c.lane, tid = c.tid;
+    uint4 gw[KT / 512 > 0 ? KT / 512 : 1];
+    if constexpr (KT >= 512) load_gains<KT>(gains(p, 2 * k.layer + 1), lane, gw);
+    if (!await_inputs(pp, k, c)) return false;
+    stage_f32<(MAX_ACT + 1023) / 1024>(0, acc_buf(p, c.parity, 2 * k.layer, 0), p.T.h, tid);
+    if (!cbarrier(pp, c, k.id)) return false;
+    tmark(c, 0);
+    {
+        float x[KT >= 512 ? KT / 64 : 8];
+        const float r = rms_scale(KT, p.eps, lane);
+        if constexpr (KT >= 512) {
+            load_x<KT>(0, lane, r, gw, x);
+        } else {
+            const uint16_t* g = gains(p, 2 * k.layer + 1);
+            constexpr int LPROW = KT / 8;
+            load_x<KT>(0, lane, r, nullptr, x);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] *= bf16f(g[(lane % LPROW) * 8 + i]);
+        }
+        if (!gemv_pages<KT>(pp, c.wave, lane, page0, 2 * k.nrows, k.wbytes, x, k.id)) return false;
+    }
+    if (!cbarrier(pp, c, k.id)) return false;
+    tmark(c, 1);
+    for (uint32_t i = (uint32_t)tid; i < k.nrows; i += NCW * 64) {
         const float gt = S.rowres[i], up = S.rowres[k.nrows + i];
         stf_dev(p.m + k.row0 + i, gt / (1.0f + __expf(-gt)) * up);
     }
     return true;
 }
 
-__device__ __noinline__ bool op_down(const Params* pp, int wave, uint32_t& cgen, const Task& k, uint32_t page0,
-                                     uint32_t parity) {
+// Down-proj K-slice tile + residual (atomic add).
+template <int KT>
+__device__ __noinline__ bool op_down(const Params* pp, const Task& k, uint32_t page0, Ctx c) {
     CParams& p = P(pp);
-    const int lane = threadIdx.x & 63;
-    if (!gemv(p.T.kd, pp, wave, page0, k.nrows, k.wbytes, 0, 1.0f, nullptr, k.id)) return false;
-    if (!cbarrier(pp, cgen, lane, k.id)) return false;
-    float* dst = acc_buf(p, parity, 2 * k.layer + 1, 0);
-    for (uint32_t i = (uint32_t)(wave * 64 + lane); i < k.nrows; i += NCW * 64) {
-        const uint32_t row = k.row0 + i;
-        float val = S.rowres[i];
-        if (k.flags & TF_RESID) val += ldf_dev(acc_buf(p, parity, 2 * k.layer, 0) + row);
-        addf_dev(dst + row, val);
+    const int lane = c.lane, tid = c.tid;
+    if (!await_inputs(pp, k, c)) return false;
+    float res[MAX_TILE_ROWS / (NCW * 64)];
+#pragma unroll
+    for (int q = 0; q < MAX_TILE_ROWS / (NCW * 64); ++q) {
+        const uint32_t i = (uint32_t)(tid + q * NCW * 64);
+        res[q] = (k.flags & TF_RESID) && i < k.nrows ? ldf_dev(acc_buf(p, c.parity, 2 * k.layer, 0) + k.row0 + i) : 0.f;
+    }
+    stage_f32<(MAX_ACT + 1023) / 1024>(0, p.m + (size_t)k.part * KT, KT, tid);
+    if (!cbarrier(pp, c, k.id)) return false;
+    tmark(c, 0);
+    {
+        float x[KT >= 512 ? KT / 64 : 8];
+        load_x<KT>(0, lane, 1.0f, nullptr, x);
+        if (!gemv_pages<KT>(pp, c.wave, lane, page0, k.nrows, k.wbytes, x, k.id)) return false;
+    }
+    if (!cbarrier(pp, c, k.id)) return false;
+    tmark(c, 1);
+    float* dst = acc_buf(p, c.parity, 2 * k.layer + 1, 0);
+#pragma unroll
+    for (int q = 0; q < MAX_TILE_ROWS / (NCW * 64); ++q) {
+        const uint32_t i = (uint32_t)(tid + q * NCW * 64);
+        if (i < k.nrows) addf_dev(dst + k.row0 + i, S.rowres[i] + res[q]);
     }
     return true;
 }
 
-__device__ __noinline__ bool op_lmhead(const Params* pp, int wave, uint32_t& cgen, const Task& k, uint32_t page0,
-                                       uint32_t parity) {
+// Final RMSNorm + LM-head tile + argmax (packed 64-bit atomic max).
+template <int KT>
+__device__ __noinline__ bool op_lmhead(const Params* pp, const Task& k, uint32_t page0, Ctx c) {
     CParams& p = P(pp);
-    const int lane = threadIdx.x & 63;
-    const float r = rms_scale(p.T.h, p.eps, lane);
-    if (!gemv(p.T.h, pp, wave, page0, k.nrows, k.wbytes, 0, r, gains(p, 2 * p.T.L), k.id)) return false;
-    if (!cbarrier(pp, cgen, lane, k.id)) return false;
+    const int lane = c.lane, tid = c.tid;
+    uint4 gw[KT / 512 > 0 ? KT / 512 : 1];
+    if constexpr (KT >= 512) load_gains<KT>(gains(p, 2 * p.T.L), lane, gw);
+    if (!await_inputs(pp, k, c)) return false;
+    stage_x<(MAX_ACT + 1023) / 1024>(p, p.T.L, c.parity, tid);
+    if (!cbarrier(pp, c, k.id)) return false;
+    tmark(c, 0);
+    {
+        float x[KT >= 512 ? KT / 64 : 8];
+        const float r = rms_scale(KT, p.eps, lane);
+        if constexpr (KT >= 512) {
+            load_x<KT>(0, lane, r, gw, x);
+        } else {
+            const uint16_t* g = gains(p, 2 * p.T.L);
+            constexpr int LPROW = KT / 8;
+            load_x<KT>(0, lane, r, nullptr, x);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] *= bf16f(g[(lane % LPROW) * 8 + i]);
+        }
+        if (!gemv_pages<KT>(pp, c.wave, lane, page0, k.nrows, k.wbytes, x, k.id)) return false;
+    }
+    if (!cbarrier(pp, c, k.id)) return false;
+    tmark(c, 1);
     float bv = -INFINITY;
     uint32_t bi = 0xffffffffu;
     float* logits = S.args.logits;
-    for (uint32_t i = (uint32_t)(wave * 64 + lane); i < k.nrows; i += NCW * 64) {
+    for (uint32_t i = (uint32_t)tid; i < k.nrows; i += NCW * 64) {
         const float val = S.rowres[i];
         if (logits) logits[k.row0 + i] = val;
         if (val > bv) {  // rows visited in increasing order: the first maximum is kept
@@ -810,7 +1041,7 @@ __device__ __noinline__ bool op_lmhead(const Params* pp, int wave, uint32_t& cge
         key = other > key ? other : key;
     }
     if (lane == 0 && key)
-        __hip_atomic_fetch_max((g_u64*)&p.key[parity * p.T.B + 0], key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_max((g_u64*)&p.key[c.parity * p.T.B + 0], key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return true;
 }
 
@@ -835,12 +1066,28 @@ __device__ __noinline__ void finish_step(const Params* pp, uint32_t epoch, uint3
     }
 }
 
+#define MK_KT_DISPATCH(fn, kt, ...)                                      \
+    ((kt) == 64     ? fn<64>(__VA_ARGS__)                                \
+     : (kt) == 128  ? fn<128>(__VA_ARGS__)                               \
+     : (kt) == 256  ? fn<256>(__VA_ARGS__)                               \
+     : (kt) == 512  ? fn<512>(__VA_ARGS__)                               \
+     : (kt) == 1024 ? fn<1024>(__VA_ARGS__)                              \
+     : (kt) == 2048 ? fn<2048>(__VA_ARGS__)                              \
+                    : fn<4096>(__VA_ARGS__))
+
 // ---- compute-wave main loop ---------------------------------------------------------------
 
 __device__ __noinline__ void compute(const Params* pp, uint32_t epoch, int wave) {
-    const int lane = threadIdx.x & 63;
-    const uint32_t parity = epoch & 1u;
     uint32_t cgen = 0;
+    Ctx c;
+    c.wave = (int)uni((uint32_t)wave);
+    c.lane = threadIdx.x & 63;
+    c.tid = c.wave * 64 + c.lane;
+    c.epoch = epoch;
+    c.parity = epoch & 1u;
+    c.cgen = &cgen;
+    CParams& p0 = P(pp);
+    const int h = p0.T.h, okt = p0.T.grp * p0.T.d, dkt = p0.T.kd, hd = p0.T.d;
     for (uint32_t t = 0;; ++t) {
         const uint32_t slot = t % FIFO;
         if (!lds_wait_ge(S.fifo_ready[slot], t + 1, pp, NONE)) return;
@@ -850,51 +1097,46 @@ __device__ __noinline__ void compute(const Params* pp, uint32_t epoch, int wave)
         const uint32_t page0 = uni(lds_ld(S.fifo_first_page[slot]));
         if (k.op == OP_END) return;
         const uint64_t t_fetch = rtc();
-        uint64_t t_ready = 0;
-        // ---- wait for the inputs and stage them (wave 0) ----
-        if (wave == 0) {
-            if (k.wait_ev != NONE && !wait_event(pp, k.wait_ev, k.wait_nsub, epoch * k.wait_target, k.id)) return;
-            t_ready = rtc();
-            stage(pp, k, parity);
-            lgkm_wait_all();
-            if (lane == 0) lds_st(S.go, t + 1);
-        } else {
-            if (!lds_wait_ge(S.go, t + 1, pp, k.id)) return;
-        }
-        // ---- execute ----
+        c.t = t;
         bool ok = true;
         switch (k.op) {
-            case OP_QKV: ok = op_qkv(pp, wave, cgen, k, page0); break;
-            case OP_ATTN: ok = P(pp).T.d == 64 ? op_attn<64>(pp, wave, k, page0) : op_attn<128>(pp, wave, k, page0); break;
-            case OP_OPROJ: ok = op_oproj(pp, wave, cgen, k, page0, parity); break;
-            case OP_GATEUP: ok = op_gateup(pp, wave, cgen, k, page0); break;
-            case OP_DOWN: ok = op_down(pp, wave, cgen, k, page0, parity); break;
-            case OP_LMHEAD: ok = op_lmhead(pp, wave, cgen, k, page0, parity); break;
+            case OP_QKV: ok = MK_KT_DISPATCH(op_qkv, h, pp, k, page0, c); break;
+            case OP_ATTN: ok = hd == 64 ? op_attn<64>(pp, k, page0, c) : op_attn<128>(pp, k, page0, c); break;
+            case OP_OPROJ: ok = MK_KT_DISPATCH(op_oproj, okt, pp, k, page0, c); break;
+            case OP_GATEUP: ok = MK_KT_DISPATCH(op_gateup, h, pp, k, page0, c); break;
+            case OP_DOWN: ok = MK_KT_DISPATCH(op_down, dkt, pp, k, page0, c); break;
+            case OP_LMHEAD: ok = MK_KT_DISPATCH(op_lmhead, h, pp, k, page0, c); break;
             default: break;
         }
-        if (!ok) return;
+        if (!uni(ok)) return;
         // ---- completion: every wave's stores are done, then wave 0 signals ----
         vm_wait_all();
         lgkm_wait_all();
-        if (lane == 0) lds_add(S.done, 1u);
-        if (wave == 0) {
+        if (c.lane == 0) lds_add(S.done, 1u);
+        if (c.wave == 0) {
             if (!lds_wait_ge(S.done, NCW * (t + 1), pp, k.id)) return;
             CParams& p = P(pp);
-            if (k.sig_ev != NONE && k.id != p.drop_task && lane == 0) {
+            if (k.sig_ev != NONE && k.id != p.drop_task && c.lane == 0) {
                 const uint32_t sub = k.sig_nsub == 8 ? xcc_id() : 0u;
                 addu_dev(&p.ctr[ctr_index(k.sig_ev, sub)], 1u);
             }
-            if (k.op == OP_LMHEAD) finish_step(pp, epoch, parity);
-            if (p.task_count && lane == 0) addu_dev(&p.task_count[k.id], 1u);
-            if (p.trace && lane == 0) {
-                unsigned long long* tr = p.trace + (size_t)k.id * 4;
+            if (k.op == OP_LMHEAD) finish_step(pp, epoch, c.parity);
+            if (p.task_count && c.lane == 0) addu_dev(&p.task_count[k.id], 1u);
+            if (p.trace && c.lane == 0) {
+                unsigned long long* tr = p.trace + (size_t)k.id * TRACE_WORDS;
+                const uint64_t t_ready = ((unsigned long long)lds_ld(S.t_ready_hi) << 32) | lds_ld(S.t_ready_lo);
+                const uint64_t hi = t_ready & ~0xffffffffull;
                 tr[0] = blockIdx.x;
                 tr[1] = t_fetch;
                 tr[2] = t_ready;
-                tr[3] = rtc();
+                tr[3] = k.op == OP_ATTN ? 0 : hi | lds_ld(S.tm[0]);
+                tr[4] = k.op == OP_ATTN ? 0 : hi | lds_ld(S.tm[1]);
+                tr[5] = rtc();
+                tr[6] = page0;
+                tr[7] = 0;
             }
             vm_wait_all();
-            if (lane == 0) lds_add(S.fifo_free[slot], 1u);
+            if (c.lane == 0) lds_add(S.fifo_free[slot], 1u);
         }
     }
 }
@@ -909,7 +1151,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) mk_step_kernel(const Params* pp, 
         S.fifo_free[threadIdx.x] = 0;
     }
     if (threadIdx.x < NPAGES) {
-        S.page_ready[threadIdx.x] = 0;
+        for (int lw = 0; lw < NLW; ++lw) S.page_ready[lw][threadIdx.x] = 0;
         S.page_free[threadIdx.x] = 0;
     }
     if (threadIdx.x == 0) {
@@ -917,6 +1159,8 @@ __global__ void __launch_bounds__(NTHREADS, 1) mk_step_kernel(const Params* pp, 
         S.cbar = 0;
         S.done = 0;
         S.abort = 0;
+        S.dyn_ready = 0;
+        S.dyn_ack = 0;
         S.args = a;
     }
     const uint32_t epoch = p.state[ST_EPOCH];
@@ -941,7 +1185,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) mk_step_kernel(const Params* pp, 
         for (size_t i = (size_t)blockIdx.x * NTHREADS + threadIdx.x; i < nacc; i += (size_t)gridDim.x * NTHREADS)
             other[i] = 0.f;
         if (blockIdx.x == 0 && (int)threadIdx.x < B) p.key[(parity ^ 1u) * B + threadIdx.x] = 0ull;
-        if (wave == NCW) loader(pp, epoch);
+        if (wave >= NCW) loader(pp, epoch, wave - NCW);
         else compute(pp, epoch, wave);
     }
     __syncthreads();
@@ -959,6 +1203,23 @@ hipError_t launch_step(const Params* dparams, const StepArgs& a, uint32_t grid, 
         return hipLaunchCooperativeKernel((const void*)mk_step_kernel, dim3(grid), dim3(NTHREADS), args, 0, stream);
     }
     hipLaunchKernelGGL(mk_step_kernel, dim3(grid), dim3(NTHREADS), 0, stream, dparams, a);
+    return hipGetLastError();
+}
+
+// Weight repacking at build time: one workgroup per copy operation.
+__global__ void __launch_bounds__(256) repack_kernel(const CopyOp* ops, uint8_t* dst) {
+    const CopyOp op = ops[blockIdx.x];
+    const uint32_t n16 = op.row_bytes / 16;
+    for (uint32_t r = 0; r < op.rows; ++r) {
+        const uint4* s = (const uint4*)(op.src + (uint64_t)r * op.src_pitch);
+        uint4* d = (uint4*)(dst + op.dst_off + (uint64_t)r * op.row_bytes);
+        for (uint32_t i = threadIdx.x; i < n16; i += 256) d[i] = s[i];
+    }
+}
+
+hipError_t launch_repack(const CopyOp* ops, uint32_t n_ops, uint8_t* dst, hipStream_t stream) {
+    if (n_ops == 0) return hipSuccess;
+    hipLaunchKernelGGL(repack_kernel, dim3(n_ops), dim3(256), 0, stream, ops, dst);
     return hipGetLastError();
 }
 

@@ -2,6 +2,7 @@
 // upload and the one-launch decode step (declarations in include/mk.h).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -92,25 +93,38 @@ mk_status plan(const mk_model_desc* desc, int32_t batch, int32_t max_ctx, const 
     return MK_OK;
 }
 
-// Copy the caller's weights into the packed layout: gains, embedding (+ LM head),
-// then per layer the QKV, O, gate/up and down tiles in task order.
+// Copy the caller's weights into the packed layout (gains, embedding, LM head,
+// then per layer the QKV, O, gate/up and down tiles in task order) with one
+// repacking kernel.
 mk_status repack(mk_handle* h, const mk_model_desc* d, uint8_t* wd) {
     const Tiling& T = h->g.T;
     const Layout& Ly = h->g.lay;
-    const size_t H = (size_t)T.h;
-    const size_t rowb = H * 2;
-    hipStream_t s = nullptr;
+    const uint64_t rowb = (uint64_t)T.h * 2;
+    std::vector<CopyOp> ops;
+    auto add = [&](const void* src, uint64_t dst_off, uint64_t rows, uint64_t row_bytes, uint64_t pitch) {
+        // split large contiguous copies so one workgroup moves at most ~1 MiB
+        const uint64_t per = row_bytes >= (1u << 20) ? 1 : std::max<uint64_t>(1, (1u << 20) / row_bytes);
+        for (uint64_t r = 0; r < rows; r += per) {
+            CopyOp o;
+            o.src = (const uint8_t*)src + r * pitch;
+            o.dst_off = dst_off + r * row_bytes;
+            o.src_pitch = pitch;
+            o.rows = (uint32_t)std::min<uint64_t>(per, rows - r);
+            o.row_bytes = (uint32_t)row_bytes;
+            ops.push_back(o);
+        }
+    };
     for (int l = 0; l < T.L; ++l) {
-        HIPCHK(hipMemcpyAsync(wd + Ly.gains + (size_t)(2 * l) * rowb, d->layers[l].attn_norm, rowb, hipMemcpyDeviceToDevice, s));
-        HIPCHK(hipMemcpyAsync(wd + Ly.gains + (size_t)(2 * l + 1) * rowb, d->layers[l].ffn_norm, rowb, hipMemcpyDeviceToDevice, s));
+        add(d->layers[l].attn_norm, Ly.gains + (uint64_t)(2 * l) * rowb, 1, rowb, rowb);
+        add(d->layers[l].ffn_norm, Ly.gains + (uint64_t)(2 * l + 1) * rowb, 1, rowb, rowb);
     }
-    HIPCHK(hipMemcpyAsync(wd + Ly.gains + (size_t)(2 * T.L) * rowb, d->final_norm, rowb, hipMemcpyDeviceToDevice, s));
-    HIPCHK(hipMemcpyAsync(wd + Ly.embed, d->tok_embed, (size_t)T.V * rowb, hipMemcpyDeviceToDevice, s));
-    if (!h->tied) HIPCHK(hipMemcpyAsync(wd + Ly.lm, d->lm_head, (size_t)T.V * rowb, hipMemcpyDeviceToDevice, s));
+    add(d->final_norm, Ly.gains + (uint64_t)(2 * T.L) * rowb, 1, rowb, rowb);
+    add(d->tok_embed, Ly.embed, (uint64_t)T.V, rowb, rowb);
+    if (!h->tied) add(d->lm_head, Ly.lm, (uint64_t)T.V, rowb, rowb);
     const int half = T.d / 2, P = T.qkv_pairs;
     for (const Task& k : h->g.tasks) {
+        const mk_layer_weights& lw = d->layers[k.layer < T.L ? k.layer : 0];
         if (k.op == OP_QKV) {
-            const mk_layer_weights& lw = d->layers[k.layer];
             const uint8_t* src;
             int hrow;
             if (k.part < T.nq) {
@@ -123,27 +137,29 @@ mk_status repack(mk_handle* h, const mk_model_desc* d, uint8_t* wd) {
                 src = (const uint8_t*)lw.wv;
                 hrow = (k.part - T.nq - T.nkv) * T.d;
             }
-            uint8_t* dst = wd + k.wofs;
-            HIPCHK(hipMemcpyAsync(dst, src + (size_t)(hrow + k.row0) * rowb, (size_t)P * rowb, hipMemcpyDeviceToDevice, s));
-            HIPCHK(hipMemcpyAsync(dst + (size_t)P * rowb, src + (size_t)(hrow + k.row0 + half) * rowb, (size_t)P * rowb,
-                                  hipMemcpyDeviceToDevice, s));
+            add(src + (uint64_t)(hrow + k.row0) * rowb, k.wofs, P, rowb, rowb);
+            add(src + (uint64_t)(hrow + k.row0 + half) * rowb, k.wofs + (uint64_t)P * rowb, P, rowb, rowb);
         } else if (k.op == OP_OPROJ) {
-            const size_t kt = (size_t)T.grp * T.d;
-            const uint8_t* src = (const uint8_t*)d->layers[k.layer].wo + ((size_t)k.row0 * T.nq * T.d + k.part * kt) * 2;
-            HIPCHK(hipMemcpy2DAsync(wd + k.wofs, kt * 2, src, (size_t)T.nq * T.d * 2, kt * 2, k.nrows,
-                                    hipMemcpyDeviceToDevice, s));
+            const uint64_t kt = (uint64_t)T.grp * T.d;
+            const uint8_t* src = (const uint8_t*)lw.wo + ((uint64_t)k.row0 * T.nq * T.d + k.part * kt) * 2;
+            add(src, k.wofs, k.nrows, kt * 2, (uint64_t)T.nq * T.d * 2);
         } else if (k.op == OP_GATEUP) {
-            const mk_layer_weights& lw = d->layers[k.layer];
-            const size_t nb = (size_t)k.nrows * rowb;
-            HIPCHK(hipMemcpyAsync(wd + k.wofs, (const uint8_t*)lw.w_gate + (size_t)k.row0 * rowb, nb, hipMemcpyDeviceToDevice, s));
-            HIPCHK(hipMemcpyAsync(wd + k.wofs + nb, (const uint8_t*)lw.w_up + (size_t)k.row0 * rowb, nb, hipMemcpyDeviceToDevice, s));
+            const uint64_t nb = (uint64_t)k.nrows * rowb;
+            add((const uint8_t*)lw.w_gate + (uint64_t)k.row0 * rowb, k.wofs, k.nrows, rowb, rowb);
+            add((const uint8_t*)lw.w_up + (uint64_t)k.row0 * rowb, k.wofs + nb, k.nrows, rowb, rowb);
         } else if (k.op == OP_DOWN) {
-            const size_t kd = (size_t)T.kd;
-            const uint8_t* src = (const uint8_t*)d->layers[k.layer].w_down + ((size_t)k.row0 * T.f + (size_t)k.part * kd) * 2;
-            HIPCHK(hipMemcpy2DAsync(wd + k.wofs, kd * 2, src, (size_t)T.f * 2, kd * 2, k.nrows, hipMemcpyDeviceToDevice, s));
+            const uint64_t kd = (uint64_t)T.kd;
+            const uint8_t* src = (const uint8_t*)lw.w_down + ((uint64_t)k.row0 * T.f + (uint64_t)k.part * kd) * 2;
+            add(src, k.wofs, k.nrows, kd * 2, (uint64_t)T.f * 2);
         }
     }
-    HIPCHK(hipStreamSynchronize(s));
+    CopyOp* dops = nullptr;
+    HIPCHK(hipMalloc(&dops, ops.size() * sizeof(CopyOp)));
+    hipError_t e = hipMemcpy(dops, ops.data(), ops.size() * sizeof(CopyOp), hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = launch_repack(dops, (uint32_t)ops.size(), wd, nullptr);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    (void)hipFree(dops);
+    HIPCHK(e);
     return MK_OK;
 }
 
@@ -286,7 +302,7 @@ mk_status mk_build_graph(const mk_model_desc* desc, int32_t batch, int32_t max_c
     ALLOC(p.next, 4 * T.B, true);
     if (o.trace) {
         ALLOC(p.task_count, h->g.tasks.size() * 4, true);
-        ALLOC(p.trace, h->g.tasks.size() * 32, true);
+        ALLOC(p.trace, h->g.tasks.size() * 8 * TRACE_WORDS, true);
     }
     auto up = [&](void* dst, const void* src, size_t n) { return hipMemcpy(dst, src, n, hipMemcpyHostToDevice); };
     if (up(td, h->g.tasks.data(), h->g.tasks.size() * sizeof(Task)) != hipSuccess ||
@@ -410,7 +426,7 @@ mk_status mk_read_trace(mk_handle* h, uint64_t* host, size_t n) {
     if (!h || !host) return MK_E_INVALID;
     if (!h->p.trace) return MK_E_UNSUPPORTED;
     HIPCHK(hipDeviceSynchronize());
-    size_t m = n < h->g.tasks.size() * 4 ? n : h->g.tasks.size() * 4;
+    size_t m = n < h->g.tasks.size() * TRACE_WORDS ? n : h->g.tasks.size() * TRACE_WORDS;
     HIPCHK(hipMemcpy(host, h->p.trace, m * 8, hipMemcpyDeviceToHost));
     return MK_OK;
 }

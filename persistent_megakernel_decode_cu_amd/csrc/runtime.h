@@ -16,6 +16,8 @@ constexpr uint32_t ST_ABORT = 96;   // set when any wave gives up
 constexpr uint32_t ST_ERR = 128;    // error record: code, workgroup, task, event, seen, target
 constexpr uint32_t ST_WORDS = 160;
 
+constexpr int TRACE_WORDS = 8;  // per task: workgroup, fetch, inputs ready, staged, computed, end, first page, 0
+
 enum ErrCode : uint32_t { ERR_NONE = 0, ERR_TIMEOUT_EVENT = 1, ERR_TIMEOUT_LDS = 2, ERR_INPUT = 3 };
 
 // Per-step pointers, passed by value with every launch.
@@ -47,13 +49,23 @@ struct Params {
     uint32_t* ticket;         // [B]
     int32_t* next;            // [B]
     uint32_t* task_count;     // [n_tasks] or null
-    unsigned long long* trace;  // [n_tasks][4] or null
+    unsigned long long* trace;  // [n_tasks][TRACE_WORDS] or null
     Tiling T;
     Layout lay;
     float eps;
     uint32_t drop_task;
     unsigned long long timeout;  // ticks of the 100 MHz device clock
 };
+
+// One strided copy of the weight repacking: rows x row_bytes from src (row pitch
+// src_pitch) to dst + dst_off (rows contiguous).  row_bytes is a multiple of 16.
+struct CopyOp {
+    const uint8_t* src;
+    uint64_t dst_off;
+    uint64_t src_pitch;
+    uint32_t rows, row_bytes;
+};
+hipError_t launch_repack(const CopyOp* ops, uint32_t n_ops, uint8_t* dst, hipStream_t stream);
 
 hipError_t launch_step(const Params* dparams, const StepArgs& a, uint32_t grid, hipStream_t stream, bool cooperative);
 int step_threads();
