@@ -160,6 +160,30 @@ void mk_destroy(mk_handle *h);
 
 const char *mk_status_str(mk_status s);
 
+/* ---- One-kernel-per-op baseline ----------------------------------------------
+ * The same decode step run the conventional way, one kernel per operator
+ * (embedding, RMSNorm, Q/K/V GEMVs, RoPE + KV append, attention partials and
+ * merge, O-proj + residual, RMSNorm, gate/up + SiLU, down + residual, final
+ * RMSNorm, LM head, argmax), for comparison: the execution model the Hazy
+ * Research megakernel news page (section 3) contrasts the megakernel with.
+ * Same inputs, layouts and arithmetic as the megakernel; reads the caller's
+ * weights in place (no copy), so they must outlive the handle.  batch must be 1;
+ * hidden, n_q*head_dim and ffn_dim must be powers of two in [512, 8192]. */
+typedef struct mkb_handle mkb_handle;
+
+mk_status mkb_create(const mk_model_desc *desc, int32_t batch, int32_t max_ctx, mkb_handle **out);
+
+/* Enqueues the step's kernels on `stream`.  tokens/positions (dev) int32 [1]:
+ * as for mk_decode_step.  When advance != 0 the last kernel also stores the
+ * next token into tokens[0] and increments positions[0], so a graph captured
+ * from one call can be replayed for consecutive greedy steps. */
+mk_status mkb_decode_step(mkb_handle *h, int32_t *tokens, int32_t *positions, void *kv_cache, float *logits,
+                          void *stream, int32_t advance);
+
+const int32_t *mkb_next_tokens(const mkb_handle *h); /* (dev) int32 [1] */
+const float *mkb_hidden_out(const mkb_handle *h);    /* (dev) float [hidden] */
+void mkb_destroy(mkb_handle *h);
+
 #ifdef __cplusplus
 }
 #endif

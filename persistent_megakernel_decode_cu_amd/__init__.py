@@ -101,6 +101,15 @@ def load():
     lib.mk_read_trace.restype = ctypes.c_int
     lib.mk_destroy.argtypes = [_P]
     lib.mk_destroy.restype = None
+    lib.mkb_create.argtypes = [ctypes.POINTER(ModelDesc), ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(_P)]
+    lib.mkb_create.restype = ctypes.c_int
+    lib.mkb_decode_step.argtypes = [_P, _P, _P, _P, _P, _P, ctypes.c_int32]
+    lib.mkb_decode_step.restype = ctypes.c_int
+    for n in ("mkb_next_tokens", "mkb_hidden_out"):
+        getattr(lib, n).argtypes = [_P]
+        getattr(lib, n).restype = _P
+    lib.mkb_destroy.argtypes = [_P]
+    lib.mkb_destroy.restype = None
     _lib = lib
     return lib
 
@@ -205,6 +214,32 @@ def mk_read_trace(h, n_tasks):
 def mk_destroy(h):
     if h:
         load().mk_destroy(h)
+
+
+# ---- one-kernel-per-op baseline -------------------------------------------------
+
+def mkb_create(desc, batch, max_ctx):
+    h = _P()
+    _check(load().mkb_create(ctypes.byref(desc), batch, max_ctx, ctypes.byref(h)), "mkb_create")
+    return h
+
+
+def mkb_decode_step(h, tokens_ptr, positions_ptr, kv_ptr, logits_ptr, stream_ptr, advance=0):
+    _check(load().mkb_decode_step(h, tokens_ptr, positions_ptr, kv_ptr, logits_ptr, stream_ptr, advance),
+           "mkb_decode_step")
+
+
+def mkb_next_tokens(h):
+    return load().mkb_next_tokens(h)
+
+
+def mkb_hidden_out(h):
+    return load().mkb_hidden_out(h)
+
+
+def mkb_destroy(h):
+    if h:
+        load().mkb_destroy(h)
 
 
 # ---- export image ------------------------------------------------------------------

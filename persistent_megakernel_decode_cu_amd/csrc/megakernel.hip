@@ -212,7 +212,7 @@ __device__ __noinline__ bool lds_wait_slow(const uint32_t& w, uint32_t v, const 
             const uint64_t now = rtc();
             if (t0 == 0) {
                 t0 = now;
-            } else if (now - t0 > p.timeout) {
+            } else if (now - t0 > 2 * p.timeout) {  // longer than an event wait: the stalled event is reported first
                 raise_error(pp, ERR_TIMEOUT_LDS, task, NONE, lds_ld(w), v);
                 return false;
             }

@@ -1,0 +1,88 @@
+"""GPU parity at the full Llama-3.2-1B shape, in the launch configuration the benchmark times
+(one workgroup per CU, static queues), against the oracle and the oracle-written golden file."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import persistent_megakernel_decode_cu_amd as mk
+import synth
+from gpu_util import Runner, compare_step, TOL_HIDDEN_REL, TOL_LOGIT_ABS
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "llama1b_greedy256.json")
+CFG = synth.configs.LLAMA_1B
+
+
+@pytest.fixture(scope="module")
+def inputs():
+    g = json.load(open(GOLDEN))
+    w = synth.make_weights(CFG)
+    kc, vc = synth.make_kv(CFG, 1, g["max_ctx"])
+    tok = synth.make_tokens(CFG, 1)
+    assert int(tok[0]) == g["first_token"]
+    return g, w, kc, vc, tok
+
+
+def _greedy(run, tok, P0, steps):
+    positions = torch.arange(P0, P0 + steps, dtype=torch.int32, device="cuda")
+    t0 = torch.tensor(tok, dtype=torch.int32, device="cuda")
+    nxt = mk.mk_next_tokens(run.h)
+    out = torch.empty(steps, dtype=torch.int32, device="cuda")
+    for s in range(steps):
+        tp = t0.data_ptr() if s == 0 else nxt
+        mk.mk_decode_step(run.h, tp, positions[s:s + 1].data_ptr(), run.kv.data_ptr(), run.logits.data_ptr(),
+                          torch.cuda.current_stream().cuda_stream)
+        out[s:s + 1].copy_(run.next_tokens())
+    run.check()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("sched", [0, 1])
+def test_llama1b_first_step(inputs, sched):
+    g, w, kc, vc, tok = inputs
+    P0 = g["first_position"]
+    print(f"case llama1b first step sched={sched}", flush=True)
+    run = Runner(CFG, w, 1, g["max_ctx"], kc, vc, sched=sched)
+    run.step(tok, [P0])
+    run.check()
+    logits = run.logits.cpu().numpy()[0]
+    hidden = run.hidden().cpu().numpy()
+    nxt = run.next_tokens().cpu().numpy()
+    run.close()
+    ref = oracle.decode_step(CFG, w, tok, [P0], kc.copy(), vc.copy())
+    res = compare_step(CFG, ref, logits[None], hidden, nxt)
+    print(res)
+    assert res["hidden_rel"] <= TOL_HIDDEN_REL
+    assert res["max_dlogit"] <= TOL_LOGIT_ABS
+    assert res["argmax_equal"] and int(nxt[0]) == g["tokens"][0]
+
+
+def test_llama1b_greedy_256_steps(inputs):
+    g, w, kc, vc, tok = inputs
+    run = Runner(CFG, w, 1, g["max_ctx"], kc, vc)
+    got = _greedy(run, tok, g["first_position"], g["steps"])
+    run.close()
+    ref = np.array(g["tokens"])
+    bad = np.nonzero(got != ref)[0]
+    if len(bad):
+        i = int(bad[0])
+        pytest.fail(f"first mismatch at step {i}: gpu {got[i]} oracle {ref[i]} (oracle top-2 gap there "
+                    f"{g['top2_gaps'][i]:.3g}); {len(bad)} mismatching steps")
+
+
+def test_llama1b_counters_and_task_counts(inputs):
+    g, w, kc, vc, tok = inputs
+    run = Runner(CFG, w, 1, g["max_ctx"], kc, vc, trace=1)
+    steps = 3
+    _greedy(run, tok, g["first_position"], steps)
+    counts = mk.mk_read_task_counts(run.h, len(run.graph["tasks"]))
+    ctr, epoch = mk.mk_read_counters(run.h, run.graph["header"]["n_events"])
+    run.close()
+    assert epoch == steps
+    np.testing.assert_array_equal(counts, np.full(len(counts), steps, np.uint32))
+    np.testing.assert_array_equal(ctr, run.graph["target"].astype(np.uint64) * steps)

@@ -96,3 +96,67 @@ def test_tiny_greedy_chain_and_counters():
     run.close()
     ref = oracle.greedy(cfg, w, tok, [P0], kc.copy(), vc.copy(), steps)
     assert got == ref["tokens"][:, 0].tolist(), (got, ref["tokens"][:, 0].tolist(), ref["gaps"][:, 0])
+
+
+def test_tiny_dynamic_queue_greedy():
+    cfg = synth.configs.TINY
+    C, P0, steps = 512, 100, 16
+    w, kc, vc, tok, pos = _setup(cfg, C, P0)
+    run = Runner(cfg, w, 1, C, kc, vc, sched=1, trace=1)
+    positions = torch.arange(P0, P0 + steps, dtype=torch.int32, device="cuda")
+    t0 = torch.tensor(tok, dtype=torch.int32, device="cuda")
+    nxt = mk.mk_next_tokens(run.h)
+    got = []
+    for s in range(steps):
+        mk.mk_decode_step(run.h, t0.data_ptr() if s == 0 else nxt, positions[s:s + 1].data_ptr(), run.kv.data_ptr(),
+                          run.logits.data_ptr(), torch.cuda.current_stream().cuda_stream)
+        got.append(int(run.next_tokens().cpu()[0]))
+    run.check()
+    counts = mk.mk_read_task_counts(run.h, len(run.graph["tasks"]))
+    np.testing.assert_array_equal(counts, np.full(len(counts), steps, np.uint32))
+    run.close()
+    ref = oracle.greedy(cfg, w, tok, [P0], kc.copy(), vc.copy(), steps)
+    assert got == ref["tokens"][:, 0].tolist()
+
+
+def test_bad_token_is_a_device_error_not_a_hang():
+    cfg = synth.configs.TINY
+    w, kc, vc, tok, pos = _setup(cfg, 256, 10)
+    run = Runner(cfg, w, 1, 256, kc, vc)
+    run.step(np.array([cfg.vocab], np.int32), pos)
+    torch.cuda.synchronize()
+    err = mk.mk_check_device_error(run.h)
+    assert err is not None and "out of range" in err
+    run.step(np.array([cfg.vocab - 1], np.int32), np.array([256], np.int32))
+    err = mk.mk_check_device_error(run.h)
+    assert err is not None and "out of range" in err
+    # the handle is re-armed: a valid step works afterwards
+    run.step(tok, pos)
+    run.check()
+    run.close()
+
+
+def test_dropped_signal_is_reported_with_its_event():
+    cfg = synth.configs.TINY
+    w, kc, vc, tok, pos = _setup(cfg, 256, 10)
+    # plan once to pick a task in the middle of layer 1 that signals an event
+    probe = Runner(cfg, w, 1, 256, kc, vc)
+    tasks = probe.graph["tasks"]
+    probe.close()
+    victim = int(np.nonzero((tasks["layer"] == 1) & (tasks["op"] == mk.OP_OPROJ))[0][0])
+    run = Runner(cfg, w, 1, 256, kc, vc, debug_drop_signal=victim, debug_timeout_ms=20)
+    run.step(tok, pos)
+    torch.cuda.synchronize()
+    err = mk.mk_check_device_error(run.h)
+    print(err)
+    assert err is not None and "timeout" in err
+    assert f"event {int(tasks['sig_ev'][victim])}" in err
+    run.close()
+
+
+def test_grid_larger_than_the_device_is_refused():
+    cfg = synth.configs.TINY
+    w, kc, vc, tok, pos = _setup(cfg, 256, 10)
+    with pytest.raises(mk.MkError) as ei:
+        Runner(cfg, w, 1, 256, kc, vc, n_workgroups=100000)
+    assert ei.value.status == mk.MK_E_NOT_RESIDENT
