@@ -57,6 +57,51 @@ def cpu_baseline(cfg, w, kc, vc, tok, P0, budget_s=10.0):
                 sample=f"{n} greedy decode steps of the same workload from position {P0} ({dt:.1f} s)"), first
 
 
+def baseline_leg(mk, torch, cfg, model, kc, vc, tok, P0, C, K, W, mk_ms):
+    """The one-kernel-per-op HIP baseline on the same inputs: plain launches and a replayed HIP graph."""
+    hb = mk.mkb_create(model.desc, 1, C)
+    kv = torch.from_numpy(np.concatenate([kc.reshape(-1), vc.reshape(-1)]).view(np.int16)).cuda()
+    logits = torch.empty(cfg.vocab, dtype=torch.float32, device="cuda")
+    tokb = torch.tensor(tok, dtype=torch.int32, device="cuda")
+    posb = torch.tensor([P0], dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def reset():
+        tokb.fill_(int(tok[0]))
+        posb.fill_(P0)
+        torch.cuda.synchronize()
+
+    def step():
+        mk.mkb_decode_step(hb, tokb.data_ptr(), posb.data_ptr(), kv.data_ptr(), logits.data_ptr(),
+                           torch.cuda.current_stream().cuda_stream, 1)
+
+    def timed(fn):
+        reset()
+        for _ in range(W):
+            fn()
+        reset()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(K):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / K
+
+    ms_stream = timed(step)
+    g = torch.cuda.CUDAGraph()
+    reset()
+    with torch.cuda.graph(g):
+        step()
+    ms_graph = timed(g.replay)
+    mk.mkb_destroy(hb)
+    best = min(ms_stream, ms_graph)
+    return {"us_per_step_stream": round(ms_stream * 1000, 2), "us_per_step_graph": round(ms_graph * 1000, 2),
+            "launches_per_step": 9 * cfg.n_layers + 5,
+            "megakernel_speedup_vs_best": round(best / mk_ms, 3)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -157,6 +202,9 @@ def main():
                      "algorithmic_bytes_per_step": int(bytes_mean)},
     }
     mk.mk_destroy(h)
+
+    if not args.no_baseline:
+        out["multi_kernel_baseline"] = baseline_leg(mk, torch, cfg, model, kc, vc, tok, P0, C, K, W, ms)
     del dev, model
 
     if not args.no_cpu_baseline:
