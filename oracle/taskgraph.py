@@ -1,5 +1,51 @@
-"""ORACLE — test infrastructure only: the independent definition of the task
-graph, its event counters and the per-CU queues (filled in with the builder)."""
+"""ORACLE — test infrastructure only.
+
+Independent definition of the task graph the megakernel interprets: which tile
+tasks exist, which event each one waits on and signals, how many producers
+(targets) each event has, how the weight tiles are laid out, and how tasks are
+placed on per-workgroup queues.  The C++ builder of the library must export
+exactly this graph (bit for bit); the checker and the interleaving simulator
+below verify the properties any such graph must have.
+
+Vocabulary of the pages: tasks are the rectangles and events the circles of
+MPK's task graph; a task's trigger edge goes to the event it completes, an
+event's dependency edges go to the tasks it releases (MPK news page, part 1);
+events are integer counters that a finishing task increments and a starting
+task waits on until they reach their target (Hazy Research megakernel news
+page, section 4, "synchronisation").  Static queues are per-workgroup lists
+fixed before launch, the dynamic queue is one global list claimed by atomic
+pops (koas-w.github.io notes, "static and dynamic scheduling").
+
+The tiling rules (written from the design, not from the C++ code):
+  * QKV tiles: 8 RoPE pairs (16 weight rows: 8 first halves then 8 second
+    halves) of one head; heads ordered by KV group: the group's query heads,
+    its key head, its value head; pair blocks in order.
+  * attention: attn_splits chunks per (sequence, KV group), default
+    clamp(ceil(max_ctx / 256), 1, 16), at most max_ctx.
+  * O-proj tiles: (KV group g, row block) over columns g*grp*d .. +grp*d, with
+    o_rows = min(h, 1024, max(8, pow2_floor(h * n_kv / W))).
+  * down tiles: (K block of kd = min(1024, f) columns, row block of
+    d_rows = min(h, 1024, max(8, pow2_floor(h * (f / kd) / W))) rows).
+  * gate/up tiles: g_rows gate rows then the same g_rows up rows, with
+    g_rows = min(kd, 512, max(4, pow2_ceil(ceil(f / W)))).
+  * LM head tiles: lm_rows = min(1024, ceil(V / W)) rows, the last one shorter.
+  * per layer the events are created in the order qkv[g], attn[g], xb, m[kb],
+    x_next; tasks in the order QKV, attention, O-proj, gate/up, down; then the
+    LM-head tiles.  An event with more than 32 producers uses 8 sub-counters.
+  * packed weights: gains ((2L+1) rows of h), embedding, LM head (if untied),
+    then per layer QKV, O, gate/up, down regions, each region padded to 256 B,
+    tiles inside a region in task order.
+  * static queues: round-robin (task i -> workgroup i mod W) or least-loaded
+    (cost = weight bytes + 8192, ties to the lowest workgroup); the dynamic
+    queue is the task order itself.
+"""
+import math
+
+import numpy as np
+
+OP_QKV, OP_ATTN, OP_OPROJ, OP_GATEUP, OP_DOWN, OP_LMHEAD = 1, 2, 3, 4, 5, 6
+NONE = 0xFFFFFFFF
+TF_RESID = 1
 
 
 def idle_units_in_last_wave(n_tasks, n_units):
@@ -7,3 +53,373 @@ def idle_units_in_last_wave(n_tasks, n_units):
     waves over n_units units (the tail effect of a one-kernel-per-op launch)."""
     rem = n_tasks % n_units
     return 0 if rem == 0 else n_units - rem
+
+
+def _pow2_floor(x):
+    p = 1
+    while p * 2 <= x:
+        p *= 2
+    return p
+
+
+def _pow2_ceil(x):
+    p = 1
+    while p < x:
+        p *= 2
+    return p
+
+
+def _pad(x):
+    return (x + 255) // 256 * 256
+
+
+def tiling(cfg, B, C, W, attn_splits=0):
+    h, nq, nkv, d, f, V = cfg.hidden, cfg.n_q, cfg.n_kv, cfg.head_dim, cfg.ffn, cfg.vocab
+    grp = nq // nkv
+    S = attn_splits if attn_splits > 0 else max(1, min(16, -(-C // 256)))
+    S = min(S, C)
+    kd = min(1024, f)
+    return dict(grp=grp, pairs=8, S=S,
+                o_rows=min(h, 1024, max(8, _pow2_floor(h * nkv // W))),
+                kd=kd, d_rows=min(h, 1024, max(8, _pow2_floor(h * (f // kd) // W))),
+                g_rows=min(kd, 512, max(4, _pow2_ceil(-(-f // W)))),
+                lm_rows=min(1024, -(-V // W)))
+
+
+def layout(cfg, tied):
+    h, L = cfg.hidden, cfg.n_layers
+    at = 0
+    lay = {"gains": at}
+    at = _pad(at + (2 * L + 1) * h * 2)
+    lay["embed"] = at
+    at = _pad(at + cfg.vocab * h * 2)
+    if tied:
+        lay["lm"] = lay["embed"]
+    else:
+        lay["lm"] = at
+        at = _pad(at + cfg.vocab * h * 2)
+    lay["layer0"] = at
+    x = 0
+    lay["qkv"] = x
+    x = _pad(x + (cfg.n_q + 2 * cfg.n_kv) * cfg.head_dim * h * 2)
+    lay["o"] = x
+    x = _pad(x + h * cfg.n_q * cfg.head_dim * 2)
+    lay["gu"] = x
+    x = _pad(x + 2 * cfg.ffn * h * 2)
+    lay["down"] = x
+    x = _pad(x + h * cfg.ffn * 2)
+    lay["layer_bytes"] = x
+    return lay
+
+
+def build(cfg, B, C, W, policy=0, attn_splits=0):
+    """The task graph as a list of task dicts plus event targets, sub-counter
+    counts, static queues and the dynamic order."""
+    t = tiling(cfg, B, C, W, attn_splits)
+    lay = layout(cfg, cfg.tied)
+    h, nq, nkv, d, f, L = cfg.hidden, cfg.n_q, cfg.n_kv, cfg.head_dim, cfg.ffn, cfg.n_layers
+    grp, P, S = t["grp"], t["pairs"], t["S"]
+    n_kb = f // t["kd"]
+    tasks, target = [], []
+
+    def event():
+        target.append(0)
+        return len(target) - 1
+
+    def task(**k):
+        rec = dict(op=0, flags=0, layer=0, part=0, row0=0, nrows=0, wait_ev=NONE, sig_ev=NONE, wbytes=0, wofs=0,
+                   seq=0)
+        rec.update(k)
+        rec["id"] = len(tasks)
+        if rec["sig_ev"] != NONE:
+            target[rec["sig_ev"]] += 1
+        tasks.append(rec)
+
+    ev_x = NONE
+    for l in range(L):
+        base = lay["layer0"] + l * lay["layer_bytes"]
+        ev_qkv = [event() for _ in range(nkv)]
+        ev_attn = [event() for _ in range(nkv)]
+        ev_xb = event()
+        ev_m = [event() for _ in range(n_kb)]
+        ev_next = event()
+        tile = 0
+        wb = 2 * P * h * 2
+        for g in range(nkv):
+            heads = [g * grp + s for s in range(grp)] + [nq + g, nq + nkv + g]
+            for slot in heads:
+                for pb in range(d // 2 // P):
+                    task(op=OP_QKV, layer=l, part=slot, row0=pb * P, nrows=P, wait_ev=ev_x, sig_ev=ev_qkv[g],
+                         wbytes=wb, wofs=base + lay["qkv"] + tile * wb)
+                    tile += 1
+        for b in range(B):
+            for g in range(nkv):
+                for c in range(S):
+                    task(op=OP_ATTN, layer=l, part=g, row0=c, nrows=grp, seq=b, wait_ev=ev_qkv[g], sig_ev=ev_attn[g])
+        wb = t["o_rows"] * grp * d * 2
+        for g in range(nkv):
+            for rb in range(h // t["o_rows"]):
+                task(op=OP_OPROJ, layer=l, part=g, row0=rb * t["o_rows"], nrows=t["o_rows"],
+                     flags=TF_RESID if g == 0 else 0, wait_ev=ev_attn[g], sig_ev=ev_xb, wbytes=wb,
+                     wofs=base + lay["o"] + (g * (h // t["o_rows"]) + rb) * wb)
+        wb = 2 * t["g_rows"] * h * 2
+        for i in range(f // t["g_rows"]):
+            task(op=OP_GATEUP, layer=l, row0=i * t["g_rows"], nrows=t["g_rows"], wait_ev=ev_xb,
+                 sig_ev=ev_m[i * t["g_rows"] // t["kd"]], wbytes=wb, wofs=base + lay["gu"] + i * wb)
+        wb = t["d_rows"] * t["kd"] * 2
+        for kb in range(n_kb):
+            for rb in range(h // t["d_rows"]):
+                task(op=OP_DOWN, layer=l, part=kb, row0=rb * t["d_rows"], nrows=t["d_rows"],
+                     flags=TF_RESID if kb == 0 else 0, wait_ev=ev_m[kb], sig_ev=ev_next, wbytes=wb,
+                     wofs=base + lay["down"] + (kb * (h // t["d_rows"]) + rb) * wb)
+        ev_x = ev_next
+    n_lm = -(-cfg.vocab // t["lm_rows"])
+    for i in range(n_lm):
+        rows = min(t["lm_rows"], cfg.vocab - i * t["lm_rows"])
+        task(op=OP_LMHEAD, layer=L, row0=i * t["lm_rows"], nrows=rows, wait_ev=ev_x, wbytes=rows * h * 2,
+             wofs=lay["lm"] + i * t["lm_rows"] * h * 2)
+    nsub = [8 if n > 32 else 1 for n in target]
+    for k in tasks:
+        k["wait_target"] = target[k["wait_ev"]] if k["wait_ev"] != NONE else 0
+        k["wait_nsub"] = nsub[k["wait_ev"]] if k["wait_ev"] != NONE else 1
+        k["sig_nsub"] = nsub[k["sig_ev"]] if k["sig_ev"] != NONE else 1
+    queues = [[] for _ in range(W)]
+    if policy == 0:
+        for i in range(len(tasks)):
+            queues[i % W].append(i)
+    else:
+        load = [0] * W
+        for i, k in enumerate(tasks):
+            w = min(range(W), key=lambda j: (load[j], j))
+            load[w] += k["wbytes"] + 8192
+            queues[w].append(i)
+    return dict(tiling=t, layout=lay, tasks=tasks, target=target, nsub=nsub, queues=queues,
+                order=list(range(len(tasks))))
+
+
+# ---- checker (properties every valid graph has) -----------------------------------------
+
+def check(g, cfg, B):
+    """Checks coverage, targets, dependency soundness, queue validity; raises AssertionError."""
+    tasks, target = g["tasks"], g["target"]
+    consumers = {}
+    for k in tasks:
+        if k["wait_ev"] != NONE:
+            consumers.setdefault(k["wait_ev"], []).append(k["id"])
+    h, nq, nkv, d, f, L, V = cfg.hidden, cfg.n_q, cfg.n_kv, cfg.head_dim, cfg.ffn, cfg.n_layers, cfg.vocab
+    grp = nq // nkv
+    # G2 targets = producers
+    prod = [0] * len(target)
+    for k in tasks:
+        if k["sig_ev"] != NONE:
+            prod[k["sig_ev"]] += 1
+    assert prod == list(target), "event targets differ from producer counts"
+    for k in tasks:
+        if k["wait_ev"] != NONE:
+            assert k["wait_target"] == target[k["wait_ev"]]
+    # G1 coverage
+    for l in range(L):
+        lt = [k for k in tasks if k["layer"] == l]
+        cov = np.zeros((nq + 2 * nkv, d // 2), int)
+        for k in lt:
+            if k["op"] == OP_QKV:
+                cov[k["part"], k["row0"]:k["row0"] + k["nrows"]] += 1
+        assert (cov == 1).all(), "QKV pairs not covered exactly once"
+        o = np.zeros((h, nkv), int)
+        for k in lt:
+            if k["op"] == OP_OPROJ:
+                o[k["row0"]:k["row0"] + k["nrows"], k["part"]] += 1
+        assert (o == 1).all(), "O-proj (row, group) not covered exactly once"
+        gu = np.zeros(f, int)
+        for k in lt:
+            if k["op"] == OP_GATEUP:
+                gu[k["row0"]:k["row0"] + k["nrows"]] += 1
+        assert (gu == 1).all(), "gate/up rows not covered exactly once"
+        kd = g["tiling"]["kd"]
+        dn = np.zeros((h, f // kd), int)
+        for k in lt:
+            if k["op"] == OP_DOWN:
+                dn[k["row0"]:k["row0"] + k["nrows"], k["part"]] += 1
+        assert (dn == 1).all(), "down (row, K block) not covered exactly once"
+        at = np.zeros((B, nkv, g["tiling"]["S"]), int)
+        for k in lt:
+            if k["op"] == OP_ATTN:
+                at[k["seq"], k["part"], k["row0"]] += 1
+        assert (at == 1).all(), "attention chunks not covered exactly once"
+        # exactly one residual-adding tile per O-proj / down row
+        r1 = np.zeros(h, int)
+        r2 = np.zeros(h, int)
+        for k in lt:
+            if k["op"] == OP_OPROJ and k["flags"] & TF_RESID:
+                r1[k["row0"]:k["row0"] + k["nrows"]] += 1
+            if k["op"] == OP_DOWN and k["flags"] & TF_RESID:
+                r2[k["row0"]:k["row0"] + k["nrows"]] += 1
+        assert (r1 == 1).all() and (r2 == 1).all(), "residual added more or less than once"
+    lm = np.zeros(V, int)
+    for k in tasks:
+        if k["op"] == OP_LMHEAD:
+            lm[k["row0"]:k["row0"] + k["nrows"]] += 1
+    assert (lm == 1).all(), "LM-head rows not covered exactly once"
+    # G3 soundness: every reader starts after every writer of what it reads, through the event edges
+    hb_sets = ancestor_sets(g)
+    by = {}
+    for k in tasks:
+        by.setdefault((k["op"], k["layer"]), []).append(k)
+    kd = g["tiling"]["kd"]
+
+    def ids(op, layer, pred=lambda w: True):
+        return {w["id"] for w in by.get((op, layer), []) if pred(w)}
+
+    def group_of_slot(s):
+        return s // grp if s < nq else (s - nq) % nkv
+
+    checked = set()
+    for k in tasks:
+        l, op = k["layer"], k["op"]
+        key = (op, l, k["part"] if op in (OP_ATTN, OP_OPROJ, OP_DOWN) else 0, k["wait_ev"])
+        if key in checked:
+            continue
+        checked.add(key)
+        need = set()
+        if op == OP_QKV and l > 0:
+            need = ids(OP_DOWN, l - 1)
+        elif op == OP_ATTN:
+            need = ids(OP_QKV, l, lambda w: group_of_slot(w["part"]) == k["part"])
+        elif op == OP_OPROJ:
+            need = ids(OP_ATTN, l, lambda w: w["part"] == k["part"]) | (ids(OP_DOWN, l - 1) if l > 0 else set())
+        elif op == OP_GATEUP:
+            need = ids(OP_OPROJ, l)
+        elif op == OP_DOWN:
+            need = ids(OP_GATEUP, l, lambda w: w["row0"] // kd == k["part"]) | ids(OP_OPROJ, l)
+        elif op == OP_LMHEAD and L > 0:
+            need = ids(OP_DOWN, L - 1)
+        anc = hb_sets(k["id"])
+        missing = need - anc
+        assert not missing, f"task {k['id']} may start before its producer(s) {sorted(missing)[:4]}"
+    # buffers reused from one layer to the next (q/k/v, attention partials, m): every reader of
+    # layer l happens before every writer of layer l+1
+    for l in range(L - 1):
+        for rop, wop in ((OP_ATTN, OP_QKV), (OP_OPROJ, OP_ATTN), (OP_DOWN, OP_GATEUP)):
+            rs = ids(rop, l)
+            for w in by.get((wop, l + 1), []):
+                missing = rs - hb_sets(w["id"])
+                assert not missing, f"writer {w['id']} of layer {l + 1} may overtake readers {sorted(missing)[:4]}"
+    # G4 queues: every task exactly once, each queue in increasing (topological) order
+    seen = sorted(i for q in g["queues"] for i in q)
+    assert seen == list(range(len(tasks))), "static queues do not hold every task exactly once"
+    for q in g["queues"]:
+        assert all(a < b for a, b in zip(q, q[1:])), "a static queue is not in task order"
+    assert list(g["order"]) == list(range(len(tasks))), "the dynamic order is not the task order"
+    for k in tasks:
+        if k["sig_ev"] != NONE:
+            for c in consumers.get(k["sig_ev"], []):
+                assert k["id"] < c, "a producer comes after its consumer in the task order"
+    # G5 weights: the tiles of each packed region cover it exactly, without overlap
+    lay = g.get("layout")
+    if lay is None:
+        return
+    spans = sorted((k["wofs"], k["wbytes"], k["op"]) for k in tasks if k["wbytes"] and k["op"] != OP_LMHEAD)
+    pos = lay["layer0"]
+    for ofs, nb, op in spans:
+        assert ofs == pos or (ofs > pos and ofs - pos < 256), f"gap or overlap in packed weights at {ofs}"
+        pos = ofs + nb
+    assert pos <= lay["layer0"] + L * lay["layer_bytes"]
+    lm = sorted((k["wofs"], k["wbytes"]) for k in tasks if k["op"] == OP_LMHEAD)
+    pos = lay["lm"]
+    for ofs, nb in lm:
+        assert ofs == pos
+        pos += nb
+    assert pos == lay["lm"] + V * h * 2
+
+
+def ancestor_sets(g):
+    """Returns anc(i): the set of tasks that finish before task i can start, through event edges."""
+    tasks = g["tasks"]
+    producers = {}
+    for k in tasks:
+        if k["sig_ev"] != NONE:
+            producers.setdefault(k["sig_ev"], []).append(k["id"])
+    memo = {}
+    # events are created in topological order, so one forward pass fills the table
+    for e in range(len(g["target"])):
+        s = set()
+        for p in producers.get(e, []):
+            s.add(p)
+            we = tasks[p]["wait_ev"]
+            if we != NONE:
+                assert we < e, "an event waits on a later event"
+                s |= memo[we]
+        memo[e] = frozenset(s)
+    return lambda i: memo[tasks[i]["wait_ev"]] if tasks[i]["wait_ev"] != NONE else frozenset()
+
+
+def simulate(g, W, seed=0, slow=None, dynamic=False, lookahead=2):
+    """Runs the graph on W virtual workgroups under a seeded random interleaving.
+
+    Static: each workgroup runs its queue in order.  Dynamic: a workgroup claims
+    the next task of the global order whenever it holds fewer than `lookahead`
+    claimed tasks (the loader claims ahead of the compute waves), and runs its
+    oldest claimed task.  A task may run once its event counter has reached its
+    target.  `slow`: a workgroup that only moves when no other one can.
+    Returns the number of tasks that ran (all of them unless the graph deadlocks).
+    """
+    rng = np.random.default_rng(seed)
+    tasks = g["tasks"]
+    ctr = [0] * len(g["target"])
+    if dynamic:
+        order = list(g["order"])
+        nxt = 0
+        held = [[] for _ in range(W)]
+    else:
+        queues = [list(q) for q in g["queues"]]
+        pos = [0] * W
+    done = 0
+
+    def head(w):
+        if dynamic:
+            return held[w][0] if held[w] else None
+        return queues[w][pos[w]] if pos[w] < len(queues[w]) else None
+
+    while True:
+        moves = []
+        for w in range(W):
+            i = head(w)
+            if i is not None:
+                k = tasks[i]
+                if k["wait_ev"] == NONE or ctr[k["wait_ev"]] >= k["wait_target"]:
+                    moves.append((w, "run"))
+            if dynamic and len(held[w]) < lookahead and nxt < len(order):
+                moves.append((w, "claim"))
+        if not moves:
+            break
+        if slow is not None:
+            others = [m for m in moves if m[0] != slow]
+            if others:
+                moves = others
+        w, what = moves[rng.integers(len(moves))]
+        if what == "claim":
+            held[w].append(order[nxt])
+            nxt += 1
+            continue
+        if dynamic:
+            i = held[w].pop(0)
+        else:
+            i = queues[w][pos[w]]
+            pos[w] += 1
+        k = tasks[i]
+        if k["sig_ev"] != NONE:
+            ctr[k["sig_ev"]] += 1
+        done += 1
+    return done
+
+
+def from_export(ex):
+    """The library's exported graph in this module's dict form (for check and simulate)."""
+    hd = ex["header"]
+    names = ex["tasks"].dtype.names
+    tasks = [{n: int(r[n]) for n in names} for r in ex["tasks"]]
+    qo = ex["queue_off"]
+    queues = [list(map(int, ex["queue"][qo[w]:qo[w + 1]])) for w in range(hd["W"])]
+    return dict(tasks=tasks, target=list(map(int, ex["target"])), nsub=list(map(int, ex["nsub"])),
+                queues=queues, order=list(map(int, ex["order"])),
+                tiling=dict(kd=hd["kd"], S=hd["attn_splits"]), layout=None)
