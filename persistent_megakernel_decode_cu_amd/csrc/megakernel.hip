@@ -44,7 +44,10 @@ constexpr int FIFO = 16;               // task records in flight in LDS
 constexpr int XS = MAX_ACT;            // activation staging (floats)
 constexpr int ROWRES = MAX_TILE_ROWS;  // per-task row results (floats)
 constexpr int LPP = 16 / NLW;          // loads per page per loader wave
-constexpr int MAX_INFLIGHT = 6;        // pages in flight per loader wave (6 * 8 loads < 64 = vmcnt range)
+// Pages in flight per loader wave.  48 KiB in flight per CU (12 MiB over the chip)
+// already keeps HBM busy; a deeper queue only adds queueing delay to every other
+// load, including the small latency-critical ones between dependent tasks.
+constexpr int MAX_INFLIGHT = 3;
 constexpr int DYNQ = 64;               // popped task ids shared between the loader waves (dynamic queue)
 constexpr int MAXB = 64;               // sequences per step held in LDS
 
@@ -64,6 +67,7 @@ struct __attribute__((aligned(16))) Smem {
     uint32_t dyn_tid[DYNQ];
     uint32_t dyn_ready, dyn_ack;
     uint32_t go, cbar, done, abort;
+    uint32_t cgen[NCW];  // compute-wave barrier generation (per wave)
     uint32_t t_ready_lo, t_ready_hi;
     uint32_t tm[4];  // trace: low 32 bits of the clock after staging / after the GEMV
 };
@@ -90,6 +94,28 @@ __device__ __forceinline__ CParams& P(const Params* pp) {
     uint64_t v = (uint64_t)pp;
     uint32_t lo = uni((uint32_t)v), hi = uni((uint32_t)(v >> 32));
     return *(CParams*)(((uint64_t)hi << 32) | lo);
+}
+
+// Plain global loads/stores through the global address space (generic pointers
+// would give flat instructions, which also count against lgkmcnt).
+template <class T>
+__device__ __forceinline__ T gld(const T* ptr) {
+    return *(const __attribute__((address_space(1))) T*)ptr;
+}
+template <class T>
+__device__ __forceinline__ void gst(T* ptr, T v) {
+    *(__attribute__((address_space(1))) T*)ptr = v;
+}
+// vector types (HIP's uint4/float2 are classes): load through clang vector types
+__device__ __forceinline__ uint4 gld_u4(const void* ptr) {
+    typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+    const v4u v = *(const __attribute__((address_space(1))) v4u*)ptr;
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float2 gld_f2(const void* ptr) {
+    typedef float v2f __attribute__((ext_vector_type(2)));
+    const v2f v = *(const __attribute__((address_space(1))) v2f*)ptr;
+    return make_float2(v.x, v.y);
 }
 
 __device__ __forceinline__ uint32_t lds_ld(const uint32_t& x) { return *(lds_u32*)&x; }
@@ -291,14 +317,17 @@ __device__ __forceinline__ uint32_t task_pages(const Task& k, int32_t splits, in
 
 // ---- loader wave ---------------------------------------------------------------------
 
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds_off) {
+// 16 bytes per lane from global memory straight into LDS, non-temporal: weights
+// and KV rows are read once per step, so they are marked evict-first in L2.
+constexpr int CPOL_NT = 2;
+__device__ __forceinline__ void dma16(const void* src, uint8_t* lds) {
     __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)src,
-                                     (__attribute__((address_space(3))) void*)((uint8_t*)&ring[0][0] + lds_off), 16, 0,
-                                     0);
+                                     (__attribute__((address_space(3))) void*)lds, 16, 0, CPOL_NT);
 }
 
+// The LPP loads of loader wave lw for page kp of task k into ring slot `slot`.
 __device__ __forceinline__ void issue_page(CParams& p, const Task& k, uint32_t kp, uint32_t slot, int lane, int lw) {
-    const uint32_t dst = slot * PAGE;
+    uint8_t* const dst = &ring[slot][0];
     if (k.op == OP_ATTN) {
         const int32_t d = p.T.d;
         const Chunk ch = attn_chunk(p.T.attn_splits, seq_pos(k.seq), k.row0);
@@ -425,7 +454,7 @@ __device__ __noinline__ void loader(const Params* pp, uint32_t epoch, int lw) {
         for (uint32_t kp = 0; kp < np; ++kp) {
             const uint32_t ps = pseq % NPAGES;
             const uint32_t need = NCW * (pseq / NPAGES);
-            if (lds_ld(S.page_free[ps]) < need) {
+            while (lds_ld(S.page_free[ps]) < need) {
                 drain();
                 if (!uni(lds_wait_ge(S.page_free[ps], need, pp, ti))) goto out;
             }
@@ -450,14 +479,32 @@ struct Ctx {
     int wave, lane, tid;  // compute wave, lane, thread index among the compute lanes
     uint32_t t;           // task sequence number of this workgroup
     uint32_t epoch, parity;
-    uint32_t* cgen;       // compute-wave barrier generation
 };
 
+// The task record of FIFO slot `slot`, read from LDS into wave-uniform registers.
+__device__ __forceinline__ Task fifo_task(uint32_t slot) {
+    Task k;
+#pragma unroll
+    for (int i = 0; i < 12; ++i) ((uint32_t*)&k)[i] = uni(lds_ld(((const uint32_t*)&S.fifo[uni(slot)])[i]));
+    return k;
+}
+__device__ __forceinline__ Ctx make_ctx(uint32_t t, uint32_t epoch) {
+    Ctx c;
+    c.wave = (int)uni(threadIdx.x >> 6);
+    c.lane = threadIdx.x & 63;
+    c.tid = c.wave * 64 + c.lane;
+    c.t = uni(t);
+    c.epoch = uni(epoch);
+    c.parity = c.epoch & 1u;
+    return c;
+}
+
 __device__ __forceinline__ bool cbarrier(const Params* pp, Ctx& c, uint32_t task) {
-    *c.cgen += NCW;
+    const uint32_t gen = uni(lds_ld(S.cgen[c.wave])) + NCW;
+    if (c.lane == 0) lds_st(S.cgen[c.wave], gen);
     lgkm_wait_all();
     if (c.lane == 0) lds_add(S.cbar, 1u);
-    return lds_wait_ge(S.cbar, *c.cgen, pp, task);
+    return lds_wait_ge(S.cbar, gen, pp, task);
 }
 
 __device__ __forceinline__ bool page_acquire(const Params* pp, uint32_t seq, uint32_t task) {
@@ -528,7 +575,7 @@ __device__ __forceinline__ void stage_bf16(int dst, const uint16_t* src, int n, 
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
         const int i = (tid + q * NCW * 64) * 8;
-        v[q] = i < n ? *(const uint4*)(src + i) : make_uint4(0, 0, 0, 0);
+        v[q] = i < n ? gld_u4(src + i) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -571,7 +618,7 @@ __device__ __forceinline__ void load_x(int xo, int lane, float scale, const uint
 template <int KT>
 __device__ __forceinline__ void load_gains(const uint16_t* g, int lane, uint4* gw) {
 #pragma unroll
-    for (int j = 0; j < KT / 512; ++j) gw[j] = *(const uint4*)(g + j * 512 + lane * 8);
+    for (int j = 0; j < KT / 512; ++j) gw[j] = gld_u4(g + j * 512 + lane * 8);
 }
 
 // 1/sqrt(mean(xs[0..n)^2) + eps), computed by each wave from LDS
@@ -584,57 +631,81 @@ __device__ __forceinline__ float rms_scale(int n, float eps, int lane) {
     return 1.0f / sqrtf(wave_sum(ss) / (float)n + eps);
 }
 
+// ---- GEMV over LDS pages --------------------------------------------------------------
+
 // y[r] = W[r, :] . x over the task's rows; weights in consecutive LDS pages from
-// page sequence `page0`; results in S.rowres[r].  Wave w computes the pages
-// pg = w (mod NCW) and releases the others untouched: every compute wave
-// releases every page of the task exactly once.
+// page sequence `page0`; results in S.rowres[r].  Every compute wave takes its
+// share of every page (KT <= 2048: whole rows, KT < 512: a quarter of the 1 KiB
+// row groups), so a page is consumed as soon as it lands and the work left after
+// the last page is a quarter page per wave.  KT = 4096 (2 rows per page): wave w
+// computes the pages pg = w (mod NCW).  Each wave releases every page once.
 template <int KT>
 __device__ __forceinline__ bool gemv_pages(const Params* pp, int wave, int lane, uint32_t page0, uint32_t nrows,
                                            uint32_t wbytes, const float* x, uint32_t task) {
     const uint32_t npages = (wbytes + PAGE - 1) / PAGE;
-    for (uint32_t pg = 0; pg < npages; ++pg) {
-        if ((int)(pg % NCW) != wave) {
-            page_skip(page0 + pg, lane);
-            continue;
-        }
-        if (!page_acquire(pp, page0 + pg, task)) return false;
-        const uint32_t slot = (page0 + pg) % NPAGES;
-        if constexpr (KT >= 512) {
-            constexpr int RB = 2 * KT;      // bytes per row
-            constexpr int RPP = PAGE / RB;  // rows per page
-            constexpr int LPR = KT / 512;   // 1 KiB wave loads per row
-            const uint32_t r_lo = pg * RPP;
-            // the whole page goes to registers first, so the page is handed back to
-            // the loader before the arithmetic
+    if constexpr (KT >= 4096) {
+        constexpr int RPP = PAGE / (2 * KT);  // rows per page
+        constexpr int LPR = KT / 512;         // 1 KiB wave loads per row
+        for (uint32_t pg = 0; pg < npages; ++pg) {
+            if ((int)(pg % NCW) != wave) {
+                page_skip(page0 + pg, lane);
+                continue;
+            }
+            if (!page_acquire(pp, page0 + pg, task)) return false;
+            const uint32_t slot = (page0 + pg) % NPAGES;
             uint4 wv[RPP * LPR];
 #pragma unroll
             for (int i = 0; i < RPP * LPR; ++i) wv[i] = *(const uint4*)&ring[slot][i * 1024 + lane * 16];
             page_release(page0 + pg, lane);
-            float acc[RPP];
 #pragma unroll
             for (int rr = 0; rr < RPP; ++rr) {
+                float a = 0.f, b = 0.f;
+#pragma unroll
+                for (int j = 0; j < LPR; j += 2) {
+                    a = dot8(wv[rr * LPR + j], x + j * 8, a);
+                    b = dot8(wv[rr * LPR + j + 1], x + (j + 1) * 8, b);
+                }
+                const float sum = wave_sum(a + b);
+                const uint32_t r = pg * RPP + rr;
+                if (lane == 0 && r < nrows) S.rowres[r] = sum;
+            }
+        }
+    } else if constexpr (KT >= 512) {
+        constexpr int RPP = PAGE / (2 * KT);  // 4, 8 or 16 rows per page
+        constexpr int RW = RPP / NCW;         // rows of each page for each wave
+        constexpr int LPR = KT / 512;
+        for (uint32_t pg = 0; pg < npages; ++pg) {
+            if (!page_acquire(pp, page0 + pg, task)) return false;
+            const uint32_t slot = (page0 + pg) % NPAGES;
+            uint4 wv[RW * LPR];
+#pragma unroll
+            for (int i = 0; i < RW * LPR; ++i) wv[i] = *(const uint4*)&ring[slot][(wave * RW * LPR + i) * 1024 + lane * 16];
+            page_release(page0 + pg, lane);
+#pragma unroll
+            for (int rr = 0; rr < RW; ++rr) {
                 float a = 0.f;
 #pragma unroll
                 for (int j = 0; j < LPR; ++j) a = dot8(wv[rr * LPR + j], x + j * 8, a);
-                acc[rr] = a;
+                const float sum = wave_sum(a);
+                const uint32_t r = pg * RPP + wave * RW + rr;
+                if (lane == 0 && r < nrows) S.rowres[r] = sum;
             }
+        }
+    } else {
+        constexpr int RPL = 1024 / (2 * KT);  // rows per 1 KiB load
+        constexpr int LPROW = 64 / RPL;       // lanes per row
+        constexpr int UW = 16 / NCW;          // 1 KiB groups of each page for each wave
+        for (uint32_t pg = 0; pg < npages; ++pg) {
+            if (!page_acquire(pp, page0 + pg, task)) return false;
+            const uint32_t slot = (page0 + pg) % NPAGES;
+            uint4 wv[UW];
 #pragma unroll
-            for (int rr = 0; rr < RPP; ++rr) {
-                const float a = wave_sum(acc[rr]);
-                if (lane == 0 && r_lo + rr < nrows) S.rowres[r_lo + rr] = a;
-            }
-        } else {
-            constexpr int RB = 2 * KT;
-            constexpr int RPL = 1024 / RB;   // rows per 1 KiB load
-            constexpr int LPROW = 64 / RPL;  // lanes per row
-            uint4 wv[16];
-#pragma unroll
-            for (int u = 0; u < 16; ++u) wv[u] = *(const uint4*)&ring[slot][u * 1024 + lane * 16];
+            for (int u = 0; u < UW; ++u) wv[u] = *(const uint4*)&ring[slot][(wave * UW + u) * 1024 + lane * 16];
             page_release(page0 + pg, lane);
 #pragma unroll
-            for (int u = 0; u < 16; ++u) {
+            for (int u = 0; u < UW; ++u) {
                 const float a = seg_sum<LPROW>(dot8(wv[u], x, 0.f));
-                const uint32_t r = (pg * 16 + u) * RPL + lane / LPROW;
+                const uint32_t r = (pg * 16 + wave * UW + u) * RPL + lane / LPROW;
                 if ((lane % LPROW) == 0 && r < nrows) S.rowres[r] = a;
             }
         }
@@ -664,7 +735,9 @@ __device__ __forceinline__ void stage_x(CParams& p, int l, uint32_t parity, int 
 // RMSNorm + QKV tile + RoPE + K/V append.  Tile rows [0, n) are the first halves
 // (j0 + i) of n RoPE pairs of one head, rows [n, 2n) the second halves (j0 + i + d/2).
 template <int KT>
-__device__ __noinline__ bool op_qkv(const Params* pp, const Task& k, uint32_t page0, Ctx c) {
+__device__ __noinline__ bool op_qkv(const Params* pp, uint32_t slot_, uint32_t page0, uint32_t t_, uint32_t epoch_) {
+    const Task k = fifo_task(slot_);
+    Ctx c = make_ctx(t_, epoch_);
     CParams& p = P(pp);
     const int lane = c.lane, tid = c.tid;
     const uint32_t n = k.nrows, slot = k.part;
@@ -673,7 +746,7 @@ __device__ __noinline__ bool op_qkv(const Params* pp, const Task& k, uint32_t pa
     uint4 gw[KT / 512 > 0 ? KT / 512 : 1];
     if constexpr (KT >= 512) load_gains<KT>(gains(p, 2 * k.layer), lane, gw);
     float2 cs = make_float2(1.f, 0.f);
-    if ((uint32_t)tid < n && slot < (uint32_t)(nq + nkv)) cs = p.rope[(size_t)P0 * half + k.row0 + tid];
+    if ((uint32_t)tid < n && slot < (uint32_t)(nq + nkv)) cs = gld_f2(p.rope + (size_t)P0 * half + k.row0 + tid);
     if (!await_inputs(pp, k, c)) return false;
     stage_x<(MAX_ACT + 1023) / 1024>(p, k.layer, c.parity, tid);
     if (!cbarrier(pp, c, k.id)) return false;
@@ -689,7 +762,7 @@ __device__ __noinline__ bool op_qkv(const Params* pp, const Task& k, uint32_t pa
             constexpr int LPROW = KT / 8;
             load_x<KT>(0, lane, r, nullptr, x);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) x[i] *= bf16f(g[(lane % LPROW) * 8 + i]);
+            for (int i = 0; i < 8; ++i) x[i] *= bf16f(gld(g + (lane % LPROW) * 8 + i));
         }
         if (!gemv_pages<KT>(pp, c.wave, lane, page0, 2 * n, k.wbytes, x, k.id)) return false;
     }
@@ -733,7 +806,9 @@ __device__ __noinline__ bool op_qkv(const Params* pp, const Task& k, uint32_t pa
 
 // Attention over one chunk of the context of (sequence, KV group): one wave per query head.
 template <int D>
-__device__ __noinline__ bool op_attn(const Params* pp, const Task& k, uint32_t page0, Ctx c) {
+__device__ __noinline__ bool op_attn(const Params* pp, uint32_t slot_, uint32_t page0, uint32_t t_, uint32_t epoch_) {
+    const Task k = fifo_task(slot_);
+    Ctx c = make_ctx(t_, epoch_);
     CParams& p = P(pp);
     const int lane = c.lane, wave = c.wave;
     const int b = (int)k.seq, g = k.part;
@@ -862,7 +937,9 @@ __device__ __noinline__ bool op_attn(const Params* pp, const Task& k, uint32_t p
 
 // Merge of the attention partials of one KV group, O-proj K-slice, residual (atomic add).
 template <int KT>
-__device__ __noinline__ bool op_oproj(const Params* pp, const Task& k, uint32_t page0, Ctx c) {
+__device__ __noinline__ bool op_oproj(const Params* pp, uint32_t slot_, uint32_t page0, uint32_t t_, uint32_t epoch_) {
+    const Task k = fifo_task(slot_);
+    Ctx c = make_ctx(t_, epoch_);
     CParams& p = P(pp);
     const int lane = c.lane, tid = c.tid, wave = c.wave;
     if (!await_inputs(pp, k, c)) return false;
@@ -875,7 +952,7 @@ __device__ __noinline__ bool op_oproj(const Params* pp, const Task& k, uint32_t 
         res[q] = 0.f;
         if ((k.flags & TF_RESID) && i < k.nrows) {
             const uint32_t row = k.row0 + i;
-            res[q] = k.layer == 0 ? bf16f(embed_row(p, 0)[row]) : ldf_dev(acc_buf(p, c.parity, 2 * k.layer - 1, 0) + row);
+            res[q] = k.layer == 0 ? bf16f(gld(embed_row(p, 0) + row)) : ldf_dev(acc_buf(p, c.parity, 2 * k.layer - 1, 0) + row);
         }
     }
     // a = sum_c e^(m_c - M) o_c / sum_c e^(m_c - M) l_c, one wave per query head
@@ -929,7 +1006,9 @@ __device__ __noinline__ bool op_oproj(const Params* pp, const Task& k, uint32_t 
 
 // RMSNorm + gate/up tile + SiLU(gate) * up.  Tile rows [0, n) gate, [n, 2n) up.
 template <int KT>
-__device__ __noinline__ bool op_gateup(const Params* pp, const Task& k, uint32_t page0, Ctx c) {
+__device__ __noinline__ bool op_gateup(const Params* pp, uint32_t slot_, uint32_t page0, uint32_t t_, uint32_t epoch_) {
+    const Task k = fifo_task(slot_);
+    Ctx c = make_ctx(t_, epoch_);
     CParams& p = P(pp);
     const int lane = c.lane, tid = c.tid;
     uint4 gw[KT / 512 > 0 ? KT / 512 : 1];
@@ -948,7 +1027,7 @@ __device__ __noinline__ bool op_gateup(const Params* pp, const Task& k, uint32_t
             constexpr int LPROW = KT / 8;
             load_x<KT>(0, lane, r, nullptr, x);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) x[i] *= bf16f(g[(lane % LPROW) * 8 + i]);
+            for (int i = 0; i < 8; ++i) x[i] *= bf16f(gld(g + (lane % LPROW) * 8 + i));
         }
         if (!gemv_pages<KT>(pp, c.wave, lane, page0, 2 * k.nrows, k.wbytes, x, k.id)) return false;
     }
@@ -963,7 +1042,9 @@ __device__ __noinline__ bool op_gateup(const Params* pp, const Task& k, uint32_t
 
 // Down-proj K-slice tile + residual (atomic add).
 template <int KT>
-__device__ __noinline__ bool op_down(const Params* pp, const Task& k, uint32_t page0, Ctx c) {
+__device__ __noinline__ bool op_down(const Params* pp, uint32_t slot_, uint32_t page0, uint32_t t_, uint32_t epoch_) {
+    const Task k = fifo_task(slot_);
+    Ctx c = make_ctx(t_, epoch_);
     CParams& p = P(pp);
     const int lane = c.lane, tid = c.tid;
     if (!await_inputs(pp, k, c)) return false;
@@ -994,7 +1075,9 @@ __device__ __noinline__ bool op_down(const Params* pp, const Task& k, uint32_t p
 
 // Final RMSNorm + LM-head tile + argmax (packed 64-bit atomic max).
 template <int KT>
-__device__ __noinline__ bool op_lmhead(const Params* pp, const Task& k, uint32_t page0, Ctx c) {
+__device__ __noinline__ bool op_lmhead(const Params* pp, uint32_t slot_, uint32_t page0, uint32_t t_, uint32_t epoch_) {
+    const Task k = fifo_task(slot_);
+    Ctx c = make_ctx(t_, epoch_);
     CParams& p = P(pp);
     const int lane = c.lane, tid = c.tid;
     uint4 gw[KT / 512 > 0 ? KT / 512 : 1];
@@ -1013,7 +1096,7 @@ __device__ __noinline__ bool op_lmhead(const Params* pp, const Task& k, uint32_t
             constexpr int LPROW = KT / 8;
             load_x<KT>(0, lane, r, nullptr, x);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) x[i] *= bf16f(g[(lane % LPROW) * 8 + i]);
+            for (int i = 0; i < 8; ++i) x[i] *= bf16f(gld(g + (lane % LPROW) * 8 + i));
         }
         if (!gemv_pages<KT>(pp, c.wave, lane, page0, k.nrows, k.wbytes, x, k.id)) return false;
     }
@@ -1024,7 +1107,7 @@ __device__ __noinline__ bool op_lmhead(const Params* pp, const Task& k, uint32_t
     float* logits = S.args.logits;
     for (uint32_t i = (uint32_t)tid; i < k.nrows; i += NCW * 64) {
         const float val = S.rowres[i];
-        if (logits) logits[k.row0 + i] = val;
+        if (logits) gst(logits + k.row0 + i, val);
         if (val > bv) {  // rows visited in increasing order: the first maximum is kept
             bv = val;
             bi = k.row0 + i;
@@ -1055,14 +1138,14 @@ __device__ __noinline__ void finish_step(const Params* pp, uint32_t epoch, uint3
     if (old + 1u != epoch * (uint32_t)p.T.n_lm_tiles) return;
     const unsigned long long key =
         __hip_atomic_load((g_u64*)&p.key[parity * p.T.B + 0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (lane == 0) p.next[0] = (int32_t)(0xffffffffu - (uint32_t)(key & 0xffffffffu));
+    if (lane == 0) gst(p.next, (int32_t)(0xffffffffu - (uint32_t)(key & 0xffffffffu)));
     const int h = p.T.h;
     if (p.T.L == 0) {
         const uint16_t* e = embed_row(p, 0);
-        for (int i = lane; i < h; i += 64) p.hidden[i] = bf16f(e[i]);
+        for (int i = lane; i < h; i += 64) gst(p.hidden + i, bf16f(gld(e + i)));
     } else {
         const float* src = acc_buf(p, parity, 2 * p.T.L - 1, 0);
-        for (int i = lane; i < h; i += 64) p.hidden[i] = ldf_dev(src + i);
+        for (int i = lane; i < h; i += 64) gst(p.hidden + i, ldf_dev(src + i));
     }
 }
 
@@ -1078,34 +1161,30 @@ __device__ __noinline__ void finish_step(const Params* pp, uint32_t epoch, uint3
 // ---- compute-wave main loop ---------------------------------------------------------------
 
 __device__ __noinline__ void compute(const Params* pp, uint32_t epoch, int wave) {
-    uint32_t cgen = 0;
     Ctx c;
     c.wave = (int)uni((uint32_t)wave);
     c.lane = threadIdx.x & 63;
     c.tid = c.wave * 64 + c.lane;
     c.epoch = epoch;
     c.parity = epoch & 1u;
-    c.cgen = &cgen;
     CParams& p0 = P(pp);
     const int h = p0.T.h, okt = p0.T.grp * p0.T.d, dkt = p0.T.kd, hd = p0.T.d;
     for (uint32_t t = 0;; ++t) {
         const uint32_t slot = t % FIFO;
         if (!lds_wait_ge(S.fifo_ready[slot], t + 1, pp, NONE)) return;
-        Task k;
-#pragma unroll
-        for (int i = 0; i < 12; ++i) ((uint32_t*)&k)[i] = uni(lds_ld(((const uint32_t*)&S.fifo[slot])[i]));
+        const Task k = fifo_task(slot);
         const uint32_t page0 = uni(lds_ld(S.fifo_first_page[slot]));
         if (k.op == OP_END) return;
         const uint64_t t_fetch = rtc();
         c.t = t;
         bool ok = true;
         switch (k.op) {
-            case OP_QKV: ok = MK_KT_DISPATCH(op_qkv, h, pp, k, page0, c); break;
-            case OP_ATTN: ok = hd == 64 ? op_attn<64>(pp, k, page0, c) : op_attn<128>(pp, k, page0, c); break;
-            case OP_OPROJ: ok = MK_KT_DISPATCH(op_oproj, okt, pp, k, page0, c); break;
-            case OP_GATEUP: ok = MK_KT_DISPATCH(op_gateup, h, pp, k, page0, c); break;
-            case OP_DOWN: ok = MK_KT_DISPATCH(op_down, dkt, pp, k, page0, c); break;
-            case OP_LMHEAD: ok = MK_KT_DISPATCH(op_lmhead, h, pp, k, page0, c); break;
+            case OP_QKV: ok = MK_KT_DISPATCH(op_qkv, h, pp, slot, page0, t, epoch); break;
+            case OP_ATTN: ok = hd == 64 ? op_attn<64>(pp, slot, page0, t, epoch) : op_attn<128>(pp, slot, page0, t, epoch); break;
+            case OP_OPROJ: ok = MK_KT_DISPATCH(op_oproj, okt, pp, slot, page0, t, epoch); break;
+            case OP_GATEUP: ok = MK_KT_DISPATCH(op_gateup, h, pp, slot, page0, t, epoch); break;
+            case OP_DOWN: ok = MK_KT_DISPATCH(op_down, dkt, pp, slot, page0, t, epoch); break;
+            case OP_LMHEAD: ok = MK_KT_DISPATCH(op_lmhead, h, pp, slot, page0, t, epoch); break;
             default: break;
         }
         if (!uni(ok)) return;
@@ -1126,14 +1205,14 @@ __device__ __noinline__ void compute(const Params* pp, uint32_t epoch, int wave)
                 unsigned long long* tr = p.trace + (size_t)k.id * TRACE_WORDS;
                 const uint64_t t_ready = ((unsigned long long)lds_ld(S.t_ready_hi) << 32) | lds_ld(S.t_ready_lo);
                 const uint64_t hi = t_ready & ~0xffffffffull;
-                tr[0] = blockIdx.x;
-                tr[1] = t_fetch;
-                tr[2] = t_ready;
-                tr[3] = k.op == OP_ATTN ? 0 : hi | lds_ld(S.tm[0]);
-                tr[4] = k.op == OP_ATTN ? 0 : hi | lds_ld(S.tm[1]);
-                tr[5] = rtc();
-                tr[6] = page0;
-                tr[7] = 0;
+                gst(tr + 0, (unsigned long long)blockIdx.x);
+                gst(tr + 1, (unsigned long long)t_fetch);
+                gst(tr + 2, (unsigned long long)t_ready);
+                gst(tr + 3, (unsigned long long)(k.op == OP_ATTN ? 0 : hi | lds_ld(S.tm[0])));
+                gst(tr + 4, (unsigned long long)(k.op == OP_ATTN ? 0 : hi | lds_ld(S.tm[1])));
+                gst(tr + 5, (unsigned long long)rtc());
+                gst(tr + 6, (unsigned long long)page0);
+                gst(tr + 7, 0ull);
             }
             vm_wait_all();
             if (c.lane == 0) lds_add(S.fifo_free[slot], 1u);
@@ -1154,6 +1233,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) mk_step_kernel(const Params* pp, 
         for (int lw = 0; lw < NLW; ++lw) S.page_ready[lw][threadIdx.x] = 0;
         S.page_free[threadIdx.x] = 0;
     }
+    if (threadIdx.x < NCW) S.cgen[threadIdx.x] = 0;
     if (threadIdx.x == 0) {
         S.go = 0;
         S.cbar = 0;
