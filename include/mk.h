@@ -152,8 +152,10 @@ mk_status mk_read_task_counts(mk_handle *h, uint32_t *host, size_t n);
 
 /* Trace (when built with trace=1): per task of the last step, eight uint64
  * values {workgroup, t_fetch, t_inputs_ready, t_staged, t_computed, t_end,
- * first LDS page, 0}; times in ticks of the 100 MHz device clock (t_staged and
- * t_computed are 0 for attention tasks); n_tasks * 8 entries into host. */
+ * first LDS page, t_last_page}; times in ticks of the 100 MHz device clock.
+ * t_staged: inputs in LDS (attention: queries staged); t_computed: arithmetic
+ * done (attention: all context pages folded in); t_last_page: compute wave 0
+ * held the last of its pages (0 if it had none).  n_tasks * 8 entries into host. */
 mk_status mk_read_trace(mk_handle *h, uint64_t *host, size_t n);
 
 void mk_destroy(mk_handle *h);

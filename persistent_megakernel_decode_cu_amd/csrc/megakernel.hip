@@ -55,7 +55,7 @@ struct __attribute__((aligned(16))) Smem {
     float xs[XS];
     float rowres[ROWRES];
     Task fifo[FIFO];
-    float wsc[NCW][64];
+    float wsc[NCW][256];  // attention: softmax weights of up to 4 pages per wave
     int32_t pos[MAXB];
     int32_t tok[MAXB];
     StepArgs args;
@@ -189,9 +189,15 @@ __device__ __forceinline__ float wave_sum(float v) {
            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, true)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, true)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, true)));
+    const float a = fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)),
+                          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16)));
+    const float b = fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32)),
+                          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48)));
+    return fmaxf(a, b);
 }
 // Sum over aligned segments of W lanes (W = 8, 16, 32); every lane gets its segment's sum.
 template <int W>
@@ -338,12 +344,21 @@ __device__ __forceinline__ void issue_page(CParams& p, const Task& k, uint32_t k
         const uint64_t row = (((uint64_t)k.layer * p.T.B + k.seq) * p.T.nkv + k.part) * (uint64_t)p.T.C + (uint64_t)p0;
         const uint8_t* kb = (const uint8_t*)S.args.kc + row * d * 2;
         const uint8_t* vb = (const uint8_t*)S.args.vc + row * d * 2;
+        // K goes in 16-byte-column-major order (column chunk c of all pb rows, then
+        // c + 1, ...: a lane per position reads its chunk without bank conflicts);
+        // V stays row-major.  Rows past the valid ones repeat the last valid row.
 #pragma unroll
         for (int i = 0; i < LPP; ++i) {
-            const int j = i * NLW + lw;  // 1 KiB load j of the page: K rows for j < 8, V rows after
-            const uint8_t* src = j < 8 ? kb : vb;
-            const uint32_t off = min((uint32_t)((j & 7) * 1024 + lane * 16), valid - 16u);
-            dma16(src + off, dst + j * 1024);
+            const int j = i * NLW + lw;  // 1 KiB load j of the page: K for j < 8, V after
+            uint32_t off;
+            if (j < 8) {
+                const uint32_t e = (uint32_t)(j * 64 + lane);  // 16-byte element of the K block
+                const uint32_t c = e / (uint32_t)pb, r = min(e % (uint32_t)pb, (uint32_t)rows - 1u);
+                off = r * (uint32_t)d * 2u + c * 16u;
+            } else {
+                off = min((uint32_t)((j - 8) * 1024 + lane * 16), valid - 16u);
+            }
+            dma16((j < 8 ? kb : vb) + off, dst + j * 1024);
         }
     } else {
         const uint8_t* base = p.w + k.wofs + (uint64_t)kp * PAGE;
@@ -652,6 +667,7 @@ __device__ __forceinline__ bool gemv_pages(const Params* pp, int wave, int lane,
                 continue;
             }
             if (!page_acquire(pp, page0 + pg, task)) return false;
+            if (wave == 0 && lane == 0) lds_st(S.tm[2], (uint32_t)rtc());
             const uint32_t slot = (page0 + pg) % NPAGES;
             uint4 wv[RPP * LPR];
 #pragma unroll
@@ -676,6 +692,7 @@ __device__ __forceinline__ bool gemv_pages(const Params* pp, int wave, int lane,
         constexpr int LPR = KT / 512;
         for (uint32_t pg = 0; pg < npages; ++pg) {
             if (!page_acquire(pp, page0 + pg, task)) return false;
+            if (wave == 0 && lane == 0) lds_st(S.tm[2], (uint32_t)rtc());
             const uint32_t slot = (page0 + pg) % NPAGES;
             uint4 wv[RW * LPR];
 #pragma unroll
@@ -697,6 +714,7 @@ __device__ __forceinline__ bool gemv_pages(const Params* pp, int wave, int lane,
         constexpr int UW = 16 / NCW;          // 1 KiB groups of each page for each wave
         for (uint32_t pg = 0; pg < npages; ++pg) {
             if (!page_acquire(pp, page0 + pg, task)) return false;
+            if (wave == 0 && lane == 0) lds_st(S.tm[2], (uint32_t)rtc());
             const uint32_t slot = (page0 + pg) % NPAGES;
             uint4 wv[UW];
 #pragma unroll
@@ -804,7 +822,12 @@ __device__ __noinline__ bool op_qkv(const Params* pp, uint32_t slot_, uint32_t p
     return true;
 }
 
-// Attention over one chunk of the context of (sequence, KV group): one wave per query head.
+// Attention over one chunk of the context of (sequence, KV group): one wave per
+// query head, softmax over 64-position pages taken in batches of up to four
+// (one running maximum and sum per batch; the split of the context into chunks
+// merged afterwards is the usual split-KV decode).  Scores: lane = position, K
+// read column-chunk-major.  P.V: lane = (8-dimension chunk, position group), V
+// read row-major; the position groups' partial sums are added through LDS.
 template <int D>
 __device__ __noinline__ bool op_attn(const Params* pp, uint32_t slot_, uint32_t page0, uint32_t t_, uint32_t epoch_) {
     const Task k = fifo_task(slot_);
@@ -813,112 +836,178 @@ __device__ __noinline__ bool op_attn(const Params* pp, uint32_t slot_, uint32_t 
     const int lane = c.lane, wave = c.wave;
     const int b = (int)k.seq, g = k.part;
     const Chunk ch = attn_chunk(p.T.attn_splits, S.pos[b], k.row0);
-    const int32_t pb = attn_block_rows(D);
+    constexpr int PB = 4096 / D;      // positions per page (64 or 32)
+    constexpr int NC = D / 8;         // 16-byte chunks per row (8 or 16)
+    constexpr int NPG = 64 / NC;      // position groups in P.V (8 or 4)
+    constexpr int IT = PB / NPG;      // positions per lane and page in P.V (8)
+    constexpr int BATCH = 4;          // pages per softmax batch
     const int32_t pre_end = min(ch.c1, ch.P);
     const int32_t npre = max(0, pre_end - ch.c0);
-    const uint32_t npages = (uint32_t)((npre + pb - 1) / pb);
+    const uint32_t npages = (uint32_t)((npre + PB - 1) / PB);
     const float scale = 1.0f / sqrtf((float)D);
-    constexpr int DL = D / 64;  // dimensions per lane
     const int G = p.T.grp;
     const int nh = (G - wave + NCW - 1) / NCW;  // heads of this wave: wave, wave + NCW, ...
     const bool has_cur = ch.c0 <= ch.P && ch.P < ch.c1;
+    const int cl = lane % NC, pgl = lane / NC;  // P.V: dimension chunk and position group of this lane
     if (!await_inputs(pp, k, c)) return false;
-    // each wave stages the query rows of its own heads, and the current token's K/V row
-    float kv[DL], vv[DL];
+    // each wave stages the query rows of its own heads, and the current token's K/V chunk
+    float kc8[8], vc8[8];
     {
         const float* qg = p.q + (size_t)b * p.T.nq * D + (size_t)g * G * D;
-        float qv[4][DL];
+        float qv[4][D / 64];
 #pragma unroll
         for (int hh = 0; hh < 4; ++hh)
 #pragma unroll
-            for (int ee = 0; ee < DL; ++ee)
+            for (int ee = 0; ee < D / 64; ++ee)
                 qv[hh][ee] = hh < nh ? ldf_dev(qg + (wave + hh * NCW) * D + lane + 64 * ee) : 0.f;
         if (has_cur) {
             const size_t row = (((size_t)k.layer * p.T.B + b) * p.T.nkv + g) * (size_t)p.T.C + (size_t)ch.P;
-            const uint16_t* kr = S.args.kc + row * D;
-            const uint16_t* vr = S.args.vc + row * D;
+            const uint32_t* kr = (const uint32_t*)(S.args.kc + row * D + cl * 8);
+            const uint32_t* vr = (const uint32_t*)(S.args.vc + row * D + cl * 8);
 #pragma unroll
-            for (int ee = 0; ee < DL; ++ee) {
-                const int t = lane + 64 * ee;
-                const uint32_t wk = ld_dev((const uint32_t*)(kr + (t & ~1)));
-                const uint32_t wv = ld_dev((const uint32_t*)(vr + (t & ~1)));
-                kv[ee] = (t & 1) ? bf16hi(wk) : bf16lo(wk);
-                vv[ee] = (t & 1) ? bf16hi(wv) : bf16lo(wv);
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t wk = ld_dev(kr + i), wv = ld_dev(vr + i);
+                kc8[2 * i] = bf16lo(wk);
+                kc8[2 * i + 1] = bf16hi(wk);
+                vc8[2 * i] = bf16lo(wv);
+                vc8[2 * i + 1] = bf16hi(wv);
             }
         }
 #pragma unroll
         for (int hh = 0; hh < 4; ++hh)
 #pragma unroll
-            for (int ee = 0; ee < DL; ++ee)
+            for (int ee = 0; ee < D / 64; ++ee)
                 if (hh < nh) S.xs[(wave + hh * NCW) * D + lane + 64 * ee] = qv[hh][ee];
         lgkm_wait_all();
     }
-    float M[4], Ls[4], o[4][DL];
+    tmark(c, 0);
+    float M[4], Ls[4], o[4][8];
 #pragma unroll
     for (int hh = 0; hh < 4; ++hh) {
         M[hh] = -INFINITY;
         Ls[hh] = 0.f;
 #pragma unroll
-        for (int e = 0; e < DL; ++e) o[hh][e] = 0.f;
+        for (int e = 0; e < 8; ++e) o[hh][e] = 0.f;
     }
-    for (uint32_t pg = 0; pg < npages; ++pg) {
-        if (!page_acquire(pp, page0 + pg, k.id)) return false;
-        const uint32_t slot = (page0 + pg) % NPAGES;
-        const int32_t rows = min(pb, pre_end - (ch.c0 + (int32_t)pg * pb));
+    float* const wsc = S.wsc[wave];
+    for (uint32_t pb0 = 0; pb0 < npages; pb0 += BATCH) {
+        const uint32_t nb = min((uint32_t)BATCH, npages - pb0);
+        for (uint32_t i = 0; i < nb; ++i)
+            if (!page_acquire(pp, page0 + pb0 + i, k.id)) return false;
+        tmark(c, 2);
 #pragma unroll
         for (int hh = 0; hh < 4; ++hh) {
             if (hh >= nh) break;
             const int hw = wave + hh * NCW;
-            // scores: lane = position within the block
-            float s = -INFINITY;
-            if (lane < rows) {
-                float a = 0.f;
+            // scores of the batch: lane = position within each page
+            float sc[BATCH];
+            float mx = -INFINITY;
 #pragma unroll
-                for (int cc = 0; cc < D / 8; ++cc) {
-                    const uint4 w = *(const uint4*)&ring[slot][lane * (2 * D) + cc * 16];
-                    a = dot8(w, &S.xs[hw * D + cc * 8], a);
+            for (int i = 0; i < BATCH; ++i) {
+                sc[i] = -INFINITY;
+                if ((uint32_t)i < nb) {
+                    const uint32_t slot = (page0 + pb0 + i) % NPAGES;
+                    const int32_t rows = min(PB, pre_end - (ch.c0 + (int32_t)(pb0 + i) * PB));
+                    if (lane < rows) {
+                        float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+                        for (int cc = 0; cc < NC; cc += 2) {
+                            const uint4 k0 = *(const uint4*)&ring[slot][cc * (PB * 16) + lane * 16];
+                            const uint4 k1 = *(const uint4*)&ring[slot][(cc + 1) * (PB * 16) + lane * 16];
+                            a0 = dot8(k0, &S.xs[hw * D + cc * 8], a0);
+                            a1 = dot8(k1, &S.xs[hw * D + (cc + 1) * 8], a1);
+                        }
+                        sc[i] = (a0 + a1) * scale;
+                    }
+                    mx = fmaxf(mx, sc[i]);
                 }
-                s = a * scale;
             }
-            const float mn = fmaxf(M[hh], wave_max(s));
+            const float mn = fmaxf(M[hh], wave_max(mx));
             const float corr = __expf(M[hh] - mn);
-            const float e = lane < rows ? __expf(s - mn) : 0.f;
-            Ls[hh] = Ls[hh] * corr + wave_sum(e);
+            float es = 0.f;
+#pragma unroll
+            for (int i = 0; i < BATCH; ++i) {
+                const float e = sc[i] == -INFINITY ? 0.f : __expf(sc[i] - mn);
+                es += e;
+                // weights stored so that lane (chunk, group) finds its IT positions contiguous
+                if ((uint32_t)i < nb) wsc[i * 64 + (lane % NPG) * IT + lane / NPG] = e;
+            }
+            Ls[hh] = Ls[hh] * corr + wave_sum(es);
             M[hh] = mn;
-            S.wsc[wave][lane] = e;
+#pragma unroll
+            for (int ee = 0; ee < 8; ++ee) o[hh][ee] *= corr;
             lgkm_wait_all();
-            // o[t] += sum_p e_p V[p][t]: lane = dimension
 #pragma unroll
-            for (int ee = 0; ee < DL; ++ee) o[hh][ee] *= corr;
-            for (int r = 0; r < rows; ++r) {
-                const float wgt = S.wsc[wave][r];
+            for (int i = 0; i < BATCH; ++i) {
+                if ((uint32_t)i >= nb) break;
+                const uint32_t slot = (page0 + pb0 + i) % NPAGES;
+                float wgt[IT];
 #pragma unroll
-                for (int ee = 0; ee < DL; ++ee) {
-                    const uint16_t vvv = *(const uint16_t*)&ring[slot][8192 + r * (2 * D) + (lane + 64 * ee) * 2];
-                    o[hh][ee] = fmaf(wgt, bf16f(vvv), o[hh][ee]);
+                for (int q = 0; q < IT; q += 4) {
+                    const float4 w4 = *(const float4*)&wsc[i * 64 + pgl * IT + q];
+                    wgt[q] = w4.x;
+                    wgt[q + 1] = w4.y;
+                    wgt[q + 2] = w4.z;
+                    wgt[q + 3] = w4.w;
                 }
+#pragma unroll
+                for (int r = 0; r < IT; ++r) {
+                    const uint4 w = *(const uint4*)&ring[slot][8192 + (pgl + NPG * r) * (2 * D) + cl * 16];
+                    o[hh][0] = fmaf(wgt[r], bf16lo(w.x), o[hh][0]);
+                    o[hh][1] = fmaf(wgt[r], bf16hi(w.x), o[hh][1]);
+                    o[hh][2] = fmaf(wgt[r], bf16lo(w.y), o[hh][2]);
+                    o[hh][3] = fmaf(wgt[r], bf16hi(w.y), o[hh][3]);
+                    o[hh][4] = fmaf(wgt[r], bf16lo(w.z), o[hh][4]);
+                    o[hh][5] = fmaf(wgt[r], bf16hi(w.z), o[hh][5]);
+                    o[hh][6] = fmaf(wgt[r], bf16lo(w.w), o[hh][6]);
+                    o[hh][7] = fmaf(wgt[r], bf16hi(w.w), o[hh][7]);
+                }
+            }
+            lgkm_wait_all();
+        }
+        for (uint32_t i = 0; i < nb; ++i) page_release(page0 + pb0 + i, lane);
+    }
+    // add the position groups' partial sums through LDS (xs above the staged queries)
+    float* const red = &S.xs[MAX_ACT / 2 + wave * 512];
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh) {
+        if (hh >= nh) break;
+        *(float4*)&red[lane * 8] = make_float4(o[hh][0], o[hh][1], o[hh][2], o[hh][3]);
+        *(float4*)&red[lane * 8 + 4] = make_float4(o[hh][4], o[hh][5], o[hh][6], o[hh][7]);
+        lgkm_wait_all();
+        if (pgl == 0) {
+#pragma unroll
+            for (int gg = 1; gg < NPG; ++gg) {
+                const float4 a = *(const float4*)&red[(gg * NC + cl) * 8];
+                const float4 bb = *(const float4*)&red[(gg * NC + cl) * 8 + 4];
+                o[hh][0] += a.x; o[hh][1] += a.y; o[hh][2] += a.z; o[hh][3] += a.w;
+                o[hh][4] += bb.x; o[hh][5] += bb.y; o[hh][6] += bb.z; o[hh][7] += bb.w;
             }
         }
-        page_release(page0 + pg, lane);
+        lgkm_wait_all();
     }
     if (has_cur) {
 #pragma unroll
         for (int hh = 0; hh < 4; ++hh) {
             if (hh >= nh) break;
             const int hw = wave + hh * NCW;
+            // q . k_cur: the lanes of position group 0 hold the NC chunks
             float a = 0.f;
+            if (pgl == 0) {
 #pragma unroll
-            for (int ee = 0; ee < DL; ++ee) a = fmaf(S.xs[hw * D + lane + 64 * ee], kv[ee], a);
-            const float s = wave_sum(a) * scale;
-            const float mn = fmaxf(M[hh], s);
+                for (int ee = 0; ee < 8; ++ee) a = fmaf(S.xs[hw * D + cl * 8 + ee], kc8[ee], a);
+            }
+            const float sc = wave_sum(a) * scale;
+            const float mn = fmaxf(M[hh], sc);
             const float corr = __expf(M[hh] - mn);
-            const float e = __expf(s - mn);
+            const float e = __expf(sc - mn);
             Ls[hh] = Ls[hh] * corr + e;
             M[hh] = mn;
 #pragma unroll
-            for (int ee = 0; ee < DL; ++ee) o[hh][ee] = fmaf(e, vv[ee], o[hh][ee] * corr);
+            for (int ee = 0; ee < 8; ++ee) o[hh][ee] = fmaf(e, vc8[ee], o[hh][ee] * corr);
         }
     }
+    tmark(c, 1);
     // partials (m, l, o) -> part[b][g][chunk][head][D + 2]
 #pragma unroll
     for (int hh = 0; hh < 4; ++hh) {
@@ -929,8 +1018,10 @@ __device__ __noinline__ bool op_attn(const Params* pp, uint32_t slot_, uint32_t 
             stf_dev(dst, M[hh]);
             stf_dev(dst + 1, Ls[hh]);
         }
+        if (pgl == 0) {
 #pragma unroll
-        for (int ee = 0; ee < DL; ++ee) stf_dev(dst + 2 + lane + 64 * ee, o[hh][ee]);
+            for (int ee = 0; ee < 8; ++ee) stf_dev(dst + 2 + cl * 8 + ee, o[hh][ee]);
+        }
     }
     return true;
 }
@@ -1208,11 +1299,12 @@ __device__ __noinline__ void compute(const Params* pp, uint32_t epoch, int wave)
                 gst(tr + 0, (unsigned long long)blockIdx.x);
                 gst(tr + 1, (unsigned long long)t_fetch);
                 gst(tr + 2, (unsigned long long)t_ready);
-                gst(tr + 3, (unsigned long long)(k.op == OP_ATTN ? 0 : hi | lds_ld(S.tm[0])));
-                gst(tr + 4, (unsigned long long)(k.op == OP_ATTN ? 0 : hi | lds_ld(S.tm[1])));
+                gst(tr + 3, (unsigned long long)(hi | lds_ld(S.tm[0])));
+                gst(tr + 4, (unsigned long long)(hi | lds_ld(S.tm[1])));
                 gst(tr + 5, (unsigned long long)rtc());
                 gst(tr + 6, (unsigned long long)page0);
-                gst(tr + 7, 0ull);
+                gst(tr + 7, (unsigned long long)(hi | lds_ld(S.tm[2])));
+                if (c.lane == 0) lds_st(S.tm[2], 0u);
             }
             vm_wait_all();
             if (c.lane == 0) lds_add(S.fifo_free[slot], 1u);
