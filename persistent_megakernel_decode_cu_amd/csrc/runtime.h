@@ -16,7 +16,7 @@ constexpr uint32_t ST_ABORT = 96;   // set when any wave gives up
 constexpr uint32_t ST_ERR = 128;    // error record: code, workgroup, task, event, seen, target
 constexpr uint32_t ST_WORDS = 160;
 
-constexpr int TRACE_WORDS = 8;  // per task: workgroup, fetch, inputs ready, staged, computed, end, first page, 0
+constexpr int TRACE_WORDS = 8;  // per task: workgroup, fetch, inputs ready, staged, computed, end, first page, last page held
 
 enum ErrCode : uint32_t { ERR_NONE = 0, ERR_TIMEOUT_EVENT = 1, ERR_TIMEOUT_LDS = 2, ERR_INPUT = 3 };
 
