@@ -23,18 +23,19 @@ The tiling rules (written from the design, not from the C++ code):
   * attention: attn_splits chunks per (sequence, KV group), default
     clamp(ceil(max_ctx / 256), 1, 16), at most max_ctx.
   * O-proj tiles: (KV group g, row block) over columns g*grp*d .. +grp*d, with
-    o_rows = min(h, 1024, max(8, pow2_floor(h * n_kv / W))).
+    o_rows = min(h, 1024, max(16, pow2_floor(h * n_kv / W))).
   * down tiles: (K block of kd = min(1024, f) columns, row block of
-    d_rows = min(h, 1024, max(8, pow2_floor(h * (f / kd) / W))) rows).
+    d_rows = min(h, 1024, max(16, pow2_floor(h * (f / kd) / W))) rows).
   * gate/up tiles: g_rows gate rows then the same g_rows up rows, with
-    g_rows = min(kd, 512, max(4, pow2_ceil(ceil(f / W)))).
-  * LM head tiles: lm_rows = min(1024, ceil(V / W)) rows, the last one shorter.
+    g_rows = min(kd, 512, max(8, pow2_ceil(ceil(f / W)))).
+  * LM head tiles: lm_rows = min(1024, ceil(V / W) rounded up to 16) rows, the
+    last one shorter; its weight bytes are its rows rounded up to 16.
   * per layer the events are created in the order qkv[g], attn[g], xb, m[kb],
     x_next; tasks in the order QKV, attention, O-proj, gate/up, down; then the
     LM-head tiles.  An event with more than 32 producers uses 8 sub-counters.
-  * packed weights: gains ((2L+1) rows of h), embedding, LM head (if untied),
-    then per layer QKV, O, gate/up, down regions, each region padded to 256 B,
-    tiles inside a region in task order.
+  * packed weights: gains ((2L+1) rows of h), embedding, LM-head tiles (always
+    a copy of their own), then per layer QKV, O, gate/up, down regions, each
+    region padded to 256 B, tiles inside a region in task order.
   * static queues: round-robin (task i -> workgroup i mod W) or least-loaded
     (cost = weight bytes + 8192, ties to the lowest workgroup); the dynamic
     queue is the task order itself.
@@ -73,6 +74,10 @@ def _pad(x):
     return (x + 255) // 256 * 256
 
 
+def _round16(x):
+    return (x + 15) // 16 * 16
+
+
 def tiling(cfg, B, C, W, attn_splits=0):
     h, nq, nkv, d, f, V = cfg.hidden, cfg.n_q, cfg.n_kv, cfg.head_dim, cfg.ffn, cfg.vocab
     grp = nq // nkv
@@ -80,24 +85,21 @@ def tiling(cfg, B, C, W, attn_splits=0):
     S = min(S, C)
     kd = min(1024, f)
     return dict(grp=grp, pairs=8, S=S,
-                o_rows=min(h, 1024, max(8, _pow2_floor(h * nkv // W))),
-                kd=kd, d_rows=min(h, 1024, max(8, _pow2_floor(h * (f // kd) // W))),
-                g_rows=min(kd, 512, max(4, _pow2_ceil(-(-f // W)))),
-                lm_rows=min(1024, -(-V // W)))
+                o_rows=min(h, 1024, max(16, _pow2_floor(h * nkv // W))),
+                kd=kd, d_rows=min(h, 1024, max(16, _pow2_floor(h * (f // kd) // W))),
+                g_rows=min(kd, 512, max(8, _pow2_ceil(-(-f // W)))),
+                lm_rows=min(1024, _round16(-(-V // W))))
 
 
-def layout(cfg, tied):
+def layout(cfg, lm_rows, n_lm):
     h, L = cfg.hidden, cfg.n_layers
     at = 0
     lay = {"gains": at}
     at = _pad(at + (2 * L + 1) * h * 2)
     lay["embed"] = at
     at = _pad(at + cfg.vocab * h * 2)
-    if tied:
-        lay["lm"] = lay["embed"]
-    else:
-        lay["lm"] = at
-        at = _pad(at + cfg.vocab * h * 2)
+    lay["lm"] = at  # own copy even when tied (tiles in GEMV page order)
+    at = _pad(at + n_lm * lm_rows * h * 2)
     lay["layer0"] = at
     x = 0
     lay["qkv"] = x
@@ -116,7 +118,8 @@ def build(cfg, B, C, W, policy=0, attn_splits=0):
     """The task graph as a list of task dicts plus event targets, sub-counter
     counts, static queues and the dynamic order."""
     t = tiling(cfg, B, C, W, attn_splits)
-    lay = layout(cfg, cfg.tied)
+    n_lm = -(-cfg.vocab // t["lm_rows"])
+    lay = layout(cfg, t["lm_rows"], n_lm)
     h, nq, nkv, d, f, L = cfg.hidden, cfg.n_q, cfg.n_kv, cfg.head_dim, cfg.ffn, cfg.n_layers
     grp, P, S = t["grp"], t["pairs"], t["S"]
     n_kb = f // t["kd"]
@@ -173,10 +176,9 @@ def build(cfg, B, C, W, policy=0, attn_splits=0):
                      flags=TF_RESID if kb == 0 else 0, wait_ev=ev_m[kb], sig_ev=ev_next, wbytes=wb,
                      wofs=base + lay["down"] + (kb * (h // t["d_rows"]) + rb) * wb)
         ev_x = ev_next
-    n_lm = -(-cfg.vocab // t["lm_rows"])
     for i in range(n_lm):
         rows = min(t["lm_rows"], cfg.vocab - i * t["lm_rows"])
-        task(op=OP_LMHEAD, layer=L, row0=i * t["lm_rows"], nrows=rows, wait_ev=ev_x, wbytes=rows * h * 2,
+        task(op=OP_LMHEAD, layer=L, row0=i * t["lm_rows"], nrows=rows, wait_ev=ev_x, wbytes=_round16(rows) * h * 2,
              wofs=lay["lm"] + i * t["lm_rows"] * h * 2)
     nsub = [8 if n > 32 else 1 for n in target]
     for k in tasks:
@@ -329,7 +331,7 @@ def check(g, cfg, B):
     for ofs, nb in lm:
         assert ofs == pos
         pos += nb
-    assert pos == lay["lm"] + V * h * 2
+    assert pos == lay["lm"] + _round16(V) * h * 2
 
 
 def ancestor_sets(g):

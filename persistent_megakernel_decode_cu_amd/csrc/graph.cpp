@@ -36,9 +36,11 @@ static int64_t pow2_ceil(int64_t x) {
 static uint64_t pad256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
 // A GEMV tile whose rows have KT bf16 columns is consumed from 16 KiB LDS
-// pages: rows must not straddle pages and a 1 KiB wave load must hold whole
-// rows or whole fractions of a row.
-static bool gemv_k_ok(int64_t kt) { return is_pow2(kt) && kt >= 64 && kt <= 8192; }
+// pages.  128 <= KT <= 2048: pages hold 16 x 32 blocks of matrix-core operands,
+// and every compute wave owns a quarter of the 32-column blocks; KT = 4096: two
+// whole rows per page.
+static bool gemv_k_ok(int64_t kt) { return is_pow2(kt) && kt >= 128 && kt <= 4096; }
+static int64_t round16(int64_t x) { return (x + 15) / 16 * 16; }
 
 int plan_tiling(const Dims& dm, int B, int C, int W, const PlanOptions& o, Tiling* t, std::string* err) {
     auto fail = [&](const char* m) {
@@ -52,10 +54,11 @@ int plan_tiling(const Dims& dm, int B, int C, int W, const PlanOptions& o, Tilin
     if (dm.n_experts != 0) return fail("mixture-of-experts FFN is not implemented by this build");
     if (B != 1) return fail("batch > 1 is not implemented by this build");
     if (dm.f <= 0) return fail("ffn_dim must be positive");
-    if (!gemv_k_ok(dm.h) || dm.h > MAX_ACT) return fail("hidden must be a power of two in [64, 4096]");
+    if (!gemv_k_ok(dm.h) || dm.h > MAX_ACT) return fail("hidden must be a power of two in [128, 4096]");
     const int grp = dm.nq / dm.nkv;
     if (grp > 16) return fail("more than 16 query heads per KV head");
-    if (!gemv_k_ok((int64_t)grp * dm.d)) return fail("query heads per KV head times head_dim must be a power of two");
+    if (!gemv_k_ok((int64_t)grp * dm.d) || (int64_t)grp * dm.d > 2048)
+        return fail("query heads per KV head times head_dim must be a power of two in [128, 2048]");
     Tiling& T = *t;
     memset(&T, 0, sizeof(T));
     T.L = dm.L; T.h = dm.h; T.nq = dm.nq; T.nkv = dm.nkv; T.d = dm.d; T.f = dm.f; T.V = dm.V;
@@ -69,21 +72,21 @@ int plan_tiling(const Dims& dm, int B, int C, int W, const PlanOptions& o, Tilin
     T.n_attn_tiles = B * dm.nkv * S;
     // O-proj: tiles (KV group g, rows) with K = grp*d columns; about W tiles per layer
     T.o_rows = (int)std::min<int64_t>(std::min<int64_t>(dm.h, MAX_TILE_ROWS),
-                                      std::max<int64_t>(8, pow2_floor((int64_t)dm.h * dm.nkv / W)));
+                                      std::max<int64_t>(16, pow2_floor((int64_t)dm.h * dm.nkv / W)));
     T.n_o_tiles = dm.nkv * (dm.h / T.o_rows);
     // down-proj K blocks of kd columns of m; gate/up tiles feed whole K blocks
     T.kd = (int)std::min<int64_t>(1024, dm.f);
-    if (dm.f % T.kd || !gemv_k_ok(T.kd)) return fail("ffn_dim must be a multiple of 1024 (or a power of two below it)");
+    if (dm.f % T.kd || !gemv_k_ok(T.kd)) return fail("ffn_dim must be a multiple of 1024 (or a power of two in [128, 1024))");
     const int64_t n_kb = dm.f / T.kd;
     T.d_rows = (int)std::min<int64_t>(std::min<int64_t>(dm.h, MAX_TILE_ROWS),
-                                      std::max<int64_t>(8, pow2_floor((int64_t)dm.h * n_kb / W)));
+                                      std::max<int64_t>(16, pow2_floor((int64_t)dm.h * n_kb / W)));
     T.n_down_tiles = (int)(n_kb * (dm.h / T.d_rows));
-    T.g_rows = (int)std::max<int64_t>(4, pow2_ceil((dm.f + W - 1) / W));
+    T.g_rows = (int)std::max<int64_t>(8, pow2_ceil((dm.f + W - 1) / W));
     if (T.g_rows > T.kd) T.g_rows = T.kd;
     if (T.g_rows > MAX_TILE_ROWS / 2) T.g_rows = MAX_TILE_ROWS / 2;
     if (T.kd % T.g_rows) return fail("gate/up tile does not divide the down-proj K block");
     T.n_gu_tiles = dm.f / T.g_rows;
-    T.lm_rows = (int)std::min<int64_t>(MAX_TILE_ROWS, (dm.V + W - 1) / W);
+    T.lm_rows = (int)std::min<int64_t>(MAX_TILE_ROWS, round16((dm.V + W - 1) / W));
     T.n_lm_tiles = (dm.V + T.lm_rows - 1) / T.lm_rows;
     return 0;
 }
@@ -97,12 +100,11 @@ void plan_layout(const Tiling& T, bool tied, Layout* out) {
     at = pad256(at + (uint64_t)(2 * T.L + 1) * h * 2);
     Ly.embed = at;
     at = pad256(at + (uint64_t)T.V * h * 2);
-    if (tied) {
-        Ly.lm = Ly.embed;
-    } else {
-        Ly.lm = at;
-        at = pad256(at + (uint64_t)T.V * h * 2);
-    }
+    // the LM head has its own copy even when tied to the embedding: its tiles
+    // are stored in GEMV page order, the embedding row by row for the gather
+    (void)tied;
+    Ly.lm = at;
+    at = pad256(at + (uint64_t)T.n_lm_tiles * T.lm_rows * h * 2);
     Ly.layer0 = at;
     uint64_t l = 0;
     Ly.qkv = l;
@@ -244,7 +246,7 @@ int build_graph(const Tiling& T, const Layout& Ly, int sched, int policy, Graph*
         k.row0 = (uint32_t)(t * T.lm_rows);
         k.nrows = (uint32_t)std::min<int64_t>(T.lm_rows, (int64_t)T.V - (int64_t)t * T.lm_rows);
         k.wait_ev = ev_x;
-        k.wbytes = (uint32_t)((uint64_t)k.nrows * h * 2);
+        k.wbytes = (uint32_t)((uint64_t)round16(k.nrows) * h * 2);
         k.wofs = Ly.lm + (uint64_t)k.row0 * h * 2;
         add(k);
     }

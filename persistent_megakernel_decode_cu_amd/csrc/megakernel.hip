@@ -68,6 +68,7 @@ struct __attribute__((aligned(16))) Smem {
     uint32_t dyn_ready, dyn_ack;
     uint32_t go, cbar, done, abort;
     uint32_t cgen[NCW];  // compute-wave barrier generation (per wave)
+    float ssq[NCW];      // per-wave partial sums of squares of the staged activation
     uint32_t t_ready_lo, t_ready_hi;
     uint32_t tm[4];  // trace: low 32 bits of the clock after staging / after the GEMV
 };
@@ -570,6 +571,16 @@ __device__ __forceinline__ bool await_inputs(const Params* pp, const Task& k, Ct
     return lds_wait_ge(S.go, c.t + 1, pp, k.id);
 }
 
+// Device-scope (sc1) loads of data written by other workgroups in this step,
+// through a bounds-checked buffer resource (offsets past `bytes` read 0).  Unlike
+// atomic loads, the compiler keeps many of these in flight before a single wait.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dev_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, bytes, RSRC_FLAGS);
+}
+__device__ __forceinline__ float ldb_dev(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 16));
+}
+
 // n floats (n a multiple of 4) from src, read with device-scope 16-byte loads spread
 // over the compute lanes (all issued before any is used), into LDS xs[dst + i].
 template <int MAXQ>
@@ -648,83 +659,231 @@ __device__ __forceinline__ float rms_scale(int n, float eps, int lane) {
 
 // ---- GEMV over LDS pages --------------------------------------------------------------
 
-// y[r] = W[r, :] . x over the task's rows; weights in consecutive LDS pages from
-// page sequence `page0`; results in S.rowres[r].  Every compute wave takes its
-// share of every page (KT <= 2048: whole rows, KT < 512: a quarter of the 1 KiB
-// row groups), so a page is consumed as soon as it lands and the work left after
-// the last page is a quarter page per wave.  KT = 4096 (2 rows per page): wave w
-// computes the pages pg = w (mod NCW).  Each wave releases every page once.
+// y[r] = W[r, :] . x over the task's rows, rows of KT = 4096 bf16 (two rows per
+// 16 KiB page, stored row by row); wave w computes the pages pg = w (mod NCW).
+// Results in S.rowres[r].  Each wave releases every page of the task once.
 template <int KT>
 __device__ __forceinline__ bool gemv_pages(const Params* pp, int wave, int lane, uint32_t page0, uint32_t nrows,
                                            uint32_t wbytes, const float* x, uint32_t task) {
+    static_assert(KT >= 4096, "row-major GEMV pages are used for K = 4096 only");
     const uint32_t npages = (wbytes + PAGE - 1) / PAGE;
-    if constexpr (KT >= 4096) {
-        constexpr int RPP = PAGE / (2 * KT);  // rows per page
-        constexpr int LPR = KT / 512;         // 1 KiB wave loads per row
-        for (uint32_t pg = 0; pg < npages; ++pg) {
-            if ((int)(pg % NCW) != wave) {
-                page_skip(page0 + pg, lane);
-                continue;
-            }
-            if (!page_acquire(pp, page0 + pg, task)) return false;
-            if (wave == 0 && lane == 0) lds_st(S.tm[2], (uint32_t)rtc());
-            const uint32_t slot = (page0 + pg) % NPAGES;
-            uint4 wv[RPP * LPR];
-#pragma unroll
-            for (int i = 0; i < RPP * LPR; ++i) wv[i] = *(const uint4*)&ring[slot][i * 1024 + lane * 16];
-            page_release(page0 + pg, lane);
-#pragma unroll
-            for (int rr = 0; rr < RPP; ++rr) {
-                float a = 0.f, b = 0.f;
-#pragma unroll
-                for (int j = 0; j < LPR; j += 2) {
-                    a = dot8(wv[rr * LPR + j], x + j * 8, a);
-                    b = dot8(wv[rr * LPR + j + 1], x + (j + 1) * 8, b);
-                }
-                const float sum = wave_sum(a + b);
-                const uint32_t r = pg * RPP + rr;
-                if (lane == 0 && r < nrows) S.rowres[r] = sum;
-            }
+    constexpr int RPP = PAGE / (2 * KT);  // rows per page
+    constexpr int LPR = KT / 512;         // 1 KiB wave loads per row
+    for (uint32_t pg = 0; pg < npages; ++pg) {
+        if ((int)(pg % NCW) != wave) {
+            page_skip(page0 + pg, lane);
+            continue;
         }
-    } else if constexpr (KT >= 512) {
-        constexpr int RPP = PAGE / (2 * KT);  // 4, 8 or 16 rows per page
-        constexpr int RW = RPP / NCW;         // rows of each page for each wave
-        constexpr int LPR = KT / 512;
-        for (uint32_t pg = 0; pg < npages; ++pg) {
-            if (!page_acquire(pp, page0 + pg, task)) return false;
-            if (wave == 0 && lane == 0) lds_st(S.tm[2], (uint32_t)rtc());
-            const uint32_t slot = (page0 + pg) % NPAGES;
-            uint4 wv[RW * LPR];
+        if (!page_acquire(pp, page0 + pg, task)) return false;
+        if (wave == 0 && lane == 0) lds_st(S.tm[2], (uint32_t)rtc());
+        const uint32_t slot = (page0 + pg) % NPAGES;
+        uint4 wv[RPP * LPR];
 #pragma unroll
-            for (int i = 0; i < RW * LPR; ++i) wv[i] = *(const uint4*)&ring[slot][(wave * RW * LPR + i) * 1024 + lane * 16];
-            page_release(page0 + pg, lane);
+        for (int i = 0; i < RPP * LPR; ++i) wv[i] = *(const uint4*)&ring[slot][i * 1024 + lane * 16];
+        page_release(page0 + pg, lane);
 #pragma unroll
-            for (int rr = 0; rr < RW; ++rr) {
-                float a = 0.f;
+        for (int rr = 0; rr < RPP; ++rr) {
+            float a = 0.f, b = 0.f;
 #pragma unroll
-                for (int j = 0; j < LPR; ++j) a = dot8(wv[rr * LPR + j], x + j * 8, a);
-                const float sum = wave_sum(a);
-                const uint32_t r = pg * RPP + wave * RW + rr;
-                if (lane == 0 && r < nrows) S.rowres[r] = sum;
+            for (int j = 0; j < LPR; j += 2) {
+                a = dot8(wv[rr * LPR + j], x + j * 8, a);
+                b = dot8(wv[rr * LPR + j + 1], x + (j + 1) * 8, b);
             }
+            const float sum = wave_sum(a + b);
+            const uint32_t r = pg * RPP + rr;
+            if (lane == 0 && r < nrows) S.rowres[r] = sum;
+        }
+    }
+    return true;
+}
+
+// ---- matrix-core GEMV (128 <= K <= 2048) --------------------------------------------------
+//
+// The activation x (fp32) is split exactly into three bf16 parts, x = hi + mid +
+// lo (8 significant bits each), kept in LDS as three bf16 arrays.  These are the
+// first three columns of the B operand of v_mfma_f32_16x16x32_bf16 (the other 13
+// are zero) and the weights the A operand, so D[m][0] + D[m][1] + D[m][2] is the
+// dot product of weight row m with x: products exact, fp32 accumulation.  The
+// weight tile is stored as 1 KiB blocks of 16 rows x 32 columns in operand order
+// (lane l: row l % 16, columns 8 (l / 16) .. +7); blocks row-group-major, 16 per
+// page; compute wave w owns the column blocks kb = w (mod 4), so every page holds
+// four blocks of every wave.  The waves' partial rows meet in S.rowres through
+// LDS float atomics.
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8v __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ uint16_t* split_arrays() { return (uint16_t*)&S.xs[0]; }
+
+// exact split of v: hi = v truncated to bf16, mid = the remainder truncated, lo = the rest
+__device__ __forceinline__ void split3(float v, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+    const uint32_t uh = __float_as_uint(v) & 0xffff0000u;
+    const float r1 = v - __uint_as_float(uh);
+    const uint32_t um = __float_as_uint(r1) & 0xffff0000u;
+    const float r2 = r1 - __uint_as_float(um);
+    hi = uh >> 16;
+    mid = um >> 16;
+    lo = __float_as_uint(r2) >> 16;
+}
+// columns c .. c+7 of x (c a multiple of 8) into the split arrays of a K = KT activation
+template <int KT>
+__device__ __forceinline__ void put_split8(int c, const float* v) {
+    uint32_t hh[4], mm[4], ll[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint32_t h0, m0, l0, h1, m1, l1;
+        split3(v[2 * i], h0, m0, l0);
+        split3(v[2 * i + 1], h1, m1, l1);
+        hh[i] = h0 | (h1 << 16);
+        mm[i] = m0 | (m1 << 16);
+        ll[i] = l0 | (l1 << 16);
+    }
+    uint16_t* sp = split_arrays();
+    *(u32x4v*)(sp + c) = u32x4v{hh[0], hh[1], hh[2], hh[3]};
+    *(u32x4v*)(sp + KT + c) = u32x4v{mm[0], mm[1], mm[2], mm[3]};
+    *(u32x4v*)(sp + 2 * KT + c) = u32x4v{ll[0], ll[1], ll[2], ll[3]};
+}
+template <int KT>
+__device__ __forceinline__ void put_split1(int c, float v) {
+    uint32_t h0, m0, l0;
+    split3(v, h0, m0, l0);
+    uint16_t* sp = split_arrays();
+    sp[c] = (uint16_t)h0;
+    sp[KT + c] = (uint16_t)m0;
+    sp[2 * KT + c] = (uint16_t)l0;
+}
+
+// Stage x (columns 8 tid .. +7 per lane) into the split arrays: from bf16 (srcb,
+// ordinary loads: the embedding) or fp32 written by other workgroups (srcf,
+// device-scope loads).  With gains (gp) x is multiplied by them; the sum of
+// squares of the unscaled x goes to S.ssq[wave] when wanted.
+template <int KT>
+__device__ __forceinline__ void stage_split(const uint16_t* srcb, const float* srcf, bool use_gains, uint4 gp,
+                                            bool want_ss, int tid, int wave, int lane) {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = 0.f;
+    const bool act = tid * 8 < KT;
+    if (srcb) {
+        if (act) {
+            const uint4 w = gld_u4(srcb + tid * 8);
+            v[0] = bf16lo(w.x); v[1] = bf16hi(w.x); v[2] = bf16lo(w.y); v[3] = bf16hi(w.y);
+            v[4] = bf16lo(w.z); v[5] = bf16hi(w.z); v[6] = bf16lo(w.w); v[7] = bf16hi(w.w);
         }
     } else {
-        constexpr int RPL = 1024 / (2 * KT);  // rows per 1 KiB load
-        constexpr int LPROW = 64 / RPL;       // lanes per row
-        constexpr int UW = 16 / NCW;          // 1 KiB groups of each page for each wave
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)srcf, 0, KT * 4, RSRC_FLAGS);
+        const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(r, tid * 32, 0, 16);
+        const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(r, tid * 32 + 16, 0, 16);
+        if (act) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                v[i] = __uint_as_float(a[i]);
+                v[4 + i] = __uint_as_float(b[i]);
+            }
+        }
+    }
+    if (want_ss) {
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ss = fmaf(v[i], v[i], ss);
+        ss = wave_sum(ss);
+        if (lane == 0) S.ssq[wave] = ss;
+    }
+    if (use_gains) {
+        v[0] *= bf16lo(gp.x); v[1] *= bf16hi(gp.x); v[2] *= bf16lo(gp.y); v[3] *= bf16hi(gp.y);
+        v[4] *= bf16lo(gp.z); v[5] *= bf16hi(gp.z); v[6] *= bf16lo(gp.w); v[7] *= bf16hi(gp.w);
+    }
+    if (act) put_split8<KT>(tid * 8, v);
+}
+// 1 / RMS of the staged activation from the per-wave partial sums (after a barrier)
+__device__ __forceinline__ float rms_from_ssq(int n, float eps) {
+    const float ss = (S.ssq[0] + S.ssq[1]) + (S.ssq[2] + S.ssq[3]);
+    return 1.0f / sqrtf(ss / (float)n + eps);
+}
+__device__ __forceinline__ void zero_rowres(int tid) { *(float4*)&S.rowres[tid * 4] = make_float4(0.f, 0.f, 0.f, 0.f); }
+
+// The B operands of this wave (column blocks kb = 4 i + wave): lanes 0..2 of each
+// 16-lane row carry hi, mid, lo of columns 32 kb + 8 (lane / 16) .. +7, the others zero.
+template <int KT>
+__device__ __forceinline__ void load_bop(int wave, int lane, u32x4v* B) {
+    const int n = lane % 16, kq = lane / 16;
+    const uint16_t* sp = split_arrays();
+#pragma unroll
+    for (int i = 0; i < KT / 128; ++i) {
+        const int col = (4 * i + wave) * 32 + kq * 8;
+        B[i] = n < 3 ? *(const u32x4v*)(sp + n * KT + col) : u32x4v{0u, 0u, 0u, 0u};
+    }
+}
+
+// Row group rg of the tile: add D[m][0] + D[m][1] + D[m][2] of this wave to S.rowres.
+__device__ __forceinline__ void flush_rows(f32x4v acc, uint32_t rg, int lane) {
+    const int n = lane % 16, kq = lane / 16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float v = acc[i];
+        const float s1 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xF, 0xF, true));
+        const float s2 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xF, 0xF, true));
+        const float t = v + s1 + s2;  // row_shr 1 and 2: lane n = 2 sums columns 0, 1, 2
+        if (n == 2 && rg * 16 < (uint32_t)ROWRES)
+            __hip_atomic_fetch_add(&S.rowres[rg * 16 + kq * 4 + i], t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+}
+
+template <int KT>
+__device__ __forceinline__ bool gemv_mfma(const Params* pp, int wave, int lane, uint32_t page0, uint32_t wbytes,
+                                          const u32x4v* B, uint32_t task) {
+    static_assert(KT >= 128 && KT <= 2048, "matrix-core GEMV covers 128 <= K <= 2048");
+    constexpr int NKB = KT / 32;  // column blocks
+    const uint32_t npages = (wbytes + PAGE - 1) / PAGE;
+    if constexpr (NKB >= 16) {
+        constexpr int PPR = NKB / 16;  // pages per row group
+        const uint32_t nrg = npages / PPR;
+        for (uint32_t rg = 0; rg < nrg; ++rg) {
+            // four independent accumulators (block slot j) keep the matrix core busy
+            f32x4v acc[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[j] = f32x4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < PPR; ++s) {
+                const uint32_t pg = rg * PPR + s;
+                if (!page_acquire(pp, page0 + pg, task)) return false;
+                if (wave == 0 && lane == 0) lds_st(S.tm[2], (uint32_t)rtc());
+                const uint32_t slot = (page0 + pg) % NPAGES;
+                u32x4v a[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) a[j] = *(const u32x4v*)&ring[slot][(4 * j + wave) * 1024 + lane * 16];
+                page_release(page0 + pg, lane);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8v, a[j]),
+                                                                     __builtin_bit_cast(bf16x8v, B[4 * s + j]), acc[j], 0,
+                                                                     0, 0);
+            }
+            flush_rows((acc[0] + acc[1]) + (acc[2] + acc[3]), rg, lane);
+        }
+    } else {
+        constexpr int RPG = 16 / NKB;  // row groups per page
+        constexpr int BPR = 4 / RPG;   // blocks per row group and wave
         for (uint32_t pg = 0; pg < npages; ++pg) {
             if (!page_acquire(pp, page0 + pg, task)) return false;
             if (wave == 0 && lane == 0) lds_st(S.tm[2], (uint32_t)rtc());
             const uint32_t slot = (page0 + pg) % NPAGES;
-            uint4 wv[UW];
+            u32x4v a[4];
 #pragma unroll
-            for (int u = 0; u < UW; ++u) wv[u] = *(const uint4*)&ring[slot][(wave * UW + u) * 1024 + lane * 16];
+            for (int j = 0; j < 4; ++j) a[j] = *(const u32x4v*)&ring[slot][(4 * j + wave) * 1024 + lane * 16];
             page_release(page0 + pg, lane);
 #pragma unroll
-            for (int u = 0; u < UW; ++u) {
-                const float a = seg_sum<LPROW>(dot8(wv[u], x, 0.f));
-                const uint32_t r = (pg * 16 + wave * UW + u) * RPL + lane / LPROW;
-                if ((lane % LPROW) == 0 && r < nrows) S.rowres[r] = a;
+            for (int rr = 0; rr < RPG; ++rr) {
+                f32x4v acc[BPR];
+#pragma unroll
+                for (int jj = 0; jj < BPR; ++jj)
+                    acc[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8v, a[rr * BPR + jj]),
+                                                                      __builtin_bit_cast(bf16x8v, B[jj]),
+                                                                      f32x4v{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                f32x4v sum = acc[0];
+#pragma unroll
+                for (int jj = 1; jj < BPR; ++jj) sum += acc[jj];
+                flush_rows(sum, pg * RPG + rr, lane);
             }
         }
     }
@@ -748,6 +907,26 @@ __device__ __forceinline__ void stage_x(CParams& p, int l, uint32_t parity, int 
     else stage_f32<H4>(0, acc_buf(p, parity, 2 * l - 1, 0), p.T.h, tid);
 }
 
+// Residual rows row0 + tid + 256 q of a residual-adding tile (zeros otherwise):
+// accumulator idx (device-scope loads) or, for idx < 0, the embedding row.
+__device__ __forceinline__ void load_residual(CParams& p, const Task& k, int idx, uint32_t parity, int tid, float* res) {
+#pragma unroll
+    for (int q = 0; q < MAX_TILE_ROWS / (NCW * 64); ++q) res[q] = 0.f;
+    if (!(k.flags & TF_RESID)) return;
+    if (idx < 0) {
+        const uint16_t* e = embed_row(p, 0) + k.row0;
+#pragma unroll
+        for (int q = 0; q < MAX_TILE_ROWS / (NCW * 64); ++q) {
+            const uint32_t i = (uint32_t)(tid + q * NCW * 64);
+            if (i < k.nrows) res[q] = bf16f(gld(e + i));
+        }
+    } else {
+        const __amdgpu_buffer_rsrc_t r = dev_rsrc(acc_buf(p, parity, idx, 0) + k.row0, k.nrows * 4);
+#pragma unroll
+        for (int q = 0; q < MAX_TILE_ROWS / (NCW * 64); ++q) res[q] = ldb_dev(r, (uint32_t)(tid + q * NCW * 64) * 4);
+    }
+}
+
 // ---- ops ---------------------------------------------------------------------------------
 
 // RMSNorm + QKV tile + RoPE + K/V append.  Tile rows [0, n) are the first halves
@@ -761,34 +940,38 @@ __device__ __noinline__ bool op_qkv(const Params* pp, uint32_t slot_, uint32_t p
     const uint32_t n = k.nrows, slot = k.part;
     const int half = p.T.d / 2, nq = p.T.nq, nkv = p.T.nkv;
     const int32_t P0 = S.pos[0];
-    uint4 gw[KT / 512 > 0 ? KT / 512 : 1];
-    if constexpr (KT >= 512) load_gains<KT>(gains(p, 2 * k.layer), lane, gw);
     float2 cs = make_float2(1.f, 0.f);
     if ((uint32_t)tid < n && slot < (uint32_t)(nq + nkv)) cs = gld_f2(p.rope + (size_t)P0 * half + k.row0 + tid);
-    if (!await_inputs(pp, k, c)) return false;
-    stage_x<(MAX_ACT + 1023) / 1024>(p, k.layer, c.parity, tid);
-    if (!cbarrier(pp, c, k.id)) return false;
-    tmark(c, 0);
-    {
-        float x[KT >= 512 ? KT / 64 : 8];
-        const float r = rms_scale(KT, p.eps, lane);
-        if constexpr (KT >= 512) {
-            load_x<KT>(0, lane, r, gw, x);
-        } else {
-            // small hidden sizes: apply the gains from LDS-staged activations directly
-            const uint16_t* g = gains(p, 2 * k.layer);
-            constexpr int LPROW = KT / 8;
-            load_x<KT>(0, lane, r, nullptr, x);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) x[i] *= bf16f(gld(g + (lane % LPROW) * 8 + i));
-        }
+    float r = 1.0f;  // 1/RMS, applied to the results (matrix-core path) or to x (K = 4096)
+    if constexpr (KT <= 2048) {
+        const uint4 gp = tid * 8 < KT ? gld_u4(gains(p, 2 * k.layer) + tid * 8) : make_uint4(0, 0, 0, 0);
+        if (!await_inputs(pp, k, c)) return false;
+        stage_split<KT>(k.layer == 0 ? embed_row(p, 0) : nullptr,
+                        k.layer == 0 ? nullptr : acc_buf(p, c.parity, 2 * k.layer - 1, 0), true, gp, true, tid, c.wave,
+                        lane);
+        zero_rowres(tid);
+        if (!cbarrier(pp, c, k.id)) return false;
+        tmark(c, 0);
+        r = rms_from_ssq(KT, p.eps);
+        u32x4v B[KT / 128];
+        load_bop<KT>(c.wave, lane, B);
+        if (!gemv_mfma<KT>(pp, c.wave, lane, page0, k.wbytes, B, k.id)) return false;
+    } else {
+        uint4 gw[KT / 512];
+        load_gains<KT>(gains(p, 2 * k.layer), lane, gw);
+        if (!await_inputs(pp, k, c)) return false;
+        stage_x<(MAX_ACT + 1023) / 1024>(p, k.layer, c.parity, tid);
+        if (!cbarrier(pp, c, k.id)) return false;
+        tmark(c, 0);
+        float x[KT / 64];
+        load_x<KT>(0, lane, rms_scale(KT, p.eps, lane), gw, x);
         if (!gemv_pages<KT>(pp, c.wave, lane, page0, 2 * n, k.wbytes, x, k.id)) return false;
     }
     if (!cbarrier(pp, c, k.id)) return false;
     tmark(c, 1);
     if ((uint32_t)tid < n) {
         const int j = (int)k.row0 + tid;
-        float lo = S.rowres[tid], hi = S.rowres[n + tid];
+        float lo = S.rowres[tid] * r, hi = S.rowres[n + tid] * r;
         if (slot < (uint32_t)(nq + nkv)) {
             const float a = lo * cs.x - hi * cs.y;
             const float b = lo * cs.y + hi * cs.x;
@@ -799,22 +982,11 @@ __device__ __noinline__ bool op_qkv(const Params* pp, uint32_t slot_, uint32_t p
             float* q = p.q + (size_t)slot * p.T.d;
             stf_dev(q + j, lo);
             stf_dev(q + j + half, hi);
-        }
-    }
-    if (slot >= (uint32_t)nq) {
-        const bool is_k = slot < (uint32_t)(nq + nkv);
-        const int g = is_k ? (int)slot - nq : (int)slot - nq - nkv;
-        uint16_t* base = (is_k ? S.args.kc : S.args.vc) +
-                         (((size_t)k.layer * p.T.B + 0) * nkv + g) * (size_t)p.T.C * p.T.d + (size_t)P0 * p.T.d;
-        if ((uint32_t)tid < n) {
-            const int j = (int)k.row0 + tid;
-            float lo = S.rowres[tid], hi = S.rowres[n + tid];
-            if (is_k) {
-                const float a = lo * cs.x - hi * cs.y;
-                const float b = lo * cs.y + hi * cs.x;
-                lo = a;
-                hi = b;
-            }
+        } else {
+            const bool is_k = slot < (uint32_t)(nq + nkv);
+            const int g = is_k ? (int)slot - nq : (int)slot - nq - nkv;
+            uint16_t* base = (is_k ? S.args.kc : S.args.vc) +
+                             (((size_t)k.layer * p.T.B + 0) * nkv + g) * (size_t)p.T.C * p.T.d + (size_t)P0 * p.T.d;
             st16_dev(base, (uint32_t)j, f2bf16(lo));
             st16_dev(base, (uint32_t)(j + half), f2bf16(hi));
         }
@@ -853,20 +1025,21 @@ __device__ __noinline__ bool op_attn(const Params* pp, uint32_t slot_, uint32_t 
     // each wave stages the query rows of its own heads, and the current token's K/V chunk
     float kc8[8], vc8[8];
     {
-        const float* qg = p.q + (size_t)b * p.T.nq * D + (size_t)g * G * D;
+        const __amdgpu_buffer_rsrc_t qr = dev_rsrc(p.q + (size_t)b * p.T.nq * D + (size_t)g * G * D, G * D * 4);
         float qv[4][D / 64];
 #pragma unroll
         for (int hh = 0; hh < 4; ++hh)
 #pragma unroll
             for (int ee = 0; ee < D / 64; ++ee)
-                qv[hh][ee] = hh < nh ? ldf_dev(qg + (wave + hh * NCW) * D + lane + 64 * ee) : 0.f;
+                qv[hh][ee] = hh < nh ? ldb_dev(qr, ((wave + hh * NCW) * D + lane + 64 * ee) * 4) : 0.f;
         if (has_cur) {
             const size_t row = (((size_t)k.layer * p.T.B + b) * p.T.nkv + g) * (size_t)p.T.C + (size_t)ch.P;
-            const uint32_t* kr = (const uint32_t*)(S.args.kc + row * D + cl * 8);
-            const uint32_t* vr = (const uint32_t*)(S.args.vc + row * D + cl * 8);
+            const __amdgpu_buffer_rsrc_t kr = dev_rsrc(S.args.kc + row * D, D * 2);
+            const __amdgpu_buffer_rsrc_t vr = dev_rsrc(S.args.vc + row * D, D * 2);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const uint32_t wk = ld_dev(kr + i), wv = ld_dev(vr + i);
+                const uint32_t wk = __float_as_uint(ldb_dev(kr, cl * 16 + i * 4));
+                const uint32_t wv = __float_as_uint(ldb_dev(vr, cl * 16 + i * 4));
                 kc8[2 * i] = bf16lo(wk);
                 kc8[2 * i + 1] = bf16hi(wk);
                 vc8[2 * i] = bf16lo(wv);
@@ -1029,36 +1202,24 @@ __device__ __noinline__ bool op_attn(const Params* pp, uint32_t slot_, uint32_t 
 // Merge of the attention partials of one KV group, O-proj K-slice, residual (atomic add).
 template <int KT>
 __device__ __noinline__ bool op_oproj(const Params* pp, uint32_t slot_, uint32_t page0, uint32_t t_, uint32_t epoch_) {
+    static_assert(KT <= 2048, "K of the O-projection slice is grp * head_dim <= 2048");
     const Task k = fifo_task(slot_);
     Ctx c = make_ctx(t_, epoch_);
     CParams& p = P(pp);
     const int lane = c.lane, tid = c.tid, wave = c.wave;
     if (!await_inputs(pp, k, c)) return false;
     const int D = p.T.d, Sp = p.T.attn_splits, G = p.T.grp;
-    // residual rows of this lane's epilogue (loaded now, used after the GEMV)
-    float res[MAX_TILE_ROWS / (NCW * 64)];
-#pragma unroll
-    for (int q = 0; q < MAX_TILE_ROWS / (NCW * 64); ++q) {
-        const uint32_t i = (uint32_t)(tid + q * NCW * 64);
-        res[q] = 0.f;
-        if ((k.flags & TF_RESID) && i < k.nrows) {
-            const uint32_t row = k.row0 + i;
-            res[q] = k.layer == 0 ? bf16f(gld(embed_row(p, 0) + row)) : ldf_dev(acc_buf(p, c.parity, 2 * k.layer - 1, 0) + row);
-        }
-    }
     // a = sum_c e^(m_c - M) o_c / sum_c e^(m_c - M) l_c, one wave per query head
+    const __amdgpu_buffer_rsrc_t pr = dev_rsrc(p.part + (size_t)k.part * Sp * G * (D + 2), Sp * G * (D + 2) * 4);
     for (int hw = wave; hw < G; hw += NCW) {
-        const float* src = p.part + ((size_t)k.part * Sp * G + hw) * (D + 2);
-        const size_t cs = (size_t)G * (D + 2);
+        const uint32_t cs = (uint32_t)G * (D + 2) * 4, h0 = (uint32_t)hw * (D + 2) * 4;
         float mc[16], lc[16], oc[16][2];
 #pragma unroll
         for (int cc = 0; cc < 16; ++cc) {
-            if (cc < Sp) {
-                mc[cc] = ldf_dev(src + cc * cs);
-                lc[cc] = ldf_dev(src + cc * cs + 1);
-                oc[cc][0] = ldf_dev(src + cc * cs + 2 + lane);
-                oc[cc][1] = D == 128 ? ldf_dev(src + cc * cs + 2 + 64 + lane) : 0.f;
-            }
+            mc[cc] = ldb_dev(pr, h0 + cc * cs);
+            lc[cc] = ldb_dev(pr, h0 + cc * cs + 4);
+            oc[cc][0] = ldb_dev(pr, h0 + cc * cs + (2 + lane) * 4);
+            oc[cc][1] = D == 128 ? ldb_dev(pr, h0 + cc * cs + (2 + 64 + lane) * 4) : 0.f;
         }
         float Mx = -INFINITY;
 #pragma unroll
@@ -1074,15 +1235,19 @@ __device__ __noinline__ bool op_oproj(const Params* pp, uint32_t slot_, uint32_t
                 n1 = fmaf(sc, oc[cc][1], n1);
             }
         }
-        S.xs[hw * D + lane] = n0 / den;
-        if (D == 128) S.xs[hw * D + 64 + lane] = n1 / den;
+        put_split1<KT>(hw * D + lane, n0 / den);
+        if (D == 128) put_split1<KT>(hw * D + 64 + lane, n1 / den);
     }
+    zero_rowres(tid);
     if (!cbarrier(pp, c, k.id)) return false;
     tmark(c, 0);
+    // residual rows of this lane's epilogue (in flight during the GEMV)
+    float res[MAX_TILE_ROWS / (NCW * 64)];
+    load_residual(p, k, k.layer == 0 ? -1 : 2 * k.layer - 1, c.parity, tid, res);
     {
-        float x[KT >= 512 ? KT / 64 : 8];
-        load_x<KT>(0, lane, 1.0f, nullptr, x);
-        if (!gemv_pages<KT>(pp, wave, lane, page0, k.nrows, k.wbytes, x, k.id)) return false;
+        u32x4v B[KT / 128];
+        load_bop<KT>(wave, lane, B);
+        if (!gemv_mfma<KT>(pp, wave, lane, page0, k.wbytes, B, k.id)) return false;
     }
     if (!cbarrier(pp, c, k.id)) return false;
     tmark(c, 1);
@@ -1102,30 +1267,33 @@ __device__ __noinline__ bool op_gateup(const Params* pp, uint32_t slot_, uint32_
     Ctx c = make_ctx(t_, epoch_);
     CParams& p = P(pp);
     const int lane = c.lane, tid = c.tid;
-    uint4 gw[KT / 512 > 0 ? KT / 512 : 1];
-    if constexpr (KT >= 512) load_gains<KT>(gains(p, 2 * k.layer + 1), lane, gw);
-    if (!await_inputs(pp, k, c)) return false;
-    stage_f32<(MAX_ACT + 1023) / 1024>(0, acc_buf(p, c.parity, 2 * k.layer, 0), p.T.h, tid);
-    if (!cbarrier(pp, c, k.id)) return false;
-    tmark(c, 0);
-    {
-        float x[KT >= 512 ? KT / 64 : 8];
-        const float r = rms_scale(KT, p.eps, lane);
-        if constexpr (KT >= 512) {
-            load_x<KT>(0, lane, r, gw, x);
-        } else {
-            const uint16_t* g = gains(p, 2 * k.layer + 1);
-            constexpr int LPROW = KT / 8;
-            load_x<KT>(0, lane, r, nullptr, x);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) x[i] *= bf16f(gld(g + (lane % LPROW) * 8 + i));
-        }
+    float r = 1.0f;
+    if constexpr (KT <= 2048) {
+        const uint4 gp = tid * 8 < KT ? gld_u4(gains(p, 2 * k.layer + 1) + tid * 8) : make_uint4(0, 0, 0, 0);
+        if (!await_inputs(pp, k, c)) return false;
+        stage_split<KT>(nullptr, acc_buf(p, c.parity, 2 * k.layer, 0), true, gp, true, tid, c.wave, lane);
+        zero_rowres(tid);
+        if (!cbarrier(pp, c, k.id)) return false;
+        tmark(c, 0);
+        r = rms_from_ssq(KT, p.eps);
+        u32x4v B[KT / 128];
+        load_bop<KT>(c.wave, lane, B);
+        if (!gemv_mfma<KT>(pp, c.wave, lane, page0, k.wbytes, B, k.id)) return false;
+    } else {
+        uint4 gw[KT / 512];
+        load_gains<KT>(gains(p, 2 * k.layer + 1), lane, gw);
+        if (!await_inputs(pp, k, c)) return false;
+        stage_f32<(MAX_ACT + 1023) / 1024>(0, acc_buf(p, c.parity, 2 * k.layer, 0), p.T.h, tid);
+        if (!cbarrier(pp, c, k.id)) return false;
+        tmark(c, 0);
+        float x[KT / 64];
+        load_x<KT>(0, lane, rms_scale(KT, p.eps, lane), gw, x);
         if (!gemv_pages<KT>(pp, c.wave, lane, page0, 2 * k.nrows, k.wbytes, x, k.id)) return false;
     }
     if (!cbarrier(pp, c, k.id)) return false;
     tmark(c, 1);
     for (uint32_t i = (uint32_t)tid; i < k.nrows; i += NCW * 64) {
-        const float gt = S.rowres[i], up = S.rowres[k.nrows + i];
+        const float gt = S.rowres[i] * r, up = S.rowres[k.nrows + i] * r;
         stf_dev(p.m + k.row0 + i, gt / (1.0f + __expf(-gt)) * up);
     }
     return true;
@@ -1134,24 +1302,23 @@ __device__ __noinline__ bool op_gateup(const Params* pp, uint32_t slot_, uint32_
 // Down-proj K-slice tile + residual (atomic add).
 template <int KT>
 __device__ __noinline__ bool op_down(const Params* pp, uint32_t slot_, uint32_t page0, uint32_t t_, uint32_t epoch_) {
+    static_assert(KT <= 2048, "down-projection K blocks are at most 1024 columns");
     const Task k = fifo_task(slot_);
     Ctx c = make_ctx(t_, epoch_);
     CParams& p = P(pp);
     const int lane = c.lane, tid = c.tid;
     if (!await_inputs(pp, k, c)) return false;
-    float res[MAX_TILE_ROWS / (NCW * 64)];
-#pragma unroll
-    for (int q = 0; q < MAX_TILE_ROWS / (NCW * 64); ++q) {
-        const uint32_t i = (uint32_t)(tid + q * NCW * 64);
-        res[q] = (k.flags & TF_RESID) && i < k.nrows ? ldf_dev(acc_buf(p, c.parity, 2 * k.layer, 0) + k.row0 + i) : 0.f;
-    }
-    stage_f32<(MAX_ACT + 1023) / 1024>(0, p.m + (size_t)k.part * KT, KT, tid);
+    stage_split<KT>(nullptr, p.m + (size_t)k.part * KT, false, make_uint4(0, 0, 0, 0), false, tid, c.wave, lane);
+    zero_rowres(tid);
     if (!cbarrier(pp, c, k.id)) return false;
     tmark(c, 0);
+    // residual rows of this lane's epilogue (in flight during the GEMV)
+    float res[MAX_TILE_ROWS / (NCW * 64)];
+    load_residual(p, k, 2 * k.layer, c.parity, tid, res);
     {
-        float x[KT >= 512 ? KT / 64 : 8];
-        load_x<KT>(0, lane, 1.0f, nullptr, x);
-        if (!gemv_pages<KT>(pp, c.wave, lane, page0, k.nrows, k.wbytes, x, k.id)) return false;
+        u32x4v B[KT / 128];
+        load_bop<KT>(c.wave, lane, B);
+        if (!gemv_mfma<KT>(pp, c.wave, lane, page0, k.wbytes, B, k.id)) return false;
     }
     if (!cbarrier(pp, c, k.id)) return false;
     tmark(c, 1);
@@ -1171,24 +1338,29 @@ __device__ __noinline__ bool op_lmhead(const Params* pp, uint32_t slot_, uint32_
     Ctx c = make_ctx(t_, epoch_);
     CParams& p = P(pp);
     const int lane = c.lane, tid = c.tid;
-    uint4 gw[KT / 512 > 0 ? KT / 512 : 1];
-    if constexpr (KT >= 512) load_gains<KT>(gains(p, 2 * p.T.L), lane, gw);
-    if (!await_inputs(pp, k, c)) return false;
-    stage_x<(MAX_ACT + 1023) / 1024>(p, p.T.L, c.parity, tid);
-    if (!cbarrier(pp, c, k.id)) return false;
-    tmark(c, 0);
-    {
-        float x[KT >= 512 ? KT / 64 : 8];
-        const float r = rms_scale(KT, p.eps, lane);
-        if constexpr (KT >= 512) {
-            load_x<KT>(0, lane, r, gw, x);
-        } else {
-            const uint16_t* g = gains(p, 2 * p.T.L);
-            constexpr int LPROW = KT / 8;
-            load_x<KT>(0, lane, r, nullptr, x);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) x[i] *= bf16f(gld(g + (lane % LPROW) * 8 + i));
-        }
+    const int L = p.T.L;
+    float r = 1.0f;
+    if constexpr (KT <= 2048) {
+        const uint4 gp = tid * 8 < KT ? gld_u4(gains(p, 2 * L) + tid * 8) : make_uint4(0, 0, 0, 0);
+        if (!await_inputs(pp, k, c)) return false;
+        stage_split<KT>(L == 0 ? embed_row(p, 0) : nullptr, L == 0 ? nullptr : acc_buf(p, c.parity, 2 * L - 1, 0), true,
+                        gp, true, tid, c.wave, lane);
+        zero_rowres(tid);
+        if (!cbarrier(pp, c, k.id)) return false;
+        tmark(c, 0);
+        r = rms_from_ssq(KT, p.eps);
+        u32x4v B[KT / 128];
+        load_bop<KT>(c.wave, lane, B);
+        if (!gemv_mfma<KT>(pp, c.wave, lane, page0, k.wbytes, B, k.id)) return false;
+    } else {
+        uint4 gw[KT / 512];
+        load_gains<KT>(gains(p, 2 * L), lane, gw);
+        if (!await_inputs(pp, k, c)) return false;
+        stage_x<(MAX_ACT + 1023) / 1024>(p, L, c.parity, tid);
+        if (!cbarrier(pp, c, k.id)) return false;
+        tmark(c, 0);
+        float x[KT / 64];
+        load_x<KT>(0, lane, rms_scale(KT, p.eps, lane), gw, x);
         if (!gemv_pages<KT>(pp, c.wave, lane, page0, k.nrows, k.wbytes, x, k.id)) return false;
     }
     if (!cbarrier(pp, c, k.id)) return false;
@@ -1197,7 +1369,7 @@ __device__ __noinline__ bool op_lmhead(const Params* pp, uint32_t slot_, uint32_
     uint32_t bi = 0xffffffffu;
     float* logits = S.args.logits;
     for (uint32_t i = (uint32_t)tid; i < k.nrows; i += NCW * 64) {
-        const float val = S.rowres[i];
+        const float val = S.rowres[i] * r;
         if (logits) gst(logits + k.row0 + i, val);
         if (val > bv) {  // rows visited in increasing order: the first maximum is kept
             bv = val;
@@ -1241,13 +1413,18 @@ __device__ __noinline__ void finish_step(const Params* pp, uint32_t epoch, uint3
 }
 
 #define MK_KT_DISPATCH(fn, kt, ...)                                      \
-    ((kt) == 64     ? fn<64>(__VA_ARGS__)                                \
-     : (kt) == 128  ? fn<128>(__VA_ARGS__)                               \
+    ((kt) == 128    ? fn<128>(__VA_ARGS__)                               \
      : (kt) == 256  ? fn<256>(__VA_ARGS__)                               \
      : (kt) == 512  ? fn<512>(__VA_ARGS__)                               \
      : (kt) == 1024 ? fn<1024>(__VA_ARGS__)                              \
      : (kt) == 2048 ? fn<2048>(__VA_ARGS__)                              \
                     : fn<4096>(__VA_ARGS__))
+#define MK_KT_DISPATCH_2K(fn, kt, ...)                                   \
+    ((kt) == 128    ? fn<128>(__VA_ARGS__)                               \
+     : (kt) == 256  ? fn<256>(__VA_ARGS__)                               \
+     : (kt) == 512  ? fn<512>(__VA_ARGS__)                               \
+     : (kt) == 1024 ? fn<1024>(__VA_ARGS__)                              \
+                    : fn<2048>(__VA_ARGS__))
 
 // ---- compute-wave main loop ---------------------------------------------------------------
 
@@ -1272,9 +1449,9 @@ __device__ __noinline__ void compute(const Params* pp, uint32_t epoch, int wave)
         switch (k.op) {
             case OP_QKV: ok = MK_KT_DISPATCH(op_qkv, h, pp, slot, page0, t, epoch); break;
             case OP_ATTN: ok = hd == 64 ? op_attn<64>(pp, slot, page0, t, epoch) : op_attn<128>(pp, slot, page0, t, epoch); break;
-            case OP_OPROJ: ok = MK_KT_DISPATCH(op_oproj, okt, pp, slot, page0, t, epoch); break;
+            case OP_OPROJ: ok = MK_KT_DISPATCH_2K(op_oproj, okt, pp, slot, page0, t, epoch); break;
             case OP_GATEUP: ok = MK_KT_DISPATCH(op_gateup, h, pp, slot, page0, t, epoch); break;
-            case OP_DOWN: ok = MK_KT_DISPATCH(op_down, dkt, pp, slot, page0, t, epoch); break;
+            case OP_DOWN: ok = MK_KT_DISPATCH_2K(op_down, dkt, pp, slot, page0, t, epoch); break;
             case OP_LMHEAD: ok = MK_KT_DISPATCH(op_lmhead, h, pp, slot, page0, t, epoch); break;
             default: break;
         }
@@ -1387,6 +1564,34 @@ __global__ void __launch_bounds__(256) repack_kernel(const CopyOp* ops, uint8_t*
         uint4* d = (uint4*)(dst + op.dst_off + (uint64_t)r * op.row_bytes);
         for (uint32_t i = threadIdx.x; i < n16; i += 256) d[i] = s[i];
     }
+}
+
+// GEMV tiles: one workgroup per tile, one 16-byte element per thread and step.
+__global__ void __launch_bounds__(256) repack_tiles_kernel(const TileOp* ops, const uint8_t* const* rowsrc, uint8_t* dst) {
+    const TileOp op = ops[blockIdx.x];
+    const uint32_t n16 = op.rows * (op.kt / 8);
+    const uint32_t nkb = op.kt / 32;
+    for (uint32_t e = threadIdx.x; e < n16; e += 256) {
+        uint32_t row, col;
+        if (op.blocked) {
+            const uint32_t b = e / 64, l = e % 64;
+            row = (b / nkb) * 16 + l % 16;
+            col = (b % nkb) * 32 + (l / 16) * 8;
+        } else {
+            row = e / (op.kt / 8);
+            col = (e % (op.kt / 8)) * 8;
+        }
+        const uint8_t* src = rowsrc[op.row_base + row];
+        const uint4 v = src ? *(const uint4*)(src + (uint64_t)col * 2) : make_uint4(0, 0, 0, 0);
+        *(uint4*)(dst + op.dst_off + (uint64_t)e * 16) = v;
+    }
+}
+
+hipError_t launch_repack_tiles(const TileOp* ops, uint32_t n_ops, const uint8_t* const* rowsrc, uint8_t* dst,
+                               hipStream_t stream) {
+    if (n_ops == 0) return hipSuccess;
+    hipLaunchKernelGGL(repack_tiles_kernel, dim3(n_ops), dim3(256), 0, stream, ops, rowsrc, dst);
+    return hipGetLastError();
 }
 
 hipError_t launch_repack(const CopyOp* ops, uint32_t n_ops, uint8_t* dst, hipStream_t stream) {

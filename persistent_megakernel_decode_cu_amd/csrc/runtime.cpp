@@ -93,9 +93,10 @@ mk_status plan(const mk_model_desc* desc, int32_t batch, int32_t max_ctx, const 
     return MK_OK;
 }
 
-// Copy the caller's weights into the packed layout (gains, embedding, LM head,
-// then per layer the QKV, O, gate/up and down tiles in task order) with one
-// repacking kernel.
+// Copy the caller's weights into the packed layout: gains and embedding row by
+// row (CopyOp), then every GEMV tile in task order (TileOp): rows of the tile
+// come from a host-built table of row addresses (null = a zero row of padding),
+// and tiles with 128 <= K <= 2048 are stored as 16 x 32 matrix-core blocks.
 mk_status repack(mk_handle* h, const mk_model_desc* d, uint8_t* wd) {
     const Tiling& T = h->g.T;
     const Layout& Ly = h->g.lay;
@@ -120,10 +121,18 @@ mk_status repack(mk_handle* h, const mk_model_desc* d, uint8_t* wd) {
     }
     add(d->final_norm, Ly.gains + (uint64_t)(2 * T.L) * rowb, 1, rowb, rowb);
     add(d->tok_embed, Ly.embed, (uint64_t)T.V, rowb, rowb);
-    if (!h->tied) add(d->lm_head, Ly.lm, (uint64_t)T.V, rowb, rowb);
+
+    std::vector<TileOp> tiles;
+    std::vector<const uint8_t*> rows;
     const int half = T.d / 2, P = T.qkv_pairs;
+    const uint8_t* lm = (const uint8_t*)(h->tied ? d->tok_embed : d->lm_head);
     for (const Task& k : h->g.tasks) {
+        if (k.op == OP_ATTN || k.wbytes == 0) continue;
         const mk_layer_weights& lw = d->layers[k.layer < T.L ? k.layer : 0];
+        TileOp t;
+        t.dst_off = k.wofs;
+        t.row_base = (uint32_t)rows.size();
+        uint32_t kt = (uint32_t)T.h;
         if (k.op == OP_QKV) {
             const uint8_t* src;
             int hrow;
@@ -137,28 +146,46 @@ mk_status repack(mk_handle* h, const mk_model_desc* d, uint8_t* wd) {
                 src = (const uint8_t*)lw.wv;
                 hrow = (k.part - T.nq - T.nkv) * T.d;
             }
-            add(src + (uint64_t)(hrow + k.row0) * rowb, k.wofs, P, rowb, rowb);
-            add(src + (uint64_t)(hrow + k.row0 + half) * rowb, k.wofs + (uint64_t)P * rowb, P, rowb, rowb);
+            for (int i = 0; i < P; ++i) rows.push_back(src + (uint64_t)(hrow + k.row0 + i) * rowb);
+            for (int i = 0; i < P; ++i) rows.push_back(src + (uint64_t)(hrow + k.row0 + half + i) * rowb);
         } else if (k.op == OP_OPROJ) {
-            const uint64_t kt = (uint64_t)T.grp * T.d;
-            const uint8_t* src = (const uint8_t*)lw.wo + ((uint64_t)k.row0 * T.nq * T.d + k.part * kt) * 2;
-            add(src, k.wofs, k.nrows, kt * 2, (uint64_t)T.nq * T.d * 2);
+            kt = (uint32_t)(T.grp * T.d);
+            const uint64_t pitch = (uint64_t)T.nq * T.d * 2;
+            for (uint32_t i = 0; i < k.nrows; ++i)
+                rows.push_back((const uint8_t*)lw.wo + (uint64_t)(k.row0 + i) * pitch + (uint64_t)k.part * kt * 2);
         } else if (k.op == OP_GATEUP) {
-            const uint64_t nb = (uint64_t)k.nrows * rowb;
-            add((const uint8_t*)lw.w_gate + (uint64_t)k.row0 * rowb, k.wofs, k.nrows, rowb, rowb);
-            add((const uint8_t*)lw.w_up + (uint64_t)k.row0 * rowb, k.wofs + nb, k.nrows, rowb, rowb);
+            for (uint32_t i = 0; i < k.nrows; ++i) rows.push_back((const uint8_t*)lw.w_gate + (uint64_t)(k.row0 + i) * rowb);
+            for (uint32_t i = 0; i < k.nrows; ++i) rows.push_back((const uint8_t*)lw.w_up + (uint64_t)(k.row0 + i) * rowb);
         } else if (k.op == OP_DOWN) {
-            const uint64_t kd = (uint64_t)T.kd;
-            const uint8_t* src = (const uint8_t*)lw.w_down + ((uint64_t)k.row0 * T.f + (uint64_t)k.part * kd) * 2;
-            add(src, k.wofs, k.nrows, kd * 2, (uint64_t)T.f * 2);
+            kt = (uint32_t)T.kd;
+            const uint64_t pitch = (uint64_t)T.f * 2;
+            for (uint32_t i = 0; i < k.nrows; ++i)
+                rows.push_back((const uint8_t*)lw.w_down + (uint64_t)(k.row0 + i) * pitch + (uint64_t)k.part * kt * 2);
+        } else if (k.op == OP_LMHEAD) {
+            for (uint32_t i = 0; i < k.nrows; ++i) rows.push_back(lm + (uint64_t)(k.row0 + i) * rowb);
         }
+        t.kt = kt;
+        t.rows = (uint32_t)(k.wbytes / (kt * 2));
+        while (rows.size() < (size_t)t.row_base + t.rows) rows.push_back(nullptr);
+        t.blocked = kt <= 2048 ? 1u : 0u;
+        tiles.push_back(t);
     }
     CopyOp* dops = nullptr;
-    HIPCHK(hipMalloc(&dops, ops.size() * sizeof(CopyOp)));
-    hipError_t e = hipMemcpy(dops, ops.data(), ops.size() * sizeof(CopyOp), hipMemcpyHostToDevice);
+    TileOp* dtiles = nullptr;
+    const uint8_t** drows = nullptr;
+    hipError_t e = hipMalloc(&dops, std::max<size_t>(1, ops.size()) * sizeof(CopyOp));
+    if (e == hipSuccess) e = hipMalloc(&dtiles, std::max<size_t>(1, tiles.size()) * sizeof(TileOp));
+    if (e == hipSuccess) e = hipMalloc(&drows, std::max<size_t>(1, rows.size()) * sizeof(void*));
+    if (e == hipSuccess) e = hipMemcpy(dops, ops.data(), ops.size() * sizeof(CopyOp), hipMemcpyHostToDevice);
+    if (e == hipSuccess && !tiles.empty())
+        e = hipMemcpy(dtiles, tiles.data(), tiles.size() * sizeof(TileOp), hipMemcpyHostToDevice);
+    if (e == hipSuccess && !rows.empty()) e = hipMemcpy(drows, rows.data(), rows.size() * sizeof(void*), hipMemcpyHostToDevice);
     if (e == hipSuccess) e = launch_repack(dops, (uint32_t)ops.size(), wd, nullptr);
+    if (e == hipSuccess) e = launch_repack_tiles(dtiles, (uint32_t)tiles.size(), drows, wd, nullptr);
     if (e == hipSuccess) e = hipDeviceSynchronize();
     (void)hipFree(dops);
+    (void)hipFree(dtiles);
+    (void)hipFree(drows);
     HIPCHK(e);
     return MK_OK;
 }

@@ -67,6 +67,18 @@ struct CopyOp {
 };
 hipError_t launch_repack(const CopyOp* ops, uint32_t n_ops, uint8_t* dst, hipStream_t stream);
 
+// One GEMV weight tile of the repacking: `rows` rows (a multiple of 16) of kt
+// bf16 columns, row r read from rowsrc[row_base + r] (null: zeros), written to
+// dst + dst_off either row by row (blocked = 0) or as 16 x 32 matrix-core blocks
+// (blocked = 1; block b = (row group b / (kt/32), column block b % (kt/32)),
+// lane l of a block holds row 16*rg + l%16, columns 32*kb + 8*(l/16) .. +7).
+struct TileOp {
+    uint64_t dst_off;
+    uint32_t row_base, rows, kt, blocked;
+};
+hipError_t launch_repack_tiles(const TileOp* ops, uint32_t n_ops, const uint8_t* const* rowsrc, uint8_t* dst,
+                               hipStream_t stream);
+
 hipError_t launch_step(const Params* dparams, const StepArgs& a, uint32_t grid, hipStream_t stream, bool cooperative);
 int step_threads();
 size_t step_lds_bytes();

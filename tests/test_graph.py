@@ -20,7 +20,7 @@ HEADER = os.path.join(ROOT, "include", "mk.h")
 FIXTURE = os.path.join(ROOT, "tests", "golden", "tiny_graph.txt")
 OPS = {"QKV": tg.OP_QKV, "ATTN": tg.OP_ATTN, "OPROJ": tg.OP_OPROJ, "GATEUP": tg.OP_GATEUP, "DOWN": tg.OP_DOWN,
        "LMHEAD": tg.OP_LMHEAD}
-TOY = synth.configs.ModelConfig("toy-1layer", 1, 64, 1, 1, 64, 64, 64, True, 10000.0)
+TOY = synth.configs.ModelConfig("toy-1layer", 1, 128, 1, 1, 128, 128, 64, True, 10000.0)
 
 
 def declared_functions():
@@ -110,7 +110,7 @@ def read_fixture():
 def test_oracle_builder_matches_hand_derived_toy_graph():
     rows, meta = read_fixture()
     g = tg.build(TOY, 1, 64, 2)
-    assert len(g["tasks"]) == len(rows) == 21
+    assert len(g["tasks"]) == len(rows) == 33
     for want, got in zip(rows, g["tasks"]):
         for k, v in want.items():
             assert got[k] == v, (want["id"], k, got[k], v)
@@ -157,6 +157,8 @@ def test_planner_rejects_what_it_does_not_implement():
         plan(cfg.with_(n_q=3), 4)
     with pytest.raises(mk.MkError):
         plan(cfg.with_(hidden=8192), 4)
+    with pytest.raises(mk.MkError):
+        plan(cfg.with_(hidden=64), 4)
 
 
 @pytest.mark.parametrize("W", [1, 3, 16, 37])
