@@ -7,10 +7,12 @@ synthetic weights ~N(0, 0.02), bf16 KV cache prefilled with N(0, 1) to
 context 1024, batch 1; K greedy decode steps at positions 1024, 1025, ...
 with the next token chained on the device.  One step = one kernel launch.
 
-Prints one JSON line: steps/s (value), ms and us per step, the roofline of the
-megakernel (algorithmic bytes = weights + KV read per step, against the 8 TB/s
-HBM peak), the one-kernel-per-op HIP baseline on the same inputs, and the
-oracle's CPU time on a bounded sample.
+Prints one JSON line: steps/s (value, launch gaps included), ms and us per step,
+the roofline of the megakernel (algorithmic bytes = weights + KV read per step,
+over the kernel's own average launch duration from an event pair around every
+launch, against the 8 TB/s HBM peak; measured HBM traffic from the committed
+counter profile when it matches the kernel source), the one-kernel-per-op HIP
+baseline on the same inputs, and the oracle's CPU time on a bounded sample.
 
   python bench.py [--gpus 1] [--steps 256] [--warmup 10] [--sched static|dynamic]
 """
@@ -33,6 +35,23 @@ def step_bytes(cfg, positions):
     """Algorithmic bytes of one decode step: every weight once + K and V rows 0..P of every layer."""
     kv = 4 * cfg.n_layers * cfg.n_kv * cfg.head_dim * (np.asarray(positions, np.int64) + 1)
     return cfg.weight_bytes() + int(kv.sum())
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mk_step_kernel_llama1b_b1_traffic.json")
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE passes (scaled by the same
+    counters on a plain copy of known size), or None if the kernel source changed since they were taken."""
+    import hashlib
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+        src = b"".join(open(os.path.join(ROOT, f), "rb").read() for f in rec["source_files"])
+    except (OSError, KeyError, ValueError):
+        return None
+    if hashlib.sha256(src).hexdigest() != rec.get("source_sha256"):
+        return None
+    return int(rec["traffic_bytes_per_launch"])
 
 
 def cpu_baseline(cfg, w, kc, vc, tok, P0, budget_s=10.0):
@@ -112,6 +131,8 @@ def main():
     ap.add_argument("--attn-splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-baseline", action="store_true", help="skip the one-kernel-per-op baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy three times (reference for the HBM byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -170,13 +191,23 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     ms_total = e0.elapsed_time(e1)
+    # the same steps again with an event pair around every launch: the kernel's own duration
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for s_ in range(K):
+        ev[s_][0].record(stream)
+        tptr = nxt
+        mk.mk_decode_step(h, tptr, positions[s_:s_ + 1].data_ptr(), kv.data_ptr(), logits.data_ptr(), sp)
+        ev[s_][1].record(stream)
+    torch.cuda.synchronize()
+    ms_launch = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     err = mk.mk_check_device_error(h)
     if err:
         raise SystemExit(f"device error: {err}")
     ms = ms_total / K
     pos_list = list(range(P0, P0 + K))
     bytes_mean = np.mean([step_bytes(cfg, [p]) for p in pos_list])
-    achieved = bytes_mean / (ms * 1e-3) / 1e9
+    achieved = bytes_mean / (ms_launch * 1e-3) / 1e9
+    traffic = measured_traffic()
 
     out = {
         "metric": METRIC,
@@ -198,10 +229,22 @@ def main():
                    "workgroups": int(graph["header"]["W"]), "tasks_per_step": int(graph["header"]["n_tasks"]),
                    "attn_splits": int(graph["header"]["attn_splits"])},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "algorithmic_bytes_per_step": int(bytes_mean)},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_step": int(bytes_mean), "kernel_us_per_launch": round(ms_launch * 1000, 2),
+                     "throughput_GBps_incl_launch_gaps": round(bytes_mean / (ms * 1e-3) / 1e9, 1)},
     }
     mk.mk_destroy(h)
+
+    if args.copy_calibration:
+        n = 256 << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").random_(0, 255)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = n
+        del src, dst
 
     if not args.no_baseline:
         out["multi_kernel_baseline"] = baseline_leg(mk, torch, cfg, model, kc, vc, tok, P0, C, K, W, ms)
