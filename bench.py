@@ -129,6 +129,7 @@ def main():
     ap.add_argument("--sched", choices=["static", "dynamic"], default="static")
     ap.add_argument("--policy", choices=["rr", "lpt"], default="rr")
     ap.add_argument("--attn-splits", type=int, default=0)
+    ap.add_argument("--cooperative", action="store_true", help="cooperative launch instead of the default plain one")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-baseline", action="store_true", help="skip the one-kernel-per-op baseline")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -157,7 +158,7 @@ def main():
     dev = {k: torch.from_numpy(v.view(np.int16)).cuda() for k, v in w.items()}
     model = mk.Model(cfg, dev)
     opt = mk.options(sched=0 if args.sched == "static" else 1, policy=0 if args.policy == "rr" else 1,
-                     attn_splits=args.attn_splits)
+                     attn_splits=args.attn_splits, cooperative=1 if args.cooperative else 0)
     h = mk.mk_build_graph(model.desc, 1, C, opt)
     graph = mk.parse_export(mk.mk_export_graph(h))
     kv = torch.from_numpy(np.concatenate([kc.reshape(-1), vc.reshape(-1)]).view(np.int16)).cuda()
@@ -226,6 +227,7 @@ def main():
         "config": {"workload": f"{cfg.name} greedy decode, batch 1, positions {P0}..{P0 + K - 1}, bf16 weights "
                                f"and KV cache, one kernel launch per step",
                    "batch": 1, "first_position": P0, "max_ctx": C, "sched": args.sched, "policy": args.policy,
+                   "launch": "cooperative" if args.cooperative else "plain",
                    "workgroups": int(graph["header"]["W"]), "tasks_per_step": int(graph["header"]["n_tasks"]),
                    "attn_splits": int(graph["header"]["attn_splits"])},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -79,7 +79,12 @@ typedef struct {
     int32_t debug_timeout_ms;  /* bound on every in-kernel wait; 0 = 2000 ms */
     int32_t debug_drop_signal; /* >= 0: the task with this index skips its signal (tests); -1 = off */
     int32_t trace;             /* 1: record per-task timestamps (mk_read_trace) */
-    int32_t reserved[9];
+    int32_t cooperative;       /* 1: cooperative launch (co-residency of every workgroup guaranteed by the
+                                  runtime, about 20 us more per step); 0 (default): plain launch of one
+                                  workgroup per CU, which needs the device to itself: if some workgroups
+                                  could not start, the others' waits time out and the step reports
+                                  MK_E_DEVICE instead of hanging */
+    int32_t reserved[8];
 } mk_options;
 
 /* Validates the description, copies the weights into a handle-owned packed

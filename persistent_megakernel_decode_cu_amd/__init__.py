@@ -45,11 +45,13 @@ class ModelDesc(ctypes.Structure):
 
 class Options(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("sched", "n_workgroups", "policy", "attn_splits", "debug_timeout_ms",
-                                               "debug_drop_signal", "trace")] + [("reserved", ctypes.c_int32 * 9)]
+                                               "debug_drop_signal", "trace", "cooperative")] + \
+               [("reserved", ctypes.c_int32 * 8)]
 
 
-def options(sched=0, n_workgroups=0, policy=0, attn_splits=0, debug_timeout_ms=0, debug_drop_signal=-1, trace=0):
-    return Options(sched, n_workgroups, policy, attn_splits, debug_timeout_ms, debug_drop_signal, trace)
+def options(sched=0, n_workgroups=0, policy=0, attn_splits=0, debug_timeout_ms=0, debug_drop_signal=-1, trace=0,
+            cooperative=0):
+    return Options(sched, n_workgroups, policy, attn_splits, debug_timeout_ms, debug_drop_signal, trace, cooperative)
 
 
 # task record (48 bytes, mirrors mk::Task)

@@ -18,7 +18,7 @@ using namespace mk;
 struct mk_handle {
     int device = 0;
     int W = 0;
-    bool cooperative = true;
+    bool cooperative = false;  // plain launch unless asked (mk_options.cooperative)
     bool tied = true;
     Graph g;
     Params p;           // host copy
@@ -259,6 +259,7 @@ mk_status mk_build_graph(const mk_model_desc* desc, int32_t batch, int32_t max_c
     o.debug_drop_signal = -1;
     if (opt) o = *opt;
     mk_handle* h = new mk_handle();
+    h->cooperative = o.cooperative != 0;
     HIPCHK(hipGetDevice(&h->device));
     hipDeviceProp_t prop;
     HIPCHK(hipGetDeviceProperties(&prop, h->device));

@@ -42,12 +42,12 @@ def _greedy(run, tok, P0, steps):
     return out.cpu().numpy()
 
 
-@pytest.mark.parametrize("sched", [0, 1])
-def test_llama1b_first_step(inputs, sched):
+@pytest.mark.parametrize("sched,coop", [(0, 0), (1, 0), (0, 1)])
+def test_llama1b_first_step(inputs, sched, coop):
     g, w, kc, vc, tok = inputs
     P0 = g["first_position"]
-    print(f"case llama1b first step sched={sched}", flush=True)
-    run = Runner(CFG, w, 1, g["max_ctx"], kc, vc, sched=sched)
+    print(f"case llama1b first step sched={sched} cooperative={coop}", flush=True)
+    run = Runner(CFG, w, 1, g["max_ctx"], kc, vc, sched=sched, cooperative=coop)
     run.step(tok, [P0])
     run.check()
     logits = run.logits.cpu().numpy()[0]

@@ -119,6 +119,26 @@ def test_tiny_dynamic_queue_greedy():
     assert got == ref["tokens"][:, 0].tolist()
 
 
+def test_tiny_cooperative_launch_greedy():
+    """The same greedy chain with the runtime's cooperative launch instead of the default plain one."""
+    cfg = synth.configs.TINY
+    C, P0, steps = 512, 77, 12
+    w, kc, vc, tok, pos = _setup(cfg, C, P0)
+    run = Runner(cfg, w, 1, C, kc, vc, cooperative=1)
+    positions = torch.arange(P0, P0 + steps, dtype=torch.int32, device="cuda")
+    t0 = torch.tensor(tok, dtype=torch.int32, device="cuda")
+    nxt = mk.mk_next_tokens(run.h)
+    got = []
+    for s in range(steps):
+        mk.mk_decode_step(run.h, t0.data_ptr() if s == 0 else nxt, positions[s:s + 1].data_ptr(), run.kv.data_ptr(),
+                          run.logits.data_ptr(), torch.cuda.current_stream().cuda_stream)
+        got.append(int(run.next_tokens().cpu()[0]))
+    run.check()
+    run.close()
+    ref = oracle.greedy(cfg, w, tok, [P0], kc.copy(), vc.copy(), steps)
+    assert got == ref["tokens"][:, 0].tolist()
+
+
 def test_bad_token_is_a_device_error_not_a_hang():
     cfg = synth.configs.TINY
     w, kc, vc, tok, pos = _setup(cfg, 256, 10)
