@@ -52,7 +52,8 @@ int plan_tiling(const Dims& dm, int B, int C, int W, const PlanOptions& o, Tilin
     if (dm.d != 64 && dm.d != 128) return fail("head_dim must be 64 or 128");
     if (dm.nq % dm.nkv) return fail("n_q_heads must be a multiple of n_kv_heads");
     if (dm.n_experts != 0) return fail("mixture-of-experts FFN is not implemented by this build");
-    if (B != 1) return fail("batch > 1 is not implemented by this build");
+    if (B > MAX_BATCH) return fail("batch is limited to 16 sequences per step");
+    if (B > 1 && dm.h > 2048) return fail("batch > 1 needs hidden <= 2048");
     if (dm.f <= 0) return fail("ffn_dim must be positive");
     if (!gemv_k_ok(dm.h) || dm.h > MAX_ACT) return fail("hidden must be a power of two in [128, 4096]");
     const int grp = dm.nq / dm.nkv;
@@ -66,27 +67,34 @@ int plan_tiling(const Dims& dm, int B, int C, int W, const PlanOptions& o, Tilin
     T.qkv_pairs = 8;
     T.n_qkv_tiles = (dm.nq + 2 * dm.nkv) * (dm.d / 2) / T.qkv_pairs;
     int S = o.attn_splits;
-    if (S <= 0) S = (int)std::max<int64_t>(1, std::min<int64_t>(16, (C + 255) / 256));
+    if (S <= 0) {
+        S = (int)std::max<int64_t>(1, std::min<int64_t>(16, (C + 255) / 256));
+        // with several sequences, about one attention task per workgroup and layer
+        if (B > 1) S = (int)std::max<int64_t>(1, std::min<int64_t>(S, W / ((int64_t)B * dm.nkv)));
+    }
     if (S > C) S = C;
     T.attn_splits = S;
     T.n_attn_tiles = B * dm.nkv * S;
+    // rows x sequences of a tile fit the LDS row-result buffer
+    const int64_t max_rows = MAX_TILE_ROWS / B;
     // O-proj: tiles (KV group g, rows) with K = grp*d columns; about W tiles per layer
-    T.o_rows = (int)std::min<int64_t>(std::min<int64_t>(dm.h, MAX_TILE_ROWS),
+    T.o_rows = (int)std::min<int64_t>(std::min<int64_t>(dm.h, max_rows),
                                       std::max<int64_t>(16, pow2_floor((int64_t)dm.h * dm.nkv / W)));
     T.n_o_tiles = dm.nkv * (dm.h / T.o_rows);
     // down-proj K blocks of kd columns of m; gate/up tiles feed whole K blocks
     T.kd = (int)std::min<int64_t>(1024, dm.f);
     if (dm.f % T.kd || !gemv_k_ok(T.kd)) return fail("ffn_dim must be a multiple of 1024 (or a power of two in [128, 1024))");
     const int64_t n_kb = dm.f / T.kd;
-    T.d_rows = (int)std::min<int64_t>(std::min<int64_t>(dm.h, MAX_TILE_ROWS),
+    T.d_rows = (int)std::min<int64_t>(std::min<int64_t>(dm.h, max_rows),
                                       std::max<int64_t>(16, pow2_floor((int64_t)dm.h * n_kb / W)));
     T.n_down_tiles = (int)(n_kb * (dm.h / T.d_rows));
     T.g_rows = (int)std::max<int64_t>(8, pow2_ceil((dm.f + W - 1) / W));
     if (T.g_rows > T.kd) T.g_rows = T.kd;
-    if (T.g_rows > MAX_TILE_ROWS / 2) T.g_rows = MAX_TILE_ROWS / 2;
+    if (T.g_rows > max_rows / 2) T.g_rows = (int)(max_rows / 2);
     if (T.kd % T.g_rows) return fail("gate/up tile does not divide the down-proj K block");
     T.n_gu_tiles = dm.f / T.g_rows;
-    T.lm_rows = (int)std::min<int64_t>(MAX_TILE_ROWS, round16((dm.V + W - 1) / W));
+    T.lm_rows = (int)std::min<int64_t>(max_rows, round16((dm.V + W - 1) / W));
+    T.norm_cols = B > 1 ? (int)std::min<int64_t>(dm.h, 256) : 0;
     T.n_lm_tiles = (dm.V + T.lm_rows - 1) / T.lm_rows;
     return 0;
 }
@@ -157,15 +165,34 @@ int build_graph(const Tiling& T, const Layout& Ly, int sched, int policy, Graph*
         return k;
     };
 
+    const bool batched = T.B > 1;
+    // batch > 1: NORM tasks prepare the normalised input of the next GEMVs for all
+    // sequences (column blocks of norm_cols), signalling `ev`
+    auto add_norm = [&](int layer, int kind, uint32_t wait, uint32_t ev) {
+        for (int c0 = 0; c0 < T.h; c0 += T.norm_cols) {
+            Task k = blank(OP_NORM, layer);
+            k.part = (uint16_t)kind;
+            k.row0 = (uint32_t)c0;
+            k.nrows = (uint32_t)T.norm_cols;
+            k.wait_ev = wait;
+            k.sig_ev = ev;
+            add(k);
+        }
+    };
+
     uint32_t ev_x = NONE;  // residual stream ready for the current layer (NONE for layer 0: embedding)
     for (int l = 0; l < L; ++l) {
         const uint64_t lbase = Ly.layer0 + (uint64_t)l * Ly.layer_bytes;
-        std::vector<uint32_t> ev_qkv(T.nkv), ev_attn(T.nkv), ev_m(n_kb);
+        std::vector<uint32_t> ev_qkv(T.nkv), ev_attn(T.nkv), ev_mg(T.nkv), ev_m(n_kb);
+        const uint32_t ev_n1 = batched ? g.new_event() : NONE;
         for (int gi = 0; gi < T.nkv; ++gi) ev_qkv[gi] = g.new_event();
         for (int gi = 0; gi < T.nkv; ++gi) ev_attn[gi] = g.new_event();
+        for (int gi = 0; gi < T.nkv; ++gi) ev_mg[gi] = batched ? g.new_event() : ev_attn[gi];
         const uint32_t ev_xb = g.new_event();
+        const uint32_t ev_n2 = batched ? g.new_event() : ev_xb;
         for (int kb = 0; kb < n_kb; ++kb) ev_m[kb] = g.new_event();
         const uint32_t ev_next = g.new_event();
+        if (batched) add_norm(l, 0, ev_x, ev_n1);
 
         // fused RMSNorm + QKV + RoPE tiles, grouped by KV head: q heads of the group, then its k and v head
         uint64_t tile = 0;
@@ -177,7 +204,7 @@ int build_graph(const Tiling& T, const Layout& Ly, int sched, int policy, Graph*
                     k.part = (uint16_t)slot;
                     k.row0 = (uint32_t)(pb * T.qkv_pairs);
                     k.nrows = (uint32_t)T.qkv_pairs;
-                    k.wait_ev = ev_x;
+                    k.wait_ev = batched ? ev_n1 : ev_x;
                     k.sig_ev = ev_qkv[gi];
                     k.wbytes = (uint32_t)(2 * T.qkv_pairs * h * 2);
                     k.wofs = lbase + Ly.qkv + tile * k.wbytes;
@@ -198,6 +225,16 @@ int build_graph(const Tiling& T, const Layout& Ly, int sched, int policy, Graph*
                     k.sig_ev = ev_attn[gi];
                     add(k);
                 }
+        // batch > 1: merge of each KV group's partials for all sequences
+        if (batched)
+            for (int gi = 0; gi < T.nkv; ++gi) {
+                Task k = blank(OP_MERGE, l);
+                k.part = (uint16_t)gi;
+                k.nrows = (uint32_t)grp;
+                k.wait_ev = ev_attn[gi];
+                k.sig_ev = ev_mg[gi];
+                add(k);
+            }
         // O-proj K slices: tile (group, row block)
         const int o_kt = grp * T.d;
         for (int gi = 0; gi < T.nkv; ++gi)
@@ -207,18 +244,19 @@ int build_graph(const Tiling& T, const Layout& Ly, int sched, int policy, Graph*
                 k.row0 = (uint32_t)(rb * T.o_rows);
                 k.nrows = (uint32_t)T.o_rows;
                 k.flags = gi == 0 ? TF_RESID : 0;
-                k.wait_ev = ev_attn[gi];
+                k.wait_ev = ev_mg[gi];
                 k.sig_ev = ev_xb;
                 k.wbytes = (uint32_t)((uint64_t)T.o_rows * o_kt * 2);
                 k.wofs = lbase + Ly.o + ((uint64_t)gi * (T.h / T.o_rows) + rb) * k.wbytes;
                 add(k);
             }
         // RMSNorm + gate/up + SiLU tiles
+        if (batched) add_norm(l, 1, ev_xb, ev_n2);
         for (int t = 0; t < T.n_gu_tiles; ++t) {
             Task k = blank(OP_GATEUP, l);
             k.row0 = (uint32_t)(t * T.g_rows);
             k.nrows = (uint32_t)T.g_rows;
-            k.wait_ev = ev_xb;
+            k.wait_ev = ev_n2;
             k.sig_ev = ev_m[(t * T.g_rows) / T.kd];
             k.wbytes = (uint32_t)(2ull * T.g_rows * h * 2);
             k.wofs = lbase + Ly.gu + (uint64_t)t * k.wbytes;
@@ -241,11 +279,16 @@ int build_graph(const Tiling& T, const Layout& Ly, int sched, int policy, Graph*
         ev_x = ev_next;
     }
     // final RMSNorm + LM head + argmax
+    uint32_t ev_nf = ev_x;
+    if (batched) {
+        ev_nf = g.new_event();
+        add_norm(L, 2, ev_x, ev_nf);
+    }
     for (int t = 0; t < T.n_lm_tiles; ++t) {
         Task k = blank(OP_LMHEAD, L);
         k.row0 = (uint32_t)(t * T.lm_rows);
         k.nrows = (uint32_t)std::min<int64_t>(T.lm_rows, (int64_t)T.V - (int64_t)t * T.lm_rows);
-        k.wait_ev = ev_x;
+        k.wait_ev = ev_nf;
         k.wbytes = (uint32_t)((uint64_t)round16(k.nrows) * h * 2);
         k.wofs = Ly.lm + (uint64_t)k.row0 * h * 2;
         add(k);
@@ -308,6 +351,7 @@ size_t export_graph(const Graph& g, void* buf, size_t cap) {
     hd.grp = T.grp; hd.qkv_pairs = T.qkv_pairs; hd.attn_splits = T.attn_splits; hd.o_rows = T.o_rows;
     hd.g_rows = T.g_rows; hd.kd = T.kd; hd.d_rows = T.d_rows; hd.lm_rows = T.lm_rows;
     hd.record_bytes = sizeof(Task);
+    hd.norm_cols = T.norm_cols;
     uint8_t* p = (uint8_t*)buf;
     memcpy(p, &hd, sizeof(hd));
     p += sizeof(hd);

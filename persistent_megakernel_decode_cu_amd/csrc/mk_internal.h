@@ -14,13 +14,18 @@ enum Op : uint8_t {
     OP_GATEUP = 4,    // RMSNorm + gate/up GEMV tile + SiLU * up
     OP_DOWN = 5,      // down-proj K-slice tile + residual (atomic)
     OP_LMHEAD = 6,    // final RMSNorm + LM-head tile + argmax (packed 64-bit atomic max)
-    OP_COUNT = 7
+    // batch > 1 only: the GEMV inputs of all sequences are prepared once in global
+    // memory as matrix-core operands (sequences = operand columns)
+    OP_NORM = 7,      // column block of RMSNorm inputs: sum of squares per sequence, gains, operand split
+    OP_MERGE = 8,     // merge of one KV group's attention partials for every sequence, operand split
+    OP_COUNT = 9
 };
 
 constexpr uint32_t NONE = 0xFFFFFFFFu;
 
 // Device-side capacities the tiling must respect.
-constexpr int MAX_TILE_ROWS = 1024;  // rows of one GEMV tile (LDS row-result buffer)
+constexpr int MAX_TILE_ROWS = 1024;  // rows x sequences of one GEMV tile (LDS row-result buffer)
+constexpr int MAX_BATCH = 16;        // sequences per step (columns of one matrix-core operand)
 constexpr int MAX_ACT = 4096;        // floats of one staged activation vector (LDS)
 
 // One instruction of the interpreter: 48 bytes, read by the loader wave into LDS.
@@ -30,9 +35,9 @@ struct Task {
     uint8_t sig_nsub;      // sub-counters of the signalled event (1 or 8)
     uint8_t flags;         // op-specific (OPROJ/DOWN: add the residual)
     uint16_t layer;
-    uint16_t part;         // QKV: head slot; ATTN/OPROJ: KV group; DOWN: K block; others 0
-    uint32_t row0;         // first output row (QKV: first RoPE pair; ATTN: chunk index)
-    uint32_t nrows;        // output rows of the tile (QKV: pairs)
+    uint16_t part;         // QKV: head slot; ATTN/OPROJ/MERGE: KV group; DOWN: K block; NORM: 0 attn, 1 ffn, 2 final
+    uint32_t row0;         // first output row (QKV: first RoPE pair; ATTN: chunk index; NORM: first column)
+    uint32_t nrows;        // output rows of the tile (QKV: pairs; NORM: columns)
     uint32_t wait_ev;      // awaited event or NONE
     uint32_t wait_target;  // producers of the awaited event (per step)
     uint32_t sig_ev;       // signalled event or NONE
@@ -60,13 +65,14 @@ struct Tiling {
     int32_t d_rows;       // down-proj tile rows
     int32_t lm_rows;      // LM-head rows per tile
     int32_t n_qkv_tiles, n_attn_tiles, n_o_tiles, n_gu_tiles, n_down_tiles, n_lm_tiles;  // per layer / total LM
+    int32_t norm_cols;    // batch > 1: columns per NORM task (0 for batch 1)
 };
 
 // Byte layout of the handle-owned packed weight buffer.
 struct Layout {
     uint64_t gains;       // (2L+1) x h bf16: attn_norm[l], ffn_norm[l] (l = 0..L-1), final
     uint64_t embed;       // V x h
-    uint64_t lm;          // V x h (== embed when tied)
+    uint64_t lm;          // LM-head tiles (a copy of its own even when tied to the embedding)
     uint64_t layer0;      // start of layer 0
     uint64_t layer_bytes; // bytes per layer
     uint64_t qkv, o, gu, down;  // offsets within a layer
@@ -83,7 +89,8 @@ struct ExportHeader {
     int32_t L, h, nq, nkv, d, f, V, B, C;
     int32_t grp, qkv_pairs, attn_splits, o_rows, g_rows, kd, d_rows, lm_rows;
     uint32_t record_bytes;
-    uint32_t reserved[7];
+    int32_t norm_cols;
+    uint32_t reserved[6];
 };
 constexpr uint32_t EXPORT_MAGIC = 0x31474B4Du;
 

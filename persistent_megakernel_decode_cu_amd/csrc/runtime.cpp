@@ -81,7 +81,7 @@ mk_status plan(const mk_model_desc* desc, int32_t batch, int32_t max_ctx, const 
     Tiling T;
     std::string err;
     Dims dm = dims_of(desc);
-    if (dm.n_experts != 0 || batch != 1) {
+    if (dm.n_experts != 0 || batch > MAX_BATCH || (batch > 1 && dm.h > 2048)) {
         if (dm.n_experts < 0 || batch < 1) return MK_E_INVALID;
         return MK_E_UNSUPPORTED;
     }
@@ -270,6 +270,10 @@ mk_status mk_build_graph(const mk_model_desc* desc, int32_t batch, int32_t max_c
     if (h->W > max_resident) {
         delete h;
         return MK_E_NOT_RESIDENT;
+    }
+    if (batch > 1) {  // planned (mk_plan_graph) but not yet run by the interpreter
+        delete h;
+        return MK_E_UNSUPPORTED;
     }
     mk_status st = plan(desc, batch, max_ctx, &o, h->W, &h->g, &h->tied);
     if (st != MK_OK) {

@@ -68,10 +68,11 @@ def plan(cfg, W, B=1, C=2048, sched=0, policy=0, attn_splits=0):
     return mk.parse_export(mk.mk_plan_graph(model.desc, B, C, opt, W))
 
 
-def compare(ex, g, cfg, W, C):
+def compare(ex, g, cfg, W, C, B=1):
     hd = ex["header"]
     t = g["tiling"]
-    assert (hd["W"], hd["C"], hd["B"]) == (W, C, 1)
+    assert (hd["W"], hd["C"], hd["B"]) == (W, C, B)
+    assert hd["norm_cols"] == t["norm_cols"]
     assert (hd["L"], hd["h"], hd["nq"], hd["nkv"], hd["d"], hd["f"], hd["V"]) == (
         cfg.n_layers, cfg.hidden, cfg.n_q, cfg.n_kv, cfg.head_dim, cfg.ffn, cfg.vocab)
     assert (hd["grp"], hd["qkv_pairs"], hd["attn_splits"], hd["o_rows"], hd["g_rows"], hd["kd"], hd["d_rows"],
@@ -147,10 +148,43 @@ def test_library_planner_equals_oracle_graph(cfg, W, C, sched, policy, splits):
         tg.check(g, cfg, 1)
 
 
+BATCH_CASES = [
+    (synth.configs.TINY, 3, 37, 512, 0),
+    (synth.configs.TINY, 16, 256, 512, 1),
+    (synth.configs.LLAMA_1B, 16, 256, 4352, 0),
+    (synth.configs.LLAMA_1B, 4, 256, 2048, 1),
+]
+
+
+@pytest.mark.parametrize("cfg,B,W,C,policy", BATCH_CASES,
+                         ids=[f"{c[0].name}-B{c[1]}-W{c[2]}-C{c[3]}-p{c[4]}" for c in BATCH_CASES])
+def test_batched_planner_equals_oracle_graph(cfg, B, W, C, policy):
+    """Batch > 1 adds NORM (operand preparation) and MERGE tasks; the library builds exactly the oracle's graph."""
+    ex = plan(cfg, W, B=B, C=C, policy=policy)
+    g = tg.build(cfg, B, C, W, policy=policy)
+    compare(ex, g, cfg, W, C, B)
+    tg.check(g, cfg, B)
+    n = len(g["tasks"])
+    assert tg.simulate(g, W, seed=B) == n
+    assert tg.simulate(g, W, seed=B + 1, dynamic=True) == n
+
+
+def test_batched_checker_catches_a_missing_merge_wait():
+    cfg = synth.configs.TINY
+    g = tg.build(cfg, 3, 512, 8)
+    k = next(k for k in g["tasks"] if k["op"] == tg.OP_OPROJ and k["part"] == 1)
+    k["wait_ev"] = next(t["sig_ev"] for t in g["tasks"] if t["op"] == tg.OP_ATTN and t["part"] == 1)
+    k["wait_target"] = g["target"][k["wait_ev"]]
+    with pytest.raises(AssertionError):
+        tg.check(g, cfg, 3)
+
+
 def test_planner_rejects_what_it_does_not_implement():
     cfg = synth.configs.TINY
     with pytest.raises(mk.MkError):
-        plan(cfg, 4, B=2)
+        plan(cfg, 4, B=17)
+    with pytest.raises(mk.MkError):
+        plan(synth.configs.LLAMA_8B, 256, B=2)
     with pytest.raises(mk.MkError):
         plan(cfg.with_(head_dim=96), 4)
     with pytest.raises(mk.MkError):
