@@ -93,7 +93,7 @@ int plan_tiling(const Dims& dm, int B, int C, int W, const PlanOptions& o, Tilin
     if (T.g_rows > max_rows / 2) T.g_rows = (int)(max_rows / 2);
     if (T.kd % T.g_rows) return fail("gate/up tile does not divide the down-proj K block");
     T.n_gu_tiles = dm.f / T.g_rows;
-    T.lm_rows = (int)std::min<int64_t>(max_rows, round16((dm.V + W - 1) / W));
+    T.lm_rows = (int)std::min<int64_t>(max_rows / 16 * 16, round16((dm.V + W - 1) / W));  // whole 16-row groups
     T.norm_cols = B > 1 ? (int)std::min<int64_t>(dm.h, 256) : 0;
     T.n_lm_tiles = (dm.V + T.lm_rows - 1) / T.lm_rows;
     return 0;

@@ -1391,6 +1391,394 @@ __device__ __noinline__ bool op_lmhead(const Params* pp, uint32_t slot_, uint32_
     return true;
 }
 
+// ---- batch > 1 -------------------------------------------------------------------------
+//
+// The GEMV inputs of all B sequences live in global memory as matrix-core B
+// operands (columns = sequences), written with device-scope stores by the NORM /
+// MERGE / gate-up tasks and read with device-scope loads, so that one pass over a
+// weight tile serves every sequence.  Each fp32 input is carried as two bf16 parts,
+// hi = its truncation to bf16 and lo = the remainder rounded to bf16, so hi + lo
+// is within 2^-17 of it (relative); both parts go through the same weights.
+
+constexpr int NPART = 2;
+constexpr int OPS_PER_COL = NPART * MAX_BATCH;  // bf16 elements per column of an operand region
+
+__device__ __forceinline__ uint16_t* opr_norm(CParams& p, int slot) { return p.xop + (size_t)slot * OPS_PER_COL * p.T.h; }
+__device__ __forceinline__ uint16_t* opr_attn(CParams& p, int l) {
+    return p.xop + ((size_t)(2 * p.T.L + 1) * p.T.h + (size_t)l * p.T.nq * p.T.d) * OPS_PER_COL;
+}
+__device__ __forceinline__ uint16_t* opr_m(CParams& p, int l) {
+    return p.xop + ((size_t)(2 * p.T.L + 1) * p.T.h + (size_t)p.T.L * p.T.nq * p.T.d + (size_t)l * p.T.f) * OPS_PER_COL;
+}
+// element of (part, column c, sequence b) in a region of nkb 32-column blocks: block
+// (part, c / 32) holds 64 lanes x 8 elements, lane = 16 ((c % 32) / 8) + b
+__device__ __forceinline__ uint32_t opr_index(int nkb, int part, int c, int b) {
+    return ((uint32_t)(part * nkb + (c >> 5)) * 64u + (uint32_t)(((c & 31) >> 3) * 16 + b)) * 8u + (uint32_t)(c & 7);
+}
+__device__ __forceinline__ float* ssq_at(CParams& p, uint32_t parity, int slot) {
+    return p.ssq + ((size_t)parity * (2 * p.T.L + 1) + slot) * p.T.B;
+}
+__device__ __forceinline__ void split2(float v, uint32_t& hi, uint32_t& lo) {
+    const uint32_t uh = __float_as_uint(v) & 0xffff0000u;
+    hi = uh >> 16;
+    lo = f2bf16(v - __uint_as_float(uh));
+}
+// the split of x[c .. c+7] of sequence b (c a multiple of 8) into region R
+__device__ __forceinline__ void put_op8(uint16_t* R, int nkb, int c, int b, const float* v) {
+    uint32_t hh[4], ll[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint32_t h0, l0, h1, l1;
+        split2(v[2 * i], h0, l0);
+        split2(v[2 * i + 1], h1, l1);
+        hh[i] = h0 | (h1 << 16);
+        ll[i] = l0 | (l1 << 16);
+    }
+    const __amdgpu_buffer_rsrc_t r = dev_rsrc(R, (uint32_t)nkb * NPART * 1024u);
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4{hh[0], hh[1], hh[2], hh[3]}, r, opr_index(nkb, 0, c, b) * 2, 0, 16);
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4{ll[0], ll[1], ll[2], ll[3]}, r, opr_index(nkb, 1, c, b) * 2, 0, 16);
+}
+__device__ __forceinline__ void put_op1(uint16_t* R, int nkb, int c, int b, float v) {
+    uint32_t h0, l0;
+    split2(v, h0, l0);
+    const __amdgpu_buffer_rsrc_t r = dev_rsrc(R, (uint32_t)nkb * NPART * 1024u);
+    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)h0, r, opr_index(nkb, 0, c, b) * 2, 0, 16);
+    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)l0, r, opr_index(nkb, 1, c, b) * 2, 0, 16);
+}
+
+// NORM (layer l, kind 0 attention / 1 FFN / 2 final, columns [c0, c0 + nc)): for
+// every sequence, the partial sum of squares of x (added into ssq) and the operand
+// split of x * gains.  1/RMS is applied by the GEMV epilogues.
+__device__ __noinline__ bool op_norm(const Params* pp, uint32_t slot_, uint32_t t_, uint32_t epoch_) {
+    const Task k = fifo_task(slot_);
+    Ctx c = make_ctx(t_, epoch_);
+    CParams& p = P(pp);
+    const int tid = c.tid, B = p.T.B, h = p.T.h, L = p.T.L;
+    const int l = k.layer, kind = k.part;
+    const int slot = kind == 2 ? 2 * L : 2 * l + kind;
+    // the residual stream entering this norm: accumulator index, or -1 for the embedding
+    const int src = kind == 1 ? 2 * l : (l == 0 ? -1 : 2 * l - 1);
+    const int CH = (int)k.nrows / 8;  // 8-column chunks per sequence (16 or 32)
+    if (!await_inputs(pp, k, c)) return false;
+    uint16_t* R = opr_norm(p, slot);
+    float* ss_out = ssq_at(p, c.parity, slot);
+    const uint16_t* g = gains(p, slot);
+    for (int base = 0; base < B * CH; base += NCW * 64) {
+        const int idx = base + tid;
+        const bool act = idx < B * CH;
+        const int b = act ? idx / CH : 0, col = (int)k.row0 + (idx % CH) * 8;
+        float v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = 0.f;
+        if (act) {
+            if (src < 0) {
+                const uint4 w = gld_u4((const uint16_t*)(p.w + p.lay.embed) + (size_t)S.tok[b] * h + col);
+                v[0] = bf16lo(w.x); v[1] = bf16hi(w.x); v[2] = bf16lo(w.y); v[3] = bf16hi(w.y);
+                v[4] = bf16lo(w.z); v[5] = bf16hi(w.z); v[6] = bf16lo(w.w); v[7] = bf16hi(w.w);
+            } else {
+                const __amdgpu_buffer_rsrc_t r = dev_rsrc(acc_buf(p, c.parity, src, b) + col, 32);
+                const u32x4 a0 = __builtin_amdgcn_raw_buffer_load_b128(r, 0, 0, 16);
+                const u32x4 a1 = __builtin_amdgcn_raw_buffer_load_b128(r, 16, 0, 16);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    v[i] = __uint_as_float(a0[i]);
+                    v[4 + i] = __uint_as_float(a1[i]);
+                }
+            }
+        }
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ss = fmaf(v[i], v[i], ss);
+        ss = CH == 32 ? seg_sum<32>(ss) : seg_sum<16>(ss);
+        if (act && idx % CH == 0)
+            __hip_atomic_fetch_add((g_f32*)&ss_out[b], ss, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (act) {
+            const uint4 gw = gld_u4(g + col);
+            v[0] *= bf16lo(gw.x); v[1] *= bf16hi(gw.x); v[2] *= bf16lo(gw.y); v[3] *= bf16hi(gw.y);
+            v[4] *= bf16lo(gw.z); v[5] *= bf16hi(gw.z); v[6] *= bf16lo(gw.w); v[7] *= bf16hi(gw.w);
+            put_op8(R, h / 32, col, b, v);
+        }
+    }
+    return true;
+}
+
+// MERGE (layer l, KV group g): the attention output of every sequence from its
+// chunks' partials, as operands for the O-projection.  Lane = (sequence, head,
+// 8-dimension chunk); the chunks' maxima and sums are read first, the partial
+// outputs in groups of four chunks.
+__device__ __noinline__ bool op_merge(const Params* pp, uint32_t slot_, uint32_t t_, uint32_t epoch_) {
+    const Task k = fifo_task(slot_);
+    Ctx c = make_ctx(t_, epoch_);
+    CParams& p = P(pp);
+    const int tid = c.tid, B = p.T.B, D = p.T.d, G = p.T.grp, Sp = p.T.attn_splits, g = k.part;
+    if (!await_inputs(pp, k, c)) return false;
+    uint16_t* R = opr_attn(p, k.layer);
+    const int nkb = p.T.nq * D / 32, per_b = G * D / 8;
+    const uint32_t cs = (uint32_t)G * (D + 2);  // floats per chunk
+    for (int idx = tid; idx < B * per_b; idx += NCW * 64) {
+        const int b = idx / per_b, head = (idx % per_b) / (D / 8), ch = idx % (D / 8);
+        const float* src = p.part + ((((size_t)b * p.T.nkv + g) * Sp) * G + head) * (D + 2);
+        const __amdgpu_buffer_rsrc_t r = dev_rsrc(src, (uint32_t)((Sp - 1) * cs + D + 2) * 4);
+        float mc[16], lc[16];
+#pragma unroll
+        for (int cc = 0; cc < 16; ++cc) {
+            mc[cc] = cc < Sp ? ldb_dev(r, (uint32_t)(cc * cs) * 4) : -INFINITY;
+            lc[cc] = cc < Sp ? ldb_dev(r, (uint32_t)(cc * cs + 1) * 4) : 0.f;
+        }
+        float Mx = -INFINITY;
+#pragma unroll
+        for (int cc = 0; cc < 16; ++cc) Mx = fmaxf(Mx, mc[cc]);
+        float den = 0.f, num[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) num[e] = 0.f;
+#pragma unroll
+        for (int c4 = 0; c4 < 16; c4 += 4) {
+            if (c4 >= Sp) break;
+            float oc[4][8];
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    oc[cc][e] = c4 + cc < Sp ? ldb_dev(r, (uint32_t)((c4 + cc) * cs + 2 + ch * 8 + e) * 4) : 0.f;
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) {
+                const float m = mc[c4 + cc];
+                const float sc = m == -INFINITY ? 0.f : __expf(m - Mx);
+                den = fmaf(sc, lc[c4 + cc], den);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) num[e] = fmaf(sc, oc[cc][e], num[e]);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) num[e] /= den;
+        put_op8(R, nkb, (g * G + head) * D + ch * 8, b, num);
+    }
+    return true;
+}
+
+// Batched matrix-core GEMV: as gemv_mfma, with the B operands (16 sequences, one
+// MFMA per bf16 part) of this wave's column blocks kb = 4 i + wave loaded from the
+// operand region R (nkb_total column blocks, this tile's columns starting at block
+// kb_off) once per task and held in registers.  Results in S.rowres[row * B + b].
+__device__ __forceinline__ void flush_rows_b(f32x4v acc, uint32_t rg, int lane, int B) {
+    const int n = lane % 16, kq = lane / 16;
+    if (n < B) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t at = (rg * 16 + kq * 4 + i) * (uint32_t)B + n;
+            if (at < (uint32_t)ROWRES)
+                __hip_atomic_fetch_add(&S.rowres[at], acc[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+    }
+}
+template <int NB>
+__device__ __forceinline__ void load_bops_b(__amdgpu_buffer_rsrc_t r, int nkb_total, int kb0, int lane,
+                                            u32x4v (*bo)[NPART]) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int pt = 0; pt < NPART; ++pt)
+            bo[i][pt] = __builtin_bit_cast(
+                u32x4v, __builtin_amdgcn_raw_buffer_load_b128(
+                            r, ((uint32_t)(pt * nkb_total + kb0 + 4 * i) * 64u + (uint32_t)lane) * 16u, 0, 16));
+}
+__device__ __forceinline__ f32x4v mfma_parts(u32x4v a, const u32x4v* b2, f32x4v acc) {
+#pragma unroll
+    for (int pt = 0; pt < NPART; ++pt)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8v, a), __builtin_bit_cast(bf16x8v, b2[pt]),
+                                                      acc, 0, 0, 0);
+    return acc;
+}
+// K >= 512: the tile's pages are stored k-step major (page s * nrg + rg holds column
+// blocks 16 s .. 16 s + 15 of row group rg), so each wave needs the B operands of
+// only four column blocks at a time (the next k-step's are loaded meanwhile) and
+// every page's products are added into the row results.  K <= 256: a page holds
+// 16 / (K / 32) whole row groups and the B operands are loaded once.
+template <int KT>
+__device__ __forceinline__ bool gemv_mfma_b(const Params* pp, int wave, int lane, uint32_t page0, uint32_t wbytes,
+                                            const uint16_t* R, int nkb_total, int kb_off, int B, uint32_t task) {
+    static_assert(KT >= 128 && KT <= 2048, "matrix-core GEMV covers 128 <= K <= 2048");
+    constexpr int NKB = KT / 32;
+    const uint32_t npages = (wbytes + PAGE - 1) / PAGE;
+    const __amdgpu_buffer_rsrc_t r = dev_rsrc(R, (uint32_t)nkb_total * NPART * 1024u);
+    if constexpr (NKB >= 16) {
+        constexpr int PPR = NKB / 16;
+        const uint32_t nrg = npages / PPR;
+        u32x4v bo[2][4][NPART];
+        load_bops_b<4>(r, nkb_total, kb_off + wave, lane, bo[0]);
+#pragma unroll
+        for (int s = 0; s < PPR; ++s) {
+            if (s + 1 < PPR) load_bops_b<4>(r, nkb_total, kb_off + 16 * (s + 1) + wave, lane, bo[(s + 1) & 1]);
+            for (uint32_t rg = 0; rg < nrg; ++rg) {
+                const uint32_t pg = s * nrg + rg;
+                if (!page_acquire(pp, page0 + pg, task)) return false;
+                const uint32_t slot = (page0 + pg) % NPAGES;
+                u32x4v a[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) a[j] = *(const u32x4v*)&ring[slot][(4 * j + wave) * 1024 + lane * 16];
+                page_release(page0 + pg, lane);
+                f32x4v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc = mfma_parts(a[j], bo[s & 1][j], acc);
+                flush_rows_b(acc, rg, lane, B);
+            }
+        }
+    } else {
+        constexpr int RPG = 16 / NKB;  // row groups per page
+        constexpr int BPR = 4 / RPG;   // blocks per row group and wave
+        u32x4v bo[BPR][NPART];
+        load_bops_b<BPR>(r, nkb_total, kb_off + wave, lane, bo);
+        for (uint32_t pg = 0; pg < npages; ++pg) {
+            if (!page_acquire(pp, page0 + pg, task)) return false;
+            const uint32_t slot = (page0 + pg) % NPAGES;
+            u32x4v a[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) a[j] = *(const u32x4v*)&ring[slot][(4 * j + wave) * 1024 + lane * 16];
+            page_release(page0 + pg, lane);
+#pragma unroll
+            for (int rr = 0; rr < RPG; ++rr) {
+                f32x4v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int jj = 0; jj < BPR; ++jj) acc = mfma_parts(a[rr * BPR + jj], bo[jj], acc);
+                flush_rows_b(acc, pg * RPG + rr, lane, B);
+            }
+        }
+    }
+    return true;
+}
+
+// Batched GEMV task (QKV, O-proj, gate/up, down, LM head) for B > 1 sequences.
+template <int KT>
+__device__ __noinline__ bool op_gemv_b(const Params* pp, uint32_t slot_, uint32_t page0, uint32_t t_, uint32_t epoch_) {
+    const Task k = fifo_task(slot_);
+    Ctx c = make_ctx(t_, epoch_);
+    CParams& p = P(pp);
+    const int lane = c.lane, tid = c.tid, wave = c.wave;
+    const int B = p.T.B, L = p.T.L, l = k.layer, D = p.T.d;
+    const uint16_t* R;
+    int nkb_total, kb_off = 0, norm_slot = -1;
+    switch (k.op) {
+        case OP_QKV: norm_slot = 2 * l; R = opr_norm(p, norm_slot); nkb_total = p.T.h / 32; break;
+        case OP_GATEUP: norm_slot = 2 * l + 1; R = opr_norm(p, norm_slot); nkb_total = p.T.h / 32; break;
+        case OP_LMHEAD: norm_slot = 2 * L; R = opr_norm(p, norm_slot); nkb_total = p.T.h / 32; break;
+        case OP_OPROJ:
+            R = opr_attn(p, l);
+            nkb_total = p.T.nq * D / 32;
+            kb_off = k.part * p.T.grp * D / 32;
+            break;
+        default:  // OP_DOWN
+            R = opr_m(p, l);
+            nkb_total = p.T.f / 32;
+            kb_off = k.part * p.T.kd / 32;
+            break;
+    }
+    if (!await_inputs(pp, k, c)) return false;
+    zero_rowres(tid);
+    if (!cbarrier(pp, c, k.id)) return false;
+    tmark(c, 0);
+    // residual (rows x sequences) of residual-adding tiles, in flight during the GEMV
+    const bool resid = (k.op == OP_OPROJ || k.op == OP_DOWN) && (k.flags & TF_RESID);
+    float res[MAX_TILE_ROWS / (NCW * 64)];
+#pragma unroll
+    for (int q = 0; q < MAX_TILE_ROWS / (NCW * 64); ++q) {
+        res[q] = 0.f;
+        const int idx = tid + q * NCW * 64;
+        if (resid && idx < (int)k.nrows * B) {
+            const int i = idx / B, b = idx % B, row = (int)k.row0 + i;
+            const int src = k.op == OP_DOWN ? 2 * l : (l == 0 ? -1 : 2 * l - 1);
+            res[q] = src < 0 ? bf16f(gld((const uint16_t*)(p.w + p.lay.embed) + (size_t)S.tok[b] * p.T.h + row))
+                             : ldb_dev(dev_rsrc(acc_buf(p, c.parity, src, b) + row, 4), 0);
+        }
+    }
+    if (!gemv_mfma_b<KT>(pp, wave, lane, page0, k.wbytes, R, nkb_total, kb_off, B, k.id)) return false;
+    if (!cbarrier(pp, c, k.id)) return false;
+    tmark(c, 1);
+    // 1/RMS of each sequence's normalised input (its sum of squares is complete: NORM tasks precede)
+    float rs = 1.0f;
+    if (norm_slot >= 0) rs = 1.0f / sqrtf(ldb_dev(dev_rsrc(ssq_at(p, c.parity, norm_slot), B * 4), (lane % B) * 4) /
+                                          (float)p.T.h + p.eps);
+    // rs of sequence b lives in lanes b, b + B, ...: fetch it for any b through LDS-free shuffles
+    auto rs_of = [&](int b) { return __shfl(rs, b, 64); };
+    if (k.op == OP_QKV) {
+        const uint32_t n = k.nrows, slot = k.part;
+        const int half = D / 2, nq = p.T.nq, nkv = p.T.nkv;
+        const int b = tid / (int)n, i = tid % (int)n;
+        const float rb = rs_of(b < B ? b : 0);
+        if (b < B) {
+            const int32_t Pb = S.pos[b];
+            const int j = (int)k.row0 + i;
+            float lo = S.rowres[i * B + b] * rb, hi = S.rowres[(n + i) * B + b] * rb;
+            if (slot < (uint32_t)(nq + nkv)) {
+                const float2 cs = gld_f2(p.rope + (size_t)Pb * half + j);
+                const float x0 = lo * cs.x - hi * cs.y, x1 = lo * cs.y + hi * cs.x;
+                lo = x0;
+                hi = x1;
+            }
+            if (slot < (uint32_t)nq) {
+                float* q = p.q + (size_t)b * nq * D + (size_t)slot * D;
+                stf_dev(q + j, lo);
+                stf_dev(q + j + half, hi);
+            } else {
+                const bool is_k = slot < (uint32_t)(nq + nkv);
+                const int g = is_k ? (int)slot - nq : (int)slot - nq - nkv;
+                uint16_t* base = (is_k ? S.args.kc : S.args.vc) +
+                                 (((size_t)l * B + b) * nkv + g) * (size_t)p.T.C * D + (size_t)Pb * D;
+                st16_dev(base, (uint32_t)j, f2bf16(lo));
+                st16_dev(base, (uint32_t)(j + half), f2bf16(hi));
+            }
+        }
+    } else if (k.op == OP_GATEUP) {
+        uint16_t* Rm = opr_m(p, l);
+        for (int base = 0; base < (int)k.nrows * B; base += NCW * 64) {  // uniform trip count: rs_of with all lanes
+            const int idx = base + tid;
+            const bool act = idx < (int)k.nrows * B;
+            const int i = act ? idx / B : 0, b = act ? idx % B : 0;
+            const float rb = rs_of(b);
+            if (act) {
+                const float gt = S.rowres[i * B + b] * rb, up = S.rowres[(k.nrows + i) * B + b] * rb;
+                put_op1(Rm, p.T.f / 32, (int)k.row0 + i, b, gt / (1.0f + __expf(-gt)) * up);
+            }
+        }
+    } else if (k.op == OP_LMHEAD) {
+        float* logits = S.args.logits;
+        for (int b = wave; b < B; b += NCW) {
+            const float rb = rs_of(b);
+            float bv = -INFINITY;
+            uint32_t bi = 0xffffffffu;
+            for (uint32_t i = (uint32_t)lane; i < k.nrows; i += 64) {
+                const float val = S.rowres[i * B + b] * rb;
+                if (logits) gst(logits + (size_t)b * p.T.V + k.row0 + i, val);
+                if (val > bv) {
+                    bv = val;
+                    bi = k.row0 + i;
+                }
+            }
+            const uint32_t ub = __float_as_uint(bv);
+            const uint32_t ord = (ub & 0x80000000u) ? ~ub : (ub | 0x80000000u);
+            unsigned long long key = bi == 0xffffffffu ? 0ull : (((unsigned long long)ord << 32) | (0xffffffffu - bi));
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) {
+                const unsigned long long other = __shfl_xor(key, o, 64);
+                key = other > key ? other : key;
+            }
+            if (lane == 0 && key)
+                __hip_atomic_fetch_max((g_u64*)&p.key[c.parity * B + b], key, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+        }
+    } else {  // O-proj / down: residual accumulation
+        const int dst = k.op == OP_DOWN ? 2 * l + 1 : 2 * l;
+#pragma unroll
+        for (int q = 0; q < MAX_TILE_ROWS / (NCW * 64); ++q) {
+            const int idx = tid + q * NCW * 64;
+            if (idx < (int)k.nrows * B) {
+                const int i = idx / B, b = idx % B;
+                addf_dev(acc_buf(p, c.parity, dst, b) + k.row0 + i, S.rowres[i * B + b] + res[q]);
+            }
+        }
+    }
+    return true;
+}
+
 // After the last LM-head tile of the step: publish the argmax and the final residual.
 __device__ __noinline__ void finish_step(const Params* pp, uint32_t epoch, uint32_t parity) {
     CParams& p = P(pp);
@@ -1399,16 +1787,20 @@ __device__ __noinline__ void finish_step(const Params* pp, uint32_t epoch, uint3
     if (lane == 0) old = addu_dev(&p.ticket[0], 1u);
     old = uni(old);
     if (old + 1u != epoch * (uint32_t)p.T.n_lm_tiles) return;
-    const unsigned long long key =
-        __hip_atomic_load((g_u64*)&p.key[parity * p.T.B + 0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (lane == 0) gst(p.next, (int32_t)(0xffffffffu - (uint32_t)(key & 0xffffffffu)));
-    const int h = p.T.h;
-    if (p.T.L == 0) {
-        const uint16_t* e = embed_row(p, 0);
-        for (int i = lane; i < h; i += 64) gst(p.hidden + i, bf16f(gld(e + i)));
-    } else {
-        const float* src = acc_buf(p, parity, 2 * p.T.L - 1, 0);
-        for (int i = lane; i < h; i += 64) gst(p.hidden + i, ldf_dev(src + i));
+    const int B = p.T.B, h = p.T.h;
+    if (lane < B) {
+        const unsigned long long key =
+            __hip_atomic_load((g_u64*)&p.key[parity * B + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        gst(p.next + lane, (int32_t)(0xffffffffu - (uint32_t)(key & 0xffffffffu)));
+    }
+    for (int b = 0; b < B; ++b) {
+        if (p.T.L == 0) {
+            const uint16_t* e = embed_row(p, b);
+            for (int i = lane; i < h; i += 64) gst(p.hidden + (size_t)b * h + i, bf16f(gld(e + i)));
+        } else {
+            const float* src = acc_buf(p, parity, 2 * p.T.L - 1, b);
+            for (int i = lane; i < h; i += 64) gst(p.hidden + (size_t)b * h + i, ldf_dev(src + i));
+        }
     }
 }
 
@@ -1446,7 +1838,19 @@ __device__ __noinline__ void compute(const Params* pp, uint32_t epoch, int wave)
         const uint64_t t_fetch = rtc();
         c.t = t;
         bool ok = true;
-        switch (k.op) {
+        if (p0.T.B > 1) {
+            switch (k.op) {
+                case OP_QKV:
+                case OP_GATEUP:
+                case OP_LMHEAD: ok = MK_KT_DISPATCH_2K(op_gemv_b, h, pp, slot, page0, t, epoch); break;
+                case OP_OPROJ: ok = MK_KT_DISPATCH_2K(op_gemv_b, okt, pp, slot, page0, t, epoch); break;
+                case OP_DOWN: ok = MK_KT_DISPATCH_2K(op_gemv_b, dkt, pp, slot, page0, t, epoch); break;
+                case OP_ATTN: ok = hd == 64 ? op_attn<64>(pp, slot, page0, t, epoch) : op_attn<128>(pp, slot, page0, t, epoch); break;
+                case OP_NORM: ok = op_norm(pp, slot, t, epoch); break;
+                case OP_MERGE: ok = op_merge(pp, slot, t, epoch); break;
+                default: break;
+            }
+        } else switch (k.op) {
             case OP_QKV: ok = MK_KT_DISPATCH(op_qkv, h, pp, slot, page0, t, epoch); break;
             case OP_ATTN: ok = hd == 64 ? op_attn<64>(pp, slot, page0, t, epoch) : op_attn<128>(pp, slot, page0, t, epoch); break;
             case OP_OPROJ: ok = MK_KT_DISPATCH_2K(op_oproj, okt, pp, slot, page0, t, epoch); break;
@@ -1534,6 +1938,10 @@ __global__ void __launch_bounds__(NTHREADS, 1) mk_step_kernel(const Params* pp, 
         for (size_t i = (size_t)blockIdx.x * NTHREADS + threadIdx.x; i < nacc; i += (size_t)gridDim.x * NTHREADS)
             other[i] = 0.f;
         if (blockIdx.x == 0 && (int)threadIdx.x < B) p.key[(parity ^ 1u) * B + threadIdx.x] = 0ull;
+        if (p.ssq && blockIdx.x == gridDim.x - 1) {
+            const int nss = (2 * p.T.L + 1) * B;
+            for (int i = threadIdx.x; i < nss; i += NTHREADS) p.ssq[(size_t)(parity ^ 1u) * nss + i] = 0.f;
+        }
         if (wave >= NCW) loader(pp, epoch, wave - NCW);
         else compute(pp, epoch, wave);
     }
@@ -1573,10 +1981,14 @@ __global__ void __launch_bounds__(256) repack_tiles_kernel(const TileOp* ops, co
     const uint32_t nkb = op.kt / 32;
     for (uint32_t e = threadIdx.x; e < n16; e += 256) {
         uint32_t row, col;
-        if (op.blocked) {
+        if (op.blocked == 1) {  // row-group major: block b = (row group, column block)
             const uint32_t b = e / 64, l = e % 64;
             row = (b / nkb) * 16 + l % 16;
             col = (b % nkb) * 32 + (l / 16) * 8;
+        } else if (op.blocked == 2) {  // k-step major: page = (k-step of 16 column blocks, row group)
+            const uint32_t b = e / 64, l = e % 64, pg = b / 16, nrg = op.rows / 16;
+            row = (pg % nrg) * 16 + l % 16;
+            col = ((pg / nrg) * 16 + b % 16) * 32 + (l / 16) * 8;
         } else {
             row = e / (op.kt / 8);
             col = (e % (op.kt / 8)) * 8;

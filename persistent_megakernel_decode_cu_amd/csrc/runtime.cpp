@@ -25,6 +25,7 @@ struct mk_handle {
     Params* dparams = nullptr;  // device copy read by the kernel
     size_t n_events = 0;
     size_t acc_bytes = 0;
+    size_t ssq_bytes = 0;
     // device allocations owned by the handle
     std::vector<void*> allocs;
 };
@@ -96,7 +97,8 @@ mk_status plan(const mk_model_desc* desc, int32_t batch, int32_t max_ctx, const 
 // Copy the caller's weights into the packed layout: gains and embedding row by
 // row (CopyOp), then every GEMV tile in task order (TileOp): rows of the tile
 // come from a host-built table of row addresses (null = a zero row of padding),
-// and tiles with 128 <= K <= 2048 are stored as 16 x 32 matrix-core blocks.
+// and tiles with 128 <= K <= 2048 are stored as 16 x 32 matrix-core blocks
+// (row-group major, or k-step major for batched tiles with K >= 512).
 mk_status repack(mk_handle* h, const mk_model_desc* d, uint8_t* wd) {
     const Tiling& T = h->g.T;
     const Layout& Ly = h->g.lay;
@@ -167,7 +169,9 @@ mk_status repack(mk_handle* h, const mk_model_desc* d, uint8_t* wd) {
         t.kt = kt;
         t.rows = (uint32_t)(k.wbytes / (kt * 2));
         while (rows.size() < (size_t)t.row_base + t.rows) rows.push_back(nullptr);
-        t.blocked = kt <= 2048 ? 1u : 0u;
+        // matrix-core blocks for 128 <= K <= 2048; with several sequences and K >= 512
+        // the pages go k-step major (the batched GEMV keeps 4 column blocks of operands)
+        t.blocked = kt > 2048 ? 0u : (T.B > 1 && kt >= 512 ? 2u : 1u);
         tiles.push_back(t);
     }
     CopyOp* dops = nullptr;
@@ -198,6 +202,7 @@ mk_status rearm(mk_handle* h) {
     st[ST_EPOCH] = 1;
     HIPCHK(hipMemcpy(p.state, st.data(), ST_WORDS * 4, hipMemcpyHostToDevice));
     HIPCHK(hipMemset(p.acc, 0, h->acc_bytes));
+    if (p.ssq) HIPCHK(hipMemset(p.ssq, 0, h->ssq_bytes));
     HIPCHK(hipMemset(p.key, 0, sizeof(unsigned long long) * 2 * T.B));
     HIPCHK(hipMemset(p.ticket, 0, 4 * T.B));
     HIPCHK(hipDeviceSynchronize());
@@ -271,10 +276,6 @@ mk_status mk_build_graph(const mk_model_desc* desc, int32_t batch, int32_t max_c
         delete h;
         return MK_E_NOT_RESIDENT;
     }
-    if (batch > 1) {  // planned (mk_plan_graph) but not yet run by the interpreter
-        delete h;
-        return MK_E_UNSUPPORTED;
-    }
     mk_status st = plan(desc, batch, max_ctx, &o, h->W, &h->g, &h->tied);
     if (st != MK_OK) {
         delete h;
@@ -328,6 +329,14 @@ mk_status mk_build_graph(const mk_model_desc* desc, int32_t batch, int32_t max_c
     ALLOC(p.m, (size_t)T.B * T.f * 4, true);
     h->acc_bytes = (size_t)2 * (2 * T.L + 1) * T.B * T.h * 4;
     ALLOC(p.acc, h->acc_bytes, true);
+    if (T.B > 1) {
+        // operand columns of absent sequences stay zero for the life of the handle
+        // matrix-core operands of every GEMV input: 2 bf16 parts x 16 sequences per column
+        const size_t xop_elems = ((size_t)(2 * T.L + 1) * T.h + (size_t)T.L * T.nq * T.d + (size_t)T.L * T.f) * 32;
+        ALLOC(p.xop, xop_elems * 2, true);
+        h->ssq_bytes = (size_t)2 * (2 * T.L + 1) * T.B * 4;
+        ALLOC(p.ssq, h->ssq_bytes, true);
+    }
     ALLOC(p.hidden, (size_t)T.B * T.h * 4, true);
     ALLOC(p.key, sizeof(unsigned long long) * 2 * T.B, true);
     ALLOC(p.ticket, 4 * T.B, true);

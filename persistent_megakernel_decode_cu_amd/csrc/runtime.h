@@ -44,6 +44,11 @@ struct Params {
     float* part;              // [B][n_kv][S][grp][d+2]
     float* m;                 // [B][f]
     float* acc;               // [2][2L+1][B][h] residual accumulators (by step parity)
+    // batch > 1: GEMV inputs of all sequences as matrix-core B operands, bf16 parts
+    // hi/mid/lo of 16 x 32 column blocks (lane l: sequence l % 16, columns 8 (l / 16) .. +7)
+    uint16_t* xop;            // [2L+1 normalised inputs][3][h/32][64][8], then [L][3][nq*d/32][64][8]
+                              // (merged attention), then [L][3][f/32][64][8] (SiLU(gate) * up)
+    float* ssq;               // [2][2L+1][B] sums of squares of the normalised inputs (by step parity)
     float* hidden;            // [B][h]
     unsigned long long* key;  // [2][B] packed argmax keys
     uint32_t* ticket;         // [B]
@@ -71,7 +76,9 @@ hipError_t launch_repack(const CopyOp* ops, uint32_t n_ops, uint8_t* dst, hipStr
 // bf16 columns, row r read from rowsrc[row_base + r] (null: zeros), written to
 // dst + dst_off either row by row (blocked = 0) or as 16 x 32 matrix-core blocks
 // (blocked = 1; block b = (row group b / (kt/32), column block b % (kt/32)),
-// lane l of a block holds row 16*rg + l%16, columns 32*kb + 8*(l/16) .. +7).
+// lane l of a block holds row 16*rg + l%16, columns 32*kb + 8*(l/16) .. +7), or
+// k-step major (blocked = 2; page p of 16 blocks = (k-step p / nrg, row group
+// p % nrg) with nrg = rows/16, its block j is column block 16 * k-step + j).
 struct TileOp {
     uint64_t dst_off;
     uint32_t row_base, rows, kt, blocked;

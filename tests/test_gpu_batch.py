@@ -1,0 +1,156 @@
+"""GPU parity of the megakernel with several sequences per step (matrix-core projections,
+NORM and MERGE tasks, split-KV attention per sequence) against the oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import persistent_megakernel_decode_cu_amd as mk
+import synth
+from gpu_util import Runner, compare_step, kv_to_host, TOL_HIDDEN_REL, TOL_LOGIT_ABS
+
+pytestmark = pytest.mark.gpu
+
+TINY = synth.configs.TINY
+LLAMA_1B = synth.configs.LLAMA_1B
+
+
+# The batched projections carry each fp32 input as two bf16 parts (hi + lo within
+# 2^-17 of it), so a projected value is off by up to about 2^-17 * sum_i |w_i x_i|
+# before its bf16 rounding; for these random weights that sum is at most a few tens
+# of times the largest |value| of the head vector.  Allowed: one bf16 ulp of the
+# oracle's value plus 2^-10 of the head vector's largest magnitude.
+KV_HEAD_REL = 2.0 ** -10
+
+
+def _check_kv(orig, ref, gpu, positions):
+    """Every slot except each sequence's own position untouched; that slot within the bound above."""
+    for a_ref, a_gpu, a0 in zip(ref, gpu, orig):
+        for b, P in enumerate(positions):
+            mask = np.ones(a0.shape[3], bool)
+            mask[P] = False
+            np.testing.assert_array_equal(a_gpu[:, b][:, :, mask], a0[:, b][:, :, mask])
+            r = oracle.bf16_to_f64(a_ref[:, b, :, P])
+            g = oracle.bf16_to_f64(a_gpu[:, b, :, P])
+            head_max = np.abs(r).max(axis=2, keepdims=True)
+            bad = np.argwhere(np.abs(g - r) > np.abs(r) * 2.0 ** -7 + KV_HEAD_REL * head_max + 1e-30)
+            for i in bad[:8]:
+                t = tuple(i)
+                print(f"seq {b} pos {P} (layer, group, dim) {t}: oracle {r[t]!r} gpu {g[t]!r} "
+                      f"head max {np.abs(r[t[0], t[1]]).max()!r}")
+            assert len(bad) == 0, (b, len(bad))
+
+
+def _one_step(cfg, B, C, positions, check_kv=True, **opt):
+    w = synth.make_weights(cfg)
+    kc, vc = synth.make_kv(cfg, B, C)
+    tok = synth.make_tokens(cfg, B)
+    pos = np.asarray(positions, np.int32)
+    print(f"case {cfg.name} B={B} C={C} positions={pos.tolist()} opt={opt}", flush=True)
+    run = Runner(cfg, w, B, C, kc, vc, **opt)
+    run.step(tok, pos)
+    run.check()
+    logits = run.logits.cpu().numpy()
+    hidden = run.hidden().cpu().numpy()
+    nxt = run.next_tokens().cpu().numpy()
+    kg, vg = kv_to_host(run.kv, kc.shape) if check_kv else (None, None)
+    run.close()
+    k2, v2 = kc.copy(), vc.copy()
+    ref = oracle.decode_step(cfg, w, tok, pos, k2, v2)
+    res = compare_step(cfg, ref, logits, hidden, nxt)
+    print(res)
+    assert res["hidden_rel"] <= TOL_HIDDEN_REL
+    assert res["max_dlogit"] <= TOL_LOGIT_ABS
+    assert res["argmax_equal"], (nxt, ref["next"])
+    if check_kv:
+        _check_kv((kc, vc), (k2, v2), (kg, vg), pos)
+
+
+@pytest.mark.parametrize("B", [2, 3, 16])
+def test_tiny_batch_one_step(B):
+    # mixed context lengths, including position 0 and the last slot
+    pos = synth.make_positions(B, 0, 511)
+    pos[0] = 0
+    pos[-1] = 511
+    _one_step(TINY, B, 512, pos)
+
+
+@pytest.mark.parametrize("W", [1, 5, 37])
+def test_tiny_batch_few_workgroups(W):
+    _one_step(TINY, 4, 256, [3, 200, 64, 255], n_workgroups=W)
+
+
+def test_tiny_batch_dynamic_queue():
+    _one_step(TINY, 5, 512, synth.make_positions(5, 100, 511), sched=1)
+
+
+def test_tiny_batch_untied_gains():
+    cfg = TINY.with_(tied=False)
+    w = synth.make_weights(cfg, gain_std=0.2)
+    B, C = 3, 256
+    kc, vc = synth.make_kv(cfg, B, C)
+    tok = synth.make_tokens(cfg, B)
+    pos = np.array([10, 128, 250], np.int32)
+    run = Runner(cfg, w, B, C, kc, vc)
+    run.step(tok, pos)
+    run.check()
+    res = compare_step(cfg, oracle.decode_step(cfg, w, tok, pos, kc.copy(), vc.copy()), run.logits.cpu().numpy(),
+                       run.hidden().cpu().numpy(), run.next_tokens().cpu().numpy())
+    run.close()
+    print(res)
+    assert res["hidden_rel"] <= TOL_HIDDEN_REL and res["max_dlogit"] <= TOL_LOGIT_ABS and res["argmax_equal"]
+
+
+def test_tiny_batch_greedy_chain_and_counters():
+    cfg = TINY
+    B, C, steps = 3, 512, 24
+    w = synth.make_weights(cfg)
+    kc, vc = synth.make_kv(cfg, B, C)
+    tok = synth.make_tokens(cfg, B)
+    P0 = np.array([40, 300, 128], np.int32)
+    run = Runner(cfg, w, B, C, kc, vc, trace=1)
+    t0 = torch.tensor(tok, dtype=torch.int32, device="cuda")
+    positions = torch.tensor(np.stack([P0 + s for s in range(steps)]), dtype=torch.int32, device="cuda")
+    nxt = mk.mk_next_tokens(run.h)
+    got = []
+    for s in range(steps):
+        mk.mk_decode_step(run.h, t0.data_ptr() if s == 0 else nxt, positions[s].data_ptr(), run.kv.data_ptr(),
+                          run.logits.data_ptr(), torch.cuda.current_stream().cuda_stream)
+        got.append(run.next_tokens().cpu().numpy().copy())
+    run.check()
+    counts = mk.mk_read_task_counts(run.h, len(run.graph["tasks"]))
+    ctr, epoch = mk.mk_read_counters(run.h, run.graph["header"]["n_events"])
+    assert epoch == steps
+    np.testing.assert_array_equal(counts, np.full(len(counts), steps, np.uint32))
+    np.testing.assert_array_equal(ctr, run.graph["target"] * steps)
+    run.close()
+    ref = oracle.greedy(cfg, w, tok, P0, kc.copy(), vc.copy(), steps)
+    np.testing.assert_array_equal(np.array(got), ref["tokens"])
+
+
+@pytest.fixture(scope="module")
+def llama1b_b16():
+    """Batch 16 at the 1B shape, per-sequence contexts uniform in [256, 4096], room for 4352."""
+    B, C = 16, 4352
+    w = synth.make_weights(LLAMA_1B)
+    kc, vc = synth.make_kv(LLAMA_1B, B, C)
+    tok = synth.make_tokens(LLAMA_1B, B)
+    pos = synth.make_positions(B, 256, 4096)
+    ref = oracle.decode_step(LLAMA_1B, w, tok, pos, kc.copy(), vc.copy())
+    return w, kc, vc, tok, pos, ref
+
+
+@pytest.mark.parametrize("sched", [0, 1])
+def test_llama1b_batch16_first_step(llama1b_b16, sched):
+    w, kc, vc, tok, pos, ref = llama1b_b16
+    print(f"case llama1b B=16 first step sched={sched}", flush=True)
+    run = Runner(LLAMA_1B, w, 16, kc.shape[3], kc, vc, sched=sched)
+    run.step(tok, pos)
+    run.check()
+    res = compare_step(LLAMA_1B, ref, run.logits.cpu().numpy(), run.hidden().cpu().numpy(),
+                       run.next_tokens().cpu().numpy())
+    run.close()
+    print(res)
+    assert res["hidden_rel"] <= TOL_HIDDEN_REL
+    assert res["max_dlogit"] <= TOL_LOGIT_ABS
+    assert res["argmax_equal"]
