@@ -15,6 +15,7 @@ counter profile when it matches the kernel source), the one-kernel-per-op HIP
 baseline on the same inputs, and the oracle's CPU time on a bounded sample.
 
   python bench.py [--gpus 1] [--steps 256] [--warmup 10] [--sched static|dynamic]
+  python bench.py --batch 16    (mixed-context batch workload, tokens/s; not the headline line)
 """
 import argparse
 import json
@@ -121,6 +122,84 @@ def baseline_leg(mk, torch, cfg, model, kc, vc, tok, P0, C, K, W, mk_ms):
             "megakernel_speedup_vs_best": round(best / mk_ms, 3)}
 
 
+def bench_batch(args, torch, synth, mk):
+    """Several sequences per step: Llama-1B shape, per-sequence contexts uniform in [256, 4096] from the
+    token seed, KV cache room for 4352 positions; K greedy steps, every sequence advancing by one."""
+    cfg = synth.configs.LLAMA_1B
+    B, C, K, W = args.batch, 4352, args.steps, args.warmup
+    t_gen = time.perf_counter()
+    w = synth.make_weights(cfg)
+    kc, vc = synth.make_kv(cfg, B, C)
+    tok = synth.make_tokens(cfg, B)
+    P0 = synth.make_positions(B, 256, 4096)
+    t_gen = time.perf_counter() - t_gen
+    if int(P0.max()) + max(K, W) > C:
+        raise SystemExit("steps exceed the KV cache")
+    dev = {k: torch.from_numpy(v.view(np.int16)).cuda() for k, v in w.items()}
+    model = mk.Model(cfg, dev)
+    opt = mk.options(sched=0 if args.sched == "static" else 1, policy=0 if args.policy == "rr" else 1,
+                     attn_splits=args.attn_splits, cooperative=1 if args.cooperative else 0)
+    h = mk.mk_build_graph(model.desc, B, C, opt)
+    del dev, model
+    graph = mk.parse_export(mk.mk_export_graph(h))
+    kv = torch.from_numpy(np.concatenate([kc.reshape(-1), vc.reshape(-1)]).view(np.int16)).cuda()
+    del kc, vc
+    logits = torch.empty(B, cfg.vocab, dtype=torch.float32, device="cuda")
+    n = max(K, W)
+    positions = torch.tensor(np.stack([P0 + s for s in range(n)]), dtype=torch.int32, device="cuda")
+    tok0 = torch.tensor(tok, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    nxt = mk.mk_next_tokens(h)
+
+    def run(n_, first=True):
+        for s in range(n_):
+            tptr = tok0.data_ptr() if (s == 0 and first) else nxt
+            mk.mk_decode_step(h, tptr, positions[s].data_ptr(), kv.data_ptr(), logits.data_ptr(), sp)
+
+    run(W)
+    torch.cuda.synchronize()
+    err = mk.mk_check_device_error(h)
+    if err:
+        raise SystemExit(f"device error: {err}")
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    run(K)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / K
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for s_ in range(K):
+        ev[s_][0].record(stream)
+        mk.mk_decode_step(h, nxt, positions[s_].data_ptr(), kv.data_ptr(), logits.data_ptr(), sp)
+        ev[s_][1].record(stream)
+    torch.cuda.synchronize()
+    ms_launch = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    err = mk.mk_check_device_error(h)
+    if err:
+        raise SystemExit(f"device error: {err}")
+    bytes_mean = np.mean([step_bytes(cfg, P0 + s) for s in range(K)])
+    achieved = bytes_mean / (ms_launch * 1e-3) / 1e9
+    mk.mk_destroy(h)
+    out = {
+        "metric": f"decode tokens/s at batch {B}, Llama-1B shape, mixed contexts",
+        "value": round(B * 1000.0 / ms, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms, 5), "us_per_step": round(ms * 1000.0, 2), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{cfg.name} greedy decode, batch {B}, contexts uniform in [256, 4096], bf16 "
+                               f"weights and KV cache, one kernel launch per step",
+                   "batch": B, "max_ctx": C, "first_positions": P0.tolist(), "sched": args.sched,
+                   "workgroups": int(graph["header"]["W"]), "tasks_per_step": int(graph["header"]["n_tasks"]),
+                   "attn_splits": int(graph["header"]["attn_splits"])},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_step": int(bytes_mean), "kernel_us_per_launch": round(ms_launch * 1000, 2)},
+        "input_generation_s": round(t_gen, 1),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -134,6 +213,9 @@ def main():
     ap.add_argument("--no-baseline", action="store_true", help="skip the one-kernel-per-op baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy three times (reference for the HBM byte counters)")
+    ap.add_argument("--batch", type=int, default=1,
+                    help="sequences per step; above 1: the mixed-context batch workload (contexts uniform in "
+                         "[256, 4096], room for 4352), reported in tokens/s")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -145,6 +227,8 @@ def main():
     import synth
     import persistent_megakernel_decode_cu_amd as mk
 
+    if args.batch > 1:
+        return bench_batch(args, torch, synth, mk)
     cfg = synth.configs.LLAMA_1B
     P0, C, K, W = 1024, 2048, args.steps, args.warmup
     if P0 + max(K, W) > C:

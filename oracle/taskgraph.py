@@ -21,7 +21,11 @@ The tiling rules (written from the design, not from the C++ code):
     halves) of one head; heads ordered by KV group: the group's query heads,
     its key head, its value head; pair blocks in order.
   * attention: attn_splits chunks per (sequence, KV group), default
-    clamp(ceil(max_ctx / 256), 1, 16), at most max_ctx.
+    clamp(ceil(max_ctx / 256), 1, 16) at batch 1 and clamp(ceil(max_ctx / 512),
+    1, 16) for batch > 1, at most max_ctx.  With several sequences the chunks
+    are slots of a fixed length (so a short context leaves some empty) and the
+    last chunk task of a (sequence, KV group) to finish merges the chunks for
+    the O-projection, which therefore waits on the same event as at batch 1.
   * O-proj tiles: (KV group g, row block) over columns g*grp*d .. +grp*d, with
     o_rows = min(h, 1024 // B, max(16, pow2_floor(h * n_kv / W))).
   * down tiles: (K block of kd = min(1024, f) columns, row block of
@@ -46,7 +50,7 @@ import math
 
 import numpy as np
 
-OP_QKV, OP_ATTN, OP_OPROJ, OP_GATEUP, OP_DOWN, OP_LMHEAD, OP_NORM, OP_MERGE = 1, 2, 3, 4, 5, 6, 7, 8
+OP_QKV, OP_ATTN, OP_OPROJ, OP_GATEUP, OP_DOWN, OP_LMHEAD = 1, 2, 3, 4, 5, 6
 NONE = 0xFFFFFFFF
 TF_RESID = 1
 
@@ -86,9 +90,9 @@ def tiling(cfg, B, C, W, attn_splits=0):
     if attn_splits > 0:
         S = attn_splits
     else:
-        S = max(1, min(16, -(-C // 256)))
-        if B > 1:  # about one attention task per workgroup and layer
-            S = max(1, min(S, W // (B * nkv)))
+        # batch 1: 256-position chunks; batch > 1: chunk slots of ceil(C / S) positions
+        # (about 512), so that long and short contexts split into equal-sized work
+        S = max(1, min(16, -(-C // (256 if B == 1 else 512))))
     S = min(S, C)
     kd = min(1024, f)
     max_rows = 1024 // B  # rows x sequences of a tile
@@ -96,8 +100,7 @@ def tiling(cfg, B, C, W, attn_splits=0):
                 o_rows=min(h, max_rows, max(16, _pow2_floor(h * nkv // W))),
                 kd=kd, d_rows=min(h, max_rows, max(16, _pow2_floor(h * (f // kd) // W))),
                 g_rows=min(kd, max_rows // 2, max(8, _pow2_ceil(-(-f // W)))),
-                lm_rows=min(max_rows // 16 * 16, _round16(-(-V // W))),
-                norm_cols=min(h, 256) if B > 1 else 0)
+                lm_rows=min(max_rows // 16 * 16, _round16(-(-V // W))))
 
 
 def layout(cfg, lm_rows, n_lm):
@@ -147,53 +150,36 @@ def build(cfg, B, C, W, policy=0, attn_splits=0):
             target[rec["sig_ev"]] += 1
         tasks.append(rec)
 
-    batched = B > 1
-
-    def norm_tasks(layer, kind, wait, ev):
-        for c0 in range(0, h, t["norm_cols"]):
-            task(op=OP_NORM, layer=layer, part=kind, row0=c0, nrows=t["norm_cols"], wait_ev=wait, sig_ev=ev)
-
     ev_x = NONE
     for l in range(L):
         base = lay["layer0"] + l * lay["layer_bytes"]
-        ev_n1 = event() if batched else NONE
         ev_qkv = [event() for _ in range(nkv)]
         ev_attn = [event() for _ in range(nkv)]
-        ev_mg = [event() for _ in range(nkv)] if batched else ev_attn
         ev_xb = event()
-        ev_n2 = event() if batched else ev_xb
         ev_m = [event() for _ in range(n_kb)]
         ev_next = event()
-        if batched:
-            norm_tasks(l, 0, ev_x, ev_n1)
         tile = 0
         wb = 2 * P * h * 2
         for g in range(nkv):
             heads = [g * grp + s for s in range(grp)] + [nq + g, nq + nkv + g]
             for slot in heads:
                 for pb in range(d // 2 // P):
-                    task(op=OP_QKV, layer=l, part=slot, row0=pb * P, nrows=P, wait_ev=ev_n1 if batched else ev_x,
-                         sig_ev=ev_qkv[g],
+                    task(op=OP_QKV, layer=l, part=slot, row0=pb * P, nrows=P, wait_ev=ev_x, sig_ev=ev_qkv[g],
                          wbytes=wb, wofs=base + lay["qkv"] + tile * wb)
                     tile += 1
         for b in range(B):
             for g in range(nkv):
                 for c in range(S):
                     task(op=OP_ATTN, layer=l, part=g, row0=c, nrows=grp, seq=b, wait_ev=ev_qkv[g], sig_ev=ev_attn[g])
-        if batched:
-            for g in range(nkv):
-                task(op=OP_MERGE, layer=l, part=g, nrows=grp, wait_ev=ev_attn[g], sig_ev=ev_mg[g])
         wb = t["o_rows"] * grp * d * 2
         for g in range(nkv):
             for rb in range(h // t["o_rows"]):
                 task(op=OP_OPROJ, layer=l, part=g, row0=rb * t["o_rows"], nrows=t["o_rows"],
-                     flags=TF_RESID if g == 0 else 0, wait_ev=ev_mg[g], sig_ev=ev_xb, wbytes=wb,
+                     flags=TF_RESID if g == 0 else 0, wait_ev=ev_attn[g], sig_ev=ev_xb, wbytes=wb,
                      wofs=base + lay["o"] + (g * (h // t["o_rows"]) + rb) * wb)
-        if batched:
-            norm_tasks(l, 1, ev_xb, ev_n2)
         wb = 2 * t["g_rows"] * h * 2
         for i in range(f // t["g_rows"]):
-            task(op=OP_GATEUP, layer=l, row0=i * t["g_rows"], nrows=t["g_rows"], wait_ev=ev_n2,
+            task(op=OP_GATEUP, layer=l, row0=i * t["g_rows"], nrows=t["g_rows"], wait_ev=ev_xb,
                  sig_ev=ev_m[i * t["g_rows"] // t["kd"]], wbytes=wb, wofs=base + lay["gu"] + i * wb)
         wb = t["d_rows"] * t["kd"] * 2
         for kb in range(n_kb):
@@ -202,13 +188,9 @@ def build(cfg, B, C, W, policy=0, attn_splits=0):
                      flags=TF_RESID if kb == 0 else 0, wait_ev=ev_m[kb], sig_ev=ev_next, wbytes=wb,
                      wofs=base + lay["down"] + (kb * (h // t["d_rows"]) + rb) * wb)
         ev_x = ev_next
-    ev_nf = ev_x
-    if batched:
-        ev_nf = event()
-        norm_tasks(L, 2, ev_x, ev_nf)
     for i in range(n_lm):
         rows = min(t["lm_rows"], cfg.vocab - i * t["lm_rows"])
-        task(op=OP_LMHEAD, layer=L, row0=i * t["lm_rows"], nrows=rows, wait_ev=ev_nf, wbytes=_round16(rows) * h * 2,
+        task(op=OP_LMHEAD, layer=L, row0=i * t["lm_rows"], nrows=rows, wait_ev=ev_x, wbytes=_round16(rows) * h * 2,
              wofs=lay["lm"] + i * t["lm_rows"] * h * 2)
     nsub = [8 if n > 32 else 1 for n in target]
     for k in tasks:
@@ -292,19 +274,6 @@ def check(g, cfg, B):
         if k["op"] == OP_LMHEAD:
             lm[k["row0"]:k["row0"] + k["nrows"]] += 1
     assert (lm == 1).all(), "LM-head rows not covered exactly once"
-    batched = B > 1
-    # batch > 1: every normalised input (attention and FFN of each layer, final) is
-    # prepared column by column exactly once; one merge per (layer, KV group)
-    for l in range(L + 1):
-        for kind in ((0, 1) if l < L else (2,)):
-            cols = np.zeros(h, int)
-            for k in tasks:
-                if k["op"] == OP_NORM and k["layer"] == l and k["part"] == kind:
-                    cols[k["row0"]:k["row0"] + k["nrows"]] += 1
-            assert (cols == (1 if batched else 0)).all(), "normalised inputs not prepared exactly once"
-        if l < L:
-            mg = sorted(k["part"] for k in tasks if k["op"] == OP_MERGE and k["layer"] == l)
-            assert mg == (list(range(nkv)) if batched else []), "attention merges missing or repeated"
     # G3 soundness: every reader starts after every writer of what it reads, through the event edges
     hb_sets = ancestor_sets(g)
     by = {}
@@ -321,38 +290,33 @@ def check(g, cfg, B):
     checked = set()
     for k in tasks:
         l, op = k["layer"], k["op"]
-        key = (op, l, k["part"] if op in (OP_ATTN, OP_OPROJ, OP_DOWN, OP_NORM, OP_MERGE) else 0, k["wait_ev"])
+        key = (op, l, k["part"] if op in (OP_ATTN, OP_OPROJ, OP_DOWN) else 0, k["wait_ev"])
         if key in checked:
             continue
         checked.add(key)
         need = set()
         prev = ids(OP_DOWN, l - 1) if l > 0 else set()
-        if op == OP_NORM:
-            need = ids(OP_OPROJ, l) if k["part"] == 1 else prev
-        elif op == OP_QKV:
-            need = ids(OP_NORM, l, lambda w: w["part"] == 0) if batched else prev
+        if op == OP_QKV:
+            need = prev
         elif op == OP_ATTN:
             need = ids(OP_QKV, l, lambda w: group_of_slot(w["part"]) == k["part"])
-        elif op == OP_MERGE:
-            need = ids(OP_ATTN, l, lambda w: w["part"] == k["part"])
         elif op == OP_OPROJ:
-            need = ids(OP_MERGE if batched else OP_ATTN, l, lambda w: w["part"] == k["part"]) | prev
+            # batch > 1: the last attention chunk of a (sequence, KV group) merges the
+            # chunks into the O-projection's operands, so all of them precede it
+            need = ids(OP_ATTN, l, lambda w: w["part"] == k["part"]) | prev
         elif op == OP_GATEUP:
-            need = ids(OP_NORM, l, lambda w: w["part"] == 1) if batched else ids(OP_OPROJ, l)
+            need = ids(OP_OPROJ, l)
         elif op == OP_DOWN:
             need = ids(OP_GATEUP, l, lambda w: w["row0"] // kd == k["part"]) | ids(OP_OPROJ, l)
-        elif op == OP_LMHEAD:
-            if batched:
-                need = ids(OP_NORM, L, lambda w: w["part"] == 2)
-            elif L > 0:
-                need = ids(OP_DOWN, L - 1)
+        elif op == OP_LMHEAD and L > 0:
+            need = ids(OP_DOWN, L - 1)
         anc = hb_sets(k["id"])
         missing = need - anc
         assert not missing, f"task {k['id']} may start before its producer(s) {sorted(missing)[:4]}"
     # buffers reused from one layer to the next (q/k/v, attention partials, m): every reader of
     # layer l happens before every writer of layer l+1
     for l in range(L - 1):
-        for rop, wop in ((OP_ATTN, OP_QKV), (OP_MERGE if batched else OP_OPROJ, OP_ATTN), (OP_DOWN, OP_GATEUP)):
+        for rop, wop in ((OP_ATTN, OP_QKV), (OP_ATTN if B > 1 else OP_OPROJ, OP_ATTN), (OP_DOWN, OP_GATEUP)):
             rs = ids(rop, l)
             for w in by.get((wop, l + 1), []):
                 missing = rs - hb_sets(w["id"])

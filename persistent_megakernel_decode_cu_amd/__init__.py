@@ -17,10 +17,9 @@ _lib = None
 MK_OK, MK_E_INVALID, MK_E_UNSUPPORTED, MK_E_NOMEM, MK_E_HIP, MK_E_NOT_RESIDENT, MK_E_DEVICE, MK_E_NO_DEVICE = range(8)
 
 # opcodes of the interpreter (mirrors csrc/mk_internal.h)
-OP_END, OP_QKV, OP_ATTN, OP_OPROJ, OP_GATEUP, OP_DOWN, OP_LMHEAD, OP_NORM, OP_MERGE = range(9)
+OP_END, OP_QKV, OP_ATTN, OP_OPROJ, OP_GATEUP, OP_DOWN, OP_LMHEAD = range(7)
 OP_NAMES = {OP_QKV: "qkv_rope", OP_ATTN: "attention", OP_OPROJ: "oproj_residual", OP_GATEUP: "gateup_silu",
-            OP_DOWN: "down_residual", OP_LMHEAD: "lmhead_argmax", OP_NORM: "norm_operands",
-            OP_MERGE: "attention_merge"}
+            OP_DOWN: "down_residual", OP_LMHEAD: "lmhead_argmax"}
 NONE = 0xFFFFFFFF
 
 _P = ctypes.c_void_p
@@ -64,8 +63,8 @@ assert TASK_DTYPE.itemsize == 48
 
 HEADER_FIELDS = ["magic", "version", "n_tasks", "n_events", "W", "sched", "L", "h", "nq", "nkv", "d", "f", "V", "B",
                  "C", "grp", "qkv_pairs", "attn_splits", "o_rows", "g_rows", "kd", "d_rows", "lm_rows",
-                 "record_bytes", "norm_cols"]
-HEADER_BYTES = 4 * (len(HEADER_FIELDS) + 6)
+                 "record_bytes"]
+HEADER_BYTES = 4 * (len(HEADER_FIELDS) + 7)
 
 
 def load():

@@ -68,9 +68,10 @@ int plan_tiling(const Dims& dm, int B, int C, int W, const PlanOptions& o, Tilin
     T.n_qkv_tiles = (dm.nq + 2 * dm.nkv) * (dm.d / 2) / T.qkv_pairs;
     int S = o.attn_splits;
     if (S <= 0) {
-        S = (int)std::max<int64_t>(1, std::min<int64_t>(16, (C + 255) / 256));
-        // with several sequences, about one attention task per workgroup and layer
-        if (B > 1) S = (int)std::max<int64_t>(1, std::min<int64_t>(S, W / ((int64_t)B * dm.nkv)));
+        // batch 1: 256-position chunks of the one context; batch > 1: slots of
+        // ceil(C / S) positions (about 512), equal work whatever the context mix
+        const int64_t span = B == 1 ? 256 : 512;
+        S = (int)std::max<int64_t>(1, std::min<int64_t>(16, (C + span - 1) / span));
     }
     if (S > C) S = C;
     T.attn_splits = S;
@@ -94,7 +95,6 @@ int plan_tiling(const Dims& dm, int B, int C, int W, const PlanOptions& o, Tilin
     if (T.kd % T.g_rows) return fail("gate/up tile does not divide the down-proj K block");
     T.n_gu_tiles = dm.f / T.g_rows;
     T.lm_rows = (int)std::min<int64_t>(max_rows / 16 * 16, round16((dm.V + W - 1) / W));  // whole 16-row groups
-    T.norm_cols = B > 1 ? (int)std::min<int64_t>(dm.h, 256) : 0;
     T.n_lm_tiles = (dm.V + T.lm_rows - 1) / T.lm_rows;
     return 0;
 }
@@ -165,34 +165,15 @@ int build_graph(const Tiling& T, const Layout& Ly, int sched, int policy, Graph*
         return k;
     };
 
-    const bool batched = T.B > 1;
-    // batch > 1: NORM tasks prepare the normalised input of the next GEMVs for all
-    // sequences (column blocks of norm_cols), signalling `ev`
-    auto add_norm = [&](int layer, int kind, uint32_t wait, uint32_t ev) {
-        for (int c0 = 0; c0 < T.h; c0 += T.norm_cols) {
-            Task k = blank(OP_NORM, layer);
-            k.part = (uint16_t)kind;
-            k.row0 = (uint32_t)c0;
-            k.nrows = (uint32_t)T.norm_cols;
-            k.wait_ev = wait;
-            k.sig_ev = ev;
-            add(k);
-        }
-    };
-
     uint32_t ev_x = NONE;  // residual stream ready for the current layer (NONE for layer 0: embedding)
     for (int l = 0; l < L; ++l) {
         const uint64_t lbase = Ly.layer0 + (uint64_t)l * Ly.layer_bytes;
-        std::vector<uint32_t> ev_qkv(T.nkv), ev_attn(T.nkv), ev_mg(T.nkv), ev_m(n_kb);
-        const uint32_t ev_n1 = batched ? g.new_event() : NONE;
+        std::vector<uint32_t> ev_qkv(T.nkv), ev_attn(T.nkv), ev_m(n_kb);
         for (int gi = 0; gi < T.nkv; ++gi) ev_qkv[gi] = g.new_event();
         for (int gi = 0; gi < T.nkv; ++gi) ev_attn[gi] = g.new_event();
-        for (int gi = 0; gi < T.nkv; ++gi) ev_mg[gi] = batched ? g.new_event() : ev_attn[gi];
         const uint32_t ev_xb = g.new_event();
-        const uint32_t ev_n2 = batched ? g.new_event() : ev_xb;
         for (int kb = 0; kb < n_kb; ++kb) ev_m[kb] = g.new_event();
         const uint32_t ev_next = g.new_event();
-        if (batched) add_norm(l, 0, ev_x, ev_n1);
 
         // fused RMSNorm + QKV + RoPE tiles, grouped by KV head: q heads of the group, then its k and v head
         uint64_t tile = 0;
@@ -204,7 +185,7 @@ int build_graph(const Tiling& T, const Layout& Ly, int sched, int policy, Graph*
                     k.part = (uint16_t)slot;
                     k.row0 = (uint32_t)(pb * T.qkv_pairs);
                     k.nrows = (uint32_t)T.qkv_pairs;
-                    k.wait_ev = batched ? ev_n1 : ev_x;
+                    k.wait_ev = ev_x;
                     k.sig_ev = ev_qkv[gi];
                     k.wbytes = (uint32_t)(2 * T.qkv_pairs * h * 2);
                     k.wofs = lbase + Ly.qkv + tile * k.wbytes;
@@ -212,7 +193,8 @@ int build_graph(const Tiling& T, const Layout& Ly, int sched, int policy, Graph*
                 }
             }
         }
-        // attention chunks per (sequence, KV group, chunk)
+        // attention chunks per (sequence, KV group, chunk); with several sequences the
+        // last chunk of a (sequence, group) to finish also merges the chunks
         for (int b = 0; b < T.B; ++b)
             for (int gi = 0; gi < T.nkv; ++gi)
                 for (int c = 0; c < T.attn_splits; ++c) {
@@ -225,16 +207,6 @@ int build_graph(const Tiling& T, const Layout& Ly, int sched, int policy, Graph*
                     k.sig_ev = ev_attn[gi];
                     add(k);
                 }
-        // batch > 1: merge of each KV group's partials for all sequences
-        if (batched)
-            for (int gi = 0; gi < T.nkv; ++gi) {
-                Task k = blank(OP_MERGE, l);
-                k.part = (uint16_t)gi;
-                k.nrows = (uint32_t)grp;
-                k.wait_ev = ev_attn[gi];
-                k.sig_ev = ev_mg[gi];
-                add(k);
-            }
         // O-proj K slices: tile (group, row block)
         const int o_kt = grp * T.d;
         for (int gi = 0; gi < T.nkv; ++gi)
@@ -244,19 +216,18 @@ int build_graph(const Tiling& T, const Layout& Ly, int sched, int policy, Graph*
                 k.row0 = (uint32_t)(rb * T.o_rows);
                 k.nrows = (uint32_t)T.o_rows;
                 k.flags = gi == 0 ? TF_RESID : 0;
-                k.wait_ev = ev_mg[gi];
+                k.wait_ev = ev_attn[gi];
                 k.sig_ev = ev_xb;
                 k.wbytes = (uint32_t)((uint64_t)T.o_rows * o_kt * 2);
                 k.wofs = lbase + Ly.o + ((uint64_t)gi * (T.h / T.o_rows) + rb) * k.wbytes;
                 add(k);
             }
         // RMSNorm + gate/up + SiLU tiles
-        if (batched) add_norm(l, 1, ev_xb, ev_n2);
         for (int t = 0; t < T.n_gu_tiles; ++t) {
             Task k = blank(OP_GATEUP, l);
             k.row0 = (uint32_t)(t * T.g_rows);
             k.nrows = (uint32_t)T.g_rows;
-            k.wait_ev = ev_n2;
+            k.wait_ev = ev_xb;
             k.sig_ev = ev_m[(t * T.g_rows) / T.kd];
             k.wbytes = (uint32_t)(2ull * T.g_rows * h * 2);
             k.wofs = lbase + Ly.gu + (uint64_t)t * k.wbytes;
@@ -279,16 +250,11 @@ int build_graph(const Tiling& T, const Layout& Ly, int sched, int policy, Graph*
         ev_x = ev_next;
     }
     // final RMSNorm + LM head + argmax
-    uint32_t ev_nf = ev_x;
-    if (batched) {
-        ev_nf = g.new_event();
-        add_norm(L, 2, ev_x, ev_nf);
-    }
     for (int t = 0; t < T.n_lm_tiles; ++t) {
         Task k = blank(OP_LMHEAD, L);
         k.row0 = (uint32_t)(t * T.lm_rows);
         k.nrows = (uint32_t)std::min<int64_t>(T.lm_rows, (int64_t)T.V - (int64_t)t * T.lm_rows);
-        k.wait_ev = ev_nf;
+        k.wait_ev = ev_x;
         k.wbytes = (uint32_t)((uint64_t)round16(k.nrows) * h * 2);
         k.wofs = Ly.lm + (uint64_t)k.row0 * h * 2;
         add(k);
@@ -351,7 +317,6 @@ size_t export_graph(const Graph& g, void* buf, size_t cap) {
     hd.grp = T.grp; hd.qkv_pairs = T.qkv_pairs; hd.attn_splits = T.attn_splits; hd.o_rows = T.o_rows;
     hd.g_rows = T.g_rows; hd.kd = T.kd; hd.d_rows = T.d_rows; hd.lm_rows = T.lm_rows;
     hd.record_bytes = sizeof(Task);
-    hd.norm_cols = T.norm_cols;
     uint8_t* p = (uint8_t*)buf;
     memcpy(p, &hd, sizeof(hd));
     p += sizeof(hd);

@@ -69,6 +69,7 @@ struct __attribute__((aligned(16))) Smem {
     uint32_t go, cbar, done, abort;
     uint32_t cgen[NCW];  // compute-wave barrier generation (per wave)
     float ssq[NCW];      // per-wave partial sums of squares of the staged activation
+    float ssqb[NCW][MAX_BATCH];  // batch > 1: per-wave, per-sequence partial sums of squares
     uint32_t t_ready_lo, t_ready_hi;
     uint32_t tm[4];  // trace: low 32 bits of the clock after staging / after the GEMV
 };
@@ -298,9 +299,15 @@ __device__ __noinline__ bool wait_event(const Params* pp, uint32_t ev, uint32_t 
 struct Chunk {
     int32_t c0, c1, P;  // chunk positions [c0, c1) of 0..P; prefix rows in LDS are [c0, min(c1, P))
 };
-__device__ __forceinline__ Chunk attn_chunk(int32_t splits, int32_t P, uint32_t c) {
+// Chunk c of the context 0..P: one of `splits` equal parts of it (fixed_len = 0), or
+// the slot [c * fixed_len, (c + 1) * fixed_len) clipped to it (several sequences:
+// every non-empty chunk is about the same work whatever the mix of contexts).
+__device__ __forceinline__ int32_t attn_fixed_len(int32_t B, int32_t C, int32_t splits) {
+    return B > 1 ? (C + splits - 1) / splits : 0;
+}
+__device__ __forceinline__ Chunk attn_chunk(int32_t splits, int32_t fixed_len, int32_t P, uint32_t c) {
     const int32_t n = P + 1;
-    const int32_t lc = (n + splits - 1) / splits;
+    const int32_t lc = fixed_len > 0 ? fixed_len : (n + splits - 1) / splits;
     Chunk ch;
     ch.P = P;
     ch.c0 = min(n, (int32_t)c * lc);
@@ -312,9 +319,9 @@ __device__ __forceinline__ int32_t attn_block_rows(int32_t d) { return 4096 / d;
 
 __device__ __forceinline__ int32_t seq_pos(uint32_t b) { return (int32_t)lds_ld(*(const uint32_t*)&S.pos[b]); }
 
-__device__ __forceinline__ uint32_t task_pages(const Task& k, int32_t splits, int32_t d) {
+__device__ __forceinline__ uint32_t task_pages(const Task& k, int32_t splits, int32_t fixed_len, int32_t d) {
     if (k.op == OP_ATTN) {
-        const Chunk ch = attn_chunk(splits, seq_pos(k.seq), k.row0);
+        const Chunk ch = attn_chunk(splits, fixed_len, seq_pos(k.seq), k.row0);
         const int32_t npre = max(0, min(ch.c1, ch.P) - ch.c0);
         const int32_t pb = attn_block_rows(d);
         return (uint32_t)((npre + pb - 1) / pb);
@@ -337,7 +344,7 @@ __device__ __forceinline__ void issue_page(CParams& p, const Task& k, uint32_t k
     uint8_t* const dst = &ring[slot][0];
     if (k.op == OP_ATTN) {
         const int32_t d = p.T.d;
-        const Chunk ch = attn_chunk(p.T.attn_splits, seq_pos(k.seq), k.row0);
+        const Chunk ch = attn_chunk(p.T.attn_splits, attn_fixed_len(p.T.B, p.T.C, p.T.attn_splits), seq_pos(k.seq), k.row0);
         const int32_t pb = attn_block_rows(d);
         const int32_t p0 = ch.c0 + (int32_t)kp * pb;
         const int32_t rows = min(pb, min(ch.c1, ch.P) - p0);
@@ -392,7 +399,7 @@ __device__ __noinline__ void loader(const Params* pp, uint32_t epoch, int lw) {
     c_task* tasks = (c_task*)p.tasks;
     const uint32_t sched = p.sched;
     const uint32_t n_tasks = p.n_tasks;
-    const int32_t splits = p.T.attn_splits, hd = p.T.d;
+    const int32_t splits = p.T.attn_splits, hd = p.T.d, fixed_len = attn_fixed_len(p.T.B, p.T.C, p.T.attn_splits);
     uint32_t qbeg = 0, qend = 0;
     if (sched == 0) {
         qbeg = qoff[blockIdx.x];
@@ -466,7 +473,7 @@ __device__ __noinline__ void loader(const Params* pp, uint32_t epoch, int lw) {
             if (lane == 0) lds_st(S.fifo_ready[slot], t + 1);
         }
         if (end) break;
-        const uint32_t np = task_pages(k, splits, hd);
+        const uint32_t np = task_pages(k, splits, fixed_len, hd);
         for (uint32_t kp = 0; kp < np; ++kp) {
             const uint32_t ps = pseq % NPAGES;
             const uint32_t need = NCW * (pseq / NPAGES);
@@ -525,8 +532,15 @@ __device__ __forceinline__ bool cbarrier(const Params* pp, Ctx& c, uint32_t task
 
 __device__ __forceinline__ bool page_acquire(const Params* pp, uint32_t seq, uint32_t task) {
 #pragma unroll
-    for (int lw = 0; lw < NLW; ++lw)
-        if (!lds_wait_ge(S.page_ready[lw][seq % NPAGES], seq / NPAGES + 1, pp, task)) return false;
+    for (int lw = 0; lw < NLW; ++lw) {
+        const uint32_t& w = S.page_ready[lw][seq % NPAGES];
+        const uint32_t want = seq / NPAGES + 1;
+        // short waits spin here: the out-of-line wait (timeouts, abort) is a call, around
+        // which a GEMV holding many operand registers would save and restore them
+        uint32_t it = 0;
+        while (lds_ld(w) < want && ++it < 512u) __builtin_amdgcn_s_sleep(1);
+        if (it == 512u && !lds_wait_ge(w, want, pp, task)) return false;
+    }
     return true;
 }
 __device__ __forceinline__ void page_release(uint32_t seq, int lane) {
@@ -927,6 +941,126 @@ __device__ __forceinline__ void load_residual(CParams& p, const Task& k, int idx
     }
 }
 
+// ---- several sequences: matrix-core operands in global memory -------------------------
+//
+// With B > 1 sequences, the inputs of the O-projection (merged attention) and of the
+// down-projection (SiLU(gate) * up) are written once per step as matrix-core B operands
+// (columns = sequences) by their producers, with device-scope stores, and read with
+// device-scope loads by every tile that consumes them.  Each fp32 input is carried as
+// two bf16 parts, hi = its truncation to bf16 and lo = the remainder rounded to bf16,
+// so hi + lo is within 2^-17 of it (relative); both parts go through the same weights.
+
+constexpr int NPART = 2;
+constexpr int OPS_PER_COL = NPART * MAX_BATCH;  // bf16 elements per column of an operand region
+
+__device__ __forceinline__ uint16_t* opr_attn(CParams& p, int l) {
+    return p.xop + (size_t)l * p.T.nq * p.T.d * OPS_PER_COL;
+}
+__device__ __forceinline__ uint16_t* opr_m(CParams& p, int l) {
+    return p.xop + ((size_t)p.T.L * p.T.nq * p.T.d + (size_t)l * p.T.f) * OPS_PER_COL;
+}
+// element of (part, column c, sequence b) in a region of nkb 32-column blocks: block
+// (part, c / 32) holds 64 lanes x 8 elements, lane = 16 ((c % 32) / 8) + b
+__device__ __forceinline__ uint32_t opr_index(int nkb, int part, int c, int b) {
+    return ((uint32_t)(part * nkb + (c >> 5)) * 64u + (uint32_t)(((c & 31) >> 3) * 16 + b)) * 8u + (uint32_t)(c & 7);
+}
+__device__ __forceinline__ void split2(float v, uint32_t& hi, uint32_t& lo) {
+    const uint32_t uh = __float_as_uint(v) & 0xffff0000u;
+    hi = uh >> 16;
+    lo = f2bf16(v - __uint_as_float(uh));
+}
+// the parts of 8 consecutive inputs as two B-operand registers (hi, lo)
+__device__ __forceinline__ void split8(const float* v, u32x4v& hi, u32x4v& lo) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint32_t h0, l0, h1, l1;
+        split2(v[2 * i], h0, l0);
+        split2(v[2 * i + 1], h1, l1);
+        hi[i] = h0 | (h1 << 16);
+        lo[i] = l0 | (l1 << 16);
+    }
+}
+// x[c .. c+7] of sequence b (c a multiple of 8) into region R
+__device__ __forceinline__ void put_op8(uint16_t* R, int nkb, int c, int b, const float* v) {
+    u32x4v hh, ll;
+    split8(v, hh, ll);
+    const __amdgpu_buffer_rsrc_t r = dev_rsrc(R, (uint32_t)nkb * NPART * 1024u);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, hh), r, opr_index(nkb, 0, c, b) * 2, 0, 16);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ll), r, opr_index(nkb, 1, c, b) * 2, 0, 16);
+}
+__device__ __forceinline__ void put_op1(uint16_t* R, int nkb, int c, int b, float v) {
+    uint32_t h0, l0;
+    split2(v, h0, l0);
+    const __amdgpu_buffer_rsrc_t r = dev_rsrc(R, (uint32_t)nkb * NPART * 1024u);
+    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)h0, r, opr_index(nkb, 0, c, b) * 2, 0, 16);
+    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)l0, r, opr_index(nkb, 1, c, b) * 2, 0, 16);
+}
+
+// One wave merges the attention chunks of (layer, sequence b, KV group g) into the
+// O-projection's operands: a = sum_c e^(m_c - M) o_c / sum_c e^(m_c - M) l_c over the
+// non-empty chunks.  Lane = (query head, 8-dimension chunk).
+__device__ __noinline__ void merge_chunks(const Params* pp, int layer, int b, int g, int32_t pos, int lane) {
+    CParams& p = P(pp);
+    const int D = p.T.d, G = p.T.grp, Sp = p.T.attn_splits;
+    const int32_t fl = attn_fixed_len(p.T.B, p.T.C, Sp);
+    const int nch = min(Sp, (pos + fl) / fl);  // chunks holding at least one of the pos + 1 positions
+    const uint32_t cs = (uint32_t)G * (D + 2);  // floats per chunk
+    uint16_t* R = opr_attn(p, layer);
+    const int nkb = p.T.nq * D / 32;
+    for (int idx = lane; idx < G * (D / 8); idx += 64) {
+        const int head = idx / (D / 8), c8 = idx % (D / 8);
+        const float* src = p.part + ((((size_t)b * p.T.nkv + g) * Sp) * G + head) * (D + 2);
+        const __amdgpu_buffer_rsrc_t r = dev_rsrc(src, (uint32_t)((Sp - 1) * cs + D + 2) * 4);
+        float mc[16], lc[16];
+#pragma unroll
+        for (int cc = 0; cc < 16; ++cc) {
+            mc[cc] = cc < nch ? ldb_dev(r, (uint32_t)(cc * cs) * 4) : -INFINITY;
+            lc[cc] = cc < nch ? ldb_dev(r, (uint32_t)(cc * cs + 1) * 4) : 0.f;
+        }
+        float Mx = -INFINITY;
+#pragma unroll
+        for (int cc = 0; cc < 16; ++cc) Mx = fmaxf(Mx, mc[cc]);
+        float den = 0.f, num[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) num[e] = 0.f;
+#pragma unroll
+        for (int c4 = 0; c4 < 16; c4 += 4) {
+            if (c4 >= nch) break;
+            float oc[4][8];
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    oc[cc][e] = c4 + cc < nch ? ldb_dev(r, (uint32_t)((c4 + cc) * cs + 2 + c8 * 8 + e) * 4) : 0.f;
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) {
+                const float m = mc[c4 + cc];
+                const float sc = m == -INFINITY ? 0.f : __expf(m - Mx);
+                den = fmaf(sc, lc[c4 + cc], den);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) num[e] = fmaf(sc, oc[cc][e], num[e]);
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) num[e] /= den;
+        put_op8(R, nkb, (g * G + head) * D + c8 * 8, b, num);
+    }
+}
+
+// The LM-head tiles also publish the final residual (hidden output): tile i copies
+// its share [i * per, (i + 1) * per) of the B x h values, per = ceil(B h / tiles).
+__device__ __forceinline__ void copy_hidden_share(CParams& p, const Task& k, uint32_t parity, int tid) {
+    const int h = p.T.h, total = p.T.B * h, nt = p.T.n_lm_tiles;
+    const int per = (total + nt - 1) / nt, ti = (int)(k.row0 / (uint32_t)p.T.lm_rows);
+    const int e0 = ti * per, e1 = min(total, e0 + per);
+    for (int e = e0 + tid; e < e1; e += NCW * 64) {
+        float v;
+        if (p.T.L == 0) v = bf16f(gld((const uint16_t*)(p.w + p.lay.embed) + (size_t)S.tok[e / h] * h + e % h));
+        else v = ldf_dev(acc_buf(p, parity, 2 * p.T.L - 1, 0) + e);
+        gst(p.hidden + e, v);
+    }
+}
+
 // ---- ops ---------------------------------------------------------------------------------
 
 // RMSNorm + QKV tile + RoPE + K/V append.  Tile rows [0, n) are the first halves
@@ -1007,7 +1141,7 @@ __device__ __noinline__ bool op_attn(const Params* pp, uint32_t slot_, uint32_t 
     CParams& p = P(pp);
     const int lane = c.lane, wave = c.wave;
     const int b = (int)k.seq, g = k.part;
-    const Chunk ch = attn_chunk(p.T.attn_splits, S.pos[b], k.row0);
+    const Chunk ch = attn_chunk(p.T.attn_splits, attn_fixed_len(p.T.B, p.T.C, p.T.attn_splits), S.pos[b], k.row0);
     constexpr int PB = 4096 / D;      // positions per page (64 or 32)
     constexpr int NC = D / 8;         // 16-byte chunks per row (8 or 16)
     constexpr int NPG = 64 / NC;      // position groups in P.V (8 or 4)
@@ -1194,6 +1328,17 @@ __device__ __noinline__ bool op_attn(const Params* pp, uint32_t slot_, uint32_t 
         if (pgl == 0) {
 #pragma unroll
             for (int ee = 0; ee < 8; ++ee) stf_dev(dst + 2 + cl * 8 + ee, o[hh][ee]);
+        }
+    }
+    if (p.T.B > 1) {
+        // several sequences: the last chunk of (sequence, group) to finish merges them all
+        vm_wait_all();  // this wave's partials are stored
+        if (!cbarrier(pp, c, k.id)) return false;
+        if (wave == 0) {
+            uint32_t old = 0;
+            if (lane == 0) old = addu_dev(&p.aticket[((size_t)k.layer * p.T.B + b) * p.T.nkv + g], 1u);
+            old = uni(old);
+            if (old + 1u == c.epoch * (uint32_t)p.T.attn_splits) merge_chunks(pp, k.layer, b, g, ch.P, lane);
         }
     }
     return true;
@@ -1388,199 +1533,76 @@ __device__ __noinline__ bool op_lmhead(const Params* pp, uint32_t slot_, uint32_
     }
     if (lane == 0 && key)
         __hip_atomic_fetch_max((g_u64*)&p.key[c.parity * p.T.B + 0], key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    copy_hidden_share(p, k, c.parity, tid);
     return true;
 }
 
-// ---- batch > 1 -------------------------------------------------------------------------
+// ---- batched GEMV tiles (B > 1) ------------------------------------------------------
 //
-// The GEMV inputs of all B sequences live in global memory as matrix-core B
-// operands (columns = sequences), written with device-scope stores by the NORM /
-// MERGE / gate-up tasks and read with device-scope loads, so that one pass over a
-// weight tile serves every sequence.  Each fp32 input is carried as two bf16 parts,
-// hi = its truncation to bf16 and lo = the remainder rounded to bf16, so hi + lo
-// is within 2^-17 of it (relative); both parts go through the same weights.
+// One pass over a weight tile serves all sequences: the tile's 16 x 32 blocks are the
+// A operands, the inputs of the 16 sequences the B operands (two bf16 parts, one MFMA
+// each).  Each compute wave owns the column blocks kb = 4 i + wave and keeps the B
+// operands of all of them in registers for the whole task.  Its products go to a
+// wave-private slice of S.xs (row-major rows x B); the epilogue adds the 4 slices.
 
-constexpr int NPART = 2;
-constexpr int OPS_PER_COL = NPART * MAX_BATCH;  // bf16 elements per column of an operand region
-
-__device__ __forceinline__ uint16_t* opr_norm(CParams& p, int slot) { return p.xop + (size_t)slot * OPS_PER_COL * p.T.h; }
-__device__ __forceinline__ uint16_t* opr_attn(CParams& p, int l) {
-    return p.xop + ((size_t)(2 * p.T.L + 1) * p.T.h + (size_t)l * p.T.nq * p.T.d) * OPS_PER_COL;
-}
-__device__ __forceinline__ uint16_t* opr_m(CParams& p, int l) {
-    return p.xop + ((size_t)(2 * p.T.L + 1) * p.T.h + (size_t)p.T.L * p.T.nq * p.T.d + (size_t)l * p.T.f) * OPS_PER_COL;
-}
-// element of (part, column c, sequence b) in a region of nkb 32-column blocks: block
-// (part, c / 32) holds 64 lanes x 8 elements, lane = 16 ((c % 32) / 8) + b
-__device__ __forceinline__ uint32_t opr_index(int nkb, int part, int c, int b) {
-    return ((uint32_t)(part * nkb + (c >> 5)) * 64u + (uint32_t)(((c & 31) >> 3) * 16 + b)) * 8u + (uint32_t)(c & 7);
-}
-__device__ __forceinline__ float* ssq_at(CParams& p, uint32_t parity, int slot) {
-    return p.ssq + ((size_t)parity * (2 * p.T.L + 1) + slot) * p.T.B;
-}
-__device__ __forceinline__ void split2(float v, uint32_t& hi, uint32_t& lo) {
-    const uint32_t uh = __float_as_uint(v) & 0xffff0000u;
-    hi = uh >> 16;
-    lo = f2bf16(v - __uint_as_float(uh));
-}
-// the split of x[c .. c+7] of sequence b (c a multiple of 8) into region R
-__device__ __forceinline__ void put_op8(uint16_t* R, int nkb, int c, int b, const float* v) {
-    uint32_t hh[4], ll[4];
+// Inputs of the normalised GEMVs: the fp32 residual rows of the sequences (or their
+// bf16 embedding rows) for this wave's column blocks 4 i + wave, lane (kq = lane / 16,
+// sequence n = lane % 16) holding columns 8 kq .. 8 kq + 7 of each block; rows past
+// the batch read zeros (offsets outside the buffer range).
+template <int NBW>
+__device__ __forceinline__ void load_rows(float (*v)[8], __amdgpu_buffer_rsrc_t r, bool emb, uint32_t row_ofs,
+                                          int wave, int lane) {
+    const int kq = lane / 16;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        uint32_t h0, l0, h1, l1;
-        split2(v[2 * i], h0, l0);
-        split2(v[2 * i + 1], h1, l1);
-        hh[i] = h0 | (h1 << 16);
-        ll[i] = l0 | (l1 << 16);
-    }
-    const __amdgpu_buffer_rsrc_t r = dev_rsrc(R, (uint32_t)nkb * NPART * 1024u);
-    __builtin_amdgcn_raw_buffer_store_b128(u32x4{hh[0], hh[1], hh[2], hh[3]}, r, opr_index(nkb, 0, c, b) * 2, 0, 16);
-    __builtin_amdgcn_raw_buffer_store_b128(u32x4{ll[0], ll[1], ll[2], ll[3]}, r, opr_index(nkb, 1, c, b) * 2, 0, 16);
-}
-__device__ __forceinline__ void put_op1(uint16_t* R, int nkb, int c, int b, float v) {
-    uint32_t h0, l0;
-    split2(v, h0, l0);
-    const __amdgpu_buffer_rsrc_t r = dev_rsrc(R, (uint32_t)nkb * NPART * 1024u);
-    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)h0, r, opr_index(nkb, 0, c, b) * 2, 0, 16);
-    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)l0, r, opr_index(nkb, 1, c, b) * 2, 0, 16);
-}
-
-// NORM (layer l, kind 0 attention / 1 FFN / 2 final, columns [c0, c0 + nc)): for
-// every sequence, the partial sum of squares of x (added into ssq) and the operand
-// split of x * gains.  1/RMS is applied by the GEMV epilogues.
-__device__ __noinline__ bool op_norm(const Params* pp, uint32_t slot_, uint32_t t_, uint32_t epoch_) {
-    const Task k = fifo_task(slot_);
-    Ctx c = make_ctx(t_, epoch_);
-    CParams& p = P(pp);
-    const int tid = c.tid, B = p.T.B, h = p.T.h, L = p.T.L;
-    const int l = k.layer, kind = k.part;
-    const int slot = kind == 2 ? 2 * L : 2 * l + kind;
-    // the residual stream entering this norm: accumulator index, or -1 for the embedding
-    const int src = kind == 1 ? 2 * l : (l == 0 ? -1 : 2 * l - 1);
-    const int CH = (int)k.nrows / 8;  // 8-column chunks per sequence (16 or 32)
-    if (!await_inputs(pp, k, c)) return false;
-    uint16_t* R = opr_norm(p, slot);
-    float* ss_out = ssq_at(p, c.parity, slot);
-    const uint16_t* g = gains(p, slot);
-    for (int base = 0; base < B * CH; base += NCW * 64) {
-        const int idx = base + tid;
-        const bool act = idx < B * CH;
-        const int b = act ? idx / CH : 0, col = (int)k.row0 + (idx % CH) * 8;
-        float v[8];
+    for (int i = 0; i < NBW; ++i) {
+        const uint32_t col = (uint32_t)(32 * (4 * i + wave) + 8 * kq);
+        if (emb) {
+            const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(r, (row_ofs + col) * 2, 0, 0);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = 0.f;
-        if (act) {
-            if (src < 0) {
-                const uint4 w = gld_u4((const uint16_t*)(p.w + p.lay.embed) + (size_t)S.tok[b] * h + col);
-                v[0] = bf16lo(w.x); v[1] = bf16hi(w.x); v[2] = bf16lo(w.y); v[3] = bf16hi(w.y);
-                v[4] = bf16lo(w.z); v[5] = bf16hi(w.z); v[6] = bf16lo(w.w); v[7] = bf16hi(w.w);
-            } else {
-                const __amdgpu_buffer_rsrc_t r = dev_rsrc(acc_buf(p, c.parity, src, b) + col, 32);
-                const u32x4 a0 = __builtin_amdgcn_raw_buffer_load_b128(r, 0, 0, 16);
-                const u32x4 a1 = __builtin_amdgcn_raw_buffer_load_b128(r, 16, 0, 16);
+            for (int e = 0; e < 4; ++e) {
+                v[i][2 * e] = bf16lo(w[e]);
+                v[i][2 * e + 1] = bf16hi(w[e]);
+            }
+        } else {
+            const u32x4 a0 = __builtin_amdgcn_raw_buffer_load_b128(r, (row_ofs + col) * 4, 0, 16);
+            const u32x4 a1 = __builtin_amdgcn_raw_buffer_load_b128(r, (row_ofs + col) * 4 + 16, 0, 16);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    v[i] = __uint_as_float(a0[i]);
-                    v[4 + i] = __uint_as_float(a1[i]);
-                }
+            for (int e = 0; e < 4; ++e) {
+                v[i][e] = __uint_as_float(a0[e]);
+                v[i][4 + e] = __uint_as_float(a1[e]);
             }
         }
-        float ss = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) ss = fmaf(v[i], v[i], ss);
-        ss = CH == 32 ? seg_sum<32>(ss) : seg_sum<16>(ss);
-        if (act && idx % CH == 0)
-            __hip_atomic_fetch_add((g_f32*)&ss_out[b], ss, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (act) {
-            const uint4 gw = gld_u4(g + col);
-            v[0] *= bf16lo(gw.x); v[1] *= bf16hi(gw.x); v[2] *= bf16lo(gw.y); v[3] *= bf16hi(gw.y);
-            v[4] *= bf16lo(gw.z); v[5] *= bf16hi(gw.z); v[6] *= bf16lo(gw.w); v[7] *= bf16hi(gw.w);
-            put_op8(R, h / 32, col, b, v);
-        }
-    }
-    return true;
-}
-
-// MERGE (layer l, KV group g): the attention output of every sequence from its
-// chunks' partials, as operands for the O-projection.  Lane = (sequence, head,
-// 8-dimension chunk); the chunks' maxima and sums are read first, the partial
-// outputs in groups of four chunks.
-__device__ __noinline__ bool op_merge(const Params* pp, uint32_t slot_, uint32_t t_, uint32_t epoch_) {
-    const Task k = fifo_task(slot_);
-    Ctx c = make_ctx(t_, epoch_);
-    CParams& p = P(pp);
-    const int tid = c.tid, B = p.T.B, D = p.T.d, G = p.T.grp, Sp = p.T.attn_splits, g = k.part;
-    if (!await_inputs(pp, k, c)) return false;
-    uint16_t* R = opr_attn(p, k.layer);
-    const int nkb = p.T.nq * D / 32, per_b = G * D / 8;
-    const uint32_t cs = (uint32_t)G * (D + 2);  // floats per chunk
-    for (int idx = tid; idx < B * per_b; idx += NCW * 64) {
-        const int b = idx / per_b, head = (idx % per_b) / (D / 8), ch = idx % (D / 8);
-        const float* src = p.part + ((((size_t)b * p.T.nkv + g) * Sp) * G + head) * (D + 2);
-        const __amdgpu_buffer_rsrc_t r = dev_rsrc(src, (uint32_t)((Sp - 1) * cs + D + 2) * 4);
-        float mc[16], lc[16];
-#pragma unroll
-        for (int cc = 0; cc < 16; ++cc) {
-            mc[cc] = cc < Sp ? ldb_dev(r, (uint32_t)(cc * cs) * 4) : -INFINITY;
-            lc[cc] = cc < Sp ? ldb_dev(r, (uint32_t)(cc * cs + 1) * 4) : 0.f;
-        }
-        float Mx = -INFINITY;
-#pragma unroll
-        for (int cc = 0; cc < 16; ++cc) Mx = fmaxf(Mx, mc[cc]);
-        float den = 0.f, num[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) num[e] = 0.f;
-#pragma unroll
-        for (int c4 = 0; c4 < 16; c4 += 4) {
-            if (c4 >= Sp) break;
-            float oc[4][8];
-#pragma unroll
-            for (int cc = 0; cc < 4; ++cc)
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    oc[cc][e] = c4 + cc < Sp ? ldb_dev(r, (uint32_t)((c4 + cc) * cs + 2 + ch * 8 + e) * 4) : 0.f;
-#pragma unroll
-            for (int cc = 0; cc < 4; ++cc) {
-                const float m = mc[c4 + cc];
-                const float sc = m == -INFINITY ? 0.f : __expf(m - Mx);
-                den = fmaf(sc, lc[c4 + cc], den);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) num[e] = fmaf(sc, oc[cc][e], num[e]);
-            }
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) num[e] /= den;
-        put_op8(R, nkb, (g * G + head) * D + ch * 8, b, num);
-    }
-    return true;
-}
-
-// Batched matrix-core GEMV: as gemv_mfma, with the B operands (16 sequences, one
-// MFMA per bf16 part) of this wave's column blocks kb = 4 i + wave loaded from the
-// operand region R (nkb_total column blocks, this tile's columns starting at block
-// kb_off) once per task and held in registers.  Results in S.rowres[row * B + b].
-__device__ __forceinline__ void flush_rows_b(f32x4v acc, uint32_t rg, int lane, int B) {
-    const int n = lane % 16, kq = lane / 16;
-    if (n < B) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t at = (rg * 16 + kq * 4 + i) * (uint32_t)B + n;
-            if (at < (uint32_t)ROWRES)
-                __hip_atomic_fetch_add(&S.rowres[at], acc[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        }
     }
 }
-template <int NB>
-__device__ __forceinline__ void load_bops_b(__amdgpu_buffer_rsrc_t r, int nkb_total, int kb0, int lane,
-                                            u32x4v (*bo)[NPART]) {
+// B operands of block 4 i + wave from its inputs: times the RMSNorm gains staged in
+// LDS (bf16, in S.rowres), split into two parts; the sum of squares of the unscaled
+// inputs is accumulated into ss.
+__device__ __forceinline__ void ops_of_row_block(const float* v, int i, int wave, int lane, float& ss, u32x4v* bo) {
+    const uint16_t* gl = (const uint16_t*)S.rowres;
+    const uint4 gw = *(const uint4*)&gl[32 * (4 * i + wave) + 8 * (lane / 16)];
+    const uint32_t gg[4] = {gw.x, gw.y, gw.z, gw.w};
+    float x[8];
 #pragma unroll
-    for (int i = 0; i < NB; ++i)
+    for (int e = 0; e < 4; ++e) {
+        ss = fmaf(v[2 * e], v[2 * e], ss);
+        ss = fmaf(v[2 * e + 1], v[2 * e + 1], ss);
+        x[2 * e] = v[2 * e] * bf16lo(gg[e]);
+        x[2 * e + 1] = v[2 * e + 1] * bf16hi(gg[e]);
+    }
+    split8(x, bo[0], bo[1]);
+}
+// B operands read from an operand region (nkb_total column blocks, this tile's first at kb_off)
+template <int NBW>
+__device__ __forceinline__ void bops_from_region(u32x4v (*bo)[NPART], __amdgpu_buffer_rsrc_t r, int nkb_total,
+                                                 int kb_off, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < NBW; ++i)
 #pragma unroll
         for (int pt = 0; pt < NPART; ++pt)
             bo[i][pt] = __builtin_bit_cast(
                 u32x4v, __builtin_amdgcn_raw_buffer_load_b128(
-                            r, ((uint32_t)(pt * nkb_total + kb0 + 4 * i) * 64u + (uint32_t)lane) * 16u, 0, 16));
+                            r, ((uint32_t)(pt * nkb_total + kb_off + 4 * i + wave) * 64u + (uint32_t)lane) * 16u, 0,
+                            16));
 }
 __device__ __forceinline__ f32x4v mfma_parts(u32x4v a, const u32x4v* b2, f32x4v acc) {
 #pragma unroll
@@ -1589,26 +1611,55 @@ __device__ __forceinline__ f32x4v mfma_parts(u32x4v a, const u32x4v* b2, f32x4v 
                                                       acc, 0, 0, 0);
     return acc;
 }
-// K >= 512: the tile's pages are stored k-step major (page s * nrg + rg holds column
-// blocks 16 s .. 16 s + 15 of row group rg), so each wave needs the B operands of
-// only four column blocks at a time (the next k-step's are loaded meanwhile) and
-// every page's products are added into the row results.  K <= 256: a page holds
-// 16 / (K / 32) whole row groups and the B operands are loaded once.
-template <int KT>
+// the 16 x 16 result block of row group rg into this wave's slice (first visit: store)
+__device__ __forceinline__ void slice_put(float* sl, f32x4v acc, uint32_t rg, int lane, int B, bool first) {
+    const int n = lane % 16, kq = lane / 16;
+    if (n < B) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t at = (rg * 16 + kq * 4 + i) * (uint32_t)B + n;
+            if (at < 1024u) sl[at] = first ? acc[i] : sl[at] + acc[i];
+        }
+    }
+}
+// row i, sequence b of the tile's result: the sum of the four waves' slices
+__device__ __forceinline__ float tile_res(int i, int b, int B) {
+    const int at = i * B + b;
+    return (S.xs[at] + S.xs[1024 + at]) + (S.xs[2048 + at] + S.xs[3072 + at]);
+}
+// 1 / RMS of sequence b from the per-wave sums of squares
+__device__ __forceinline__ float rs_seq(int b, int n, float eps) {
+    const float ss = (S.ssqb[0][b] + S.ssqb[1][b]) + (S.ssqb[2][b] + S.ssqb[3][b]);
+    return 1.0f / sqrtf(ss / (float)n + eps);
+}
+
+// K >= 512: pages stored k-step major (page s * nrg + rg holds column blocks
+// 16 s .. 16 s + 15 of row group rg); K <= 256: a page holds 16 / (K / 32) whole
+// row groups.  ROWS: the B operands are made from raw inputs (v, one k-step's four
+// blocks at a time, summing squares into ss); otherwise they are bo.
+template <int KT, bool ROWS>
 __device__ __forceinline__ bool gemv_mfma_b(const Params* pp, int wave, int lane, uint32_t page0, uint32_t wbytes,
-                                            const uint16_t* R, int nkb_total, int kb_off, int B, uint32_t task) {
+                                            const float (*v)[8], const u32x4v (*bo)[NPART], float& ss, int B,
+                                            uint32_t task) {
     static_assert(KT >= 128 && KT <= 2048, "matrix-core GEMV covers 128 <= K <= 2048");
     constexpr int NKB = KT / 32;
     const uint32_t npages = (wbytes + PAGE - 1) / PAGE;
-    const __amdgpu_buffer_rsrc_t r = dev_rsrc(R, (uint32_t)nkb_total * NPART * 1024u);
+    float* const sl = &S.xs[wave * 1024];
     if constexpr (NKB >= 16) {
         constexpr int PPR = NKB / 16;
         const uint32_t nrg = npages / PPR;
-        u32x4v bo[2][4][NPART];
-        load_bops_b<4>(r, nkb_total, kb_off + wave, lane, bo[0]);
 #pragma unroll
         for (int s = 0; s < PPR; ++s) {
-            if (s + 1 < PPR) load_bops_b<4>(r, nkb_total, kb_off + 16 * (s + 1) + wave, lane, bo[(s + 1) & 1]);
+            u32x4v cur[4][NPART];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if constexpr (ROWS) {
+                    ops_of_row_block(v[4 * s + j], 4 * s + j, wave, lane, ss, cur[j]);
+                } else {
+                    cur[j][0] = bo[4 * s + j][0];
+                    cur[j][1] = bo[4 * s + j][1];
+                }
+            }
             for (uint32_t rg = 0; rg < nrg; ++rg) {
                 const uint32_t pg = s * nrg + rg;
                 if (!page_acquire(pp, page0 + pg, task)) return false;
@@ -1619,15 +1670,23 @@ __device__ __forceinline__ bool gemv_mfma_b(const Params* pp, int wave, int lane
                 page_release(page0 + pg, lane);
                 f32x4v acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc = mfma_parts(a[j], bo[s & 1][j], acc);
-                flush_rows_b(acc, rg, lane, B);
+                for (int j = 0; j < 4; ++j) acc = mfma_parts(a[j], cur[j], acc);
+                slice_put(sl, acc, rg, lane, B, s == 0);
             }
         }
     } else {
         constexpr int RPG = 16 / NKB;  // row groups per page
         constexpr int BPR = 4 / RPG;   // blocks per row group and wave
-        u32x4v bo[BPR][NPART];
-        load_bops_b<BPR>(r, nkb_total, kb_off + wave, lane, bo);
+        u32x4v cur[BPR][NPART];
+#pragma unroll
+        for (int j = 0; j < BPR; ++j) {
+            if constexpr (ROWS) {
+                ops_of_row_block(v[j], j, wave, lane, ss, cur[j]);
+            } else {
+                cur[j][0] = bo[j][0];
+                cur[j][1] = bo[j][1];
+            }
+        }
         for (uint32_t pg = 0; pg < npages; ++pg) {
             if (!page_acquire(pp, page0 + pg, task)) return false;
             const uint32_t slot = (page0 + pg) % NPAGES;
@@ -1639,42 +1698,57 @@ __device__ __forceinline__ bool gemv_mfma_b(const Params* pp, int wave, int lane
             for (int rr = 0; rr < RPG; ++rr) {
                 f32x4v acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int jj = 0; jj < BPR; ++jj) acc = mfma_parts(a[rr * BPR + jj], bo[jj], acc);
-                flush_rows_b(acc, pg * RPG + rr, lane, B);
+                for (int jj = 0; jj < BPR; ++jj) acc = mfma_parts(a[rr * BPR + jj], cur[jj], acc);
+                slice_put(sl, acc, pg * RPG + rr, lane, B, true);
             }
         }
     }
     return true;
 }
 
-// Batched GEMV task (QKV, O-proj, gate/up, down, LM head) for B > 1 sequences.
-template <int KT>
+// Batched GEMV task (QKV, O-proj, gate/up, down, LM head) for B > 1 sequences.  QKV,
+// gate/up and LM head read the residual rows themselves and apply RMSNorm (gains on
+// the inputs, 1/RMS per sequence on the results); O-proj and down read the operand
+// regions their producers wrote.
+template <int KT, bool NORMED>
 __device__ __noinline__ bool op_gemv_b(const Params* pp, uint32_t slot_, uint32_t page0, uint32_t t_, uint32_t epoch_) {
     const Task k = fifo_task(slot_);
     Ctx c = make_ctx(t_, epoch_);
     CParams& p = P(pp);
     const int lane = c.lane, tid = c.tid, wave = c.wave;
-    const int B = p.T.B, L = p.T.L, l = k.layer, D = p.T.d;
-    const uint16_t* R;
-    int nkb_total, kb_off = 0, norm_slot = -1;
-    switch (k.op) {
-        case OP_QKV: norm_slot = 2 * l; R = opr_norm(p, norm_slot); nkb_total = p.T.h / 32; break;
-        case OP_GATEUP: norm_slot = 2 * l + 1; R = opr_norm(p, norm_slot); nkb_total = p.T.h / 32; break;
-        case OP_LMHEAD: norm_slot = 2 * L; R = opr_norm(p, norm_slot); nkb_total = p.T.h / 32; break;
-        case OP_OPROJ:
-            R = opr_attn(p, l);
-            nkb_total = p.T.nq * D / 32;
-            kb_off = k.part * p.T.grp * D / 32;
-            break;
-        default:  // OP_DOWN
-            R = opr_m(p, l);
-            nkb_total = p.T.f / 32;
-            kb_off = k.part * p.T.kd / 32;
-            break;
-    }
+    const int B = p.T.B, L = p.T.L, l = k.layer, D = p.T.d, h = p.T.h;
+    constexpr bool normed = NORMED;  // QKV, gate/up, LM head
+    // normalised inputs: gains slot and source residual (-1: the embedding)
+    const int gslot = k.op == OP_QKV ? 2 * l : (k.op == OP_GATEUP ? 2 * l + 1 : 2 * L);
+    const int src = k.op == OP_GATEUP ? 2 * l : (l == 0 ? -1 : 2 * l - 1);
+    uint4 gpre = make_uint4(0, 0, 0, 0);
+    if (normed && tid * 8 < h) gpre = gld_u4(gains(p, gslot) + tid * 8);
     if (!await_inputs(pp, k, c)) return false;
-    zero_rowres(tid);
-    if (!cbarrier(pp, c, k.id)) return false;
+    constexpr int NBW = KT / 128;
+    float v[NORMED ? NBW : 1][8];
+    u32x4v bo[NORMED ? 1 : NBW][NPART];
+    if constexpr (NORMED) {
+        if (tid * 8 < h) *(uint4*)&((uint16_t*)S.rowres)[tid * 8] = gpre;
+        const int n = lane % 16;
+        const bool emb = src < 0;
+        __amdgpu_buffer_rsrc_t r;
+        uint32_t row_ofs;
+        if (emb) {
+            r = __builtin_amdgcn_make_buffer_rsrc((void*)(p.w + p.lay.embed), 0, (uint32_t)((uint64_t)p.T.V * h * 2),
+                                                  RSRC_FLAGS);
+            row_ofs = n < B ? (uint32_t)S.tok[n] * (uint32_t)h : (uint32_t)p.T.V * (uint32_t)h;
+        } else {
+            r = dev_rsrc(acc_buf(p, c.parity, src, 0), (uint32_t)(B * h * 4));
+            row_ofs = (uint32_t)(n * h);  // sequences past B read zeros (out of the buffer's range)
+        }
+        load_rows<NBW>(v, r, emb, row_ofs, wave, lane);
+        if (!cbarrier(pp, c, k.id)) return false;  // gains staged
+    } else {
+        const uint16_t* R = k.op == OP_OPROJ ? opr_attn(p, l) : opr_m(p, l);
+        const int nkb_total = k.op == OP_OPROJ ? p.T.nq * D / 32 : p.T.f / 32;
+        const int kb_off = k.op == OP_OPROJ ? k.part * p.T.grp * D / 32 : k.part * p.T.kd / 32;
+        bops_from_region<NBW>(bo, dev_rsrc(R, (uint32_t)nkb_total * NPART * 1024u), nkb_total, kb_off, wave, lane);
+    }
     tmark(c, 0);
     // residual (rows x sequences) of residual-adding tiles, in flight during the GEMV
     const bool resid = (k.op == OP_OPROJ || k.op == OP_DOWN) && (k.flags & TF_RESID);
@@ -1685,29 +1759,31 @@ __device__ __noinline__ bool op_gemv_b(const Params* pp, uint32_t slot_, uint32_
         const int idx = tid + q * NCW * 64;
         if (resid && idx < (int)k.nrows * B) {
             const int i = idx / B, b = idx % B, row = (int)k.row0 + i;
-            const int src = k.op == OP_DOWN ? 2 * l : (l == 0 ? -1 : 2 * l - 1);
-            res[q] = src < 0 ? bf16f(gld((const uint16_t*)(p.w + p.lay.embed) + (size_t)S.tok[b] * p.T.h + row))
-                             : ldb_dev(dev_rsrc(acc_buf(p, c.parity, src, b) + row, 4), 0);
+            const int rsrc_i = k.op == OP_DOWN ? 2 * l : (l == 0 ? -1 : 2 * l - 1);
+            res[q] = rsrc_i < 0 ? bf16f(gld((const uint16_t*)(p.w + p.lay.embed) + (size_t)S.tok[b] * h + row))
+                                : ldb_dev(dev_rsrc(acc_buf(p, c.parity, rsrc_i, b) + row, 4), 0);
         }
     }
-    if (!gemv_mfma_b<KT>(pp, wave, lane, page0, k.wbytes, R, nkb_total, kb_off, B, k.id)) return false;
+    float ss = 0.f;
+    if constexpr (NORMED) {
+        if (!gemv_mfma_b<KT, true>(pp, wave, lane, page0, k.wbytes, v, bo, ss, B, k.id)) return false;
+        ss += __shfl_xor(ss, 16, 64);
+        ss += __shfl_xor(ss, 32, 64);
+        if (lane < MAX_BATCH) S.ssqb[wave][lane] = ss;
+    } else {
+        if (!gemv_mfma_b<KT, false>(pp, wave, lane, page0, k.wbytes, v, bo, ss, B, k.id)) return false;
+    }
     if (!cbarrier(pp, c, k.id)) return false;
     tmark(c, 1);
-    // 1/RMS of each sequence's normalised input (its sum of squares is complete: NORM tasks precede)
-    float rs = 1.0f;
-    if (norm_slot >= 0) rs = 1.0f / sqrtf(ldb_dev(dev_rsrc(ssq_at(p, c.parity, norm_slot), B * 4), (lane % B) * 4) /
-                                          (float)p.T.h + p.eps);
-    // rs of sequence b lives in lanes b, b + B, ...: fetch it for any b through LDS-free shuffles
-    auto rs_of = [&](int b) { return __shfl(rs, b, 64); };
     if (k.op == OP_QKV) {
         const uint32_t n = k.nrows, slot = k.part;
         const int half = D / 2, nq = p.T.nq, nkv = p.T.nkv;
         const int b = tid / (int)n, i = tid % (int)n;
-        const float rb = rs_of(b < B ? b : 0);
         if (b < B) {
+            const float rb = rs_seq(b, h, p.eps);
             const int32_t Pb = S.pos[b];
             const int j = (int)k.row0 + i;
-            float lo = S.rowres[i * B + b] * rb, hi = S.rowres[(n + i) * B + b] * rb;
+            float lo = tile_res(i, b, B) * rb, hi = tile_res((int)n + i, b, B) * rb;
             if (slot < (uint32_t)(nq + nkv)) {
                 const float2 cs = gld_f2(p.rope + (size_t)Pb * half + j);
                 const float x0 = lo * cs.x - hi * cs.y, x1 = lo * cs.y + hi * cs.x;
@@ -1729,24 +1805,20 @@ __device__ __noinline__ bool op_gemv_b(const Params* pp, uint32_t slot_, uint32_
         }
     } else if (k.op == OP_GATEUP) {
         uint16_t* Rm = opr_m(p, l);
-        for (int base = 0; base < (int)k.nrows * B; base += NCW * 64) {  // uniform trip count: rs_of with all lanes
-            const int idx = base + tid;
-            const bool act = idx < (int)k.nrows * B;
-            const int i = act ? idx / B : 0, b = act ? idx % B : 0;
-            const float rb = rs_of(b);
-            if (act) {
-                const float gt = S.rowres[i * B + b] * rb, up = S.rowres[(k.nrows + i) * B + b] * rb;
-                put_op1(Rm, p.T.f / 32, (int)k.row0 + i, b, gt / (1.0f + __expf(-gt)) * up);
-            }
+        for (int idx = tid; idx < (int)k.nrows * B; idx += NCW * 64) {
+            const int i = idx / B, b = idx % B;
+            const float rb = rs_seq(b, h, p.eps);
+            const float gt = tile_res(i, b, B) * rb, up = tile_res((int)k.nrows + i, b, B) * rb;
+            put_op1(Rm, p.T.f / 32, (int)k.row0 + i, b, gt / (1.0f + __expf(-gt)) * up);
         }
     } else if (k.op == OP_LMHEAD) {
         float* logits = S.args.logits;
         for (int b = wave; b < B; b += NCW) {
-            const float rb = rs_of(b);
+            const float rb = rs_seq(b, h, p.eps);
             float bv = -INFINITY;
             uint32_t bi = 0xffffffffu;
             for (uint32_t i = (uint32_t)lane; i < k.nrows; i += 64) {
-                const float val = S.rowres[i * B + b] * rb;
+                const float val = tile_res((int)i, b, B) * rb;
                 if (logits) gst(logits + (size_t)b * p.T.V + k.row0 + i, val);
                 if (val > bv) {
                     bv = val;
@@ -1765,6 +1837,7 @@ __device__ __noinline__ bool op_gemv_b(const Params* pp, uint32_t slot_, uint32_
                 __hip_atomic_fetch_max((g_u64*)&p.key[c.parity * B + b], key, __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_AGENT);
         }
+        copy_hidden_share(p, k, c.parity, tid);
     } else {  // O-proj / down: residual accumulation
         const int dst = k.op == OP_DOWN ? 2 * l + 1 : 2 * l;
 #pragma unroll
@@ -1772,14 +1845,24 @@ __device__ __noinline__ bool op_gemv_b(const Params* pp, uint32_t slot_, uint32_
             const int idx = tid + q * NCW * 64;
             if (idx < (int)k.nrows * B) {
                 const int i = idx / B, b = idx % B;
-                addf_dev(acc_buf(p, c.parity, dst, b) + k.row0 + i, S.rowres[i * B + b] + res[q]);
+                addf_dev(acc_buf(p, c.parity, dst, b) + k.row0 + i, tile_res(i, b, B) + res[q]);
             }
         }
     }
     return true;
 }
 
-// After the last LM-head tile of the step: publish the argmax and the final residual.
+template <int KT>
+__device__ __forceinline__ bool op_gemv_bn(const Params* pp, uint32_t slot, uint32_t page0, uint32_t t, uint32_t epoch) {
+    return op_gemv_b<KT, true>(pp, slot, page0, t, epoch);
+}
+template <int KT>
+__device__ __forceinline__ bool op_gemv_br(const Params* pp, uint32_t slot, uint32_t page0, uint32_t t, uint32_t epoch) {
+    return op_gemv_b<KT, false>(pp, slot, page0, t, epoch);
+}
+
+// After the last LM-head tile of the step: publish the argmax (the LM-head tiles
+// have published the final residual).
 __device__ __noinline__ void finish_step(const Params* pp, uint32_t epoch, uint32_t parity) {
     CParams& p = P(pp);
     const int lane = threadIdx.x & 63;
@@ -1787,20 +1870,11 @@ __device__ __noinline__ void finish_step(const Params* pp, uint32_t epoch, uint3
     if (lane == 0) old = addu_dev(&p.ticket[0], 1u);
     old = uni(old);
     if (old + 1u != epoch * (uint32_t)p.T.n_lm_tiles) return;
-    const int B = p.T.B, h = p.T.h;
-    if (lane < B) {
+    const int B = p.T.B;
+    for (int b = lane; b < B; b += 64) {
         const unsigned long long key =
-            __hip_atomic_load((g_u64*)&p.key[parity * B + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        gst(p.next + lane, (int32_t)(0xffffffffu - (uint32_t)(key & 0xffffffffu)));
-    }
-    for (int b = 0; b < B; ++b) {
-        if (p.T.L == 0) {
-            const uint16_t* e = embed_row(p, b);
-            for (int i = lane; i < h; i += 64) gst(p.hidden + (size_t)b * h + i, bf16f(gld(e + i)));
-        } else {
-            const float* src = acc_buf(p, parity, 2 * p.T.L - 1, b);
-            for (int i = lane; i < h; i += 64) gst(p.hidden + (size_t)b * h + i, ldf_dev(src + i));
-        }
+            __hip_atomic_load((g_u64*)&p.key[parity * B + b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        gst(p.next + b, (int32_t)(0xffffffffu - (uint32_t)(key & 0xffffffffu)));
     }
 }
 
@@ -1842,12 +1916,10 @@ __device__ __noinline__ void compute(const Params* pp, uint32_t epoch, int wave)
             switch (k.op) {
                 case OP_QKV:
                 case OP_GATEUP:
-                case OP_LMHEAD: ok = MK_KT_DISPATCH_2K(op_gemv_b, h, pp, slot, page0, t, epoch); break;
-                case OP_OPROJ: ok = MK_KT_DISPATCH_2K(op_gemv_b, okt, pp, slot, page0, t, epoch); break;
-                case OP_DOWN: ok = MK_KT_DISPATCH_2K(op_gemv_b, dkt, pp, slot, page0, t, epoch); break;
+                case OP_LMHEAD: ok = MK_KT_DISPATCH_2K(op_gemv_bn, h, pp, slot, page0, t, epoch); break;
+                case OP_OPROJ: ok = MK_KT_DISPATCH_2K(op_gemv_br, okt, pp, slot, page0, t, epoch); break;
+                case OP_DOWN: ok = MK_KT_DISPATCH_2K(op_gemv_br, dkt, pp, slot, page0, t, epoch); break;
                 case OP_ATTN: ok = hd == 64 ? op_attn<64>(pp, slot, page0, t, epoch) : op_attn<128>(pp, slot, page0, t, epoch); break;
-                case OP_NORM: ok = op_norm(pp, slot, t, epoch); break;
-                case OP_MERGE: ok = op_merge(pp, slot, t, epoch); break;
                 default: break;
             }
         } else switch (k.op) {
@@ -1938,10 +2010,6 @@ __global__ void __launch_bounds__(NTHREADS, 1) mk_step_kernel(const Params* pp, 
         for (size_t i = (size_t)blockIdx.x * NTHREADS + threadIdx.x; i < nacc; i += (size_t)gridDim.x * NTHREADS)
             other[i] = 0.f;
         if (blockIdx.x == 0 && (int)threadIdx.x < B) p.key[(parity ^ 1u) * B + threadIdx.x] = 0ull;
-        if (p.ssq && blockIdx.x == gridDim.x - 1) {
-            const int nss = (2 * p.T.L + 1) * B;
-            for (int i = threadIdx.x; i < nss; i += NTHREADS) p.ssq[(size_t)(parity ^ 1u) * nss + i] = 0.f;
-        }
         if (wave >= NCW) loader(pp, epoch, wave - NCW);
         else compute(pp, epoch, wave);
     }

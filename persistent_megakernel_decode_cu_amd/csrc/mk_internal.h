@@ -14,11 +14,7 @@ enum Op : uint8_t {
     OP_GATEUP = 4,    // RMSNorm + gate/up GEMV tile + SiLU * up
     OP_DOWN = 5,      // down-proj K-slice tile + residual (atomic)
     OP_LMHEAD = 6,    // final RMSNorm + LM-head tile + argmax (packed 64-bit atomic max)
-    // batch > 1 only: the GEMV inputs of all sequences are prepared once in global
-    // memory as matrix-core operands (sequences = operand columns)
-    OP_NORM = 7,      // column block of RMSNorm inputs: sum of squares per sequence, gains, operand split
-    OP_MERGE = 8,     // merge of one KV group's attention partials for every sequence, operand split
-    OP_COUNT = 9
+    OP_COUNT = 7
 };
 
 constexpr uint32_t NONE = 0xFFFFFFFFu;
@@ -35,9 +31,9 @@ struct Task {
     uint8_t sig_nsub;      // sub-counters of the signalled event (1 or 8)
     uint8_t flags;         // op-specific (OPROJ/DOWN: add the residual)
     uint16_t layer;
-    uint16_t part;         // QKV: head slot; ATTN/OPROJ/MERGE: KV group; DOWN: K block; NORM: 0 attn, 1 ffn, 2 final
-    uint32_t row0;         // first output row (QKV: first RoPE pair; ATTN: chunk index; NORM: first column)
-    uint32_t nrows;        // output rows of the tile (QKV: pairs; NORM: columns)
+    uint16_t part;         // QKV: head slot; ATTN/OPROJ: KV group; DOWN: K block
+    uint32_t row0;         // first output row (QKV: first RoPE pair; ATTN: chunk index)
+    uint32_t nrows;        // output rows of the tile (QKV: pairs)
     uint32_t wait_ev;      // awaited event or NONE
     uint32_t wait_target;  // producers of the awaited event (per step)
     uint32_t sig_ev;       // signalled event or NONE
@@ -65,7 +61,6 @@ struct Tiling {
     int32_t d_rows;       // down-proj tile rows
     int32_t lm_rows;      // LM-head rows per tile
     int32_t n_qkv_tiles, n_attn_tiles, n_o_tiles, n_gu_tiles, n_down_tiles, n_lm_tiles;  // per layer / total LM
-    int32_t norm_cols;    // batch > 1: columns per NORM task (0 for batch 1)
 };
 
 // Byte layout of the handle-owned packed weight buffer.
@@ -89,8 +84,7 @@ struct ExportHeader {
     int32_t L, h, nq, nkv, d, f, V, B, C;
     int32_t grp, qkv_pairs, attn_splits, o_rows, g_rows, kd, d_rows, lm_rows;
     uint32_t record_bytes;
-    int32_t norm_cols;
-    uint32_t reserved[6];
+    uint32_t reserved[7];
 };
 constexpr uint32_t EXPORT_MAGIC = 0x31474B4Du;
 

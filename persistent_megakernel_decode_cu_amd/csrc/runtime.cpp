@@ -25,7 +25,6 @@ struct mk_handle {
     Params* dparams = nullptr;  // device copy read by the kernel
     size_t n_events = 0;
     size_t acc_bytes = 0;
-    size_t ssq_bytes = 0;
     // device allocations owned by the handle
     std::vector<void*> allocs;
 };
@@ -202,7 +201,7 @@ mk_status rearm(mk_handle* h) {
     st[ST_EPOCH] = 1;
     HIPCHK(hipMemcpy(p.state, st.data(), ST_WORDS * 4, hipMemcpyHostToDevice));
     HIPCHK(hipMemset(p.acc, 0, h->acc_bytes));
-    if (p.ssq) HIPCHK(hipMemset(p.ssq, 0, h->ssq_bytes));
+    if (p.aticket) HIPCHK(hipMemset(p.aticket, 0, (size_t)T.L * T.B * T.nkv * 4));
     HIPCHK(hipMemset(p.key, 0, sizeof(unsigned long long) * 2 * T.B));
     HIPCHK(hipMemset(p.ticket, 0, 4 * T.B));
     HIPCHK(hipDeviceSynchronize());
@@ -330,12 +329,11 @@ mk_status mk_build_graph(const mk_model_desc* desc, int32_t batch, int32_t max_c
     h->acc_bytes = (size_t)2 * (2 * T.L + 1) * T.B * T.h * 4;
     ALLOC(p.acc, h->acc_bytes, true);
     if (T.B > 1) {
-        // operand columns of absent sequences stay zero for the life of the handle
-        // matrix-core operands of every GEMV input: 2 bf16 parts x 16 sequences per column
-        const size_t xop_elems = ((size_t)(2 * T.L + 1) * T.h + (size_t)T.L * T.nq * T.d + (size_t)T.L * T.f) * 32;
+        // matrix-core operands of the O- and down-projection inputs: 2 bf16 parts x 16
+        // sequences per column (columns of absent sequences stay zero for the handle's life)
+        const size_t xop_elems = ((size_t)T.L * T.nq * T.d + (size_t)T.L * T.f) * 32;
         ALLOC(p.xop, xop_elems * 2, true);
-        h->ssq_bytes = (size_t)2 * (2 * T.L + 1) * T.B * 4;
-        ALLOC(p.ssq, h->ssq_bytes, true);
+        ALLOC(p.aticket, (size_t)T.L * T.B * T.nkv * 4, true);
     }
     ALLOC(p.hidden, (size_t)T.B * T.h * 4, true);
     ALLOC(p.key, sizeof(unsigned long long) * 2 * T.B, true);

@@ -44,11 +44,11 @@ struct Params {
     float* part;              // [B][n_kv][S][grp][d+2]
     float* m;                 // [B][f]
     float* acc;               // [2][2L+1][B][h] residual accumulators (by step parity)
-    // batch > 1: GEMV inputs of all sequences as matrix-core B operands, bf16 parts
-    // hi/mid/lo of 16 x 32 column blocks (lane l: sequence l % 16, columns 8 (l / 16) .. +7)
-    uint16_t* xop;            // [2L+1 normalised inputs][3][h/32][64][8], then [L][3][nq*d/32][64][8]
-                              // (merged attention), then [L][3][f/32][64][8] (SiLU(gate) * up)
-    float* ssq;               // [2][2L+1][B] sums of squares of the normalised inputs (by step parity)
+    // batch > 1: inputs of the O-projection and down-projection of all sequences as
+    // matrix-core B operands, bf16 parts hi/lo of 16 x 32 column blocks (lane l:
+    // sequence l % 16, columns 8 (l / 16) .. +7)
+    uint16_t* xop;            // [L][2][nq*d/32][64][8] (merged attention), then [L][2][f/32][64][8] (SiLU(gate) * up)
+    uint32_t* aticket;        // batch > 1: [L][B][n_kv] finished attention chunks (the last one merges)
     float* hidden;            // [B][h]
     unsigned long long* key;  // [2][B] packed argmax keys
     uint32_t* ticket;         // [B]

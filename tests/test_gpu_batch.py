@@ -1,5 +1,6 @@
-"""GPU parity of the megakernel with several sequences per step (matrix-core projections,
-NORM and MERGE tasks, split-KV attention per sequence) against the oracle, through the C ABI."""
+"""GPU parity of the megakernel with several sequences per step (matrix-core projections
+over all sequences, fixed-length split-KV attention chunks merged by the last chunk of each
+sequence and KV group) against the oracle, through the C ABI."""
 import numpy as np
 import pytest
 import torch
