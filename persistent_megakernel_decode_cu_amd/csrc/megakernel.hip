@@ -1236,8 +1236,10 @@ __device__ __noinline__ bool op_attn(const Params* pp, uint32_t slot_, uint32_t 
             for (int i = 0; i < BATCH; ++i) {
                 const float e = sc[i] == -INFINITY ? 0.f : __expf(sc[i] - mn);
                 es += e;
-                // weights stored so that lane (chunk, group) finds its IT positions contiguous
-                if ((uint32_t)i < nb) wsc[i * 64 + (lane % NPG) * IT + lane / NPG] = e;
+                // weights stored so that lane (chunk, group) finds its IT positions contiguous;
+                // with fewer positions per page than lanes (head_dim 128) only the position
+                // lanes store, the others would land on the same slots
+                if ((uint32_t)i < nb && lane < PB) wsc[i * 64 + (lane % NPG) * IT + lane / NPG] = e;
             }
             Ls[hh] = Ls[hh] * corr + wave_sum(es);
             M[hh] = mn;
