@@ -32,10 +32,10 @@ The tiling rules (written from the design, not from the C++ code):
     d_rows = min(h, 1024 // B, max(16, pow2_floor(h * (f / kd) / W))) rows).
   * gate/up tiles: g_rows gate rows then the same g_rows up rows, with
     g_rows = min(kd, (1024 // B) // 2, max(8, pow2_ceil(ceil(f / W)))).
-  * LM head tiles: lm_rows = min(1024 // B rounded down to 16, ceil(V / W)
-    rounded up to 16) rows, the last one shorter; its weight bytes are its rows
-    rounded up to 16 (rows x sequences of every tile, padding included, stay
-    within the 1024 row results a workgroup holds).
+  * LM head tiles: lm_rows = min(1024, ceil(V / W) rounded up to 16) rows, the
+    last one shorter; its weight bytes are its rows rounded up to 16.  (With
+    several sequences a workgroup takes an LM tile in chunks of
+    (1024 // B) // 64 * 64 rows, so its row results stay within 1024 values.)
   * per layer the events are created in the order qkv[g], attn[g], xb, m[kb],
     x_next; tasks in the order QKV, attention, O-proj, gate/up, down; then the
     LM-head tiles.  An event with more than 32 producers uses 8 sub-counters.
@@ -100,7 +100,7 @@ def tiling(cfg, B, C, W, attn_splits=0):
                 o_rows=min(h, max_rows, max(16, _pow2_floor(h * nkv // W))),
                 kd=kd, d_rows=min(h, max_rows, max(16, _pow2_floor(h * (f // kd) // W))),
                 g_rows=min(kd, max_rows // 2, max(8, _pow2_ceil(-(-f // W)))),
-                lm_rows=min(max_rows // 16 * 16, _round16(-(-V // W))))
+                lm_rows=min(1024, _round16(-(-V // W))))
 
 
 def layout(cfg, lm_rows, n_lm):

@@ -94,7 +94,9 @@ int plan_tiling(const Dims& dm, int B, int C, int W, const PlanOptions& o, Tilin
     if (T.g_rows > max_rows / 2) T.g_rows = (int)(max_rows / 2);
     if (T.kd % T.g_rows) return fail("gate/up tile does not divide the down-proj K block");
     T.n_gu_tiles = dm.f / T.g_rows;
-    T.lm_rows = (int)std::min<int64_t>(max_rows / 16 * 16, round16((dm.V + W - 1) / W));  // whole 16-row groups
+    // LM head: about one tile per workgroup (with several sequences the device takes a
+    // tile in chunks of whole row groups within the row-result bound)
+    T.lm_rows = (int)std::min<int64_t>(MAX_TILE_ROWS, round16((dm.V + W - 1) / W));
     T.n_lm_tiles = (dm.V + T.lm_rows - 1) / T.lm_rows;
     return 0;
 }

@@ -1155,6 +1155,9 @@ __device__ __noinline__ bool op_attn(const Params* pp, uint32_t slot_, uint32_t 
     const int nh = (G - wave + NCW - 1) / NCW;  // heads of this wave: wave, wave + NCW, ...
     const bool has_cur = ch.c0 <= ch.P && ch.P < ch.c1;
     const int cl = lane % NC, pgl = lane / NC;  // P.V: dimension chunk and position group of this lane
+    // an empty chunk slot (several sequences; their merge reads only the non-empty
+    // chunks): no pages, no partials.  At batch 1 every chunk writes its partials.
+    if (p.T.B > 1 && ch.c0 > ch.P) return true;
     if (!await_inputs(pp, k, c)) return false;
     // each wave stages the query rows of its own heads, and the current token's K/V chunk
     float kc8[8], vc8[8];
@@ -1332,16 +1335,19 @@ __device__ __noinline__ bool op_attn(const Params* pp, uint32_t slot_, uint32_t 
             for (int ee = 0; ee < 8; ++ee) stf_dev(dst + 2 + cl * 8 + ee, o[hh][ee]);
         }
     }
-    if (p.T.B > 1) {
-        // several sequences: the last chunk of (sequence, group) to finish merges them all
+    if (p.T.B > 1 && nh > 0) {
+        // several sequences: every wave with heads counts its finished partials on the
+        // step's ticket of (sequence, group); the wave completing the count over the
+        // non-empty chunks merges them all
         vm_wait_all();  // this wave's partials are stored
-        if (!cbarrier(pp, c, k.id)) return false;
-        if (wave == 0) {
-            uint32_t old = 0;
-            if (lane == 0) old = addu_dev(&p.aticket[((size_t)k.layer * p.T.B + b) * p.T.nkv + g], 1u);
-            old = uni(old);
-            if (old + 1u == c.epoch * (uint32_t)p.T.attn_splits) merge_chunks(pp, k.layer, b, g, ch.P, lane);
-        }
+        const int32_t fl = attn_fixed_len(p.T.B, p.T.C, p.T.attn_splits);
+        const uint32_t nch = (uint32_t)min(p.T.attn_splits, (ch.P + fl) / fl);
+        const uint32_t want = nch * (uint32_t)min(G, NCW);
+        uint32_t old = 0;
+        if (lane == 0)
+            old = addu_dev(&p.aticket[(((size_t)c.parity * p.T.L + k.layer) * p.T.B + b) * p.T.nkv + g], 1u);
+        old = uni(old);
+        if (old + 1u == want) merge_chunks(pp, k.layer, b, g, ch.P, lane);
     }
     return true;
 }
@@ -1640,16 +1646,14 @@ __device__ __forceinline__ float rs_seq(int b, int n, float eps) {
 // row groups.  ROWS: the B operands are made from raw inputs (v, one k-step's four
 // blocks at a time, summing squares into ss); otherwise they are bo.
 template <int KT, bool ROWS>
-__device__ __forceinline__ bool gemv_mfma_b(const Params* pp, int wave, int lane, uint32_t page0, uint32_t wbytes,
+__device__ __forceinline__ bool gemv_mfma_b(const Params* pp, int wave, int lane, uint32_t page0, uint32_t nrg,
                                             const float (*v)[8], const u32x4v (*bo)[NPART], float& ss, int B,
                                             uint32_t task) {
     static_assert(KT >= 128 && KT <= 2048, "matrix-core GEMV covers 128 <= K <= 2048");
     constexpr int NKB = KT / 32;
-    const uint32_t npages = (wbytes + PAGE - 1) / PAGE;
     float* const sl = &S.xs[wave * 1024];
     if constexpr (NKB >= 16) {
         constexpr int PPR = NKB / 16;
-        const uint32_t nrg = npages / PPR;
 #pragma unroll
         for (int s = 0; s < PPR; ++s) {
             u32x4v cur[4][NPART];
@@ -1679,6 +1683,7 @@ __device__ __forceinline__ bool gemv_mfma_b(const Params* pp, int wave, int lane
     } else {
         constexpr int RPG = 16 / NKB;  // row groups per page
         constexpr int BPR = 4 / RPG;   // blocks per row group and wave
+        const uint32_t npages = (nrg + RPG - 1) / RPG;
         u32x4v cur[BPR][NPART];
 #pragma unroll
         for (int j = 0; j < BPR; ++j) {
@@ -1766,16 +1771,53 @@ __device__ __noinline__ bool op_gemv_b(const Params* pp, uint32_t slot_, uint32_
                                 : ldb_dev(dev_rsrc(acc_buf(p, c.parity, rsrc_i, b) + row, 4), 0);
         }
     }
-    float ss = 0.f;
-    if constexpr (NORMED) {
-        if (!gemv_mfma_b<KT, true>(pp, wave, lane, page0, k.wbytes, v, bo, ss, B, k.id)) return false;
-        ss += __shfl_xor(ss, 16, 64);
-        ss += __shfl_xor(ss, 32, 64);
-        if (lane < MAX_BATCH) S.ssqb[wave][lane] = ss;
-    } else {
-        if (!gemv_mfma_b<KT, false>(pp, wave, lane, page0, k.wbytes, v, bo, ss, B, k.id)) return false;
+    // the tile's rows in chunks of whole row groups whose results fit the slices
+    // (one chunk except for LM-head tiles)
+    constexpr int NKB = KT / 32;
+    const int CR = MAX_TILE_ROWS / B / 64 * 64;
+    const int rows_pad = (int)(k.wbytes / (KT * 2));
+    float lm_bv[MAX_BATCH / NCW];
+    uint32_t lm_bi[MAX_BATCH / NCW];
+#pragma unroll
+    for (int j = 0; j < MAX_BATCH / NCW; ++j) {
+        lm_bv[j] = -INFINITY;
+        lm_bi[j] = 0xffffffffu;
     }
-    if (!cbarrier(pp, c, k.id)) return false;
+    for (int c0 = 0; c0 < rows_pad; c0 += CR) {
+        const uint32_t nrg = (uint32_t)min(CR, rows_pad - c0) / 16;
+        const uint32_t pbase = page0 + (NKB >= 16 ? (uint32_t)(c0 / 16) * (NKB / 16) : (uint32_t)(c0 / 16) / (16 / NKB));
+        if (c0 > 0 && !cbarrier(pp, c, k.id)) return false;  // the previous chunk's results are consumed
+        float ss = 0.f;
+        if constexpr (NORMED) {
+            if (!gemv_mfma_b<KT, true>(pp, wave, lane, pbase, nrg, v, bo, ss, B, k.id)) return false;
+            if (c0 == 0) {
+                ss += __shfl_xor(ss, 16, 64);
+                ss += __shfl_xor(ss, 32, 64);
+                if (lane < MAX_BATCH) S.ssqb[wave][lane] = ss;
+            }
+        } else {
+            if (!gemv_mfma_b<KT, false>(pp, wave, lane, pbase, nrg, v, bo, ss, B, k.id)) return false;
+        }
+        if (!cbarrier(pp, c, k.id)) return false;
+        if (k.op == OP_LMHEAD) {  // logits of the chunk, running argmax per sequence
+            float* logits = S.args.logits;
+            const int nr = min(CR, (int)k.nrows - c0);
+#pragma unroll
+            for (int j = 0; j < MAX_BATCH / NCW; ++j) {
+                const int b = wave + j * NCW;
+                if (b >= B) break;
+                const float rb = rs_seq(b, h, p.eps);
+                for (int i = lane; i < nr; i += 64) {
+                    const float val = tile_res(i, b, B) * rb;
+                    if (logits) gst(logits + (size_t)b * p.T.V + k.row0 + c0 + i, val);
+                    if (val > lm_bv[j]) {  // rows visited in increasing order per lane: the first maximum is kept
+                        lm_bv[j] = val;
+                        lm_bi[j] = k.row0 + (uint32_t)(c0 + i);
+                    }
+                }
+            }
+        }
+    }
     tmark(c, 1);
     if (k.op == OP_QKV) {
         const uint32_t n = k.nrows, slot = k.part;
@@ -1814,19 +1856,12 @@ __device__ __noinline__ bool op_gemv_b(const Params* pp, uint32_t slot_, uint32_
             put_op1(Rm, p.T.f / 32, (int)k.row0 + i, b, gt / (1.0f + __expf(-gt)) * up);
         }
     } else if (k.op == OP_LMHEAD) {
-        float* logits = S.args.logits;
-        for (int b = wave; b < B; b += NCW) {
-            const float rb = rs_seq(b, h, p.eps);
-            float bv = -INFINITY;
-            uint32_t bi = 0xffffffffu;
-            for (uint32_t i = (uint32_t)lane; i < k.nrows; i += 64) {
-                const float val = tile_res((int)i, b, B) * rb;
-                if (logits) gst(logits + (size_t)b * p.T.V + k.row0 + i, val);
-                if (val > bv) {
-                    bv = val;
-                    bi = k.row0 + i;
-                }
-            }
+#pragma unroll
+        for (int j = 0; j < MAX_BATCH / NCW; ++j) {
+            const int b = wave + j * NCW;
+            if (b >= B) break;
+            const float bv = lm_bv[j];
+            const uint32_t bi = lm_bi[j];
             const uint32_t ub = __float_as_uint(bv);
             const uint32_t ord = (ub & 0x80000000u) ? ~ub : (ub | 0x80000000u);
             unsigned long long key = bi == 0xffffffffu ? 0ull : (((unsigned long long)ord << 32) | (0xffffffffu - bi));
@@ -2012,6 +2047,11 @@ __global__ void __launch_bounds__(NTHREADS, 1) mk_step_kernel(const Params* pp, 
         for (size_t i = (size_t)blockIdx.x * NTHREADS + threadIdx.x; i < nacc; i += (size_t)gridDim.x * NTHREADS)
             other[i] = 0.f;
         if (blockIdx.x == 0 && (int)threadIdx.x < B) p.key[(parity ^ 1u) * B + threadIdx.x] = 0ull;
+        if (p.aticket) {
+            const size_t nt = (size_t)p.T.L * B * p.T.nkv;
+            for (size_t i = (size_t)blockIdx.x * NTHREADS + threadIdx.x; i < nt; i += (size_t)gridDim.x * NTHREADS)
+                p.aticket[(parity ^ 1u) * nt + i] = 0u;
+        }
         if (wave >= NCW) loader(pp, epoch, wave - NCW);
         else compute(pp, epoch, wave);
     }
@@ -2055,10 +2095,13 @@ __global__ void __launch_bounds__(256) repack_tiles_kernel(const TileOp* ops, co
             const uint32_t b = e / 64, l = e % 64;
             row = (b / nkb) * 16 + l % 16;
             col = (b % nkb) * 32 + (l / 16) * 8;
-        } else if (op.blocked == 2) {  // k-step major: page = (k-step of 16 column blocks, row group)
-            const uint32_t b = e / 64, l = e % 64, pg = b / 16, nrg = op.rows / 16;
-            row = (pg % nrg) * 16 + l % 16;
-            col = ((pg / nrg) * 16 + b % 16) * 32 + (l / 16) * 8;
+        } else if (op.blocked == 2) {  // chunks of row groups, each k-step major
+            const uint32_t b = e / 64, l = e % 64, pg = b / 16;
+            const uint32_t cg = op.chunk_rows / 16, ppr = nkb / 16;  // row groups per chunk, pages per row group
+            const uint32_t ch = pg / (cg * ppr), pl = pg % (cg * ppr);
+            const uint32_t nrg = min(cg, op.rows / 16 - ch * cg);
+            row = (ch * cg + pl % nrg) * 16 + l % 16;
+            col = ((pl / nrg) * 16 + b % 16) * 32 + (l / 16) * 8;
         } else {
             row = e / (op.kt / 8);
             col = (e % (op.kt / 8)) * 8;

@@ -171,6 +171,10 @@ mk_status repack(mk_handle* h, const mk_model_desc* d, uint8_t* wd) {
         // matrix-core blocks for 128 <= K <= 2048; with several sequences and K >= 512
         // the pages go k-step major (the batched GEMV keeps 4 column blocks of operands)
         t.blocked = kt > 2048 ? 0u : (T.B > 1 && kt >= 512 ? 2u : 1u);
+        // batches: chunks of whole row groups within the row-result bound (one chunk
+        // except for LM-head tiles)
+        t.chunk_rows = (uint32_t)(MAX_TILE_ROWS / T.B / 64 * 64);
+        t.pad_ = 0;
         tiles.push_back(t);
     }
     CopyOp* dops = nullptr;
@@ -201,7 +205,7 @@ mk_status rearm(mk_handle* h) {
     st[ST_EPOCH] = 1;
     HIPCHK(hipMemcpy(p.state, st.data(), ST_WORDS * 4, hipMemcpyHostToDevice));
     HIPCHK(hipMemset(p.acc, 0, h->acc_bytes));
-    if (p.aticket) HIPCHK(hipMemset(p.aticket, 0, (size_t)T.L * T.B * T.nkv * 4));
+    if (p.aticket) HIPCHK(hipMemset(p.aticket, 0, (size_t)2 * T.L * T.B * T.nkv * 4));
     HIPCHK(hipMemset(p.key, 0, sizeof(unsigned long long) * 2 * T.B));
     HIPCHK(hipMemset(p.ticket, 0, 4 * T.B));
     HIPCHK(hipDeviceSynchronize());
@@ -333,7 +337,7 @@ mk_status mk_build_graph(const mk_model_desc* desc, int32_t batch, int32_t max_c
         // sequences per column (columns of absent sequences stay zero for the handle's life)
         const size_t xop_elems = ((size_t)T.L * T.nq * T.d + (size_t)T.L * T.f) * 32;
         ALLOC(p.xop, xop_elems * 2, true);
-        ALLOC(p.aticket, (size_t)T.L * T.B * T.nkv * 4, true);
+        ALLOC(p.aticket, (size_t)2 * T.L * T.B * T.nkv * 4, true);
     }
     ALLOC(p.hidden, (size_t)T.B * T.h * 4, true);
     ALLOC(p.key, sizeof(unsigned long long) * 2 * T.B, true);

@@ -48,7 +48,7 @@ struct Params {
     // matrix-core B operands, bf16 parts hi/lo of 16 x 32 column blocks (lane l:
     // sequence l % 16, columns 8 (l / 16) .. +7)
     uint16_t* xop;            // [L][2][nq*d/32][64][8] (merged attention), then [L][2][f/32][64][8] (SiLU(gate) * up)
-    uint32_t* aticket;        // batch > 1: [L][B][n_kv] finished attention chunks (the last one merges)
+    uint32_t* aticket;        // batch > 1: [2][L][B][n_kv] finished attention partials per step parity
     float* hidden;            // [B][h]
     unsigned long long* key;  // [2][B] packed argmax keys
     uint32_t* ticket;         // [B]
@@ -77,11 +77,13 @@ hipError_t launch_repack(const CopyOp* ops, uint32_t n_ops, uint8_t* dst, hipStr
 // dst + dst_off either row by row (blocked = 0) or as 16 x 32 matrix-core blocks
 // (blocked = 1; block b = (row group b / (kt/32), column block b % (kt/32)),
 // lane l of a block holds row 16*rg + l%16, columns 32*kb + 8*(l/16) .. +7), or
-// k-step major (blocked = 2; page p of 16 blocks = (k-step p / nrg, row group
-// p % nrg) with nrg = rows/16, its block j is column block 16 * k-step + j).
+// k-step major (blocked = 2): the rows go in chunks of chunk_rows (the last one
+// shorter), and page p of a chunk with nrg row groups holds row group p % nrg,
+// column blocks 16 (p / nrg) .. +15.
 struct TileOp {
     uint64_t dst_off;
     uint32_t row_base, rows, kt, blocked;
+    uint32_t chunk_rows, pad_;
 };
 hipError_t launch_repack_tiles(const TileOp* ops, uint32_t n_ops, const uint8_t* const* rowsrc, uint8_t* dst,
                                hipStream_t stream);
