@@ -69,9 +69,10 @@ int plan_tiling(const Dims& dm, int B, int C, int W, const PlanOptions& o, Tilin
     int S = o.attn_splits;
     if (S <= 0) {
         // batch 1: 256-position chunks of the one context; batch > 1: slots of
-        // ceil(C / S) positions (about 512), equal work whatever the context mix
-        const int64_t span = B == 1 ? 256 : 512;
-        S = (int)std::max<int64_t>(1, std::min<int64_t>(16, (C + span - 1) / span));
+        // ceil(C / S) >= 1024 positions (fewer, longer attention tasks: each one
+        // carries a fixed cost of a few microseconds)
+        S = B == 1 ? (int)std::max<int64_t>(1, std::min<int64_t>(16, (C + 255) / 256))
+                   : (int)std::max<int64_t>(1, std::min<int64_t>(16, C / 1024));
     }
     if (S > C) S = C;
     T.attn_splits = S;

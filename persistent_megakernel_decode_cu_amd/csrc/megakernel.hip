@@ -948,7 +948,7 @@ __device__ __forceinline__ void load_residual(CParams& p, const Task& k, int idx
 // (columns = sequences) by their producers, with device-scope stores, and read with
 // device-scope loads by every tile that consumes them.  Each fp32 input is carried as
 // two bf16 parts, hi = its truncation to bf16 and lo = the remainder rounded to bf16,
-// so hi + lo is within 2^-17 of it (relative); both parts go through the same weights.
+// so hi + lo is within 2^-16 of it (relative); both parts go through the same weights.
 
 constexpr int NPART = 2;
 constexpr int OPS_PER_COL = NPART * MAX_BATCH;  // bf16 elements per column of an operand region
@@ -964,10 +964,13 @@ __device__ __forceinline__ uint16_t* opr_m(CParams& p, int l) {
 __device__ __forceinline__ uint32_t opr_index(int nkb, int part, int c, int b) {
     return ((uint32_t)(part * nkb + (c >> 5)) * 64u + (uint32_t)(((c & 31) >> 3) * 16 + b)) * 8u + (uint32_t)(c & 7);
 }
+// hi = v truncated to bf16; lo = the (exact) remainder rounded to nearest even bf16,
+// branch-free (the remainder of a finite input is finite)
 __device__ __forceinline__ void split2(float v, uint32_t& hi, uint32_t& lo) {
     const uint32_t uh = __float_as_uint(v) & 0xffff0000u;
+    const uint32_t r = __float_as_uint(v - __uint_as_float(uh));
     hi = uh >> 16;
-    lo = f2bf16(v - __uint_as_float(uh));
+    lo = (r + 0x7fffu + ((r >> 16) & 1u)) >> 16;
 }
 // the parts of 8 consecutive inputs as two B-operand registers (hi, lo)
 __device__ __forceinline__ void split8(const float* v, u32x4v& hi, u32x4v& lo) {
@@ -1556,9 +1559,10 @@ __device__ __noinline__ bool op_lmhead(const Params* pp, uint32_t slot_, uint32_
 // Inputs of the normalised GEMVs: the fp32 residual rows of the sequences (or their
 // bf16 embedding rows) for this wave's column blocks 4 i + wave, lane (kq = lane / 16,
 // sequence n = lane % 16) holding columns 8 kq .. 8 kq + 7 of each block; rows past
-// the batch read zeros (offsets outside the buffer range).
+// the batch read zeros (offsets outside the buffer range).  The 8 fp32 values of block
+// i land in bo[i] as raw bits, to be turned into the block's operands in place.
 template <int NBW>
-__device__ __forceinline__ void load_rows(float (*v)[8], __amdgpu_buffer_rsrc_t r, bool emb, uint32_t row_ofs,
+__device__ __forceinline__ void load_rows(u32x4v (*bo)[NPART], __amdgpu_buffer_rsrc_t r, bool emb, uint32_t row_ofs,
                                           int wave, int lane) {
     const int kq = lane / 16;
 #pragma unroll
@@ -1566,36 +1570,29 @@ __device__ __forceinline__ void load_rows(float (*v)[8], __amdgpu_buffer_rsrc_t 
         const uint32_t col = (uint32_t)(32 * (4 * i + wave) + 8 * kq);
         if (emb) {
             const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(r, (row_ofs + col) * 2, 0, 0);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                v[i][2 * e] = bf16lo(w[e]);
-                v[i][2 * e + 1] = bf16hi(w[e]);
-            }
+            bo[i][0] = u32x4v{w[0] << 16, w[0] & 0xffff0000u, w[1] << 16, w[1] & 0xffff0000u};
+            bo[i][1] = u32x4v{w[2] << 16, w[2] & 0xffff0000u, w[3] << 16, w[3] & 0xffff0000u};
         } else {
-            const u32x4 a0 = __builtin_amdgcn_raw_buffer_load_b128(r, (row_ofs + col) * 4, 0, 16);
-            const u32x4 a1 = __builtin_amdgcn_raw_buffer_load_b128(r, (row_ofs + col) * 4 + 16, 0, 16);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                v[i][e] = __uint_as_float(a0[e]);
-                v[i][4 + e] = __uint_as_float(a1[e]);
-            }
+            bo[i][0] = __builtin_bit_cast(u32x4v, __builtin_amdgcn_raw_buffer_load_b128(r, (row_ofs + col) * 4, 0, 16));
+            bo[i][1] = __builtin_bit_cast(u32x4v, __builtin_amdgcn_raw_buffer_load_b128(r, (row_ofs + col) * 4 + 16, 0, 16));
         }
     }
 }
-// B operands of block 4 i + wave from its inputs: times the RMSNorm gains staged in
-// LDS (bf16, in S.rowres), split into two parts; the sum of squares of the unscaled
-// inputs is accumulated into ss.
-__device__ __forceinline__ void ops_of_row_block(const float* v, int i, int wave, int lane, float& ss, u32x4v* bo) {
+// Block i's inputs (raw fp32 bits in bo) times the RMSNorm gains staged in LDS (bf16,
+// in S.rowres), split into the two B-operand parts in place; the sum of squares of the
+// unscaled inputs is accumulated into ss.
+__device__ __forceinline__ void ops_of_row_block(u32x4v* bo, int i, int wave, int lane, float& ss) {
     const uint16_t* gl = (const uint16_t*)S.rowres;
     const uint4 gw = *(const uint4*)&gl[32 * (4 * i + wave) + 8 * (lane / 16)];
     const uint32_t gg[4] = {gw.x, gw.y, gw.z, gw.w};
     float x[8];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        ss = fmaf(v[2 * e], v[2 * e], ss);
-        ss = fmaf(v[2 * e + 1], v[2 * e + 1], ss);
-        x[2 * e] = v[2 * e] * bf16lo(gg[e]);
-        x[2 * e + 1] = v[2 * e + 1] * bf16hi(gg[e]);
+        const float v0 = __uint_as_float(bo[e / 2][(e % 2) * 2]), v1 = __uint_as_float(bo[e / 2][(e % 2) * 2 + 1]);
+        ss = fmaf(v0, v0, ss);
+        ss = fmaf(v1, v1, ss);
+        x[2 * e] = v0 * bf16lo(gg[e]);
+        x[2 * e + 1] = v1 * bf16hi(gg[e]);
     }
     split8(x, bo[0], bo[1]);
 }
@@ -1641,61 +1638,50 @@ __device__ __forceinline__ float rs_seq(int b, int n, float eps) {
     return 1.0f / sqrtf(ss / (float)n + eps);
 }
 
-// K >= 512: pages stored k-step major (page s * nrg + rg holds column blocks
-// 16 s .. 16 s + 15 of row group rg); K <= 256: a page holds 16 / (K / 32) whole
-// row groups.  ROWS: the B operands are made from raw inputs (v, one k-step's four
-// blocks at a time, summing squares into ss); otherwise they are bo.
-template <int KT, bool ROWS>
+// The tile's pages in the batch-1 order (row group by row group; a page holds K = 512
+// columns of one row group, or 16 / (K / 32) whole row groups for K <= 256); bo holds
+// this wave's B operands for all of K (column blocks 4 i + wave).  Row group rg's
+// products are summed over its pages in two accumulators (one per part) and stored
+// once into this wave's slice.
+template <int KT>
 __device__ __forceinline__ bool gemv_mfma_b(const Params* pp, int wave, int lane, uint32_t page0, uint32_t nrg,
-                                            const float (*v)[8], const u32x4v (*bo)[NPART], float& ss, int B,
-                                            uint32_t task) {
+                                            const u32x4v (*bo)[NPART], int B, uint32_t task) {
     static_assert(KT >= 128 && KT <= 2048, "matrix-core GEMV covers 128 <= K <= 2048");
     constexpr int NKB = KT / 32;
     float* const sl = &S.xs[wave * 1024];
+    auto mfma = [](u32x4v a, u32x4v b, f32x4v acc) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8v, a), __builtin_bit_cast(bf16x8v, b),
+                                                       acc, 0, 0, 0);
+    };
     if constexpr (NKB >= 16) {
-        constexpr int PPR = NKB / 16;
+        constexpr int PPR = NKB / 16;  // pages per row group
+        for (uint32_t rg = 0; rg < nrg; ++rg) {
+            f32x4v acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < PPR; ++s) {
-            u32x4v cur[4][NPART];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if constexpr (ROWS) {
-                    ops_of_row_block(v[4 * s + j], 4 * s + j, wave, lane, ss, cur[j]);
-                } else {
-                    cur[j][0] = bo[4 * s + j][0];
-                    cur[j][1] = bo[4 * s + j][1];
-                }
-            }
-            for (uint32_t rg = 0; rg < nrg; ++rg) {
-                const uint32_t pg = s * nrg + rg;
+            for (int s = 0; s < PPR; ++s) {
+                const uint32_t pg = rg * PPR + s;
                 if (!page_acquire(pp, page0 + pg, task)) return false;
+                if (wave == 0 && lane == 0) lds_st(S.tm[2], (uint32_t)rtc());
                 const uint32_t slot = (page0 + pg) % NPAGES;
                 u32x4v a[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) a[j] = *(const u32x4v*)&ring[slot][(4 * j + wave) * 1024 + lane * 16];
                 page_release(page0 + pg, lane);
-                f32x4v acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc = mfma_parts(a[j], cur[j], acc);
-                slice_put(sl, acc, rg, lane, B, s == 0);
+                for (int j = 0; j < 4; ++j) {
+                    acc0 = mfma(a[j], bo[4 * s + j][0], acc0);
+                    acc1 = mfma(a[j], bo[4 * s + j][1], acc1);
+                }
             }
+            slice_put(sl, acc0 + acc1, rg, lane, B, true);
         }
     } else {
         constexpr int RPG = 16 / NKB;  // row groups per page
         constexpr int BPR = 4 / RPG;   // blocks per row group and wave
         const uint32_t npages = (nrg + RPG - 1) / RPG;
-        u32x4v cur[BPR][NPART];
-#pragma unroll
-        for (int j = 0; j < BPR; ++j) {
-            if constexpr (ROWS) {
-                ops_of_row_block(v[j], j, wave, lane, ss, cur[j]);
-            } else {
-                cur[j][0] = bo[j][0];
-                cur[j][1] = bo[j][1];
-            }
-        }
         for (uint32_t pg = 0; pg < npages; ++pg) {
             if (!page_acquire(pp, page0 + pg, task)) return false;
+            if (wave == 0 && lane == 0) lds_st(S.tm[2], (uint32_t)rtc());
             const uint32_t slot = (page0 + pg) % NPAGES;
             u32x4v a[4];
 #pragma unroll
@@ -1703,10 +1689,13 @@ __device__ __forceinline__ bool gemv_mfma_b(const Params* pp, int wave, int lane
             page_release(page0 + pg, lane);
 #pragma unroll
             for (int rr = 0; rr < RPG; ++rr) {
-                f32x4v acc = {0.f, 0.f, 0.f, 0.f};
+                f32x4v acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int jj = 0; jj < BPR; ++jj) acc = mfma_parts(a[rr * BPR + jj], cur[jj], acc);
-                slice_put(sl, acc, pg * RPG + rr, lane, B, true);
+                for (int jj = 0; jj < BPR; ++jj) {
+                    acc0 = mfma(a[rr * BPR + jj], bo[jj][0], acc0);
+                    acc1 = mfma(a[rr * BPR + jj], bo[jj][1], acc1);
+                }
+                slice_put(sl, acc0 + acc1, pg * RPG + rr, lane, B, true);
             }
         }
     }
@@ -1732,8 +1721,7 @@ __device__ __noinline__ bool op_gemv_b(const Params* pp, uint32_t slot_, uint32_
     if (normed && tid * 8 < h) gpre = gld_u4(gains(p, gslot) + tid * 8);
     if (!await_inputs(pp, k, c)) return false;
     constexpr int NBW = KT / 128;
-    float v[NORMED ? NBW : 1][8];
-    u32x4v bo[NORMED ? 1 : NBW][NPART];
+    u32x4v bo[NBW][NPART];
     if constexpr (NORMED) {
         if (tid * 8 < h) *(uint4*)&((uint16_t*)S.rowres)[tid * 8] = gpre;
         const int n = lane % 16;
@@ -1748,8 +1736,14 @@ __device__ __noinline__ bool op_gemv_b(const Params* pp, uint32_t slot_, uint32_
             r = dev_rsrc(acc_buf(p, c.parity, src, 0), (uint32_t)(B * h * 4));
             row_ofs = (uint32_t)(n * h);  // sequences past B read zeros (out of the buffer's range)
         }
-        load_rows<NBW>(v, r, emb, row_ofs, wave, lane);
+        load_rows<NBW>(bo, r, emb, row_ofs, wave, lane);
         if (!cbarrier(pp, c, k.id)) return false;  // gains staged
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < NBW; ++i) ops_of_row_block(bo[i], i, wave, lane, ss);
+        ss += __shfl_xor(ss, 16, 64);
+        ss += __shfl_xor(ss, 32, 64);
+        if (lane < MAX_BATCH) S.ssqb[wave][lane] = ss;
     } else {
         const uint16_t* R = k.op == OP_OPROJ ? opr_attn(p, l) : opr_m(p, l);
         const int nkb_total = k.op == OP_OPROJ ? p.T.nq * D / 32 : p.T.f / 32;
@@ -1787,17 +1781,7 @@ __device__ __noinline__ bool op_gemv_b(const Params* pp, uint32_t slot_, uint32_
         const uint32_t nrg = (uint32_t)min(CR, rows_pad - c0) / 16;
         const uint32_t pbase = page0 + (NKB >= 16 ? (uint32_t)(c0 / 16) * (NKB / 16) : (uint32_t)(c0 / 16) / (16 / NKB));
         if (c0 > 0 && !cbarrier(pp, c, k.id)) return false;  // the previous chunk's results are consumed
-        float ss = 0.f;
-        if constexpr (NORMED) {
-            if (!gemv_mfma_b<KT, true>(pp, wave, lane, pbase, nrg, v, bo, ss, B, k.id)) return false;
-            if (c0 == 0) {
-                ss += __shfl_xor(ss, 16, 64);
-                ss += __shfl_xor(ss, 32, 64);
-                if (lane < MAX_BATCH) S.ssqb[wave][lane] = ss;
-            }
-        } else {
-            if (!gemv_mfma_b<KT, false>(pp, wave, lane, pbase, nrg, v, bo, ss, B, k.id)) return false;
-        }
+        if (!gemv_mfma_b<KT>(pp, wave, lane, pbase, nrg, bo, B, k.id)) return false;
         if (!cbarrier(pp, c, k.id)) return false;
         if (k.op == OP_LMHEAD) {  // logits of the chunk, running argmax per sequence
             float* logits = S.args.logits;
@@ -2091,17 +2075,10 @@ __global__ void __launch_bounds__(256) repack_tiles_kernel(const TileOp* ops, co
     const uint32_t nkb = op.kt / 32;
     for (uint32_t e = threadIdx.x; e < n16; e += 256) {
         uint32_t row, col;
-        if (op.blocked == 1) {  // row-group major: block b = (row group, column block)
+        if (op.blocked) {  // row-group major: block b = (row group, column block)
             const uint32_t b = e / 64, l = e % 64;
             row = (b / nkb) * 16 + l % 16;
             col = (b % nkb) * 32 + (l / 16) * 8;
-        } else if (op.blocked == 2) {  // chunks of row groups, each k-step major
-            const uint32_t b = e / 64, l = e % 64, pg = b / 16;
-            const uint32_t cg = op.chunk_rows / 16, ppr = nkb / 16;  // row groups per chunk, pages per row group
-            const uint32_t ch = pg / (cg * ppr), pl = pg % (cg * ppr);
-            const uint32_t nrg = min(cg, op.rows / 16 - ch * cg);
-            row = (ch * cg + pl % nrg) * 16 + l % 16;
-            col = ((pl / nrg) * 16 + b % 16) * 32 + (l / 16) * 8;
         } else {
             row = e / (op.kt / 8);
             col = (e % (op.kt / 8)) * 8;

@@ -96,8 +96,7 @@ mk_status plan(const mk_model_desc* desc, int32_t batch, int32_t max_ctx, const 
 // Copy the caller's weights into the packed layout: gains and embedding row by
 // row (CopyOp), then every GEMV tile in task order (TileOp): rows of the tile
 // come from a host-built table of row addresses (null = a zero row of padding),
-// and tiles with 128 <= K <= 2048 are stored as 16 x 32 matrix-core blocks
-// (row-group major, or k-step major for batched tiles with K >= 512).
+// and tiles with 128 <= K <= 2048 are stored as 16 x 32 matrix-core blocks.
 mk_status repack(mk_handle* h, const mk_model_desc* d, uint8_t* wd) {
     const Tiling& T = h->g.T;
     const Layout& Ly = h->g.lay;
@@ -168,13 +167,7 @@ mk_status repack(mk_handle* h, const mk_model_desc* d, uint8_t* wd) {
         t.kt = kt;
         t.rows = (uint32_t)(k.wbytes / (kt * 2));
         while (rows.size() < (size_t)t.row_base + t.rows) rows.push_back(nullptr);
-        // matrix-core blocks for 128 <= K <= 2048; with several sequences and K >= 512
-        // the pages go k-step major (the batched GEMV keeps 4 column blocks of operands)
-        t.blocked = kt > 2048 ? 0u : (T.B > 1 && kt >= 512 ? 2u : 1u);
-        // batches: chunks of whole row groups within the row-result bound (one chunk
-        // except for LM-head tiles)
-        t.chunk_rows = (uint32_t)(MAX_TILE_ROWS / T.B / 64 * 64);
-        t.pad_ = 0;
+        t.blocked = kt <= 2048 ? 1u : 0u;
         tiles.push_back(t);
     }
     CopyOp* dops = nullptr;

@@ -76,14 +76,10 @@ hipError_t launch_repack(const CopyOp* ops, uint32_t n_ops, uint8_t* dst, hipStr
 // bf16 columns, row r read from rowsrc[row_base + r] (null: zeros), written to
 // dst + dst_off either row by row (blocked = 0) or as 16 x 32 matrix-core blocks
 // (blocked = 1; block b = (row group b / (kt/32), column block b % (kt/32)),
-// lane l of a block holds row 16*rg + l%16, columns 32*kb + 8*(l/16) .. +7), or
-// k-step major (blocked = 2): the rows go in chunks of chunk_rows (the last one
-// shorter), and page p of a chunk with nrg row groups holds row group p % nrg,
-// column blocks 16 (p / nrg) .. +15.
+// lane l of a block holds row 16*rg + l%16, columns 32*kb + 8*(l/16) .. +7).
 struct TileOp {
     uint64_t dst_off;
     uint32_t row_base, rows, kt, blocked;
-    uint32_t chunk_rows, pad_;
 };
 hipError_t launch_repack_tiles(const TileOp* ops, uint32_t n_ops, const uint8_t* const* rowsrc, uint8_t* dst,
                                hipStream_t stream);

@@ -17,7 +17,7 @@ LLAMA_1B = synth.configs.LLAMA_1B
 
 
 # The batched projections carry each fp32 input as two bf16 parts (hi + lo within
-# 2^-17 of it), so a projected value is off by up to about 2^-17 * sum_i |w_i x_i|
+# 2^-16 of it), so a projected value is off by up to about 2^-16 * sum_i |w_i x_i|
 # before its bf16 rounding; for these random weights that sum is at most a few tens
 # of times the largest |value| of the head vector.  Allowed: one bf16 ulp of the
 # oracle's value plus 2^-10 of the head vector's largest magnitude.
@@ -79,6 +79,14 @@ def test_tiny_batch_one_step(B):
 @pytest.mark.parametrize("W", [1, 5, 37])
 def test_tiny_batch_few_workgroups(W):
     _one_step(TINY, 4, 256, [3, 200, 64, 255], n_workgroups=W)
+
+
+@pytest.mark.parametrize("splits", [3, 7])
+def test_tiny_batch_attention_chunk_slots(splits):
+    # fixed-length chunk slots of ceil(512 / splits) positions: short contexts leave
+    # empty slots, long ones fill several; the last partial of each (sequence, group)
+    # merges the non-empty ones
+    _one_step(TINY, 5, 512, [0, 72, 73, 300, 511], attn_splits=splits)
 
 
 def test_tiny_batch_dynamic_queue():
