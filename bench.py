@@ -55,6 +55,45 @@ def measured_traffic():
     return int(rec["traffic_bytes_per_launch"])
 
 
+TRAFFIC_SOURCES = ["persistent_megakernel_decode_cu_amd/csrc/megakernel.hip",
+                   "persistent_megakernel_decode_cu_amd/csrc/graph.cpp"]
+
+
+def traffic_from_counters(fetch_csv, write_csv, kernel="mk::mk_step_kernel", copy_bytes=256 << 20):
+    """HBM bytes per launch of `kernel` from two rocprofv3 --pmc runs of this bench with
+    --copy-calibration (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each scaled by what the
+    same counter reads for the plain device copy of copy_bytes (its three largest dispatches)."""
+    import csv
+    import hashlib
+
+    def read(path, counter):
+        mk_vals, copy_vals = [], []
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                v = float(r["Counter_Value"])
+                if r["Kernel_Name"].startswith(kernel):
+                    mk_vals.append(v)
+                elif "copyBuffer" in r["Kernel_Name"]:
+                    copy_vals.append(v)
+        copy_vals = sorted(copy_vals)[-3:]
+        return float(np.median(mk_vals)), float(np.median(copy_vals)), len(mk_vals)
+
+    f_mk, f_copy, n = read(fetch_csv, "FETCH_SIZE")
+    w_mk, w_copy, _ = read(write_csv, "WRITE_SIZE")
+    fs, ws = (copy_bytes / 1024) / f_copy, (copy_bytes / 1024) / w_copy
+    src = b"".join(open(os.path.join(ROOT, f), "rb").read() for f in TRAFFIC_SOURCES)
+    rd, wr = int(f_mk * 1024 * fs), int(w_mk * 1024 * ws)
+    return {"kernel": kernel, "workload": "llama-3.2-1b-shape, batch 1, decode from position 1024, max_ctx 2048",
+            "source_sha256": hashlib.sha256(src).hexdigest(), "source_files": TRAFFIC_SOURCES,
+            "fetch_size_kib_median": f_mk, "write_size_kib_median": w_mk, "copy_bytes": copy_bytes,
+            "copy_fetch_size_kib": f_copy, "copy_write_size_kib": w_copy,
+            "fetch_scale": round(fs, 4), "write_scale": round(ws, 4),
+            "hbm_read_bytes_per_launch": rd, "hbm_write_bytes_per_launch": wr,
+            "traffic_bytes_per_launch": rd + wr, "launches": n}
+
+
 def cpu_baseline(cfg, w, kc, vc, tok, P0, budget_s=10.0):
     """The oracle (plain C, double precision, OpenMP over output rows) on the same inputs."""
     import oracle
@@ -218,7 +257,15 @@ def main():
     ap.add_argument("--batch", type=int, default=1,
                     help="sequences per step; above 1: the mixed-context batch workload (contexts uniform in "
                          "[256, 4096], room for 4352), reported in tokens/s")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the measured-traffic record from two rocprofv3 counter-collection CSVs and exit")
     args = ap.parse_args()
+    if args.traffic_from:
+        rec = traffic_from_counters(*args.traffic_from)
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(rec, f, indent=1)
+        print(json.dumps(rec))
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; multi-GPU runs are not part of this "
