@@ -90,9 +90,12 @@ typedef struct {
 /* Validates the description, copies the weights into a handle-owned packed
  * layout (the caller may free its copies afterwards), builds the task graph,
  * the event targets and the queues, and uploads them to the current device.
- * batch >= 1 sequences; max_ctx >= 1 positions per sequence in the KV cache.
- * Errors: MK_E_INVALID (NULL pointers, unsupported shapes), MK_E_NO_DEVICE,
- * MK_E_NOMEM, MK_E_HIP.  On success *out receives the handle. */
+ * 1 <= batch <= 32 sequences (batch > 1 also needs hidden <= 2048; the
+ * projections of up to 16 sequences share one pass over the weights, so
+ * 17..32 sequences take two); max_ctx >= 1 positions per sequence in the KV
+ * cache.  Errors: MK_E_INVALID (NULL pointers, unsupported shapes),
+ * MK_E_UNSUPPORTED (batch > 32, batch > 1 with hidden > 2048, MoE),
+ * MK_E_NO_DEVICE, MK_E_NOMEM, MK_E_HIP.  On success *out receives the handle. */
 mk_status mk_build_graph(const mk_model_desc *desc, int32_t batch, int32_t max_ctx, const mk_options *opt,
                          mk_handle **out);
 

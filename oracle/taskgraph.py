@@ -27,15 +27,18 @@ The tiling rules (written from the design, not from the C++ code):
     last chunk task of a (sequence, KV group) to finish merges the chunks for
     the O-projection, which therefore waits on the same event as at batch 1.
   * O-proj tiles: (KV group g, row block) over columns g*grp*d .. +grp*d, with
-    o_rows = min(h, 1024 // B, max(16, pow2_floor(h * n_kv / W))).
+    o_rows = min(h, 1024 // min(B, 16), max(16, pow2_floor(h * n_kv / W))).
   * down tiles: (K block of kd = min(1024, f) columns, row block of
-    d_rows = min(h, 1024 // B, max(16, pow2_floor(h * (f / kd) / W))) rows).
+    d_rows = min(h, 1024 // min(B, 16), max(16, pow2_floor(h * (f / kd) / W))) rows).
   * gate/up tiles: g_rows gate rows then the same g_rows up rows, with
-    g_rows = min(kd, (1024 // B) // 2, max(8, pow2_ceil(ceil(f / W)))).
+    g_rows = min(kd, (1024 // min(B, 16)) // 2, max(8, pow2_ceil(ceil(f / W)))).
   * LM head tiles: lm_rows = min(1024, ceil(V / W) rounded up to 16) rows, the
     last one shorter; its weight bytes are its rows rounded up to 16.  (With
     several sequences a workgroup takes an LM tile in chunks of
     (1024 // B) // 64 * 64 rows, so its row results stay within 1024 values.)
+  * with more than 16 sequences every GEMV tile (QKV, O-proj, gate/up, down,
+    LM head) is emitted once per column group of 16 sequences (task field seq =
+    the group), group by group within each op, on the same weights.
   * per layer the events are created in the order qkv[g], attn[g], xb, m[kb],
     x_next; tasks in the order QKV, attention, O-proj, gate/up, down; then the
     LM-head tiles.  An event with more than 32 producers uses 8 sub-counters.
@@ -95,7 +98,7 @@ def tiling(cfg, B, C, W, attn_splits=0):
         S = max(1, min(16, -(-C // 256))) if B == 1 else max(1, min(16, C // 1024))
     S = min(S, C)
     kd = min(1024, f)
-    max_rows = 1024 // B  # rows x sequences of a tile
+    max_rows = 1024 // min(B, 16)  # rows x sequences (of one column group) of a tile
     return dict(grp=grp, pairs=8, S=S,
                 o_rows=min(h, max_rows, max(16, _pow2_floor(h * nkv // W))),
                 kd=kd, d_rows=min(h, max_rows, max(16, _pow2_floor(h * (f // kd) // W))),
@@ -135,6 +138,7 @@ def build(cfg, B, C, W, policy=0, attn_splits=0):
     h, nq, nkv, d, f, L = cfg.hidden, cfg.n_q, cfg.n_kv, cfg.head_dim, cfg.ffn, cfg.n_layers
     grp, P, S = t["grp"], t["pairs"], t["S"]
     n_kb = f // t["kd"]
+    n_sg = -(-B // 16)  # column groups of 16 sequences
     tasks, target = [], []
 
     def event():
@@ -158,40 +162,45 @@ def build(cfg, B, C, W, policy=0, attn_splits=0):
         ev_xb = event()
         ev_m = [event() for _ in range(n_kb)]
         ev_next = event()
-        tile = 0
         wb = 2 * P * h * 2
-        for g in range(nkv):
-            heads = [g * grp + s for s in range(grp)] + [nq + g, nq + nkv + g]
-            for slot in heads:
-                for pb in range(d // 2 // P):
-                    task(op=OP_QKV, layer=l, part=slot, row0=pb * P, nrows=P, wait_ev=ev_x, sig_ev=ev_qkv[g],
-                         wbytes=wb, wofs=base + lay["qkv"] + tile * wb)
-                    tile += 1
+        for sg in range(n_sg):
+            tile = 0
+            for g in range(nkv):
+                heads = [g * grp + s for s in range(grp)] + [nq + g, nq + nkv + g]
+                for slot in heads:
+                    for pb in range(d // 2 // P):
+                        task(op=OP_QKV, layer=l, part=slot, row0=pb * P, nrows=P, seq=sg, wait_ev=ev_x,
+                             sig_ev=ev_qkv[g], wbytes=wb, wofs=base + lay["qkv"] + tile * wb)
+                        tile += 1
         for b in range(B):
             for g in range(nkv):
                 for c in range(S):
                     task(op=OP_ATTN, layer=l, part=g, row0=c, nrows=grp, seq=b, wait_ev=ev_qkv[g], sig_ev=ev_attn[g])
         wb = t["o_rows"] * grp * d * 2
-        for g in range(nkv):
-            for rb in range(h // t["o_rows"]):
-                task(op=OP_OPROJ, layer=l, part=g, row0=rb * t["o_rows"], nrows=t["o_rows"],
-                     flags=TF_RESID if g == 0 else 0, wait_ev=ev_attn[g], sig_ev=ev_xb, wbytes=wb,
-                     wofs=base + lay["o"] + (g * (h // t["o_rows"]) + rb) * wb)
+        for sg in range(n_sg):
+            for g in range(nkv):
+                for rb in range(h // t["o_rows"]):
+                    task(op=OP_OPROJ, layer=l, part=g, row0=rb * t["o_rows"], nrows=t["o_rows"], seq=sg,
+                         flags=TF_RESID if g == 0 else 0, wait_ev=ev_attn[g], sig_ev=ev_xb, wbytes=wb,
+                         wofs=base + lay["o"] + (g * (h // t["o_rows"]) + rb) * wb)
         wb = 2 * t["g_rows"] * h * 2
-        for i in range(f // t["g_rows"]):
-            task(op=OP_GATEUP, layer=l, row0=i * t["g_rows"], nrows=t["g_rows"], wait_ev=ev_xb,
-                 sig_ev=ev_m[i * t["g_rows"] // t["kd"]], wbytes=wb, wofs=base + lay["gu"] + i * wb)
+        for sg in range(n_sg):
+            for i in range(f // t["g_rows"]):
+                task(op=OP_GATEUP, layer=l, row0=i * t["g_rows"], nrows=t["g_rows"], seq=sg, wait_ev=ev_xb,
+                     sig_ev=ev_m[i * t["g_rows"] // t["kd"]], wbytes=wb, wofs=base + lay["gu"] + i * wb)
         wb = t["d_rows"] * t["kd"] * 2
-        for kb in range(n_kb):
-            for rb in range(h // t["d_rows"]):
-                task(op=OP_DOWN, layer=l, part=kb, row0=rb * t["d_rows"], nrows=t["d_rows"],
-                     flags=TF_RESID if kb == 0 else 0, wait_ev=ev_m[kb], sig_ev=ev_next, wbytes=wb,
-                     wofs=base + lay["down"] + (kb * (h // t["d_rows"]) + rb) * wb)
+        for sg in range(n_sg):
+            for kb in range(n_kb):
+                for rb in range(h // t["d_rows"]):
+                    task(op=OP_DOWN, layer=l, part=kb, row0=rb * t["d_rows"], nrows=t["d_rows"], seq=sg,
+                         flags=TF_RESID if kb == 0 else 0, wait_ev=ev_m[kb], sig_ev=ev_next, wbytes=wb,
+                         wofs=base + lay["down"] + (kb * (h // t["d_rows"]) + rb) * wb)
         ev_x = ev_next
-    for i in range(n_lm):
-        rows = min(t["lm_rows"], cfg.vocab - i * t["lm_rows"])
-        task(op=OP_LMHEAD, layer=L, row0=i * t["lm_rows"], nrows=rows, wait_ev=ev_x, wbytes=_round16(rows) * h * 2,
-             wofs=lay["lm"] + i * t["lm_rows"] * h * 2)
+    for sg in range(n_sg):
+        for i in range(n_lm):
+            rows = min(t["lm_rows"], cfg.vocab - i * t["lm_rows"])
+            task(op=OP_LMHEAD, layer=L, row0=i * t["lm_rows"], nrows=rows, seq=sg, wait_ev=ev_x,
+                 wbytes=_round16(rows) * h * 2, wofs=lay["lm"] + i * t["lm_rows"] * h * 2)
     nsub = [8 if n > 32 else 1 for n in target]
     for k in tasks:
         k["wait_target"] = target[k["wait_ev"]] if k["wait_ev"] != NONE else 0
@@ -222,6 +231,7 @@ def check(g, cfg, B):
             consumers.setdefault(k["wait_ev"], []).append(k["id"])
     h, nq, nkv, d, f, L, V = cfg.hidden, cfg.n_q, cfg.n_kv, cfg.head_dim, cfg.ffn, cfg.n_layers, cfg.vocab
     grp = nq // nkv
+    n_sg = -(-B // 16)
     # G2 targets = producers
     prod = [0] * len(target)
     for k in tasks:
@@ -234,26 +244,27 @@ def check(g, cfg, B):
     # G1 coverage
     for l in range(L):
         lt = [k for k in tasks if k["layer"] == l]
-        cov = np.zeros((nq + 2 * nkv, d // 2), int)
+        # every GEMV output is produced exactly once per column group of 16 sequences
+        cov = np.zeros((n_sg, nq + 2 * nkv, d // 2), int)
         for k in lt:
             if k["op"] == OP_QKV:
-                cov[k["part"], k["row0"]:k["row0"] + k["nrows"]] += 1
+                cov[k["seq"], k["part"], k["row0"]:k["row0"] + k["nrows"]] += 1
         assert (cov == 1).all(), "QKV pairs not covered exactly once"
-        o = np.zeros((h, nkv), int)
+        o = np.zeros((n_sg, h, nkv), int)
         for k in lt:
             if k["op"] == OP_OPROJ:
-                o[k["row0"]:k["row0"] + k["nrows"], k["part"]] += 1
+                o[k["seq"], k["row0"]:k["row0"] + k["nrows"], k["part"]] += 1
         assert (o == 1).all(), "O-proj (row, group) not covered exactly once"
-        gu = np.zeros(f, int)
+        gu = np.zeros((n_sg, f), int)
         for k in lt:
             if k["op"] == OP_GATEUP:
-                gu[k["row0"]:k["row0"] + k["nrows"]] += 1
+                gu[k["seq"], k["row0"]:k["row0"] + k["nrows"]] += 1
         assert (gu == 1).all(), "gate/up rows not covered exactly once"
         kd = g["tiling"]["kd"]
-        dn = np.zeros((h, f // kd), int)
+        dn = np.zeros((n_sg, h, f // kd), int)
         for k in lt:
             if k["op"] == OP_DOWN:
-                dn[k["row0"]:k["row0"] + k["nrows"], k["part"]] += 1
+                dn[k["seq"], k["row0"]:k["row0"] + k["nrows"], k["part"]] += 1
         assert (dn == 1).all(), "down (row, K block) not covered exactly once"
         at = np.zeros((B, nkv, g["tiling"]["S"]), int)
         for k in lt:
@@ -261,18 +272,18 @@ def check(g, cfg, B):
                 at[k["seq"], k["part"], k["row0"]] += 1
         assert (at == 1).all(), "attention chunks not covered exactly once"
         # exactly one residual-adding tile per O-proj / down row
-        r1 = np.zeros(h, int)
-        r2 = np.zeros(h, int)
+        r1 = np.zeros((n_sg, h), int)
+        r2 = np.zeros((n_sg, h), int)
         for k in lt:
             if k["op"] == OP_OPROJ and k["flags"] & TF_RESID:
-                r1[k["row0"]:k["row0"] + k["nrows"]] += 1
+                r1[k["seq"], k["row0"]:k["row0"] + k["nrows"]] += 1
             if k["op"] == OP_DOWN and k["flags"] & TF_RESID:
-                r2[k["row0"]:k["row0"] + k["nrows"]] += 1
+                r2[k["seq"], k["row0"]:k["row0"] + k["nrows"]] += 1
         assert (r1 == 1).all() and (r2 == 1).all(), "residual added more or less than once"
-    lm = np.zeros(V, int)
+    lm = np.zeros((n_sg, V), int)
     for k in tasks:
         if k["op"] == OP_LMHEAD:
-            lm[k["row0"]:k["row0"] + k["nrows"]] += 1
+            lm[k["seq"], k["row0"]:k["row0"] + k["nrows"]] += 1
     assert (lm == 1).all(), "LM-head rows not covered exactly once"
     # G3 soundness: every reader starts after every writer of what it reads, through the event edges
     hb_sets = ancestor_sets(g)
@@ -335,6 +346,13 @@ def check(g, cfg, B):
     lay = g.get("layout")
     if lay is None:
         return
+    # (the tiles of column groups past the first read the first group's tiles)
+    first = {(k["op"], k["layer"], k["part"], k["row0"]): (k["wofs"], k["wbytes"]) for k in tasks if k["seq"] == 0}
+    for k in tasks:
+        if k["wbytes"] and k["op"] != OP_ATTN and k["seq"] > 0:
+            assert first[(k["op"], k["layer"], k["part"], k["row0"])] == (k["wofs"], k["wbytes"]), \
+                "a column group's tile reads other weights than the first group's"
+    tasks = [k for k in tasks if k["op"] == OP_ATTN or k["seq"] == 0]
     spans = sorted((k["wofs"], k["wbytes"], k["op"]) for k in tasks if k["wbytes"] and k["op"] != OP_LMHEAD)
     pos = lay["layer0"]
     for ofs, nb, op in spans:

@@ -52,7 +52,7 @@ int plan_tiling(const Dims& dm, int B, int C, int W, const PlanOptions& o, Tilin
     if (dm.d != 64 && dm.d != 128) return fail("head_dim must be 64 or 128");
     if (dm.nq % dm.nkv) return fail("n_q_heads must be a multiple of n_kv_heads");
     if (dm.n_experts != 0) return fail("mixture-of-experts FFN is not implemented by this build");
-    if (B > MAX_BATCH) return fail("batch is limited to 16 sequences per step");
+    if (B > MAX_BATCH) return fail("batch is limited to 32 sequences per step");
     if (B > 1 && dm.h > 2048) return fail("batch > 1 needs hidden <= 2048");
     if (dm.f <= 0) return fail("ffn_dim must be positive");
     if (!gemv_k_ok(dm.h) || dm.h > MAX_ACT) return fail("hidden must be a power of two in [128, 4096]");
@@ -77,8 +77,8 @@ int plan_tiling(const Dims& dm, int B, int C, int W, const PlanOptions& o, Tilin
     if (S > C) S = C;
     T.attn_splits = S;
     T.n_attn_tiles = B * dm.nkv * S;
-    // rows x sequences of a tile fit the LDS row-result buffer
-    const int64_t max_rows = MAX_TILE_ROWS / B;
+    // rows x sequences (of one column group) of a tile fit the LDS row-result buffer
+    const int64_t max_rows = MAX_TILE_ROWS / std::min<int64_t>(B, GROUP_SEQS);
     // O-proj: tiles (KV group g, rows) with K = grp*d columns; about W tiles per layer
     T.o_rows = (int)std::min<int64_t>(std::min<int64_t>(dm.h, max_rows),
                                       std::max<int64_t>(16, pow2_floor((int64_t)dm.h * dm.nkv / W)));
@@ -150,6 +150,7 @@ int build_graph(const Tiling& T, const Layout& Ly, int sched, int policy, Graph*
     const int L = T.L, grp = T.grp, half = T.d / 2;
     const int pair_blocks = half / T.qkv_pairs;
     const int n_kb = T.f / T.kd;
+    const int n_sg = (T.B + GROUP_SEQS - 1) / GROUP_SEQS;  // column groups of the batched GEMV tiles
 
     auto add = [&](Task k) {
         k.id = (uint32_t)g.tasks.size();
@@ -179,20 +180,24 @@ int build_graph(const Tiling& T, const Layout& Ly, int sched, int policy, Graph*
         const uint32_t ev_next = g.new_event();
 
         // fused RMSNorm + QKV + RoPE tiles, grouped by KV head: q heads of the group, then its k and v head
-        uint64_t tile = 0;
-        for (int gi = 0; gi < T.nkv; ++gi) {
-            for (int s = 0; s < grp + 2; ++s) {
-                int slot = s < grp ? gi * grp + s : (s == grp ? T.nq + gi : T.nq + T.nkv + gi);
-                for (int pb = 0; pb < pair_blocks; ++pb, ++tile) {
-                    Task k = blank(OP_QKV, l);
-                    k.part = (uint16_t)slot;
-                    k.row0 = (uint32_t)(pb * T.qkv_pairs);
-                    k.nrows = (uint32_t)T.qkv_pairs;
-                    k.wait_ev = ev_x;
-                    k.sig_ev = ev_qkv[gi];
-                    k.wbytes = (uint32_t)(2 * T.qkv_pairs * h * 2);
-                    k.wofs = lbase + Ly.qkv + tile * k.wbytes;
-                    add(k);
+        // (more than 16 sequences: every GEMV tile once per column group of 16, on the same weights)
+        for (int sg = 0; sg < n_sg; ++sg) {
+            uint64_t tile = 0;
+            for (int gi = 0; gi < T.nkv; ++gi) {
+                for (int s = 0; s < grp + 2; ++s) {
+                    int slot = s < grp ? gi * grp + s : (s == grp ? T.nq + gi : T.nq + T.nkv + gi);
+                    for (int pb = 0; pb < pair_blocks; ++pb, ++tile) {
+                        Task k = blank(OP_QKV, l);
+                        k.part = (uint16_t)slot;
+                        k.row0 = (uint32_t)(pb * T.qkv_pairs);
+                        k.nrows = (uint32_t)T.qkv_pairs;
+                        k.seq = (uint32_t)sg;
+                        k.wait_ev = ev_x;
+                        k.sig_ev = ev_qkv[gi];
+                        k.wbytes = (uint32_t)(2 * T.qkv_pairs * h * 2);
+                        k.wofs = lbase + Ly.qkv + tile * k.wbytes;
+                        add(k);
+                    }
                 }
             }
         }
@@ -212,12 +217,14 @@ int build_graph(const Tiling& T, const Layout& Ly, int sched, int policy, Graph*
                 }
         // O-proj K slices: tile (group, row block)
         const int o_kt = grp * T.d;
+        for (int sg = 0; sg < n_sg; ++sg)
         for (int gi = 0; gi < T.nkv; ++gi)
             for (int rb = 0; rb < T.h / T.o_rows; ++rb) {
                 Task k = blank(OP_OPROJ, l);
                 k.part = (uint16_t)gi;
                 k.row0 = (uint32_t)(rb * T.o_rows);
                 k.nrows = (uint32_t)T.o_rows;
+                k.seq = (uint32_t)sg;
                 k.flags = gi == 0 ? TF_RESID : 0;
                 k.wait_ev = ev_attn[gi];
                 k.sig_ev = ev_xb;
@@ -226,10 +233,12 @@ int build_graph(const Tiling& T, const Layout& Ly, int sched, int policy, Graph*
                 add(k);
             }
         // RMSNorm + gate/up + SiLU tiles
+        for (int sg = 0; sg < n_sg; ++sg)
         for (int t = 0; t < T.n_gu_tiles; ++t) {
             Task k = blank(OP_GATEUP, l);
             k.row0 = (uint32_t)(t * T.g_rows);
             k.nrows = (uint32_t)T.g_rows;
+            k.seq = (uint32_t)sg;
             k.wait_ev = ev_xb;
             k.sig_ev = ev_m[(t * T.g_rows) / T.kd];
             k.wbytes = (uint32_t)(2ull * T.g_rows * h * 2);
@@ -237,12 +246,14 @@ int build_graph(const Tiling& T, const Layout& Ly, int sched, int policy, Graph*
             add(k);
         }
         // down-proj K slices: tile (K block, row block)
+        for (int sg = 0; sg < n_sg; ++sg)
         for (int kb = 0; kb < n_kb; ++kb)
             for (int rb = 0; rb < T.h / T.d_rows; ++rb) {
                 Task k = blank(OP_DOWN, l);
                 k.part = (uint16_t)kb;
                 k.row0 = (uint32_t)(rb * T.d_rows);
                 k.nrows = (uint32_t)T.d_rows;
+                k.seq = (uint32_t)sg;
                 k.flags = kb == 0 ? TF_RESID : 0;
                 k.wait_ev = ev_m[kb];
                 k.sig_ev = ev_next;
@@ -253,8 +264,10 @@ int build_graph(const Tiling& T, const Layout& Ly, int sched, int policy, Graph*
         ev_x = ev_next;
     }
     // final RMSNorm + LM head + argmax
+    for (int sg = 0; sg < n_sg; ++sg)
     for (int t = 0; t < T.n_lm_tiles; ++t) {
         Task k = blank(OP_LMHEAD, L);
+        k.seq = (uint32_t)sg;
         k.row0 = (uint32_t)(t * T.lm_rows);
         k.nrows = (uint32_t)std::min<int64_t>(T.lm_rows, (int64_t)T.V - (int64_t)t * T.lm_rows);
         k.wait_ev = ev_x;

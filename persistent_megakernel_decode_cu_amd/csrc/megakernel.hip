@@ -69,7 +69,7 @@ struct __attribute__((aligned(16))) Smem {
     uint32_t go, cbar, done, abort;
     uint32_t cgen[NCW];  // compute-wave barrier generation (per wave)
     float ssq[NCW];      // per-wave partial sums of squares of the staged activation
-    float ssqb[NCW][MAX_BATCH];  // batch > 1: per-wave, per-sequence partial sums of squares
+    float ssqb[NCW][GROUP_SEQS];  // batch > 1: per-wave, per-sequence partial sums of squares
     uint32_t t_ready_lo, t_ready_hi;
     uint32_t tm[4];  // trace: low 32 bits of the clock after staging / after the GEMV
 };
@@ -951,13 +951,16 @@ __device__ __forceinline__ void load_residual(CParams& p, const Task& k, int idx
 // so hi + lo is within 2^-16 of it (relative); both parts go through the same weights.
 
 constexpr int NPART = 2;
-constexpr int OPS_PER_COL = NPART * MAX_BATCH;  // bf16 elements per column of an operand region
+constexpr int OPS_PER_COL = NPART * GROUP_SEQS;  // bf16 elements per column of an operand region
 
-__device__ __forceinline__ uint16_t* opr_attn(CParams& p, int l) {
-    return p.xop + (size_t)l * p.T.nq * p.T.d * OPS_PER_COL;
+// operand regions of layer l and column group sg (sequences 16 sg .. 16 sg + 15)
+__device__ __forceinline__ int n_col_groups(CParams& p) { return (p.T.B + GROUP_SEQS - 1) / GROUP_SEQS; }
+__device__ __forceinline__ uint16_t* opr_attn(CParams& p, int l, int sg) {
+    return p.xop + ((size_t)l * n_col_groups(p) + sg) * p.T.nq * p.T.d * OPS_PER_COL;
 }
-__device__ __forceinline__ uint16_t* opr_m(CParams& p, int l) {
-    return p.xop + ((size_t)p.T.L * p.T.nq * p.T.d + (size_t)l * p.T.f) * OPS_PER_COL;
+__device__ __forceinline__ uint16_t* opr_m(CParams& p, int l, int sg) {
+    return p.xop + ((size_t)p.T.L * n_col_groups(p) * p.T.nq * p.T.d + ((size_t)l * n_col_groups(p) + sg) * p.T.f) *
+                       OPS_PER_COL;
 }
 // element of (part, column c, sequence b) in a region of nkb 32-column blocks: block
 // (part, c / 32) holds 64 lanes x 8 elements, lane = 16 ((c % 32) / 8) + b
@@ -1008,7 +1011,7 @@ __device__ __noinline__ void merge_chunks(const Params* pp, int layer, int b, in
     const int32_t fl = attn_fixed_len(p.T.B, p.T.C, Sp);
     const int nch = min(Sp, (pos + fl) / fl);  // chunks holding at least one of the pos + 1 positions
     const uint32_t cs = (uint32_t)G * (D + 2);  // floats per chunk
-    uint16_t* R = opr_attn(p, layer);
+    uint16_t* R = opr_attn(p, layer, b / GROUP_SEQS);
     const int nkb = p.T.nq * D / 32;
     for (int idx = lane; idx < G * (D / 8); idx += 64) {
         const int head = idx / (D / 8), c8 = idx % (D / 8);
@@ -1046,7 +1049,7 @@ __device__ __noinline__ void merge_chunks(const Params* pp, int layer, int b, in
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) num[e] /= den;
-        put_op8(R, nkb, (g * G + head) * D + c8 * 8, b, num);
+        put_op8(R, nkb, (g * G + head) * D + c8 * 8, b % GROUP_SEQS, num);
     }
 }
 
@@ -1159,8 +1162,15 @@ __device__ __noinline__ bool op_attn(const Params* pp, uint32_t slot_, uint32_t 
     const bool has_cur = ch.c0 <= ch.P && ch.P < ch.c1;
     const int cl = lane % NC, pgl = lane / NC;  // P.V: dimension chunk and position group of this lane
     // an empty chunk slot (several sequences; their merge reads only the non-empty
-    // chunks): no pages, no partials.  At batch 1 every chunk writes its partials.
-    if (p.T.B > 1 && ch.c0 > ch.P) return true;
+    // chunks): no pages, no partials, no wait for the event.  It still takes the
+    // workgroup's start-of-task handshake: without it the waves that have no work
+    // would run ahead into later tasks and count their completions early.  At batch 1
+    // every chunk writes its partials.
+    if (p.T.B > 1 && ch.c0 > ch.P) {
+        Task none = k;
+        none.wait_ev = NONE;
+        return await_inputs(pp, none, c);
+    }
     if (!await_inputs(pp, k, c)) return false;
     // each wave stages the query rows of its own heads, and the current token's K/V chunk
     float kc8[8], vc8[8];
@@ -1712,7 +1722,9 @@ __device__ __noinline__ bool op_gemv_b(const Params* pp, uint32_t slot_, uint32_
     Ctx c = make_ctx(t_, epoch_);
     CParams& p = P(pp);
     const int lane = c.lane, tid = c.tid, wave = c.wave;
-    const int B = p.T.B, L = p.T.L, l = k.layer, D = p.T.d, h = p.T.h;
+    // this tile's column group: sequences gb0 .. gb0 + B - 1 of the Btot in the step
+    const int Btot = p.T.B, gb0 = (int)k.seq * GROUP_SEQS, B = min(GROUP_SEQS, Btot - gb0);
+    const int L = p.T.L, l = k.layer, D = p.T.d, h = p.T.h;
     constexpr bool normed = NORMED;  // QKV, gate/up, LM head
     // normalised inputs: gains slot and source residual (-1: the embedding)
     const int gslot = k.op == OP_QKV ? 2 * l : (k.op == OP_GATEUP ? 2 * l + 1 : 2 * L);
@@ -1731,9 +1743,9 @@ __device__ __noinline__ bool op_gemv_b(const Params* pp, uint32_t slot_, uint32_
         if (emb) {
             r = __builtin_amdgcn_make_buffer_rsrc((void*)(p.w + p.lay.embed), 0, (uint32_t)((uint64_t)p.T.V * h * 2),
                                                   RSRC_FLAGS);
-            row_ofs = n < B ? (uint32_t)S.tok[n] * (uint32_t)h : (uint32_t)p.T.V * (uint32_t)h;
+            row_ofs = n < B ? (uint32_t)S.tok[gb0 + n] * (uint32_t)h : (uint32_t)p.T.V * (uint32_t)h;
         } else {
-            r = dev_rsrc(acc_buf(p, c.parity, src, 0), (uint32_t)(B * h * 4));
+            r = dev_rsrc(acc_buf(p, c.parity, src, gb0), (uint32_t)(B * h * 4));
             row_ofs = (uint32_t)(n * h);  // sequences past B read zeros (out of the buffer's range)
         }
         load_rows<NBW>(bo, r, emb, row_ofs, wave, lane);
@@ -1743,9 +1755,9 @@ __device__ __noinline__ bool op_gemv_b(const Params* pp, uint32_t slot_, uint32_
         for (int i = 0; i < NBW; ++i) ops_of_row_block(bo[i], i, wave, lane, ss);
         ss += __shfl_xor(ss, 16, 64);
         ss += __shfl_xor(ss, 32, 64);
-        if (lane < MAX_BATCH) S.ssqb[wave][lane] = ss;
+        if (lane < GROUP_SEQS) S.ssqb[wave][lane] = ss;
     } else {
-        const uint16_t* R = k.op == OP_OPROJ ? opr_attn(p, l) : opr_m(p, l);
+        const uint16_t* R = k.op == OP_OPROJ ? opr_attn(p, l, (int)k.seq) : opr_m(p, l, (int)k.seq);
         const int nkb_total = k.op == OP_OPROJ ? p.T.nq * D / 32 : p.T.f / 32;
         const int kb_off = k.op == OP_OPROJ ? k.part * p.T.grp * D / 32 : k.part * p.T.kd / 32;
         bops_from_region<NBW>(bo, dev_rsrc(R, (uint32_t)nkb_total * NPART * 1024u), nkb_total, kb_off, wave, lane);
@@ -1761,8 +1773,8 @@ __device__ __noinline__ bool op_gemv_b(const Params* pp, uint32_t slot_, uint32_
         if (resid && idx < (int)k.nrows * B) {
             const int i = idx / B, b = idx % B, row = (int)k.row0 + i;
             const int rsrc_i = k.op == OP_DOWN ? 2 * l : (l == 0 ? -1 : 2 * l - 1);
-            res[q] = rsrc_i < 0 ? bf16f(gld((const uint16_t*)(p.w + p.lay.embed) + (size_t)S.tok[b] * h + row))
-                                : ldb_dev(dev_rsrc(acc_buf(p, c.parity, rsrc_i, b) + row, 4), 0);
+            res[q] = rsrc_i < 0 ? bf16f(gld((const uint16_t*)(p.w + p.lay.embed) + (size_t)S.tok[gb0 + b] * h + row))
+                                : ldb_dev(dev_rsrc(acc_buf(p, c.parity, rsrc_i, gb0 + b) + row, 4), 0);
         }
     }
     // the tile's rows in chunks of whole row groups whose results fit the slices
@@ -1770,10 +1782,10 @@ __device__ __noinline__ bool op_gemv_b(const Params* pp, uint32_t slot_, uint32_
     constexpr int NKB = KT / 32;
     const int CR = MAX_TILE_ROWS / B / 64 * 64;
     const int rows_pad = (int)(k.wbytes / (KT * 2));
-    float lm_bv[MAX_BATCH / NCW];
-    uint32_t lm_bi[MAX_BATCH / NCW];
+    float lm_bv[GROUP_SEQS / NCW];
+    uint32_t lm_bi[GROUP_SEQS / NCW];
 #pragma unroll
-    for (int j = 0; j < MAX_BATCH / NCW; ++j) {
+    for (int j = 0; j < GROUP_SEQS / NCW; ++j) {
         lm_bv[j] = -INFINITY;
         lm_bi[j] = 0xffffffffu;
     }
@@ -1787,13 +1799,13 @@ __device__ __noinline__ bool op_gemv_b(const Params* pp, uint32_t slot_, uint32_
             float* logits = S.args.logits;
             const int nr = min(CR, (int)k.nrows - c0);
 #pragma unroll
-            for (int j = 0; j < MAX_BATCH / NCW; ++j) {
+            for (int j = 0; j < GROUP_SEQS / NCW; ++j) {
                 const int b = wave + j * NCW;
                 if (b >= B) break;
                 const float rb = rs_seq(b, h, p.eps);
                 for (int i = lane; i < nr; i += 64) {
                     const float val = tile_res(i, b, B) * rb;
-                    if (logits) gst(logits + (size_t)b * p.T.V + k.row0 + c0 + i, val);
+                    if (logits) gst(logits + (size_t)(gb0 + b) * p.T.V + k.row0 + c0 + i, val);
                     if (val > lm_bv[j]) {  // rows visited in increasing order per lane: the first maximum is kept
                         lm_bv[j] = val;
                         lm_bi[j] = k.row0 + (uint32_t)(c0 + i);
@@ -1809,7 +1821,7 @@ __device__ __noinline__ bool op_gemv_b(const Params* pp, uint32_t slot_, uint32_
         const int b = tid / (int)n, i = tid % (int)n;
         if (b < B) {
             const float rb = rs_seq(b, h, p.eps);
-            const int32_t Pb = S.pos[b];
+            const int32_t Pb = S.pos[gb0 + b];
             const int j = (int)k.row0 + i;
             float lo = tile_res(i, b, B) * rb, hi = tile_res((int)n + i, b, B) * rb;
             if (slot < (uint32_t)(nq + nkv)) {
@@ -1819,20 +1831,20 @@ __device__ __noinline__ bool op_gemv_b(const Params* pp, uint32_t slot_, uint32_
                 hi = x1;
             }
             if (slot < (uint32_t)nq) {
-                float* q = p.q + (size_t)b * nq * D + (size_t)slot * D;
+                float* q = p.q + (size_t)(gb0 + b) * nq * D + (size_t)slot * D;
                 stf_dev(q + j, lo);
                 stf_dev(q + j + half, hi);
             } else {
                 const bool is_k = slot < (uint32_t)(nq + nkv);
                 const int g = is_k ? (int)slot - nq : (int)slot - nq - nkv;
                 uint16_t* base = (is_k ? S.args.kc : S.args.vc) +
-                                 (((size_t)l * B + b) * nkv + g) * (size_t)p.T.C * D + (size_t)Pb * D;
+                                 (((size_t)l * Btot + gb0 + b) * nkv + g) * (size_t)p.T.C * D + (size_t)Pb * D;
                 st16_dev(base, (uint32_t)j, f2bf16(lo));
                 st16_dev(base, (uint32_t)(j + half), f2bf16(hi));
             }
         }
     } else if (k.op == OP_GATEUP) {
-        uint16_t* Rm = opr_m(p, l);
+        uint16_t* Rm = opr_m(p, l, (int)k.seq);
         for (int idx = tid; idx < (int)k.nrows * B; idx += NCW * 64) {
             const int i = idx / B, b = idx % B;
             const float rb = rs_seq(b, h, p.eps);
@@ -1841,7 +1853,7 @@ __device__ __noinline__ bool op_gemv_b(const Params* pp, uint32_t slot_, uint32_
         }
     } else if (k.op == OP_LMHEAD) {
 #pragma unroll
-        for (int j = 0; j < MAX_BATCH / NCW; ++j) {
+        for (int j = 0; j < GROUP_SEQS / NCW; ++j) {
             const int b = wave + j * NCW;
             if (b >= B) break;
             const float bv = lm_bv[j];
@@ -1855,10 +1867,10 @@ __device__ __noinline__ bool op_gemv_b(const Params* pp, uint32_t slot_, uint32_
                 key = other > key ? other : key;
             }
             if (lane == 0 && key)
-                __hip_atomic_fetch_max((g_u64*)&p.key[c.parity * B + b], key, __ATOMIC_RELAXED,
+                __hip_atomic_fetch_max((g_u64*)&p.key[c.parity * Btot + gb0 + b], key, __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_AGENT);
         }
-        copy_hidden_share(p, k, c.parity, tid);
+        if (k.seq == 0) copy_hidden_share(p, k, c.parity, tid);  // once, by the first column group's tiles
     } else {  // O-proj / down: residual accumulation
         const int dst = k.op == OP_DOWN ? 2 * l + 1 : 2 * l;
 #pragma unroll
@@ -1866,7 +1878,7 @@ __device__ __noinline__ bool op_gemv_b(const Params* pp, uint32_t slot_, uint32_
             const int idx = tid + q * NCW * 64;
             if (idx < (int)k.nrows * B) {
                 const int i = idx / B, b = idx % B;
-                addf_dev(acc_buf(p, c.parity, dst, b) + k.row0 + i, tile_res(i, b, B) + res[q]);
+                addf_dev(acc_buf(p, c.parity, dst, gb0 + b) + k.row0 + i, tile_res(i, b, B) + res[q]);
             }
         }
     }
@@ -1890,7 +1902,7 @@ __device__ __noinline__ void finish_step(const Params* pp, uint32_t epoch, uint3
     uint32_t old = 0;
     if (lane == 0) old = addu_dev(&p.ticket[0], 1u);
     old = uni(old);
-    if (old + 1u != epoch * (uint32_t)p.T.n_lm_tiles) return;
+    if (old + 1u != epoch * (uint32_t)(p.T.n_lm_tiles * n_col_groups(p))) return;
     const int B = p.T.B;
     for (int b = lane; b < B; b += 64) {
         const unsigned long long key =

@@ -21,7 +21,8 @@ constexpr uint32_t NONE = 0xFFFFFFFFu;
 
 // Device-side capacities the tiling must respect.
 constexpr int MAX_TILE_ROWS = 1024;  // rows x sequences of one GEMV tile (LDS row-result buffer)
-constexpr int MAX_BATCH = 16;        // sequences per step (columns of one matrix-core operand)
+constexpr int GROUP_SEQS = 16;       // sequences per column group (columns of one matrix-core operand)
+constexpr int MAX_BATCH = 32;        // sequences per step: GEMV tiles run once per column group
 constexpr int MAX_ACT = 4096;        // floats of one staged activation vector (LDS)
 
 // One instruction of the interpreter: 48 bytes, read by the loader wave into LDS.
@@ -39,7 +40,7 @@ struct Task {
     uint32_t sig_ev;       // signalled event or NONE
     uint32_t wbytes;       // bytes of weights streamed into LDS pages for this task
     uint64_t wofs;         // byte offset of those weights in the packed weight buffer
-    uint32_t seq;          // sequence (batch index) for ATTN; 0 otherwise
+    uint32_t seq;          // ATTN: sequence (batch index); GEMV tiles: column group of 16 sequences
     uint32_t id;           // global task index (topological order)
 };
 static_assert(sizeof(Task) == 48, "task record is 48 bytes");

@@ -127,7 +127,7 @@ mk_status repack(mk_handle* h, const mk_model_desc* d, uint8_t* wd) {
     const int half = T.d / 2, P = T.qkv_pairs;
     const uint8_t* lm = (const uint8_t*)(h->tied ? d->tok_embed : d->lm_head);
     for (const Task& k : h->g.tasks) {
-        if (k.op == OP_ATTN || k.wbytes == 0) continue;
+        if (k.op == OP_ATTN || k.wbytes == 0 || k.seq != 0) continue;  // column groups share the tiles
         const mk_layer_weights& lw = d->layers[k.layer < T.L ? k.layer : 0];
         TileOp t;
         t.dst_off = k.wofs;
@@ -328,7 +328,8 @@ mk_status mk_build_graph(const mk_model_desc* desc, int32_t batch, int32_t max_c
     if (T.B > 1) {
         // matrix-core operands of the O- and down-projection inputs: 2 bf16 parts x 16
         // sequences per column (columns of absent sequences stay zero for the handle's life)
-        const size_t xop_elems = ((size_t)T.L * T.nq * T.d + (size_t)T.L * T.f) * 32;
+        const size_t n_sg = (size_t)(T.B + GROUP_SEQS - 1) / GROUP_SEQS;
+        const size_t xop_elems = ((size_t)T.L * T.nq * T.d + (size_t)T.L * T.f) * n_sg * 32;
         ALLOC(p.xop, xop_elems * 2, true);
         ALLOC(p.aticket, (size_t)2 * T.L * T.B * T.nkv * 4, true);
     }

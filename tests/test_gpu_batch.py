@@ -67,7 +67,7 @@ def _one_step(cfg, B, C, positions, check_kv=True, **opt):
         _check_kv((kc, vc), (k2, v2), (kg, vg), pos)
 
 
-@pytest.mark.parametrize("B", [2, 3, 16])
+@pytest.mark.parametrize("B", [2, 3, 16, 20, 32])
 def test_tiny_batch_one_step(B):
     # mixed context lengths, including position 0 and the last slot
     pos = synth.make_positions(B, 0, 511)
@@ -87,6 +87,27 @@ def test_tiny_batch_attention_chunk_slots(splits):
     # empty slots, long ones fill several; the last partial of each (sequence, group)
     # merges the non-empty ones
     _one_step(TINY, 5, 512, [0, 72, 73, 300, 511], attn_splits=splits)
+
+
+def test_tiny_batch_merge_after_every_chunk_repeated():
+    # sequences with 5 and 7 chunk slots among ones with a single slot: the merge of a
+    # (sequence, group) must see every chunk's partials, and the O-projection every
+    # merge, in every run (waves that have no work in a task must not run ahead)
+    cfg, B, C = TINY, 5, 512
+    pos = np.array([0, 72, 73, 300, 511], np.int32)
+    w = synth.make_weights(cfg)
+    kc, vc = synth.make_kv(cfg, B, C)
+    tok = synth.make_tokens(cfg, B)
+    ref = oracle.decode_step(cfg, w, tok, pos, kc.copy(), vc.copy())
+    for rep in range(8):
+        run = Runner(cfg, w, B, C, kc, vc, attn_splits=7)
+        run.step(tok, pos)
+        run.check()
+        res = compare_step(cfg, ref, run.logits.cpu().numpy(), run.hidden().cpu().numpy(),
+                           run.next_tokens().cpu().numpy())
+        run.close()
+        print(rep, res)
+        assert res["hidden_rel"] <= TOL_HIDDEN_REL and res["max_dlogit"] <= TOL_LOGIT_ABS, rep
 
 
 def test_tiny_batch_dynamic_queue():
@@ -159,6 +180,27 @@ def test_llama1b_batch16_first_step(llama1b_b16, sched):
     res = compare_step(LLAMA_1B, ref, run.logits.cpu().numpy(), run.hidden().cpu().numpy(),
                        run.next_tokens().cpu().numpy())
     run.close()
+    print(res)
+    assert res["hidden_rel"] <= TOL_HIDDEN_REL
+    assert res["max_dlogit"] <= TOL_LOGIT_ABS
+    assert res["argmax_equal"]
+
+
+def test_llama1b_batch32_first_step():
+    """32 sequences: every GEMV tile runs for two column groups of 16 on the same weights."""
+    B, C = 32, 4352
+    w = synth.make_weights(LLAMA_1B)
+    kc, vc = synth.make_kv(LLAMA_1B, B, C)
+    tok = synth.make_tokens(LLAMA_1B, B)
+    pos = synth.make_positions(B, 256, 4096)
+    print(f"case llama1b B=32 first step positions={pos.tolist()}", flush=True)
+    run = Runner(LLAMA_1B, w, B, C, kc, vc)
+    run.step(tok, pos)
+    run.check()
+    logits, hidden, nxt = run.logits.cpu().numpy(), run.hidden().cpu().numpy(), run.next_tokens().cpu().numpy()
+    run.close()
+    ref = oracle.decode_step(LLAMA_1B, w, tok, pos, kc.copy(), vc.copy())
+    res = compare_step(LLAMA_1B, ref, logits, hidden, nxt)
     print(res)
     assert res["hidden_rel"] <= TOL_HIDDEN_REL
     assert res["max_dlogit"] <= TOL_LOGIT_ABS

@@ -152,6 +152,8 @@ BATCH_CASES = [
     (synth.configs.TINY, 16, 256, 512, 1),
     (synth.configs.LLAMA_1B, 16, 256, 4352, 0),
     (synth.configs.LLAMA_1B, 4, 256, 2048, 1),
+    (synth.configs.TINY, 20, 64, 512, 0),
+    (synth.configs.LLAMA_1B, 32, 256, 4352, 0),
 ]
 
 
@@ -182,7 +184,7 @@ def test_batched_checker_catches_an_oproj_that_skips_attention():
 def test_planner_rejects_what_it_does_not_implement():
     cfg = synth.configs.TINY
     with pytest.raises(mk.MkError):
-        plan(cfg, 4, B=17)
+        plan(cfg, 4, B=33)
     with pytest.raises(mk.MkError):
         plan(synth.configs.LLAMA_8B, 256, B=2)
     with pytest.raises(mk.MkError):
