@@ -53,7 +53,7 @@ import math
 
 import numpy as np
 
-OP_QKV, OP_ATTN, OP_OPROJ, OP_GATEUP, OP_DOWN, OP_LMHEAD = 1, 2, 3, 4, 5, 6
+OP_QKV, OP_ATTN, OP_OPROJ, OP_GATEUP, OP_DOWN, OP_LMHEAD, OP_ROUTE, OP_EGU, OP_EDOWN = 1, 2, 3, 4, 5, 6, 7, 8, 9
 NONE = 0xFFFFFFFF
 TF_RESID = 1
 
@@ -97,9 +97,18 @@ def tiling(cfg, B, C, W, attn_splits=0):
         # positions, so that long and short contexts split into equal-sized work
         S = max(1, min(16, -(-C // 256))) if B == 1 else max(1, min(16, C // 1024))
     S = min(S, C)
-    kd = min(1024, f)
     max_rows = 1024 // min(B, 16)  # rows x sequences (of one column group) of a tile
-    return dict(grp=grp, pairs=8, S=S,
+    E = cfg.n_experts
+    if E:  # mixture of experts: about one expert gate/up tile and one expert down tile per workgroup
+        fe = cfg.expert_ffn
+        return dict(grp=grp, pairs=8, S=S,
+                    o_rows=min(h, max_rows, max(16, _pow2_floor(h * nkv // W))),
+                    E=E, topk=cfg.top_k, fe=fe,
+                    r_gu=min(fe, max(32, _pow2_floor(E * fe // W))),
+                    r_dn=min(h, max(64, _pow2_floor(E * h // W))),
+                    lm_rows=min(1024, _round16(-(-V // W))))
+    kd = min(1024, f)
+    return dict(grp=grp, pairs=8, S=S, E=0,
                 o_rows=min(h, max_rows, max(16, _pow2_floor(h * nkv // W))),
                 kd=kd, d_rows=min(h, max_rows, max(16, _pow2_floor(h * (f // kd) // W))),
                 g_rows=min(kd, max_rows // 2, max(8, _pow2_ceil(-(-f // W)))),
@@ -121,10 +130,19 @@ def layout(cfg, lm_rows, n_lm):
     x = _pad(x + (cfg.n_q + 2 * cfg.n_kv) * cfg.head_dim * h * 2)
     lay["o"] = x
     x = _pad(x + h * cfg.n_q * cfg.head_dim * 2)
-    lay["gu"] = x
-    x = _pad(x + 2 * cfg.ffn * h * 2)
-    lay["down"] = x
-    x = _pad(x + h * cfg.ffn * 2)
+    if cfg.n_experts:
+        E, fe = cfg.n_experts, cfg.expert_ffn
+        lay["router"] = x  # E rows padded to 16
+        x = _pad(x + _round16(E) * h * 2)
+        lay["egu"] = x
+        x = _pad(x + 2 * E * fe * h * 2)
+        lay["edown"] = x
+        x = _pad(x + E * h * fe * 2)
+    else:
+        lay["gu"] = x
+        x = _pad(x + 2 * cfg.ffn * h * 2)
+        lay["down"] = x
+        x = _pad(x + h * cfg.ffn * 2)
     lay["layer_bytes"] = x
     return lay
 
@@ -137,7 +155,8 @@ def build(cfg, B, C, W, policy=0, attn_splits=0):
     lay = layout(cfg, t["lm_rows"], n_lm)
     h, nq, nkv, d, f, L = cfg.hidden, cfg.n_q, cfg.n_kv, cfg.head_dim, cfg.ffn, cfg.n_layers
     grp, P, S = t["grp"], t["pairs"], t["S"]
-    n_kb = f // t["kd"]
+    E = t["E"]
+    n_kb = 0 if E else f // t["kd"]
     n_sg = -(-B // 16)  # column groups of 16 sequences
     tasks, target = [], []
 
@@ -161,6 +180,8 @@ def build(cfg, B, C, W, policy=0, attn_splits=0):
         ev_attn = [event() for _ in range(nkv)]
         ev_xb = event()
         ev_m = [event() for _ in range(n_kb)]
+        ev_route = event() if E else NONE
+        ev_me = [event() for _ in range(E)]
         ev_next = event()
         wb = 2 * P * h * 2
         for sg in range(n_sg):
@@ -183,6 +204,28 @@ def build(cfg, B, C, W, policy=0, attn_splits=0):
                     task(op=OP_OPROJ, layer=l, part=g, row0=rb * t["o_rows"], nrows=t["o_rows"], seq=sg,
                          flags=TF_RESID if g == 0 else 0, wait_ev=ev_attn[g], sig_ev=ev_xb, wbytes=wb,
                          wofs=base + lay["o"] + (g * (h // t["o_rows"]) + rb) * wb)
+        if E:
+            # the router (all E rows, one tile per column group), then every expert's
+            # gate/up tiles (r_gu rows of m, gate and up interleaved by 32) and down tiles
+            for sg in range(n_sg):
+                task(op=OP_ROUTE, layer=l, nrows=E, seq=sg, wait_ev=ev_xb, sig_ev=ev_route,
+                     wbytes=_round16(E) * h * 2, wofs=base + lay["router"])
+            fe, rg, rd = t["fe"], t["r_gu"], t["r_dn"]
+            wb = 2 * rg * h * 2
+            for sg in range(n_sg):
+                for e in range(E):
+                    for i in range(fe // rg):
+                        task(op=OP_EGU, layer=l, part=e, row0=i * rg, nrows=rg, seq=sg, wait_ev=ev_route,
+                             sig_ev=ev_me[e], wbytes=wb, wofs=base + lay["egu"] + (e * (fe // rg) + i) * wb)
+            wb = rd * fe * 2
+            for sg in range(n_sg):
+                for e in range(E):
+                    for rb in range(h // rd):
+                        task(op=OP_EDOWN, layer=l, part=e, row0=rb * rd, nrows=rd, seq=sg,
+                             flags=TF_RESID if e == 0 else 0, wait_ev=ev_me[e], sig_ev=ev_next, wbytes=wb,
+                             wofs=base + lay["edown"] + (e * (h // rd) + rb) * wb)
+            ev_x = ev_next
+            continue
         wb = 2 * t["g_rows"] * h * 2
         for sg in range(n_sg):
             for i in range(f // t["g_rows"]):
@@ -232,6 +275,8 @@ def check(g, cfg, B):
     h, nq, nkv, d, f, L, V = cfg.hidden, cfg.n_q, cfg.n_kv, cfg.head_dim, cfg.ffn, cfg.n_layers, cfg.vocab
     grp = nq // nkv
     n_sg = -(-B // 16)
+    E = g["tiling"]["E"]
+    DOWN = OP_EDOWN if E else OP_DOWN  # the op that completes a layer
     # G2 targets = producers
     prod = [0] * len(target)
     for k in tasks:
@@ -255,17 +300,34 @@ def check(g, cfg, B):
             if k["op"] == OP_OPROJ:
                 o[k["seq"], k["row0"]:k["row0"] + k["nrows"], k["part"]] += 1
         assert (o == 1).all(), "O-proj (row, group) not covered exactly once"
-        gu = np.zeros((n_sg, f), int)
-        for k in lt:
-            if k["op"] == OP_GATEUP:
-                gu[k["seq"], k["row0"]:k["row0"] + k["nrows"]] += 1
-        assert (gu == 1).all(), "gate/up rows not covered exactly once"
-        kd = g["tiling"]["kd"]
-        dn = np.zeros((n_sg, h, f // kd), int)
-        for k in lt:
-            if k["op"] == OP_DOWN:
-                dn[k["seq"], k["row0"]:k["row0"] + k["nrows"], k["part"]] += 1
-        assert (dn == 1).all(), "down (row, K block) not covered exactly once"
+        if E:
+            fe = g["tiling"]["fe"]
+            rt = np.zeros(n_sg, int)
+            egu = np.zeros((n_sg, E, fe), int)
+            edn = np.zeros((n_sg, E, h), int)
+            for k in lt:
+                if k["op"] == OP_ROUTE:
+                    rt[k["seq"]] += 1
+                    assert k["nrows"] == E, "the router tile holds every expert"
+                if k["op"] == OP_EGU:
+                    egu[k["seq"], k["part"], k["row0"]:k["row0"] + k["nrows"]] += 1
+                if k["op"] == OP_EDOWN:
+                    edn[k["seq"], k["part"], k["row0"]:k["row0"] + k["nrows"]] += 1
+            assert (rt == 1).all(), "routing not done exactly once per column group"
+            assert (egu == 1).all(), "expert gate/up rows not covered exactly once"
+            assert (edn == 1).all(), "expert down rows not covered exactly once"
+        else:
+            gu = np.zeros((n_sg, f), int)
+            for k in lt:
+                if k["op"] == OP_GATEUP:
+                    gu[k["seq"], k["row0"]:k["row0"] + k["nrows"]] += 1
+            assert (gu == 1).all(), "gate/up rows not covered exactly once"
+            kd = g["tiling"]["kd"]
+            dn = np.zeros((n_sg, h, f // kd), int)
+            for k in lt:
+                if k["op"] == OP_DOWN:
+                    dn[k["seq"], k["row0"]:k["row0"] + k["nrows"], k["part"]] += 1
+            assert (dn == 1).all(), "down (row, K block) not covered exactly once"
         at = np.zeros((B, nkv, g["tiling"]["S"]), int)
         for k in lt:
             if k["op"] == OP_ATTN:
@@ -277,7 +339,7 @@ def check(g, cfg, B):
         for k in lt:
             if k["op"] == OP_OPROJ and k["flags"] & TF_RESID:
                 r1[k["seq"], k["row0"]:k["row0"] + k["nrows"]] += 1
-            if k["op"] == OP_DOWN and k["flags"] & TF_RESID:
+            if k["op"] == DOWN and k["flags"] & TF_RESID:
                 r2[k["seq"], k["row0"]:k["row0"] + k["nrows"]] += 1
         assert (r1 == 1).all() and (r2 == 1).all(), "residual added more or less than once"
     lm = np.zeros((n_sg, V), int)
@@ -290,7 +352,7 @@ def check(g, cfg, B):
     by = {}
     for k in tasks:
         by.setdefault((k["op"], k["layer"]), []).append(k)
-    kd = g["tiling"]["kd"]
+    kd = g["tiling"].get("kd", 0)
 
     def ids(op, layer, pred=lambda w: True):
         return {w["id"] for w in by.get((op, layer), []) if pred(w)}
@@ -301,12 +363,12 @@ def check(g, cfg, B):
     checked = set()
     for k in tasks:
         l, op = k["layer"], k["op"]
-        key = (op, l, k["part"] if op in (OP_ATTN, OP_OPROJ, OP_DOWN) else 0, k["wait_ev"])
+        key = (op, l, k["part"] if op in (OP_ATTN, OP_OPROJ, OP_DOWN, OP_EDOWN) else 0, k["wait_ev"])
         if key in checked:
             continue
         checked.add(key)
         need = set()
-        prev = ids(OP_DOWN, l - 1) if l > 0 else set()
+        prev = ids(DOWN, l - 1) if l > 0 else set()
         if op == OP_QKV:
             need = prev
         elif op == OP_ATTN:
@@ -319,15 +381,22 @@ def check(g, cfg, B):
             need = ids(OP_OPROJ, l)
         elif op == OP_DOWN:
             need = ids(OP_GATEUP, l, lambda w: w["row0"] // kd == k["part"]) | ids(OP_OPROJ, l)
+        elif op == OP_ROUTE:
+            need = ids(OP_OPROJ, l)
+        elif op == OP_EGU:  # the routing weights and the normalised residual
+            need = ids(OP_ROUTE, l) | ids(OP_OPROJ, l)
+        elif op == OP_EDOWN:  # its expert's m rows and the residual
+            need = ids(OP_EGU, l, lambda w: w["part"] == k["part"]) | ids(OP_OPROJ, l)
         elif op == OP_LMHEAD and L > 0:
-            need = ids(OP_DOWN, L - 1)
+            need = ids(DOWN, L - 1)
         anc = hb_sets(k["id"])
         missing = need - anc
         assert not missing, f"task {k['id']} may start before its producer(s) {sorted(missing)[:4]}"
     # buffers reused from one layer to the next (q/k/v, attention partials, m): every reader of
     # layer l happens before every writer of layer l+1
     for l in range(L - 1):
-        for rop, wop in ((OP_ATTN, OP_QKV), (OP_ATTN if B > 1 else OP_OPROJ, OP_ATTN), (OP_DOWN, OP_GATEUP)):
+        for rop, wop in ((OP_ATTN, OP_QKV), (OP_ATTN if B > 1 else OP_OPROJ, OP_ATTN),
+                         (OP_EDOWN, OP_EGU) if E else (OP_DOWN, OP_GATEUP)):
             rs = ids(rop, l)
             for w in by.get((wop, l + 1), []):
                 missing = rs - hb_sets(w["id"])

@@ -17,9 +17,10 @@ _lib = None
 MK_OK, MK_E_INVALID, MK_E_UNSUPPORTED, MK_E_NOMEM, MK_E_HIP, MK_E_NOT_RESIDENT, MK_E_DEVICE, MK_E_NO_DEVICE = range(8)
 
 # opcodes of the interpreter (mirrors csrc/mk_internal.h)
-OP_END, OP_QKV, OP_ATTN, OP_OPROJ, OP_GATEUP, OP_DOWN, OP_LMHEAD = range(7)
+OP_END, OP_QKV, OP_ATTN, OP_OPROJ, OP_GATEUP, OP_DOWN, OP_LMHEAD, OP_ROUTE, OP_EGU, OP_EDOWN = range(10)
 OP_NAMES = {OP_QKV: "qkv_rope", OP_ATTN: "attention", OP_OPROJ: "oproj_residual", OP_GATEUP: "gateup_silu",
-            OP_DOWN: "down_residual", OP_LMHEAD: "lmhead_argmax"}
+            OP_DOWN: "down_residual", OP_LMHEAD: "lmhead_argmax", OP_ROUTE: "router_topk",
+            OP_EGU: "expert_gateup_silu", OP_EDOWN: "expert_down_residual"}
 NONE = 0xFFFFFFFF
 
 _P = ctypes.c_void_p
@@ -63,8 +64,8 @@ assert TASK_DTYPE.itemsize == 48
 
 HEADER_FIELDS = ["magic", "version", "n_tasks", "n_events", "W", "sched", "L", "h", "nq", "nkv", "d", "f", "V", "B",
                  "C", "grp", "qkv_pairs", "attn_splits", "o_rows", "g_rows", "kd", "d_rows", "lm_rows",
-                 "record_bytes"]
-HEADER_BYTES = 4 * (len(HEADER_FIELDS) + 7)
+                 "record_bytes", "E", "topk", "fe", "r_gu", "r_dn"]
+HEADER_BYTES = 4 * (len(HEADER_FIELDS) + 2)
 
 
 def load():

@@ -51,10 +51,18 @@ int plan_tiling(const Dims& dm, int B, int C, int W, const PlanOptions& o, Tilin
     if (B < 1 || C < 1 || W < 1) return fail("batch, max_ctx and workgroups must be >= 1");
     if (dm.d != 64 && dm.d != 128) return fail("head_dim must be 64 or 128");
     if (dm.nq % dm.nkv) return fail("n_q_heads must be a multiple of n_kv_heads");
-    if (dm.n_experts != 0) return fail("mixture-of-experts FFN is not implemented by this build");
+    const bool moe = dm.n_experts != 0;
     if (B > MAX_BATCH) return fail("batch is limited to 32 sequences per step");
     if (B > 1 && dm.h > 2048) return fail("batch > 1 needs hidden <= 2048");
-    if (dm.f <= 0) return fail("ffn_dim must be positive");
+    if (moe) {
+        // expert routing runs on the batched (several-sequence) path
+        if (B < 2) return fail("the mixture-of-experts FFN needs batch >= 2");
+        if (dm.n_experts < 1 || dm.n_experts > 64) return fail("1..64 experts");
+        if (dm.top_k < 1 || dm.top_k > dm.n_experts) return fail("top_k must be in [1, n_experts]");
+        if (!gemv_k_ok(dm.fe) || dm.fe > 2048) return fail("expert_ffn must be a power of two in [128, 2048]");
+    } else if (dm.f <= 0) {
+        return fail("ffn_dim must be positive");
+    }
     if (!gemv_k_ok(dm.h) || dm.h > MAX_ACT) return fail("hidden must be a power of two in [128, 4096]");
     const int grp = dm.nq / dm.nkv;
     if (grp > 16) return fail("more than 16 query heads per KV head");
@@ -83,6 +91,15 @@ int plan_tiling(const Dims& dm, int B, int C, int W, const PlanOptions& o, Tilin
     T.o_rows = (int)std::min<int64_t>(std::min<int64_t>(dm.h, max_rows),
                                       std::max<int64_t>(16, pow2_floor((int64_t)dm.h * dm.nkv / W)));
     T.n_o_tiles = dm.nkv * (dm.h / T.o_rows);
+    if (moe) {
+        // about one expert gate/up tile and one expert down tile per workgroup and layer;
+        // gate/up tiles hold whole 32-row blocks of m, down tiles whole 64-row chunks
+        T.E = dm.n_experts;
+        T.topk = dm.top_k;
+        T.fe = dm.fe;
+        T.r_gu = (int)std::min<int64_t>(dm.fe, std::max<int64_t>(32, pow2_floor((int64_t)dm.n_experts * dm.fe / W)));
+        T.r_dn = (int)std::min<int64_t>(dm.h, std::max<int64_t>(64, pow2_floor((int64_t)dm.n_experts * dm.h / W)));
+    } else {
     // down-proj K blocks of kd columns of m; gate/up tiles feed whole K blocks
     T.kd = (int)std::min<int64_t>(1024, dm.f);
     if (dm.f % T.kd || !gemv_k_ok(T.kd)) return fail("ffn_dim must be a multiple of 1024 (or a power of two in [128, 1024))");
@@ -95,6 +112,7 @@ int plan_tiling(const Dims& dm, int B, int C, int W, const PlanOptions& o, Tilin
     if (T.g_rows > max_rows / 2) T.g_rows = (int)(max_rows / 2);
     if (T.kd % T.g_rows) return fail("gate/up tile does not divide the down-proj K block");
     T.n_gu_tiles = dm.f / T.g_rows;
+    }
     // LM head: about one tile per workgroup (with several sequences the device takes a
     // tile in chunks of whole row groups within the row-result bound)
     T.lm_rows = (int)std::min<int64_t>(MAX_TILE_ROWS, round16((dm.V + W - 1) / W));
@@ -122,10 +140,19 @@ void plan_layout(const Tiling& T, bool tied, Layout* out) {
     l = pad256(l + (uint64_t)(T.nq + 2 * T.nkv) * T.d * h * 2);
     Ly.o = l;
     l = pad256(l + h * (uint64_t)T.nq * T.d * 2);
-    Ly.gu = l;
-    l = pad256(l + 2ull * T.f * h * 2);
-    Ly.down = l;
-    l = pad256(l + h * (uint64_t)T.f * 2);
+    if (T.E == 0) {
+        Ly.gu = l;
+        l = pad256(l + 2ull * T.f * h * 2);
+        Ly.down = l;
+        l = pad256(l + h * (uint64_t)T.f * 2);
+    } else {
+        Ly.router = l;  // E rows padded to 16
+        l = pad256(l + (uint64_t)round16(T.E) * h * 2);
+        Ly.egu = l;
+        l = pad256(l + 2ull * T.E * T.fe * h * 2);
+        Ly.edown = l;
+        l = pad256(l + (uint64_t)T.E * h * T.fe * 2);
+    }
     Ly.layer_bytes = l;
     Ly.total = Ly.layer0 + (uint64_t)T.L * l;
 }
@@ -149,7 +176,7 @@ int build_graph(const Tiling& T, const Layout& Ly, int sched, int policy, Graph*
     const uint64_t h = T.h;
     const int L = T.L, grp = T.grp, half = T.d / 2;
     const int pair_blocks = half / T.qkv_pairs;
-    const int n_kb = T.f / T.kd;
+    const int n_kb = T.E ? 0 : T.f / T.kd;
     const int n_sg = (T.B + GROUP_SEQS - 1) / GROUP_SEQS;  // column groups of the batched GEMV tiles
 
     auto add = [&](Task k) {
@@ -177,6 +204,10 @@ int build_graph(const Tiling& T, const Layout& Ly, int sched, int policy, Graph*
         for (int gi = 0; gi < T.nkv; ++gi) ev_attn[gi] = g.new_event();
         const uint32_t ev_xb = g.new_event();
         for (int kb = 0; kb < n_kb; ++kb) ev_m[kb] = g.new_event();
+        // mixture of experts: the routing, then one event per expert's gate/up tiles
+        const uint32_t ev_route = T.E ? g.new_event() : NONE;
+        std::vector<uint32_t> ev_me(T.E);
+        for (int e = 0; e < T.E; ++e) ev_me[e] = g.new_event();
         const uint32_t ev_next = g.new_event();
 
         // fused RMSNorm + QKV + RoPE tiles, grouped by KV head: q heads of the group, then its k and v head
@@ -232,6 +263,52 @@ int build_graph(const Tiling& T, const Layout& Ly, int sched, int policy, Graph*
                 k.wofs = lbase + Ly.o + ((uint64_t)gi * (T.h / T.o_rows) + rb) * k.wbytes;
                 add(k);
             }
+        if (T.E) {
+            // router: all E rows in one tile per column group; then every expert's
+            // gate/up tiles (m rows row0 .. row0 + r_gu) and down tiles (h rows)
+            for (int sg = 0; sg < n_sg; ++sg) {
+                Task k = blank(OP_ROUTE, l);
+                k.nrows = (uint32_t)T.E;
+                k.seq = (uint32_t)sg;
+                k.wait_ev = ev_xb;
+                k.sig_ev = ev_route;
+                k.wbytes = (uint32_t)((uint64_t)round16(T.E) * h * 2);
+                k.wofs = lbase + Ly.router;
+                add(k);
+            }
+            const int gu_per_e = T.fe / T.r_gu, dn_per_e = T.h / T.r_dn;
+            for (int sg = 0; sg < n_sg; ++sg)
+                for (int e = 0; e < T.E; ++e)
+                    for (int t = 0; t < gu_per_e; ++t) {
+                        Task k = blank(OP_EGU, l);
+                        k.part = (uint16_t)e;
+                        k.row0 = (uint32_t)(t * T.r_gu);
+                        k.nrows = (uint32_t)T.r_gu;
+                        k.seq = (uint32_t)sg;
+                        k.wait_ev = ev_route;
+                        k.sig_ev = ev_me[e];
+                        k.wbytes = (uint32_t)(2ull * T.r_gu * h * 2);
+                        k.wofs = lbase + Ly.egu + ((uint64_t)e * gu_per_e + t) * k.wbytes;
+                        add(k);
+                    }
+            for (int sg = 0; sg < n_sg; ++sg)
+                for (int e = 0; e < T.E; ++e)
+                    for (int rb = 0; rb < dn_per_e; ++rb) {
+                        Task k = blank(OP_EDOWN, l);
+                        k.part = (uint16_t)e;
+                        k.row0 = (uint32_t)(rb * T.r_dn);
+                        k.nrows = (uint32_t)T.r_dn;
+                        k.seq = (uint32_t)sg;
+                        k.flags = e == 0 ? TF_RESID : 0;
+                        k.wait_ev = ev_me[e];
+                        k.sig_ev = ev_next;
+                        k.wbytes = (uint32_t)((uint64_t)T.r_dn * T.fe * 2);
+                        k.wofs = lbase + Ly.edown + ((uint64_t)e * dn_per_e + rb) * k.wbytes;
+                        add(k);
+                    }
+            ev_x = ev_next;
+            continue;
+        }
         // RMSNorm + gate/up + SiLU tiles
         for (int sg = 0; sg < n_sg; ++sg)
         for (int t = 0; t < T.n_gu_tiles; ++t) {
@@ -332,6 +409,7 @@ size_t export_graph(const Graph& g, void* buf, size_t cap) {
     hd.L = T.L; hd.h = T.h; hd.nq = T.nq; hd.nkv = T.nkv; hd.d = T.d; hd.f = T.f; hd.V = T.V; hd.B = T.B; hd.C = T.C;
     hd.grp = T.grp; hd.qkv_pairs = T.qkv_pairs; hd.attn_splits = T.attn_splits; hd.o_rows = T.o_rows;
     hd.g_rows = T.g_rows; hd.kd = T.kd; hd.d_rows = T.d_rows; hd.lm_rows = T.lm_rows;
+    hd.E = T.E; hd.topk = T.topk; hd.fe = T.fe; hd.r_gu = T.r_gu; hd.r_dn = T.r_dn;
     hd.record_bytes = sizeof(Task);
     uint8_t* p = (uint8_t*)buf;
     memcpy(p, &hd, sizeof(hd));

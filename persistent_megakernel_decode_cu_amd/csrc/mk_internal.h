@@ -14,7 +14,11 @@ enum Op : uint8_t {
     OP_GATEUP = 4,    // RMSNorm + gate/up GEMV tile + SiLU * up
     OP_DOWN = 5,      // down-proj K-slice tile + residual (atomic)
     OP_LMHEAD = 6,    // final RMSNorm + LM-head tile + argmax (packed 64-bit atomic max)
-    OP_COUNT = 7
+    // mixture-of-experts FFN (several sequences): routing decided inside the step
+    OP_ROUTE = 7,     // RMSNorm + router GEMV + top-k + softmax over the selected: per-expert weights
+    OP_EGU = 8,       // RMSNorm + one expert's gate/up rows + SiLU * up * routing weight
+    OP_EDOWN = 9,     // one expert's down-proj rows + residual (atomic)
+    OP_COUNT = 10
 };
 
 constexpr uint32_t NONE = 0xFFFFFFFFu;
@@ -32,7 +36,7 @@ struct Task {
     uint8_t sig_nsub;      // sub-counters of the signalled event (1 or 8)
     uint8_t flags;         // op-specific (OPROJ/DOWN: add the residual)
     uint16_t layer;
-    uint16_t part;         // QKV: head slot; ATTN/OPROJ: KV group; DOWN: K block
+    uint16_t part;         // QKV: head slot; ATTN/OPROJ: KV group; DOWN: K block; EGU/EDOWN: expert
     uint32_t row0;         // first output row (QKV: first RoPE pair; ATTN: chunk index)
     uint32_t nrows;        // output rows of the tile (QKV: pairs)
     uint32_t wait_ev;      // awaited event or NONE
@@ -62,6 +66,10 @@ struct Tiling {
     int32_t d_rows;       // down-proj tile rows
     int32_t lm_rows;      // LM-head rows per tile
     int32_t n_qkv_tiles, n_attn_tiles, n_o_tiles, n_gu_tiles, n_down_tiles, n_lm_tiles;  // per layer / total LM
+    // mixture of experts (E = 0: dense FFN): E experts of expert_ffn fe rows, top-k
+    // routing; expert gate/up tiles of r_gu rows of m (gate and up rows interleaved in
+    // blocks of 32), expert down tiles of r_dn rows
+    int32_t E, topk, fe, r_gu, r_dn;
 };
 
 // Byte layout of the handle-owned packed weight buffer.
@@ -71,7 +79,8 @@ struct Layout {
     uint64_t lm;          // LM-head tiles (a copy of its own even when tied to the embedding)
     uint64_t layer0;      // start of layer 0
     uint64_t layer_bytes; // bytes per layer
-    uint64_t qkv, o, gu, down;  // offsets within a layer
+    uint64_t qkv, o, gu, down;  // offsets within a layer (dense FFN)
+    uint64_t router, egu, edown;  // offsets within a layer (mixture of experts)
     uint64_t total;
 };
 
@@ -85,7 +94,8 @@ struct ExportHeader {
     int32_t L, h, nq, nkv, d, f, V, B, C;
     int32_t grp, qkv_pairs, attn_splits, o_rows, g_rows, kd, d_rows, lm_rows;
     uint32_t record_bytes;
-    uint32_t reserved[7];
+    int32_t E, topk, fe, r_gu, r_dn;
+    uint32_t reserved[2];
 };
 constexpr uint32_t EXPORT_MAGIC = 0x31474B4Du;
 

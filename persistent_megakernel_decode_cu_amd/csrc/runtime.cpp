@@ -81,7 +81,7 @@ mk_status plan(const mk_model_desc* desc, int32_t batch, int32_t max_ctx, const 
     Tiling T;
     std::string err;
     Dims dm = dims_of(desc);
-    if (dm.n_experts != 0 || batch > MAX_BATCH || (batch > 1 && dm.h > 2048)) {
+    if (batch > MAX_BATCH || (batch > 1 && dm.h > 2048) || (dm.n_experts != 0 && batch < 2)) {
         if (dm.n_experts < 0 || batch < 1) return MK_E_INVALID;
         return MK_E_UNSUPPORTED;
     }
@@ -253,6 +253,7 @@ mk_status mk_build_graph(const mk_model_desc* desc, int32_t batch, int32_t max_c
     if (!out) return MK_E_INVALID;
     *out = nullptr;
     if (!desc_ok(desc)) return MK_E_INVALID;
+    if (desc->n_experts != 0) return MK_E_UNSUPPORTED;  // planned (mk_plan_graph) but not yet executed
     int ndev = 0;
     if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) return MK_E_NO_DEVICE;
     mk_options o;

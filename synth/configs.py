@@ -39,4 +39,7 @@ LLAMA_8B = ModelConfig("llama-3-8b-shape", 32, 4096, 32, 8, 128, 14336, 128256, 
 MOE_1B = ModelConfig("moe-16l-64e-top8", 16, 2048, 32, 8, 64, 0, 128256, True, 500000.0,
                      n_experts=64, top_k=8, expert_ffn=1024)
 
-CONFIGS = {c.name: c for c in (TINY, LLAMA_1B, LLAMA_8B, MOE_1B)}
+# Tiny sparse MoE for the GPU tests: the tiny attention shape, 8 experts of SwiGLU 256, top-2.
+TINY_MOE = ModelConfig("tiny-moe", 2, 256, 4, 2, 64, 0, 4096, True, 10000.0, n_experts=8, top_k=2, expert_ffn=256)
+
+CONFIGS = {c.name: c for c in (TINY, LLAMA_1B, LLAMA_8B, MOE_1B, TINY_MOE)}

@@ -61,8 +61,8 @@ class _Fake:
 def plan(cfg, W, B=1, C=2048, sched=0, policy=0, attn_splits=0):
     names = ["tok_embed", "final_norm"] + ([] if cfg.tied else ["lm_head"])
     for l in range(cfg.n_layers):
-        names += [f"l{l}.{n}" for n in ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up",
-                                        "w_down")]
+        ffn = ("router", "exp_gate", "exp_up", "exp_down") if cfg.n_experts else ("w_gate", "w_up", "w_down")
+        names += [f"l{l}.{n}" for n in ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm") + ffn]
     model = mk.Model(cfg, {n: _Fake() for n in names})
     opt = mk.options(sched=sched, policy=policy, attn_splits=attn_splits)
     return mk.parse_export(mk.mk_plan_graph(model.desc, B, C, opt, W))
@@ -74,9 +74,13 @@ def compare(ex, g, cfg, W, C, B=1):
     assert (hd["W"], hd["C"], hd["B"]) == (W, C, B)
     assert (hd["L"], hd["h"], hd["nq"], hd["nkv"], hd["d"], hd["f"], hd["V"]) == (
         cfg.n_layers, cfg.hidden, cfg.n_q, cfg.n_kv, cfg.head_dim, cfg.ffn, cfg.vocab)
-    assert (hd["grp"], hd["qkv_pairs"], hd["attn_splits"], hd["o_rows"], hd["g_rows"], hd["kd"], hd["d_rows"],
-            hd["lm_rows"]) == (t["grp"], t["pairs"], t["S"], t["o_rows"], t["g_rows"], t["kd"], t["d_rows"],
-                               t["lm_rows"])
+    assert (hd["grp"], hd["qkv_pairs"], hd["attn_splits"], hd["o_rows"], hd["lm_rows"]) == (
+        t["grp"], t["pairs"], t["S"], t["o_rows"], t["lm_rows"])
+    if t["E"]:
+        assert (hd["E"], hd["topk"], hd["fe"], hd["r_gu"], hd["r_dn"]) == (
+            t["E"], t["topk"], t["fe"], t["r_gu"], t["r_dn"])
+    else:
+        assert (hd["g_rows"], hd["kd"], hd["d_rows"], hd["E"]) == (t["g_rows"], t["kd"], t["d_rows"], 0)
     assert hd["n_tasks"] == len(g["tasks"]) and hd["n_events"] == len(g["target"])
     rec = ex["tasks"]
     for name in rec.dtype.names:
@@ -154,14 +158,18 @@ BATCH_CASES = [
     (synth.configs.LLAMA_1B, 4, 256, 2048, 1),
     (synth.configs.TINY, 20, 64, 512, 0),
     (synth.configs.LLAMA_1B, 32, 256, 4352, 0),
+    (synth.configs.TINY_MOE, 5, 37, 512, 0),
+    (synth.configs.TINY_MOE, 20, 64, 512, 1),
+    (synth.configs.MOE_1B, 16, 256, 2048, 0),
 ]
 
 
 @pytest.mark.parametrize("cfg,B,W,C,policy", BATCH_CASES,
                          ids=[f"{c[0].name}-B{c[1]}-W{c[2]}-C{c[3]}-p{c[4]}" for c in BATCH_CASES])
 def test_batched_planner_equals_oracle_graph(cfg, B, W, C, policy):
-    """Batch > 1: attention tasks per sequence, tiles bounded by rows x sequences; the library builds exactly
-    the oracle's graph, which passes the checker and every simulated interleaving."""
+    """Batch > 1: attention tasks per sequence, tiles bounded by rows x sequences, GEMV tiles per column group,
+    router and expert tasks for MoE; the library builds exactly the oracle's graph, which passes the checker
+    and every simulated interleaving."""
     ex = plan(cfg, W, B=B, C=C, policy=policy)
     g = tg.build(cfg, B, C, W, policy=policy)
     compare(ex, g, cfg, W, C, B)
@@ -185,6 +193,8 @@ def test_planner_rejects_what_it_does_not_implement():
     cfg = synth.configs.TINY
     with pytest.raises(mk.MkError):
         plan(cfg, 4, B=33)
+    with pytest.raises(mk.MkError):  # expert routing runs on the several-sequence path
+        plan(synth.configs.TINY_MOE, 4, B=1)
     with pytest.raises(mk.MkError):
         plan(synth.configs.LLAMA_8B, 256, B=2)
     with pytest.raises(mk.MkError):
