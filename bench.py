@@ -16,6 +16,7 @@ baseline on the same inputs, and the oracle's CPU time on a bounded sample.
 
   python bench.py [--gpus 1] [--steps 256] [--warmup 10] [--sched static|dynamic]
   python bench.py --batch 16    (mixed-context batch workload, tokens/s; not the headline line)
+  python bench.py --model moe   (the same batch workload on a 64-expert top-8 MoE, batch 16)
 """
 import argparse
 import json
@@ -161,10 +162,29 @@ def baseline_leg(mk, torch, cfg, model, kc, vc, tok, P0, C, K, W, mk_ms):
             "megakernel_speedup_vs_best": round(best / mk_ms, 3)}
 
 
+def moe_step_bytes(cfg, positions, experts):
+    """Algorithmic bytes of one MoE decode step: the dense part (attention, norms, LM head), every layer's
+    router, each expert that at least one sequence selected in that layer once, and the K/V rows read.
+    experts: [L][B][top_k] selected ids of that step."""
+    h, fe = cfg.hidden, cfg.expert_ffn
+    touched = sum(len(np.unique(experts[l])) for l in range(cfg.n_layers))
+    return step_bytes(cfg, positions) + 2 * cfg.n_layers * cfg.n_experts * h + 2 * 3 * h * fe * touched
+
+
+def _hip_copy_async(torch, dst, src_ptr, nbytes, stream_ptr):
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    rc = hip.hipMemcpyAsync(ctypes.c_void_p(dst), ctypes.c_void_p(src_ptr), nbytes, 3, ctypes.c_void_p(stream_ptr))
+    if rc != 0:
+        raise SystemExit(f"hipMemcpyAsync failed ({rc})")
+
+
 def bench_batch(args, torch, synth, mk):
-    """Several sequences per step: Llama-1B shape, per-sequence contexts uniform in [256, 4096] from the
-    token seed, KV cache room for 4352 positions; K greedy steps, every sequence advancing by one."""
-    cfg = synth.configs.LLAMA_1B
+    """Several sequences per step: Llama-1B shape (or the 64-expert top-8 MoE on the same attention shape),
+    per-sequence contexts uniform in [256, 4096] from the token seed, KV cache room for 4352 positions;
+    K greedy steps, every sequence advancing by one."""
+    cfg = synth.configs.MOE_1B if args.model == "moe" else synth.configs.LLAMA_1B
     B, C, K, W = args.batch, 4352, args.steps, args.warmup
     t_gen = time.perf_counter()
     w = synth.make_weights(cfg)
@@ -209,20 +229,35 @@ def bench_batch(args, torch, synth, mk):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / K
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    moe = cfg.n_experts > 0
+    if moe:
+        # each step's selections, copied out after the launch's closing event
+        sel = torch.empty(K, cfg.n_layers * B * cfg.top_k, dtype=torch.int32, device="cuda")
+        eids = mk.mk_expert_ids(h)
     for s_ in range(K):
         ev[s_][0].record(stream)
         mk.mk_decode_step(h, nxt, positions[s_].data_ptr(), kv.data_ptr(), logits.data_ptr(), sp)
         ev[s_][1].record(stream)
+        if moe:
+            _hip_copy_async(torch, sel[s_].data_ptr(), eids, sel.shape[1] * 4, sp)
     torch.cuda.synchronize()
     ms_launch = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     err = mk.mk_check_device_error(h)
     if err:
         raise SystemExit(f"device error: {err}")
-    bytes_mean = np.mean([step_bytes(cfg, P0 + s) for s in range(K)])
+    if moe:
+        sel = sel.cpu().numpy().reshape(K, cfg.n_layers, B, cfg.top_k)
+        per_step = [moe_step_bytes(cfg, P0 + s, sel[s]) for s in range(K)]
+        experts_touched = float(np.mean([sum(len(np.unique(sel[s, l])) for l in range(cfg.n_layers))
+                                         for s in range(K)]) / cfg.n_layers)
+    else:
+        per_step = [step_bytes(cfg, P0 + s) for s in range(K)]
+    bytes_mean = np.mean(per_step)
     achieved = bytes_mean / (ms_launch * 1e-3) / 1e9
     mk.mk_destroy(h)
     out = {
-        "metric": f"decode tokens/s at batch {B}, Llama-1B shape, mixed contexts",
+        "metric": f"decode tokens/s at batch {B}, {'64-expert top-8 MoE on the ' if moe else ''}Llama-1B shape, "
+                  f"mixed contexts",
         "value": round(B * 1000.0 / ms, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": round(ms, 5), "us_per_step": round(ms * 1000.0, 2), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
@@ -236,6 +271,9 @@ def bench_batch(args, torch, synth, mk):
                      "algorithmic_bytes_per_step": int(bytes_mean), "kernel_us_per_launch": round(ms_launch * 1000, 2)},
         "input_generation_s": round(t_gen, 1),
     }
+    if moe:
+        out["config"]["experts"] = {"n_experts": cfg.n_experts, "top_k": cfg.top_k, "expert_ffn": cfg.expert_ffn,
+                                    "mean_distinct_experts_per_layer": round(experts_touched, 2)}
     print(json.dumps(out), flush=True)
 
 
@@ -252,8 +290,10 @@ def main():
     ap.add_argument("--no-baseline", action="store_true", help="skip the one-kernel-per-op baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy three times (reference for the HBM byte counters)")
-    ap.add_argument("--model", choices=["1b", "8b"], default="1b",
-                    help="8b: the Llama-3-8B shape at batch 1, context 8192 (not the headline line)")
+    ap.add_argument("--model", choices=["1b", "8b", "moe"], default="1b",
+                    help="8b: the Llama-3-8B shape at batch 1, context 8192; moe: 64 experts of SwiGLU 1024, "
+                         "top-8, on the 1B attention shape, in the batch workload (default batch 16); neither "
+                         "is the headline line")
     ap.add_argument("--batch", type=int, default=1,
                     help="sequences per step; above 1: the mixed-context batch workload (contexts uniform in "
                          "[256, 4096], room for 4352), reported in tokens/s")
@@ -276,6 +316,10 @@ def main():
     import synth
     import persistent_megakernel_decode_cu_amd as mk
 
+    if args.model == "8b" and args.batch > 1:
+        raise SystemExit("the batch workload runs on the 1B shape or the MoE only")
+    if args.model == "moe" and args.batch == 1:
+        args.batch = 16
     if args.batch > 1:
         return bench_batch(args, torch, synth, mk)
     cfg = synth.configs.LLAMA_1B

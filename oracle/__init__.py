@@ -59,7 +59,7 @@ def _load():
         lib.orc_argmax_f32.restype = ctypes.c_int32
         lib.orc_topk_softmax.argtypes = [_P, ctypes.c_int32, ctypes.c_int32, _P, _P]
         lib.orc_decode_step.argtypes = [ctypes.POINTER(_Cfg), ctypes.POINTER(_Layer), _P, _P, _P, ctypes.c_int32,
-                                        _P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P, _P]
+                                        _P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P, _P, _P]
         lib.orc_decode_step.restype = ctypes.c_int32
         _lib = lib
     return _lib
@@ -146,7 +146,8 @@ def decode_step(cfg, w, tokens, positions, k_cache, v_cache, kv_round=True, want
 
     w: dict from synth.make_weights; k_cache, v_cache: uint16 [L][B][n_kv][C][d].
     Returns dict(hidden [B][h], logits [B][V] (float64), next [B] int32,
-                 layers [L][B][h] or None, experts [L][B][top_k] or None).
+                 layers [L][B][h] or None, experts [L][B][top_k] or None,
+                 router [L][B][n_experts] router logits or None).
     """
     lib = _load()
     tokens = np.ascontiguousarray(tokens, dtype=np.int32)
@@ -173,14 +174,16 @@ def decode_step(cfg, w, tokens, positions, k_cache, v_cache, kv_round=True, want
     nxt = np.empty(B, dtype=np.int32)
     lay = np.empty((L, B, cfg.hidden), dtype=np.float64) if want_layers else None
     exp = np.empty((L, B, cfg.top_k), dtype=np.int32) if cfg.n_experts else None
+    rl = np.empty((L, B, cfg.n_experts), dtype=np.float64) if cfg.n_experts else None
     rc = lib.orc_decode_step(ctypes.byref(cs), layers, _ptr(w["tok_embed"], np.uint16), _ptr(lm, np.uint16),
                              _ptr(w["final_norm"], np.uint16), B, tokens.ctypes.data, positions.ctypes.data,
                              _ptr(k_cache, np.uint16), _ptr(v_cache, np.uint16), C, 1 if kv_round else 0,
                              hidden.ctypes.data, logits.ctypes.data, nxt.ctypes.data,
-                             None if lay is None else lay.ctypes.data, None if exp is None else exp.ctypes.data)
+                             None if lay is None else lay.ctypes.data, None if exp is None else exp.ctypes.data,
+                             None if rl is None else rl.ctypes.data)
     if rc != 0:
         raise ValueError(f"oracle decode_step rejected its input (code {rc})")
-    return dict(hidden=hidden, logits=logits, next=nxt, layers=lay, experts=exp)
+    return dict(hidden=hidden, logits=logits, next=nxt, layers=lay, experts=exp, router=rl)
 
 
 def top2_gap(logits_row):

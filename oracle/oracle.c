@@ -215,12 +215,14 @@ static void swiglu(const uint16_t *wg, const uint16_t *wu, const uint16_t *wd, i
  *             0 = they enter unrounded (used only to compare with fp64 references).
  *   hidden_out [batch][h], logits [batch][vocab], next [batch];
  *   layer_out (optional) [n_layers][batch][h]: the residual after each layer;
- *   expert_ids (optional, MoE) [n_layers][batch][top_k].
+ *   expert_ids (optional, MoE) [n_layers][batch][top_k];
+ *   router_out (optional, MoE) [n_layers][batch][n_experts]: the router logits.
  */
 int32_t orc_decode_step(const orc_cfg *cfg, const orc_layer *layers, const uint16_t *embed, const uint16_t *lm_head,
                         const uint16_t *final_norm, int32_t batch, const int32_t *tokens, const int32_t *positions,
                         uint16_t *k_cache, uint16_t *v_cache, int32_t max_ctx, int32_t kv_round, double *hidden_out,
-                        double *logits, int32_t *next, double *layer_out, int32_t *expert_ids) {
+                        double *logits, int32_t *next, double *layer_out, int32_t *expert_ids,
+                        double *router_out) {
     const int32_t h = cfg->hidden, nq = cfg->n_q, nkv = cfg->n_kv, d = cfg->head_dim, L = cfg->n_layers;
     const int32_t grp = nq / nkv;
     for (int32_t b = 0; b < batch; ++b) {
@@ -274,6 +276,8 @@ int32_t orc_decode_step(const orc_cfg *cfg, const orc_layer *layers, const uint1
                 double *wt = (double *)malloc(sizeof(double) * (size_t)K);
                 orc_gemv(W->router, E, h, xn, rl);
                 orc_topk_softmax(rl, E, K, ids, wt);
+                if (router_out)
+                    for (int32_t e = 0; e < E; ++e) router_out[((size_t)l * batch + b) * E + e] = rl[e];
                 double *acc = (double *)calloc((size_t)h, sizeof(double));
                 for (int32_t j = 0; j < K; ++j) {
                     size_t e = (size_t)ids[j];

@@ -70,6 +70,7 @@ struct __attribute__((aligned(16))) Smem {
     uint32_t cgen[NCW];  // compute-wave barrier generation (per wave)
     float ssq[NCW];      // per-wave partial sums of squares of the staged activation
     float ssqb[NCW][GROUP_SEQS];  // batch > 1: per-wave, per-sequence partial sums of squares
+    float rwb[GROUP_SEQS];        // expert gate/up tiles: the expert's routing weight per sequence
     uint32_t t_ready_lo, t_ready_hi;
     uint32_t tm[4];  // trace: low 32 bits of the clock after staging / after the GEMV
 };
@@ -962,6 +963,12 @@ __device__ __forceinline__ uint16_t* opr_m(CParams& p, int l, int sg) {
     return p.xop + ((size_t)p.T.L * n_col_groups(p) * p.T.nq * p.T.d + ((size_t)l * n_col_groups(p) + sg) * p.T.f) *
                        OPS_PER_COL;
 }
+// expert e's m rows (mixture of experts), after the attention and dense-FFN regions
+__device__ __forceinline__ uint16_t* opr_me(CParams& p, int l, int e, int sg) {
+    const size_t ng = (size_t)n_col_groups(p);
+    return p.xop + ((size_t)p.T.L * ng * p.T.nq * p.T.d + (size_t)p.T.L * ng * p.T.f +
+                    (((size_t)l * p.T.E + e) * ng + sg) * p.T.fe) * OPS_PER_COL;
+}
 // element of (part, column c, sequence b) in a region of nkb 32-column blocks: block
 // (part, c / 32) holds 64 lanes x 8 elements, lane = 16 ((c % 32) / 8) + b
 __device__ __forceinline__ uint32_t opr_index(int nkb, int part, int c, int b) {
@@ -1727,8 +1734,9 @@ __device__ __noinline__ bool op_gemv_b(const Params* pp, uint32_t slot_, uint32_
     const int L = p.T.L, l = k.layer, D = p.T.d, h = p.T.h;
     constexpr bool normed = NORMED;  // QKV, gate/up, LM head
     // normalised inputs: gains slot and source residual (-1: the embedding)
-    const int gslot = k.op == OP_QKV ? 2 * l : (k.op == OP_GATEUP ? 2 * l + 1 : 2 * L);
-    const int src = k.op == OP_GATEUP ? 2 * l : (l == 0 ? -1 : 2 * l - 1);
+    const bool ffn_in = k.op == OP_GATEUP || k.op == OP_ROUTE || k.op == OP_EGU;  // the FFN's normalised input
+    const int gslot = k.op == OP_QKV ? 2 * l : (ffn_in ? 2 * l + 1 : 2 * L);
+    const int src = ffn_in ? 2 * l : (l == 0 ? -1 : 2 * l - 1);
     uint4 gpre = make_uint4(0, 0, 0, 0);
     if (normed && tid * 8 < h) gpre = gld_u4(gains(p, gslot) + tid * 8);
     if (!await_inputs(pp, k, c)) return false;
@@ -1749,7 +1757,10 @@ __device__ __noinline__ bool op_gemv_b(const Params* pp, uint32_t slot_, uint32_
             row_ofs = (uint32_t)(n * h);  // sequences past B read zeros (out of the buffer's range)
         }
         load_rows<NBW>(bo, r, emb, row_ofs, wave, lane);
-        if (!cbarrier(pp, c, k.id)) return false;  // gains staged
+        if (k.op == OP_EGU && tid < B)  // the expert's routing weight of each sequence
+            S.rwb[tid] = ldb_dev(dev_rsrc(p.rw + (size_t)l * Btot * p.T.E, (uint32_t)(Btot * p.T.E * 4)),
+                                 (uint32_t)((gb0 + tid) * p.T.E + k.part) * 4);
+        if (!cbarrier(pp, c, k.id)) return false;  // gains (and routing weights) staged
         float ss = 0.f;
 #pragma unroll
         for (int i = 0; i < NBW; ++i) ops_of_row_block(bo[i], i, wave, lane, ss);
@@ -1757,9 +1768,11 @@ __device__ __noinline__ bool op_gemv_b(const Params* pp, uint32_t slot_, uint32_
         ss += __shfl_xor(ss, 32, 64);
         if (lane < GROUP_SEQS) S.ssqb[wave][lane] = ss;
     } else {
-        const uint16_t* R = k.op == OP_OPROJ ? opr_attn(p, l, (int)k.seq) : opr_m(p, l, (int)k.seq);
-        const int nkb_total = k.op == OP_OPROJ ? p.T.nq * D / 32 : p.T.f / 32;
-        const int kb_off = k.op == OP_OPROJ ? k.part * p.T.grp * D / 32 : k.part * p.T.kd / 32;
+        const uint16_t* R = k.op == OP_OPROJ ? opr_attn(p, l, (int)k.seq)
+                            : k.op == OP_EDOWN ? opr_me(p, l, k.part, (int)k.seq)
+                                               : opr_m(p, l, (int)k.seq);
+        const int nkb_total = k.op == OP_OPROJ ? p.T.nq * D / 32 : k.op == OP_EDOWN ? p.T.fe / 32 : p.T.f / 32;
+        const int kb_off = k.op == OP_OPROJ ? k.part * p.T.grp * D / 32 : k.op == OP_EDOWN ? 0 : k.part * p.T.kd / 32;
         bops_from_region<NBW>(bo, dev_rsrc(R, (uint32_t)nkb_total * NPART * 1024u), nkb_total, kb_off, wave, lane);
     }
     tmark(c, 0);
@@ -1780,7 +1793,8 @@ __device__ __noinline__ bool op_gemv_b(const Params* pp, uint32_t slot_, uint32_
     // the tile's rows in chunks of whole row groups whose results fit the slices
     // (one chunk except for LM-head tiles)
     constexpr int NKB = KT / 32;
-    const int CR = MAX_TILE_ROWS / B / 64 * 64;
+    const bool expert = k.op == OP_EGU || k.op == OP_EDOWN;
+    const int CR = expert ? 64 : MAX_TILE_ROWS / B / 64 * 64;  // expert chunks: 32 gate + 32 up rows / 64 down rows
     const int rows_pad = (int)(k.wbytes / (KT * 2));
     float lm_bv[GROUP_SEQS / NCW];
     uint32_t lm_bi[GROUP_SEQS / NCW];
@@ -1795,7 +1809,23 @@ __device__ __noinline__ bool op_gemv_b(const Params* pp, uint32_t slot_, uint32_
         if (c0 > 0 && !cbarrier(pp, c, k.id)) return false;  // the previous chunk's results are consumed
         if (!gemv_mfma_b<KT>(pp, wave, lane, pbase, nrg, bo, B, k.id)) return false;
         if (!cbarrier(pp, c, k.id)) return false;
-        if (k.op == OP_LMHEAD) {  // logits of the chunk, running argmax per sequence
+        if (k.op == OP_EGU) {  // m = SiLU(gate) * up * routing weight, rows row0 + c0 / 2 .. + 31
+            uint16_t* Rm = opr_me(p, l, k.part, (int)k.seq);
+            for (int idx = tid; idx < 32 * B; idx += NCW * 64) {
+                const int i = idx / B, b = idx % B;
+                const float rb = rs_seq(b, h, p.eps);
+                const float gt = tile_res(i, b, B) * rb, up = tile_res(32 + i, b, B) * rb;
+                put_op1(Rm, p.T.fe / 32, (int)k.row0 + c0 / 2 + i, b, gt / (1.0f + __expf(-gt)) * up * S.rwb[b]);
+            }
+        } else if (k.op == OP_EDOWN) {  // residual accumulation of the chunk's rows
+            const int nr = min(CR, (int)k.nrows - c0);
+            for (int idx = tid; idx < nr * B; idx += NCW * 64) {
+                const int i = idx / B, b = idx % B, row = (int)k.row0 + c0 + i;
+                float v = tile_res(i, b, B);
+                if (k.flags & TF_RESID) v += ldb_dev(dev_rsrc(acc_buf(p, c.parity, 2 * l, gb0 + b) + row, 4), 0);
+                addf_dev(acc_buf(p, c.parity, 2 * l + 1, gb0 + b) + row, v);
+            }
+        } else if (k.op == OP_LMHEAD) {  // logits of the chunk, running argmax per sequence
             float* logits = S.args.logits;
             const int nr = min(CR, (int)k.nrows - c0);
 #pragma unroll
@@ -1843,6 +1873,38 @@ __device__ __noinline__ bool op_gemv_b(const Params* pp, uint32_t slot_, uint32_
                 st16_dev(base, (uint32_t)(j + half), f2bf16(hi));
             }
         }
+    } else if (k.op == OP_ROUTE) {
+        // per sequence: the top-k experts by router logit (ties: lowest id), then the softmax
+        // over the selected logits as their weights (0 for the others); lane = expert
+        const int E = p.T.E, K = p.T.topk;
+#pragma unroll
+        for (int j = 0; j < GROUP_SEQS / NCW; ++j) {
+            const int b = wave + j * NCW;
+            if (b >= B) break;
+            const float rb = rs_seq(b, h, p.eps);
+            const bool valid = lane < E;
+            const float v = valid ? tile_res(lane, b, B) * rb : 0.f;
+            bool taken = !valid;
+            float top = 0.f;
+            int32_t* ids = p.eids + ((size_t)l * Btot + gb0 + b) * K;
+            for (int r = 0; r < K; ++r) {
+                const uint32_t ub = __float_as_uint(v);
+                const uint32_t ord = (ub & 0x80000000u) ? ~ub : (ub | 0x80000000u);
+                unsigned long long key = taken ? 0ull : (((unsigned long long)ord << 32) | (uint32_t)(63 - lane));
+#pragma unroll
+                for (int o = 32; o > 0; o >>= 1) {
+                    const unsigned long long other = __shfl_xor(key, o, 64);
+                    key = other > key ? other : key;
+                }
+                const int win = 63 - (int)(uint32_t)(key & 0xffffffffull);
+                if (r == 0) top = __shfl(v, win, 64);
+                if (lane == win) taken = true;
+                if (lane == 0) gst(ids + r, (int32_t)win);
+            }
+            const float ex = (valid && taken) ? __expf(v - top) : 0.f;
+            const float z = wave_sum(ex);
+            if (valid) stf_dev(p.rw + ((size_t)l * Btot + gb0 + b) * E + lane, ex / z);
+        }
     } else if (k.op == OP_GATEUP) {
         uint16_t* Rm = opr_m(p, l, (int)k.seq);
         for (int idx = tid; idx < (int)k.nrows * B; idx += NCW * 64) {
@@ -1871,7 +1933,7 @@ __device__ __noinline__ bool op_gemv_b(const Params* pp, uint32_t slot_, uint32_
                                        __HIP_MEMORY_SCOPE_AGENT);
         }
         if (k.seq == 0) copy_hidden_share(p, k, c.parity, tid);  // once, by the first column group's tiles
-    } else {  // O-proj / down: residual accumulation
+    } else if (k.op == OP_OPROJ || k.op == OP_DOWN) {  // residual accumulation (expert tiles did theirs per chunk)
         const int dst = k.op == OP_DOWN ? 2 * l + 1 : 2 * l;
 #pragma unroll
         for (int q = 0; q < MAX_TILE_ROWS / (NCW * 64); ++q) {
@@ -1952,6 +2014,9 @@ __device__ __noinline__ void compute(const Params* pp, uint32_t epoch, int wave)
                 case OP_LMHEAD: ok = MK_KT_DISPATCH_2K(op_gemv_bn, h, pp, slot, page0, t, epoch); break;
                 case OP_OPROJ: ok = MK_KT_DISPATCH_2K(op_gemv_br, okt, pp, slot, page0, t, epoch); break;
                 case OP_DOWN: ok = MK_KT_DISPATCH_2K(op_gemv_br, dkt, pp, slot, page0, t, epoch); break;
+                case OP_ROUTE:
+                case OP_EGU: ok = MK_KT_DISPATCH_2K(op_gemv_bn, h, pp, slot, page0, t, epoch); break;
+                case OP_EDOWN: ok = MK_KT_DISPATCH_2K(op_gemv_br, p0.T.fe, pp, slot, page0, t, epoch); break;
                 case OP_ATTN: ok = hd == 64 ? op_attn<64>(pp, slot, page0, t, epoch) : op_attn<128>(pp, slot, page0, t, epoch); break;
                 default: break;
             }

@@ -163,6 +163,20 @@ mk_status repack(mk_handle* h, const mk_model_desc* d, uint8_t* wd) {
                 rows.push_back((const uint8_t*)lw.w_down + (uint64_t)(k.row0 + i) * pitch + (uint64_t)k.part * kt * 2);
         } else if (k.op == OP_LMHEAD) {
             for (uint32_t i = 0; i < k.nrows; ++i) rows.push_back(lm + (uint64_t)(k.row0 + i) * rowb);
+        } else if (k.op == OP_ROUTE) {
+            for (uint32_t i = 0; i < k.nrows; ++i) rows.push_back((const uint8_t*)lw.router + (uint64_t)i * rowb);
+        } else if (k.op == OP_EGU) {
+            // m rows row0 .. row0 + nrows of expert `part`, gate and up interleaved in blocks of 32
+            const uint64_t e0 = (uint64_t)k.part * T.fe;
+            for (uint32_t q = 0; q < k.nrows; q += 32) {
+                for (uint32_t i = 0; i < 32; ++i) rows.push_back((const uint8_t*)lw.exp_gate + (e0 + k.row0 + q + i) * rowb);
+                for (uint32_t i = 0; i < 32; ++i) rows.push_back((const uint8_t*)lw.exp_up + (e0 + k.row0 + q + i) * rowb);
+            }
+        } else if (k.op == OP_EDOWN) {
+            kt = (uint32_t)T.fe;
+            const uint64_t pitch = (uint64_t)T.fe * 2;
+            for (uint32_t i = 0; i < k.nrows; ++i)
+                rows.push_back((const uint8_t*)lw.exp_down + ((uint64_t)k.part * T.h + k.row0 + i) * pitch);
         }
         t.kt = kt;
         t.rows = (uint32_t)(k.wbytes / (kt * 2));
@@ -212,6 +226,7 @@ bool desc_ok(const mk_model_desc* d) {
         const mk_layer_weights& w = d->layers[l];
         if (!w.attn_norm || !w.wq || !w.wk || !w.wv || !w.wo || !w.ffn_norm) return false;
         if (d->n_experts == 0 && (!w.w_gate || !w.w_up || !w.w_down)) return false;
+        if (d->n_experts != 0 && (!w.router || !w.exp_gate || !w.exp_up || !w.exp_down)) return false;
     }
     return true;
 }
@@ -253,7 +268,6 @@ mk_status mk_build_graph(const mk_model_desc* desc, int32_t batch, int32_t max_c
     if (!out) return MK_E_INVALID;
     *out = nullptr;
     if (!desc_ok(desc)) return MK_E_INVALID;
-    if (desc->n_experts != 0) return MK_E_UNSUPPORTED;  // planned (mk_plan_graph) but not yet executed
     int ndev = 0;
     if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) return MK_E_NO_DEVICE;
     mk_options o;
@@ -330,9 +344,15 @@ mk_status mk_build_graph(const mk_model_desc* desc, int32_t batch, int32_t max_c
         // matrix-core operands of the O- and down-projection inputs: 2 bf16 parts x 16
         // sequences per column (columns of absent sequences stay zero for the handle's life)
         const size_t n_sg = (size_t)(T.B + GROUP_SEQS - 1) / GROUP_SEQS;
-        const size_t xop_elems = ((size_t)T.L * T.nq * T.d + (size_t)T.L * T.f) * n_sg * 32;
+        // (then, for a mixture of experts, every expert's m rows)
+        const size_t xop_elems =
+            ((size_t)T.L * T.nq * T.d + (size_t)T.L * T.f + (size_t)T.L * T.E * T.fe) * n_sg * 32;
         ALLOC(p.xop, xop_elems * 2, true);
         ALLOC(p.aticket, (size_t)2 * T.L * T.B * T.nkv * 4, true);
+        if (T.E) {
+            ALLOC(p.rw, (size_t)T.L * T.B * T.E * 4, true);
+            ALLOC(p.eids, (size_t)T.L * T.B * T.topk * 4, true);
+        }
     }
     ALLOC(p.hidden, (size_t)T.B * T.h * 4, true);
     ALLOC(p.key, sizeof(unsigned long long) * 2 * T.B, true);
@@ -401,10 +421,7 @@ mk_status mk_decode_step(mk_handle* h, const int32_t* tokens, const int32_t* pos
 
 const int32_t* mk_next_tokens(const mk_handle* h) { return h ? h->p.next : nullptr; }
 const float* mk_hidden_out(const mk_handle* h) { return h ? h->p.hidden : nullptr; }
-const int32_t* mk_expert_ids(const mk_handle* h) {
-    (void)h;
-    return nullptr;
-}
+const int32_t* mk_expert_ids(const mk_handle* h) { return h ? h->p.eids : nullptr; }
 
 mk_status mk_check_device_error(mk_handle* h, char* msg, size_t cap) {
     if (!h) return MK_E_INVALID;

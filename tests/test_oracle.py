@@ -374,10 +374,15 @@ def test_moe_step_matches_transformers_mixtral():
         cache.update(torch.tensor(f(kc[l, 0, :, :P]))[None], torch.tensor(f(vc[l, 0, :, :P]))[None], l)
     with torch.no_grad():
         out = m(input_ids=torch.tensor([[3]]), position_ids=torch.tensor([[P]]), past_key_values=cache,
-                use_cache=True, cache_position=torch.tensor([P]))
+                use_cache=True, cache_position=torch.tensor([P]), output_router_logits=True)
     ref = out.logits[0, 0].numpy()
     r = oracle.decode_step(cfg, w, [3], [P], kc.copy(), vc.copy(), kv_round=False)
     np.testing.assert_allclose(r["logits"][0], ref, rtol=0, atol=2e-6 * np.abs(ref).max())
+    # router logits of every layer, and the experts they select
+    for l in range(cfg.n_layers):
+        rl = out.router_logits[l].reshape(-1).numpy()
+        np.testing.assert_allclose(r["router"][l, 0], rl, rtol=0, atol=1e-6 * np.abs(rl).max())
+        np.testing.assert_array_equal(np.sort(r["experts"][l, 0]), np.sort(np.argsort(-rl)[:cfg.top_k]))
 
 
 # ---- the pages' own arithmetic ------------------------------------------------
