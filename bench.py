@@ -16,7 +16,7 @@ baseline on the same inputs, and the oracle's CPU time on a bounded sample.
 
   python bench.py [--gpus 1] [--steps 256] [--warmup 10] [--sched static|dynamic]
   python bench.py --batch 16    (mixed-context batch workload, tokens/s; not the headline line)
-  python bench.py --model moe   (the same batch workload on a 64-expert top-8 MoE, batch 16)
+  python bench.py --model moe   (64-expert top-8 MoE on the 1B attention shape, batch 16, context 2048)
 """
 import argparse
 import json
@@ -181,16 +181,19 @@ def _hip_copy_async(torch, dst, src_ptr, nbytes, stream_ptr):
 
 
 def bench_batch(args, torch, synth, mk):
-    """Several sequences per step: Llama-1B shape (or the 64-expert top-8 MoE on the same attention shape),
-    per-sequence contexts uniform in [256, 4096] from the token seed, KV cache room for 4352 positions;
-    K greedy steps, every sequence advancing by one."""
+    """Several sequences per step.  Dense: Llama-1B shape, per-sequence contexts uniform in [256, 4096] from
+    the token seed, KV cache room for 4352 positions.  MoE: 64 experts of SwiGLU 1024, top-8, on the 1B
+    attention shape, every sequence at context 2048.  K greedy steps, every sequence advancing by one."""
     cfg = synth.configs.MOE_1B if args.model == "moe" else synth.configs.LLAMA_1B
-    B, C, K, W = args.batch, 4352, args.steps, args.warmup
+    moe = cfg.n_experts > 0
+    # MoE: every sequence at context 2048; dense: contexts uniform in [256, 4096]
+    B, K, W = args.batch, args.steps, args.warmup
+    C = 2048 + (max(K, W) + 63) // 64 * 64 if moe else 4352
     t_gen = time.perf_counter()
     w = synth.make_weights(cfg)
     kc, vc = synth.make_kv(cfg, B, C)
     tok = synth.make_tokens(cfg, B)
-    P0 = synth.make_positions(B, 256, 4096)
+    P0 = np.full(B, 2048, np.int32) if moe else synth.make_positions(B, 256, 4096)
     t_gen = time.perf_counter() - t_gen
     if int(P0.max()) + max(K, W) > C:
         raise SystemExit("steps exceed the KV cache")
@@ -229,7 +232,6 @@ def bench_batch(args, torch, synth, mk):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / K
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    moe = cfg.n_experts > 0
     if moe:
         # each step's selections, copied out after the launch's closing event
         sel = torch.empty(K, cfg.n_layers * B * cfg.top_k, dtype=torch.int32, device="cuda")
@@ -256,13 +258,14 @@ def bench_batch(args, torch, synth, mk):
     achieved = bytes_mean / (ms_launch * 1e-3) / 1e9
     mk.mk_destroy(h)
     out = {
-        "metric": f"decode tokens/s at batch {B}, {'64-expert top-8 MoE on the ' if moe else ''}Llama-1B shape, "
-                  f"mixed contexts",
+        "metric": f"decode tokens/s at batch {B}, " + ("64-expert top-8 MoE on the Llama-1B attention shape, "
+                                                        "context 2048" if moe else "Llama-1B shape, mixed contexts"),
         "value": round(B * 1000.0 / ms, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": round(ms, 5), "us_per_step": round(ms * 1000.0, 2), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": f"{cfg.name} greedy decode, batch {B}, contexts uniform in [256, 4096], bf16 "
-                               f"weights and KV cache, one kernel launch per step",
+        "config": {"workload": f"{cfg.name} greedy decode, batch {B}, "
+                               + ("every context 2048" if moe else "contexts uniform in [256, 4096]")
+                               + ", bf16 weights and KV cache, one kernel launch per step",
                    "batch": B, "max_ctx": C, "first_positions": P0.tolist(), "sched": args.sched,
                    "workgroups": int(graph["header"]["W"]), "tasks_per_step": int(graph["header"]["n_tasks"]),
                    "attn_splits": int(graph["header"]["attn_splits"])},

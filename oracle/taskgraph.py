@@ -56,6 +56,14 @@ import numpy as np
 OP_QKV, OP_ATTN, OP_OPROJ, OP_GATEUP, OP_DOWN, OP_LMHEAD, OP_ROUTE, OP_EGU, OP_EDOWN = 1, 2, 3, 4, 5, 6, 7, 8, 9
 NONE = 0xFFFFFFFF
 TF_RESID = 1
+TF_SIGRANGE = 2  # a router tile raises the events of all E experts, sig_ev .. sig_ev + E - 1
+
+
+def signals(k, E):
+    """The events task k raises when it finishes."""
+    if k["sig_ev"] == NONE:
+        return []
+    return [k["sig_ev"] + i for i in range(E)] if k["flags"] & TF_SIGRANGE else [k["sig_ev"]]
 
 
 def idle_units_in_last_wave(n_tasks, n_units):
@@ -169,8 +177,8 @@ def build(cfg, B, C, W, policy=0, attn_splits=0):
                    seq=0)
         rec.update(k)
         rec["id"] = len(tasks)
-        if rec["sig_ev"] != NONE:
-            target[rec["sig_ev"]] += 1
+        for ev in signals(rec, E):
+            target[ev] += 1
         tasks.append(rec)
 
     ev_x = NONE
@@ -180,7 +188,6 @@ def build(cfg, B, C, W, policy=0, attn_splits=0):
         ev_attn = [event() for _ in range(nkv)]
         ev_xb = event()
         ev_m = [event() for _ in range(n_kb)]
-        ev_route = event() if E else NONE
         ev_me = [event() for _ in range(E)]
         ev_next = event()
         wb = 2 * P * h * 2
@@ -205,24 +212,26 @@ def build(cfg, B, C, W, policy=0, attn_splits=0):
                          flags=TF_RESID if g == 0 else 0, wait_ev=ev_attn[g], sig_ev=ev_xb, wbytes=wb,
                          wofs=base + lay["o"] + (g * (h // t["o_rows"]) + rb) * wb)
         if E:
-            # the router (all E rows, one tile per column group), then every expert's
-            # gate/up tiles (r_gu rows of m, gate and up interleaved by 32) and down tiles
+            # router tiles of 16 experts' logits, each raising every expert's event; every
+            # expert's gate/up tiles (r_gu rows of m, gate and up interleaved by 32), which
+            # need only the normalised residual; its down tiles, which apply the routing
             for sg in range(n_sg):
-                task(op=OP_ROUTE, layer=l, nrows=E, seq=sg, wait_ev=ev_xb, sig_ev=ev_route,
-                     wbytes=_round16(E) * h * 2, wofs=base + lay["router"])
+                for r0 in range(0, E, 16):
+                    task(op=OP_ROUTE, layer=l, row0=r0, nrows=min(16, E - r0), seq=sg, flags=TF_SIGRANGE,
+                         wait_ev=ev_xb, sig_ev=ev_me[0], wbytes=16 * h * 2, wofs=base + lay["router"] + r0 * h * 2)
             fe, rg, rd = t["fe"], t["r_gu"], t["r_dn"]
             wb = 2 * rg * h * 2
             for sg in range(n_sg):
                 for e in range(E):
                     for i in range(fe // rg):
-                        task(op=OP_EGU, layer=l, part=e, row0=i * rg, nrows=rg, seq=sg, wait_ev=ev_route,
+                        task(op=OP_EGU, layer=l, part=e, row0=i * rg, nrows=rg, seq=sg, wait_ev=ev_xb,
                              sig_ev=ev_me[e], wbytes=wb, wofs=base + lay["egu"] + (e * (fe // rg) + i) * wb)
             wb = rd * fe * 2
             for sg in range(n_sg):
                 for e in range(E):
                     for rb in range(h // rd):
                         task(op=OP_EDOWN, layer=l, part=e, row0=rb * rd, nrows=rd, seq=sg,
-                             flags=TF_RESID if e == 0 else 0, wait_ev=ev_me[e], sig_ev=ev_next, wbytes=wb,
+                             wait_ev=ev_me[e], sig_ev=ev_next, wbytes=wb,
                              wofs=base + lay["edown"] + (e * (h // rd) + rb) * wb)
             ev_x = ev_next
             continue
@@ -280,8 +289,8 @@ def check(g, cfg, B):
     # G2 targets = producers
     prod = [0] * len(target)
     for k in tasks:
-        if k["sig_ev"] != NONE:
-            prod[k["sig_ev"]] += 1
+        for ev in signals(k, E):
+            prod[ev] += 1
     assert prod == list(target), "event targets differ from producer counts"
     for k in tasks:
         if k["wait_ev"] != NONE:
@@ -302,18 +311,17 @@ def check(g, cfg, B):
         assert (o == 1).all(), "O-proj (row, group) not covered exactly once"
         if E:
             fe = g["tiling"]["fe"]
-            rt = np.zeros(n_sg, int)
+            rt = np.zeros((n_sg, E), int)
             egu = np.zeros((n_sg, E, fe), int)
             edn = np.zeros((n_sg, E, h), int)
             for k in lt:
                 if k["op"] == OP_ROUTE:
-                    rt[k["seq"]] += 1
-                    assert k["nrows"] == E, "the router tile holds every expert"
+                    rt[k["seq"], k["row0"]:k["row0"] + k["nrows"]] += 1
                 if k["op"] == OP_EGU:
                     egu[k["seq"], k["part"], k["row0"]:k["row0"] + k["nrows"]] += 1
                 if k["op"] == OP_EDOWN:
                     edn[k["seq"], k["part"], k["row0"]:k["row0"] + k["nrows"]] += 1
-            assert (rt == 1).all(), "routing not done exactly once per column group"
+            assert (rt == 1).all(), "router logits not covered exactly once per column group"
             assert (egu == 1).all(), "expert gate/up rows not covered exactly once"
             assert (edn == 1).all(), "expert down rows not covered exactly once"
         else:
@@ -341,7 +349,9 @@ def check(g, cfg, B):
                 r1[k["seq"], k["row0"]:k["row0"] + k["nrows"]] += 1
             if k["op"] == DOWN and k["flags"] & TF_RESID:
                 r2[k["seq"], k["row0"]:k["row0"] + k["nrows"]] += 1
-        assert (r1 == 1).all() and (r2 == 1).all(), "residual added more or less than once"
+        # (with experts, the residual rides on each sequence's first-choice expert: no tile flag,
+        # and every expert's down tiles cover every row, checked above)
+        assert (r1 == 1).all() and (r2 == (0 if E else 1)).all(), "residual added more or less than once"
     lm = np.zeros((n_sg, V), int)
     for k in tasks:
         if k["op"] == OP_LMHEAD:
@@ -383,10 +393,10 @@ def check(g, cfg, B):
             need = ids(OP_GATEUP, l, lambda w: w["row0"] // kd == k["part"]) | ids(OP_OPROJ, l)
         elif op == OP_ROUTE:
             need = ids(OP_OPROJ, l)
-        elif op == OP_EGU:  # the routing weights and the normalised residual
-            need = ids(OP_ROUTE, l) | ids(OP_OPROJ, l)
-        elif op == OP_EDOWN:  # its expert's m rows and the residual
-            need = ids(OP_EGU, l, lambda w: w["part"] == k["part"]) | ids(OP_OPROJ, l)
+        elif op == OP_EGU:  # the normalised residual
+            need = ids(OP_OPROJ, l)
+        elif op == OP_EDOWN:  # its expert's m rows, every router logit (the routing) and the residual
+            need = ids(OP_EGU, l, lambda w: w["part"] == k["part"]) | ids(OP_ROUTE, l) | ids(OP_OPROJ, l)
         elif op == OP_LMHEAD and L > 0:
             need = ids(DOWN, L - 1)
         anc = hb_sets(k["id"])
@@ -408,8 +418,8 @@ def check(g, cfg, B):
         assert all(a < b for a, b in zip(q, q[1:])), "a static queue is not in task order"
     assert list(g["order"]) == list(range(len(tasks))), "the dynamic order is not the task order"
     for k in tasks:
-        if k["sig_ev"] != NONE:
-            for c in consumers.get(k["sig_ev"], []):
+        for ev in signals(k, E):
+            for c in consumers.get(ev, []):
                 assert k["id"] < c, "a producer comes after its consumer in the task order"
     # G5 weights: the tiles of each packed region cover it exactly, without overlap
     lay = g.get("layout")
@@ -439,10 +449,11 @@ def check(g, cfg, B):
 def ancestor_sets(g):
     """Returns anc(i): the set of tasks that finish before task i can start, through event edges."""
     tasks = g["tasks"]
+    E = g["tiling"].get("E", 0)
     producers = {}
     for k in tasks:
-        if k["sig_ev"] != NONE:
-            producers.setdefault(k["sig_ev"], []).append(k["id"])
+        for ev in signals(k, E):
+            producers.setdefault(ev, []).append(k["id"])
     memo = {}
     # events are created in topological order, so one forward pass fills the table
     for e in range(len(g["target"])):
@@ -469,6 +480,7 @@ def simulate(g, W, seed=0, slow=None, dynamic=False, lookahead=2):
     """
     rng = np.random.default_rng(seed)
     tasks = g["tasks"]
+    E = g["tiling"].get("E", 0)
     ctr = [0] * len(g["target"])
     if dynamic:
         order = list(g["order"])
@@ -511,8 +523,8 @@ def simulate(g, W, seed=0, slow=None, dynamic=False, lookahead=2):
             i = queues[w][pos[w]]
             pos[w] += 1
         k = tasks[i]
-        if k["sig_ev"] != NONE:
-            ctr[k["sig_ev"]] += 1
+        for ev in signals(k, E):
+            ctr[ev] += 1
         done += 1
     return done
 
@@ -526,4 +538,4 @@ def from_export(ex):
     queues = [list(map(int, ex["queue"][qo[w]:qo[w + 1]])) for w in range(hd["W"])]
     return dict(tasks=tasks, target=list(map(int, ex["target"])), nsub=list(map(int, ex["nsub"])),
                 queues=queues, order=list(map(int, ex["order"])),
-                tiling=dict(kd=hd["kd"], S=hd["attn_splits"]), layout=None)
+                tiling=dict(kd=hd["kd"], S=hd["attn_splits"], E=hd["E"]), layout=None)

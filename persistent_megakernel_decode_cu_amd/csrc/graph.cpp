@@ -182,7 +182,10 @@ int build_graph(const Tiling& T, const Layout& Ly, int sched, int policy, Graph*
     auto add = [&](Task k) {
         k.id = (uint32_t)g.tasks.size();
         g.tasks.push_back(k);
-        if (k.sig_ev != NONE) g.target[k.sig_ev] += 1;
+        if (k.sig_ev != NONE) {
+            const int n_sig = (k.flags & TF_SIGRANGE) ? T.E : 1;
+            for (int i = 0; i < n_sig; ++i) g.target[k.sig_ev + i] += 1;
+        }
     };
     auto blank = [](uint8_t op, int layer) {
         Task k;
@@ -204,8 +207,8 @@ int build_graph(const Tiling& T, const Layout& Ly, int sched, int policy, Graph*
         for (int gi = 0; gi < T.nkv; ++gi) ev_attn[gi] = g.new_event();
         const uint32_t ev_xb = g.new_event();
         for (int kb = 0; kb < n_kb; ++kb) ev_m[kb] = g.new_event();
-        // mixture of experts: the routing, then one event per expert's gate/up tiles
-        const uint32_t ev_route = T.E ? g.new_event() : NONE;
+        // mixture of experts: one event per expert, raised by its gate/up tiles and by every
+        // router tile (the expert's down tiles need both the expert's m and all router logits)
         std::vector<uint32_t> ev_me(T.E);
         for (int e = 0; e < T.E; ++e) ev_me[e] = g.new_event();
         const uint32_t ev_next = g.new_event();
@@ -264,18 +267,22 @@ int build_graph(const Tiling& T, const Layout& Ly, int sched, int policy, Graph*
                 add(k);
             }
         if (T.E) {
-            // router: all E rows in one tile per column group; then every expert's
-            // gate/up tiles (m rows row0 .. row0 + r_gu) and down tiles (h rows)
-            for (int sg = 0; sg < n_sg; ++sg) {
-                Task k = blank(OP_ROUTE, l);
-                k.nrows = (uint32_t)T.E;
-                k.seq = (uint32_t)sg;
-                k.wait_ev = ev_xb;
-                k.sig_ev = ev_route;
-                k.wbytes = (uint32_t)((uint64_t)round16(T.E) * h * 2);
-                k.wofs = lbase + Ly.router;
-                add(k);
-            }
+            // router: tiles of 16 experts' logits per column group, each raising every expert's
+            // event; then every expert's gate/up tiles (m rows row0 .. row0 + r_gu), which need
+            // only the normalised residual, and its down tiles (h rows), which apply the routing
+            for (int sg = 0; sg < n_sg; ++sg)
+                for (int r0 = 0; r0 < T.E; r0 += 16) {
+                    Task k = blank(OP_ROUTE, l);
+                    k.row0 = (uint32_t)r0;
+                    k.nrows = (uint32_t)std::min(16, T.E - r0);
+                    k.seq = (uint32_t)sg;
+                    k.flags = TF_SIGRANGE;
+                    k.wait_ev = ev_xb;
+                    k.sig_ev = ev_me[0];
+                    k.wbytes = (uint32_t)(16 * h * 2);
+                    k.wofs = lbase + Ly.router + (uint64_t)r0 * h * 2;
+                    add(k);
+                }
             const int gu_per_e = T.fe / T.r_gu, dn_per_e = T.h / T.r_dn;
             for (int sg = 0; sg < n_sg; ++sg)
                 for (int e = 0; e < T.E; ++e)
@@ -285,7 +292,7 @@ int build_graph(const Tiling& T, const Layout& Ly, int sched, int policy, Graph*
                         k.row0 = (uint32_t)(t * T.r_gu);
                         k.nrows = (uint32_t)T.r_gu;
                         k.seq = (uint32_t)sg;
-                        k.wait_ev = ev_route;
+                        k.wait_ev = ev_xb;
                         k.sig_ev = ev_me[e];
                         k.wbytes = (uint32_t)(2ull * T.r_gu * h * 2);
                         k.wofs = lbase + Ly.egu + ((uint64_t)e * gu_per_e + t) * k.wbytes;
@@ -299,7 +306,6 @@ int build_graph(const Tiling& T, const Layout& Ly, int sched, int policy, Graph*
                         k.row0 = (uint32_t)(rb * T.r_dn);
                         k.nrows = (uint32_t)T.r_dn;
                         k.seq = (uint32_t)sg;
-                        k.flags = e == 0 ? TF_RESID : 0;
                         k.wait_ev = ev_me[e];
                         k.sig_ev = ev_next;
                         k.wbytes = (uint32_t)((uint64_t)T.r_dn * T.fe * 2);

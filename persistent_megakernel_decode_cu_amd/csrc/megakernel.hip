@@ -70,7 +70,8 @@ struct __attribute__((aligned(16))) Smem {
     uint32_t cgen[NCW];  // compute-wave barrier generation (per wave)
     float ssq[NCW];      // per-wave partial sums of squares of the staged activation
     float ssqb[NCW][GROUP_SEQS];  // batch > 1: per-wave, per-sequence partial sums of squares
-    float rwb[GROUP_SEQS];        // expert gate/up tiles: the expert's routing weight per sequence
+    float rwb[GROUP_SEQS];        // expert down tiles: the expert's routing weight per sequence
+    int32_t rtop[GROUP_SEQS];     // expert down tiles: 1 if the expert is the sequence's first choice
     uint32_t t_ready_lo, t_ready_hi;
     uint32_t tm[4];  // trace: low 32 bits of the clock after staging / after the GEMV
 };
@@ -201,6 +202,29 @@ __device__ __forceinline__ float wave_max(float v) {
     const float b = fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32)),
                           __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48)));
     return fmaxf(a, b);
+}
+// Top-k routing of one sequence, lane j holding the router logit v of expert j (j < E):
+// expert j's rank is the number of experts with a larger logit, or an equal one and a
+// lower id; the k of rank < k are selected, in rank order, and weighted by the softmax
+// over the selected logits.  Returns the weight of expert e (0 if not selected) and
+// sets slot to its rank (-1 if not selected).  Wave-uniform results.  Expert e's own
+// rank takes one ballot; only if e is selected are all ranks counted for the softmax.
+__device__ __forceinline__ float route_weight(float v, int lane, int E, int K, int e, int& slot) {
+    const float ve = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), e));
+    const int rank_e = __popcll(__ballot(lane < E && (v > ve || (v == ve && lane < e))));
+    slot = -1;
+    if (rank_e >= K) return 0.f;
+    slot = rank_e;
+    int rank = 0;
+    for (int j = 0; j < E; ++j) {
+        const float vj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), j));
+        rank += (vj > v || (vj == v && j < lane)) ? 1 : 0;
+    }
+    const bool sel = lane < E && rank < K;
+    const float top = wave_max(lane < E ? v : -INFINITY);
+    const float ex = sel ? __expf(v - top) : 0.f;
+    const float z = wave_sum(ex);
+    return __expf(ve - top) / z;
 }
 // Sum over aligned segments of W lanes (W = 8, 16, 32); every lane gets its segment's sum.
 template <int W>
@@ -1757,10 +1781,7 @@ __device__ __noinline__ bool op_gemv_b(const Params* pp, uint32_t slot_, uint32_
             row_ofs = (uint32_t)(n * h);  // sequences past B read zeros (out of the buffer's range)
         }
         load_rows<NBW>(bo, r, emb, row_ofs, wave, lane);
-        if (k.op == OP_EGU && tid < B)  // the expert's routing weight of each sequence
-            S.rwb[tid] = ldb_dev(dev_rsrc(p.rw + (size_t)l * Btot * p.T.E, (uint32_t)(Btot * p.T.E * 4)),
-                                 (uint32_t)((gb0 + tid) * p.T.E + k.part) * 4);
-        if (!cbarrier(pp, c, k.id)) return false;  // gains (and routing weights) staged
+        if (!cbarrier(pp, c, k.id)) return false;  // gains staged
         float ss = 0.f;
 #pragma unroll
         for (int i = 0; i < NBW; ++i) ops_of_row_block(bo[i], i, wave, lane, ss);
@@ -1773,10 +1794,44 @@ __device__ __noinline__ bool op_gemv_b(const Params* pp, uint32_t slot_, uint32_
                                                : opr_m(p, l, (int)k.seq);
         const int nkb_total = k.op == OP_OPROJ ? p.T.nq * D / 32 : k.op == OP_EDOWN ? p.T.fe / 32 : p.T.f / 32;
         const int kb_off = k.op == OP_OPROJ ? k.part * p.T.grp * D / 32 : k.op == OP_EDOWN ? 0 : k.part * p.T.kd / 32;
+        // expert down tiles: the router logits of this wave's sequences, loaded ahead of the
+        // operands so that the routing is computed while those are in flight
+        const int E = p.T.E;
+        float rlv[GROUP_SEQS / NCW];
+#pragma unroll
+        for (int j = 0; j < GROUP_SEQS / NCW; ++j) {
+            const int b = wave + j * NCW;
+            rlv[j] = -INFINITY;
+            if (k.op == OP_EDOWN && b < B && lane < E)
+                rlv[j] = ldb_dev(dev_rsrc(p.rlogit + ((size_t)l * Btot + gb0 + b) * E, (uint32_t)E * 4u),
+                                 (uint32_t)lane * 4u);
+        }
         bops_from_region<NBW>(bo, dev_rsrc(R, (uint32_t)nkb_total * NPART * 1024u), nkb_total, kb_off, wave, lane);
+        if (k.op == OP_EDOWN) {
+            // the routing weight of this expert for each sequence, from all router logits
+            // (the expert's event also counts every router tile); its selection slot too
+            const int K = p.T.topk, e = k.part;
+#pragma unroll
+            for (int j = 0; j < GROUP_SEQS / NCW; ++j) {
+                const int b = wave + j * NCW;
+                if (b >= B) break;
+                int slot;
+                const float wgt = route_weight(rlv[j], lane, E, K, e, slot);
+                if (lane == 0) {
+                    S.rwb[b] = wgt;
+                    S.rtop[b] = slot == 0;
+                    if (k.row0 == 0 && slot >= 0) gst(p.eids + ((size_t)l * Btot + gb0 + b) * K + slot, (int32_t)e);
+                }
+            }
+            if (!cbarrier(pp, c, k.id)) return false;  // routing of every sequence staged
+        }
     }
     tmark(c, 0);
-    // residual (rows x sequences) of residual-adding tiles, in flight during the GEMV
+    // residual (rows x sequences) of residual-adding tiles, in flight during the GEMV.
+    // Element idx of an O-projection or down tile's results is row idx % rows of sequence
+    // idx / rows, so the lanes of one residual load or atomic touch consecutive rows of
+    // one sequence.  (Expert down tiles, where most sequences add nothing, keep
+    // sequence-minor order: measured faster there.)
     const bool resid = (k.op == OP_OPROJ || k.op == OP_DOWN) && (k.flags & TF_RESID);
     float res[MAX_TILE_ROWS / (NCW * 64)];
 #pragma unroll
@@ -1784,7 +1839,7 @@ __device__ __noinline__ bool op_gemv_b(const Params* pp, uint32_t slot_, uint32_
         res[q] = 0.f;
         const int idx = tid + q * NCW * 64;
         if (resid && idx < (int)k.nrows * B) {
-            const int i = idx / B, b = idx % B, row = (int)k.row0 + i;
+            const int i = idx % (int)k.nrows, b = idx / (int)k.nrows, row = (int)k.row0 + i;
             const int rsrc_i = k.op == OP_DOWN ? 2 * l : (l == 0 ? -1 : 2 * l - 1);
             res[q] = rsrc_i < 0 ? bf16f(gld((const uint16_t*)(p.w + p.lay.embed) + (size_t)S.tok[gb0 + b] * h + row))
                                 : ldb_dev(dev_rsrc(acc_buf(p, c.parity, rsrc_i, gb0 + b) + row, 4), 0);
@@ -1795,6 +1850,7 @@ __device__ __noinline__ bool op_gemv_b(const Params* pp, uint32_t slot_, uint32_
     constexpr int NKB = KT / 32;
     const bool expert = k.op == OP_EGU || k.op == OP_EDOWN;
     const int CR = expert ? 64 : MAX_TILE_ROWS / B / 64 * 64;  // expert chunks: 32 gate + 32 up rows / 64 down rows
+    static_assert(64 * GROUP_SEQS <= MAX_TILE_ROWS, "an expert chunk's results (and residual rows) fit res[] and the slices");
     const int rows_pad = (int)(k.wbytes / (KT * 2));
     float lm_bv[GROUP_SEQS / NCW];
     uint32_t lm_bi[GROUP_SEQS / NCW];
@@ -1807,23 +1863,39 @@ __device__ __noinline__ bool op_gemv_b(const Params* pp, uint32_t slot_, uint32_
         const uint32_t nrg = (uint32_t)min(CR, rows_pad - c0) / 16;
         const uint32_t pbase = page0 + (NKB >= 16 ? (uint32_t)(c0 / 16) * (NKB / 16) : (uint32_t)(c0 / 16) / (16 / NKB));
         if (c0 > 0 && !cbarrier(pp, c, k.id)) return false;  // the previous chunk's results are consumed
+        // expert down tiles: the residual rows of the chunk (64 x up to 16 sequences, in
+        // res[]) of the sequences whose first choice is this expert, in flight during its
+        // GEMV; so each sequence's residual is added exactly once, with that expert's output
+        if (k.op == OP_EDOWN) {
+            const int nr = min(CR, (int)k.nrows - c0);
+#pragma unroll
+            for (int q = 0; q < MAX_TILE_ROWS / (NCW * 64); ++q) {
+                const int idx = tid + q * NCW * 64, i = idx / B, b = idx % B;
+                res[q] = i < nr && S.rtop[b]
+                             ? ldb_dev(dev_rsrc(acc_buf(p, c.parity, 2 * l, gb0 + b) + k.row0 + c0 + i, 4), 0)
+                             : 0.f;
+            }
+        }
         if (!gemv_mfma_b<KT>(pp, wave, lane, pbase, nrg, bo, B, k.id)) return false;
         if (!cbarrier(pp, c, k.id)) return false;
-        if (k.op == OP_EGU) {  // m = SiLU(gate) * up * routing weight, rows row0 + c0 / 2 .. + 31
+        if (k.op == OP_EGU) {  // m = SiLU(gate) * up, rows row0 + c0 / 2 .. + 31
             uint16_t* Rm = opr_me(p, l, k.part, (int)k.seq);
             for (int idx = tid; idx < 32 * B; idx += NCW * 64) {
                 const int i = idx / B, b = idx % B;
                 const float rb = rs_seq(b, h, p.eps);
                 const float gt = tile_res(i, b, B) * rb, up = tile_res(32 + i, b, B) * rb;
-                put_op1(Rm, p.T.fe / 32, (int)k.row0 + c0 / 2 + i, b, gt / (1.0f + __expf(-gt)) * up * S.rwb[b]);
+                put_op1(Rm, p.T.fe / 32, (int)k.row0 + c0 / 2 + i, b, gt / (1.0f + __expf(-gt)) * up);
             }
-        } else if (k.op == OP_EDOWN) {  // residual accumulation of the chunk's rows
+        } else if (k.op == OP_EDOWN) {  // weighted residual accumulation of the chunk's rows
+            // (sequences that did not select the expert add nothing)
             const int nr = min(CR, (int)k.nrows - c0);
-            for (int idx = tid; idx < nr * B; idx += NCW * 64) {
-                const int i = idx / B, b = idx % B, row = (int)k.row0 + c0 + i;
-                float v = tile_res(i, b, B);
-                if (k.flags & TF_RESID) v += ldb_dev(dev_rsrc(acc_buf(p, c.parity, 2 * l, gb0 + b) + row, 4), 0);
-                addf_dev(acc_buf(p, c.parity, 2 * l + 1, gb0 + b) + row, v);
+#pragma unroll
+            for (int q = 0; q < MAX_TILE_ROWS / (NCW * 64); ++q) {
+                const int idx = tid + q * NCW * 64, i = idx / B, b = idx % B;
+                if (i >= nr) break;
+                const float wb = S.rwb[b];
+                if (wb == 0.f) continue;
+                addf_dev(acc_buf(p, c.parity, 2 * l + 1, gb0 + b) + k.row0 + c0 + i, tile_res(i, b, B) * wb + res[q]);
             }
         } else if (k.op == OP_LMHEAD) {  // logits of the chunk, running argmax per sequence
             float* logits = S.args.logits;
@@ -1873,37 +1945,10 @@ __device__ __noinline__ bool op_gemv_b(const Params* pp, uint32_t slot_, uint32_
                 st16_dev(base, (uint32_t)(j + half), f2bf16(hi));
             }
         }
-    } else if (k.op == OP_ROUTE) {
-        // per sequence: the top-k experts by router logit (ties: lowest id), then the softmax
-        // over the selected logits as their weights (0 for the others); lane = expert
-        const int E = p.T.E, K = p.T.topk;
-#pragma unroll
-        for (int j = 0; j < GROUP_SEQS / NCW; ++j) {
-            const int b = wave + j * NCW;
-            if (b >= B) break;
-            const float rb = rs_seq(b, h, p.eps);
-            const bool valid = lane < E;
-            const float v = valid ? tile_res(lane, b, B) * rb : 0.f;
-            bool taken = !valid;
-            float top = 0.f;
-            int32_t* ids = p.eids + ((size_t)l * Btot + gb0 + b) * K;
-            for (int r = 0; r < K; ++r) {
-                const uint32_t ub = __float_as_uint(v);
-                const uint32_t ord = (ub & 0x80000000u) ? ~ub : (ub | 0x80000000u);
-                unsigned long long key = taken ? 0ull : (((unsigned long long)ord << 32) | (uint32_t)(63 - lane));
-#pragma unroll
-                for (int o = 32; o > 0; o >>= 1) {
-                    const unsigned long long other = __shfl_xor(key, o, 64);
-                    key = other > key ? other : key;
-                }
-                const int win = 63 - (int)(uint32_t)(key & 0xffffffffull);
-                if (r == 0) top = __shfl(v, win, 64);
-                if (lane == win) taken = true;
-                if (lane == 0) gst(ids + r, (int32_t)win);
-            }
-            const float ex = (valid && taken) ? __expf(v - top) : 0.f;
-            const float z = wave_sum(ex);
-            if (valid) stf_dev(p.rw + ((size_t)l * Btot + gb0 + b) * E + lane, ex / z);
+    } else if (k.op == OP_ROUTE) {  // router logits of experts row0 .. row0 + nrows - 1
+        for (int idx = tid; idx < (int)k.nrows * B; idx += NCW * 64) {
+            const int i = idx / B, b = idx % B;
+            stf_dev(p.rlogit + ((size_t)l * Btot + gb0 + b) * p.T.E + k.row0 + i, tile_res(i, b, B) * rs_seq(b, h, p.eps));
         }
     } else if (k.op == OP_GATEUP) {
         uint16_t* Rm = opr_m(p, l, (int)k.seq);
@@ -1939,7 +1984,7 @@ __device__ __noinline__ bool op_gemv_b(const Params* pp, uint32_t slot_, uint32_
         for (int q = 0; q < MAX_TILE_ROWS / (NCW * 64); ++q) {
             const int idx = tid + q * NCW * 64;
             if (idx < (int)k.nrows * B) {
-                const int i = idx / B, b = idx % B;
+                const int i = idx % (int)k.nrows, b = idx / (int)k.nrows;
                 addf_dev(acc_buf(p, c.parity, dst, gb0 + b) + k.row0 + i, tile_res(i, b, B) + res[q]);
             }
         }
@@ -2037,9 +2082,10 @@ __device__ __noinline__ void compute(const Params* pp, uint32_t epoch, int wave)
         if (c.wave == 0) {
             if (!lds_wait_ge(S.done, NCW * (t + 1), pp, k.id)) return;
             CParams& p = P(pp);
-            if (k.sig_ev != NONE && k.id != p.drop_task && c.lane == 0) {
+            const int n_sig = (k.flags & TF_SIGRANGE) ? p0.T.E : 1;  // router tiles: every expert's event
+            if (k.sig_ev != NONE && k.id != p.drop_task && c.lane < n_sig) {
                 const uint32_t sub = k.sig_nsub == 8 ? xcc_id() : 0u;
-                addu_dev(&p.ctr[ctr_index(k.sig_ev, sub)], 1u);
+                addu_dev(&p.ctr[ctr_index(k.sig_ev + (uint32_t)c.lane, sub)], 1u);
             }
             if (k.op == OP_LMHEAD) finish_step(pp, epoch, c.parity);
             if (p.task_count && c.lane == 0) addu_dev(&p.task_count[k.id], 1u);

@@ -15,9 +15,9 @@ enum Op : uint8_t {
     OP_DOWN = 5,      // down-proj K-slice tile + residual (atomic)
     OP_LMHEAD = 6,    // final RMSNorm + LM-head tile + argmax (packed 64-bit atomic max)
     // mixture-of-experts FFN (several sequences): routing decided inside the step
-    OP_ROUTE = 7,     // RMSNorm + router GEMV + top-k + softmax over the selected: per-expert weights
-    OP_EGU = 8,       // RMSNorm + one expert's gate/up rows + SiLU * up * routing weight
-    OP_EDOWN = 9,     // one expert's down-proj rows + residual (atomic)
+    OP_ROUTE = 7,     // RMSNorm + router GEMV rows: router logits of up to 16 experts
+    OP_EGU = 8,       // RMSNorm + one expert's gate/up rows + SiLU * up
+    OP_EDOWN = 9,     // routing weights (top-k + softmax) + one expert's down-proj rows, weighted, + residual (atomic)
     OP_COUNT = 10
 };
 
@@ -34,7 +34,7 @@ struct Task {
     uint8_t op;
     uint8_t wait_nsub;     // sub-counters of the awaited event (1 or 8)
     uint8_t sig_nsub;      // sub-counters of the signalled event (1 or 8)
-    uint8_t flags;         // op-specific (OPROJ/DOWN: add the residual)
+    uint8_t flags;         // TaskFlags
     uint16_t layer;
     uint16_t part;         // QKV: head slot; ATTN/OPROJ: KV group; DOWN: K block; EGU/EDOWN: expert
     uint32_t row0;         // first output row (QKV: first RoPE pair; ATTN: chunk index)
@@ -50,8 +50,8 @@ struct Task {
 static_assert(sizeof(Task) == 48, "task record is 48 bytes");
 
 enum TaskFlags : uint8_t {
-    TF_RESID = 1,   // OPROJ / DOWN: this tile also adds the residual input
-    TF_ZEROKEY = 2  // reserved
+    TF_RESID = 1,    // OPROJ / DOWN: this tile also adds the residual input
+    TF_SIGRANGE = 2  // ROUTE: signals the E consecutive events sig_ev .. sig_ev + E - 1
 };
 
 // Tiling of one model on W workgroups (computed once on the host).

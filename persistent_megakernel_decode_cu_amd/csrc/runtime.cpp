@@ -164,7 +164,7 @@ mk_status repack(mk_handle* h, const mk_model_desc* d, uint8_t* wd) {
         } else if (k.op == OP_LMHEAD) {
             for (uint32_t i = 0; i < k.nrows; ++i) rows.push_back(lm + (uint64_t)(k.row0 + i) * rowb);
         } else if (k.op == OP_ROUTE) {
-            for (uint32_t i = 0; i < k.nrows; ++i) rows.push_back((const uint8_t*)lw.router + (uint64_t)i * rowb);
+            for (uint32_t i = 0; i < k.nrows; ++i) rows.push_back((const uint8_t*)lw.router + (uint64_t)(k.row0 + i) * rowb);
         } else if (k.op == OP_EGU) {
             // m rows row0 .. row0 + nrows of expert `part`, gate and up interleaved in blocks of 32
             const uint64_t e0 = (uint64_t)k.part * T.fe;
@@ -350,7 +350,7 @@ mk_status mk_build_graph(const mk_model_desc* desc, int32_t batch, int32_t max_c
         ALLOC(p.xop, xop_elems * 2, true);
         ALLOC(p.aticket, (size_t)2 * T.L * T.B * T.nkv * 4, true);
         if (T.E) {
-            ALLOC(p.rw, (size_t)T.L * T.B * T.E * 4, true);
+            ALLOC(p.rlogit, (size_t)T.L * T.B * T.E * 4, true);
             ALLOC(p.eids, (size_t)T.L * T.B * T.topk * 4, true);
         }
     }

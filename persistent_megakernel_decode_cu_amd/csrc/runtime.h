@@ -49,7 +49,7 @@ struct Params {
     // sequence l % 16, columns 8 (l / 16) .. +7)
     uint16_t* xop;            // [L][2][nq*d/32][64][8] (merged attention), then [L][2][f/32][64][8] (SiLU(gate) * up)
     uint32_t* aticket;        // batch > 1: [2][L][B][n_kv] finished attention partials per step parity
-    float* rw;                // MoE: [L][B][E] routing weight of each expert (0: not selected)
+    float* rlogit;            // MoE: [L][B][E] router logits
     int32_t* eids;            // MoE: [L][B][top_k] selected experts, in selection order
     float* hidden;            // [B][h]
     unsigned long long* key;  // [2][B] packed argmax keys

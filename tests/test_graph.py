@@ -275,3 +275,33 @@ def test_checker_and_simulator_catch_planted_mistakes():
     q.remove(i)
     q.insert(0, i)
     assert tg.simulate(g, 1) < len(g["tasks"])
+
+
+def test_checker_catches_planted_routing_mistakes():
+    """Expert down tiles must follow every router tile: a router tile that raises only its first
+    event (targets recounted to match) or a missing router row is caught."""
+    cfg = synth.configs.TINY_MOE
+    B, W = 5, 8
+
+    def recount(g):
+        g["target"] = [0] * len(g["target"])
+        for k in g["tasks"]:
+            for ev in tg.signals(k, cfg.n_experts):
+                g["target"][ev] += 1
+        for k in g["tasks"]:
+            if k["wait_ev"] != tg.NONE:
+                k["wait_target"] = g["target"][k["wait_ev"]]
+
+    g = tg.build(cfg, B, 512, W)
+    tg.check(g, cfg, B)
+    k = next(k for k in g["tasks"] if k["op"] == tg.OP_ROUTE and k["layer"] == 1)
+    k["flags"] &= ~tg.TF_SIGRANGE
+    recount(g)
+    with pytest.raises(AssertionError, match="before its producer"):
+        tg.check(g, cfg, B)
+
+    g = tg.build(cfg, B, 512, W)
+    k = next(k for k in g["tasks"] if k["op"] == tg.OP_ROUTE)
+    k["nrows"] -= 1
+    with pytest.raises(AssertionError, match="router logits"):
+        tg.check(g, cfg, B)
