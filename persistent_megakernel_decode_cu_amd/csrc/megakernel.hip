@@ -341,6 +341,9 @@ __device__ __forceinline__ Chunk attn_chunk(int32_t splits, int32_t fixed_len, i
 }
 // one page holds 8 KiB of K rows then 8 KiB of V rows of consecutive positions
 __device__ __forceinline__ int32_t attn_block_rows(int32_t d) { return 4096 / d; }
+// attention on the matrix cores (head_dim 64, at most 4 query heads per KV head), whose
+// K pages are row-major with XOR-swizzled 16-byte chunks
+__device__ __forceinline__ bool attn_kswizzle(int32_t d, int32_t grp) { return d == 64 && grp <= 4; }
 
 __device__ __forceinline__ int32_t seq_pos(uint32_t b) { return (int32_t)lds_ld(*(const uint32_t*)&S.pos[b]); }
 
@@ -377,17 +380,26 @@ __device__ __forceinline__ void issue_page(CParams& p, const Task& k, uint32_t k
         const uint64_t row = (((uint64_t)k.layer * p.T.B + k.seq) * p.T.nkv + k.part) * (uint64_t)p.T.C + (uint64_t)p0;
         const uint8_t* kb = (const uint8_t*)S.args.kc + row * d * 2;
         const uint8_t* vb = (const uint8_t*)S.args.vc + row * d * 2;
-        // K goes in 16-byte-column-major order (column chunk c of all pb rows, then
-        // c + 1, ...: a lane per position reads its chunk without bank conflicts);
-        // V stays row-major.  Rows past the valid ones repeat the last valid row.
+        // K: for the matrix-core attention (head_dim 64, up to 4 heads per group) rows stay
+        // row-major with the 16-byte chunks of row r XOR-swizzled by r % 8, so every load
+        // reads 1 KiB of consecutive K rows and the operand reads (16 rows, one chunk) hit
+        // distinct banks; otherwise 16-byte-column-major order (column chunk c of all pb
+        // rows, then c + 1, ...: a lane per position reads its chunk without bank
+        // conflicts).  V stays row-major.  Rows past the valid ones repeat the last valid row.
+        const bool swz = attn_kswizzle(p.T.d, p.T.grp);
 #pragma unroll
         for (int i = 0; i < LPP; ++i) {
             const int j = i * NLW + lw;  // 1 KiB load j of the page: K for j < 8, V after
             uint32_t off;
             if (j < 8) {
                 const uint32_t e = (uint32_t)(j * 64 + lane);  // 16-byte element of the K block
-                const uint32_t c = e / (uint32_t)pb, r = min(e % (uint32_t)pb, (uint32_t)rows - 1u);
-                off = r * (uint32_t)d * 2u + c * 16u;
+                if (swz) {
+                    const uint32_t r = e / 8u, c = (e % 8u) ^ (r & 7u);
+                    off = min(r, (uint32_t)rows - 1u) * (uint32_t)d * 2u + c * 16u;
+                } else {
+                    const uint32_t c = e / (uint32_t)pb, r = min(e % (uint32_t)pb, (uint32_t)rows - 1u);
+                    off = r * (uint32_t)d * 2u + c * 16u;
+                }
             } else {
                 off = min((uint32_t)((j - 8) * 1024 + lane * 16), valid - 16u);
             }
@@ -1396,6 +1408,212 @@ __device__ __noinline__ bool op_attn(const Params* pp, uint32_t slot_, uint32_t 
     return true;
 }
 
+// GQA decode attention over one KV chunk on the matrix cores (head_dim 64, up to four
+// query heads per KV head).  Wave w takes positions 16 w .. 16 w + 15 of every page, for
+// all heads.  Scores: S^T = K q^T on v_mfma_f32_16x16x32_bf16 with the K rows as the A
+// operand (one 16-byte chunk of a row per lane) and the query in
+// the B operand split exactly into three bf16 parts, column n holding part n / 4 of head
+// n % 4 (part 3 zero): summing a row's columns of one head gives the fp32-exact dot
+// product.  The output layout puts, in lane (n, kq), the scores of positions 4 kq .. +3
+// for head n % 4 -- exactly the positions and head whose probabilities that lane feeds to
+// O^T += V^T P^T (v_mfma_f32_16x16x16_bf16, P split the same way), so the probabilities
+// never move between lanes.  Each wave keeps its own running max, sum and output per head;
+// the four are merged through LDS at the end, together with the current token's K/V.
+// The page's K rows are row-major with 16-byte chunk c of row r stored at chunk c ^ (r % 8).
+typedef short s16x4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t split_part(float v, int part) {
+    uint32_t hi, mid, lo;
+    split3(v, hi, mid, lo);
+    return part == 0 ? hi : part == 1 ? mid : part == 2 ? lo : 0u;
+}
+// sum over the four columns n, n +- 4, n +- 8 of a 16-lane row (the parts of one head)
+__device__ __forceinline__ float sum_parts(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, true));  // row_ror:8
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, true));  // row_ror:4
+    return v;
+}
+
+__device__ __noinline__ bool op_attn_mfma(const Params* pp, uint32_t slot_, uint32_t page0, uint32_t t_,
+                                          uint32_t epoch_) {
+    constexpr int D = 64, PB = 4096 / D, BATCH = 4, MW = 8 + 4 * D;  // merge record: M[4], L[4], O[4][D]
+    const Task k = fifo_task(slot_);
+    Ctx c = make_ctx(t_, epoch_);
+    CParams& p = P(pp);
+    const int lane = c.lane, wave = c.wave;
+    const int b = (int)k.seq, g = k.part, G = p.T.grp;
+    const Chunk ch = attn_chunk(p.T.attn_splits, attn_fixed_len(p.T.B, p.T.C, p.T.attn_splits), S.pos[b], k.row0);
+    const int32_t pre_end = min(ch.c1, ch.P);
+    const int32_t npre = max(0, pre_end - ch.c0);
+    const uint32_t npages = (uint32_t)((npre + PB - 1) / PB);
+    const float scale = 1.0f / sqrtf((float)D);
+    const bool has_cur = ch.c0 <= ch.P && ch.P < ch.c1;
+    // an empty chunk slot (several sequences): no pages, no partials, but the start-of-task
+    // handshake (see op_attn)
+    if (p.T.B > 1 && ch.c0 > ch.P) {
+        Task none = k;
+        none.wait_ev = NONE;
+        return await_inputs(pp, none, c);
+    }
+    if (!await_inputs(pp, k, c)) return false;
+    const int n = lane % 16, kq = lane / 16, hq = n % 4, part = n / 4;
+    const __amdgpu_buffer_rsrc_t qr = dev_rsrc(p.q + (size_t)b * p.T.nq * D + (size_t)g * G * D, (uint32_t)(G * D * 4));
+    // B operand of the scores: part `part` of q[head hq][32 ks + 8 kq .. +7]
+    u32x4v qb[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        u32x4v raw = u32x4v{0u, 0u, 0u, 0u};
+        if (hq < G) raw = __builtin_bit_cast(u32x4v, __builtin_amdgcn_raw_buffer_load_b128(qr, (hq * D + 32 * ks + 8 * kq) * 4, 0, 16));
+        u32x4v raw2 = u32x4v{0u, 0u, 0u, 0u};
+        if (hq < G) raw2 = __builtin_bit_cast(u32x4v, __builtin_amdgcn_raw_buffer_load_b128(qr, (hq * D + 32 * ks + 8 * kq + 4) * 4, 0, 16));
+        const float qv[8] = {__uint_as_float(raw.x), __uint_as_float(raw.y), __uint_as_float(raw.z), __uint_as_float(raw.w),
+                             __uint_as_float(raw2.x), __uint_as_float(raw2.y), __uint_as_float(raw2.z), __uint_as_float(raw2.w)};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qb[ks][i] = split_part(qv[2 * i], part) | (split_part(qv[2 * i + 1], part) << 16);
+    }
+    tmark(c, 0);
+    f32x4v oacc[D / 16];  // O^T accumulators: rows d = 16 dg + 4 kq + r, column n
+#pragma unroll
+    for (int dg = 0; dg < D / 16; ++dg) oacc[dg] = f32x4v{0.f, 0.f, 0.f, 0.f};
+    float M = -INFINITY, L = 0.f;  // running max and this lane's sum (head hq, its positions)
+    for (uint32_t pb0 = 0; pb0 < npages; pb0 += BATCH) {
+        const uint32_t nb = min((uint32_t)BATCH, npages - pb0);
+        for (uint32_t i = 0; i < nb; ++i)
+            if (!page_acquire(pp, page0 + pb0 + i, k.id)) return false;
+        tmark(c, 2);
+        float sc[BATCH][4];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < BATCH; ++i) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sc[i][r] = -INFINITY;
+            if ((uint32_t)i < nb) {
+                const uint32_t slot = (page0 + pb0 + i) % NPAGES;
+                const int32_t rows = min(PB, pre_end - (ch.c0 + (int32_t)(pb0 + i) * PB));
+                f32x4v acc = f32x4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const int pos = 16 * wave + n, cix = (4 * ks + kq) ^ (pos & 7);
+                    const u32x4v a = *(const u32x4v*)&ring[slot][pos * (2 * D) + cix * 16];
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8v, a),
+                                                                   __builtin_bit_cast(bf16x8v, qb[ks]), acc, 0, 0, 0);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float v = sum_parts(acc[r]) * scale;
+                    if (16 * wave + 4 * kq + r < rows) sc[i][r] = v;
+                    mx = fmaxf(mx, sc[i][r]);
+                }
+            }
+        }
+        // this wave's max for head hq: over the four lane rows (the part columns agree)
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float mn = fmaxf(M, mx);
+        const float mref = mn == -INFINITY ? 0.f : mn;
+        const float corr = __expf(M - mref);
+        L *= corr;
+#pragma unroll
+        for (int dg = 0; dg < D / 16; ++dg) oacc[dg] *= corr;
+        M = mn;
+#pragma unroll
+        for (int i = 0; i < BATCH; ++i) {
+            if ((uint32_t)i >= nb) break;
+            const uint32_t slot = (page0 + pb0 + i) % NPAGES;
+            float pr[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                pr[r] = __expf(sc[i][r] - mref);
+                L += pr[r];
+            }
+            // B operand: part `part` of p at positions 4 kq + r (r = 0..3), head hq
+            const s16x4v pbv = __builtin_bit_cast(
+                s16x4v, u32x2v{split_part(pr[0], part) | (split_part(pr[1], part) << 16),
+                               split_part(pr[2], part) | (split_part(pr[3], part) << 16)});
+            const uint16_t* vrow = (const uint16_t*)&ring[slot][8192] + (16 * wave + 4 * kq) * D;
+#pragma unroll
+            for (int dg = 0; dg < D / 16; ++dg) {
+                // A operand: V^T row d = 16 dg + n, positions 4 kq .. +3 of this wave's 16
+                const int d = 16 * dg + n;
+                const uint32_t v01 = (uint32_t)vrow[d] | ((uint32_t)vrow[D + d] << 16);
+                const uint32_t v23 = (uint32_t)vrow[2 * D + d] | ((uint32_t)vrow[3 * D + d] << 16);
+                oacc[dg] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4v, u32x2v{v01, v23}), pbv,
+                                                                      oacc[dg], 0, 0, 0);
+            }
+        }
+        for (uint32_t i = 0; i < nb; ++i) page_release(page0 + pb0 + i, lane);
+    }
+    // this wave's record for the merge: M and L per head, O[head][d]
+    float* const mrec = &S.xs[MAX_ACT / 2 + wave * MW];
+    float Lh = part == 0 ? L : 0.f;  // the part columns hold copies of the same sums
+    Lh += __shfl_xor(Lh, 16, 64);
+    Lh += __shfl_xor(Lh, 32, 64);
+#pragma unroll
+    for (int dg = 0; dg < D / 16; ++dg)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float o = sum_parts(oacc[dg][r]);
+            if (part == 0) mrec[8 + hq * D + 16 * dg + 4 * kq + r] = o;
+        }
+    if (part == 0 && kq == 0) {
+        mrec[hq] = M;
+        mrec[4 + hq] = Lh;
+    }
+    if (!cbarrier(pp, c, k.id)) return false;  // every wave's record is in LDS
+    tmark(c, 1);
+    if (wave < G) {
+        // head `wave`: merge the four waves' records (lane = dimension), then the current token
+        const int h = wave;
+        float Mx = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NCW; ++w) Mx = fmaxf(Mx, S.xs[MAX_ACT / 2 + w * MW + h]);
+        const float mref = Mx == -INFINITY ? 0.f : Mx;
+        float Lt = 0.f, o = 0.f;
+#pragma unroll
+        for (int w = 0; w < NCW; ++w) {
+            const float* rec = &S.xs[MAX_ACT / 2 + w * MW];
+            const float a = __expf(rec[h] - mref);
+            Lt += a * rec[4 + h];
+            o += a * rec[8 + h * D + lane];
+        }
+        if (has_cur) {
+            const size_t row = (((size_t)k.layer * p.T.B + b) * p.T.nkv + g) * (size_t)p.T.C + (size_t)ch.P;
+            const uint32_t wk = __float_as_uint(ldb_dev(dev_rsrc(S.args.kc + row * D, D * 2), (lane / 2) * 4));
+            const uint32_t wv = __float_as_uint(ldb_dev(dev_rsrc(S.args.vc + row * D, D * 2), (lane / 2) * 4));
+            const float kcur = (lane & 1) ? bf16hi(wk) : bf16lo(wk), vcur = (lane & 1) ? bf16hi(wv) : bf16lo(wv);
+            const float sc = wave_sum(ldb_dev(qr, (h * D + lane) * 4) * kcur) * scale;
+            const float mn = fmaxf(Mx, sc);
+            const float corr = __expf(Mx - mn);
+            const float e = __expf(sc - mn);
+            Lt = Lt * corr + e;
+            o = fmaf(e, vcur, o * corr);
+            Mx = mn;
+        }
+        // partials (m, l, o) -> part[b][g][chunk][head][D + 2]
+        float* dst = p.part + ((((size_t)b * p.T.nkv + g) * p.T.attn_splits + k.row0) * G + h) * (D + 2);
+        if (lane == 0) {
+            stf_dev(dst, Mx);
+            stf_dev(dst + 1, Lt);
+        }
+        stf_dev(dst + 2 + lane, o);
+        if (p.T.B > 1) {
+            // several sequences: count this head's partial on the step's ticket of
+            // (sequence, group); the wave completing the count merges the chunks
+            vm_wait_all();
+            const int32_t fl = attn_fixed_len(p.T.B, p.T.C, p.T.attn_splits);
+            const uint32_t nch = (uint32_t)min(p.T.attn_splits, (ch.P + fl) / fl);
+            const uint32_t want = nch * (uint32_t)min(G, NCW);
+            uint32_t old = 0;
+            if (lane == 0)
+                old = addu_dev(&p.aticket[(((size_t)c.parity * p.T.L + k.layer) * p.T.B + b) * p.T.nkv + g], 1u);
+            old = uni(old);
+            if (old + 1u == want) merge_chunks(pp, k.layer, b, g, ch.P, lane);
+        }
+    }
+    return true;
+}
+
 // Merge of the attention partials of one KV group, O-proj K-slice, residual (atomic add).
 template <int KT>
 __device__ __noinline__ bool op_oproj(const Params* pp, uint32_t slot_, uint32_t page0, uint32_t t_, uint32_t epoch_) {
@@ -2062,12 +2280,18 @@ __device__ __noinline__ void compute(const Params* pp, uint32_t epoch, int wave)
                 case OP_ROUTE:
                 case OP_EGU: ok = MK_KT_DISPATCH_2K(op_gemv_bn, h, pp, slot, page0, t, epoch); break;
                 case OP_EDOWN: ok = MK_KT_DISPATCH_2K(op_gemv_br, p0.T.fe, pp, slot, page0, t, epoch); break;
-                case OP_ATTN: ok = hd == 64 ? op_attn<64>(pp, slot, page0, t, epoch) : op_attn<128>(pp, slot, page0, t, epoch); break;
+                case OP_ATTN: ok = attn_kswizzle(p0.T.d, p0.T.grp) ? op_attn_mfma(pp, slot, page0, t, epoch)
+                               : hd == 64 ? op_attn<64>(pp, slot, page0, t, epoch)
+                                          : op_attn<128>(pp, slot, page0, t, epoch);
+                break;
                 default: break;
             }
         } else switch (k.op) {
             case OP_QKV: ok = MK_KT_DISPATCH(op_qkv, h, pp, slot, page0, t, epoch); break;
-            case OP_ATTN: ok = hd == 64 ? op_attn<64>(pp, slot, page0, t, epoch) : op_attn<128>(pp, slot, page0, t, epoch); break;
+            case OP_ATTN: ok = attn_kswizzle(p0.T.d, p0.T.grp) ? op_attn_mfma(pp, slot, page0, t, epoch)
+                               : hd == 64 ? op_attn<64>(pp, slot, page0, t, epoch)
+                                          : op_attn<128>(pp, slot, page0, t, epoch);
+                break;
             case OP_OPROJ: ok = MK_KT_DISPATCH_2K(op_oproj, okt, pp, slot, page0, t, epoch); break;
             case OP_GATEUP: ok = MK_KT_DISPATCH(op_gateup, h, pp, slot, page0, t, epoch); break;
             case OP_DOWN: ok = MK_KT_DISPATCH_2K(op_down, dkt, pp, slot, page0, t, epoch); break;
