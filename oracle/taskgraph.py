@@ -200,10 +200,15 @@ def build(cfg, B, C, W, policy=0, attn_splits=0):
                         task(op=OP_QKV, layer=l, part=slot, row0=pb * P, nrows=P, seq=sg, wait_ev=ev_x,
                              sig_ev=ev_qkv[g], wbytes=wb, wofs=base + lay["qkv"] + tile * wb)
                         tile += 1
-        for b in range(B):
-            for g in range(nkv):
-                for c in range(S):
-                    task(op=OP_ATTN, layer=l, part=g, row0=c, nrows=grp, seq=b, wait_ev=ev_qkv[g], sig_ev=ev_attn[g])
+        # several sequences: chunk slots in the order 0, 1, .., S/2 - 1, S - 1, .., S/2 (outermost),
+        # so that round-robin queues pair slot c with slot S - 1 - c; one sequence: per group
+        if B > 1:
+            corder = list(range((S + 1) // 2)) + list(range(S - 1, (S + 1) // 2 - 1, -1))
+            attn = [(b, g, c) for c in corder for b in range(B) for g in range(nkv)]
+        else:
+            attn = [(0, g, c) for g in range(nkv) for c in range(S)]
+        for b, g, c in attn:
+            task(op=OP_ATTN, layer=l, part=g, row0=c, nrows=grp, seq=b, wait_ev=ev_qkv[g], sig_ev=ev_attn[g])
         wb = t["o_rows"] * grp * d * 2
         for sg in range(n_sg):
             for g in range(nkv):

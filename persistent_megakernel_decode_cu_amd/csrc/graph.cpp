@@ -17,6 +17,7 @@
 #include "graph.h"
 
 #include <algorithm>
+#include <array>
 #include <cstring>
 #include <numeric>
 
@@ -236,19 +237,34 @@ int build_graph(const Tiling& T, const Layout& Ly, int sched, int policy, Graph*
             }
         }
         // attention chunks per (sequence, KV group, chunk); with several sequences the
-        // last chunk of a (sequence, group) to finish also merges the chunks
-        for (int b = 0; b < T.B; ++b)
+        // last chunk of a (sequence, group) to finish also merges the chunks.  Several
+        // sequences: fixed-length chunk slots, of which the first is non-empty most often,
+        // so the slots go in chunk order 0, 1, .., S/2 - 1, then S - 1, S - 2, .., S/2: the
+        // round-robin queues, which give a workgroup tasks half a block apart, then pair
+        // slot c with slot S - 1 - c.  One sequence: chunks in order per group.
+        std::vector<int> corder;
+        for (int c = 0; c < (T.attn_splits + 1) / 2; ++c) corder.push_back(c);
+        for (int c = T.attn_splits - 1; c >= (T.attn_splits + 1) / 2; --c) corder.push_back(c);
+        std::vector<std::array<int, 3>> attn;  // (sequence, group, chunk)
+        if (T.B > 1) {
+            for (int c : corder)
+                for (int b = 0; b < T.B; ++b)
+                    for (int gi = 0; gi < T.nkv; ++gi) attn.push_back({b, gi, c});
+        } else {
             for (int gi = 0; gi < T.nkv; ++gi)
-                for (int c = 0; c < T.attn_splits; ++c) {
-                    Task k = blank(OP_ATTN, l);
-                    k.part = (uint16_t)gi;
-                    k.row0 = (uint32_t)c;
-                    k.nrows = (uint32_t)grp;
-                    k.seq = (uint32_t)b;
-                    k.wait_ev = ev_qkv[gi];
-                    k.sig_ev = ev_attn[gi];
-                    add(k);
-                }
+                for (int c = 0; c < T.attn_splits; ++c) attn.push_back({0, gi, c});
+        }
+        for (const auto& a : attn) {
+            const int b = a[0], gi = a[1], c = a[2];
+            Task k = blank(OP_ATTN, l);
+            k.part = (uint16_t)gi;
+            k.row0 = (uint32_t)c;
+            k.nrows = (uint32_t)grp;
+            k.seq = (uint32_t)b;
+            k.wait_ev = ev_qkv[gi];
+            k.sig_ev = ev_attn[gi];
+            add(k);
+        }
         // O-proj K slices: tile (group, row block)
         const int o_kt = grp * T.d;
         for (int sg = 0; sg < n_sg; ++sg)
