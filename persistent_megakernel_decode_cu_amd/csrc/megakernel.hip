@@ -1459,6 +1459,19 @@ __device__ __noinline__ bool op_attn_mfma(const Params* pp, uint32_t slot_, uint
     if (!await_inputs(pp, k, c)) return false;
     const int n = lane % 16, kq = lane / 16, hq = n % 4, part = n / 4;
     const __amdgpu_buffer_rsrc_t qr = dev_rsrc(p.q + (size_t)b * p.T.nq * D + (size_t)g * G * D, (uint32_t)(G * D * 4));
+    // for the merge (wave = head, lane = dimension): q and the current token's K and V,
+    // loaded now so that they arrive during the page loop
+    float qd = 0.f, kcur = 0.f, vcur = 0.f;
+    if (wave < G) {
+        qd = ldb_dev(qr, (wave * D + lane) * 4);
+        if (has_cur) {
+            const size_t row = (((size_t)k.layer * p.T.B + b) * p.T.nkv + g) * (size_t)p.T.C + (size_t)ch.P;
+            const uint32_t wk = __float_as_uint(ldb_dev(dev_rsrc(S.args.kc + row * D, D * 2), (lane / 2) * 4));
+            const uint32_t wv = __float_as_uint(ldb_dev(dev_rsrc(S.args.vc + row * D, D * 2), (lane / 2) * 4));
+            kcur = (lane & 1) ? bf16hi(wk) : bf16lo(wk);
+            vcur = (lane & 1) ? bf16hi(wv) : bf16lo(wv);
+        }
+    }
     // B operand of the scores: part `part` of q[head hq][32 ks + 8 kq .. +7]
     u32x4v qb[2];
 #pragma unroll
@@ -1578,11 +1591,7 @@ __device__ __noinline__ bool op_attn_mfma(const Params* pp, uint32_t slot_, uint
             o += a * rec[8 + h * D + lane];
         }
         if (has_cur) {
-            const size_t row = (((size_t)k.layer * p.T.B + b) * p.T.nkv + g) * (size_t)p.T.C + (size_t)ch.P;
-            const uint32_t wk = __float_as_uint(ldb_dev(dev_rsrc(S.args.kc + row * D, D * 2), (lane / 2) * 4));
-            const uint32_t wv = __float_as_uint(ldb_dev(dev_rsrc(S.args.vc + row * D, D * 2), (lane / 2) * 4));
-            const float kcur = (lane & 1) ? bf16hi(wk) : bf16lo(wk), vcur = (lane & 1) ? bf16hi(wv) : bf16lo(wv);
-            const float sc = wave_sum(ldb_dev(qr, (h * D + lane) * 4) * kcur) * scale;
+            const float sc = wave_sum(qd * kcur) * scale;
             const float mn = fmaxf(Mx, sc);
             const float corr = __expf(Mx - mn);
             const float e = __expf(sc - mn);
