@@ -14,7 +14,7 @@ launch, against the 8 TB/s HBM peak; measured HBM traffic from the committed
 counter profile when it matches the kernel source), the one-kernel-per-op HIP
 baseline on the same inputs, and the oracle's CPU time on a bounded sample.
 
-  python bench.py [--gpus 1] [--steps 256] [--warmup 10] [--sched static|dynamic]
+  python bench.py [--gpus 1] [--steps 256] [--warmup 10] [--sched static|dynamic|event]
   python bench.py --batch 16    (mixed-context batch workload, tokens/s; not the headline line)
   python bench.py --model moe   (64-expert top-8 MoE on the 1B attention shape, batch 16, context 2048)
 """
@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode µs/step (steps/s) at batch 1, Llama-1B shape; achieved HBM GB/s vs peak"
 HBM_PEAK_GBS = 8000.0
+SCHEDS = {"static": 0, "dynamic": 1, "event": 2}
 
 
 def step_bytes(cfg, positions):
@@ -199,7 +200,7 @@ def bench_batch(args, torch, synth, mk):
         raise SystemExit("steps exceed the KV cache")
     dev = {k: torch.from_numpy(v.view(np.int16)).cuda() for k, v in w.items()}
     model = mk.Model(cfg, dev)
-    opt = mk.options(sched=0 if args.sched == "static" else 1, policy=0 if args.policy == "rr" else 1,
+    opt = mk.options(sched=SCHEDS[args.sched], policy=0 if args.policy == "rr" else 1,
                      attn_splits=args.attn_splits, cooperative=1 if args.cooperative else 0)
     h = mk.mk_build_graph(model.desc, B, C, opt)
     del dev, model
@@ -285,7 +286,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--sched", choices=["static", "dynamic"], default="static")
+    ap.add_argument("--sched", choices=list(SCHEDS), default="static",
+                    help="static per-CU queues, dynamic global queue, or event-driven ready queue")
     ap.add_argument("--policy", choices=["rr", "lpt"], default="rr")
     ap.add_argument("--attn-splits", type=int, default=0)
     ap.add_argument("--cooperative", action="store_true", help="cooperative launch instead of the default plain one")
@@ -341,7 +343,7 @@ def main():
 
     dev = {k: torch.from_numpy(v.view(np.int16)).cuda() for k, v in w.items()}
     model = mk.Model(cfg, dev)
-    opt = mk.options(sched=0 if args.sched == "static" else 1, policy=0 if args.policy == "rr" else 1,
+    opt = mk.options(sched=SCHEDS[args.sched], policy=0 if args.policy == "rr" else 1,
                      attn_splits=args.attn_splits, cooperative=1 if args.cooperative else 0)
     h = mk.mk_build_graph(model.desc, 1, C, opt)
     graph = mk.parse_export(mk.mk_export_graph(h))

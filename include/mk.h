@@ -72,7 +72,9 @@ typedef struct {
 
 /* Build options; pass NULL for the defaults (all fields 0 / -1 as noted). */
 typedef struct {
-    int32_t sched;             /* 0 static per-CU queues (default), 1 dynamic global queue (atomic pop) */
+    int32_t sched;             /* 0 static per-CU queues (default), 1 dynamic global queue (atomic pop),
+                                * 2 event-driven: tasks taken from a global ready queue in the order their
+                                * events activated them (MPK news page, part 2); every event one counter */
     int32_t n_workgroups;      /* persistent workgroups; 0 = one per CU of the device */
     int32_t policy;            /* static assignment: 0 round-robin, 1 least-loaded (bytes) first */
     int32_t attn_splits;       /* KV chunks per (sequence, KV head); 0 = automatic */

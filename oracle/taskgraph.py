@@ -155,9 +155,10 @@ def layout(cfg, lm_rows, n_lm):
     return lay
 
 
-def build(cfg, B, C, W, policy=0, attn_splits=0):
+def build(cfg, B, C, W, policy=0, attn_splits=0, sched=0):
     """The task graph as a list of task dicts plus event targets, sub-counter
-    counts, static queues and the dynamic order."""
+    counts, static queues, the dynamic order and, for event-driven dispatch
+    (sched 2), the dependents of every event and the tasks that wait on none."""
     t = tiling(cfg, B, C, W, attn_splits)
     n_lm = -(-cfg.vocab // t["lm_rows"])
     lay = layout(cfg, t["lm_rows"], n_lm)
@@ -258,7 +259,9 @@ def build(cfg, B, C, W, policy=0, attn_splits=0):
             rows = min(t["lm_rows"], cfg.vocab - i * t["lm_rows"])
             task(op=OP_LMHEAD, layer=L, row0=i * t["lm_rows"], nrows=rows, seq=sg, wait_ev=ev_x,
                  wbytes=_round16(rows) * h * 2, wofs=lay["lm"] + i * t["lm_rows"] * h * 2)
-    nsub = [8 if n > 32 else 1 for n in target]
+    # events with many producers spread their counts over 8 sub-counters, except under
+    # event-driven dispatch, where one counter per event tells its last producer
+    nsub = [8 if n > 32 and sched != 2 else 1 for n in target]
     for k in tasks:
         k["wait_target"] = target[k["wait_ev"]] if k["wait_ev"] != NONE else 0
         k["wait_nsub"] = nsub[k["wait_ev"]] if k["wait_ev"] != NONE else 1
@@ -273,8 +276,13 @@ def build(cfg, B, C, W, policy=0, attn_splits=0):
             w = min(range(W), key=lambda j: (load[j], j))
             load[w] += k["wbytes"] + 8192
             queues[w].append(i)
+    cons = [[] for _ in target]
+    for k in tasks:
+        if k["wait_ev"] != NONE:
+            cons[k["wait_ev"]].append(k["id"])
+    init = [k["id"] for k in tasks if k["wait_ev"] == NONE]
     return dict(tiling=t, layout=lay, tasks=tasks, target=target, nsub=nsub, queues=queues,
-                order=list(range(len(tasks))))
+                order=list(range(len(tasks))), cons=cons, init=init)
 
 
 # ---- checker (properties every valid graph has) -----------------------------------------
@@ -473,24 +481,39 @@ def ancestor_sets(g):
     return lambda i: memo[tasks[i]["wait_ev"]] if tasks[i]["wait_ev"] != NONE else frozenset()
 
 
-def simulate(g, W, seed=0, slow=None, dynamic=False, lookahead=2):
+def simulate(g, W, seed=0, slow=None, dynamic=False, lookahead=2, event=False):
     """Runs the graph on W virtual workgroups under a seeded random interleaving.
 
     Static: each workgroup runs its queue in order.  Dynamic: a workgroup claims
     the next task of the global order whenever it holds fewer than `lookahead`
     claimed tasks (the loader claims ahead of the compute waves), and runs its
-    oldest claimed task.  A task may run once its event counter has reached its
-    target.  `slow`: a workgroup that only moves when no other one can.
-    Returns the number of tasks that ran (all of them unless the graph deadlocks).
+    oldest claimed task.  Event-driven: the same claims, but of the next slot of a
+    ready queue that starts with the tasks that wait on no event; when a task's count
+    completes an event, the event's dependents are appended to the queue, and a
+    claimed slot can run only once it is filled.  A task may run once its event
+    counter has reached its target.  `slow`: a workgroup that only moves when no
+    other one can.  Returns the number of tasks that ran (all of them unless the
+    graph deadlocks).
     """
     rng = np.random.default_rng(seed)
     tasks = g["tasks"]
     E = g["tiling"].get("E", 0)
     ctr = [0] * len(g["target"])
+    n = len(tasks)
+    if event:
+        dynamic = True
+        rq = list(g["init"])  # the ready queue: filled slots
+        if "cons" in g:
+            cons = g["cons"]
+        else:
+            cons = [[] for _ in g["target"]]
+            for k in tasks:
+                if k["wait_ev"] != NONE:
+                    cons[k["wait_ev"]].append(k["id"])
     if dynamic:
         order = list(g["order"])
         nxt = 0
-        held = [[] for _ in range(W)]
+        held = [[] for _ in range(W)]  # claimed slots (event) or task ids
     else:
         queues = [list(q) for q in g["queues"]]
         pos = [0] * W
@@ -498,7 +521,12 @@ def simulate(g, W, seed=0, slow=None, dynamic=False, lookahead=2):
 
     def head(w):
         if dynamic:
-            return held[w][0] if held[w] else None
+            if not held[w]:
+                return None
+            if event:
+                s = held[w][0]
+                return rq[s] if s < len(rq) else None
+            return held[w][0]
         return queues[w][pos[w]] if pos[w] < len(queues[w]) else None
 
     while True:
@@ -509,7 +537,7 @@ def simulate(g, W, seed=0, slow=None, dynamic=False, lookahead=2):
                 k = tasks[i]
                 if k["wait_ev"] == NONE or ctr[k["wait_ev"]] >= k["wait_target"]:
                     moves.append((w, "run"))
-            if dynamic and len(held[w]) < lookahead and nxt < len(order):
+            if dynamic and len(held[w]) < lookahead and nxt < n:
                 moves.append((w, "claim"))
         if not moves:
             break
@@ -519,17 +547,20 @@ def simulate(g, W, seed=0, slow=None, dynamic=False, lookahead=2):
                 moves = others
         w, what = moves[rng.integers(len(moves))]
         if what == "claim":
-            held[w].append(order[nxt])
+            held[w].append(nxt if event else order[nxt])
             nxt += 1
             continue
         if dynamic:
-            i = held[w].pop(0)
+            s = held[w].pop(0)
+            i = rq[s] if event else s
         else:
             i = queues[w][pos[w]]
             pos[w] += 1
         k = tasks[i]
         for ev in signals(k, E):
             ctr[ev] += 1
+            if event and ctr[ev] == g["target"][ev]:
+                rq.extend(cons[ev])
         done += 1
     return done
 

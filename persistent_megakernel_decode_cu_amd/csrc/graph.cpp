@@ -14,6 +14,15 @@
 // (koas-w.github.io notes, "static and dynamic scheduling").  Both queue kinds
 // are subsequences of one topological order, so the task that is lowest in
 // that order among the unfinished ones can always run: no deadlock.
+//
+// Event-driven dispatch follows the MPK runtime (MPK news page, part 2: a task
+// completes by counting its event; the event is activated when the count reaches
+// its threshold, and the scheduling unit then launches every task that depends on
+// it).  Here the task whose count activates an event appends the event's
+// dependents to one global ready queue, and workgroups take tasks from that queue
+// in the order they became ready.  The builder lists each event's dependents and
+// the tasks that depend on nothing; every event has one counter (the count that
+// activates it has to be seen by one producer).
 #include "graph.h"
 
 #include <algorithm>
@@ -375,7 +384,22 @@ int build_graph(const Tiling& T, const Layout& Ly, int sched, int policy, Graph*
         add(k);
     }
     // sub-counters: events with many producers spread their increments over 8 counters
-    for (size_t e = 0; e < g.target.size(); ++e) g.nsub[e] = g.target[e] > 32 ? 8 : 1;
+    // (event-driven dispatch: one counter per event)
+    for (size_t e = 0; e < g.target.size(); ++e) g.nsub[e] = sched != 2 && g.target[e] > 32 ? 8 : 1;
+    // dependents of every event, and the tasks that wait on none
+    g.cons_off.assign(g.target.size() + 1, 0);
+    g.cons.clear();
+    g.init.clear();
+    for (const auto& k : g.tasks)
+        if (k.wait_ev != NONE) ++g.cons_off[k.wait_ev + 1];
+        else g.init.push_back(k.id);
+    for (size_t e = 0; e < g.target.size(); ++e) g.cons_off[e + 1] += g.cons_off[e];
+    g.cons.resize(g.cons_off.back());
+    {
+        std::vector<uint32_t> fill(g.cons_off.begin(), g.cons_off.end() - 1);
+        for (const auto& k : g.tasks)
+            if (k.wait_ev != NONE) g.cons[fill[k.wait_ev]++] = k.id;
+    }
     for (auto& k : g.tasks) {
         if (k.wait_ev != NONE) {
             k.wait_target = g.target[k.wait_ev];

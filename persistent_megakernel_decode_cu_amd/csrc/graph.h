@@ -24,6 +24,9 @@ struct Graph {
     std::vector<uint32_t> nsub;     // sub-counters per event
     std::vector<uint32_t> queue_off, queue;  // static per-workgroup queues
     std::vector<uint32_t> order;    // dynamic queue (topological order)
+    // event-driven dispatch (sched 2): the tasks released by each event, in task order
+    // (cons[cons_off[e] .. cons_off[e + 1]]), and the tasks that wait on no event
+    std::vector<uint32_t> cons_off, cons, init;
     uint32_t new_event();
 };
 

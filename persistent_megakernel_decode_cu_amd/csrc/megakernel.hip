@@ -417,6 +417,48 @@ __device__ __forceinline__ void issue_page(CParams& p, const Task& k, uint32_t k
     }
 }
 
+// ---- event-driven dispatch --------------------------------------------------------------
+
+// Wait until slot `slot` of the ready queue has been filled in step `epoch`.
+__device__ __noinline__ bool wait_ready_slot(const Params* pp, uint32_t slot, uint32_t epoch) {
+    CParams& p = P(pp);
+    const uint64_t t0 = rtc();
+    for (uint32_t it = 1;; ++it) {
+        if (uni(ld_dev(&p.rq_stamp[slot])) == epoch) return true;
+        if (lds_ld(S.abort)) return false;
+        if ((it & 63u) == 0u) {
+            if (ld_dev(&p.state[ST_ABORT])) {
+                lds_st(S.abort, 1u);
+                return false;
+            }
+            if (rtc() - t0 > p.timeout) {
+                raise_error(pp, ERR_TIMEOUT_EVENT, NONE, NONE, slot, epoch);
+                return false;
+            }
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
+// The activated event ev launches its dependents: the whole wave appends them to the
+// ready queue (ids first, then, once those are stored, the step number of each slot).
+__device__ __noinline__ void launch_dependents(const Params* pp, uint32_t ev, uint32_t epoch, int lane) {
+    CParams& p = P(pp);
+    const uint32_t c0 = p.cons_off[ev], n = p.cons_off[ev + 1] - c0;
+    if (n == 0) return;
+    uint32_t base = 0;
+    if (lane == 0) base = addu_dev(&p.state[ST_TAIL], n);
+    base = uni(base) - (epoch - 1u) * (p.n_tasks - p.n_init) + p.n_init;
+    if (base < p.n_init || base + n > p.n_tasks) {  // an event activated twice in a step: never expected
+        if (lane == 0) raise_error(pp, ERR_TIMEOUT_EVENT, NONE, ev, base, p.n_tasks);
+        return;
+    }
+    for (uint32_t j = (uint32_t)lane; j < n; j += 64) st_dev(&p.rq[base + j], p.cons[c0 + j]);
+    vm_wait_all();
+    for (uint32_t j = (uint32_t)lane; j < n; j += 64) st_dev(&p.rq_stamp[base + j], epoch);
+    vm_wait_all();
+}
+
 typedef const __attribute__((address_space(4))) uint32_t c_u32;
 typedef const __attribute__((address_space(4))) Task c_task;
 
@@ -467,6 +509,11 @@ __device__ __noinline__ void loader(const Params* pp, uint32_t epoch, int lw) {
             const uint32_t rel = old - (epoch - 1u) * (n_tasks + W);
             end = rel >= n_tasks;
             ti = end ? NONE : rel;
+            if (sched == 2 && !end) {
+                // event-driven: slot rel of the ready queue, once a completed event has filled it
+                if (rel >= p.n_init && !wait_ready_slot(pp, rel, epoch)) break;
+                ti = uni(ld_dev(&p.rq[rel]));
+            }
             if (NLW > 1) {
                 if (lds_ld(S.dyn_ack) + DYNQ < t + 1 && !uni(lds_wait_ge(S.dyn_ack, t + 1 - DYNQ, pp, ti))) break;
                 if (lane == 0) lds_st(S.dyn_tid[t % DYNQ], ti);
@@ -2316,9 +2363,21 @@ __device__ __noinline__ void compute(const Params* pp, uint32_t epoch, int wave)
             if (!lds_wait_ge(S.done, NCW * (t + 1), pp, k.id)) return;
             CParams& p = P(pp);
             const int n_sig = (k.flags & TF_SIGRANGE) ? p0.T.E : 1;  // router tiles: every expert's event
+            bool activated = false;
             if (k.sig_ev != NONE && k.id != p.drop_task && c.lane < n_sig) {
+                const uint32_t ev = k.sig_ev + (uint32_t)c.lane;
                 const uint32_t sub = k.sig_nsub == 8 ? xcc_id() : 0u;
-                addu_dev(&p.ctr[ctr_index(k.sig_ev + (uint32_t)c.lane, sub)], 1u);
+                const uint32_t old = addu_dev(&p.ctr[ctr_index(ev, sub)], 1u);
+                // event-driven dispatch: the count that reaches the event's threshold activates it
+                activated = p.sched == 2 && old + 1u == epoch * p.ev_target[ev];
+            }
+            if (p.sched == 2) {
+                uint64_t act = __ballot(activated);
+                while (act) {
+                    const int l = __ffsll((unsigned long long)act) - 1;
+                    act &= act - 1;
+                    launch_dependents(pp, k.sig_ev + (uint32_t)l, epoch, c.lane);
+                }
             }
             if (k.op == OP_LMHEAD) finish_step(pp, epoch, c.parity);
             if (p.task_count && c.lane == 0) addu_dev(&p.task_count[k.id], 1u);

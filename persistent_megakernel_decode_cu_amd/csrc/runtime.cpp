@@ -75,7 +75,7 @@ mk_status plan(const mk_model_desc* desc, int32_t batch, int32_t max_ctx, const 
     memset(&o, 0, sizeof(o));
     o.debug_drop_signal = -1;
     if (opt) o = *opt;
-    if (o.sched < 0 || o.sched > 1 || o.policy < 0 || o.policy > 1) return MK_E_INVALID;
+    if (o.sched < 0 || o.sched > 2 || o.policy < 0 || o.policy > 1) return MK_E_INVALID;
     PlanOptions po;
     po.attn_splits = o.attn_splits;
     Tiling T;
@@ -213,6 +213,7 @@ mk_status rearm(mk_handle* h) {
     HIPCHK(hipMemcpy(p.state, st.data(), ST_WORDS * 4, hipMemcpyHostToDevice));
     HIPCHK(hipMemset(p.acc, 0, h->acc_bytes));
     if (p.aticket) HIPCHK(hipMemset(p.aticket, 0, (size_t)2 * T.L * T.B * T.nkv * 4));
+    if (p.rq_stamp) HIPCHK(hipMemset(p.rq_stamp, 0, h->g.tasks.size() * 4));
     HIPCHK(hipMemset(p.key, 0, sizeof(unsigned long long) * 2 * T.B));
     HIPCHK(hipMemset(p.ticket, 0, 4 * T.B));
     HIPCHK(hipDeviceSynchronize());
@@ -330,6 +331,28 @@ mk_status mk_build_graph(const mk_model_desc* desc, int32_t batch, int32_t max_c
     p.queue_off = qo;
     p.queue = qq;
     ALLOC(p.ctr, h->n_events * 8 * 32 * 4, true);
+    if (o.sched == 2) {
+        uint32_t *evt, *co, *cs, *rq;
+        ALLOC(evt, h->n_events * 4, false);
+        ALLOC(co, h->g.cons_off.size() * 4, false);
+        ALLOC(cs, std::max<size_t>(1, h->g.cons.size()) * 4, false);
+        ALLOC(rq, h->g.tasks.size() * 4, true);
+        ALLOC(p.rq_stamp, h->g.tasks.size() * 4, true);
+        p.ev_target = evt;
+        p.cons_off = co;
+        p.cons = cs;
+        p.rq = rq;
+        p.n_init = (uint32_t)h->g.init.size();
+        if (hipMemcpy(evt, h->g.target.data(), h->n_events * 4, hipMemcpyHostToDevice) != hipSuccess ||
+            hipMemcpy(co, h->g.cons_off.data(), h->g.cons_off.size() * 4, hipMemcpyHostToDevice) != hipSuccess ||
+            (!h->g.cons.empty() &&
+             hipMemcpy(cs, h->g.cons.data(), h->g.cons.size() * 4, hipMemcpyHostToDevice) != hipSuccess) ||
+            (!h->g.init.empty() &&
+             hipMemcpy(rq, h->g.init.data(), h->g.init.size() * 4, hipMemcpyHostToDevice) != hipSuccess)) {
+            mk_destroy(h);
+            return MK_E_HIP;
+        }
+    }
     ALLOC(p.state, ST_WORDS * 4, true);
     float2* rope;
     const int half = T.d / 2;

@@ -14,7 +14,8 @@ constexpr uint32_t ST_EXIT = 32;    // workgroups that finished (monotonic)
 constexpr uint32_t ST_HEAD = 64;    // dynamic queue head (monotonic)
 constexpr uint32_t ST_ABORT = 96;   // set when any wave gives up
 constexpr uint32_t ST_ERR = 128;    // error record: code, workgroup, task, event, seen, target
-constexpr uint32_t ST_WORDS = 160;
+constexpr uint32_t ST_TAIL = 160;   // event-driven dispatch: ready-queue slots reserved (monotonic)
+constexpr uint32_t ST_WORDS = 192;
 
 constexpr int TRACE_WORDS = 8;  // per task: workgroup, fetch, inputs ready, staged, computed, end, first page, last page held
 
@@ -35,7 +36,16 @@ struct Params {
     const uint32_t* queue_off;
     const uint32_t* queue;
     uint32_t n_tasks;
-    uint32_t sched;
+    uint32_t sched;           // 0 static queues, 1 dynamic (atomic pop), 2 event-driven
+    // event-driven dispatch: producers per event, each event's dependents (CSR), the ready
+    // queue [n_tasks] (the first n_init slots: the tasks that wait on no event, written once)
+    // and the step that filled each of its slots
+    const uint32_t* ev_target;
+    const uint32_t* cons_off;
+    const uint32_t* cons;
+    uint32_t* rq;
+    uint32_t* rq_stamp;
+    uint32_t n_init;
     uint32_t* ctr;            // event counters [n_events][8 sub-counters][32 words]
     uint32_t* state;          // control words
     const uint8_t* w;         // packed weights

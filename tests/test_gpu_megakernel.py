@@ -98,11 +98,15 @@ def test_tiny_greedy_chain_and_counters():
     assert got == ref["tokens"][:, 0].tolist(), (got, ref["tokens"][:, 0].tolist(), ref["gaps"][:, 0])
 
 
-def test_tiny_dynamic_queue_greedy():
+@pytest.mark.parametrize("sched", [1, 2], ids=["dynamic", "event"])
+def test_tiny_dynamic_queue_greedy(sched):
+    """Greedy chain with tasks taken from one global queue: in task order (1) or in the order their
+    events activated them (2, event-driven dispatch); every task runs once per step, counters = k x target."""
     cfg = synth.configs.TINY
     C, P0, steps = 512, 100, 16
     w, kc, vc, tok, pos = _setup(cfg, C, P0)
-    run = Runner(cfg, w, 1, C, kc, vc, sched=1, trace=1)
+    print(f"case tiny greedy sched={sched}", flush=True)
+    run = Runner(cfg, w, 1, C, kc, vc, sched=sched, trace=1)
     positions = torch.arange(P0, P0 + steps, dtype=torch.int32, device="cuda")
     t0 = torch.tensor(tok, dtype=torch.int32, device="cuda")
     nxt = mk.mk_next_tokens(run.h)
@@ -114,9 +118,20 @@ def test_tiny_dynamic_queue_greedy():
     run.check()
     counts = mk.mk_read_task_counts(run.h, len(run.graph["tasks"]))
     np.testing.assert_array_equal(counts, np.full(len(counts), steps, np.uint32))
+    ctr, epoch = mk.mk_read_counters(run.h, run.graph["header"]["n_events"])
+    assert epoch == steps
+    np.testing.assert_array_equal(ctr, run.graph["target"] * steps)
     run.close()
     ref = oracle.greedy(cfg, w, tok, [P0], kc.copy(), vc.copy(), steps)
     assert got == ref["tokens"][:, 0].tolist()
+
+
+@pytest.mark.parametrize("W", [1, 5, 37])
+def test_tiny_event_driven_few_workgroups(W):
+    ref, res, orig, refkv, gkv = _one_step(synth.configs.TINY, 512, 300, sched=2, n_workgroups=W)
+    print(res)
+    assert res["hidden_rel"] <= TOL_HIDDEN_REL and res["max_dlogit"] <= TOL_LOGIT_ABS and res["argmax_equal"]
+    _check_kv(orig, refkv, gkv, 300)
 
 
 def test_tiny_cooperative_launch_greedy():

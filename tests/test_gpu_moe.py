@@ -86,8 +86,9 @@ def test_tiny_moe_few_workgroups(W):
     _one_step(TINY_MOE, 3, 256, [7, 100, 255], n_workgroups=W)
 
 
-def test_tiny_moe_dynamic_queue():
-    _one_step(TINY_MOE, 4, 512, [50, 300, 11, 499], sched=1)
+@pytest.mark.parametrize("sched", [1, 2], ids=["dynamic", "event"])
+def test_tiny_moe_dynamic_queue(sched):
+    _one_step(TINY_MOE, 4, 512, [50, 300, 11, 499], sched=sched)
 
 
 def test_tiny_moe_greedy_chain_and_counters():

@@ -138,6 +138,8 @@ CASES = [
     (synth.configs.LLAMA_1B, 100, 8192, 0, 0, 0),
     (synth.configs.LLAMA_1B, 304, 4096, 0, 0, 5),
     (synth.configs.LLAMA_8B, 256, 4096, 0, 0, 0),
+    (synth.configs.TINY, 4, 512, 2, 0, 0),
+    (synth.configs.LLAMA_1B, 256, 2048, 2, 0, 0),
 ]
 
 
@@ -145,8 +147,9 @@ CASES = [
                          ids=[f"{c[0].name}-W{c[1]}-C{c[2]}-s{c[3]}-p{c[4]}-a{c[5]}" for c in CASES])
 def test_library_planner_equals_oracle_graph(cfg, W, C, sched, policy, splits):
     ex = plan(cfg, W, C=C, sched=sched, policy=policy, attn_splits=splits)
-    g = tg.build(cfg, 1, C, W, policy=policy, attn_splits=splits)
+    g = tg.build(cfg, 1, C, W, policy=policy, attn_splits=splits, sched=sched)
     compare(ex, g, cfg, W, C)
+    assert ex["header"]["sched"] == sched
     if cfg.n_layers <= 16:
         tg.check(g, cfg, 1)
 
@@ -177,6 +180,7 @@ def test_batched_planner_equals_oracle_graph(cfg, B, W, C, policy):
     n = len(g["tasks"])
     assert tg.simulate(g, W, seed=B) == n
     assert tg.simulate(g, W, seed=B + 1, dynamic=True) == n
+    assert tg.simulate(g, W, seed=B + 2, event=True) == n
 
 
 def test_batched_checker_catches_an_oproj_that_skips_attention():
@@ -305,3 +309,23 @@ def test_checker_catches_planted_routing_mistakes():
     k["nrows"] -= 1
     with pytest.raises(AssertionError, match="router logits"):
         tg.check(g, cfg, B)
+
+
+@pytest.mark.parametrize("cfg,B,W", [(synth.configs.TINY, 1, 1), (synth.configs.TINY, 1, 37),
+                                     (synth.configs.TINY, 5, 8), (synth.configs.TINY_MOE, 5, 8)],
+                         ids=["tiny-W1", "tiny-W37", "tiny-B5", "tiny-moe-B5"])
+def test_event_driven_dispatch_completes(cfg, B, W):
+    """Event-driven dispatch (tasks taken from a ready queue that each activated event extends with its
+    dependents): every task is released exactly once, and random and adversarial interleavings finish."""
+    g = tg.build(cfg, B, 512, W, sched=2)
+    n = len(g["tasks"])
+    released = sorted(g["init"] + [i for c in g["cons"] for i in c])
+    assert released == list(range(n))
+    assert all(n_ == 1 for n_ in g["nsub"])
+    for seed in range(3):
+        assert tg.simulate(g, W, seed=seed, event=True) == n
+    assert tg.simulate(g, W, seed=7, event=True, slow=0) == n
+    # an event whose count never completes (one producer's signal lost) stalls its dependents
+    k = next(k for k in g["tasks"] if k["op"] == tg.OP_QKV and k["layer"] == 1)
+    k["sig_ev"] = tg.NONE
+    assert tg.simulate(g, W, seed=1, event=True) < n
