@@ -1470,10 +1470,14 @@ __device__ __noinline__ bool op_attn(const Params* pp, uint32_t slot_, uint32_t 
 typedef short s16x4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ uint32_t split_part(float v, int part) {
-    uint32_t hi, mid, lo;
-    split3(v, hi, mid, lo);
-    return part == 0 ? hi : part == 1 ? mid : part == 2 ? lo : 0u;
+// Part `part` (0 hi, 1 mid, 2 lo, 3 zero) of the exact split of v, chosen with the lane's
+// masks pm[i] = 0xffff if part == i else 0 (no branches: part differs between lanes).
+__device__ __forceinline__ uint32_t split_part(float v, const uint32_t (&pm)[3]) {
+    const uint32_t uh = __float_as_uint(v) & 0xffff0000u;
+    const float r1 = v - __uint_as_float(uh);
+    const uint32_t um = __float_as_uint(r1) & 0xffff0000u;
+    const float r2 = r1 - __uint_as_float(um);
+    return ((uh >> 16) & pm[0]) | ((um >> 16) & pm[1]) | ((__float_as_uint(r2) >> 16) & pm[2]);
 }
 // sum over the four columns n, n +- 4, n +- 8 of a 16-lane row (the parts of one head)
 __device__ __forceinline__ float sum_parts(float v) {
@@ -1490,7 +1494,10 @@ __device__ __noinline__ bool op_attn_mfma(const Params* pp, uint32_t slot_, uint
     CParams& p = P(pp);
     const int lane = c.lane, wave = c.wave;
     const int b = (int)k.seq, g = k.part, G = p.T.grp;
-    const Chunk ch = attn_chunk(p.T.attn_splits, attn_fixed_len(p.T.B, p.T.C, p.T.attn_splits), S.pos[b], k.row0);
+    Chunk ch = attn_chunk(p.T.attn_splits, attn_fixed_len(p.T.B, p.T.C, p.T.attn_splits), S.pos[b], k.row0);
+    ch.c0 = (int32_t)uni((uint32_t)ch.c0);  // wave-uniform: scalar loop bounds and branches
+    ch.c1 = (int32_t)uni((uint32_t)ch.c1);
+    ch.P = (int32_t)uni((uint32_t)ch.P);
     const int32_t pre_end = min(ch.c1, ch.P);
     const int32_t npre = max(0, pre_end - ch.c0);
     const uint32_t npages = (uint32_t)((npre + PB - 1) / PB);
@@ -1505,6 +1512,7 @@ __device__ __noinline__ bool op_attn_mfma(const Params* pp, uint32_t slot_, uint
     }
     if (!await_inputs(pp, k, c)) return false;
     const int n = lane % 16, kq = lane / 16, hq = n % 4, part = n / 4;
+    const uint32_t pm[3] = {part == 0 ? 0xffffu : 0u, part == 1 ? 0xffffu : 0u, part == 2 ? 0xffffu : 0u};
     const __amdgpu_buffer_rsrc_t qr = dev_rsrc(p.q + (size_t)b * p.T.nq * D + (size_t)g * G * D, (uint32_t)(G * D * 4));
     // for the merge (wave = head, lane = dimension): q and the current token's K and V,
     // loaded now so that they arrive during the page loop
@@ -1530,10 +1538,10 @@ __device__ __noinline__ bool op_attn_mfma(const Params* pp, uint32_t slot_, uint
         const float qv[8] = {__uint_as_float(raw.x), __uint_as_float(raw.y), __uint_as_float(raw.z), __uint_as_float(raw.w),
                              __uint_as_float(raw2.x), __uint_as_float(raw2.y), __uint_as_float(raw2.z), __uint_as_float(raw2.w)};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) qb[ks][i] = split_part(qv[2 * i], part) | (split_part(qv[2 * i + 1], part) << 16);
+        for (int i = 0; i < 4; ++i) qb[ks][i] = split_part(qv[2 * i], pm) | (split_part(qv[2 * i + 1], pm) << 16);
     }
     tmark(c, 0);
-    f32x4v oacc[D / 16];  // O^T accumulators: rows d = 16 dg + 4 kq + r, column n
+    f32x4v oacc[D / 16];  // O^T accumulators: operand t, rows d = 16 kq + 4 r + t, column n
 #pragma unroll
     for (int dg = 0; dg < D / 16; ++dg) oacc[dg] = f32x4v{0.f, 0.f, 0.f, 0.f};
     float M = -INFINITY, L = 0.f;  // running max and this lane's sum (head hq, its positions)
@@ -1551,6 +1559,7 @@ __device__ __noinline__ bool op_attn_mfma(const Params* pp, uint32_t slot_, uint
             if ((uint32_t)i < nb) {
                 const uint32_t slot = (page0 + pb0 + i) % NPAGES;
                 const int32_t rows = min(PB, pre_end - (ch.c0 + (int32_t)(pb0 + i) * PB));
+                const int32_t lim = rows - 16 * wave - 4 * kq;  // this lane's valid positions: r < lim
                 f32x4v acc = f32x4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
@@ -1561,8 +1570,8 @@ __device__ __noinline__ bool op_attn_mfma(const Params* pp, uint32_t slot_, uint
                 }
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float v = sum_parts(acc[r]) * scale;
-                    if (16 * wave + 4 * kq + r < rows) sc[i][r] = v;
+                    // every lane takes part in the row sums; positions past the page's rows get -inf
+                    sc[i][r] = sum_parts(acc[r]) * scale + (r < lim ? 0.f : -INFINITY);
                     mx = fmaxf(mx, sc[i][r]);
                 }
             }
@@ -1589,17 +1598,23 @@ __device__ __noinline__ bool op_attn_mfma(const Params* pp, uint32_t slot_, uint
             }
             // B operand: part `part` of p at positions 4 kq + r (r = 0..3), head hq
             const s16x4v pbv = __builtin_bit_cast(
-                s16x4v, u32x2v{split_part(pr[0], part) | (split_part(pr[1], part) << 16),
-                               split_part(pr[2], part) | (split_part(pr[3], part) << 16)});
-            const uint16_t* vrow = (const uint16_t*)&ring[slot][8192] + (16 * wave + 4 * kq) * D;
+                s16x4v, u32x2v{split_part(pr[0], pm) | (split_part(pr[1], pm) << 16),
+                               split_part(pr[2], pm) | (split_part(pr[3], pm) << 16)});
+            // V of positions 4 kq + j (j = 0..3) of this wave's 16, dimensions 4 n .. 4 n + 3 (8 bytes
+            // each); A operand t is V^T with row n standing for dimension d = 4 n + t
+            const uint16_t* vrow = (const uint16_t*)&ring[slot][8192] + (16 * wave + 4 * kq) * D + 4 * n;
+            u32x2v vw[4];
 #pragma unroll
-            for (int dg = 0; dg < D / 16; ++dg) {
-                // A operand: V^T row d = 16 dg + n, positions 4 kq .. +3 of this wave's 16
-                const int d = 16 * dg + n;
-                const uint32_t v01 = (uint32_t)vrow[d] | ((uint32_t)vrow[D + d] << 16);
-                const uint32_t v23 = (uint32_t)vrow[2 * D + d] | ((uint32_t)vrow[3 * D + d] << 16);
-                oacc[dg] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4v, u32x2v{v01, v23}), pbv,
-                                                                      oacc[dg], 0, 0, 0);
+            for (int j = 0; j < 4; ++j) vw[j] = *(const u32x2v*)(vrow + j * D);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int c = t / 2;
+                const uint32_t a01 = (t & 1) ? (vw[0][c] >> 16) | (vw[1][c] & 0xffff0000u)
+                                             : (vw[0][c] & 0xffffu) | (vw[1][c] << 16);
+                const uint32_t a23 = (t & 1) ? (vw[2][c] >> 16) | (vw[3][c] & 0xffff0000u)
+                                             : (vw[2][c] & 0xffffu) | (vw[3][c] << 16);
+                oacc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4v, u32x2v{a01, a23}), pbv,
+                                                                     oacc[t], 0, 0, 0);
             }
         }
         for (uint32_t i = 0; i < nb; ++i) page_release(page0 + pb0 + i, lane);
@@ -1610,11 +1625,11 @@ __device__ __noinline__ bool op_attn_mfma(const Params* pp, uint32_t slot_, uint
     Lh += __shfl_xor(Lh, 16, 64);
     Lh += __shfl_xor(Lh, 32, 64);
 #pragma unroll
-    for (int dg = 0; dg < D / 16; ++dg)
+    for (int t = 0; t < D / 16; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const float o = sum_parts(oacc[dg][r]);
-            if (part == 0) mrec[8 + hq * D + 16 * dg + 4 * kq + r] = o;
+            const float o = sum_parts(oacc[t][r]);
+            if (part == 0) mrec[8 + hq * D + 16 * kq + 4 * r + t] = o;
         }
     if (part == 0 && kq == 0) {
         mrec[hq] = M;
