@@ -281,6 +281,25 @@ def bench_batch(args, torch, synth, mk):
     print(json.dumps(out), flush=True)
 
 
+def bench_micro(mk):
+    """The costs the megakernel trades against each other, measured on this GPU."""
+    us_stream, us_graph = mk.mkm_launch_latency(2000)
+    hop_x, xa, xb = mk.mkm_pingpong(20000, same_xcd=False)
+    hop_s, sa, sb = mk.mkm_pingpong(20000, same_xcd=True)
+    fill = {f"{n_wg}wg_depth{d}": round(mk.mkm_lds_fill(8 << 20 if n_wg > 1 else 64 << 20, n_wg, d), 1)
+            for n_wg in (1, 256) for d in (4, 8, 16)}
+    out = {
+        "metric": "microbenchmarks", "n_gpus": 1,
+        "empty_kernel_launch_us": {"stream": round(us_stream, 3), "hip_graph": round(us_graph, 3)},
+        "dependency_hop_ns": {"cross_xcd": round(hop_x, 1), "xcds": [xa, xb], "same_xcd": round(hop_s, 1),
+                              "same_xcds": [sa, sb]},
+        "workgroup_barrier_ns": round(mk.mkm_barrier(200000), 2),
+        "lds_fill_GBps": fill,
+        "stream_read_GBps": round(mk.mkm_stream_read(4 << 30), 1),
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -302,6 +321,9 @@ def main():
     ap.add_argument("--batch", type=int, default=1,
                     help="sequences per step; above 1: the mixed-context batch workload (contexts uniform in "
                          "[256, 4096], room for 4352), reported in tokens/s")
+    ap.add_argument("--micro", action="store_true",
+                    help="run the measurement microbenchmarks (launch latency, dependency hop, barrier, LDS fill, "
+                         "streaming read) and print their JSON line instead of the step benchmark")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the measured-traffic record from two rocprofv3 counter-collection CSVs and exit")
     args = ap.parse_args()
@@ -321,6 +343,8 @@ def main():
     import synth
     import persistent_megakernel_decode_cu_amd as mk
 
+    if args.micro:
+        return bench_micro(mk)
     if args.model == "8b" and args.batch > 1:
         raise SystemExit("the batch workload runs on the 1B shape or the MoE only")
     if args.model == "moe" and args.batch == 1:
@@ -386,7 +410,8 @@ def main():
         mk.mk_decode_step(h, tptr, positions[s_:s_ + 1].data_ptr(), kv.data_ptr(), logits.data_ptr(), sp)
         ev[s_][1].record(stream)
     torch.cuda.synchronize()
-    ms_launch = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    launch_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    ms_launch = float(np.mean(launch_ms))
     err = mk.mk_check_device_error(h)
     if err:
         raise SystemExit(f"device error: {err}")
@@ -419,9 +444,15 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_step": int(bytes_mean), "kernel_us_per_launch": round(ms_launch * 1000, 2),
-                     "throughput_GBps_incl_launch_gaps": round(bytes_mean / (ms * 1e-3) / 1e9, 1)},
+                     "throughput_GBps_incl_launch_gaps": round(bytes_mean / (ms * 1e-3) / 1e9, 1),
+                     "kernel_us_p10_median_p90": [round(float(np.percentile(launch_ms, q)) * 1000, 2)
+                                                  for q in (10, 50, 90)]},
     }
     mk.mk_destroy(h)
+    # context: the practical read ceiling of this GPU (a plain 4 GiB streaming read)
+    read_peak = mk.mkm_stream_read(4 << 30)
+    out["roofline"]["measured_read_peak_GBps"] = round(read_peak, 1)
+    out["roofline"]["frac_of_measured_read_peak"] = round(achieved / read_peak, 4)
 
     if args.copy_calibration:
         n = 256 << 20

@@ -196,6 +196,37 @@ const int32_t *mkb_next_tokens(const mkb_handle *h); /* (dev) int32 [1] */
 const float *mkb_hidden_out(const mkb_handle *h);    /* (dev) float [hidden] */
 void mkb_destroy(mkb_handle *h);
 
+/* ---- Measurement microbenchmarks ----------------------------------------------
+ * The costs the megakernel trades against each other, each measured on the current
+ * device with its own allocations (freed before returning).  All are synchronous.
+ * Errors: MK_E_INVALID for arguments outside the stated ranges, MK_E_HIP for a
+ * failing HIP call, MK_E_DEVICE if a wait in the kernel gave up. */
+
+/* Launch cost of an empty kernel: n (1..100000) launches on a new stream, then the
+ * same n captured in one HIP graph and replayed; microseconds per kernel of each
+ * (Hazy Research megakernel news page, section 3: per-kernel launch overhead). */
+mk_status mkm_launch_latency(int32_t n, float *us_stream, float *us_graph);
+
+/* One dependency hop between two workgroups: a counter passed back and forth
+ * `rounds` times (1..10^6) through device memory with device-scope stores and
+ * loads, as the megakernel's events are; nanoseconds per one-way hop.  same_xcd:
+ * 0 = the workgroups sit on different XCDs, 1 = on the same one; the XCD ids
+ * the two workgroups ran on are returned (Hazy Research megakernel news page,
+ * section 4: the cost of one synchronisation through global memory). */
+mk_status mkm_pingpong(int32_t rounds, int32_t same_xcd, float *ns_per_hop, int32_t *xcd_a, int32_t *xcd_b);
+
+/* Nanoseconds per workgroup barrier of 384 threads, over n (1..10^7) barriers. */
+mk_status mkm_barrier(int32_t n, float *ns_per_barrier);
+
+/* LDS fill rate: n_wg (1..4096) workgroups each stream bytes_per_wg (a multiple of
+ * 4096, at least 64 KiB) from device memory into LDS with direct 16-byte
+ * global-to-LDS loads, depth (4, 8 or 16) loads in flight per wave; GB/s over all. */
+mk_status mkm_lds_fill(uint64_t bytes_per_wg, int32_t n_wg, int32_t depth, float *gbps);
+
+/* Plain streaming read of `bytes` (a multiple of 16, at least 1 MiB) of device
+ * memory by the whole device; GB/s. */
+mk_status mkm_stream_read(uint64_t bytes, float *gbps);
+
 #ifdef __cplusplus
 }
 #endif

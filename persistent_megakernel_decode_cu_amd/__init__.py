@@ -113,6 +113,15 @@ def load():
         getattr(lib, n).restype = _P
     lib.mkb_destroy.argtypes = [_P]
     lib.mkb_destroy.restype = None
+    _F = ctypes.POINTER(ctypes.c_float)
+    _I = ctypes.POINTER(ctypes.c_int32)
+    lib.mkm_launch_latency.argtypes = [ctypes.c_int32, _F, _F]
+    lib.mkm_pingpong.argtypes = [ctypes.c_int32, ctypes.c_int32, _F, _I, _I]
+    lib.mkm_barrier.argtypes = [ctypes.c_int32, _F]
+    lib.mkm_lds_fill.argtypes = [ctypes.c_uint64, ctypes.c_int32, ctypes.c_int32, _F]
+    lib.mkm_stream_read.argtypes = [ctypes.c_uint64, _F]
+    for n in ("mkm_launch_latency", "mkm_pingpong", "mkm_barrier", "mkm_lds_fill", "mkm_stream_read"):
+        getattr(lib, n).restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -300,3 +309,41 @@ class Model:
                               weights["tok_embed"].data_ptr(),
                               0 if cfg.tied else weights["lm_head"].data_ptr(),
                               weights["final_norm"].data_ptr(), self.layers)
+
+
+# ---- measurement microbenchmarks (synchronous; each allocates and frees its own buffers) ----
+
+def mkm_launch_latency(n=2000):
+    """(us per empty kernel launched on a stream, us per kernel replayed from a HIP graph)."""
+    a, b = ctypes.c_float(), ctypes.c_float()
+    _check(load().mkm_launch_latency(n, ctypes.byref(a), ctypes.byref(b)), "mkm_launch_latency")
+    return a.value, b.value
+
+
+def mkm_pingpong(rounds=20000, same_xcd=False):
+    """(ns per one-way hop between two workgroups through device memory, XCD of each workgroup)."""
+    ns, xa, xb = ctypes.c_float(), ctypes.c_int32(), ctypes.c_int32()
+    _check(load().mkm_pingpong(rounds, 1 if same_xcd else 0, ctypes.byref(ns), ctypes.byref(xa), ctypes.byref(xb)),
+           "mkm_pingpong")
+    return ns.value, xa.value, xb.value
+
+
+def mkm_barrier(n=100000):
+    """ns per workgroup barrier of 384 threads."""
+    ns = ctypes.c_float()
+    _check(load().mkm_barrier(n, ctypes.byref(ns)), "mkm_barrier")
+    return ns.value
+
+
+def mkm_lds_fill(bytes_per_wg=8 << 20, n_wg=256, depth=8):
+    """GB/s of n_wg workgroups streaming bytes_per_wg each from device memory straight into LDS."""
+    g = ctypes.c_float()
+    _check(load().mkm_lds_fill(bytes_per_wg, n_wg, depth, ctypes.byref(g)), "mkm_lds_fill")
+    return g.value
+
+
+def mkm_stream_read(nbytes=4 << 30):
+    """GB/s of a plain streaming read of nbytes of device memory."""
+    g = ctypes.c_float()
+    _check(load().mkm_stream_read(nbytes, ctypes.byref(g)), "mkm_stream_read")
+    return g.value
