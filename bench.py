@@ -114,8 +114,21 @@ def cpu_baseline(cfg, w, kc, vc, tok, P0, budget_s=10.0):
         if time.perf_counter() - t0 > budget_s and n >= 2:
             break
     dt = time.perf_counter() - t0
-    return dict(value=n / dt, unit="steps/s", cores=threads, kind="oracle",
-                sample=f"{n} greedy decode steps of the same workload from position {P0} ({dt:.1f} s)"), first
+    out = dict(value=n / dt, unit="steps/s", cores=threads, kind="oracle",
+               sample=f"{n} greedy decode steps of the same workload from position {P0} ({dt:.1f} s)")
+    # the same oracle on one thread: one step (OpenMP's thread count set through its runtime)
+    try:
+        import ctypes
+        gomp = ctypes.CDLL("libgomp.so.1")
+        gomp.omp_set_num_threads(1)
+        t1 = time.perf_counter()
+        oracle.decode_step(cfg, w, t, [P0 + n], k2, v2)
+        out["single_thread"] = {"value": 1.0 / (time.perf_counter() - t1), "unit": "steps/s", "cores": 1,
+                                "sample": "1 decode step"}
+        gomp.omp_set_num_threads(threads)
+    except OSError:
+        pass
+    return out, first
 
 
 def baseline_leg(mk, torch, cfg, model, kc, vc, tok, P0, C, K, W, mk_ms):
