@@ -348,8 +348,8 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU only; multi-GPU runs are not part of this "
-                                   "build (see DESIGN.md for how the path would shard)", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "this benchmark runs on one GPU only (--gpus 1): the megakernel has no "
+                                   "multi-GPU sharding", "n_gpus": args.gpus}))
         sys.exit(2)
 
     import torch
