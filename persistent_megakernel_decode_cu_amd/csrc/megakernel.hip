@@ -1461,9 +1461,9 @@ __device__ __noinline__ bool op_attn(const Params* pp, uint32_t slot_, uint32_t 
 // operand (one 16-byte chunk of a row per lane) and the query in
 // the B operand split exactly into three bf16 parts, column n holding part n / 4 of head
 // n % 4 (part 3 zero): summing a row's columns of one head gives the fp32-exact dot
-// product.  The output layout puts, in lane (n, kq), the scores of positions 4 kq .. +3
+// product.  The probabilities (in [0, 1]) go in as two parts, within 2^-16 of them.  The output layout puts, in lane (n, kq), the scores of positions 4 kq .. +3
 // for head n % 4 -- exactly the positions and head whose probabilities that lane feeds to
-// O^T += V^T P^T (v_mfma_f32_16x16x16_bf16, P split the same way), so the probabilities
+// O^T += V^T P^T (v_mfma_f32_16x16x16_bf16), so the probabilities
 // never move between lanes.  Each wave keeps its own running max, sum and output per head;
 // the four are merged through LDS at the end, together with the current token's K/V.
 // The page's K rows are row-major with 16-byte chunk c of row r stored at chunk c ^ (r % 8).
@@ -1478,6 +1478,14 @@ __device__ __forceinline__ uint32_t split_part(float v, const uint32_t (&pm)[3])
     const uint32_t um = __float_as_uint(r1) & 0xffff0000u;
     const float r2 = r1 - __uint_as_float(um);
     return ((uh >> 16) & pm[0]) | ((um >> 16) & pm[1]) | ((__float_as_uint(r2) >> 16) & pm[2]);
+}
+// Part `part` of a two-part split of v in [0, 1]: hi = v truncated to bf16, lo = the
+// remainder rounded to nearest even (v - hi - lo within 2^-16 of v); part 2 and 3 zero.
+__device__ __forceinline__ uint32_t split_part2(float v, const uint32_t (&pm)[3]) {
+    const uint32_t uh = __float_as_uint(v) & 0xffff0000u;
+    const uint32_t r = __float_as_uint(v - __uint_as_float(uh));
+    const uint32_t lo = (r + 0x7fffu + ((r >> 16) & 1u)) >> 16;
+    return ((uh >> 16) & pm[0]) | (lo & pm[1]);
 }
 // sum over the four columns n, n +- 4, n +- 8 of a 16-lane row (the parts of one head)
 __device__ __forceinline__ float sum_parts(float v) {
@@ -1598,8 +1606,8 @@ __device__ __noinline__ bool op_attn_mfma(const Params* pp, uint32_t slot_, uint
             }
             // B operand: part `part` of p at positions 4 kq + r (r = 0..3), head hq
             const s16x4v pbv = __builtin_bit_cast(
-                s16x4v, u32x2v{split_part(pr[0], pm) | (split_part(pr[1], pm) << 16),
-                               split_part(pr[2], pm) | (split_part(pr[3], pm) << 16)});
+                s16x4v, u32x2v{split_part2(pr[0], pm) | (split_part2(pr[1], pm) << 16),
+                               split_part2(pr[2], pm) | (split_part2(pr[3], pm) << 16)});
             // V of positions 4 kq + j (j = 0..3) of this wave's 16, dimensions 4 n .. 4 n + 3 (8 bytes
             // each); A operand t is V^T with row n standing for dimension d = 4 n + t
             const uint16_t* vrow = (const uint16_t*)&ring[slot][8192] + (16 * wave + 4 * kq) * D + 4 * n;
