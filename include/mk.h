@@ -179,21 +179,29 @@ const char *mk_status_str(mk_status s);
  * RMSNorm, LM head, argmax), for comparison: the execution model the Hazy
  * Research megakernel news page (section 3) contrasts the megakernel with.
  * Same inputs, layouts and arithmetic as the megakernel; reads the caller's
- * weights in place (no copy), so they must outlive the handle.  batch must be 1;
- * hidden, n_q*head_dim and ffn_dim must be powers of two in [512, 8192]. */
+ * weights in place (no copy), so they must outlive the handle.  batch 1..32,
+ * dense models only, n_q_heads / n_kv_heads <= 8.  batch 1: hidden,
+ * n_q*head_dim and ffn_dim must be powers of two in [512, 8192] (vector-ALU
+ * GEMVs).  batch > 1: the projections run on the matrix cores with each fp32
+ * activation carried as two bf16 parts, K cut into slices whose partial sums the
+ * consuming kernel adds; hidden, n_q*head_dim and ffn_dim must be multiples of
+ * 256, every projection's row count a multiple of 16, and of 64 where a stacked
+ * projection (Q/K/V, gate/up, LM head) has 8192 rows or more.  The KV cache,
+ * tokens, positions and logits are laid out as for mk_decode_step. */
 typedef struct mkb_handle mkb_handle;
 
 mk_status mkb_create(const mk_model_desc *desc, int32_t batch, int32_t max_ctx, mkb_handle **out);
 
-/* Enqueues the step's kernels on `stream`.  tokens/positions (dev) int32 [1]:
+/* Enqueues the step's kernels on `stream`.  tokens/positions (dev) int32 [batch]:
  * as for mk_decode_step.  When advance != 0 the last kernel also stores the
- * next token into tokens[0] and increments positions[0], so a graph captured
- * from one call can be replayed for consecutive greedy steps. */
+ * next tokens into tokens[] and increments every positions[b], so a graph
+ * captured from one call can be replayed for consecutive greedy steps. */
 mk_status mkb_decode_step(mkb_handle *h, int32_t *tokens, int32_t *positions, void *kv_cache, float *logits,
                           void *stream, int32_t advance);
 
-const int32_t *mkb_next_tokens(const mkb_handle *h); /* (dev) int32 [1] */
-const float *mkb_hidden_out(const mkb_handle *h);    /* (dev) float [hidden] */
+const int32_t *mkb_next_tokens(const mkb_handle *h); /* (dev) int32 [batch] */
+const float *mkb_hidden_out(const mkb_handle *h);    /* (dev) float [batch][hidden] */
+int32_t mkb_launches_per_step(const mkb_handle *h);  /* kernels the last mkb_decode_step enqueued (0 before any) */
 void mkb_destroy(mkb_handle *h);
 
 /* ---- Measurement microbenchmarks ----------------------------------------------

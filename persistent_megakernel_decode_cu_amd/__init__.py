@@ -111,6 +111,8 @@ def load():
     for n in ("mkb_next_tokens", "mkb_hidden_out"):
         getattr(lib, n).argtypes = [_P]
         getattr(lib, n).restype = _P
+    lib.mkb_launches_per_step.argtypes = [_P]
+    lib.mkb_launches_per_step.restype = ctypes.c_int32
     lib.mkb_destroy.argtypes = [_P]
     lib.mkb_destroy.restype = None
     _F = ctypes.POINTER(ctypes.c_float)
@@ -247,6 +249,10 @@ def mkb_next_tokens(h):
 
 def mkb_hidden_out(h):
     return load().mkb_hidden_out(h)
+
+
+def mkb_launches_per_step(h):
+    return int(load().mkb_launches_per_step(h))
 
 
 def mkb_destroy(h):
