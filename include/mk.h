@@ -77,7 +77,7 @@ typedef struct {
                                 * events activated them (MPK news page, part 2); every event one counter */
     int32_t n_workgroups;      /* persistent workgroups; 0 = one per CU of the device */
     int32_t policy;            /* static assignment: 0 round-robin, 1 least-loaded (bytes) first */
-    int32_t attn_splits;       /* KV chunks per (sequence, KV head); 0 = automatic */
+    int32_t attn_splits;       /* KV chunks per (sequence, KV head), at most 16; 0 = automatic */
     int32_t debug_timeout_ms;  /* bound on every in-kernel wait; 0 = 2000 ms */
     int32_t debug_drop_signal; /* >= 0: the task with this index skips its signal (tests); -1 = off */
     int32_t trace;             /* 1: record per-task timestamps (mk_read_trace) */

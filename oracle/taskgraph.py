@@ -27,11 +27,11 @@ The tiling rules (written from the design, not from the C++ code):
     last chunk task of a (sequence, KV group) to finish merges the chunks for
     the O-projection, which therefore waits on the same event as at batch 1.
   * O-proj tiles: (KV group g, row block) over columns g*grp*d .. +grp*d, with
-    o_rows = min(h, 1024 // min(B, 16), max(16, pow2_floor(h * n_kv / W))).
+    o_rows = min(h, R, max(16, pow2_floor(h * n_kv / W))), R = pow2_floor(1024 // min(B, 16)).
   * down tiles: (K block of kd = min(1024, f) columns, row block of
-    d_rows = min(h, 1024 // min(B, 16), max(16, pow2_floor(h * (f / kd) / W))) rows).
+    d_rows = min(h, R, max(16, pow2_floor(h * (f / kd) / W))) rows).
   * gate/up tiles: g_rows gate rows then the same g_rows up rows, with
-    g_rows = min(kd, (1024 // min(B, 16)) // 2, max(8, pow2_ceil(ceil(f / W)))).
+    g_rows = min(kd, R // 2, max(8, pow2_ceil(ceil(f / W)))).
   * LM head tiles: lm_rows = min(1024, ceil(V / W) rounded up to 16) rows, the
     last one shorter; its weight bytes are its rows rounded up to 16.  (With
     several sequences a workgroup takes an LM tile in chunks of
@@ -105,7 +105,7 @@ def tiling(cfg, B, C, W, attn_splits=0):
         # positions, so that long and short contexts split into equal-sized work
         S = max(1, min(16, -(-C // 256))) if B == 1 else max(1, min(16, C // 1024))
     S = min(S, C)
-    max_rows = 1024 // min(B, 16)  # rows x sequences (of one column group) of a tile
+    max_rows = _pow2_floor(1024 // min(B, 16))  # rows x sequences (of one column group) of a tile
     E = cfg.n_experts
     if E:  # mixture of experts: about one expert gate/up tile and one expert down tile per workgroup
         fe = cfg.expert_ffn

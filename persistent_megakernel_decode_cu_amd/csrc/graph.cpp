@@ -85,6 +85,7 @@ int plan_tiling(const Dims& dm, int B, int C, int W, const PlanOptions& o, Tilin
     T.qkv_pairs = 8;
     T.n_qkv_tiles = (dm.nq + 2 * dm.nkv) * (dm.d / 2) / T.qkv_pairs;
     int S = o.attn_splits;
+    if (S > 16) return fail("attn_splits must be at most 16 (the merge reads up to 16 chunk partials)");
     if (S <= 0) {
         // batch 1: 256-position chunks of the one context; batch > 1: slots of
         // ceil(C / S) >= 1024 positions (fewer, longer attention tasks: each one
@@ -95,8 +96,9 @@ int plan_tiling(const Dims& dm, int B, int C, int W, const PlanOptions& o, Tilin
     if (S > C) S = C;
     T.attn_splits = S;
     T.n_attn_tiles = B * dm.nkv * S;
-    // rows x sequences (of one column group) of a tile fit the LDS row-result buffer
-    const int64_t max_rows = MAX_TILE_ROWS / std::min<int64_t>(B, GROUP_SEQS);
+    // rows x sequences (of one column group) of a tile fit the LDS row-result buffer;
+    // a power of two, so that every tile height derived from it divides its matrix
+    const int64_t max_rows = pow2_floor(MAX_TILE_ROWS / std::min<int64_t>(B, GROUP_SEQS));
     // O-proj: tiles (KV group g, rows) with K = grp*d columns; about W tiles per layer
     T.o_rows = (int)std::min<int64_t>(std::min<int64_t>(dm.h, max_rows),
                                       std::max<int64_t>(16, pow2_floor((int64_t)dm.h * dm.nkv / W)));

@@ -81,6 +81,11 @@ def test_tiny_batch_few_workgroups(W):
     _one_step(TINY, 4, 256, [3, 200, 64, 255], n_workgroups=W)
 
 
+def test_tiny_batch_of_three_on_four_workgroups():
+    # row bound 1024 // 3 is not a power of two: tile heights come from its power-of-two floor
+    _one_step(TINY, 3, 256, [3, 200, 64], n_workgroups=4)
+
+
 @pytest.mark.parametrize("splits", [3, 7])
 def test_tiny_batch_attention_chunk_slots(splits):
     # fixed-length chunk slots of ceil(512 / splits) positions: short contexts leave

@@ -156,6 +156,10 @@ def test_library_planner_equals_oracle_graph(cfg, W, C, sched, policy, splits):
 
 BATCH_CASES = [
     (synth.configs.TINY, 3, 37, 512, 0),
+    # batches whose row bound 1024 // B is not a power of two, with few workgroups
+    # (tile heights then come from the bound)
+    (synth.configs.TINY, 3, 4, 512, 0),
+    (synth.configs.LLAMA_1B, 6, 32, 2048, 0),
     (synth.configs.TINY, 16, 256, 512, 1),
     (synth.configs.LLAMA_1B, 16, 256, 4352, 0),
     (synth.configs.LLAMA_1B, 4, 256, 2048, 1),
@@ -209,6 +213,9 @@ def test_planner_rejects_what_it_does_not_implement():
         plan(cfg.with_(hidden=8192), 4)
     with pytest.raises(mk.MkError):
         plan(cfg.with_(hidden=64), 4)
+    with pytest.raises(mk.MkError):  # the merges read at most 16 chunk partials
+        plan(cfg, 16, B=3, attn_splits=17)
+    assert plan(cfg, 16, B=3, attn_splits=16)["header"]["attn_splits"] == 16
 
 
 @pytest.mark.parametrize("W", [1, 3, 16, 37])
