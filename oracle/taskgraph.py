@@ -21,8 +21,8 @@ The tiling rules (written from the design, not from the C++ code):
     halves) of one head; heads ordered by KV group: the group's query heads,
     its key head, its value head; pair blocks in order.
   * attention: attn_splits chunks per (sequence, KV group), default
-    clamp(ceil(max_ctx / 256), 1, 16) at batch 1 and clamp(floor(max_ctx /
-    1024), 1, 16) for batch > 1, at most max_ctx.  With several sequences the chunks
+    clamp(ceil(max_ctx / 256), 1, 16) at batch 1 and clamp(pow2_floor(W /
+    (B n_kv)), 1, 8) for batch > 1, at most max_ctx.  With several sequences the chunks
     are slots of a fixed length (so a short context leaves some empty) and the
     last chunk task of a (sequence, KV group) to finish merges the chunks for
     the O-projection, which therefore waits on the same event as at batch 1.
@@ -101,9 +101,9 @@ def tiling(cfg, B, C, W, attn_splits=0):
     if attn_splits > 0:
         S = attn_splits
     else:
-        # batch 1: 256-position chunks; batch > 1: chunk slots of ceil(C / S) >= 1024
-        # positions, so that long and short contexts split into equal-sized work
-        S = max(1, min(16, -(-C // 256))) if B == 1 else max(1, min(16, C // 1024))
+        # batch 1: 256-position chunks; batch > 1: about one attention task per
+        # workgroup and layer over all sequences and KV groups, at most 8 slots
+        S = max(1, min(16, -(-C // 256))) if B == 1 else max(1, min(8, _pow2_floor(max(1, W // (B * nkv)))))
     S = min(S, C)
     max_rows = _pow2_floor(1024 // min(B, 16))  # rows x sequences (of one column group) of a tile
     E = cfg.n_experts

@@ -87,11 +87,13 @@ int plan_tiling(const Dims& dm, int B, int C, int W, const PlanOptions& o, Tilin
     int S = o.attn_splits;
     if (S > 16) return fail("attn_splits must be at most 16 (the merge reads up to 16 chunk partials)");
     if (S <= 0) {
-        // batch 1: 256-position chunks of the one context; batch > 1: slots of
-        // ceil(C / S) >= 1024 positions (fewer, longer attention tasks: each one
-        // carries a fixed cost of a few microseconds)
+        // batch 1: 256-position chunks of the one context; batch > 1: about one
+        // attention task per workgroup and layer over all sequences and KV groups, at
+        // most 8 slots (each task carries a fixed cost of a few microseconds, so more,
+        // shorter slots measured slower)
         S = B == 1 ? (int)std::max<int64_t>(1, std::min<int64_t>(16, (C + 255) / 256))
-                   : (int)std::max<int64_t>(1, std::min<int64_t>(16, C / 1024));
+                   : (int)std::max<int64_t>(1, std::min<int64_t>(8, pow2_floor(std::max<int64_t>(
+                                                                     1, (int64_t)W / ((int64_t)B * dm.nkv)))));
     }
     if (S > C) S = C;
     T.attn_splits = S;
