@@ -15,7 +15,8 @@ counter profile when it matches the kernel source), the one-kernel-per-op HIP
 baseline on the same inputs, and the oracle's CPU time on a bounded sample.
 
   python bench.py [--gpus 1] [--steps 256] [--warmup 10] [--sched static|dynamic|event]
-  python bench.py --batch 16    (mixed-context batch workload, tokens/s; not the headline line)
+  python bench.py --batch 16    (mixed-context batch workload, tokens/s, with the one-kernel-per-op baseline
+                                on the same inputs beside it; not the headline line)
   python bench.py --model moe   (64-expert top-8 MoE on the 1B attention shape, batch 16, context 2048)
 """
 import argparse
