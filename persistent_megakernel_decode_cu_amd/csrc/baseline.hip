@@ -455,7 +455,7 @@ __global__ void __launch_bounds__(256) k_argmax1(const float* v, int n, float* b
     si[threadIdx.x] = idx;
     __syncthreads();
     for (int s = 128; s > 0; s >>= 1) {
-        if (threadIdx.x < s) better(sv[threadIdx.x], si[threadIdx.x], sv[threadIdx.x + s], si[threadIdx.x + s]);
+        if ((int)threadIdx.x < s) better(sv[threadIdx.x], si[threadIdx.x], sv[threadIdx.x + s], si[threadIdx.x + s]);
         __syncthreads();
     }
     if (threadIdx.x == 0) {
@@ -613,7 +613,7 @@ mk_status mkb_create(const mk_model_desc* d, int32_t batch, int32_t max_ctx, mkb
     }
     const size_t na = (size_t)B * hb->nb_arg;
     const size_t nsplit = B > 1 ? (size_t)B * (h + qd + f) : 0;  // floats holding the bf16 part pairs
-    const size_t nf = (size_t)B * ((size_t)h * 4 + R3 + qd * 2 + f + d->vocab) +
+    const size_t nf = (size_t)B * ((size_t)h * 4 + R3 + qd * 2 + f + d->vocab) +  // (an upper bound)
                       (size_t)B * d->n_q_heads * hb->S * (d->head_dim + 2) + gpart + nsplit + na * 2 + B + 16 * 20;
     if (hipMalloc(&hb->buf, nf * 4) != hipSuccess) {
         delete hb;
@@ -625,14 +625,17 @@ mk_status mkb_create(const mk_model_desc* d, int32_t batch, int32_t max_ctx, mkb
         p += (n + 15) & ~size_t(15);
         return r;
     };
+    // fp32 projection inputs and outputs of the one-sequence path (several sequences
+    // use the bf16 part pairs and the K-slice partials instead)
+    const size_t one = B == 1 ? 1 : 0;
     hb->x = take((size_t)B * h);
-    hb->xn = take((size_t)B * h);
+    hb->xn = take(one * h);
     hb->xb = take((size_t)B * h);
     hb->hidden = take((size_t)B * h);
-    hb->qkv = take((size_t)B * R3);
+    hb->qkv = take(one * R3);
     hb->q = take((size_t)B * qd);
-    hb->a = take((size_t)B * qd);
-    hb->m = take((size_t)B * f);
+    hb->a = take(one * qd);
+    hb->m = take(one * f);
     hb->lg = take((size_t)B * d->vocab);
     hb->part = take((size_t)B * d->n_q_heads * hb->S * (d->head_dim + 2));
     hb->gpart = take(gpart);
