@@ -2044,9 +2044,10 @@ __device__ __forceinline__ bool gemv_mfma_b(const Params* pp, int wave, int lane
 // gate/up and LM head read the residual rows themselves and apply RMSNorm (gains on
 // the inputs, 1/RMS per sequence on the results); O-proj and down read the operand
 // regions their producers wrote.
-template <int KT, bool NORMED>
+template <int KT, bool NORMED, int OPK>
 __device__ __noinline__ bool op_gemv_b(const Params* pp, uint32_t slot_, uint32_t page0, uint32_t t_, uint32_t epoch_) {
-    const Task k = fifo_task(slot_);
+    Task k = fifo_task(slot_);
+    k.op = (uint8_t)OPK;  // one instance per operation: the other operations' code folds away
     Ctx c = make_ctx(t_, epoch_);
     CParams& p = P(pp);
     const int lane = c.lane, tid = c.tid, wave = c.wave;
@@ -2289,14 +2290,18 @@ __device__ __noinline__ bool op_gemv_b(const Params* pp, uint32_t slot_, uint32_
     return true;
 }
 
-template <int KT>
-__device__ __forceinline__ bool op_gemv_bn(const Params* pp, uint32_t slot, uint32_t page0, uint32_t t, uint32_t epoch) {
-    return op_gemv_b<KT, true>(pp, slot, page0, t, epoch);
-}
-template <int KT>
-__device__ __forceinline__ bool op_gemv_br(const Params* pp, uint32_t slot, uint32_t page0, uint32_t t, uint32_t epoch) {
-    return op_gemv_b<KT, false>(pp, slot, page0, t, epoch);
-}
+// The several-sequence GEMV of operation OPK: normalised input (n) or operand region (r)
+template <int OPK>
+struct GemvB {
+    template <int KT>
+    static __device__ __forceinline__ bool n(const Params* pp, uint32_t slot, uint32_t page0, uint32_t t, uint32_t epoch) {
+        return op_gemv_b<KT, true, OPK>(pp, slot, page0, t, epoch);
+    }
+    template <int KT>
+    static __device__ __forceinline__ bool r(const Params* pp, uint32_t slot, uint32_t page0, uint32_t t, uint32_t epoch) {
+        return op_gemv_b<KT, false, OPK>(pp, slot, page0, t, epoch);
+    }
+};
 
 // After the last LM-head tile of the step: publish the argmax (the LM-head tiles
 // have published the final residual).
@@ -2349,33 +2354,39 @@ __device__ __noinline__ void compute(const Params* pp, uint32_t epoch, int wave)
         const uint64_t t_fetch = rtc();
         c.t = t;
         bool ok = true;
-        if (p0.T.B > 1) {
+        // single-sequence operations referenced first: their functions are emitted next
+        // to the loader, ahead of the several-sequence GEMV instances
+        if (p0.T.B == 1) {
             switch (k.op) {
-                case OP_QKV:
-                case OP_GATEUP:
-                case OP_LMHEAD: ok = MK_KT_DISPATCH_2K(op_gemv_bn, h, pp, slot, page0, t, epoch); break;
-                case OP_OPROJ: ok = MK_KT_DISPATCH_2K(op_gemv_br, okt, pp, slot, page0, t, epoch); break;
-                case OP_DOWN: ok = MK_KT_DISPATCH_2K(op_gemv_br, dkt, pp, slot, page0, t, epoch); break;
-                case OP_ROUTE:
-                case OP_EGU: ok = MK_KT_DISPATCH_2K(op_gemv_bn, h, pp, slot, page0, t, epoch); break;
-                case OP_EDOWN: ok = MK_KT_DISPATCH_2K(op_gemv_br, p0.T.fe, pp, slot, page0, t, epoch); break;
+                case OP_QKV: ok = MK_KT_DISPATCH(op_qkv, h, pp, slot, page0, t, epoch); break;
+                case OP_ATTN: ok = attn_kswizzle(p0.T.d, p0.T.grp) ? op_attn_mfma(pp, slot, page0, t, epoch)
+                                   : hd == 64 ? op_attn<64>(pp, slot, page0, t, epoch)
+                                              : op_attn<128>(pp, slot, page0, t, epoch);
+                    break;
+                case OP_OPROJ: ok = MK_KT_DISPATCH_2K(op_oproj, okt, pp, slot, page0, t, epoch); break;
+                case OP_GATEUP: ok = MK_KT_DISPATCH(op_gateup, h, pp, slot, page0, t, epoch); break;
+                case OP_DOWN: ok = MK_KT_DISPATCH_2K(op_down, dkt, pp, slot, page0, t, epoch); break;
+                case OP_LMHEAD: ok = MK_KT_DISPATCH(op_lmhead, h, pp, slot, page0, t, epoch); break;
+                default: break;
+            }
+        } else {
+            switch (k.op) {
+                case OP_QKV: ok = MK_KT_DISPATCH_2K(GemvB<OP_QKV>::template n, h, pp, slot, page0, t, epoch); break;
+                case OP_GATEUP: ok = MK_KT_DISPATCH_2K(GemvB<OP_GATEUP>::template n, h, pp, slot, page0, t, epoch); break;
+                case OP_LMHEAD: ok = MK_KT_DISPATCH_2K(GemvB<OP_LMHEAD>::template n, h, pp, slot, page0, t, epoch); break;
+                case OP_OPROJ: ok = MK_KT_DISPATCH_2K(GemvB<OP_OPROJ>::template r, okt, pp, slot, page0, t, epoch); break;
+                case OP_DOWN: ok = MK_KT_DISPATCH_2K(GemvB<OP_DOWN>::template r, dkt, pp, slot, page0, t, epoch); break;
+                case OP_ROUTE: ok = MK_KT_DISPATCH_2K(GemvB<OP_ROUTE>::template n, h, pp, slot, page0, t, epoch); break;
+                case OP_EGU: ok = MK_KT_DISPATCH_2K(GemvB<OP_EGU>::template n, h, pp, slot, page0, t, epoch); break;
+                case OP_EDOWN:
+                    ok = MK_KT_DISPATCH_2K(GemvB<OP_EDOWN>::template r, p0.T.fe, pp, slot, page0, t, epoch);
+                    break;
                 case OP_ATTN: ok = attn_kswizzle(p0.T.d, p0.T.grp) ? op_attn_mfma(pp, slot, page0, t, epoch)
                                : hd == 64 ? op_attn<64>(pp, slot, page0, t, epoch)
                                           : op_attn<128>(pp, slot, page0, t, epoch);
                 break;
                 default: break;
             }
-        } else switch (k.op) {
-            case OP_QKV: ok = MK_KT_DISPATCH(op_qkv, h, pp, slot, page0, t, epoch); break;
-            case OP_ATTN: ok = attn_kswizzle(p0.T.d, p0.T.grp) ? op_attn_mfma(pp, slot, page0, t, epoch)
-                               : hd == 64 ? op_attn<64>(pp, slot, page0, t, epoch)
-                                          : op_attn<128>(pp, slot, page0, t, epoch);
-                break;
-            case OP_OPROJ: ok = MK_KT_DISPATCH_2K(op_oproj, okt, pp, slot, page0, t, epoch); break;
-            case OP_GATEUP: ok = MK_KT_DISPATCH(op_gateup, h, pp, slot, page0, t, epoch); break;
-            case OP_DOWN: ok = MK_KT_DISPATCH_2K(op_down, dkt, pp, slot, page0, t, epoch); break;
-            case OP_LMHEAD: ok = MK_KT_DISPATCH(op_lmhead, h, pp, slot, page0, t, epoch); break;
-            default: break;
         }
         if (!uni(ok)) return;
         // ---- completion: every wave's stores are done, then wave 0 signals ----
