@@ -1901,11 +1901,11 @@ __device__ __noinline__ bool op_lmhead(const Params* pp, uint32_t slot_, uint32_
 // i land in bo[i] as raw bits, to be turned into the block's operands in place.
 template <int NBW>
 __device__ __forceinline__ void load_rows(u32x4v (*bo)[NPART], __amdgpu_buffer_rsrc_t r, bool emb, uint32_t row_ofs,
-                                          int wave, int lane) {
+                                          int wave, int lane, int c0 = 0) {
     const int kq = lane / 16;
 #pragma unroll
     for (int i = 0; i < NBW; ++i) {
-        const uint32_t col = (uint32_t)(32 * (4 * i + wave) + 8 * kq);
+        const uint32_t col = (uint32_t)(c0 + 32 * (4 * i + wave) + 8 * kq);
         if (emb) {
             const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(r, (row_ofs + col) * 2, 0, 0);
             bo[i][0] = u32x4v{w[0] << 16, w[0] & 0xffff0000u, w[1] << 16, w[1] & 0xffff0000u};
@@ -1919,9 +1919,9 @@ __device__ __forceinline__ void load_rows(u32x4v (*bo)[NPART], __amdgpu_buffer_r
 // Block i's inputs (raw fp32 bits in bo) times the RMSNorm gains staged in LDS (bf16,
 // in S.rowres), split into the two B-operand parts in place; the sum of squares of the
 // unscaled inputs is accumulated into ss.
-__device__ __forceinline__ void ops_of_row_block(u32x4v* bo, int i, int wave, int lane, float& ss) {
+__device__ __forceinline__ void ops_of_row_block(u32x4v* bo, int i, int wave, int lane, float& ss, int c0 = 0) {
     const uint16_t* gl = (const uint16_t*)S.rowres;
-    const uint4 gw = *(const uint4*)&gl[32 * (4 * i + wave) + 8 * (lane / 16)];
+    const uint4 gw = *(const uint4*)&gl[c0 + 32 * (4 * i + wave) + 8 * (lane / 16)];
     const uint32_t gg[4] = {gw.x, gw.y, gw.z, gw.w};
     float x[8];
 #pragma unroll
@@ -1983,7 +1983,7 @@ __device__ __forceinline__ float rs_seq(int b, int n, float eps) {
 // once into this wave's slice.
 template <int KT>
 __device__ __forceinline__ bool gemv_mfma_b(const Params* pp, int wave, int lane, uint32_t page0, uint32_t nrg,
-                                            const u32x4v (*bo)[NPART], int B, uint32_t task) {
+                                            const u32x4v (*bo)[NPART], int B, uint32_t task, bool first = true) {
     static_assert(KT >= 128 && KT <= 2048, "matrix-core GEMV covers 128 <= K <= 2048");
     constexpr int NKB = KT / 32;
     float* const sl = &S.xs[wave * 1024];
@@ -2011,7 +2011,7 @@ __device__ __forceinline__ bool gemv_mfma_b(const Params* pp, int wave, int lane
                     acc1 = mfma(a[j], bo[4 * s + j][1], acc1);
                 }
             }
-            slice_put(sl, acc0 + acc1, rg, lane, B, true);
+            slice_put(sl, acc0 + acc1, rg, lane, B, first);
         }
     } else {
         constexpr int RPG = 16 / NKB;  // row groups per page
@@ -2062,30 +2062,35 @@ __device__ __noinline__ bool op_gemv_b(const Params* pp, uint32_t slot_, uint32_
     uint4 gpre = make_uint4(0, 0, 0, 0);
     if (normed && tid * 8 < h) gpre = gld_u4(gains(p, gslot) + tid * 8);
     if (!await_inputs(pp, k, c)) return false;
-    constexpr int NBW = KT / 128;
+    // QKV and gate/up tiles of K = 2048 are packed in K halves: the operands of one half at a time
+    constexpr bool HV = NORMED && KT == 2048 && (OPK == OP_QKV || OPK == OP_GATEUP);
+    constexpr int NBW = HV ? KT / 256 : KT / 128;
     u32x4v bo[NBW][NPART];
+    __amdgpu_buffer_rsrc_t nr;  // normalised inputs: the residual rows, or the embedding rows
+    uint32_t nrow_ofs = 0;
+    bool nemb = false;
+    float ss = 0.f;
     if constexpr (NORMED) {
         if (tid * 8 < h) *(uint4*)&((uint16_t*)S.rowres)[tid * 8] = gpre;
         const int n = lane % 16;
-        const bool emb = src < 0;
-        __amdgpu_buffer_rsrc_t r;
-        uint32_t row_ofs;
-        if (emb) {
-            r = __builtin_amdgcn_make_buffer_rsrc((void*)(p.w + p.lay.embed), 0, (uint32_t)((uint64_t)p.T.V * h * 2),
-                                                  RSRC_FLAGS);
-            row_ofs = n < B ? (uint32_t)S.tok[gb0 + n] * (uint32_t)h : (uint32_t)p.T.V * (uint32_t)h;
+        nemb = src < 0;
+        if (nemb) {
+            nr = __builtin_amdgcn_make_buffer_rsrc((void*)(p.w + p.lay.embed), 0, (uint32_t)((uint64_t)p.T.V * h * 2),
+                                                   RSRC_FLAGS);
+            nrow_ofs = n < B ? (uint32_t)S.tok[gb0 + n] * (uint32_t)h : (uint32_t)p.T.V * (uint32_t)h;
         } else {
-            r = dev_rsrc(acc_buf(p, c.parity, src, gb0), (uint32_t)(B * h * 4));
-            row_ofs = (uint32_t)(n * h);  // sequences past B read zeros (out of the buffer's range)
+            nr = dev_rsrc(acc_buf(p, c.parity, src, gb0), (uint32_t)(B * h * 4));
+            nrow_ofs = (uint32_t)(n * h);  // sequences past B read zeros (out of the buffer's range)
         }
-        load_rows<NBW>(bo, r, emb, row_ofs, wave, lane);
+        if constexpr (!HV) load_rows<NBW>(bo, nr, nemb, nrow_ofs, wave, lane);
         if (!cbarrier(pp, c, k.id)) return false;  // gains staged
-        float ss = 0.f;
+        if constexpr (!HV) {
 #pragma unroll
-        for (int i = 0; i < NBW; ++i) ops_of_row_block(bo[i], i, wave, lane, ss);
-        ss += __shfl_xor(ss, 16, 64);
-        ss += __shfl_xor(ss, 32, 64);
-        if (lane < GROUP_SEQS) S.ssqb[wave][lane] = ss;
+            for (int i = 0; i < NBW; ++i) ops_of_row_block(bo[i], i, wave, lane, ss);
+            ss += __shfl_xor(ss, 16, 64);
+            ss += __shfl_xor(ss, 32, 64);
+            if (lane < GROUP_SEQS) S.ssqb[wave][lane] = ss;
+        }
     } else {
         const uint16_t* R = k.op == OP_OPROJ ? opr_attn(p, l, (int)k.seq)
                             : k.op == OP_EDOWN ? opr_me(p, l, k.part, (int)k.seq)
@@ -2147,7 +2152,7 @@ __device__ __noinline__ bool op_gemv_b(const Params* pp, uint32_t slot_, uint32_
     // (one chunk except for LM-head tiles)
     constexpr int NKB = KT / 32;
     const bool expert = k.op == OP_EGU || k.op == OP_EDOWN;
-    const int CR = expert ? 64 : MAX_TILE_ROWS / B / 64 * 64;  // expert chunks: 32 gate + 32 up rows / 64 down rows
+    const int CR = expert ? 64 : HV ? halves_chunk_rows(Btot) : MAX_TILE_ROWS / B / 64 * 64;  // expert chunks: 32 gate + 32 up rows / 64 down rows
     static_assert(64 * GROUP_SEQS <= MAX_TILE_ROWS, "an expert chunk's results (and residual rows) fit res[] and the slices");
     const int rows_pad = (int)(k.wbytes / (KT * 2));
     float lm_bv[GROUP_SEQS / NCW];
@@ -2174,7 +2179,28 @@ __device__ __noinline__ bool op_gemv_b(const Params* pp, uint32_t slot_, uint32_
                              : 0.f;
             }
         }
-        if (!gemv_mfma_b<KT>(pp, wave, lane, pbase, nrg, bo, B, k.id)) return false;
+        if constexpr (HV) {
+            // the chunk's rows over columns 0 .. K/2 - 1, then K/2 .. K - 1 (added); the sums
+            // of squares of the inputs from the first chunk's two halves
+#pragma unroll 1
+            for (int hh = 0; hh < 2; ++hh) {
+                load_rows<NBW>(bo, nr, nemb, nrow_ofs, wave, lane, hh * (KT / 2));
+                float ssh = 0.f;
+#pragma unroll
+                for (int i = 0; i < NBW; ++i) ops_of_row_block(bo[i], i, wave, lane, ssh, hh * (KT / 2));
+                if (c0 == 0) ss += ssh;
+                if (!gemv_mfma_b<KT / 2>(pp, wave, lane, pbase + (uint32_t)hh * nrg * (KT / 1024), nrg, bo, B, k.id,
+                                         hh == 0))
+                    return false;
+            }
+            if (c0 == 0) {
+                ss += __shfl_xor(ss, 16, 64);
+                ss += __shfl_xor(ss, 32, 64);
+                if (lane < GROUP_SEQS) S.ssqb[wave][lane] = ss;
+            }
+        } else {
+            if (!gemv_mfma_b<KT>(pp, wave, lane, pbase, nrg, bo, B, k.id)) return false;
+        }
         if (!cbarrier(pp, c, k.id)) return false;
         if (k.op == OP_EGU) {  // m = SiLU(gate) * up, rows row0 + c0 / 2 .. + 31
             uint16_t* Rm = opr_me(p, l, k.part, (int)k.seq);
@@ -2524,7 +2550,15 @@ __global__ void __launch_bounds__(256) repack_tiles_kernel(const TileOp* ops, co
     const uint32_t nkb = op.kt / 32;
     for (uint32_t e = threadIdx.x; e < n16; e += 256) {
         uint32_t row, col;
-        if (op.blocked) {  // row-group major: block b = (row group, column block)
+        if (op.blocked == 2) {  // chunk, then K half, then row group, then column block of the half
+            const uint32_t b = e / 64, l = e % 64;
+            const uint32_t nrg = op.rows / 16, cr = op.chunk_rows / 16, hb = nkb / 2;
+            const uint32_t c = b / (cr * nkb), w = b - c * cr * nkb;
+            const uint32_t rgs = min(cr, nrg - c * cr);
+            const uint32_t half = w / (rgs * hb), w2 = w % (rgs * hb);
+            row = (c * cr + w2 / hb) * 16 + l % 16;
+            col = (half * hb + w2 % hb) * 32 + (l / 16) * 8;
+        } else if (op.blocked) {  // row-group major: block b = (row group, column block)
             const uint32_t b = e / 64, l = e % 64;
             row = (b / nkb) * 16 + l % 16;
             col = (b % nkb) * 32 + (l / 16) * 8;

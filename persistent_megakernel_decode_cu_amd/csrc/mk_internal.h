@@ -29,6 +29,12 @@ constexpr int GROUP_SEQS = 16;       // sequences per column group (columns of o
 constexpr int MAX_BATCH = 32;        // sequences per step: GEMV tiles run once per column group
 constexpr int MAX_ACT = 4096;        // floats of one staged activation vector (LDS)
 
+// Several-sequence QKV and gate/up tiles with K = 2048 are packed in two halves of K
+// (chunk by chunk of halves_chunk_rows rows: all row groups of columns 0..1023, then
+// of 1024..2047), so that their GEMV holds the operands of one half at a time.
+constexpr int halves_chunk_rows(int B) { return (MAX_TILE_ROWS / (B < GROUP_SEQS ? B : GROUP_SEQS)) / 64 * 64; }
+constexpr bool halves_packed(int B, int op, int kt) { return B > 1 && kt == 2048 && (op == OP_QKV || op == OP_GATEUP); }
+
 // One instruction of the interpreter: 48 bytes, read by the loader wave into LDS.
 struct Task {
     uint8_t op;

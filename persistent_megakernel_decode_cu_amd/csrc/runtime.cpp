@@ -182,6 +182,11 @@ mk_status repack(mk_handle* h, const mk_model_desc* d, uint8_t* wd) {
         t.rows = (uint32_t)(k.wbytes / (kt * 2));
         while (rows.size() < (size_t)t.row_base + t.rows) rows.push_back(nullptr);
         t.blocked = kt <= 2048 ? 1u : 0u;
+        t.chunk_rows = 0;
+        if (halves_packed(T.B, k.op, (int)kt)) {
+            t.blocked = 2u;
+            t.chunk_rows = (uint32_t)halves_chunk_rows(T.B);
+        }
         tiles.push_back(t);
     }
     CopyOp* dops = nullptr;

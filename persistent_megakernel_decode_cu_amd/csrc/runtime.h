@@ -91,7 +91,8 @@ hipError_t launch_repack(const CopyOp* ops, uint32_t n_ops, uint8_t* dst, hipStr
 // lane l of a block holds row 16*rg + l%16, columns 32*kb + 8*(l/16) .. +7).
 struct TileOp {
     uint64_t dst_off;
-    uint32_t row_base, rows, kt, blocked;
+    uint32_t row_base, rows, kt, blocked;  // blocked: 0 row-major, 1 matrix-core blocks, 2 the same in K halves
+    uint32_t chunk_rows;                   // blocked == 2: rows per chunk
 };
 hipError_t launch_repack_tiles(const TileOp* ops, uint32_t n_ops, const uint8_t* const* rowsrc, uint8_t* dst,
                                hipStream_t stream);
