@@ -192,6 +192,14 @@ def test_llama1b_batch16_first_step(llama1b_b16, sched):
     assert res["argmax_equal"]
 
 
+@pytest.mark.parametrize("B", [3, 6])
+def test_llama1b_small_batch_first_step(B):
+    """A few sequences at the 1B shape: QKV and gate/up tiles packed in K halves with the
+    chunk size of this batch (1024 // B rounded down to 64 rows)."""
+    C = 2048
+    _one_step(LLAMA_1B, B, C, synth.make_positions(B, 100, C - 1), check_kv=False)
+
+
 def test_llama1b_batch32_first_step():
     """32 sequences: every GEMV tile runs for two column groups of 16 on the same weights."""
     B, C = 32, 4352
