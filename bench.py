@@ -58,8 +58,13 @@ def measured_traffic():
     return int(rec["traffic_bytes_per_launch"])
 
 
+# every source the kernel's memory traffic depends on: the kernel, the planner (tiles, queues) and the
+# runtime's weight packing (tile order in HBM)
 TRAFFIC_SOURCES = ["persistent_megakernel_decode_cu_amd/csrc/megakernel.hip",
-                   "persistent_megakernel_decode_cu_amd/csrc/graph.cpp"]
+                   "persistent_megakernel_decode_cu_amd/csrc/graph.cpp",
+                   "persistent_megakernel_decode_cu_amd/csrc/runtime.cpp",
+                   "persistent_megakernel_decode_cu_amd/csrc/runtime.h",
+                   "persistent_megakernel_decode_cu_amd/csrc/mk_internal.h"]
 
 
 def traffic_from_counters(fetch_csv, write_csv, kernel="mk::mk_step_kernel", copy_bytes=256 << 20):
@@ -95,6 +100,42 @@ def traffic_from_counters(fetch_csv, write_csv, kernel="mk::mk_step_kernel", cop
             "fetch_scale": round(fs, 4), "write_scale": round(ws, 4),
             "hbm_read_bytes_per_launch": rd, "hbm_write_bytes_per_launch": wr,
             "traffic_bytes_per_launch": rd + wr, "launches": n}
+
+
+def host_info():
+    """The host CPU model and the GPU clocks as amd-smi reports them (raw, trimmed), for the record."""
+    import subprocess
+    info = {"cpu_model": None, "cpu_threads": len(os.sched_getaffinity(0)), "gpu_clocks": None}
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                info["cpu_model"] = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    for cmd in (["amd-smi", "metric", "--clock", "--json"], ["rocm-smi", "--showclocks", "--json"]):
+        try:
+            r = subprocess.run(cmd, capture_output=True, text=True, timeout=30)
+        except (OSError, subprocess.TimeoutExpired):
+            continue
+        if r.returncode == 0 and r.stdout.strip():
+            try:
+                raw = json.loads(r.stdout)
+                # amd-smi: {"gpu_data": [{"gpu": 0, "clock": {"gfx_0": {"clk": {"value": .., "unit": "MHz"},
+                # "max_clk": ..}, "mem_0": ..}}]} -> current / max MHz of the compute and memory clocks
+                clk = {}
+                for g in raw.get("gpu_data", []) if isinstance(raw, dict) else []:
+                    for dom, v in g.get("clock", {}).items():
+                        if dom.startswith(("gfx", "mem")) and isinstance(v, dict):
+                            cur, mx = v.get("clk"), v.get("max_clk")
+                            clk[dom] = [cur.get("value") if isinstance(cur, dict) else cur,
+                                        mx.get("value") if isinstance(mx, dict) else mx]
+                info["gpu_clocks"] = {"MHz_current_max": clk} if clk else raw
+            except ValueError:
+                info["gpu_clocks"] = r.stdout.strip()[:2000]
+            info["gpu_clocks_tool"] = " ".join(cmd)
+            break
+    return info
 
 
 def cpu_baseline(cfg, w, kc, vc, tok, P0, budget_s=10.0):
@@ -181,6 +222,113 @@ def baseline_leg(mk, torch, cfg, desc, kv, tok, P0, C, K, W, mk_ms):
             "launches_per_step": launches, "megakernel_speedup_vs_best": round(best / mk_ms, 3)}
 
 
+TRACE_OPS = {1: "QKV+RoPE", 2: "attention", 3: "O-proj", 4: "gate/up", 5: "down", 6: "LM head", 7: "router",
+             8: "expert gate/up", 9: "expert down"}
+
+
+def trace_summary(tr, ex, title, command):
+    """Markdown summary of one traced step (mk_read_trace, 16 words per task: workgroup, t_fetch,
+    t_inputs_ready, t_staged, t_computed, t_end, t_stored, t_last_page, first page, last wave's epilogue
+    issued, last wave's stores acknowledged, ...; 100 MHz ticks): where each operation's time goes, when
+    each layer's phases end, and how long each dependency hop takes."""
+    tasks = ex["tasks"]
+    us = 0.01  # one tick of the 100 MHz clock in microseconds
+    (fetch, ready, staged, computed, end, stored, last_pg, epi, acked) = (
+        tr[:, i].astype(np.int64) for i in (1, 2, 3, 4, 5, 6, 7, 9, 10))
+    t0 = int(fetch.min())
+    ops = tasks["op"]
+    lines = [f"# {title}", "", f"Command: `{command}`", "",
+             f"Step span (first task fetched to last task ended): {(int(end.max()) - t0) * us:.1f} µs over "
+             f"{len(tasks)} tasks on {ex['header']['W']} workgroups.", "",
+             "## Per operation (µs; median over the step's tasks, p90 in brackets)", "",
+             "Columns: waiting for the input event; staging the inputs; compute (page waits included) and, of it, "
+             "how long after staging wave 0 got its last page; the epilogue until the last wave issued its "
+             "stores; until the last wave's stores were acknowledged; until the signal was issued (done "
+             "barrier, counter add); inputs ready to end.", "",
+             "| op | tasks | wait | stage | compute | last page after staging | epilogue issued | stores acked | "
+             "barrier + signal | busy |", "|---|---|---|---|---|---|---|---|---|---|"]
+
+    def med(a):
+        return f"{np.median(a) * us:.2f} [{np.percentile(a, 90) * us:.2f}]" if len(a) else "-"
+
+    for op in sorted(set(int(o) for o in ops)):
+        s = ops == op
+        lp = last_pg[s] - staged[s]
+        lp = lp[last_pg[s] > 0]
+        lines.append(f"| {TRACE_OPS.get(op, op)} | {int(s.sum())} | {med(ready[s] - fetch[s])} | "
+                     f"{med(staged[s] - ready[s])} | {med(computed[s] - staged[s])} | {med(np.maximum(lp, 0))} | "
+                     f"{med(epi[s] - computed[s])} | {med(acked[s] - epi[s])} | {med(end[s] - acked[s])} | "
+                     f"{med(end[s] - ready[s])} |")
+    # per layer: when each phase's last task ended (from the step's first fetch)
+    layers = tasks["layer"]
+    L = ex["header"]["L"]
+    phase_ops = [o for o in (1, 2, 3, 4, 5, 7, 8, 9) if (ops == o).any()]
+    lines += ["", "## Layer phases (µs from the step's first fetch: the end of each phase's last task)", "",
+              "| layer | " + " | ".join(TRACE_OPS[o] for o in phase_ops) + " | layer time |",
+              "|---|" + "---|" * (len(phase_ops) + 1)]
+    prev = None
+    layer_times = []
+    for l in range(L):
+        row = []
+        for o in phase_ops:
+            s = (layers == l) & (ops == o)
+            row.append((int(end[s].max()) - t0) * us if s.any() else float("nan"))
+        last = max(r for r in row if r == r)
+        lt = last - prev if prev is not None else last
+        layer_times.append(lt)
+        prev = last
+        if l < 3 or l >= L - 2:
+            lines.append(f"| {l} | " + " | ".join(f"{r:.1f}" for r in row) + f" | {lt:.1f} |")
+        elif l == 3:
+            lines.append("| … |" + " |" * (len(phase_ops) + 1))
+    s = ops == 6
+    if s.any():
+        lm_end = (int(end[s].max()) - t0) * us
+        lines += ["", f"Median layer time {np.median(layer_times[1:] or layer_times):.1f} µs; LM head phase "
+                      f"{lm_end - prev:.1f} µs after the last layer (ends at {lm_end:.1f} µs)."]
+    # dependency hops: an event's last producer ends -> its consumers see the event
+    prod_end = {}
+    for i, k in enumerate(tasks):
+        if k["sig_ev"] != 0xFFFFFFFF:
+            e = int(k["sig_ev"])
+            prod_end[e] = max(prod_end.get(e, 0), int(end[i]))
+    hops = {}
+    for i, k in enumerate(tasks):
+        e = int(k["wait_ev"])
+        if e != 0xFFFFFFFF and e in prod_end:
+            hops.setdefault(int(k["op"]), []).append(int(ready[i]) - prod_end[e])
+    lines += ["", "## Dependency hops (µs: the awaited event's last producer ended → the consumer saw the event;",
+              "negative when the consumer saw it before the producer's own end record)", "",
+              "| consumer | median | p10 | p90 |", "|---|---|---|---|"]
+    for op, v in sorted(hops.items()):
+        v = np.asarray(v)
+        lines.append(f"| {TRACE_OPS.get(op, op)} | {np.median(v) * us:.2f} | {np.percentile(v, 10) * us:.2f} | "
+                     f"{np.percentile(v, 90) * us:.2f} |")
+    return "\n".join(lines) + "\n"
+
+
+def traced_step_summary(mk, torch, model, B, C, opt_kw, run_args, title, command, out_path, steps=4):
+    """Builds a handle with per-task tracing on, runs a few chained steps, writes the trace summary."""
+    tok0, positions, kv, logits = run_args
+    h = mk.mk_build_graph(model.desc, B, C, mk.options(trace=1, **opt_kw))
+    ex = mk.parse_export(mk.mk_export_graph(h))
+    sp = torch.cuda.current_stream().cuda_stream
+    nxt = mk.mk_next_tokens(h)
+    for s in range(steps):
+        mk.mk_decode_step(h, tok0.data_ptr() if s == 0 else nxt, positions[s].data_ptr(), kv.data_ptr(),
+                          logits.data_ptr(), sp)
+    torch.cuda.synchronize()
+    err = mk.mk_check_device_error(h)
+    if err:
+        raise SystemExit(f"device error: {err}")
+    tr = mk.mk_read_trace(h, int(ex["header"]["n_tasks"]))
+    mk.mk_destroy(h)
+    text = trace_summary(tr, ex, title, command)
+    with open(out_path, "w") as f:
+        f.write(text)
+    return text
+
+
 def moe_step_bytes(cfg, positions, experts):
     """Algorithmic bytes of one MoE decode step: the dense part (attention, norms, LM head), every layer's
     router, each expert that at least one sequence selected in that layer once, and the K/V rows read.
@@ -218,9 +366,9 @@ def bench_batch(args, torch, synth, mk):
         raise SystemExit("steps exceed the KV cache")
     dev = {k: torch.from_numpy(v.view(np.int16)).cuda() for k, v in w.items()}
     model = mk.Model(cfg, dev)
-    opt = mk.options(sched=SCHEDS[args.sched], policy=0 if args.policy == "rr" else 1,
-                     attn_splits=args.attn_splits, cooperative=1 if args.cooperative else 0)
-    h = mk.mk_build_graph(model.desc, B, C, opt)
+    opt_kw = dict(sched=SCHEDS[args.sched], policy=0 if args.policy == "rr" else 1, attn_splits=args.attn_splits,
+                  cooperative=1 if args.cooperative else 0)
+    h = mk.mk_build_graph(model.desc, B, C, mk.options(**opt_kw))
     graph = mk.parse_export(mk.mk_export_graph(h))
     kv = torch.from_numpy(np.concatenate([kc.reshape(-1), vc.reshape(-1)]).view(np.int16)).cuda()
     del kc, vc
@@ -280,7 +428,7 @@ def bench_batch(args, torch, synth, mk):
                                                         "context 2048" if moe else "Llama-1B shape, mixed contexts"),
         "value": round(B * 1000.0 / ms, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": round(ms, 5), "us_per_step": round(ms * 1000.0, 2), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"{cfg.name} greedy decode, batch {B}, "
                                + ("every context 2048" if moe else "contexts uniform in [256, 4096]")
                                + ", bf16 weights and KV cache, one kernel launch per step",
@@ -299,6 +447,11 @@ def bench_batch(args, torch, synth, mk):
         # same weights, the same KV cache (the baseline rewrites the slots the megakernel wrote), same first
         # tokens and positions
         out["multi_kernel_baseline"] = baseline_leg(mk, torch, cfg, model.desc, kv, tok, P0, C, K, W, ms)
+    if args.trace:
+        traced_step_summary(mk, torch, model, B, C, opt_kw, (tok0, positions, kv, logits),
+                            f"Trace of one decode step: {out['config']['workload']}", " ".join(["python"] + sys.argv),
+                            args.trace)
+        out["trace_summary"] = args.trace
     del dev, model
     print(json.dumps(out), flush=True)
 
@@ -346,6 +499,9 @@ def main():
     ap.add_argument("--micro", action="store_true",
                     help="run the measurement microbenchmarks (launch latency, dependency hop, barrier, LDS fill, "
                          "streaming read) and print their JSON line instead of the step benchmark")
+    ap.add_argument("--trace", metavar="OUT_MD",
+                    help="after the timed steps, run a few steps of a handle built with per-task tracing and write "
+                         "the per-operation / per-layer / dependency-hop summary of the last one to OUT_MD")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the measured-traffic record from two rocprofv3 counter-collection CSVs and exit")
     args = ap.parse_args()
@@ -389,9 +545,9 @@ def main():
 
     dev = {k: torch.from_numpy(v.view(np.int16)).cuda() for k, v in w.items()}
     model = mk.Model(cfg, dev)
-    opt = mk.options(sched=SCHEDS[args.sched], policy=0 if args.policy == "rr" else 1,
-                     attn_splits=args.attn_splits, cooperative=1 if args.cooperative else 0)
-    h = mk.mk_build_graph(model.desc, 1, C, opt)
+    opt_kw = dict(sched=SCHEDS[args.sched], policy=0 if args.policy == "rr" else 1, attn_splits=args.attn_splits,
+                  cooperative=1 if args.cooperative else 0)
+    h = mk.mk_build_graph(model.desc, 1, C, mk.options(**opt_kw))
     graph = mk.parse_export(mk.mk_export_graph(h))
     kv = torch.from_numpy(np.concatenate([kc.reshape(-1), vc.reshape(-1)]).view(np.int16)).cuda()
     logits = torch.empty(cfg.vocab, dtype=torch.float32, device="cuda")
@@ -455,7 +611,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16",
+        "arithmetic": "bf16 weights and KV cache; fp32 activations between tasks; fp32 accumulation",
         "data": "synthetic",
         "config": {"workload": f"{cfg.name} greedy decode, batch 1, positions {P0}..{P0 + K - 1}, bf16 weights "
                                f"and KV cache, one kernel launch per step",
@@ -471,6 +628,12 @@ def main():
                                                   for q in (10, 50, 90)]},
     }
     mk.mk_destroy(h)
+    if args.trace:
+        pos2 = positions.reshape(-1, 1)
+        traced_step_summary(mk, torch, model, 1, C, opt_kw, (tok0, pos2, kv, logits),
+                            f"Trace of one decode step: {out['config']['workload']}", " ".join(["python"] + sys.argv),
+                            args.trace)
+        out["trace_summary"] = args.trace
     # context: the practical read ceiling of this GPU (a plain 4 GiB streaming read)
     read_peak = mk.mkm_stream_read(4 << 30)
     out["roofline"]["measured_read_peak_GBps"] = round(read_peak, 1)
@@ -495,11 +658,14 @@ def main():
 
     if not args.no_cpu_baseline:
         cb, first = cpu_baseline(cfg, w, kc, vc, tok, P0, budget_s=10.0 if args.model == "1b" else 20.0)
+        hi = host_info()
+        cb["cpu_model"] = hi["cpu_model"]
         out["cpu_baseline"] = cb
         out["parity_first_step"] = {
             "max_abs_dlogit": float(np.abs(first_logits.astype(np.float64) - first["logits"][0]).max()),
             "argmax_equal": bool(int(np.argmax(first_logits)) == int(first["next"][0]))}
     out["input_generation_s"] = round(t_gen, 1)
+    out["host"] = host_info()
     print(json.dumps(out), flush=True)
 
 

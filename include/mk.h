@@ -160,12 +160,18 @@ mk_status mk_read_counters(mk_handle *h, uint32_t *host, size_t n, uint32_t *epo
  * entries, host) — each task runs exactly once per step. */
 mk_status mk_read_task_counts(mk_handle *h, uint32_t *host, size_t n);
 
-/* Trace (when built with trace=1): per task of the last step, eight uint64
+/* Trace (when built with trace=1): per task of the last step, sixteen uint64
  * values {workgroup, t_fetch, t_inputs_ready, t_staged, t_computed, t_end,
- * first LDS page, t_last_page}; times in ticks of the 100 MHz device clock.
- * t_staged: inputs in LDS (attention: queries staged); t_computed: arithmetic
- * done (attention: all context pages folded in); t_last_page: compute wave 0
- * held the last of its pages (0 if it had none).  n_tasks * 8 entries into host. */
+ * t_stored, t_last_page, first LDS page, t_epilogue_issued, t_epilogue_acked,
+ * t_wave0_epilogue_issued, 0, 0, 0, 0}; times in ticks of the 100 MHz device
+ * clock.  t_staged: inputs in LDS (attention: queries staged); t_computed:
+ * arithmetic done (attention: all context pages folded in); t_epilogue_issued /
+ * t_epilogue_acked: the last compute wave to issue its result stores / to have
+ * them acknowledged by memory; t_stored: every wave done, just before the
+ * signal; t_end: signal issued; t_last_page: compute wave 0 held the last of
+ * its pages (0 if it had none).  n_tasks * 16 entries into host (the
+ * per-phase time breakdown of the Hazy Research megakernel news page,
+ * section 5). */
 mk_status mk_read_trace(mk_handle *h, uint64_t *host, size_t n);
 
 void mk_destroy(mk_handle *h);

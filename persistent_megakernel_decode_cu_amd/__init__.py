@@ -11,7 +11,8 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmk.so")
+# MK_LIBRARY: path of another build of the library (a variant built with build.build(out=...)) to load instead
+LIB_PATH = os.environ.get("MK_LIBRARY") or os.path.join(_HERE, "libmk.so")
 _lib = None
 
 MK_OK, MK_E_INVALID, MK_E_UNSUPPORTED, MK_E_NOMEM, MK_E_HIP, MK_E_NOT_RESIDENT, MK_E_DEVICE, MK_E_NO_DEVICE = range(8)
@@ -216,7 +217,7 @@ def mk_read_task_counts(h, n_tasks):
     return out
 
 
-TRACE_WORDS = 8
+TRACE_WORDS = 16
 
 
 def mk_read_trace(h, n_tasks):

@@ -15,10 +15,12 @@ HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-W
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
-def build(verbose=False):
-    """Compile every source and link libmk.so (always rebuilds)."""
+def build(verbose=False, out=None, extra_flags=()):
+    """Compile every source and link libmk.so (always rebuilds).  out / extra_flags: another library
+    path and extra compiler flags (e.g. -D overrides of tuning constants) for variant builds."""
     objs = []
-    bdir = os.path.join(HERE, "_build")
+    lib = out or LIB
+    bdir = os.path.join(HERE, "_build") if out is None else os.path.splitext(out)[0] + "_build"
     os.makedirs(bdir, exist_ok=True)
     for src in SOURCES:
         path = os.path.join(CSRC, src)
@@ -26,7 +28,7 @@ def build(verbose=False):
             continue
         obj = os.path.join(bdir, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [HIPCC] + HIP_FLAGS + lang + ["-c", path, "-o", obj]
+        cmd = [HIPCC] + HIP_FLAGS + list(extra_flags) + lang + ["-c", path, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
@@ -38,10 +40,10 @@ def build(verbose=False):
         if out.strip() and verbose:
             print(out)
         objs.append(obj)
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", LIB + ".tmp"] + objs
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", lib + ".tmp"] + objs
     subprocess.check_call(cmd)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(lib + ".tmp", lib)
+    return lib
 
 
 if __name__ == "__main__":

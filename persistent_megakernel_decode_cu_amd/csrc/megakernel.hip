@@ -47,7 +47,10 @@ constexpr int LPP = 16 / NLW;          // loads per page per loader wave
 // Pages in flight per loader wave.  48 KiB in flight per CU (12 MiB over the chip)
 // already keeps HBM busy; a deeper queue only adds queueing delay to every other
 // load, including the small latency-critical ones between dependent tasks.
-constexpr int MAX_INFLIGHT = 3;
+#ifndef MK_MAX_INFLIGHT
+#define MK_MAX_INFLIGHT 3
+#endif
+constexpr int MAX_INFLIGHT = MK_MAX_INFLIGHT;
 constexpr int DYNQ = 64;               // popped task ids shared between the loader waves (dynamic queue)
 constexpr int MAXB = 64;               // sequences per step held in LDS
 
@@ -74,6 +77,7 @@ struct __attribute__((aligned(16))) Smem {
     int32_t rtop[GROUP_SEQS];     // expert down tiles: 1 if the expert is the sequence's first choice
     uint32_t t_ready_lo, t_ready_hi;
     uint32_t tm[4];  // trace: low 32 bits of the clock after staging / after the GEMV
+    uint32_t tw_epi[NCW], tw_ack[NCW];  // trace: per wave, epilogue issued / its stores acknowledged
 };
 
 __shared__ Smem S;
@@ -2416,11 +2420,14 @@ __device__ __noinline__ void compute(const Params* pp, uint32_t epoch, int wave)
         }
         if (!uni(ok)) return;
         // ---- completion: every wave's stores are done, then wave 0 signals ----
+        if (p0.trace && c.lane == 0) lds_st(S.tw_epi[c.wave], (uint32_t)rtc());
         vm_wait_all();
+        if (p0.trace && c.lane == 0) lds_st(S.tw_ack[c.wave], (uint32_t)rtc());
         lgkm_wait_all();
         if (c.lane == 0) lds_add(S.done, 1u);
         if (c.wave == 0) {
             if (!lds_wait_ge(S.done, NCW * (t + 1), pp, k.id)) return;
+            const uint64_t t_stored = rtc();  // every wave's results acknowledged by memory
             CParams& p = P(pp);
             const int n_sig = (k.flags & TF_SIGRANGE) ? p0.T.E : 1;  // router tiles: every expert's event
             bool activated = false;
@@ -2451,8 +2458,18 @@ __device__ __noinline__ void compute(const Params* pp, uint32_t epoch, int wave)
                 gst(tr + 3, (unsigned long long)(hi | lds_ld(S.tm[0])));
                 gst(tr + 4, (unsigned long long)(hi | lds_ld(S.tm[1])));
                 gst(tr + 5, (unsigned long long)rtc());
-                gst(tr + 6, (unsigned long long)page0);
+                gst(tr + 6, (unsigned long long)t_stored);
                 gst(tr + 7, (unsigned long long)(hi | lds_ld(S.tm[2])));
+                gst(tr + 8, (unsigned long long)page0);
+                uint32_t we = 0, wa = 0;  // the last wave to finish its epilogue / to have its stores acknowledged
+#pragma unroll
+                for (int w = 0; w < NCW; ++w) {
+                    we = max(we, lds_ld(S.tw_epi[w]) - (uint32_t)t_fetch);
+                    wa = max(wa, lds_ld(S.tw_ack[w]) - (uint32_t)t_fetch);
+                }
+                gst(tr + 9, (unsigned long long)(t_fetch + we));
+                gst(tr + 10, (unsigned long long)(t_fetch + wa));
+                gst(tr + 11, (unsigned long long)(hi | lds_ld(S.tw_epi[0])));
                 if (c.lane == 0) lds_st(S.tm[2], 0u);
             }
             vm_wait_all();

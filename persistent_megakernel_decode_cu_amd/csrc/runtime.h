@@ -17,7 +17,10 @@ constexpr uint32_t ST_ERR = 128;    // error record: code, workgroup, task, even
 constexpr uint32_t ST_TAIL = 160;   // event-driven dispatch: ready-queue slots reserved (monotonic)
 constexpr uint32_t ST_WORDS = 192;
 
-constexpr int TRACE_WORDS = 8;  // per task: workgroup, fetch, inputs ready, staged, computed, end, first page, last page held
+// per task: workgroup, fetch, inputs ready, staged, computed, end (signalled), results acknowledged, last
+// page held, first page, last wave's epilogue issued, last wave's stores acknowledged, wave 0's epilogue
+// issued, 4 reserved
+constexpr int TRACE_WORDS = 16;
 
 enum ErrCode : uint32_t { ERR_NONE = 0, ERR_TIMEOUT_EVENT = 1, ERR_TIMEOUT_LDS = 2, ERR_INPUT = 3 };
 
