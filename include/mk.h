@@ -70,7 +70,8 @@ typedef struct {
     const mk_layer_weights *layers;
 } mk_model_desc;
 
-/* Build options; pass NULL for the defaults (all fields 0 / -1 as noted). */
+/* Build options; pass NULL for the defaults.  A zero-filled struct is the default
+ * configuration: every field's 0 means "automatic" or "off". */
 typedef struct {
     int32_t sched;             /* 0 static per-CU queues (default), 1 dynamic global queue (atomic pop),
                                 * 2 event-driven: tasks taken from a global ready queue in the order their
@@ -79,14 +80,25 @@ typedef struct {
     int32_t policy;            /* static assignment: 0 round-robin, 1 least-loaded (bytes) first */
     int32_t attn_splits;       /* KV chunks per (sequence, KV head), at most 16; 0 = automatic */
     int32_t debug_timeout_ms;  /* bound on every in-kernel wait; 0 = 2000 ms */
-    int32_t debug_drop_signal; /* >= 0: the task with this index skips its signal (tests); -1 = off */
+    int32_t debug_drop_signal; /* n > 0: the task with index n - 1 skips its signal (tests of the timeout
+                                  path); 0 or negative = off */
     int32_t trace;             /* 1: record per-task timestamps (mk_read_trace) */
     int32_t cooperative;       /* 1: cooperative launch (co-residency of every workgroup guaranteed by the
                                   runtime, about 20 us more per step); 0 (default): plain launch of one
                                   workgroup per CU, which needs the device to itself: if some workgroups
                                   could not start, the others' waits time out and the step reports
                                   MK_E_DEVICE instead of hanging */
-    int32_t reserved[8];
+    int32_t page_kib;          /* LDS page size in KiB: 0 or 16.  The ring is eight 16 KiB pages (128 KiB of
+                                  the CU's 160 KiB LDS) and is not a run-time choice: the packed weight layout
+                                  stores every GEMV tile as 1 KiB matrix-core blocks, sixteen to a page, so the
+                                  page size is part of the layout built here.  Any other value: MK_E_INVALID */
+    int32_t poison;            /* 1: before every step, fill the step's scratch that producers overwrite (query
+                                  rows, attention partials, SiLU(gate)*up rows, matrix-core operand regions,
+                                  router logits) and the logits and hidden outputs with NaN, so a task that
+                                  read any of them before its producer wrote it would put NaN in the outputs
+                                  (precision-regression testing of fused kernels: cloud.baidu.com
+                                  explainer, section 8).  Costs one extra kernel launch per step. */
+    int32_t reserved[6];
 } mk_options;
 
 /* Validates the description, copies the weights into a handle-owned packed
@@ -95,9 +107,13 @@ typedef struct {
  * 1 <= batch <= 32 sequences (batch > 1 also needs hidden <= 2048; the
  * projections of up to 16 sequences share one pass over the weights, so
  * 17..32 sequences take two); max_ctx >= 1 positions per sequence in the KV
- * cache.  Errors: MK_E_INVALID (NULL pointers, unsupported shapes),
- * MK_E_UNSUPPORTED (batch > 32, batch > 1 with hidden > 2048, MoE),
- * MK_E_NO_DEVICE, MK_E_NOMEM, MK_E_HIP.  On success *out receives the handle. */
+ * cache.  Errors: MK_E_INVALID (NULL pointers, unsupported shapes, bad options),
+ * MK_E_UNSUPPORTED (batch > 32, batch > 1 with hidden > 2048, a mixture of
+ * experts at batch 1), MK_E_NO_DEVICE, MK_E_NOMEM, MK_E_HIP.  On success *out
+ * receives the handle.  Defined by: the task graph built once on the host and
+ * reused for every forward (Hazy Research megakernel news page, section 4,
+ * "fusion big bang"; MPK news page, part 1: the model becomes a graph of tasks
+ * and events; koas-w.github.io notes, "SM-level task graph"). */
 mk_status mk_build_graph(const mk_model_desc *desc, int32_t batch, int32_t max_ctx, const mk_options *opt,
                          mk_handle **out);
 
@@ -105,12 +121,16 @@ mk_status mk_build_graph(const mk_model_desc *desc, int32_t batch, int32_t max_c
  * mk_build_graph would for `n_workgroups` workgroups (weight pointers in desc
  * are ignored and may be NULL) and writes the export image (format as
  * mk_export_graph) into buf (host) of capacity cap; *need receives the size.
- * Touches no GPU.  Returns MK_E_INVALID when cap is too small (need is set). */
+ * Touches no GPU.  Returns MK_E_INVALID when cap is too small (need is set).
+ * Defined by: static per-SM queues fixed before launch, or one global queue
+ * claimed at run time (koas-w.github.io notes, "static and dynamic
+ * scheduling"; MPK news page, part 1, the task graph). */
 mk_status mk_plan_graph(const mk_model_desc *desc, int32_t batch, int32_t max_ctx, const mk_options *opt,
                         int32_t n_workgroups, void *buf, size_t cap, size_t *need);
 
 /* Bytes of the KV cache the caller allocates for this handle: K then V, each
- * bf16 [n_layers][batch][n_kv][max_ctx][head_dim]. */
+ * bf16 [n_layers][batch][n_kv][max_ctx][head_dim] (the model's attention cache;
+ * the pages take the model as given). */
 size_t mk_kv_cache_bytes(const mk_handle *h);
 
 /* One decode step, asynchronous on `stream` (a hipStream_t; NULL = the null
@@ -124,40 +144,55 @@ size_t mk_kv_cache_bytes(const mk_handle *h);
  * [0, max_ctx), a wait exceeding debug_timeout_ms) record an error that
  * mk_check_device_error reports; outputs are then unspecified.
  * Errors: MK_E_INVALID (NULL handle/tokens/positions/kv_cache), MK_E_HIP,
- * MK_E_NOT_RESIDENT. */
+ * MK_E_NOT_RESIDENT.  Defined by: one persistent kernel runs the whole forward,
+ * every SM interpreting its instruction queue (Hazy Research megakernel news
+ * page, section 4; koas-w.github.io notes, "on-GPU interpreter / persistent
+ * kernel"); tasks wait on and increment counters in global memory (same Hazy
+ * page, section 4, "synchronisation"; MPK news page, part 2). */
 mk_status mk_decode_step(mk_handle *h, const int32_t *tokens, const int32_t *positions, void *kv_cache,
                          float *logits, void *stream);
 
 /* (dev) int32 [batch]: greedy next token of the last step (lowest index among
- * equal maximal logits).  Owned by the handle, valid until mk_destroy. */
+ * equal maximal logits), the argmax of the LM head that ends the forward (Hazy
+ * Research megakernel news page, section 5: the LM head closes the forward).
+ * Owned by the handle, valid until mk_destroy. */
 const int32_t *mk_next_tokens(const mk_handle *h);
 
 /* (dev) float [batch][hidden]: the final residual (before the final norm) of
- * the last step.  Owned by the handle. */
+ * the last step, for precision checks of the fused step against a plain
+ * evaluation (cloud.baidu.com explainer, section 8).  Owned by the handle. */
 const float *mk_hidden_out(const mk_handle *h);
 
 /* (dev) int32 [n_layers][batch][top_k]: experts chosen in the last step (MoE
- * models only; NULL otherwise).  Owned by the handle. */
+ * models only; NULL otherwise), the data-dependent routing decided inside the
+ * step (MPK news page, outlook: dynamic routing as the open problem of static
+ * task graphs; cloud.baidu.com explainer, section 2).  Owned by the handle. */
 const int32_t *mk_expert_ids(const mk_handle *h);
 
 /* Synchronises the device, then reports a device-side error of the last
  * steps: MK_OK if none, MK_E_DEVICE with a message in msg (host, cap bytes)
  * otherwise.  Clears the record and re-arms the counters so the handle can be
- * used again. */
+ * used again.  (A fused kernel is hard to debug from outside: cloud.baidu.com
+ * explainer, section 8; the record names the workgroup, task and event.) */
 mk_status mk_check_device_error(mk_handle *h, char *msg, size_t cap);
 
 /* Writes the task graph of the handle (records, event targets, queues) into
  * buf (host, cap bytes) in the export format of mk_plan_graph; *need gets the
- * size.  MK_E_INVALID if cap is too small. */
+ * size.  MK_E_INVALID if cap is too small.  (The task graph: MPK news page,
+ * part 1; koas-w.github.io notes, "SM-level task graph".) */
 mk_status mk_export_graph(const mk_handle *h, void *buf, size_t cap, size_t *need);
 
 /* Test hook: synchronises the device and copies the event counters (summed
  * over their sub-counters) into host (n entries) and the step epoch into
- * *epoch.  After k steps from a fresh handle, counter e equals k * target(e). */
+ * *epoch.  After k steps from a fresh handle, counter e equals k * target(e)
+ * (counters that finishing tasks increment and waiting tasks compare with
+ * their target: Hazy Research megakernel news page, section 4). */
 mk_status mk_read_counters(mk_handle *h, uint32_t *host, size_t n, uint32_t *epoch);
 
 /* Test hook: synchronises and copies per-task execution counts (n_tasks
- * entries, host) — each task runs exactly once per step. */
+ * entries, host) — each task runs exactly once per step (every instruction of
+ * the queues executes once per forward: Hazy Research megakernel news page,
+ * section 4). */
 mk_status mk_read_task_counts(mk_handle *h, uint32_t *host, size_t n);
 
 /* Trace (when built with trace=1): per task of the last step, sixteen uint64
@@ -174,8 +209,10 @@ mk_status mk_read_task_counts(mk_handle *h, uint32_t *host, size_t n);
  * section 5). */
 mk_status mk_read_trace(mk_handle *h, uint64_t *host, size_t n);
 
+/* Frees every allocation of the handle (synchronises the device first).  NULL is a no-op. */
 void mk_destroy(mk_handle *h);
 
+/* Static text of a status code ("unknown status" for values outside mk_status). */
 const char *mk_status_str(mk_status s);
 
 /* ---- One-kernel-per-op baseline ----------------------------------------------
@@ -196,19 +233,25 @@ const char *mk_status_str(mk_status s);
  * tokens, positions and logits are laid out as for mk_decode_step. */
 typedef struct mkb_handle mkb_handle;
 
+/* Validates the description against the limits above and allocates the baseline's activation buffers
+ * (the weights are read in place).  Errors: MK_E_INVALID (NULL pointers, batch outside 1..32, a mixture
+ * of experts, head_dim other than 64 or 128), MK_E_UNSUPPORTED (projection shapes outside the limits
+ * above), MK_E_NOMEM, MK_E_HIP.  (One kernel per
+ * operator, a launch boundary as the only synchronisation: Hazy Research megakernel news page, section 3.) */
 mk_status mkb_create(const mk_model_desc *desc, int32_t batch, int32_t max_ctx, mkb_handle **out);
 
 /* Enqueues the step's kernels on `stream`.  tokens/positions (dev) int32 [batch]:
  * as for mk_decode_step.  When advance != 0 the last kernel also stores the
  * next tokens into tokens[] and increments every positions[b], so a graph
- * captured from one call can be replayed for consecutive greedy steps. */
+ * captured from one call can be replayed for consecutive greedy steps.  Errors: MK_E_INVALID (NULL
+ * handle/tokens/positions/kv_cache), MK_E_HIP. */
 mk_status mkb_decode_step(mkb_handle *h, int32_t *tokens, int32_t *positions, void *kv_cache, float *logits,
                           void *stream, int32_t advance);
 
 const int32_t *mkb_next_tokens(const mkb_handle *h); /* (dev) int32 [batch] */
 const float *mkb_hidden_out(const mkb_handle *h);    /* (dev) float [batch][hidden] */
 int32_t mkb_launches_per_step(const mkb_handle *h);  /* kernels the last mkb_decode_step enqueued (0 before any) */
-void mkb_destroy(mkb_handle *h);
+void mkb_destroy(mkb_handle *h);                     /* frees the handle; NULL is a no-op */
 
 /* ---- Measurement microbenchmarks ----------------------------------------------
  * The costs the megakernel trades against each other, each measured on the current

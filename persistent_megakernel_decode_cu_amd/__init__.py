@@ -47,13 +47,16 @@ class ModelDesc(ctypes.Structure):
 
 class Options(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("sched", "n_workgroups", "policy", "attn_splits", "debug_timeout_ms",
-                                               "debug_drop_signal", "trace", "cooperative")] + \
-               [("reserved", ctypes.c_int32 * 8)]
+                                               "debug_drop_signal", "trace", "cooperative", "page_kib", "poison")] + \
+               [("reserved", ctypes.c_int32 * 6)]
 
 
-def options(sched=0, n_workgroups=0, policy=0, attn_splits=0, debug_timeout_ms=0, debug_drop_signal=-1, trace=0,
-            cooperative=0):
-    return Options(sched, n_workgroups, policy, attn_splits, debug_timeout_ms, debug_drop_signal, trace, cooperative)
+def options(sched=0, n_workgroups=0, policy=0, attn_splits=0, debug_timeout_ms=0, drop_signal_of_task=None,
+            trace=0, cooperative=0, page_kib=0, poison=0):
+    """mk_options; drop_signal_of_task: index of a task that skips its signal (tests of the timeout path)."""
+    drop = 0 if drop_signal_of_task is None else drop_signal_of_task + 1
+    return Options(sched, n_workgroups, policy, attn_splits, debug_timeout_ms, drop, trace, cooperative, page_kib,
+                   poison)
 
 
 # task record (48 bytes, mirrors mk::Task)

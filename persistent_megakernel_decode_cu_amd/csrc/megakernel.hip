@@ -2549,6 +2549,20 @@ hipError_t launch_step(const Params* dparams, const StepArgs& a, uint32_t grid, 
     return hipGetLastError();
 }
 
+// Poison mode: fill each span with its pattern (NaN for floats and bf16 pairs, -1 for expert ids).
+__global__ void __launch_bounds__(256) poison_kernel(PoisonSpans s) {
+    for (int i = 0; i < s.n; ++i) {
+        uint32_t* w = (uint32_t*)s.ptr[i];
+        for (uint64_t j = (uint64_t)blockIdx.x * 256 + threadIdx.x; j < s.words[i]; j += (uint64_t)gridDim.x * 256)
+            w[j] = s.pattern[i];
+    }
+}
+
+hipError_t launch_poison(const PoisonSpans& s, hipStream_t stream) {
+    hipLaunchKernelGGL(poison_kernel, dim3(256), dim3(256), 0, stream, s);
+    return hipGetLastError();
+}
+
 // Weight repacking at build time: one workgroup per copy operation.
 __global__ void __launch_bounds__(256) repack_kernel(const CopyOp* ops, uint8_t* dst) {
     const CopyOp op = ops[blockIdx.x];

@@ -19,6 +19,8 @@ struct mk_handle {
     int device = 0;
     int W = 0;
     bool cooperative = false;  // plain launch unless asked (mk_options.cooperative)
+    bool poison = false;       // fill the step's scratch with NaN before every step (mk_options.poison)
+    size_t xop_bytes = 0;
     bool tied = true;
     Graph g;
     Params p;           // host copy
@@ -73,9 +75,10 @@ mk_status plan(const mk_model_desc* desc, int32_t batch, int32_t max_ctx, const 
     if (!desc) return MK_E_INVALID;
     mk_options o;
     memset(&o, 0, sizeof(o));
-    o.debug_drop_signal = -1;
     if (opt) o = *opt;
     if (o.sched < 0 || o.sched > 2 || o.policy < 0 || o.policy > 1) return MK_E_INVALID;
+    if (o.page_kib != 0 && o.page_kib != 16) return MK_E_INVALID;  // the page size is part of the weight layout
+    if (o.poison < 0 || o.poison > 1) return MK_E_INVALID;
     PlanOptions po;
     po.attn_splits = o.attn_splits;
     Tiling T;
@@ -278,10 +281,10 @@ mk_status mk_build_graph(const mk_model_desc* desc, int32_t batch, int32_t max_c
     if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) return MK_E_NO_DEVICE;
     mk_options o;
     memset(&o, 0, sizeof(o));
-    o.debug_drop_signal = -1;
     if (opt) o = *opt;
     mk_handle* h = new mk_handle();
     h->cooperative = o.cooperative != 0;
+    h->poison = o.poison != 0;
     HIPCHK(hipGetDevice(&h->device));
     hipDeviceProp_t prop;
     HIPCHK(hipGetDeviceProperties(&prop, h->device));
@@ -306,7 +309,7 @@ mk_status mk_build_graph(const mk_model_desc* desc, int32_t batch, int32_t max_c
     p.eps = desc->rms_eps;
     p.sched = (uint32_t)o.sched;
     p.n_tasks = (uint32_t)h->g.tasks.size();
-    p.drop_task = o.debug_drop_signal >= 0 ? (uint32_t)o.debug_drop_signal : NONE;
+    p.drop_task = o.debug_drop_signal > 0 ? (uint32_t)(o.debug_drop_signal - 1) : NONE;
     const double ms = o.debug_timeout_ms > 0 ? o.debug_timeout_ms : 2000.0;
     p.timeout = (unsigned long long)(ms * 1e5);  // 100 MHz clock
     h->n_events = h->g.target.size();
@@ -375,6 +378,7 @@ mk_status mk_build_graph(const mk_model_desc* desc, int32_t batch, int32_t max_c
         // (then, for a mixture of experts, every expert's m rows)
         const size_t xop_elems =
             ((size_t)T.L * T.nq * T.d + (size_t)T.L * T.f + (size_t)T.L * T.E * T.fe) * n_sg * 32;
+        h->xop_bytes = xop_elems * 2;
         ALLOC(p.xop, xop_elems * 2, true);
         ALLOC(p.aticket, (size_t)2 * T.L * T.B * T.nkv * 4, true);
         if (T.E) {
@@ -442,6 +446,30 @@ mk_status mk_decode_step(mk_handle* h, const int32_t* tokens, const int32_t* pos
     a.kc = (uint16_t*)kv_cache;
     a.vc = (uint16_t*)kv_cache + (size_t)T.L * T.B * T.nkv * (size_t)T.C * T.d;
     a.logits = logits;
+    if (h->poison) {
+        // everything a producer of this step overwrites: a task that read it first would see NaN
+        const Params& p = h->p;
+        PoisonSpans ps;
+        memset(&ps, 0, sizeof(ps));
+        auto span = [&](void* ptr, size_t bytes, uint32_t pattern) {
+            if (!ptr || !bytes) return;
+            ps.ptr[ps.n] = ptr;
+            ps.words[ps.n] = bytes / 4;
+            ps.pattern[ps.n] = pattern;
+            ++ps.n;
+        };
+        const uint32_t fnan = 0x7fc00000u, bnan2 = 0x7fc07fc0u, neg1 = 0xffffffffu;
+        span(p.q, (size_t)T.B * T.nq * T.d * 4, fnan);
+        span(p.part, (size_t)T.B * T.nkv * T.attn_splits * T.grp * (T.d + 2) * 4, fnan);
+        span(p.m, (size_t)T.B * T.f * 4, fnan);
+        span(p.xop, h->xop_bytes, bnan2);
+        span(p.rlogit, (size_t)T.L * T.B * T.E * 4, fnan);
+        span(p.eids, (size_t)T.L * T.B * T.topk * 4, neg1);
+        span(p.hidden, (size_t)T.B * T.h * 4, fnan);
+        span(logits, (size_t)T.B * T.V * 4, fnan);
+        hipError_t e = launch_poison(ps, (hipStream_t)stream);
+        if (e != hipSuccess) return MK_E_HIP;
+    }
     hipError_t e = launch_step(h->dparams, a, (uint32_t)h->W, (hipStream_t)stream, h->cooperative);
     if (e == hipErrorCooperativeLaunchTooLarge) return MK_E_NOT_RESIDENT;
     return e == hipSuccess ? MK_OK : MK_E_HIP;

@@ -101,6 +101,15 @@ hipError_t launch_repack_tiles(const TileOp* ops, uint32_t n_ops, const uint8_t*
                                hipStream_t stream);
 
 hipError_t launch_step(const Params* dparams, const StepArgs& a, uint32_t grid, hipStream_t stream, bool cooperative);
+
+// Poison mode: up to 8 spans of 32-bit words filled with a pattern before a step.
+struct PoisonSpans {
+    void* ptr[8];
+    uint64_t words[8];
+    uint32_t pattern[8];
+    int32_t n;
+};
+hipError_t launch_poison(const PoisonSpans& s, hipStream_t stream);
 int step_threads();
 size_t step_lds_bytes();
 const void* step_kernel_ptr();

@@ -179,7 +179,7 @@ def test_dropped_signal_is_reported_with_its_event():
     tasks = probe.graph["tasks"]
     probe.close()
     victim = int(np.nonzero((tasks["layer"] == 1) & (tasks["op"] == mk.OP_OPROJ))[0][0])
-    run = Runner(cfg, w, 1, 256, kc, vc, debug_drop_signal=victim, debug_timeout_ms=20)
+    run = Runner(cfg, w, 1, 256, kc, vc, drop_signal_of_task=victim, debug_timeout_ms=20)
     run.step(tok, pos)
     torch.cuda.synchronize()
     err = mk.mk_check_device_error(run.h)

@@ -18,9 +18,14 @@ from oracle import taskgraph as tg
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mk.h")
 FIXTURE = os.path.join(ROOT, "tests", "golden", "tiny_graph.txt")
+BATCH_FIXTURE = os.path.join(ROOT, "tests", "golden", "batch_graph.txt")
+MOE_FIXTURE = os.path.join(ROOT, "tests", "golden", "moe_graph.txt")
 OPS = {"QKV": tg.OP_QKV, "ATTN": tg.OP_ATTN, "OPROJ": tg.OP_OPROJ, "GATEUP": tg.OP_GATEUP, "DOWN": tg.OP_DOWN,
-       "LMHEAD": tg.OP_LMHEAD}
+       "LMHEAD": tg.OP_LMHEAD, "ROUTE": tg.OP_ROUTE, "EGU": tg.OP_EGU, "EDOWN": tg.OP_EDOWN}
 TOY = synth.configs.ModelConfig("toy-1layer", 1, 128, 1, 1, 128, 128, 64, True, 10000.0)
+# the same attention shape with 4 experts of SwiGLU 128 and top-2 routing
+TOY_MOE = synth.configs.ModelConfig("toy-moe-1layer", 1, 128, 1, 1, 128, 0, 64, True, 10000.0,
+                                    n_experts=4, top_k=2, expert_ffn=128)
 
 
 def declared_functions():
@@ -94,9 +99,9 @@ def compare(ex, g, cfg, W, C, B=1):
         np.testing.assert_array_equal(ex["queue"][qo[w]:qo[w + 1]], g["queues"][w], err_msg=f"queue {w}")
 
 
-def read_fixture():
+def read_fixture(path=FIXTURE):
     rows, meta = [], {}
-    for line in open(FIXTURE):
+    for line in open(path):
         if line.startswith("#"):
             m = re.match(r"#\s*(targets|queue \d+):\s*(.*)", line)
             if m:
@@ -126,6 +131,46 @@ def test_oracle_builder_matches_hand_derived_toy_graph():
 def test_library_planner_matches_hand_derived_toy_graph():
     g = tg.build(TOY, 1, 64, 2)
     compare(plan(TOY, 2, C=64), g, TOY, 2, 64)
+
+
+def _fixture_equals(path, g, n_tasks):
+    rows, meta = read_fixture(path)
+    assert len(g["tasks"]) == len(rows) == n_tasks
+    for want, got in zip(rows, g["tasks"]):
+        for k, v in want.items():
+            assert got[k] == v, (want["id"], k, got[k], v)
+    assert g["target"] == meta["targets"]
+    assert g["queues"] == [meta["queue 0"], meta["queue 1"]]
+
+
+def test_oracle_builder_matches_hand_derived_batch_graph():
+    """Three sequences with four fixed-length chunk slots: slot order 0, 1, 3, 2 outermost, then sequences;
+    one event per KV group counting every slot task of every sequence (the O-projection waits for all of
+    them, the run-time merge included); GEMV tiles of the single column group."""
+    g = tg.build(TOY, 3, 64, 2, attn_splits=4)
+    _fixture_equals(BATCH_FIXTURE, g, 44)
+    tg.check(g, TOY, 3)
+
+
+def test_library_planner_matches_hand_derived_batch_graph():
+    g = tg.build(TOY, 3, 64, 2, attn_splits=4)
+    _fixture_equals(BATCH_FIXTURE, g, 44)
+    compare(plan(TOY, 2, B=3, C=64, attn_splits=4), g, TOY, 2, 64, B=3)
+
+
+def test_oracle_builder_matches_hand_derived_moe_graph():
+    """Four experts, top-2: one router tile raising every expert's event, each expert's gate/up tile raising
+    its own, each expert's down tile waiting for its expert (two producers each) and feeding the layer's
+    residual event (four producers)."""
+    g = tg.build(TOY_MOE, 2, 64, 2)
+    _fixture_equals(MOE_FIXTURE, g, 39)
+    tg.check(g, TOY_MOE, 2)
+
+
+def test_library_planner_matches_hand_derived_moe_graph():
+    g = tg.build(TOY_MOE, 2, 64, 2)
+    _fixture_equals(MOE_FIXTURE, g, 39)
+    compare(plan(TOY_MOE, 2, B=2, C=64), g, TOY_MOE, 2, 64, B=2)
 
 
 CASES = [
@@ -216,6 +261,39 @@ def test_planner_rejects_what_it_does_not_implement():
     with pytest.raises(mk.MkError):  # the merges read at most 16 chunk partials
         plan(cfg, 16, B=3, attn_splits=17)
     assert plan(cfg, 16, B=3, attn_splits=16)["header"]["attn_splits"] == 16
+
+
+def _plan_with(cfg, W, opt):
+    names = ["tok_embed", "final_norm"] + ([] if cfg.tied else ["lm_head"])
+    for l in range(cfg.n_layers):
+        names += [f"l{l}.{n}" for n in ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up", "w_down")]
+    model = mk.Model(cfg, {n: _Fake() for n in names})
+    return mk.mk_plan_graph(model.desc, 1, 512, opt, W)
+
+
+def test_options_zero_filled_is_the_default_and_bad_values_are_refused():
+    """A zero-filled mk_options is the default configuration (the same graph as NULL options); the page size
+    is fixed at 16 KiB (0 or 16 accepted); poison is 0 or 1."""
+    import ctypes
+    cfg = synth.configs.TINY
+    lib = mk.load()
+    names = ["tok_embed", "final_norm"] + [f"l{l}.{n}" for l in range(cfg.n_layers)
+                                           for n in ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate",
+                                                     "w_up", "w_down")]
+    model = mk.Model(cfg, {n: _Fake() for n in names})
+    need = ctypes.c_size_t(0)
+    assert lib.mk_plan_graph(model.desc, 1, 512, None, 4, None, 0, ctypes.byref(need)) == mk.MK_E_INVALID
+    buf = ctypes.create_string_buffer(need.value)
+    assert lib.mk_plan_graph(model.desc, 1, 512, None, 4, buf, need.value, ctypes.byref(need)) == mk.MK_OK
+    assert _plan_with(cfg, 4, mk.Options()) == buf.raw
+    assert _plan_with(cfg, 4, mk.options(page_kib=16)) == buf.raw
+    for bad in (mk.options(page_kib=8), mk.options(page_kib=32), mk.options(poison=2), mk.options(sched=3)):
+        with pytest.raises(mk.MkError) as ei:
+            _plan_with(cfg, 4, bad)
+        assert ei.value.status == mk.MK_E_INVALID
+    # the dropped-signal test hook: task n - 1 for a positive value, off for 0
+    assert mk.options(drop_signal_of_task=0).debug_drop_signal == 1
+    assert mk.options().debug_drop_signal == 0
 
 
 @pytest.mark.parametrize("W", [1, 3, 16, 37])
