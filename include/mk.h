@@ -152,6 +152,24 @@ size_t mk_kv_cache_bytes(const mk_handle *h);
 mk_status mk_decode_step(mk_handle *h, const int32_t *tokens, const int32_t *positions, void *kv_cache,
                          float *logits, void *stream);
 
+/* The same step for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): enqueues a small fill
+ * kernel and the step kernel on `stream` and calls no hipMalloc, hipFree or allocating
+ * library routine.  Arguments, outputs and errors as mk_decode_step.  The step's scratch
+ * (event counters, control words, residual accumulators, query rows, attention partials,
+ * m rows, operand regions, argmax keys and tickets) lives in one file-scope device array
+ * of 32 MiB that each GPU running the library holds until the process ends, instead of
+ * the handle's buffers; the fill kernel first clears what must start at zero (so every
+ * call starts from step 1 of a fresh handle), since the array keeps whatever the last
+ * call on that GPU left in it.  Calls that overlap on one GPU (on two streams, or from
+ * two threads) share the array and race: the caller must order them.  The handle (built
+ * by mk_build_graph) still owns the weights, task graph and outputs.  MK_E_UNSUPPORTED
+ * when the handle's scratch exceeds the array (about 1.1 MiB at the 1B shape with one
+ * sequence, 20 MiB with 16 sequences, 40 MiB with 32: refused).  mk_check_device_error
+ * reports a device error of such a step until the next one on that GPU. */
+mk_status mk_decode_step_noalloc(mk_handle *h, const int32_t *tokens, const int32_t *positions, void *kv_cache,
+                                 float *logits, void *stream);
+
 /* (dev) int32 [batch]: greedy next token of the last step (lowest index among
  * equal maximal logits), the argmax of the LM head that ends the forward (Hazy
  * Research megakernel news page, section 5: the LM head closes the forward).

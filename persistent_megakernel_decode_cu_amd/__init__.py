@@ -93,6 +93,8 @@ def load():
     lib.mk_kv_cache_bytes.restype = ctypes.c_size_t
     lib.mk_decode_step.argtypes = [_P, _P, _P, _P, _P, _P]
     lib.mk_decode_step.restype = ctypes.c_int
+    lib.mk_decode_step_noalloc.argtypes = [_P, _P, _P, _P, _P, _P]
+    lib.mk_decode_step_noalloc.restype = ctypes.c_int
     for n in ("mk_next_tokens", "mk_hidden_out", "mk_expert_ids"):
         getattr(lib, n).argtypes = [_P]
         getattr(lib, n).restype = _P
@@ -173,6 +175,12 @@ def mk_kv_cache_bytes(h):
 
 def mk_decode_step(h, tokens_ptr, positions_ptr, kv_ptr, logits_ptr, stream_ptr):
     _check(load().mk_decode_step(h, tokens_ptr, positions_ptr, kv_ptr, logits_ptr, stream_ptr), "mk_decode_step")
+
+
+def mk_decode_step_noalloc(h, tokens_ptr, positions_ptr, kv_ptr, logits_ptr, stream_ptr):
+    """The allocation-free step (scratch in the library's static per-GPU array)."""
+    _check(load().mk_decode_step_noalloc(h, tokens_ptr, positions_ptr, kv_ptr, logits_ptr, stream_ptr),
+           "mk_decode_step_noalloc")
 
 
 def mk_next_tokens(h):

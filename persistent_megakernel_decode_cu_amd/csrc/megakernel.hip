@@ -30,6 +30,8 @@
 // ordinary (LDS-DMA) loads.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "mk_internal.h"
 #include "runtime.h"
 
@@ -2561,6 +2563,32 @@ __global__ void __launch_bounds__(256) poison_kernel(PoisonSpans s) {
 hipError_t launch_poison(const PoisonSpans& s, hipStream_t stream) {
     hipLaunchKernelGGL(poison_kernel, dim3(256), dim3(256), 0, stream, s);
     return hipGetLastError();
+}
+
+// ---- the allocation-free step's scratch ----------------------------------------------------
+//
+// mk_decode_step_noalloc keeps the step's scratch (event counters, control words, residual
+// accumulators, query rows, attention partials, m rows, operand regions, argmax keys, tickets) in
+// this file-scope array instead of handle-owned buffers.  Each GPU holds its own copy from the
+// moment the library's code object is loaded on it until the process ends.  In host code `scratch`
+// names a host-side stand-in, not the device array: only the address hipGetSymbolAddress returns
+// for the current device may be handed to kernels or copies.
+static __device__ __align__(256) uint8_t scratch[NOALLOC_SCRATCH_BYTES];
+
+hipError_t noalloc_scratch_base(int device, uint8_t** out) {
+    static std::mutex mu;
+    static void* addr[MAX_DEVICES] = {};
+    if (device < 0 || device >= MAX_DEVICES) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[device]) {
+        void* ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));  // the current device's copy
+        if (e != hipSuccess) return e;
+        if (!ptr) return hipErrorInvalidSymbol;
+        addr[device] = ptr;
+    }
+    *out = (uint8_t*)addr[device];
+    return hipSuccess;
 }
 
 // Weight repacking at build time: one workgroup per copy operation.

@@ -21,6 +21,11 @@ struct mk_handle {
     bool cooperative = false;  // plain launch unless asked (mk_options.cooperative)
     bool poison = false;       // fill the step's scratch with NaN before every step (mk_options.poison)
     size_t xop_bytes = 0;
+    // the allocation-free step: the same parameters with the step's scratch in the per-GPU static
+    // array (null when this handle's scratch does not fit it)
+    Params p_na;
+    Params* dparams_na = nullptr;
+    size_t na_bytes = 0;  // scratch this handle's steps need
     bool tied = true;
     Graph g;
     Params p;           // host copy
@@ -228,6 +233,8 @@ mk_status rearm(mk_handle* h) {
     return MK_OK;
 }
 
+mk_status enqueue_poison(mk_handle* h, const Params& p, float* logits, hipStream_t stream);
+
 bool desc_ok(const mk_model_desc* d) {
     if (!d || !d->tok_embed || !d->final_norm || (!d->tied_lm_head && !d->lm_head)) return false;
     if (d->n_layers > 0 && !d->layers) return false;
@@ -412,6 +419,55 @@ mk_status mk_build_graph(const mk_model_desc* desc, int32_t batch, int32_t max_c
         mk_destroy(h);
         return MK_E_HIP;
     }
+    {
+        // the allocation-free step: the same buffers laid out in this GPU's static scratch array
+        // (tasks, queues, weights, RoPE table, outputs and the event-driven lists stay the handle's)
+        size_t at = 0;
+        auto take = [&](size_t bytes) {  // 256-byte aligned, at least 256 bytes (as dalloc)
+            const size_t o = at;
+            at += std::max<size_t>(256, (bytes + 255) / 256 * 256);
+            return o;
+        };
+        const size_t o_ctr = take(h->n_events * 8 * 32 * 4), o_state = take(ST_WORDS * 4);
+        const size_t o_q = take((size_t)T.B * T.nq * T.d * 4);
+        const size_t o_part = take((size_t)T.B * T.nkv * T.attn_splits * T.grp * (T.d + 2) * 4);
+        const size_t o_m = take((size_t)T.B * T.f * 4), o_acc = take(h->acc_bytes);
+        const size_t o_xop = T.B > 1 ? take(h->xop_bytes) : 0;
+        const size_t o_at = T.B > 1 ? take((size_t)2 * T.L * T.B * T.nkv * 4) : 0;
+        const size_t o_rl = T.E ? take((size_t)T.L * T.B * T.E * 4) : 0;
+        const size_t o_key = take(sizeof(unsigned long long) * 2 * T.B), o_ticket = take(4 * (size_t)T.B);
+        const size_t o_rqs = o.sched == 2 ? take(h->g.tasks.size() * 4) : 0;
+        h->na_bytes = at;
+        if (at <= NOALLOC_SCRATCH_BYTES) {
+            uint8_t* base = nullptr;
+            const hipError_t e = noalloc_scratch_base(h->device, &base);
+            if (e != hipSuccess) {
+                mk_destroy(h);
+                return hip_fail(e);
+            }
+            Params q = p;
+            q.ctr = (uint32_t*)(base + o_ctr);
+            q.state = (uint32_t*)(base + o_state);
+            q.q = (float*)(base + o_q);
+            q.part = (float*)(base + o_part);
+            q.m = (float*)(base + o_m);
+            q.acc = (float*)(base + o_acc);
+            q.xop = T.B > 1 ? (uint16_t*)(base + o_xop) : nullptr;
+            q.aticket = T.B > 1 ? (uint32_t*)(base + o_at) : nullptr;
+            q.rlogit = T.E ? (float*)(base + o_rl) : nullptr;
+            q.key = (unsigned long long*)(base + o_key);
+            q.ticket = (uint32_t*)(base + o_ticket);
+            q.rq_stamp = o.sched == 2 ? (uint32_t*)(base + o_rqs) : nullptr;
+            h->p_na = q;
+            Params* dq;
+            ALLOC2(dq, sizeof(Params));
+            h->dparams_na = dq;
+            if (up(dq, &q, sizeof(Params)) != hipSuccess) {
+                mk_destroy(h);
+                return MK_E_HIP;
+            }
+        }
+    }
     Params* dp;
     ALLOC2(dp, sizeof(Params));
     h->dparams = dp;
@@ -447,8 +503,64 @@ mk_status mk_decode_step(mk_handle* h, const int32_t* tokens, const int32_t* pos
     a.vc = (uint16_t*)kv_cache + (size_t)T.L * T.B * T.nkv * (size_t)T.C * T.d;
     a.logits = logits;
     if (h->poison) {
-        // everything a producer of this step overwrites: a task that read it first would see NaN
-        const Params& p = h->p;
+        const mk_status st = enqueue_poison(h, h->p, logits, (hipStream_t)stream);
+        if (st != MK_OK) return st;
+    }
+    hipError_t e = launch_step(h->dparams, a, (uint32_t)h->W, (hipStream_t)stream, h->cooperative);
+    if (e == hipErrorCooperativeLaunchTooLarge) return MK_E_NOT_RESIDENT;
+    return e == hipSuccess ? MK_OK : MK_E_HIP;
+}
+
+mk_status mk_decode_step_noalloc(mk_handle* h, const int32_t* tokens, const int32_t* positions, void* kv_cache,
+                                 float* logits, void* stream) {
+    if (!h || !tokens || !positions || (!kv_cache && h->g.T.L > 0)) return MK_E_INVALID;
+    if (!h->dparams_na) return MK_E_UNSUPPORTED;  // this handle's scratch exceeds the static array
+    const Tiling& T = h->g.T;
+    const Params& p = h->p_na;
+    // This GPU's array keeps whatever the last call (of any handle) left in it: clear what must start
+    // at zero and start the step at epoch 1 (parity 1), with a fill kernel (no memset, no allocation).
+    PoisonSpans cs;
+    memset(&cs, 0, sizeof(cs));
+    auto span = [&](void* ptr, size_t bytes, uint32_t pattern) {
+        if (!ptr || !bytes) return;
+        cs.ptr[cs.n] = ptr;
+        cs.words[cs.n] = bytes / 4;
+        cs.pattern[cs.n] = pattern;
+        ++cs.n;
+    };
+    const size_t nacc = (size_t)(2 * T.L + 1) * T.B * T.h, nat = (size_t)T.L * T.B * T.nkv;
+    span(p.ctr, h->n_events * 8 * 32 * 4, 0u);
+    span(p.state + 1, (ST_WORDS - 1) * 4, 0u);
+    span(p.state + ST_EPOCH, 4, 1u);  // ST_EPOCH is word 0
+    span(p.acc + nacc, nacc * 4, 0u);  // parity 1
+    span(p.key + T.B, (size_t)T.B * 8, 0u);
+    span(p.ticket, (size_t)T.B * 4, 0u);
+    span(p.aticket ? p.aticket + nat : nullptr, nat * 4, 0u);
+    span(p.rq_stamp, h->g.tasks.size() * 4, 0u);
+    hipError_t e = launch_poison(cs, (hipStream_t)stream);
+    if (e != hipSuccess) return MK_E_HIP;
+    if (h->poison) {
+        const mk_status st = enqueue_poison(h, p, logits, (hipStream_t)stream);
+        if (st != MK_OK) return st;
+    }
+    StepArgs a;
+    a.tokens = tokens;
+    a.positions = positions;
+    a.kc = (uint16_t*)kv_cache;
+    a.vc = (uint16_t*)kv_cache + (size_t)T.L * T.B * T.nkv * (size_t)T.C * T.d;
+    a.logits = logits;
+    e = launch_step(h->dparams_na, a, (uint32_t)h->W, (hipStream_t)stream, h->cooperative);
+    if (e == hipErrorCooperativeLaunchTooLarge) return MK_E_NOT_RESIDENT;
+    return e == hipSuccess ? MK_OK : MK_E_HIP;
+}
+
+}  // extern "C"
+
+namespace {
+// Poison mode: everything a producer of the step overwrites, so a task that read it first would see NaN.
+mk_status enqueue_poison(mk_handle* h, const Params& p, float* logits, hipStream_t stream) {
+    const Tiling& T = h->g.T;
+    {
         PoisonSpans ps;
         memset(&ps, 0, sizeof(ps));
         auto span = [&](void* ptr, size_t bytes, uint32_t pattern) {
@@ -467,13 +579,14 @@ mk_status mk_decode_step(mk_handle* h, const int32_t* tokens, const int32_t* pos
         span(p.eids, (size_t)T.L * T.B * T.topk * 4, neg1);
         span(p.hidden, (size_t)T.B * T.h * 4, fnan);
         span(logits, (size_t)T.B * T.V * 4, fnan);
-        hipError_t e = launch_poison(ps, (hipStream_t)stream);
+        hipError_t e = launch_poison(ps, stream);
         if (e != hipSuccess) return MK_E_HIP;
     }
-    hipError_t e = launch_step(h->dparams, a, (uint32_t)h->W, (hipStream_t)stream, h->cooperative);
-    if (e == hipErrorCooperativeLaunchTooLarge) return MK_E_NOT_RESIDENT;
-    return e == hipSuccess ? MK_OK : MK_E_HIP;
+    return MK_OK;
 }
+}  // namespace
+
+extern "C" {
 
 const int32_t* mk_next_tokens(const mk_handle* h) { return h ? h->p.next : nullptr; }
 const float* mk_hidden_out(const mk_handle* h) { return h ? h->p.hidden : nullptr; }
@@ -484,6 +597,14 @@ mk_status mk_check_device_error(mk_handle* h, char* msg, size_t cap) {
     HIPCHK(hipDeviceSynchronize());
     uint32_t rec[8];
     HIPCHK(hipMemcpy(rec, h->p.state + ST_ERR, sizeof(rec), hipMemcpyDeviceToHost));
+    if (rec[0] == ERR_NONE && h->dparams_na) {
+        // the last allocation-free step's record (kept until the next such step on this GPU clears it)
+        HIPCHK(hipMemcpy(rec, h->p_na.state + ST_ERR, sizeof(rec), hipMemcpyDeviceToHost));
+        if (rec[0] != ERR_NONE) {
+            const uint32_t zero[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+            HIPCHK(hipMemcpy(h->p_na.state + ST_ERR, zero, sizeof(zero), hipMemcpyHostToDevice));
+        }
+    }
     if (rec[0] == ERR_NONE) return MK_OK;
     if (msg && cap) {
         const char* what = rec[0] == ERR_TIMEOUT_EVENT ? "timeout waiting for an event counter"

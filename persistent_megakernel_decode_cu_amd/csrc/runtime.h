@@ -110,6 +110,13 @@ struct PoisonSpans {
     int32_t n;
 };
 hipError_t launch_poison(const PoisonSpans& s, hipStream_t stream);
+
+// The allocation-free step: its scratch is a file-scope device array of this many bytes, one per GPU.
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)32 << 20;
+constexpr int MAX_DEVICES = 64;
+// Device address of the current device's copy of that array (`device` is the current device's id),
+// looked up once per device and kept.
+hipError_t noalloc_scratch_base(int device, uint8_t** out);
 int step_threads();
 size_t step_lds_bytes();
 const void* step_kernel_ptr();
