@@ -154,6 +154,20 @@ __device__ __forceinline__ void st16_dev(uint16_t* base, uint32_t idx, uint16_t 
     __builtin_amdgcn_raw_buffer_store_b16(v, r, idx * 2, 0, 16 /* sc1 */);
 }
 __device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Cross-check build of the synchronisation protocol (-DMK_FENCED=1): agent-scope release fences before
+// every signal (counter, ticket or ready-queue stamp) and agent-scope acquire fences after every wait
+// that a signal ends, as the memory model's generic sequences would have them.  The default build
+// issues none (every cross-CU datum already goes through device-scope accesses; see the design notes).
+#ifndef MK_FENCED
+#define MK_FENCED 0
+#endif
+__device__ __forceinline__ void release_fence() {
+    if constexpr (MK_FENCED) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+}
+__device__ __forceinline__ void acquire_fence() {
+    if constexpr (MK_FENCED) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
 __device__ __forceinline__ void lgkm_wait_all() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 template <int N>
 __device__ __forceinline__ void vm_wait() {
@@ -430,7 +444,10 @@ __device__ __noinline__ bool wait_ready_slot(const Params* pp, uint32_t slot, ui
     CParams& p = P(pp);
     const uint64_t t0 = rtc();
     for (uint32_t it = 1;; ++it) {
-        if (uni(ld_dev(&p.rq_stamp[slot])) == epoch) return true;
+        if (uni(ld_dev(&p.rq_stamp[slot])) == epoch) {
+            acquire_fence();
+            return true;
+        }
         if (lds_ld(S.abort)) return false;
         if ((it & 63u) == 0u) {
             if (ld_dev(&p.state[ST_ABORT])) {
@@ -461,6 +478,7 @@ __device__ __noinline__ void launch_dependents(const Params* pp, uint32_t ev, ui
     }
     for (uint32_t j = (uint32_t)lane; j < n; j += 64) st_dev(&p.rq[base + j], p.cons[c0 + j]);
     vm_wait_all();
+    release_fence();
     for (uint32_t j = (uint32_t)lane; j < n; j += 64) st_dev(&p.rq_stamp[base + j], epoch);
     vm_wait_all();
 }
@@ -664,6 +682,7 @@ __device__ __forceinline__ bool await_inputs(const Params* pp, const Task& k, Ct
                 !uni(wait_event(pp, k.wait_ev, k.wait_nsub, want, k.id)))
                 return false;
         }
+        acquire_fence();
         const uint64_t tr = rtc();
         if (c.lane == 0) {
             lds_st(S.t_ready_lo, (uint32_t)tr);
@@ -672,7 +691,9 @@ __device__ __forceinline__ bool await_inputs(const Params* pp, const Task& k, Ct
         }
         return true;
     }
-    return lds_wait_ge(S.go, c.t + 1, pp, k.id);
+    const bool ok = lds_wait_ge(S.go, c.t + 1, pp, k.id);
+    acquire_fence();
+    return ok;
 }
 
 // Device-scope (sc1) loads of data written by other workgroups in this step,
@@ -1453,10 +1474,14 @@ __device__ __noinline__ bool op_attn(const Params* pp, uint32_t slot_, uint32_t 
         const uint32_t nch = (uint32_t)min(p.T.attn_splits, (ch.P + fl) / fl);
         const uint32_t want = nch * (uint32_t)min(G, NCW);
         uint32_t old = 0;
+        release_fence();
         if (lane == 0)
             old = addu_dev(&p.aticket[(((size_t)c.parity * p.T.L + k.layer) * p.T.B + b) * p.T.nkv + g], 1u);
         old = uni(old);
-        if (old + 1u == want) merge_chunks(pp, k.layer, b, g, ch.P, lane);
+        if (old + 1u == want) {
+            acquire_fence();
+            merge_chunks(pp, k.layer, b, g, ch.P, lane);
+        }
     }
     return true;
 }
@@ -1690,10 +1715,14 @@ __device__ __noinline__ bool op_attn_mfma(const Params* pp, uint32_t slot_, uint
             const uint32_t nch = (uint32_t)min(p.T.attn_splits, (ch.P + fl) / fl);
             const uint32_t want = nch * (uint32_t)min(G, NCW);
             uint32_t old = 0;
+            release_fence();
             if (lane == 0)
                 old = addu_dev(&p.aticket[(((size_t)c.parity * p.T.L + k.layer) * p.T.B + b) * p.T.nkv + g], 1u);
             old = uni(old);
-            if (old + 1u == want) merge_chunks(pp, k.layer, b, g, ch.P, lane);
+            if (old + 1u == want) {
+                acquire_fence();
+                merge_chunks(pp, k.layer, b, g, ch.P, lane);
+            }
         }
     }
     return true;
@@ -2341,9 +2370,11 @@ __device__ __noinline__ void finish_step(const Params* pp, uint32_t epoch, uint3
     CParams& p = P(pp);
     const int lane = threadIdx.x & 63;
     uint32_t old = 0;
+    release_fence();
     if (lane == 0) old = addu_dev(&p.ticket[0], 1u);
     old = uni(old);
     if (old + 1u != epoch * (uint32_t)(p.T.n_lm_tiles * n_col_groups(p))) return;
+    acquire_fence();
     const int B = p.T.B;
     for (int b = lane; b < B; b += 64) {
         const unsigned long long key =
@@ -2425,11 +2456,13 @@ __device__ __noinline__ void compute(const Params* pp, uint32_t epoch, int wave)
         if (p0.trace && c.lane == 0) lds_st(S.tw_epi[c.wave], (uint32_t)rtc());
         vm_wait_all();
         if (p0.trace && c.lane == 0) lds_st(S.tw_ack[c.wave], (uint32_t)rtc());
+        release_fence();  // (fenced build) this wave's results before the workgroup's signal
         lgkm_wait_all();
         if (c.lane == 0) lds_add(S.done, 1u);
         if (c.wave == 0) {
             if (!lds_wait_ge(S.done, NCW * (t + 1), pp, k.id)) return;
             const uint64_t t_stored = rtc();  // every wave's results acknowledged by memory
+            release_fence();
             CParams& p = P(pp);
             const int n_sig = (k.flags & TF_SIGRANGE) ? p0.T.E : 1;  // router tiles: every expert's event
             bool activated = false;
