@@ -93,8 +93,9 @@ def load():
     lib.mk_kv_cache_bytes.restype = ctypes.c_size_t
     lib.mk_decode_step.argtypes = [_P, _P, _P, _P, _P, _P]
     lib.mk_decode_step.restype = ctypes.c_int
-    lib.mk_decode_step_noalloc.argtypes = [_P, _P, _P, _P, _P, _P]
-    lib.mk_decode_step_noalloc.restype = ctypes.c_int
+    if hasattr(lib, "mk_decode_step_noalloc"):  # (older variant builds loaded through MK_LIBRARY lack it)
+        lib.mk_decode_step_noalloc.argtypes = [_P, _P, _P, _P, _P, _P]
+        lib.mk_decode_step_noalloc.restype = ctypes.c_int
     for n in ("mk_next_tokens", "mk_hidden_out", "mk_expert_ids"):
         getattr(lib, n).argtypes = [_P]
         getattr(lib, n).restype = _P

@@ -46,11 +46,12 @@ constexpr int FIFO = 16;               // task records in flight in LDS
 constexpr int XS = MAX_ACT;            // activation staging (floats)
 constexpr int ROWRES = MAX_TILE_ROWS;  // per-task row results (floats)
 constexpr int LPP = 16 / NLW;          // loads per page per loader wave
-// Pages in flight per loader wave.  48 KiB in flight per CU (12 MiB over the chip)
-// already keeps HBM busy; a deeper queue only adds queueing delay to every other
-// load, including the small latency-critical ones between dependent tasks.
+// Pages in flight per loader wave: two, i.e. 32 KiB per CU and 8 MiB over the chip.  That keeps HBM
+// busy; every deeper queue only adds queueing delay to the small latency-critical loads and stores
+// between dependent tasks, which share the CU's memory pipeline with the page loads (measured: 3 -> 2
+// pages saved 4 us per step at batch 1 and 8 us at batch 16; 4 cost 2 us).
 #ifndef MK_MAX_INFLIGHT
-#define MK_MAX_INFLIGHT 3
+#define MK_MAX_INFLIGHT 2
 #endif
 constexpr int MAX_INFLIGHT = MK_MAX_INFLIGHT;
 constexpr int DYNQ = 64;               // popped task ids shared between the loader waves (dynamic queue)
@@ -80,6 +81,7 @@ struct __attribute__((aligned(16))) Smem {
     uint32_t t_ready_lo, t_ready_hi;
     uint32_t tm[4];  // trace: low 32 bits of the clock after staging / after the GEMV
     uint32_t tw_epi[NCW], tw_ack[NCW];  // trace: per wave, epilogue issued / its stores acknowledged
+    uint32_t trace_on;                  // 1 when the handle records a trace: the clock is read only then
 };
 
 __shared__ Smem S;
@@ -610,6 +612,7 @@ struct Ctx {
     int wave, lane, tid;  // compute wave, lane, thread index among the compute lanes
     uint32_t t;           // task sequence number of this workgroup
     uint32_t epoch, parity;
+    bool tr;              // tracing: take time stamps (a clock read stalls wave 0 on the scalar memory path)
 };
 
 // The task record of FIFO slot `slot`, read from LDS into wave-uniform registers.
@@ -627,6 +630,7 @@ __device__ __forceinline__ Ctx make_ctx(uint32_t t, uint32_t epoch) {
     c.t = uni(t);
     c.epoch = uni(epoch);
     c.parity = c.epoch & 1u;
+    c.tr = uni(lds_ld(S.trace_on)) != 0;
     return c;
 }
 
@@ -660,7 +664,7 @@ __device__ __forceinline__ void page_skip(uint32_t seq, int lane) {
 }
 
 __device__ __forceinline__ void tmark(const Ctx& c, int i) {
-    if (c.wave == 0 && c.lane == 0) lds_st(S.tm[i], (uint32_t)rtc());
+    if (c.tr && c.wave == 0 && c.lane == 0) lds_st(S.tm[i], (uint32_t)rtc());
 }
 
 // One poll of an event: do its sub-counters sum to `want`?
@@ -683,12 +687,14 @@ __device__ __forceinline__ bool await_inputs(const Params* pp, const Task& k, Ct
                 return false;
         }
         acquire_fence();
-        const uint64_t tr = rtc();
-        if (c.lane == 0) {
-            lds_st(S.t_ready_lo, (uint32_t)tr);
-            lds_st(S.t_ready_hi, (uint32_t)(tr >> 32));
-            lds_st(S.go, c.t + 1);
+        if (c.tr) {
+            const uint64_t tr = rtc();
+            if (c.lane == 0) {
+                lds_st(S.t_ready_lo, (uint32_t)tr);
+                lds_st(S.t_ready_hi, (uint32_t)(tr >> 32));
+            }
         }
+        if (c.lane == 0) lds_st(S.go, c.t + 1);
         return true;
     }
     const bool ok = lds_wait_ge(S.go, c.t + 1, pp, k.id);
@@ -791,6 +797,7 @@ template <int KT>
 __device__ __forceinline__ bool gemv_pages(const Params* pp, int wave, int lane, uint32_t page0, uint32_t nrows,
                                            uint32_t wbytes, const float* x, uint32_t task) {
     static_assert(KT >= 4096, "row-major GEMV pages are used for K = 4096 only");
+    const bool trace_pages = wave == 0 && uni(lds_ld(S.trace_on)) != 0;
     const uint32_t npages = (wbytes + PAGE - 1) / PAGE;
     constexpr int RPP = PAGE / (2 * KT);  // rows per page
     constexpr int LPR = KT / 512;         // 1 KiB wave loads per row
@@ -800,7 +807,7 @@ __device__ __forceinline__ bool gemv_pages(const Params* pp, int wave, int lane,
             continue;
         }
         if (!page_acquire(pp, page0 + pg, task)) return false;
-        if (wave == 0 && lane == 0) lds_st(S.tm[2], (uint32_t)rtc());
+        if (trace_pages && wave == 0 && lane == 0) lds_st(S.tm[2], (uint32_t)rtc());
         const uint32_t slot = (page0 + pg) % NPAGES;
         uint4 wv[RPP * LPR];
 #pragma unroll
@@ -959,6 +966,7 @@ __device__ __forceinline__ bool gemv_mfma(const Params* pp, int wave, int lane, 
                                           const u32x4v* B, uint32_t task) {
     static_assert(KT >= 128 && KT <= 2048, "matrix-core GEMV covers 128 <= K <= 2048");
     constexpr int NKB = KT / 32;  // column blocks
+    const bool trace_pages = wave == 0 && uni(lds_ld(S.trace_on)) != 0;
     const uint32_t npages = (wbytes + PAGE - 1) / PAGE;
     if constexpr (NKB >= 16) {
         constexpr int PPR = NKB / 16;  // pages per row group
@@ -972,7 +980,7 @@ __device__ __forceinline__ bool gemv_mfma(const Params* pp, int wave, int lane, 
             for (int s = 0; s < PPR; ++s) {
                 const uint32_t pg = rg * PPR + s;
                 if (!page_acquire(pp, page0 + pg, task)) return false;
-                if (wave == 0 && lane == 0) lds_st(S.tm[2], (uint32_t)rtc());
+                if (trace_pages && wave == 0 && lane == 0) lds_st(S.tm[2], (uint32_t)rtc());
                 const uint32_t slot = (page0 + pg) % NPAGES;
                 u32x4v a[4];
 #pragma unroll
@@ -991,7 +999,7 @@ __device__ __forceinline__ bool gemv_mfma(const Params* pp, int wave, int lane, 
         constexpr int BPR = 4 / RPG;   // blocks per row group and wave
         for (uint32_t pg = 0; pg < npages; ++pg) {
             if (!page_acquire(pp, page0 + pg, task)) return false;
-            if (wave == 0 && lane == 0) lds_st(S.tm[2], (uint32_t)rtc());
+            if (trace_pages && wave == 0 && lane == 0) lds_st(S.tm[2], (uint32_t)rtc());
             const uint32_t slot = (page0 + pg) % NPAGES;
             u32x4v a[4];
 #pragma unroll
@@ -2021,6 +2029,7 @@ __device__ __forceinline__ bool gemv_mfma_b(const Params* pp, int wave, int lane
                                             const u32x4v (*bo)[NPART], int B, uint32_t task, bool first = true) {
     static_assert(KT >= 128 && KT <= 2048, "matrix-core GEMV covers 128 <= K <= 2048");
     constexpr int NKB = KT / 32;
+    const bool trace_pages = wave == 0 && uni(lds_ld(S.trace_on)) != 0;
     float* const sl = &S.xs[wave * 1024];
     auto mfma = [](u32x4v a, u32x4v b, f32x4v acc) {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8v, a), __builtin_bit_cast(bf16x8v, b),
@@ -2034,7 +2043,7 @@ __device__ __forceinline__ bool gemv_mfma_b(const Params* pp, int wave, int lane
             for (int s = 0; s < PPR; ++s) {
                 const uint32_t pg = rg * PPR + s;
                 if (!page_acquire(pp, page0 + pg, task)) return false;
-                if (wave == 0 && lane == 0) lds_st(S.tm[2], (uint32_t)rtc());
+                if (trace_pages && wave == 0 && lane == 0) lds_st(S.tm[2], (uint32_t)rtc());
                 const uint32_t slot = (page0 + pg) % NPAGES;
                 u32x4v a[4];
 #pragma unroll
@@ -2054,7 +2063,7 @@ __device__ __forceinline__ bool gemv_mfma_b(const Params* pp, int wave, int lane
         const uint32_t npages = (nrg + RPG - 1) / RPG;
         for (uint32_t pg = 0; pg < npages; ++pg) {
             if (!page_acquire(pp, page0 + pg, task)) return false;
-            if (wave == 0 && lane == 0) lds_st(S.tm[2], (uint32_t)rtc());
+            if (trace_pages && wave == 0 && lane == 0) lds_st(S.tm[2], (uint32_t)rtc());
             const uint32_t slot = (page0 + pg) % NPAGES;
             u32x4v a[4];
 #pragma unroll
@@ -2408,13 +2417,19 @@ __device__ __noinline__ void compute(const Params* pp, uint32_t epoch, int wave)
     c.parity = epoch & 1u;
     CParams& p0 = P(pp);
     const int h = p0.T.h, okt = p0.T.grp * p0.T.d, dkt = p0.T.kd, hd = p0.T.d;
+    const bool tracing = uni(lds_ld(S.trace_on)) != 0;  // clock reads only when tracing
+    // what the completion of every task reads, loaded once (not a scalar-load round trip per task between
+    // the workgroup's done barrier and its signal)
+    uint32_t* const ctr = p0.ctr;
+    const uint32_t drop_task = p0.drop_task, sched = p0.sched, n_exp = (uint32_t)p0.T.E;
+    uint32_t* const task_count = p0.task_count;
     for (uint32_t t = 0;; ++t) {
         const uint32_t slot = t % FIFO;
         if (!lds_wait_ge(S.fifo_ready[slot], t + 1, pp, NONE)) return;
         const Task k = fifo_task(slot);
         const uint32_t page0 = uni(lds_ld(S.fifo_first_page[slot]));
         if (k.op == OP_END) return;
-        const uint64_t t_fetch = rtc();
+        const uint64_t t_fetch = tracing ? rtc() : 0;
         c.t = t;
         bool ok = true;
         // single-sequence operations referenced first: their functions are emitted next
@@ -2453,27 +2468,27 @@ __device__ __noinline__ void compute(const Params* pp, uint32_t epoch, int wave)
         }
         if (!uni(ok)) return;
         // ---- completion: every wave's stores are done, then wave 0 signals ----
-        if (p0.trace && c.lane == 0) lds_st(S.tw_epi[c.wave], (uint32_t)rtc());
+        if (tracing && c.lane == 0) lds_st(S.tw_epi[c.wave], (uint32_t)rtc());
         vm_wait_all();
-        if (p0.trace && c.lane == 0) lds_st(S.tw_ack[c.wave], (uint32_t)rtc());
+        if (tracing && c.lane == 0) lds_st(S.tw_ack[c.wave], (uint32_t)rtc());
         release_fence();  // (fenced build) this wave's results before the workgroup's signal
         lgkm_wait_all();
         if (c.lane == 0) lds_add(S.done, 1u);
         if (c.wave == 0) {
             if (!lds_wait_ge(S.done, NCW * (t + 1), pp, k.id)) return;
-            const uint64_t t_stored = rtc();  // every wave's results acknowledged by memory
+            const uint64_t t_stored = tracing ? rtc() : 0;  // every wave's results acknowledged by memory
             release_fence();
             CParams& p = P(pp);
-            const int n_sig = (k.flags & TF_SIGRANGE) ? p0.T.E : 1;  // router tiles: every expert's event
+            const uint32_t n_sig = (k.flags & TF_SIGRANGE) ? n_exp : 1u;  // router tiles: every expert's event
             bool activated = false;
-            if (k.sig_ev != NONE && k.id != p.drop_task && c.lane < n_sig) {
+            if (k.sig_ev != NONE && k.id != drop_task && (uint32_t)c.lane < n_sig) {
                 const uint32_t ev = k.sig_ev + (uint32_t)c.lane;
                 const uint32_t sub = k.sig_nsub == 8 ? xcc_id() : 0u;
-                const uint32_t old = addu_dev(&p.ctr[ctr_index(ev, sub)], 1u);
+                const uint32_t old = addu_dev(&ctr[ctr_index(ev, sub)], 1u);
                 // event-driven dispatch: the count that reaches the event's threshold activates it
-                activated = p.sched == 2 && old + 1u == epoch * p.ev_target[ev];
+                activated = sched == 2 && old + 1u == epoch * p.ev_target[ev];
             }
-            if (p.sched == 2) {
+            if (sched == 2) {
                 uint64_t act = __ballot(activated);
                 while (act) {
                     const int l = __ffsll((unsigned long long)act) - 1;
@@ -2482,8 +2497,8 @@ __device__ __noinline__ void compute(const Params* pp, uint32_t epoch, int wave)
                 }
             }
             if (k.op == OP_LMHEAD) finish_step(pp, epoch, c.parity);
-            if (p.task_count && c.lane == 0) addu_dev(&p.task_count[k.id], 1u);
-            if (p.trace && c.lane == 0) {
+            if (task_count && c.lane == 0) addu_dev(&task_count[k.id], 1u);
+            if (tracing && c.lane == 0) {
                 unsigned long long* tr = p.trace + (size_t)k.id * TRACE_WORDS;
                 const uint64_t t_ready = ((unsigned long long)lds_ld(S.t_ready_hi) << 32) | lds_ld(S.t_ready_lo);
                 const uint64_t hi = t_ready & ~0xffffffffull;
@@ -2534,6 +2549,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) mk_step_kernel(const Params* pp, 
         S.abort = 0;
         S.dyn_ready = 0;
         S.dyn_ack = 0;
+        S.trace_on = p.trace != nullptr ? 1u : 0u;
         S.args = a;
     }
     const uint32_t epoch = p.state[ST_EPOCH];
