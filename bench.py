@@ -113,6 +113,8 @@ def host_info():
                 break
     except OSError:
         pass
+    if "rocprof" in os.environ.get("LD_PRELOAD", "") or "ROCPROF_OUTPUT_PATH" in os.environ:
+        return info  # under the profiler: a child process would inherit its GPU-initialising preload
     for cmd in (["amd-smi", "metric", "--clock", "--json"], ["rocm-smi", "--showclocks", "--json"]):
         try:
             r = subprocess.run(cmd, capture_output=True, text=True, timeout=30)
