@@ -4,13 +4,14 @@
 // LDS it declares leaves room for no second one) and runs an interpreter over
 // a queue of tile tasks (koas-w.github.io megakernel notes, "on-GPU
 // interpreter / persistent kernel"; Hazy Research megakernel news page,
-// section 4, "fusion big bang").  The workgroup has five waves:
+// section 4, "fusion big bang").  The workgroup has six waves:
 //
-//   wave 4 (loader): fetches task records (static: its own queue; dynamic: an
-//     atomic pop from one global queue, koas-w.github.io notes, "static and
-//     dynamic scheduling") into an LDS FIFO, and streams every task's weights
-//     (attention: its KV-cache chunk) into a ring of 16 KiB LDS pages with
-//     global_load_lds_dwordx4.  Weights never depend on activations, so the
+//   waves 4-5 (loaders): fetch task records (static: the workgroup's queue;
+//     dynamic: an atomic pop from one global queue, koas-w.github.io notes,
+//     "static and dynamic scheduling"; event-driven: slots of a ready queue)
+//     into an LDS FIFO (wave 4), and stream every task's weights (attention:
+//     its KV-cache chunk) into a ring of eight 16 KiB LDS pages with
+//     global_load_lds_dwordx4, each loader wave issuing half of every page.  Weights never depend on activations, so the
 //     loader runs ahead of the compute waves as far as free pages allow: the
 //     next tasks' weights arrive while the current task still waits on its
 //     inputs (Hazy page, section 4, "shared memory to remove memory bubbles":

@@ -197,18 +197,54 @@ def test_llama1b_small_batch_first_step(B):
     """A few sequences at the 1B shape: QKV and gate/up tiles packed in K halves with the
     chunk size of this batch (1024 // B rounded down to 64 rows)."""
     C = 2048
-    _one_step(LLAMA_1B, B, C, synth.make_positions(B, 100, C - 1), check_kv=False)
+    _one_step(LLAMA_1B, B, C, synth.make_positions(B, 100, C - 1), check_kv=True)
 
 
-def test_llama1b_batch32_first_step():
+def _greedy_chain(cfg, B, C, P0, steps, **opt):
+    """`steps` chained greedy steps (next tokens fed on the device) against the oracle's greedy decode, plus
+    counters = steps * target and every task run once per step."""
+    w = synth.make_weights(cfg)
+    kc, vc = synth.make_kv(cfg, B, C)
+    tok = synth.make_tokens(cfg, B)
+    print(f"case {cfg.name} B={B} greedy chain of {steps} from {P0.tolist()} opt={opt}", flush=True)
+    run = Runner(cfg, w, B, C, kc, vc, trace=1, **opt)
+    t0 = torch.tensor(tok, dtype=torch.int32, device="cuda")
+    positions = torch.tensor(np.stack([P0 + s for s in range(steps)]), dtype=torch.int32, device="cuda")
+    nxt = mk.mk_next_tokens(run.h)
+    got = []
+    for s in range(steps):
+        mk.mk_decode_step(run.h, t0.data_ptr() if s == 0 else nxt, positions[s].data_ptr(), run.kv.data_ptr(),
+                          run.logits.data_ptr(), torch.cuda.current_stream().cuda_stream)
+        got.append(run.next_tokens().cpu().numpy().copy())
+    run.check()
+    counts = mk.mk_read_task_counts(run.h, len(run.graph["tasks"]))
+    ctr, epoch = mk.mk_read_counters(run.h, run.graph["header"]["n_events"])
+    assert epoch == steps
+    np.testing.assert_array_equal(counts, np.full(len(counts), steps, np.uint32))
+    np.testing.assert_array_equal(ctr, run.graph["target"] * steps)
+    run.close()
+    ref = oracle.greedy(cfg, w, tok, P0, kc.copy(), vc.copy(), steps)
+    print("oracle smallest top-2 gap per step:", np.asarray(ref["gaps"]).min(axis=-1) if ref["gaps"].ndim > 1
+          else ref["gaps"])
+    np.testing.assert_array_equal(np.array(got), ref["tokens"])
+
+
+def test_llama1b_batch16_greedy_chain_dynamic_queue():
+    """Four chained steps of 16 sequences at the 1B shape (contexts U[256, 4096]) from the dynamic queue: both
+    accumulator parities, the per-step attention tickets and the argmax keys are reused across steps."""
+    _greedy_chain(LLAMA_1B, 16, 4352, synth.make_positions(16, 256, 4096), 4, sched=1)
+
+
+@pytest.mark.parametrize("sched", [0, 1, 2], ids=["static", "dynamic", "event"])
+def test_llama1b_batch32_first_step(sched):
     """32 sequences: every GEMV tile runs for two column groups of 16 on the same weights."""
     B, C = 32, 4352
     w = synth.make_weights(LLAMA_1B)
     kc, vc = synth.make_kv(LLAMA_1B, B, C)
     tok = synth.make_tokens(LLAMA_1B, B)
     pos = synth.make_positions(B, 256, 4096)
-    print(f"case llama1b B=32 first step positions={pos.tolist()}", flush=True)
-    run = Runner(LLAMA_1B, w, B, C, kc, vc)
+    print(f"case llama1b B=32 first step sched={sched} positions={pos.tolist()}", flush=True)
+    run = Runner(LLAMA_1B, w, B, C, kc, vc, sched=sched)
     run.step(tok, pos)
     run.check()
     logits, hidden, nxt = run.logits.cpu().numpy(), run.hidden().cpu().numpy(), run.next_tokens().cpu().numpy()

@@ -120,3 +120,27 @@ def test_tiny_moe_greedy_chain_and_counters():
 def test_moe_1b_batch16_first_step():
     """The 16-layer, 64-expert top-8 MoE at batch 16, context 2048 for every sequence."""
     _one_step(MOE_1B, 16, 2112, np.full(16, 2048, np.int32), exact_experts=False)
+
+
+def test_moe_1b_batch16_greedy_chain():
+    """Three chained steps of the 64-expert top-8 MoE at batch 16: routing decided inside every step on the
+    tokens the previous step chose, against the oracle's greedy decode."""
+    cfg, B, C, steps = MOE_1B, 16, 2112, 3
+    w = synth.make_weights(cfg)
+    kc, vc = synth.make_kv(cfg, B, C)
+    tok = synth.make_tokens(cfg, B)
+    P0 = np.full(B, 2048, np.int32)
+    print(f"case {cfg.name} B={B} greedy chain of {steps}", flush=True)
+    run = Runner(cfg, w, B, C, kc, vc)
+    t0 = torch.tensor(tok, dtype=torch.int32, device="cuda")
+    positions = torch.tensor(np.stack([P0 + s for s in range(steps)]), dtype=torch.int32, device="cuda")
+    nxt = mk.mk_next_tokens(run.h)
+    got = []
+    for s in range(steps):
+        mk.mk_decode_step(run.h, t0.data_ptr() if s == 0 else nxt, positions[s].data_ptr(), run.kv.data_ptr(),
+                          run.logits.data_ptr(), torch.cuda.current_stream().cuda_stream)
+        got.append(run.next_tokens().cpu().numpy().copy())
+    run.check()
+    run.close()
+    ref = oracle.greedy(cfg, w, tok, P0, kc.copy(), vc.copy(), steps)
+    np.testing.assert_array_equal(np.array(got), ref["tokens"])
