@@ -41,15 +41,18 @@ def step_bytes(cfg, positions):
     return cfg.weight_bytes() + int(kv.sum())
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mk_step_kernel_llama1b_b1_traffic.json")
+def traffic_file(batch=1):
+    """The committed counter-traffic record of the 1B-shape workload at this batch."""
+    return os.path.join(ROOT, "profiles", f"mk_step_kernel_llama1b_b{batch}_traffic.json")
 
 
-def measured_traffic():
+def measured_traffic(batch=1):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE passes (scaled by the same
-    counters on a plain copy of known size), or None if the kernel source changed since they were taken."""
+    counters on a plain copy of known size), or None if there is no record for this workload or the kernel
+    source changed since they were taken."""
     import hashlib
     try:
-        rec = json.load(open(TRAFFIC_FILE))
+        rec = json.load(open(traffic_file(batch)))
         src = b"".join(open(os.path.join(ROOT, f), "rb").read() for f in rec["source_files"])
     except (OSError, KeyError, ValueError):
         return None
@@ -67,7 +70,8 @@ TRAFFIC_SOURCES = ["persistent_megakernel_decode_cu_amd/csrc/megakernel.hip",
                    "persistent_megakernel_decode_cu_amd/csrc/mk_internal.h"]
 
 
-def traffic_from_counters(fetch_csv, write_csv, kernel="mk::mk_step_kernel", copy_bytes=256 << 20):
+def traffic_from_counters(fetch_csv, write_csv, kernel="mk::mk_step_kernel", copy_bytes=256 << 20,
+                          workload="llama-3.2-1b-shape, batch 1, decode from position 1024, max_ctx 2048"):
     """HBM bytes per launch of `kernel` from two rocprofv3 --pmc runs of this bench with
     --copy-calibration (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each scaled by what the
     same counter reads for the plain device copy of copy_bytes (its three largest dispatches)."""
@@ -93,7 +97,7 @@ def traffic_from_counters(fetch_csv, write_csv, kernel="mk::mk_step_kernel", cop
     fs, ws = (copy_bytes / 1024) / f_copy, (copy_bytes / 1024) / w_copy
     src = b"".join(open(os.path.join(ROOT, f), "rb").read() for f in TRAFFIC_SOURCES)
     rd, wr = int(f_mk * 1024 * fs), int(w_mk * 1024 * ws)
-    return {"kernel": kernel, "workload": "llama-3.2-1b-shape, batch 1, decode from position 1024, max_ctx 2048",
+    return {"kernel": kernel, "workload": workload,
             "source_sha256": hashlib.sha256(src).hexdigest(), "source_files": TRAFFIC_SOURCES,
             "fetch_size_kib_median": f_mk, "write_size_kib_median": w_mk, "copy_bytes": copy_bytes,
             "copy_fetch_size_kib": f_copy, "copy_write_size_kib": w_copy,
@@ -231,8 +235,9 @@ TRACE_OPS = {1: "QKV+RoPE", 2: "attention", 3: "O-proj", 4: "gate/up", 5: "down"
 def trace_summary(tr, ex, title, command):
     """Markdown summary of one traced step (mk_read_trace, 16 words per task: workgroup, t_fetch,
     t_inputs_ready, t_staged, t_computed, t_end, t_stored, t_last_page, first page, last wave's epilogue
-    issued, last wave's stores acknowledged, ...; 100 MHz ticks): where each operation's time goes, when
-    each layer's phases end, and how long each dependency hop takes."""
+    issued, last wave's stores acknowledged, wave 0's epilogue issued, the loader's first and last page
+    issued, its last page published; 100 MHz ticks): where each operation's time goes, when each layer's
+    phases end, and how long each dependency hop takes."""
     tasks = ex["tasks"]
     us = 0.01  # one tick of the 100 MHz clock in microseconds
     (fetch, ready, staged, computed, end, stored, last_pg, epi, acked) = (
@@ -261,6 +266,20 @@ def trace_summary(tr, ex, title, command):
                      f"{med(staged[s] - ready[s])} | {med(computed[s] - staged[s])} | {med(np.maximum(lp, 0))} | "
                      f"{med(epi[s] - computed[s])} | {med(acked[s] - epi[s])} | {med(end[s] - acked[s])} | "
                      f"{med(end[s] - ready[s])} |")
+    # the loader's side: when the task's pages were issued and its last page published
+    iss0, iss1, pubd = (tr[:, i].astype(np.int64) for i in (12, 13, 14))
+    lines += ["", "## Loader (µs from the task's inputs being ready; negative: before)", "",
+              "Columns: loader wave 0 issued the task's first page; issued its last page; published its last "
+              "page (its loads had landed); that last page's issue-to-publish latency; the time compute wave 0 "
+              "spent waiting for pages (attention and several-sequence GEMV tasks only).", "",
+              "| op | tasks with pages | first page issued | last page issued | last page published | "
+              "last page latency | wave 0 waiting for pages |", "|---|---|---|---|---|---|---|"]
+    pwait = tr[:, 15].astype(np.int64)
+    for op in sorted(set(int(o) for o in ops)):
+        s = (ops == op) & (iss0 > 0) & (pubd > 0)
+        lines.append(f"| {TRACE_OPS.get(op, op)} | {int(s.sum())} | {med(iss0[s] - ready[s])} | "
+                     f"{med(iss1[s] - ready[s])} | {med(pubd[s] - ready[s])} | {med(pubd[s] - iss1[s])} | "
+                     f"{med(pwait[s])} |")
     # per layer: when each phase's last task ended (from the step's first fetch)
     layers = tasks["layer"]
     L = ex["header"]["L"]
@@ -438,10 +457,19 @@ def bench_batch(args, torch, synth, mk):
                    "workgroups": int(graph["header"]["W"]), "tasks_per_step": int(graph["header"]["n_tasks"]),
                    "attn_splits": int(graph["header"]["attn_splits"])},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None if moe or args.sched != "static" else measured_traffic(B),
                      "algorithmic_bytes_per_step": int(bytes_mean), "kernel_us_per_launch": round(ms_launch * 1000, 2)},
         "input_generation_s": round(t_gen, 1),
     }
+    if args.copy_calibration:  # reference dispatches for the HBM byte counters
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").random_(0, 255)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = 256 << 20
+        del src, dst
     if moe:
         out["config"]["experts"] = {"n_experts": cfg.n_experts, "top_k": cfg.top_k, "expert_ffn": cfg.expert_ffn,
                                     "mean_distinct_experts_per_layer": round(experts_touched, 2)}
@@ -508,8 +536,10 @@ def main():
                     help="write the measured-traffic record from two rocprofv3 counter-collection CSVs and exit")
     args = ap.parse_args()
     if args.traffic_from:
-        rec = traffic_from_counters(*args.traffic_from)
-        with open(TRAFFIC_FILE, "w") as f:
+        wl = None if args.batch == 1 else (f"llama-3.2-1b-shape, batch {args.batch}, contexts uniform in [256, 4096] "
+                                           "from the token seed, max_ctx 4352")
+        rec = traffic_from_counters(*args.traffic_from, **({"workload": wl} if wl else {}))
+        with open(traffic_file(args.batch), "w") as f:
             json.dump(rec, f, indent=1)
         print(json.dumps(rec))
         return
@@ -599,7 +629,7 @@ def main():
     pos_list = list(range(P0, P0 + K))
     bytes_mean = np.mean([step_bytes(cfg, [p]) for p in pos_list])
     achieved = bytes_mean / (ms_launch * 1e-3) / 1e9
-    traffic = measured_traffic() if args.model == "1b" else None
+    traffic = measured_traffic(1) if args.model == "1b" else None
 
     out = {
         "metric": METRIC if args.model == "1b" else "decode µs/step (steps/s) at batch 1, Llama-3-8B shape; achieved HBM GB/s vs peak",

@@ -108,8 +108,8 @@ typedef struct {
  * projections of up to 16 sequences share one pass over the weights, so
  * 17..32 sequences take two); max_ctx >= 1 positions per sequence in the KV
  * cache.  Errors: MK_E_INVALID (NULL pointers, unsupported shapes, bad options),
- * MK_E_UNSUPPORTED (batch > 32, batch > 1 with hidden > 2048, a mixture of
- * experts at batch 1), MK_E_NO_DEVICE, MK_E_NOMEM, MK_E_HIP.  On success *out
+ * MK_E_UNSUPPORTED (batch > 32; batch > 1, or a mixture of experts, with
+ * hidden > 2048), MK_E_NO_DEVICE, MK_E_NOMEM, MK_E_HIP.  On success *out
  * receives the handle.  Defined by: the task graph built once on the host and
  * reused for every forward (Hazy Research megakernel news page, section 4,
  * "fusion big bang"; MPK news page, part 1: the model becomes a graph of tasks
@@ -216,8 +216,13 @@ mk_status mk_read_task_counts(mk_handle *h, uint32_t *host, size_t n);
 /* Trace (when built with trace=1): per task of the last step, sixteen uint64
  * values {workgroup, t_fetch, t_inputs_ready, t_staged, t_computed, t_end,
  * t_stored, t_last_page, first LDS page, t_epilogue_issued, t_epilogue_acked,
- * t_wave0_epilogue_issued, 0, 0, 0, 0}; times in ticks of the 100 MHz device
- * clock.  t_staged: inputs in LDS (attention: queries staged); t_computed:
+ * t_wave0_epilogue_issued, t_first_page_issued, t_last_page_issued,
+ * t_last_page_published, page_wait}; times in ticks of the 100 MHz device
+ * clock (the three loader stamps: 0 for a task without pages; "published":
+ * loader wave 0 saw the page's loads land and handed it to the compute waves;
+ * page_wait: ticks compute wave 0 spent waiting for pages, in the attention and
+ * several-sequence GEMV tasks, else 0).
+ * t_staged: inputs in LDS (attention: queries staged); t_computed:
  * arithmetic done (attention: all context pages folded in); t_epilogue_issued /
  * t_epilogue_acked: the last compute wave to issue its result stores / to have
  * them acknowledged by memory; t_stored: every wave done, just before the

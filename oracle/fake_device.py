@@ -67,13 +67,31 @@ class FakeDevice:
     def _norm(self, x, gain):
         return x / np.sqrt(np.mean(x * x) + self.cfg.eps) * gain
 
-    def _chunk(self, P, c):
-        """Positions [c0, c1) of 0..P covered by chunk c (one sequence: S equal parts of the context;
-        several: fixed slots of ceil(C / S) positions)."""
-        n = P + 1
-        lc = -(-self.C // self.S) if self.B > 1 else -(-n // self.S)
-        c0 = min(n, c * lc)
-        return c0, min(n, c0 + lc)
+    def _several(self):
+        return self.B > 1 or self.cfg.n_experts > 0
+
+    def _deal(self):
+        """Several sequences: the B S attention slots of a KV group dealt to the sequences in proportion to
+        their contexts.  L = the smallest whole number of pages (pb positions each) with at most 16 chunks
+        per sequence and sum_b ceil(n_b / L) <= B S; sequence b takes ceil(n_b / L) consecutive slots (in
+        sequence order) of chunks of ceil(n_b / s_b) positions rounded up to whole pages.
+        Returns {slot: (b, c)} for the non-empty chunks, and per sequence (chunk length, chunks)."""
+        B, T, pb = self.B, self.B * self.S, 4096 // self.cfg.head_dim
+        n = [int(p) + 1 for p in self.pos]
+        m = max(1, -(-max(n) // (16 * pb)))
+        while sum(-(-x // (m * pb)) for x in n) > T:
+            m += 1
+        slots, per, j = {}, [], 0
+        for b in range(B):
+            s = -(-n[b] // (m * pb))
+            ln = -(-(-(-n[b] // s)) // pb) * pb
+            nch = -(-n[b] // ln)
+            per.append((ln, nch))
+            for c in range(nch):
+                slots[j + c] = (b, c)
+            j += s
+        assert j <= T
+        return slots, per
 
     def _qkv(self, k):
         cfg, l, slot, d = self.cfg, k["layer"], k["part"], self.cfg.head_dim
@@ -101,9 +119,19 @@ class FakeDevice:
                     cache[l, b, g, P, j], cache[l, b, g, P, j + half] = _bf16_bits(lo), _bf16_bits(hi)
 
     def _attn(self, k):
-        d, l, g, c, b = self.cfg.head_dim, k["layer"], k["part"], k["row0"], k["seq"]
+        d, l, g = self.cfg.head_dim, k["layer"], k["part"]
+        if self._several():  # the slot the step's deal gave this record; an empty slot does nothing
+            slot = k["seq"] * self.S + k["row0"]
+            if slot not in self.slots:
+                return
+            b, c = self.slots[slot]
+            ln = self.per[b][0]
+        else:  # one sequence: chunk row0 of S equal parts of its context
+            b, c = k["seq"], k["row0"]
+            ln = -(-(self.pos[b] + 1) // self.S)
         P = self.pos[b]
-        c0, c1 = self._chunk(P, c)
+        c0 = min(P + 1, c * ln)
+        c1 = min(P + 1, c0 + ln)
         K = _f64(self.kc[l, b, g, c0:c1])
         V = _f64(self.vc[l, b, g, c0:c1])
         parts = []
@@ -122,8 +150,9 @@ class FakeDevice:
         """Attention output of the group's query heads: the chunks' partials merged with max rescaling."""
         d = self.cfg.head_dim
         out = np.empty(self.grp * d)
+        nch = self.per[b][1] if self._several() else self.S
         for hh in range(self.grp):
-            ps = [self.part[(l, b, g, c)][hh] for c in range(self.S)]  # KeyError: a chunk not yet run
+            ps = [self.part[(l, b, g, c)][hh] for c in range(nch)]  # KeyError: a chunk not yet run
             M = max(p[0] for p in ps)
             num, den = np.zeros(d), 0.0
             for m, s, o in ps:
@@ -212,6 +241,8 @@ class FakeDevice:
         L, h, f = cfg.n_layers, cfg.hidden, cfg.ffn
         self.tok, self.pos = np.asarray(tokens), np.asarray(positions)
         self.kc, self.vc = k_cache, v_cache
+        if self._several():
+            self.slots, self.per = self._deal()
         nan = np.nan
         self.acc = np.zeros((2 * L + 1, B, h))
         self.q = np.full((B, cfg.n_q * cfg.head_dim), nan)

@@ -20,12 +20,16 @@ The tiling rules (written from the design, not from the C++ code):
   * QKV tiles: 8 RoPE pairs (16 weight rows: 8 first halves then 8 second
     halves) of one head; heads ordered by KV group: the group's query heads,
     its key head, its value head; pair blocks in order.
+  * the several-sequence rules below ("batch > 1") hold for every graph with
+    experts too, at batch 1 as well: expert routing exists only on that path.
   * attention: attn_splits chunks per (sequence, KV group), default
     clamp(ceil(max_ctx / 256), 1, 16) at batch 1 and clamp(pow2_floor(W /
-    (B n_kv)), 1, 8) for batch > 1, at most max_ctx.  With several sequences the chunks
-    are slots of a fixed length (so a short context leaves some empty) and the
-    last chunk task of a (sequence, KV group) to finish merges the chunks for
-    the O-projection, which therefore waits on the same event as at batch 1.
+    (B n_kv)), 1, 8) for batch > 1, at most max_ctx.  With several sequences the
+    B S attention records of a KV group are slots (slot = seq S + chunk) that the
+    device deals to the sequences at every step in proportion to their contexts
+    (fake_device.py gives the rule); some slots may stay empty.  The last chunk
+    task of a (sequence, KV group) to finish merges the chunks for the
+    O-projection, which therefore waits on the same event as at batch 1.
   * O-proj tiles: (KV group g, row block) over columns g*grp*d .. +grp*d, with
     o_rows = min(h, R, max(16, pow2_floor(h * n_kv / W))), R = pow2_floor(1024 // min(B, 16)).
   * down tiles: (K block of kd = min(1024, f) columns, row block of
@@ -98,12 +102,13 @@ def _round16(x):
 def tiling(cfg, B, C, W, attn_splits=0):
     h, nq, nkv, d, f, V = cfg.hidden, cfg.n_q, cfg.n_kv, cfg.head_dim, cfg.ffn, cfg.vocab
     grp = nq // nkv
+    several = B > 1 or cfg.n_experts > 0
     if attn_splits > 0:
         S = attn_splits
     else:
         # batch 1: 256-position chunks; batch > 1: about one attention task per
         # workgroup and layer over all sequences and KV groups, at most 8 slots
-        S = max(1, min(16, -(-C // 256))) if B == 1 else max(1, min(8, _pow2_floor(max(1, W // (B * nkv)))))
+        S = max(1, min(16, -(-C // 256))) if not several else max(1, min(8, _pow2_floor(max(1, W // (B * nkv)))))
     S = min(S, C)
     max_rows = _pow2_floor(1024 // min(B, 16))  # rows x sequences (of one column group) of a tile
     E = cfg.n_experts
@@ -203,7 +208,7 @@ def build(cfg, B, C, W, policy=0, attn_splits=0, sched=0):
                         tile += 1
         # several sequences: chunk slots in the order 0, 1, .., S/2 - 1, S - 1, .., S/2 (outermost),
         # so that round-robin queues pair slot c with slot S - 1 - c; one sequence: per group
-        if B > 1:
+        if B > 1 or E:
             corder = list(range((S + 1) // 2)) + list(range(S - 1, (S + 1) // 2 - 1, -1))
             attn = [(b, g, c) for c in corder for b in range(B) for g in range(nkv)]
         else:

@@ -63,10 +63,9 @@ int plan_tiling(const Dims& dm, int B, int C, int W, const PlanOptions& o, Tilin
     if (dm.nq % dm.nkv) return fail("n_q_heads must be a multiple of n_kv_heads");
     const bool moe = dm.n_experts != 0;
     if (B > MAX_BATCH) return fail("batch is limited to 32 sequences per step");
-    if (B > 1 && dm.h > 2048) return fail("batch > 1 needs hidden <= 2048");
+    const bool batched = batched_path(B, dm.n_experts);
+    if (batched && dm.h > 2048) return fail("batch > 1 and experts need hidden <= 2048");
     if (moe) {
-        // expert routing runs on the batched (several-sequence) path
-        if (B < 2) return fail("the mixture-of-experts FFN needs batch >= 2");
         if (dm.n_experts < 1 || dm.n_experts > 64) return fail("1..64 experts");
         if (dm.top_k < 1 || dm.top_k > dm.n_experts) return fail("top_k must be in [1, n_experts]");
         if (!gemv_k_ok(dm.fe) || dm.fe > 2048) return fail("expert_ffn must be a power of two in [128, 2048]");
@@ -87,11 +86,11 @@ int plan_tiling(const Dims& dm, int B, int C, int W, const PlanOptions& o, Tilin
     int S = o.attn_splits;
     if (S > 16) return fail("attn_splits must be at most 16 (the merge reads up to 16 chunk partials)");
     if (S <= 0) {
-        // batch 1: 256-position chunks of the one context; batch > 1: about one
-        // attention task per workgroup and layer over all sequences and KV groups, at
-        // most 8 slots (each task carries a fixed cost of a few microseconds, so more,
-        // shorter slots measured slower)
-        S = B == 1 ? (int)std::max<int64_t>(1, std::min<int64_t>(16, (C + 255) / 256))
+        // one sequence: 256-position chunks of its context; the several-sequence path:
+        // about one attention task per workgroup and layer over all sequences and KV
+        // groups, at most 8 slots (each task carries a fixed cost of a few microseconds,
+        // so more, shorter slots measured slower)
+        S = !batched ? (int)std::max<int64_t>(1, std::min<int64_t>(16, (C + 255) / 256))
                    : (int)std::max<int64_t>(1, std::min<int64_t>(8, pow2_floor(std::max<int64_t>(
                                                                      1, (int64_t)W / ((int64_t)B * dm.nkv)))));
     }
@@ -249,17 +248,17 @@ int build_graph(const Tiling& T, const Layout& Ly, int sched, int policy, Graph*
                 }
             }
         }
-        // attention chunks per (sequence, KV group, chunk); with several sequences the
-        // last chunk of a (sequence, group) to finish also merges the chunks.  Several
-        // sequences: fixed-length chunk slots, of which the first is non-empty most often,
-        // so the slots go in chunk order 0, 1, .., S/2 - 1, then S - 1, S - 2, .., S/2: the
-        // round-robin queues, which give a workgroup tasks half a block apart, then pair
-        // slot c with slot S - 1 - c.  One sequence: chunks in order per group.
+        // attention tasks per (sequence, KV group, chunk).  One sequence: chunks in order
+        // per group.  Several sequences (or experts): the B x S tasks of a group are slots
+        // j = seq * S + chunk that the device deals to the sequences at every step, in
+        // proportion to their contexts; the last chunk of a (sequence, group) to finish
+        // merges the chunks.  The records go in slot-chunk order 0, 1, .., S/2 - 1, then
+        // S - 1, .., S/2, so that round-robin queues give a workgroup slots c and S - 1 - c.
         std::vector<int> corder;
         for (int c = 0; c < (T.attn_splits + 1) / 2; ++c) corder.push_back(c);
         for (int c = T.attn_splits - 1; c >= (T.attn_splits + 1) / 2; --c) corder.push_back(c);
         std::vector<std::array<int, 3>> attn;  // (sequence, group, chunk)
-        if (T.B > 1) {
+        if (batched_path(T.B, T.E)) {
             for (int c : corder)
                 for (int b = 0; b < T.B; ++b)
                     for (int gi = 0; gi < T.nkv; ++gi) attn.push_back({b, gi, c});

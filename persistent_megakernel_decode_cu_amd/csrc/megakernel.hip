@@ -55,6 +55,12 @@ constexpr int LPP = 16 / NLW;          // loads per page per loader wave
 #define MK_MAX_INFLIGHT 2
 #endif
 constexpr int MAX_INFLIGHT = MK_MAX_INFLIGHT;
+// Pages in flight per loader wave while it streams an attention task's KV rows.
+#ifndef MK_ATTN_INFLIGHT
+#define MK_ATTN_INFLIGHT MK_MAX_INFLIGHT
+#endif
+constexpr int ATTN_INFLIGHT = MK_ATTN_INFLIGHT;
+static_assert(ATTN_INFLIGHT >= 1 && ATTN_INFLIGHT <= NPAGES && LPP * ATTN_INFLIGHT <= 63, "vmcnt range");
 constexpr int DYNQ = 64;               // popped task ids shared between the loader waves (dynamic queue)
 constexpr int MAXB = 64;               // sequences per step held in LDS
 
@@ -83,6 +89,15 @@ struct __attribute__((aligned(16))) Smem {
     uint32_t tm[4];  // trace: low 32 bits of the clock after staging / after the GEMV
     uint32_t tw_epi[NCW], tw_ack[NCW];  // trace: per wave, epilogue issued / its stores acknowledged
     uint32_t trace_on;                  // 1 when the handle records a trace: the clock is read only then
+    // trace, loader wave 0: per FIFO slot, when the task's first and last pages were issued and when
+    // its last page was published; per ring slot, the FIFO slot of the task whose page it holds
+    uint32_t tl_issue0[FIFO], tl_issue1[FIFO], tl_pub[FIFO];
+    uint32_t pg_fslot[NPAGES];
+    // several sequences: this step's deal of every KV group's attention slots (attn_deal)
+    uint32_t amap[MAX_BATCH * ATTN_MAX_CHUNKS];  // slot -> sequence << 8 | chunk, 0xffff: empty
+    uint32_t alen[MAX_BATCH];                    // chunk length of each sequence (positions)
+    uint32_t anch[MAX_BATCH];                    // non-empty chunks of each sequence
+    uint32_t adealt;                             // 1 once loader wave 0 has dealt this step's slots
 };
 
 __shared__ Smem S;
@@ -347,15 +362,10 @@ __device__ __noinline__ bool wait_event(const Params* pp, uint32_t ev, uint32_t 
 struct Chunk {
     int32_t c0, c1, P;  // chunk positions [c0, c1) of 0..P; prefix rows in LDS are [c0, min(c1, P))
 };
-// Chunk c of the context 0..P: one of `splits` equal parts of it (fixed_len = 0), or
-// the slot [c * fixed_len, (c + 1) * fixed_len) clipped to it (several sequences:
-// every non-empty chunk is about the same work whatever the mix of contexts).
-__device__ __forceinline__ int32_t attn_fixed_len(int32_t B, int32_t C, int32_t splits) {
-    return B > 1 ? (C + splits - 1) / splits : 0;
-}
-__device__ __forceinline__ Chunk attn_chunk(int32_t splits, int32_t fixed_len, int32_t P, uint32_t c) {
+// Chunk c of the one context 0..P at batch 1: one of `splits` equal parts of it.
+__device__ __forceinline__ Chunk attn_chunk(int32_t splits, int32_t P, uint32_t c) {
     const int32_t n = P + 1;
-    const int32_t lc = fixed_len > 0 ? fixed_len : (n + splits - 1) / splits;
+    const int32_t lc = (n + splits - 1) / splits;
     Chunk ch;
     ch.P = P;
     ch.c0 = min(n, (int32_t)c * lc);
@@ -370,9 +380,96 @@ __device__ __forceinline__ bool attn_kswizzle(int32_t d, int32_t grp) { return d
 
 __device__ __forceinline__ int32_t seq_pos(uint32_t b) { return (int32_t)lds_ld(*(const uint32_t*)&S.pos[b]); }
 
-__device__ __forceinline__ uint32_t task_pages(const Task& k, int32_t splits, int32_t fixed_len, int32_t d) {
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+#pragma unroll
+    for (int o = 1; o < 64; o *= 2) v += (uint32_t)__shfl_xor((int)v, o, 64);
+    return uni(v);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+    for (int o = 1; o < 64; o *= 2) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
+    return uni(v);
+}
+
+// Several sequences: the B x S attention tasks of each KV group and layer (task slot
+// j = seq * S + chunk of the record) are dealt to the sequences in proportion to their
+// contexts, at every step, so that the step's attention tasks carry about the same
+// number of positions whatever the mix of context lengths (split-KV decode load
+// balance).  The chunk length L is the smallest whole number of pages with
+// sum_b ceil(n_b / L) <= B S and at most 16 chunks per sequence (n_b = P_b + 1);
+// sequence b takes s_b = ceil(n_b / L) consecutive slots in sequence order, with chunks
+// of len_b = ceil(n_b / s_b) rounded up to whole pages, and the slots past the last
+// non-empty chunk stay empty.  Every workgroup computes the same deal from the
+// positions; loader wave 0 does it (one wave, lane = sequence) before it hands the
+// first attention task of the step to the compute waves.
+__device__ __noinline__ void attn_deal(CParams& p, int lane) {
+    const int B = p.T.B, T = B * p.T.attn_splits;
+    const uint32_t pb = (uint32_t)(4096 / p.T.d);
+    const bool mine = lane < B;
+    const uint32_t n = mine ? (uint32_t)min(max(seq_pos((uint32_t)lane) + 1, 1), p.T.C) : 0u;
+    const uint32_t nmax = wave_max_u32(n);
+    uint32_t lo = max(1u, (nmax + ATTN_MAX_CHUNKS * pb - 1) / (ATTN_MAX_CHUNKS * pb)), hi = (nmax + pb - 1) / pb;
+    while (lo < hi) {  // wave-uniform bisection over the chunk length in pages
+        const uint32_t mid = (lo + hi) / 2, L = mid * pb;
+        if (wave_sum_u32(mine ? (n + L - 1) / L : 0u) <= (uint32_t)T) hi = mid;
+        else lo = mid + 1;
+    }
+    const uint32_t L = lo * pb;
+    const uint32_t sl = mine ? (n + L - 1) / L : 0u;
+    const uint32_t len = mine ? ((n + sl - 1) / sl + pb - 1) / pb * pb : 0u;
+    const uint32_t nch = mine ? (n + len - 1) / len : 0u;
+    uint32_t incl = sl;  // inclusive prefix sum of the slots over the sequences
+#pragma unroll
+    for (int o = 1; o < 64; o *= 2) {
+        const uint32_t t = (uint32_t)__shfl_up((int)incl, o, 64);
+        if (lane >= o) incl += t;
+    }
+    const uint32_t base = incl - sl, used = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+    if (mine) {
+        S.alen[lane] = len;
+        S.anch[lane] = nch;
+        for (uint32_t c = 0; c < sl; ++c) S.amap[base + c] = c < nch ? (((uint32_t)lane << 8) | c) : 0xffffu;
+    }
+    for (uint32_t j = used + (uint32_t)lane; j < (uint32_t)T; j += 64) S.amap[j] = 0xffffu;
+}
+
+// The chunk of attention task k: batch 1, chunk row0 of the one context; several
+// sequences, the slot the deal gave it (an empty slot: b = 0 and c0 = c1 = P + 1).
+struct AttnTask {
+    int32_t b, c, nch;  // sequence, chunk, non-empty chunks of the sequence (several sequences)
+    Chunk ch;
+};
+__device__ __forceinline__ AttnTask attn_task(CParams& p, const Task& k) {
+    AttnTask a;
+    if (!batched_path(p.T.B, p.T.E)) {
+        a.b = (int32_t)k.seq;
+        a.c = (int32_t)k.row0;
+        a.nch = p.T.attn_splits;
+        a.ch = attn_chunk(p.T.attn_splits, seq_pos(k.seq), k.row0);
+        return a;
+    }
+    const uint32_t e = lds_ld(S.amap[k.seq * (uint32_t)p.T.attn_splits + k.row0]);
+    if (e == 0xffffu) {
+        a.b = 0;
+        a.c = 0;
+        a.nch = 0;
+        a.ch.P = seq_pos(0);
+        a.ch.c0 = a.ch.c1 = a.ch.P + 1;
+        return a;
+    }
+    a.b = (int32_t)(e >> 8);
+    a.c = (int32_t)(e & 0xffu);
+    a.nch = (int32_t)lds_ld(S.anch[a.b]);
+    const int32_t len = (int32_t)lds_ld(S.alen[a.b]);
+    a.ch.P = seq_pos((uint32_t)a.b);
+    a.ch.c0 = min(a.ch.P + 1, a.c * len);
+    a.ch.c1 = min(a.ch.P + 1, a.ch.c0 + len);
+    return a;
+}
+
+__device__ __forceinline__ uint32_t task_pages(CParams& p, const Task& k, int32_t d) {
     if (k.op == OP_ATTN) {
-        const Chunk ch = attn_chunk(splits, fixed_len, seq_pos(k.seq), k.row0);
+        const Chunk ch = attn_task(p, k).ch;
         const int32_t npre = max(0, min(ch.c1, ch.P) - ch.c0);
         const int32_t pb = attn_block_rows(d);
         return (uint32_t)((npre + pb - 1) / pb);
@@ -395,12 +492,13 @@ __device__ __forceinline__ void issue_page(CParams& p, const Task& k, uint32_t k
     uint8_t* const dst = &ring[slot][0];
     if (k.op == OP_ATTN) {
         const int32_t d = p.T.d;
-        const Chunk ch = attn_chunk(p.T.attn_splits, attn_fixed_len(p.T.B, p.T.C, p.T.attn_splits), seq_pos(k.seq), k.row0);
+        const AttnTask at = attn_task(p, k);
+        const Chunk ch = at.ch;
         const int32_t pb = attn_block_rows(d);
         const int32_t p0 = ch.c0 + (int32_t)kp * pb;
         const int32_t rows = min(pb, min(ch.c1, ch.P) - p0);
         const uint32_t valid = (uint32_t)rows * (uint32_t)d * 2u;
-        const uint64_t row = (((uint64_t)k.layer * p.T.B + k.seq) * p.T.nkv + k.part) * (uint64_t)p.T.C + (uint64_t)p0;
+        const uint64_t row = (((uint64_t)k.layer * p.T.B + (uint32_t)at.b) * p.T.nkv + k.part) * (uint64_t)p.T.C + (uint64_t)p0;
         const uint8_t* kb = (const uint8_t*)S.args.kc + row * d * 2;
         const uint8_t* vb = (const uint8_t*)S.args.vc + row * d * 2;
         // K: for the matrix-core attention (head_dim 64, up to 4 heads per group) rows stay
@@ -505,16 +603,20 @@ __device__ __noinline__ void loader(const Params* pp, uint32_t epoch, int lw) {
     c_task* tasks = (c_task*)p.tasks;
     const uint32_t sched = p.sched;
     const uint32_t n_tasks = p.n_tasks;
-    const int32_t splits = p.T.attn_splits, hd = p.T.d, fixed_len = attn_fixed_len(p.T.B, p.T.C, p.T.attn_splits);
+    const int32_t hd = p.T.d;
+    const bool deal = batched_path(p.T.B, p.T.E);
+    bool dealt = false;
     uint32_t qbeg = 0, qend = 0;
     if (sched == 0) {
         qbeg = qoff[blockIdx.x];
         qend = qoff[blockIdx.x + 1];
     }
     uint32_t pseq = 0, pub = 0;  // next page to issue / to publish
+    const bool tr = lw == 0 && uni(lds_ld(S.trace_on)) != 0;
 
     auto publish_one = [&]() {
         if (lane == 0) lds_st(S.page_ready[lw][pub % NPAGES], pub / NPAGES + 1);
+        if (tr && lane == 0) lds_st(S.tl_pub[lds_ld(S.pg_fslot[pub % NPAGES])], (uint32_t)rtc());
         ++pub;
     };
     auto drain = [&]() {
@@ -569,6 +671,19 @@ __device__ __noinline__ void loader(const Params* pp, uint32_t epoch, int lw) {
             k = Task();
             k.op = OP_END;
         }
+        if (deal && !dealt && !end && k.op == OP_ATTN) {
+            // this step's deal of the attention slots, before the first attention task
+            // reaches the compute waves or its pages are issued
+            if (lw == 0) {
+                attn_deal(p, lane);
+                lgkm_wait_all();
+                if (lane == 0) lds_st(S.adealt, 1u);
+            } else if (lds_ld(S.adealt) == 0u) {
+                drain();  // publish this wave's pages in flight before it waits
+                if (!uni(lds_wait_ge(S.adealt, 1u, pp, ti))) break;
+            }
+            dealt = true;
+        }
         if (lw == 0) {
             const uint32_t slot = t % FIFO;
             if (lds_ld(S.fifo_free[slot]) < t / FIFO) {
@@ -579,12 +694,17 @@ __device__ __noinline__ void loader(const Params* pp, uint32_t epoch, int lw) {
 #pragma unroll
                 for (int i = 0; i < 12; ++i) lds_st(((uint32_t*)&S.fifo[slot])[i], ((const uint32_t*)&k)[i]);
                 lds_st(S.fifo_first_page[slot], pseq);
+                if (tr) {
+                    lds_st(S.tl_issue0[slot], 0u);
+                    lds_st(S.tl_issue1[slot], 0u);
+                    lds_st(S.tl_pub[slot], 0u);
+                }
             }
             lgkm_wait_all();
             if (lane == 0) lds_st(S.fifo_ready[slot], t + 1);
         }
         if (end) break;
-        const uint32_t np = task_pages(k, splits, fixed_len, hd);
+        const uint32_t np = task_pages(p, k, hd);
         for (uint32_t kp = 0; kp < np; ++kp) {
             const uint32_t ps = pseq % NPAGES;
             const uint32_t need = NCW * (pseq / NPAGES);
@@ -593,10 +713,27 @@ __device__ __noinline__ void loader(const Params* pp, uint32_t epoch, int lw) {
                 if (!uni(lds_wait_ge(S.page_free[ps], need, pp, ti))) goto out;
             }
             issue_page(p, k, kp, ps, lane, lw);
+            if (tr && lane == 0) {
+                const uint32_t now = (uint32_t)rtc(), fs = t % FIFO;
+                lds_st(S.pg_fslot[ps], fs);
+                if (kp == 0) lds_st(S.tl_issue0[fs], now);
+                lds_st(S.tl_issue1[fs], now);
+            }
             ++pseq;
-            if (pseq - pub == MAX_INFLIGHT) {
+            if constexpr (ATTN_INFLIGHT == MAX_INFLIGHT) {
+                if (pseq - pub == MAX_INFLIGHT) {
+                    vm_wait<LPP * (MAX_INFLIGHT - 1)>();
+                    publish_one();
+                }
+            } else if (k.op == OP_ATTN) {
+                if (pseq - pub >= (uint32_t)ATTN_INFLIGHT) {
+                    vm_wait<LPP * (ATTN_INFLIGHT - 1)>();
+                    while (pseq - pub > (uint32_t)ATTN_INFLIGHT - 1u) publish_one();
+                }
+            } else if (pseq - pub >= (uint32_t)MAX_INFLIGHT) {
+                // (after an attention task's deeper queue: every page but the newest MAX_INFLIGHT - 1)
                 vm_wait<LPP * (MAX_INFLIGHT - 1)>();
-                publish_one();
+                while (pseq - pub > (uint32_t)MAX_INFLIGHT - 1u) publish_one();
             }
         }
     }
@@ -655,6 +792,14 @@ __device__ __forceinline__ bool page_acquire(const Params* pp, uint32_t seq, uin
         if (it == 512u && !lds_wait_ge(w, want, pp, task)) return false;
     }
     return true;
+}
+// Traced wave 0: page_acquire, its waiting time added to tm[3] (ticks).
+__device__ __forceinline__ bool page_acquire_tr(const Params* pp, uint32_t seq, uint32_t task, bool tr, int lane) {
+    if (!tr) return page_acquire(pp, seq, task);
+    const uint32_t t0 = (uint32_t)rtc();
+    const bool ok = page_acquire(pp, seq, task);
+    if (lane == 0) lds_st(S.tm[3], lds_ld(S.tm[3]) + ((uint32_t)rtc() - t0));
+    return ok;
 }
 __device__ __forceinline__ void page_release(uint32_t seq, int lane) {
     lgkm_wait_all();
@@ -1063,7 +1208,7 @@ __device__ __forceinline__ void load_residual(CParams& p, const Task& k, int idx
 
 // ---- several sequences: matrix-core operands in global memory -------------------------
 //
-// With B > 1 sequences, the inputs of the O-projection (merged attention) and of the
+// On the several-sequence path (B > 1, or any B with experts), the inputs of the O-projection (merged attention) and of the
 // down-projection (SiLU(gate) * up) are written once per step as matrix-core B operands
 // (columns = sequences) by their producers, with device-scope stores, and read with
 // device-scope loads by every tile that consumes them.  Each fp32 input is carried as
@@ -1128,14 +1273,12 @@ __device__ __forceinline__ void put_op1(uint16_t* R, int nkb, int c, int b, floa
     __builtin_amdgcn_raw_buffer_store_b16((uint16_t)l0, r, opr_index(nkb, 1, c, b) * 2, 0, 16);
 }
 
-// One wave merges the attention chunks of (layer, sequence b, KV group g) into the
-// O-projection's operands: a = sum_c e^(m_c - M) o_c / sum_c e^(m_c - M) l_c over the
-// non-empty chunks.  Lane = (query head, 8-dimension chunk).
-__device__ __noinline__ void merge_chunks(const Params* pp, int layer, int b, int g, int32_t pos, int lane) {
+// One wave merges the nch attention chunks of (layer, sequence b, KV group g) into the
+// O-projection's operands: a = sum_c e^(m_c - M) o_c / sum_c e^(m_c - M) l_c.
+// Lane = (query head, 8-dimension chunk).
+__device__ __noinline__ void merge_chunks(const Params* pp, int layer, int b, int g, int nch, int lane) {
     CParams& p = P(pp);
-    const int D = p.T.d, G = p.T.grp, Sp = p.T.attn_splits;
-    const int32_t fl = attn_fixed_len(p.T.B, p.T.C, Sp);
-    const int nch = min(Sp, (pos + fl) / fl);  // chunks holding at least one of the pos + 1 positions
+    const int D = p.T.d, G = p.T.grp, Sp = ATTN_MAX_CHUNKS;  // partials: ATTN_MAX_CHUNKS chunks per (b, g)
     const uint32_t cs = (uint32_t)G * (D + 2);  // floats per chunk
     uint16_t* R = opr_attn(p, layer, b / GROUP_SEQS);
     const int nkb = p.T.nq * D / 32;
@@ -1272,8 +1415,9 @@ __device__ __noinline__ bool op_attn(const Params* pp, uint32_t slot_, uint32_t 
     Ctx c = make_ctx(t_, epoch_);
     CParams& p = P(pp);
     const int lane = c.lane, wave = c.wave;
-    const int b = (int)k.seq, g = k.part;
-    const Chunk ch = attn_chunk(p.T.attn_splits, attn_fixed_len(p.T.B, p.T.C, p.T.attn_splits), S.pos[b], k.row0);
+    const AttnTask at = attn_task(p, k);
+    const int b = at.b, g = k.part;
+    const Chunk ch = at.ch;
     constexpr int PB = 4096 / D;      // positions per page (64 or 32)
     constexpr int NC = D / 8;         // 16-byte chunks per row (8 or 16)
     constexpr int NPG = 64 / NC;      // position groups in P.V (8 or 4)
@@ -1287,12 +1431,12 @@ __device__ __noinline__ bool op_attn(const Params* pp, uint32_t slot_, uint32_t 
     const int nh = (G - wave + NCW - 1) / NCW;  // heads of this wave: wave, wave + NCW, ...
     const bool has_cur = ch.c0 <= ch.P && ch.P < ch.c1;
     const int cl = lane % NC, pgl = lane / NC;  // P.V: dimension chunk and position group of this lane
-    // an empty chunk slot (several sequences; their merge reads only the non-empty
-    // chunks): no pages, no partials, no wait for the event.  It still takes the
+    // an empty slot (several sequences; the merge reads only the non-empty chunks):
+    // no pages, no partials, no wait for the event.  It still takes the
     // workgroup's start-of-task handshake: without it the waves that have no work
     // would run ahead into later tasks and count their completions early.  At batch 1
     // every chunk writes its partials.
-    if (p.T.B > 1 && ch.c0 > ch.P) {
+    if (batched_path(p.T.B, p.T.E) && ch.c0 > ch.P) {
         Task none = k;
         none.wait_ev = NONE;
         return await_inputs(pp, none, c);
@@ -1464,7 +1608,8 @@ __device__ __noinline__ bool op_attn(const Params* pp, uint32_t slot_, uint32_t 
     for (int hh = 0; hh < 4; ++hh) {
         if (hh >= nh) break;
         const int hw = wave + hh * NCW;
-        float* dst = p.part + ((((size_t)b * p.T.nkv + g) * p.T.attn_splits + k.row0) * G + hw) * (D + 2);
+        float* dst = p.part + ((((size_t)b * p.T.nkv + g) * part_chunks(batched_path(p.T.B, p.T.E), p.T.attn_splits) +
+                               (size_t)at.c) * G + hw) * (D + 2);
         if (lane == 0) {
             stf_dev(dst, M[hh]);
             stf_dev(dst + 1, Ls[hh]);
@@ -1474,14 +1619,12 @@ __device__ __noinline__ bool op_attn(const Params* pp, uint32_t slot_, uint32_t 
             for (int ee = 0; ee < 8; ++ee) stf_dev(dst + 2 + cl * 8 + ee, o[hh][ee]);
         }
     }
-    if (p.T.B > 1 && nh > 0) {
+    if (batched_path(p.T.B, p.T.E) && nh > 0) {
         // several sequences: every wave with heads counts its finished partials on the
         // step's ticket of (sequence, group); the wave completing the count over the
         // non-empty chunks merges them all
         vm_wait_all();  // this wave's partials are stored
-        const int32_t fl = attn_fixed_len(p.T.B, p.T.C, p.T.attn_splits);
-        const uint32_t nch = (uint32_t)min(p.T.attn_splits, (ch.P + fl) / fl);
-        const uint32_t want = nch * (uint32_t)min(G, NCW);
+        const uint32_t want = (uint32_t)at.nch * (uint32_t)min(G, NCW);
         uint32_t old = 0;
         release_fence();
         if (lane == 0)
@@ -1489,7 +1632,7 @@ __device__ __noinline__ bool op_attn(const Params* pp, uint32_t slot_, uint32_t 
         old = uni(old);
         if (old + 1u == want) {
             acquire_fence();
-            merge_chunks(pp, k.layer, b, g, ch.P, lane);
+            merge_chunks(pp, k.layer, b, g, at.nch, lane);
         }
     }
     return true;
@@ -1541,8 +1684,9 @@ __device__ __noinline__ bool op_attn_mfma(const Params* pp, uint32_t slot_, uint
     Ctx c = make_ctx(t_, epoch_);
     CParams& p = P(pp);
     const int lane = c.lane, wave = c.wave;
-    const int b = (int)k.seq, g = k.part, G = p.T.grp;
-    Chunk ch = attn_chunk(p.T.attn_splits, attn_fixed_len(p.T.B, p.T.C, p.T.attn_splits), S.pos[b], k.row0);
+    const AttnTask at = attn_task(p, k);
+    const int b = at.b, g = k.part, G = p.T.grp;
+    Chunk ch = at.ch;
     ch.c0 = (int32_t)uni((uint32_t)ch.c0);  // wave-uniform: scalar loop bounds and branches
     ch.c1 = (int32_t)uni((uint32_t)ch.c1);
     ch.P = (int32_t)uni((uint32_t)ch.P);
@@ -1553,7 +1697,7 @@ __device__ __noinline__ bool op_attn_mfma(const Params* pp, uint32_t slot_, uint
     const bool has_cur = ch.c0 <= ch.P && ch.P < ch.c1;
     // an empty chunk slot (several sequences): no pages, no partials, but the start-of-task
     // handshake (see op_attn)
-    if (p.T.B > 1 && ch.c0 > ch.P) {
+    if (batched_path(p.T.B, p.T.E) && ch.c0 > ch.P) {
         Task none = k;
         none.wait_ev = NONE;
         return await_inputs(pp, none, c);
@@ -1596,8 +1740,27 @@ __device__ __noinline__ bool op_attn_mfma(const Params* pp, uint32_t slot_, uint
     for (uint32_t pb0 = 0; pb0 < npages; pb0 += BATCH) {
         const uint32_t nb = min((uint32_t)BATCH, npages - pb0);
         for (uint32_t i = 0; i < nb; ++i)
-            if (!page_acquire(pp, page0 + pb0 + i, k.id)) return false;
+            if (!page_acquire_tr(pp, page0 + pb0 + i, k.id, c.tr && wave == 0, lane)) return false;
         tmark(c, 2);
+        // this wave's K operands and V words of the batch's pages into registers, then the
+        // pages go back to the loader, which refills them during the arithmetic below
+        u32x4v ka[BATCH][2];
+        u32x2v vw4[BATCH][4];
+#pragma unroll
+        for (int i = 0; i < BATCH; ++i) {
+            if ((uint32_t)i >= nb) break;
+            const uint32_t slot = (page0 + pb0 + i) % NPAGES;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const int pos = 16 * wave + n, cix = (4 * ks + kq) ^ (pos & 7);
+                ka[i][ks] = *(const u32x4v*)&ring[slot][pos * (2 * D) + cix * 16];
+            }
+            // V of positions 4 kq + j (j = 0..3) of this wave's 16, dimensions 4 n .. 4 n + 3
+            const uint16_t* vrow = (const uint16_t*)&ring[slot][8192] + (16 * wave + 4 * kq) * D + 4 * n;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) vw4[i][j] = *(const u32x2v*)(vrow + j * D);
+        }
+        for (uint32_t i = 0; i < nb; ++i) page_release(page0 + pb0 + i, lane);  // (waits for the reads)
         float sc[BATCH][4];
         float mx = -INFINITY;
 #pragma unroll
@@ -1605,17 +1768,13 @@ __device__ __noinline__ bool op_attn_mfma(const Params* pp, uint32_t slot_, uint
 #pragma unroll
             for (int r = 0; r < 4; ++r) sc[i][r] = -INFINITY;
             if ((uint32_t)i < nb) {
-                const uint32_t slot = (page0 + pb0 + i) % NPAGES;
                 const int32_t rows = min(PB, pre_end - (ch.c0 + (int32_t)(pb0 + i) * PB));
                 const int32_t lim = rows - 16 * wave - 4 * kq;  // this lane's valid positions: r < lim
                 f32x4v acc = f32x4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    const int pos = 16 * wave + n, cix = (4 * ks + kq) ^ (pos & 7);
-                    const u32x4v a = *(const u32x4v*)&ring[slot][pos * (2 * D) + cix * 16];
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8v, a),
+                for (int ks = 0; ks < 2; ++ks)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8v, ka[i][ks]),
                                                                    __builtin_bit_cast(bf16x8v, qb[ks]), acc, 0, 0, 0);
-                }
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     // every lane takes part in the row sums; positions past the page's rows get -inf
@@ -1637,7 +1796,6 @@ __device__ __noinline__ bool op_attn_mfma(const Params* pp, uint32_t slot_, uint
 #pragma unroll
         for (int i = 0; i < BATCH; ++i) {
             if ((uint32_t)i >= nb) break;
-            const uint32_t slot = (page0 + pb0 + i) % NPAGES;
             float pr[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -1648,12 +1806,8 @@ __device__ __noinline__ bool op_attn_mfma(const Params* pp, uint32_t slot_, uint
             const s16x4v pbv = __builtin_bit_cast(
                 s16x4v, u32x2v{split_part2(pr[0], pm) | (split_part2(pr[1], pm) << 16),
                                split_part2(pr[2], pm) | (split_part2(pr[3], pm) << 16)});
-            // V of positions 4 kq + j (j = 0..3) of this wave's 16, dimensions 4 n .. 4 n + 3 (8 bytes
-            // each); A operand t is V^T with row n standing for dimension d = 4 n + t
-            const uint16_t* vrow = (const uint16_t*)&ring[slot][8192] + (16 * wave + 4 * kq) * D + 4 * n;
-            u32x2v vw[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) vw[j] = *(const u32x2v*)(vrow + j * D);
+            // A operand t is V^T with row n standing for dimension d = 4 n + t (V words read above)
+            const u32x2v* vw = vw4[i];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const int c = t / 2;
@@ -1665,7 +1819,6 @@ __device__ __noinline__ bool op_attn_mfma(const Params* pp, uint32_t slot_, uint
                                                                      oacc[t], 0, 0, 0);
             }
         }
-        for (uint32_t i = 0; i < nb; ++i) page_release(page0 + pb0 + i, lane);
     }
     // this wave's record for the merge: M and L per head, O[head][d]
     float* const mrec = &S.xs[MAX_ACT / 2 + wave * MW];
@@ -1710,19 +1863,18 @@ __device__ __noinline__ bool op_attn_mfma(const Params* pp, uint32_t slot_, uint
             Mx = mn;
         }
         // partials (m, l, o) -> part[b][g][chunk][head][D + 2]
-        float* dst = p.part + ((((size_t)b * p.T.nkv + g) * p.T.attn_splits + k.row0) * G + h) * (D + 2);
+        float* dst = p.part + ((((size_t)b * p.T.nkv + g) * part_chunks(batched_path(p.T.B, p.T.E), p.T.attn_splits) +
+                               (size_t)at.c) * G + h) * (D + 2);
         if (lane == 0) {
             stf_dev(dst, Mx);
             stf_dev(dst + 1, Lt);
         }
         stf_dev(dst + 2 + lane, o);
-        if (p.T.B > 1) {
+        if (batched_path(p.T.B, p.T.E)) {
             // several sequences: count this head's partial on the step's ticket of
             // (sequence, group); the wave completing the count merges the chunks
             vm_wait_all();
-            const int32_t fl = attn_fixed_len(p.T.B, p.T.C, p.T.attn_splits);
-            const uint32_t nch = (uint32_t)min(p.T.attn_splits, (ch.P + fl) / fl);
-            const uint32_t want = nch * (uint32_t)min(G, NCW);
+            const uint32_t want = (uint32_t)at.nch * (uint32_t)min(G, NCW);
             uint32_t old = 0;
             release_fence();
             if (lane == 0)
@@ -1730,7 +1882,7 @@ __device__ __noinline__ bool op_attn_mfma(const Params* pp, uint32_t slot_, uint
             old = uni(old);
             if (old + 1u == want) {
                 acquire_fence();
-                merge_chunks(pp, k.layer, b, g, ch.P, lane);
+                merge_chunks(pp, k.layer, b, g, at.nch, lane);
             }
         }
     }
@@ -1930,7 +2082,7 @@ __device__ __noinline__ bool op_lmhead(const Params* pp, uint32_t slot_, uint32_
     return true;
 }
 
-// ---- batched GEMV tiles (B > 1) ------------------------------------------------------
+// ---- batched GEMV tiles (B > 1, or experts) ------------------------------------------
 //
 // One pass over a weight tile serves all sequences: the tile's 16 x 32 blocks are the
 // A operands, the inputs of the 16 sequences the B operands (two bf16 parts, one MFMA
@@ -2043,7 +2195,7 @@ __device__ __forceinline__ bool gemv_mfma_b(const Params* pp, int wave, int lane
 #pragma unroll
             for (int s = 0; s < PPR; ++s) {
                 const uint32_t pg = rg * PPR + s;
-                if (!page_acquire(pp, page0 + pg, task)) return false;
+                if (!page_acquire_tr(pp, page0 + pg, task, trace_pages, lane)) return false;
                 if (trace_pages && wave == 0 && lane == 0) lds_st(S.tm[2], (uint32_t)rtc());
                 const uint32_t slot = (page0 + pg) % NPAGES;
                 u32x4v a[4];
@@ -2063,7 +2215,7 @@ __device__ __forceinline__ bool gemv_mfma_b(const Params* pp, int wave, int lane
         constexpr int BPR = 4 / RPG;   // blocks per row group and wave
         const uint32_t npages = (nrg + RPG - 1) / RPG;
         for (uint32_t pg = 0; pg < npages; ++pg) {
-            if (!page_acquire(pp, page0 + pg, task)) return false;
+            if (!page_acquire_tr(pp, page0 + pg, task, trace_pages, lane)) return false;
             if (trace_pages && wave == 0 && lane == 0) lds_st(S.tm[2], (uint32_t)rtc());
             const uint32_t slot = (page0 + pg) % NPAGES;
             u32x4v a[4];
@@ -2085,7 +2237,8 @@ __device__ __forceinline__ bool gemv_mfma_b(const Params* pp, int wave, int lane
     return true;
 }
 
-// Batched GEMV task (QKV, O-proj, gate/up, down, LM head) for B > 1 sequences.  QKV,
+// Batched GEMV task (QKV, O-proj, gate/up, down, LM head, router, expert gate/up and down)
+// on the several-sequence path.  QKV,
 // gate/up and LM head read the residual rows themselves and apply RMSNorm (gains on
 // the inputs, 1/RMS per sequence on the results); O-proj and down read the operand
 // regions their producers wrote.
@@ -2424,6 +2577,7 @@ __device__ __noinline__ void compute(const Params* pp, uint32_t epoch, int wave)
     uint32_t* const ctr = p0.ctr;
     const uint32_t drop_task = p0.drop_task, sched = p0.sched, n_exp = (uint32_t)p0.T.E;
     uint32_t* const task_count = p0.task_count;
+    const bool batched = batched_path(p0.T.B, p0.T.E);
     for (uint32_t t = 0;; ++t) {
         const uint32_t slot = t % FIFO;
         if (!lds_wait_ge(S.fifo_ready[slot], t + 1, pp, NONE)) return;
@@ -2435,7 +2589,7 @@ __device__ __noinline__ void compute(const Params* pp, uint32_t epoch, int wave)
         bool ok = true;
         // single-sequence operations referenced first: their functions are emitted next
         // to the loader, ahead of the several-sequence GEMV instances
-        if (p0.T.B == 1) {
+        if (!batched) {
             switch (k.op) {
                 case OP_QKV: ok = MK_KT_DISPATCH(op_qkv, h, pp, slot, page0, t, epoch); break;
                 case OP_ATTN: ok = attn_kswizzle(p0.T.d, p0.T.grp) ? op_attn_mfma(pp, slot, page0, t, epoch)
@@ -2521,7 +2675,16 @@ __device__ __noinline__ void compute(const Params* pp, uint32_t epoch, int wave)
                 gst(tr + 9, (unsigned long long)(t_fetch + we));
                 gst(tr + 10, (unsigned long long)(t_fetch + wa));
                 gst(tr + 11, (unsigned long long)(hi | lds_ld(S.tw_epi[0])));
-                if (c.lane == 0) lds_st(S.tm[2], 0u);
+                // the loader's stamps (0: the task has no pages)
+                const uint32_t i0 = lds_ld(S.tl_issue0[slot]), i1 = lds_ld(S.tl_issue1[slot]), pb_ = lds_ld(S.tl_pub[slot]);
+                gst(tr + 12, i0 ? (unsigned long long)(hi | i0) : 0ull);
+                gst(tr + 13, i1 ? (unsigned long long)(hi | i1) : 0ull);
+                gst(tr + 14, pb_ ? (unsigned long long)(hi | pb_) : 0ull);
+                gst(tr + 15, (unsigned long long)lds_ld(S.tm[3]));  // wave 0's page waits (ticks)
+                if (c.lane == 0) {
+                    lds_st(S.tm[2], 0u);
+                    lds_st(S.tm[3], 0u);
+                }
             }
             vm_wait_all();
             if (c.lane == 0) lds_add(S.fifo_free[slot], 1u);
@@ -2551,6 +2714,9 @@ __global__ void __launch_bounds__(NTHREADS, 1) mk_step_kernel(const Params* pp, 
         S.dyn_ready = 0;
         S.dyn_ack = 0;
         S.trace_on = p.trace != nullptr ? 1u : 0u;
+        S.adealt = 0;
+        S.tm[2] = 0;
+        S.tm[3] = 0;
         S.args = a;
     }
     const uint32_t epoch = p.state[ST_EPOCH];

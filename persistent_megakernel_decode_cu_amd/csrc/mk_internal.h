@@ -33,7 +33,19 @@ constexpr int MAX_ACT = 4096;        // floats of one staged activation vector (
 // (chunk by chunk of halves_chunk_rows rows: all row groups of columns 0..1023, then
 // of 1024..2047), so that their GEMV holds the operands of one half at a time.
 constexpr int halves_chunk_rows(int B) { return (MAX_TILE_ROWS / (B < GROUP_SEQS ? B : GROUP_SEQS)) / 64 * 64; }
-constexpr bool halves_packed(int B, int op, int kt) { return B > 1 && kt == 2048 && (op == OP_QKV || op == OP_GATEUP); }
+constexpr bool halves_packed(bool batched, int op, int kt) { return batched && kt == 2048 && (op == OP_QKV || op == OP_GATEUP); }
+
+// The several-sequence path (batched GEMV tiles over column groups of sequences,
+// fixed-length attention chunk slots merged by the last chunk, operand regions) runs
+// every step of more than one sequence and every mixture-of-experts step: expert
+// routing is implemented there only, so one sequence with experts is a column group
+// of one.
+constexpr bool batched_path(int B, int E) { return B > 1 || E > 0; }
+
+// Attention partials per (sequence, KV group): at most 16 chunks are merged; on the
+// several-sequence path a sequence may take up to 16 of its group's chunk slots.
+constexpr int ATTN_MAX_CHUNKS = 16;
+constexpr int part_chunks(bool batched, int splits) { return batched ? ATTN_MAX_CHUNKS : splits; }
 
 // One instruction of the interpreter: 48 bytes, read by the loader wave into LDS.
 struct Task {

@@ -89,10 +89,8 @@ mk_status plan(const mk_model_desc* desc, int32_t batch, int32_t max_ctx, const 
     Tiling T;
     std::string err;
     Dims dm = dims_of(desc);
-    if (batch > MAX_BATCH || (batch > 1 && dm.h > 2048) || (dm.n_experts != 0 && batch < 2)) {
-        if (dm.n_experts < 0 || batch < 1) return MK_E_INVALID;
-        return MK_E_UNSUPPORTED;
-    }
+    if (dm.n_experts < 0 || batch < 1) return MK_E_INVALID;
+    if (batch > MAX_BATCH || (batched_path(batch, dm.n_experts) && dm.h > 2048)) return MK_E_UNSUPPORTED;
     if (plan_tiling(dm, batch, max_ctx, W, po, &T, &err) != 0) return MK_E_INVALID;
     Layout Ly;
     *tied = desc->tied_lm_head != 0;
@@ -191,7 +189,7 @@ mk_status repack(mk_handle* h, const mk_model_desc* d, uint8_t* wd) {
         while (rows.size() < (size_t)t.row_base + t.rows) rows.push_back(nullptr);
         t.blocked = kt <= 2048 ? 1u : 0u;
         t.chunk_rows = 0;
-        if (halves_packed(T.B, k.op, (int)kt)) {
+        if (halves_packed(batched_path(T.B, T.E), k.op, (int)kt)) {
             t.blocked = 2u;
             t.chunk_rows = (uint32_t)halves_chunk_rows(T.B);
         }
@@ -374,11 +372,11 @@ mk_status mk_build_graph(const mk_model_desc* desc, int32_t batch, int32_t max_c
     ALLOC(rope, (size_t)T.C * half * sizeof(float2), false);
     p.rope = rope;
     ALLOC(p.q, (size_t)T.B * T.nq * T.d * 4, true);
-    ALLOC(p.part, (size_t)T.B * T.nkv * T.attn_splits * T.grp * (T.d + 2) * 4, true);
+    ALLOC(p.part, (size_t)T.B * T.nkv * part_chunks(batched_path(T.B, T.E), T.attn_splits) * T.grp * (T.d + 2) * 4, true);
     ALLOC(p.m, (size_t)T.B * T.f * 4, true);
     h->acc_bytes = (size_t)2 * (2 * T.L + 1) * T.B * T.h * 4;
     ALLOC(p.acc, h->acc_bytes, true);
-    if (T.B > 1) {
+    if (batched_path(T.B, T.E)) {
         // matrix-core operands of the O- and down-projection inputs: 2 bf16 parts x 16
         // sequences per column (columns of absent sequences stay zero for the handle's life)
         const size_t n_sg = (size_t)(T.B + GROUP_SEQS - 1) / GROUP_SEQS;
@@ -430,10 +428,10 @@ mk_status mk_build_graph(const mk_model_desc* desc, int32_t batch, int32_t max_c
         };
         const size_t o_ctr = take(h->n_events * 8 * 32 * 4), o_state = take(ST_WORDS * 4);
         const size_t o_q = take((size_t)T.B * T.nq * T.d * 4);
-        const size_t o_part = take((size_t)T.B * T.nkv * T.attn_splits * T.grp * (T.d + 2) * 4);
+        const size_t o_part = take((size_t)T.B * T.nkv * part_chunks(batched_path(T.B, T.E), T.attn_splits) * T.grp * (T.d + 2) * 4);
         const size_t o_m = take((size_t)T.B * T.f * 4), o_acc = take(h->acc_bytes);
-        const size_t o_xop = T.B > 1 ? take(h->xop_bytes) : 0;
-        const size_t o_at = T.B > 1 ? take((size_t)2 * T.L * T.B * T.nkv * 4) : 0;
+        const size_t o_xop = batched_path(T.B, T.E) ? take(h->xop_bytes) : 0;
+        const size_t o_at = batched_path(T.B, T.E) ? take((size_t)2 * T.L * T.B * T.nkv * 4) : 0;
         const size_t o_rl = T.E ? take((size_t)T.L * T.B * T.E * 4) : 0;
         const size_t o_key = take(sizeof(unsigned long long) * 2 * T.B), o_ticket = take(4 * (size_t)T.B);
         const size_t o_rqs = o.sched == 2 ? take(h->g.tasks.size() * 4) : 0;
@@ -452,8 +450,8 @@ mk_status mk_build_graph(const mk_model_desc* desc, int32_t batch, int32_t max_c
             q.part = (float*)(base + o_part);
             q.m = (float*)(base + o_m);
             q.acc = (float*)(base + o_acc);
-            q.xop = T.B > 1 ? (uint16_t*)(base + o_xop) : nullptr;
-            q.aticket = T.B > 1 ? (uint32_t*)(base + o_at) : nullptr;
+            q.xop = batched_path(T.B, T.E) ? (uint16_t*)(base + o_xop) : nullptr;
+            q.aticket = batched_path(T.B, T.E) ? (uint32_t*)(base + o_at) : nullptr;
             q.rlogit = T.E ? (float*)(base + o_rl) : nullptr;
             q.key = (unsigned long long*)(base + o_key);
             q.ticket = (uint32_t*)(base + o_ticket);
@@ -572,7 +570,7 @@ mk_status enqueue_poison(mk_handle* h, const Params& p, float* logits, hipStream
         };
         const uint32_t fnan = 0x7fc00000u, bnan2 = 0x7fc07fc0u, neg1 = 0xffffffffu;
         span(p.q, (size_t)T.B * T.nq * T.d * 4, fnan);
-        span(p.part, (size_t)T.B * T.nkv * T.attn_splits * T.grp * (T.d + 2) * 4, fnan);
+        span(p.part, (size_t)T.B * T.nkv * part_chunks(batched_path(T.B, T.E), T.attn_splits) * T.grp * (T.d + 2) * 4, fnan);
         span(p.m, (size_t)T.B * T.f * 4, fnan);
         span(p.xop, h->xop_bytes, bnan2);
         span(p.rlogit, (size_t)T.L * T.B * T.E * 4, fnan);

@@ -63,6 +63,7 @@ CASES = [
     (TINY, 1, 700, 5, (520, 520)),  # three chunks, the last one ragged
     (TINY, 3, 256, 16, (3, 200)),
     (TINY, 17, 64, 32, (1, 60)),
+    (TINY_MOE, 1, 300, 16, (200, 200)),
     (TINY_MOE, 2, 128, 16, (5, 100)),
     (TINY_MOE, 17, 32, 24, (0, 30)),
 ]
@@ -81,7 +82,7 @@ def test_oracle_graph_on_the_fake_device_equals_the_decode_step(cfg, B, C, W, ct
         assert _agrees(cfg, out, kk, vv, want), mode
 
 
-@pytest.mark.parametrize("cfg,B,C,W,ctx", CASES[:1] + CASES[3:4] + CASES[5:], ids=lambda x: getattr(x, "name", str(x)))
+@pytest.mark.parametrize("cfg,B,C,W,ctx", CASES[:1] + CASES[3:5] + CASES[6:], ids=lambda x: getattr(x, "name", str(x)))
 @pytest.mark.parametrize("policy", [0, 1])
 def test_library_plan_on_the_fake_device_equals_the_decode_step(cfg, B, C, W, ctx, policy):
     case = _case(cfg, B, C, *ctx)
@@ -140,3 +141,43 @@ def test_planted_mistakes_break_the_result():
 
     for edit in (no_resid, head_twice, oproj_waits_on_qkv, low_target, chunk_twice):
         assert broken(edit), edit.__name__
+
+
+def _deal_of(pos, S, C=1 << 20, d=64):
+    dev = fd.FakeDevice(TINY.with_(head_dim=d), {}, len(pos), C, S)
+    dev.pos = np.asarray(pos)
+    return dev._deal()
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_attention_deal_is_the_min_max_split_by_brute_force(seed):
+    """The deal covers every context exactly once with at most B S chunks (16 per sequence at most), and its
+    longest chunk, in pages, is the smallest any split of the contexts into that many chunks can reach
+    (all allocations of chunks to sequences enumerated)."""
+    import itertools
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 5))
+    S = int(rng.integers(1, 5))
+    pos = rng.integers(0, 1200, B)
+    pb = 64
+    slots, per = _deal_of(pos, S)
+    n = pos + 1
+    for b in range(B):
+        ln, nch = per[b]
+        assert ln % pb == 0 and 1 <= nch <= 16
+        got = sorted(c for (bb, c) in slots.values() if bb == b)
+        assert got == list(range(nch))
+        assert (nch - 1) * ln < n[b] <= nch * ln  # chunks [c ln, (c + 1) ln) clipped to n cover 0..n-1
+    assert len(slots) <= B * S and max(slots) < B * S
+    best = min(max(-(-(-(-n[b] // s[b])) // pb) for b in range(B))
+               for s in itertools.product(range(1, min(16, B * S) + 1), repeat=B) if sum(s) <= B * S)
+    assert max(per[b][0] // pb for b in range(B)) == best
+
+
+def test_attention_deal_worked_example():
+    """Two sequences at positions 4095 and 299 (n = 4096 and 300) share 2 x 8 slots: L = 5 pages (320
+    positions: 13 + 1 chunks fit 16, 4 pages would need 16 + 2); sequence 0 takes 13 slots of 320 positions
+    (the last chunk 256), sequence 1 one slot of 320; slots 14 and 15 stay empty."""
+    slots, per = _deal_of([4095, 299], 8)
+    assert per == [(320, 13), (320, 1)]
+    assert slots == {**{c: (0, c) for c in range(13)}, 13: (1, 0)}

@@ -74,7 +74,7 @@ def _one_step(cfg, B, C, pos, exact_experts=True, **opt):
     assert res["argmax_equal"]
 
 
-@pytest.mark.parametrize("B", [2, 5, 20])
+@pytest.mark.parametrize("B", [1, 2, 5, 20])
 def test_tiny_moe_one_step(B):
     pos = synth.make_positions(B, 0, 511)
     pos[0] = 0
@@ -91,12 +91,15 @@ def test_tiny_moe_dynamic_queue(sched):
     _one_step(TINY_MOE, 4, 512, [50, 300, 11, 499], sched=sched)
 
 
-def test_tiny_moe_greedy_chain_and_counters():
-    cfg, B, C, steps = TINY_MOE, 4, 512, 12
+@pytest.mark.parametrize("B", [1, 4])
+def test_tiny_moe_greedy_chain_and_counters(B):
+    """12 chained steps (one sequence: the several-sequence path with a column group of one)."""
+    cfg, C, steps = TINY_MOE, 512, 12
     w = synth.make_weights(cfg)
     kc, vc = synth.make_kv(cfg, B, C)
     tok = synth.make_tokens(cfg, B)
-    P0 = np.array([30, 200, 64, 400], np.int32)
+    P0 = np.array([30, 200, 64, 400][:B], np.int32)
+    print(f"case {cfg.name} B={B} greedy chain of {steps}", flush=True)
     run = Runner(cfg, w, B, C, kc, vc, trace=1)
     t0 = torch.tensor(tok, dtype=torch.int32, device="cuda")
     positions = torch.tensor(np.stack([P0 + s for s in range(steps)]), dtype=torch.int32, device="cuda")
@@ -115,6 +118,11 @@ def test_tiny_moe_greedy_chain_and_counters():
     run.close()
     ref = oracle.greedy(cfg, w, tok, P0, kc.copy(), vc.copy(), steps)
     np.testing.assert_array_equal(np.array(got), ref["tokens"])
+
+
+def test_moe_1b_batch1_first_step():
+    """The 64-expert top-8 MoE with one sequence at context 2048."""
+    _one_step(MOE_1B, 1, 2112, [2048], exact_experts=False)
 
 
 def test_moe_1b_batch16_first_step():

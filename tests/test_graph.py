@@ -211,6 +211,9 @@ BATCH_CASES = [
     (synth.configs.TINY, 20, 64, 512, 0),
     (synth.configs.LLAMA_1B, 32, 256, 4352, 0),
     (synth.configs.TINY_MOE, 5, 37, 512, 0),
+    # one sequence with experts: the several-sequence path with a column group of one
+    (synth.configs.TINY_MOE, 1, 16, 512, 0),
+    (synth.configs.MOE_1B, 1, 256, 2048, 0),
     (synth.configs.TINY_MOE, 20, 64, 512, 1),
     (synth.configs.MOE_1B, 16, 256, 2048, 0),
 ]
@@ -246,8 +249,6 @@ def test_planner_rejects_what_it_does_not_implement():
     cfg = synth.configs.TINY
     with pytest.raises(mk.MkError):
         plan(cfg, 4, B=33)
-    with pytest.raises(mk.MkError):  # expert routing runs on the several-sequence path
-        plan(synth.configs.TINY_MOE, 4, B=1)
     with pytest.raises(mk.MkError):
         plan(synth.configs.LLAMA_8B, 256, B=2)
     with pytest.raises(mk.MkError):
