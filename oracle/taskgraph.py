@@ -23,8 +23,9 @@ The tiling rules (written from the design, not from the C++ code):
   * the several-sequence rules below ("batch > 1") hold for every graph with
     experts too, at batch 1 as well: expert routing exists only on that path.
   * attention: attn_splits chunks per (sequence, KV group), default
-    clamp(ceil(max_ctx / 256), 1, 16) at batch 1 and clamp(pow2_floor(W /
-    (B n_kv)), 1, 8) for batch > 1, at most max_ctx.  With several sequences the
+    clamp(ceil(max_ctx / 256), 1, 16) at batch 1, clamp(pow2_floor(W /
+    (B n_kv)), 1, 8) for batch 2 (and experts at batch 1) and clamp(pow2_floor(2 W /
+    (B n_kv)), 1, 4) for batch > 2, at most max_ctx.  With several sequences the
     B S attention records of a KV group are slots (slot = seq S + chunk) that the
     device deals to the sequences at every step in proportion to their contexts
     (fake_device.py gives the rule); some slots may stay empty.  The last chunk
@@ -108,7 +109,9 @@ def tiling(cfg, B, C, W, attn_splits=0):
     else:
         # batch 1: 256-position chunks; batch > 1: about one attention task per
         # workgroup and layer over all sequences and KV groups, at most 8 slots
-        S = max(1, min(16, -(-C // 256))) if not several else max(1, min(8, _pow2_floor(max(1, W // (B * nkv)))))
+        S = max(1, min(16, -(-C // 256))) if not several else (
+            max(1, min(8, _pow2_floor(max(1, W // (B * nkv))))) if B <= 2 else
+            max(1, min(4, _pow2_floor(max(1, 2 * W // (B * nkv))))))
     S = min(S, C)
     max_rows = _pow2_floor(1024 // min(B, 16))  # rows x sequences (of one column group) of a tile
     E = cfg.n_experts

@@ -86,13 +86,15 @@ int plan_tiling(const Dims& dm, int B, int C, int W, const PlanOptions& o, Tilin
     int S = o.attn_splits;
     if (S > 16) return fail("attn_splits must be at most 16 (the merge reads up to 16 chunk partials)");
     if (S <= 0) {
-        // one sequence: 256-position chunks of its context; the several-sequence path:
-        // about one attention task per workgroup and layer over all sequences and KV
-        // groups, at most 8 slots (each task carries a fixed cost of a few microseconds,
-        // so more, shorter slots measured slower)
+        // one sequence: 256-position chunks of its context.  The several-sequence path
+        // (slots dealt per step in proportion to the contexts): up to two sequences,
+        // about one attention task per workgroup and layer, at most 8 slots; more
+        // sequences, about two, at most 4 slots (each task carries a fixed cost of a few
+        // microseconds; measured at 2..32 sequences of the 1B shape)
+        const int64_t per_wg = batched && B > 2 ? 2 : 1, cap = batched && B > 2 ? 4 : 8;
         S = !batched ? (int)std::max<int64_t>(1, std::min<int64_t>(16, (C + 255) / 256))
-                   : (int)std::max<int64_t>(1, std::min<int64_t>(8, pow2_floor(std::max<int64_t>(
-                                                                     1, (int64_t)W / ((int64_t)B * dm.nkv)))));
+                   : (int)std::max<int64_t>(1, std::min<int64_t>(cap, pow2_floor(std::max<int64_t>(
+                                                                     1, per_wg * W / ((int64_t)B * dm.nkv)))));
     }
     if (S > C) S = C;
     T.attn_splits = S;

@@ -110,12 +110,20 @@ typedef __attribute__((address_space(3))) volatile uint32_t lds_u32;
 typedef __attribute__((address_space(1))) uint32_t g_u32;
 typedef __attribute__((address_space(1))) float g_f32;
 typedef __attribute__((address_space(1))) unsigned long long g_u64;
+typedef __attribute__((address_space(1))) uint16_t g_u16;
 
 // ---- small device helpers -----------------------------------------------------
 
 __device__ __forceinline__ uint64_t rtc() { return __builtin_amdgcn_s_memrealtime(); }
 __device__ __forceinline__ uint32_t xcc_id() { return __builtin_amdgcn_s_getreg(20 | (3 << 11)) & 7u; }
 __device__ __forceinline__ uint32_t uni(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+// A pointer every lane holds the same value of (say, read from LDS), made visibly
+// wave-uniform: a buffer resource built from it then needs no per-lane loop.
+template <class T>
+__device__ __forceinline__ T* uni_ptr(T* ptr) {
+    const uint64_t v = (uint64_t)ptr;
+    return (T*)(((uint64_t)uni((uint32_t)(v >> 32)) << 32) | (uint64_t)uni((uint32_t)v));
+}
 
 // Params are read through the constant address space with a wave-uniform pointer: scalar loads.
 __device__ __forceinline__ CParams& P(const Params* pp) {
@@ -166,10 +174,9 @@ __device__ __forceinline__ void addf_dev(float* p, float v) {
 __device__ __forceinline__ uint32_t addu_dev(uint32_t* p, uint32_t v) {
     return __hip_atomic_fetch_add((g_u32*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// 16-bit device-scope store through a buffer resource whose base is wave-uniform
-__device__ __forceinline__ void st16_dev(uint16_t* base, uint32_t idx, uint16_t v) {
-    __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7ffffff0, 0x00020000);
-    __builtin_amdgcn_raw_buffer_store_b16(v, r, idx * 2, 0, 16 /* sc1 */);
+// 16-bit device-scope store (a plain store with the sc1 bit; each lane its own address)
+__device__ __forceinline__ void st16_dev(uint16_t* p, uint16_t v) {
+    __hip_atomic_store((g_u16*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -457,11 +464,11 @@ __device__ __forceinline__ AttnTask attn_task(CParams& p, const Task& k) {
         a.ch.c0 = a.ch.c1 = a.ch.P + 1;
         return a;
     }
-    a.b = (int32_t)(e >> 8);
-    a.c = (int32_t)(e & 0xffu);
-    a.nch = (int32_t)lds_ld(S.anch[a.b]);
-    const int32_t len = (int32_t)lds_ld(S.alen[a.b]);
-    a.ch.P = seq_pos((uint32_t)a.b);
+    a.b = (int32_t)uni(e >> 8);
+    a.c = (int32_t)uni(e & 0xffu);
+    a.nch = (int32_t)uni(lds_ld(S.anch[a.b]));
+    const int32_t len = (int32_t)uni(lds_ld(S.alen[a.b]));
+    a.ch.P = (int32_t)uni((uint32_t)seq_pos((uint32_t)a.b));
     a.ch.c0 = min(a.ch.P + 1, a.c * len);
     a.ch.c1 = min(a.ch.P + 1, a.ch.c0 + len);
     return a;
@@ -1276,21 +1283,25 @@ __device__ __forceinline__ void put_op1(uint16_t* R, int nkb, int c, int b, floa
 // One wave merges the nch attention chunks of (layer, sequence b, KV group g) into the
 // O-projection's operands: a = sum_c e^(m_c - M) o_c / sum_c e^(m_c - M) l_c.
 // Lane = (query head, 8-dimension chunk).
-__device__ __noinline__ void merge_chunks(const Params* pp, int layer, int b, int g, int nch, int lane) {
+__device__ __noinline__ void merge_chunks(const Params* pp, int layer_, int b_, int g_, int nch_, int lane) {
     CParams& p = P(pp);
+    // wave-uniform arguments (a call passes them in vector registers)
+    const int layer = (int)uni((uint32_t)layer_), b = (int)uni((uint32_t)b_), g = (int)uni((uint32_t)g_),
+              nch = (int)uni((uint32_t)nch_);
     const int D = p.T.d, G = p.T.grp, Sp = ATTN_MAX_CHUNKS;  // partials: ATTN_MAX_CHUNKS chunks per (b, g)
     const uint32_t cs = (uint32_t)G * (D + 2);  // floats per chunk
     uint16_t* R = opr_attn(p, layer, b / GROUP_SEQS);
     const int nkb = p.T.nq * D / 32;
     for (int idx = lane; idx < G * (D / 8); idx += 64) {
         const int head = idx / (D / 8), c8 = idx % (D / 8);
-        const float* src = p.part + ((((size_t)b * p.T.nkv + g) * Sp) * G + head) * (D + 2);
-        const __amdgpu_buffer_rsrc_t r = dev_rsrc(src, (uint32_t)((Sp - 1) * cs + D + 2) * 4);
+        // one wave-uniform resource over the (b, g) partials; this lane's head at offset head (D + 2)
+        const __amdgpu_buffer_rsrc_t r = dev_rsrc(p.part + (((size_t)b * p.T.nkv + g) * Sp) * cs, (uint32_t)(Sp * cs) * 4);
+        const uint32_t ho = (uint32_t)head * (uint32_t)(D + 2);
         float mc[16], lc[16];
 #pragma unroll
         for (int cc = 0; cc < 16; ++cc) {
-            mc[cc] = cc < nch ? ldb_dev(r, (uint32_t)(cc * cs) * 4) : -INFINITY;
-            lc[cc] = cc < nch ? ldb_dev(r, (uint32_t)(cc * cs + 1) * 4) : 0.f;
+            mc[cc] = cc < nch ? ldb_dev(r, (uint32_t)(cc * cs + ho) * 4) : -INFINITY;
+            lc[cc] = cc < nch ? ldb_dev(r, (uint32_t)(cc * cs + ho + 1) * 4) : 0.f;
         }
         float Mx = -INFINITY;
 #pragma unroll
@@ -1306,7 +1317,7 @@ __device__ __noinline__ void merge_chunks(const Params* pp, int layer, int b, in
             for (int cc = 0; cc < 4; ++cc)
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    oc[cc][e] = c4 + cc < nch ? ldb_dev(r, (uint32_t)((c4 + cc) * cs + 2 + c8 * 8 + e) * 4) : 0.f;
+                    oc[cc][e] = c4 + cc < nch ? ldb_dev(r, (uint32_t)((c4 + cc) * cs + ho + 2 + c8 * 8 + e) * 4) : 0.f;
 #pragma unroll
             for (int cc = 0; cc < 4; ++cc) {
                 const float m = mc[c4 + cc];
@@ -1396,8 +1407,8 @@ __device__ __noinline__ bool op_qkv(const Params* pp, uint32_t slot_, uint32_t p
             const int g = is_k ? (int)slot - nq : (int)slot - nq - nkv;
             uint16_t* base = (is_k ? S.args.kc : S.args.vc) +
                              (((size_t)k.layer * p.T.B + 0) * nkv + g) * (size_t)p.T.C * p.T.d + (size_t)P0 * p.T.d;
-            st16_dev(base, (uint32_t)j, f2bf16(lo));
-            st16_dev(base, (uint32_t)(j + half), f2bf16(hi));
+            st16_dev(base + j, f2bf16(lo));
+            st16_dev(base + j + half, f2bf16(hi));
         }
     }
     return true;
@@ -1454,8 +1465,8 @@ __device__ __noinline__ bool op_attn(const Params* pp, uint32_t slot_, uint32_t 
                 qv[hh][ee] = hh < nh ? ldb_dev(qr, ((wave + hh * NCW) * D + lane + 64 * ee) * 4) : 0.f;
         if (has_cur) {
             const size_t row = (((size_t)k.layer * p.T.B + b) * p.T.nkv + g) * (size_t)p.T.C + (size_t)ch.P;
-            const __amdgpu_buffer_rsrc_t kr = dev_rsrc(S.args.kc + row * D, D * 2);
-            const __amdgpu_buffer_rsrc_t vr = dev_rsrc(S.args.vc + row * D, D * 2);
+            const __amdgpu_buffer_rsrc_t kr = dev_rsrc(uni_ptr(S.args.kc) + row * D, D * 2);
+            const __amdgpu_buffer_rsrc_t vr = dev_rsrc(uni_ptr(S.args.vc) + row * D, D * 2);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const uint32_t wk = __float_as_uint(ldb_dev(kr, cl * 16 + i * 4));
@@ -1713,8 +1724,8 @@ __device__ __noinline__ bool op_attn_mfma(const Params* pp, uint32_t slot_, uint
         qd = ldb_dev(qr, (wave * D + lane) * 4);
         if (has_cur) {
             const size_t row = (((size_t)k.layer * p.T.B + b) * p.T.nkv + g) * (size_t)p.T.C + (size_t)ch.P;
-            const uint32_t wk = __float_as_uint(ldb_dev(dev_rsrc(S.args.kc + row * D, D * 2), (lane / 2) * 4));
-            const uint32_t wv = __float_as_uint(ldb_dev(dev_rsrc(S.args.vc + row * D, D * 2), (lane / 2) * 4));
+            const uint32_t wk = __float_as_uint(ldb_dev(dev_rsrc(uni_ptr(S.args.kc) + row * D, D * 2), (lane / 2) * 4));
+            const uint32_t wv = __float_as_uint(ldb_dev(dev_rsrc(uni_ptr(S.args.vc) + row * D, D * 2), (lane / 2) * 4));
             kcur = (lane & 1) ? bf16hi(wk) : bf16lo(wk);
             vcur = (lane & 1) ? bf16hi(wv) : bf16lo(wv);
         }
@@ -2343,7 +2354,8 @@ __device__ __noinline__ bool op_gemv_b(const Params* pp, uint32_t slot_, uint32_
             const int i = idx % (int)k.nrows, b = idx / (int)k.nrows, row = (int)k.row0 + i;
             const int rsrc_i = k.op == OP_DOWN ? 2 * l : (l == 0 ? -1 : 2 * l - 1);
             res[q] = rsrc_i < 0 ? bf16f(gld((const uint16_t*)(p.w + p.lay.embed) + (size_t)S.tok[gb0 + b] * h + row))
-                                : ldb_dev(dev_rsrc(acc_buf(p, c.parity, rsrc_i, gb0 + b) + row, 4), 0);
+                                : ldb_dev(dev_rsrc(acc_buf(p, c.parity, rsrc_i, gb0), (uint32_t)(B * h) * 4u),
+                                          (uint32_t)(b * h + row) * 4u);
         }
     }
     // the tile's rows in chunks of whole row groups whose results fit the slices
@@ -2373,7 +2385,8 @@ __device__ __noinline__ bool op_gemv_b(const Params* pp, uint32_t slot_, uint32_
             for (int q = 0; q < MAX_TILE_ROWS / (NCW * 64); ++q) {
                 const int idx = tid + q * NCW * 64, i = idx / B, b = idx % B;
                 res[q] = i < nr && S.rtop[b]
-                             ? ldb_dev(dev_rsrc(acc_buf(p, c.parity, 2 * l, gb0 + b) + k.row0 + c0 + i, 4), 0)
+                             ? ldb_dev(dev_rsrc(acc_buf(p, c.parity, 2 * l, gb0), (uint32_t)(B * h) * 4u),
+                                       (uint32_t)(b * h + (int)k.row0 + c0 + i) * 4u)
                              : 0.f;
             }
         }
@@ -2463,8 +2476,8 @@ __device__ __noinline__ bool op_gemv_b(const Params* pp, uint32_t slot_, uint32_
                 const int g = is_k ? (int)slot - nq : (int)slot - nq - nkv;
                 uint16_t* base = (is_k ? S.args.kc : S.args.vc) +
                                  (((size_t)l * Btot + gb0 + b) * nkv + g) * (size_t)p.T.C * D + (size_t)Pb * D;
-                st16_dev(base, (uint32_t)j, f2bf16(lo));
-                st16_dev(base, (uint32_t)(j + half), f2bf16(hi));
+                st16_dev(base + j, f2bf16(lo));
+                st16_dev(base + j + half, f2bf16(hi));
             }
         }
     } else if (k.op == OP_ROUTE) {  // router logits of experts row0 .. row0 + nrows - 1

@@ -36,7 +36,7 @@ constexpr int halves_chunk_rows(int B) { return (MAX_TILE_ROWS / (B < GROUP_SEQS
 constexpr bool halves_packed(bool batched, int op, int kt) { return batched && kt == 2048 && (op == OP_QKV || op == OP_GATEUP); }
 
 // The several-sequence path (batched GEMV tiles over column groups of sequences,
-// fixed-length attention chunk slots merged by the last chunk, operand regions) runs
+// attention chunk slots dealt per step and merged by the last chunk, operand regions) runs
 // every step of more than one sequence and every mixture-of-experts step: expert
 // routing is implemented there only, so one sequence with experts is a column group
 // of one.

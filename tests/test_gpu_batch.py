@@ -1,6 +1,7 @@
 """GPU parity of the megakernel with several sequences per step (matrix-core projections
-over all sequences, fixed-length split-KV attention chunks merged by the last chunk of each
-sequence and KV group) against the oracle, through the C ABI."""
+over all sequences, split-KV attention chunk slots dealt per step in proportion to the
+contexts and merged by the last chunk of each sequence and KV group) against the oracle,
+through the C ABI."""
 import numpy as np
 import pytest
 import torch
@@ -88,14 +89,14 @@ def test_tiny_batch_of_three_on_four_workgroups():
 
 @pytest.mark.parametrize("splits", [3, 7])
 def test_tiny_batch_attention_chunk_slots(splits):
-    # fixed-length chunk slots of ceil(512 / splits) positions: short contexts leave
-    # empty slots, long ones fill several; the last partial of each (sequence, group)
-    # merges the non-empty ones
+    # 5 x splits slots per group dealt by context (position 0: one chunk of one
+    # position; 511: most slots), some left empty; the last partial of each (sequence,
+    # group) merges that sequence's chunks
     _one_step(TINY, 5, 512, [0, 72, 73, 300, 511], attn_splits=splits)
 
 
 def test_tiny_batch_merge_after_every_chunk_repeated():
-    # sequences with 5 and 7 chunk slots among ones with a single slot: the merge of a
+    # the deal gives the sequences 1, 2, 2, 5 and 8 one-page chunks (35 slots): the merge of a
     # (sequence, group) must see every chunk's partials, and the O-projection every
     # merge, in every run (waves that have no work in a task must not run ahead)
     cfg, B, C = TINY, 5, 512

@@ -144,7 +144,7 @@ def _fixture_equals(path, g, n_tasks):
 
 
 def test_oracle_builder_matches_hand_derived_batch_graph():
-    """Three sequences with four fixed-length chunk slots: slot order 0, 1, 3, 2 outermost, then sequences;
+    """Three sequences with four chunk slots each (dealt at run time): slot order 0, 1, 3, 2 outermost, then sequences;
     one event per KV group counting every slot task of every sequence (the O-projection waits for all of
     them, the run-time merge included); GEMV tiles of the single column group."""
     g = tg.build(TOY, 3, 64, 2, attn_splits=4)
