@@ -32,7 +32,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode µs/step (steps/s) at batch 1, Llama-1B shape; achieved HBM GB/s vs peak"
 HBM_PEAK_GBS = 8000.0
-SCHEDS = {"static": 0, "dynamic": 1, "event": 2}
+SCHEDS = {"static": 0, "dynamic": 1, "event": 2, "scheduler": 3}
 
 
 def step_bytes(cfg, positions):
@@ -511,7 +511,8 @@ def main():
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--sched", choices=list(SCHEDS), default="static",
-                    help="static per-CU queues, dynamic global queue, or event-driven ready queue")
+                    help="static per-CU queues, dynamic global queue, event-driven ready queue filled by the "
+                         "activating workers, or filled by scheduler waves from activated-event queues")
     ap.add_argument("--policy", choices=["rr", "lpt"], default="rr")
     ap.add_argument("--attn-splits", type=int, default=0)
     ap.add_argument("--cooperative", action="store_true", help="cooperative launch instead of the default plain one")

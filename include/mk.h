@@ -75,7 +75,12 @@ typedef struct {
 typedef struct {
     int32_t sched;             /* 0 static per-CU queues (default), 1 dynamic global queue (atomic pop),
                                 * 2 event-driven: tasks taken from a global ready queue in the order their
-                                * events activated them (MPK news page, part 2); every event one counter */
+                                * events activated them, the activating worker appending the dependents;
+                                * 3 event-driven with scheduler waves: the activating worker posts the event
+                                * to the activated-event queue of workgroup (event mod workgroups), whose
+                                * second loader wave dispatches its dependents to the ready queue (MPK news
+                                * page, part 2: scheduler units with activated-event queues); 2 and 3 keep
+                                * one counter per event */
     int32_t n_workgroups;      /* persistent workgroups; 0 = one per CU of the device */
     int32_t policy;            /* static assignment: 0 round-robin, 1 least-loaded (bytes) first */
     int32_t attn_splits;       /* KV chunks per (sequence, KV head), at most 16; 0 = automatic */

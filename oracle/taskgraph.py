@@ -269,7 +269,7 @@ def build(cfg, B, C, W, policy=0, attn_splits=0, sched=0):
                  wbytes=_round16(rows) * h * 2, wofs=lay["lm"] + i * t["lm_rows"] * h * 2)
     # events with many producers spread their counts over 8 sub-counters, except under
     # event-driven dispatch, where one counter per event tells its last producer
-    nsub = [8 if n > 32 and sched != 2 else 1 for n in target]
+    nsub = [8 if n > 32 and sched < 2 else 1 for n in target]
     for k in tasks:
         k["wait_target"] = target[k["wait_ev"]] if k["wait_ev"] != NONE else 0
         k["wait_nsub"] = nsub[k["wait_ev"]] if k["wait_ev"] != NONE else 1
@@ -489,8 +489,12 @@ def ancestor_sets(g):
     return lambda i: memo[tasks[i]["wait_ev"]] if tasks[i]["wait_ev"] != NONE else frozenset()
 
 
-def simulate(g, W, seed=0, slow=None, dynamic=False, lookahead=2, event=False):
+def simulate(g, W, seed=0, slow=None, dynamic=False, lookahead=2, event=False, scheduler=False):
     """Runs the graph on W virtual workgroups under a seeded random interleaving.
+
+    scheduler (implies event): an activated event is not dispatched at once but
+    posted to the queue of scheduler ev % W, which dispatches its events in id
+    order, each once it has been activated (one more kind of move).
 
     Static: each workgroup runs its queue in order.  Dynamic: a workgroup claims
     the next task of the global order whenever it holds fewer than `lookahead`
@@ -508,6 +512,9 @@ def simulate(g, W, seed=0, slow=None, dynamic=False, lookahead=2, event=False):
     E = g["tiling"].get("E", 0)
     ctr = [0] * len(g["target"])
     n = len(tasks)
+    n_ev = len(g["target"])
+    event = event or scheduler
+    next_ev = list(range(W))  # each scheduler's next event: w, w + W, ...
     if event:
         dynamic = True
         rq = list(g["init"])  # the ready queue: filled slots
@@ -547,6 +554,8 @@ def simulate(g, W, seed=0, slow=None, dynamic=False, lookahead=2, event=False):
                     moves.append((w, "run"))
             if dynamic and len(held[w]) < lookahead and nxt < n:
                 moves.append((w, "claim"))
+            if scheduler and next_ev[w] < n_ev and ctr[next_ev[w]] >= g["target"][next_ev[w]]:
+                moves.append((w, "dispatch"))
         if not moves:
             break
         if slow is not None:
@@ -558,6 +567,10 @@ def simulate(g, W, seed=0, slow=None, dynamic=False, lookahead=2, event=False):
             held[w].append(nxt if event else order[nxt])
             nxt += 1
             continue
+        if what == "dispatch":
+            rq.extend(cons[next_ev[w]])
+            next_ev[w] += W
+            continue
         if dynamic:
             s = held[w].pop(0)
             i = rq[s] if event else s
@@ -567,7 +580,7 @@ def simulate(g, W, seed=0, slow=None, dynamic=False, lookahead=2, event=False):
         k = tasks[i]
         for ev in signals(k, E):
             ctr[ev] += 1
-            if event and ctr[ev] == g["target"][ev]:
+            if event and not scheduler and ctr[ev] == g["target"][ev]:
                 rq.extend(cons[ev])
         done += 1
     return done

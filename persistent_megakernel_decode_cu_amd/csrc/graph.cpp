@@ -18,11 +18,12 @@
 // Event-driven dispatch follows the MPK runtime (MPK news page, part 2: a task
 // completes by counting its event; the event is activated when the count reaches
 // its threshold, and the scheduling unit then launches every task that depends on
-// it).  Here the task whose count activates an event appends the event's
-// dependents to one global ready queue, and workgroups take tasks from that queue
-// in the order they became ready.  The builder lists each event's dependents and
-// the tasks that depend on nothing; every event has one counter (the count that
-// activates it has to be seen by one producer).
+// it).  Here (sched 2) the task whose count activates an event appends the event's
+// dependents to one global ready queue, or (sched 3) posts the event to the
+// activated-event queue of one workgroup, whose scheduler wave appends them; either
+// way workgroups take tasks from that queue in the order they became ready.  The
+// builder lists each event's dependents and the tasks that depend on nothing; every
+// event has one counter (the count that activates it has to be seen by one producer).
 #include "graph.h"
 
 #include <algorithm>
@@ -390,7 +391,7 @@ int build_graph(const Tiling& T, const Layout& Ly, int sched, int policy, Graph*
     }
     // sub-counters: events with many producers spread their increments over 8 counters
     // (event-driven dispatch: one counter per event)
-    for (size_t e = 0; e < g.target.size(); ++e) g.nsub[e] = sched != 2 && g.target[e] > 32 ? 8 : 1;
+    for (size_t e = 0; e < g.target.size(); ++e) g.nsub[e] = sched < 2 && g.target[e] > 32 ? 8 : 1;
     // dependents of every event, and the tasks that wait on none
     g.cons_off.assign(g.target.size() + 1, 0);
     g.cons.clear();

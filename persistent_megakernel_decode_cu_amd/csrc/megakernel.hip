@@ -591,6 +591,68 @@ __device__ __noinline__ void launch_dependents(const Params* pp, uint32_t ev, ui
     vm_wait_all();
 }
 
+// Scheduler waves (sched 3; MPK news page, part 2: scheduler units with activated-event
+// queues that hand the dependents of each activated event to the workers).  The worker
+// whose count activates an event posts it (stamps it with the step); event ev sits in the
+// activated-event queue of workgroup ev % W, whose second loader wave is that queue's
+// scheduler: it takes its events in id order (a topological order) and launches each
+// one's dependents into the ready queue the workers pop.  It serves its queue while it
+// waits for its next task and, after its last one, until every event of its queue has
+// been dispatched.
+//
+// One pass over the queue without blocking: dispatch the events that have been posted,
+// in order, up to the first that has not.
+__device__ __forceinline__ void serve_events(const Params* pp, uint32_t epoch, int lane, uint32_t& next_ev) {
+    CParams& p = P(pp);
+    while (next_ev < p.n_events && uni(ld_dev(&p.aeq_stamp[next_ev])) == epoch) {
+        acquire_fence();
+        launch_dependents(pp, next_ev, epoch, lane);
+        next_ev += gridDim.x;
+    }
+}
+// Serve the queue until the LDS word w reaches v (the next task handed over), bounded in time.
+__device__ __noinline__ bool serve_until(const Params* pp, uint32_t epoch, int lane, uint32_t& next_ev,
+                                         const uint32_t& w, uint32_t v) {
+    CParams& p = P(pp);
+    const uint64_t t0 = rtc();
+    for (uint32_t it = 1;; ++it) {
+        if (uni(lds_ld(w)) >= v) return true;
+        serve_events(pp, epoch, lane, next_ev);
+        if (lds_ld(S.abort)) return false;
+        if ((it & 63u) == 0u) {
+            if (ld_dev(&p.state[ST_ABORT])) {
+                lds_st(S.abort, 1u);
+                return false;
+            }
+            if (rtc() - t0 > 2 * p.timeout) {
+                raise_error(pp, ERR_TIMEOUT_LDS, NONE, NONE, lds_ld(w), v);
+                return false;
+            }
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+// After the scheduler's last task: dispatch the rest of its queue, bounded in time.
+__device__ __noinline__ void serve_rest(const Params* pp, uint32_t epoch, int lane, uint32_t& next_ev) {
+    CParams& p = P(pp);
+    const uint64_t t0 = rtc();
+    for (uint32_t it = 1; next_ev < p.n_events; ++it) {
+        serve_events(pp, epoch, lane, next_ev);
+        if (next_ev >= p.n_events || lds_ld(S.abort)) return;
+        if ((it & 63u) == 0u) {
+            if (ld_dev(&p.state[ST_ABORT])) {
+                lds_st(S.abort, 1u);
+                return;
+            }
+            if (rtc() - t0 > p.timeout) {
+                raise_error(pp, ERR_TIMEOUT_EVENT, NONE, next_ev, 0, epoch);
+                return;
+            }
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
 typedef const __attribute__((address_space(4))) uint32_t c_u32;
 typedef const __attribute__((address_space(4))) Task c_task;
 
@@ -620,6 +682,7 @@ __device__ __noinline__ void loader(const Params* pp, uint32_t epoch, int lw) {
     }
     uint32_t pseq = 0, pub = 0;  // next page to issue / to publish
     const bool tr = lw == 0 && uni(lds_ld(S.trace_on)) != 0;
+    uint32_t next_ev = blockIdx.x;  // scheduler waves: the next event of this workgroup's queue
 
     auto publish_one = [&]() {
         if (lane == 0) lds_st(S.page_ready[lw][pub % NPAGES], pub / NPAGES + 1);
@@ -645,7 +708,7 @@ __device__ __noinline__ void loader(const Params* pp, uint32_t epoch, int lw) {
             const uint32_t rel = old - (epoch - 1u) * (n_tasks + W);
             end = rel >= n_tasks;
             ti = end ? NONE : rel;
-            if (sched == 2 && !end) {
+            if (sched >= 2 && !end) {
                 // event-driven: slot rel of the ready queue, once a completed event has filled it
                 if (rel >= p.n_init && !wait_ready_slot(pp, rel, epoch)) break;
                 ti = uni(ld_dev(&p.rq[rel]));
@@ -660,7 +723,11 @@ __device__ __noinline__ void loader(const Params* pp, uint32_t epoch, int lw) {
         } else {
             if (lds_ld(S.dyn_ready) < t + 1) {
                 drain();
-                if (!uni(lds_wait_ge(S.dyn_ready, t + 1, pp, NONE))) break;
+                if (sched == 3) {
+                    if (!uni(serve_until(pp, epoch, lane, next_ev, S.dyn_ready, t + 1))) break;
+                } else if (!uni(lds_wait_ge(S.dyn_ready, t + 1, pp, NONE))) {
+                    break;
+                }
             }
             ti = uni(lds_ld(S.dyn_tid[t % DYNQ]));
             lgkm_wait_all();
@@ -746,6 +813,7 @@ __device__ __noinline__ void loader(const Params* pp, uint32_t epoch, int lw) {
     }
 out:
     drain();
+    if (sched == 3 && lw == 1) serve_rest(pp, epoch, lane, next_ev);
 }
 
 // ---- compute-wave primitives -------------------------------------------------------
@@ -2654,7 +2722,7 @@ __device__ __noinline__ void compute(const Params* pp, uint32_t epoch, int wave)
                 const uint32_t sub = k.sig_nsub == 8 ? xcc_id() : 0u;
                 const uint32_t old = addu_dev(&ctr[ctr_index(ev, sub)], 1u);
                 // event-driven dispatch: the count that reaches the event's threshold activates it
-                activated = sched == 2 && old + 1u == epoch * p.ev_target[ev];
+                activated = sched >= 2 && old + 1u == epoch * p.ev_target[ev];
             }
             if (sched == 2) {
                 uint64_t act = __ballot(activated);
@@ -2663,6 +2731,9 @@ __device__ __noinline__ void compute(const Params* pp, uint32_t epoch, int wave)
                     act &= act - 1;
                     launch_dependents(pp, k.sig_ev + (uint32_t)l, epoch, c.lane);
                 }
+            } else if (sched == 3 && activated) {
+                // post the event to its scheduler's activated-event queue
+                st_dev(&p.aeq_stamp[k.sig_ev + (uint32_t)c.lane], epoch);
             }
             if (k.op == OP_LMHEAD) finish_step(pp, epoch, c.parity);
             if (task_count && c.lane == 0) addu_dev(&task_count[k.id], 1u);

@@ -81,7 +81,7 @@ mk_status plan(const mk_model_desc* desc, int32_t batch, int32_t max_ctx, const 
     mk_options o;
     memset(&o, 0, sizeof(o));
     if (opt) o = *opt;
-    if (o.sched < 0 || o.sched > 2 || o.policy < 0 || o.policy > 1) return MK_E_INVALID;
+    if (o.sched < 0 || o.sched > 3 || o.policy < 0 || o.policy > 1) return MK_E_INVALID;
     if (o.page_kib != 0 && o.page_kib != 16) return MK_E_INVALID;  // the page size is part of the weight layout
     if (o.poison < 0 || o.poison > 1) return MK_E_INVALID;
     PlanOptions po;
@@ -225,6 +225,7 @@ mk_status rearm(mk_handle* h) {
     HIPCHK(hipMemset(p.acc, 0, h->acc_bytes));
     if (p.aticket) HIPCHK(hipMemset(p.aticket, 0, (size_t)2 * T.L * T.B * T.nkv * 4));
     if (p.rq_stamp) HIPCHK(hipMemset(p.rq_stamp, 0, h->g.tasks.size() * 4));
+    if (p.aeq_stamp) HIPCHK(hipMemset(p.aeq_stamp, 0, h->n_events * 4));
     HIPCHK(hipMemset(p.key, 0, sizeof(unsigned long long) * 2 * T.B));
     HIPCHK(hipMemset(p.ticket, 0, 4 * T.B));
     HIPCHK(hipDeviceSynchronize());
@@ -318,6 +319,7 @@ mk_status mk_build_graph(const mk_model_desc* desc, int32_t batch, int32_t max_c
     const double ms = o.debug_timeout_ms > 0 ? o.debug_timeout_ms : 2000.0;
     p.timeout = (unsigned long long)(ms * 1e5);  // 100 MHz clock
     h->n_events = h->g.target.size();
+    p.n_events = (uint32_t)h->n_events;
 #define ALLOC(ptr, bytes, zero)                                   \
     do {                                                          \
         mk_status s_ = dalloc(h, &(ptr), (bytes), (zero));        \
@@ -344,13 +346,14 @@ mk_status mk_build_graph(const mk_model_desc* desc, int32_t batch, int32_t max_c
     p.queue_off = qo;
     p.queue = qq;
     ALLOC(p.ctr, h->n_events * 8 * 32 * 4, true);
-    if (o.sched == 2) {
+    if (o.sched >= 2) {
         uint32_t *evt, *co, *cs, *rq;
         ALLOC(evt, h->n_events * 4, false);
         ALLOC(co, h->g.cons_off.size() * 4, false);
         ALLOC(cs, std::max<size_t>(1, h->g.cons.size()) * 4, false);
         ALLOC(rq, h->g.tasks.size() * 4, true);
         ALLOC(p.rq_stamp, h->g.tasks.size() * 4, true);
+        if (o.sched == 3) ALLOC(p.aeq_stamp, h->n_events * 4, true);
         p.ev_target = evt;
         p.cons_off = co;
         p.cons = cs;
@@ -434,7 +437,8 @@ mk_status mk_build_graph(const mk_model_desc* desc, int32_t batch, int32_t max_c
         const size_t o_at = batched_path(T.B, T.E) ? take((size_t)2 * T.L * T.B * T.nkv * 4) : 0;
         const size_t o_rl = T.E ? take((size_t)T.L * T.B * T.E * 4) : 0;
         const size_t o_key = take(sizeof(unsigned long long) * 2 * T.B), o_ticket = take(4 * (size_t)T.B);
-        const size_t o_rqs = o.sched == 2 ? take(h->g.tasks.size() * 4) : 0;
+        const size_t o_rqs = o.sched >= 2 ? take(h->g.tasks.size() * 4) : 0;
+        const size_t o_aeq = o.sched == 3 ? take(h->n_events * 4) : 0;
         h->na_bytes = at;
         if (at <= NOALLOC_SCRATCH_BYTES) {
             uint8_t* base = nullptr;
@@ -455,7 +459,8 @@ mk_status mk_build_graph(const mk_model_desc* desc, int32_t batch, int32_t max_c
             q.rlogit = T.E ? (float*)(base + o_rl) : nullptr;
             q.key = (unsigned long long*)(base + o_key);
             q.ticket = (uint32_t*)(base + o_ticket);
-            q.rq_stamp = o.sched == 2 ? (uint32_t*)(base + o_rqs) : nullptr;
+            q.rq_stamp = o.sched >= 2 ? (uint32_t*)(base + o_rqs) : nullptr;
+            q.aeq_stamp = o.sched == 3 ? (uint32_t*)(base + o_aeq) : nullptr;
             h->p_na = q;
             Params* dq;
             ALLOC2(dq, sizeof(Params));
@@ -519,8 +524,13 @@ mk_status mk_decode_step_noalloc(mk_handle* h, const int32_t* tokens, const int3
     // at zero and start the step at epoch 1 (parity 1), with a fill kernel (no memset, no allocation).
     PoisonSpans cs;
     memset(&cs, 0, sizeof(cs));
+    bool too_many = false;  // (more spans than the fill kernel takes: a build error, never expected)
     auto span = [&](void* ptr, size_t bytes, uint32_t pattern) {
         if (!ptr || !bytes) return;
+        if (cs.n >= MAX_SPANS) {
+            too_many = true;
+            return;
+        }
         cs.ptr[cs.n] = ptr;
         cs.words[cs.n] = bytes / 4;
         cs.pattern[cs.n] = pattern;
@@ -535,6 +545,8 @@ mk_status mk_decode_step_noalloc(mk_handle* h, const int32_t* tokens, const int3
     span(p.ticket, (size_t)T.B * 4, 0u);
     span(p.aticket ? p.aticket + nat : nullptr, nat * 4, 0u);
     span(p.rq_stamp, h->g.tasks.size() * 4, 0u);
+    span(p.aeq_stamp, h->n_events * 4, 0u);
+    if (too_many) return MK_E_INVALID;
     hipError_t e = launch_poison(cs, (hipStream_t)stream);
     if (e != hipSuccess) return MK_E_HIP;
     if (h->poison) {
@@ -562,7 +574,7 @@ mk_status enqueue_poison(mk_handle* h, const Params& p, float* logits, hipStream
         PoisonSpans ps;
         memset(&ps, 0, sizeof(ps));
         auto span = [&](void* ptr, size_t bytes, uint32_t pattern) {
-            if (!ptr || !bytes) return;
+            if (!ptr || !bytes || ps.n >= MAX_SPANS) return;  // (8 spans at most are named below)
             ps.ptr[ps.n] = ptr;
             ps.words[ps.n] = bytes / 4;
             ps.pattern[ps.n] = pattern;

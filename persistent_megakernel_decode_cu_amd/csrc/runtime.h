@@ -39,7 +39,8 @@ struct Params {
     const uint32_t* queue_off;
     const uint32_t* queue;
     uint32_t n_tasks;
-    uint32_t sched;           // 0 static queues, 1 dynamic (atomic pop), 2 event-driven
+    uint32_t sched;           // 0 static queues, 1 dynamic (atomic pop), 2 event-driven, 3 event-driven
+                              // with scheduler waves
     // event-driven dispatch: producers per event, each event's dependents (CSR), the ready
     // queue [n_tasks] (the first n_init slots: the tasks that wait on no event, written once)
     // and the step that filled each of its slots
@@ -49,6 +50,10 @@ struct Params {
     uint32_t* rq;
     uint32_t* rq_stamp;
     uint32_t n_init;
+    // scheduler waves (sched 3): the step that activated each event [n_events]; event ev
+    // is in the activated-event queue of workgroup ev % W, which dispatches it
+    uint32_t* aeq_stamp;
+    uint32_t n_events;
     uint32_t* ctr;            // event counters [n_events][8 sub-counters][32 words]
     uint32_t* state;          // control words
     const uint8_t* w;         // packed weights
@@ -102,11 +107,13 @@ hipError_t launch_repack_tiles(const TileOp* ops, uint32_t n_ops, const uint8_t*
 
 hipError_t launch_step(const Params* dparams, const StepArgs& a, uint32_t grid, hipStream_t stream, bool cooperative);
 
-// Poison mode: up to 8 spans of 32-bit words filled with a pattern before a step.
+// Fill spans (poison mode, and the allocation-free step's clears): up to MAX_SPANS spans of
+// 32-bit words, each filled with a pattern before a step.
+constexpr int MAX_SPANS = 12;
 struct PoisonSpans {
-    void* ptr[8];
-    uint64_t words[8];
-    uint32_t pattern[8];
+    void* ptr[MAX_SPANS];
+    uint64_t words[MAX_SPANS];
+    uint32_t pattern[MAX_SPANS];
     int32_t n;
 };
 hipError_t launch_poison(const PoisonSpans& s, hipStream_t stream);

@@ -116,7 +116,7 @@ def test_tiny_batch_merge_after_every_chunk_repeated():
         assert res["hidden_rel"] <= TOL_HIDDEN_REL and res["max_dlogit"] <= TOL_LOGIT_ABS, rep
 
 
-@pytest.mark.parametrize("sched", [1, 2], ids=["dynamic", "event"])
+@pytest.mark.parametrize("sched", [1, 2, 3], ids=["dynamic", "event", "scheduler"])
 def test_tiny_batch_dynamic_queue(sched):
     _one_step(TINY, 5, 512, synth.make_positions(5, 100, 511), sched=sched)
 
@@ -177,7 +177,7 @@ def llama1b_b16():
     return w, kc, vc, tok, pos, ref
 
 
-@pytest.mark.parametrize("sched", [0, 1, 2])
+@pytest.mark.parametrize("sched", [0, 1, 2, 3])
 def test_llama1b_batch16_first_step(llama1b_b16, sched):
     w, kc, vc, tok, pos, ref = llama1b_b16
     print(f"case llama1b B=16 first step sched={sched}", flush=True)

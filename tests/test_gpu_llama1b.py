@@ -42,7 +42,7 @@ def _greedy(run, tok, P0, steps):
     return out.cpu().numpy()
 
 
-@pytest.mark.parametrize("sched,coop", [(0, 0), (1, 0), (0, 1), (2, 0)])
+@pytest.mark.parametrize("sched,coop", [(0, 0), (1, 0), (0, 1), (2, 0), (3, 0)])
 def test_llama1b_first_step(inputs, sched, coop):
     g, w, kc, vc, tok = inputs
     P0 = g["first_position"]

@@ -98,10 +98,11 @@ def test_tiny_greedy_chain_and_counters():
     assert got == ref["tokens"][:, 0].tolist(), (got, ref["tokens"][:, 0].tolist(), ref["gaps"][:, 0])
 
 
-@pytest.mark.parametrize("sched", [1, 2], ids=["dynamic", "event"])
+@pytest.mark.parametrize("sched", [1, 2, 3], ids=["dynamic", "event", "scheduler"])
 def test_tiny_dynamic_queue_greedy(sched):
     """Greedy chain with tasks taken from one global queue: in task order (1) or in the order their
-    events activated them (2, event-driven dispatch); every task runs once per step, counters = k x target."""
+    events activated them (2: the activating worker appends the dependents; 3: scheduler waves append
+    them from activated-event queues); every task runs once per step, counters = k x target."""
     cfg = synth.configs.TINY
     C, P0, steps = 512, 100, 16
     w, kc, vc, tok, pos = _setup(cfg, C, P0)
@@ -126,9 +127,10 @@ def test_tiny_dynamic_queue_greedy(sched):
     assert got == ref["tokens"][:, 0].tolist()
 
 
+@pytest.mark.parametrize("sched", [2, 3], ids=["event", "scheduler"])
 @pytest.mark.parametrize("W", [1, 5, 37])
-def test_tiny_event_driven_few_workgroups(W):
-    ref, res, orig, refkv, gkv = _one_step(synth.configs.TINY, 512, 300, sched=2, n_workgroups=W)
+def test_tiny_event_driven_few_workgroups(W, sched):
+    ref, res, orig, refkv, gkv = _one_step(synth.configs.TINY, 512, 300, sched=sched, n_workgroups=W)
     print(res)
     assert res["hidden_rel"] <= TOL_HIDDEN_REL and res["max_dlogit"] <= TOL_LOGIT_ABS and res["argmax_equal"]
     _check_kv(orig, refkv, gkv, 300)

@@ -86,7 +86,7 @@ def test_tiny_moe_few_workgroups(W):
     _one_step(TINY_MOE, 3, 256, [7, 100, 255], n_workgroups=W)
 
 
-@pytest.mark.parametrize("sched", [1, 2], ids=["dynamic", "event"])
+@pytest.mark.parametrize("sched", [1, 2, 3], ids=["dynamic", "event", "scheduler"])
 def test_tiny_moe_dynamic_queue(sched):
     _one_step(TINY_MOE, 4, 512, [50, 300, 11, 499], sched=sched)
 

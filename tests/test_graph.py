@@ -185,6 +185,8 @@ CASES = [
     (synth.configs.LLAMA_8B, 256, 4096, 0, 0, 0),
     (synth.configs.TINY, 4, 512, 2, 0, 0),
     (synth.configs.LLAMA_1B, 256, 2048, 2, 0, 0),
+    (synth.configs.TINY, 4, 512, 3, 0, 0),
+    (synth.configs.LLAMA_1B, 256, 2048, 3, 0, 0),
 ]
 
 
@@ -288,7 +290,7 @@ def test_options_zero_filled_is_the_default_and_bad_values_are_refused():
     assert lib.mk_plan_graph(model.desc, 1, 512, None, 4, buf, need.value, ctypes.byref(need)) == mk.MK_OK
     assert _plan_with(cfg, 4, mk.Options()) == buf.raw
     assert _plan_with(cfg, 4, mk.options(page_kib=16)) == buf.raw
-    for bad in (mk.options(page_kib=8), mk.options(page_kib=32), mk.options(poison=2), mk.options(sched=3)):
+    for bad in (mk.options(page_kib=8), mk.options(page_kib=32), mk.options(poison=2), mk.options(sched=4)):
         with pytest.raises(mk.MkError) as ei:
             _plan_with(cfg, 4, bad)
         assert ei.value.status == mk.MK_E_INVALID
@@ -410,7 +412,10 @@ def test_event_driven_dispatch_completes(cfg, B, W):
     assert all(n_ == 1 for n_ in g["nsub"])
     for seed in range(3):
         assert tg.simulate(g, W, seed=seed, event=True) == n
+        # scheduler waves: events posted to scheduler ev % W, dispatched in id order
+        assert tg.simulate(g, W, seed=seed, scheduler=True) == n
     assert tg.simulate(g, W, seed=7, event=True, slow=0) == n
+    assert tg.simulate(g, W, seed=7, scheduler=True, slow=0) == n
     # an event whose count never completes (one producer's signal lost) stalls its dependents
     k = next(k for k in g["tasks"] if k["op"] == tg.OP_QKV and k["layer"] == 1)
     k["sig_ev"] = tg.NONE
