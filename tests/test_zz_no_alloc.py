@@ -93,6 +93,27 @@ def test_noalloc_equals_the_ordinary_step_two_calls_in_a_row_second_smaller():
     small.run.close()
 
 
+@pytest.mark.parametrize("sched", [2, 3], ids=["event", "scheduler"])
+def test_noalloc_event_driven_two_calls_in_a_row(sched):
+    """Event-driven dispatch (the ready queue's step stamps, and with scheduler waves the activated-event
+    stamps, live in the static scratch and are cleared by each call): five sequences, then one."""
+    pos5 = synth.make_positions(5, 0, 511)
+    big = Case(TINY, 5, 512, pos5, sched=sched)
+    small = Case(TINY, 1, 512, [300], sched=sched)
+    print(f"case tiny B=5 then B=1, sched {sched}", flush=True)
+    big.step(False)
+    ref_big = big.outputs(False)
+    small.step(False)
+    ref_small = small.outputs(False)
+    big.step(True)
+    small.step(True)
+    torch.cuda.synchronize()
+    _same(ref_small, small.outputs(True), small.run.kv, small.kv_na, small.shape)
+    _same(ref_big, big.outputs(True), big.run.kv, big.kv_na, big.shape)
+    big.run.close()
+    small.run.close()
+
+
 def test_noalloc_llama1b_and_a_greedy_chain():
     case = Case(LLAMA_1B, 1, 2048, [1024])
     print("case 1B B=1: ordinary then allocation-free, 3 chained steps each", flush=True)
