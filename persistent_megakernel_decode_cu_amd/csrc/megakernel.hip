@@ -183,7 +183,8 @@ __device__ __forceinline__ void vm_wait_all() { asm volatile("s_waitcnt vmcnt(0)
 // Cross-check build of the synchronisation protocol (-DMK_FENCED=1): agent-scope release fences before
 // every signal (counter, ticket or ready-queue stamp) and agent-scope acquire fences after every wait
 // that a signal ends, as the memory model's generic sequences would have them.  The default build
-// issues none (every cross-CU datum already goes through device-scope accesses; see the design notes).
+// issues none: every datum read across CUs is written and read with device-scope (sc1) accesses, and a
+// producer waits for its stores to be acknowledged before it signals.
 #ifndef MK_FENCED
 #define MK_FENCED 0
 #endif
