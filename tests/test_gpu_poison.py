@@ -55,7 +55,7 @@ def test_poison_tiny_one_sequence():
     _poisoned_step(TINY, 1, 512, [128])
 
 
-@pytest.mark.parametrize("sched", [0, 1])
+@pytest.mark.parametrize("sched", [0, 1, 2, 3], ids=["static", "dynamic", "event", "scheduler"])
 def test_poison_tiny_five_sequences(sched):
     pos = synth.make_positions(5, 0, 511)
     pos[0] = 0
@@ -67,8 +67,17 @@ def test_poison_tiny_moe():
     _poisoned_step(TINY_MOE, 5, 512, pos)
 
 
+def test_poison_tiny_moe_one_sequence():
+    _poisoned_step(TINY_MOE, 1, 512, [300])
+
+
 def test_poison_llama1b_one_sequence():
     _poisoned_step(LLAMA_1B, 1, 2048, [1024])
+
+
+def test_poison_llama1b_sixteen_sequences():
+    """The several-sequence path at scale under poison: dealt attention chunks, column-group operands."""
+    _poisoned_step(LLAMA_1B, 16, 4352, synth.make_positions(16, 256, 4096))
 
 
 def test_poison_tiny_greedy_chain():
