@@ -402,3 +402,79 @@ def test_page_arithmetic_fixtures():
     assert taskgraph.idle_units_in_last_wave(n_blocks, n_sms) == idle
     n_pages, page_kib, total = facts["paged_smem_pages_kib_bytes"]
     assert n_pages * page_kib * 1024 == total
+
+
+# ---- causal prefill (oracle/prefill.py) ----------------------------------------
+
+from oracle import prefill as oprefill  # noqa: E402
+
+
+def _prefill_case(cfg, T, pos0, C, gain_std=0.1, seed=0):
+    w = synth.make_weights(cfg, gain_std=gain_std)
+    kc, vc = synth.make_kv(cfg, 1, C)
+    toks = np.random.default_rng(seed).integers(0, cfg.vocab, T)
+    return w, kc, vc, toks
+
+
+@pytest.mark.parametrize("T,pos0", [(1, 0), (7, 0), (19, 33)])
+def test_prefill_equals_sequential_decode_steps(T, pos0):
+    # Causal prefill of T tokens is T decode steps over the same tokens (the C decode-step
+    # definition, pinned above against transformers): every K/V byte equal, every token's
+    # final residual and the last token's logits to rounding.
+    cfg = synth.configs.TINY
+    w, kc, vc, toks = _prefill_case(cfg, T, pos0, 64)
+    k1, v1 = kc.copy(), vc.copy()
+    r = oprefill.prefill(cfg, w, toks, pos0, k1, v1)
+    k2, v2 = kc.copy(), vc.copy()
+    for t in range(T):
+        s = oracle.decode_step(cfg, w, [int(toks[t])], [pos0 + t], k2, v2)
+        np.testing.assert_allclose(r["hidden"][t], s["hidden"][0], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(r["logits"], s["logits"][0], rtol=1e-10, atol=1e-12)
+    assert r["next"] == int(s["next"][0])
+    np.testing.assert_array_equal(k1, k2)
+    np.testing.assert_array_equal(v1, v2)
+    # slots outside pos0 .. pos0 + T - 1 untouched
+    mask = np.ones(64, bool)
+    mask[pos0:pos0 + T] = False
+    np.testing.assert_array_equal(k1[:, :, :, mask], kc[:, :, :, mask])
+
+
+def test_prefill_matches_transformers_llama_causal_forward():
+    # HF's Llama run over the whole prompt at once (its causal mask, its RoPE, its cache of
+    # the earlier context), unrounded K/V on both sides
+    from transformers.cache_utils import DynamicCache
+    cfg = synth.configs.TINY.with_(tied=False)
+    T, P, C = 12, 40, 64
+    w, kc, vc, toks = _prefill_case(cfg, T, P, C, gain_std=0.2, seed=3)
+    m = _hf_llama(cfg, w)
+    cache = DynamicCache()
+    for l in range(cfg.n_layers):
+        cache.update(torch.tensor(oracle.bf16_to_f64(kc[l, 0, :, :P]))[None],
+                     torch.tensor(oracle.bf16_to_f64(vc[l, 0, :, :P]))[None], l)
+    resid = {}
+    hk = m.model.layers[-1].register_forward_hook(
+        lambda mod, i, o: resid.__setitem__("x", o[0] if isinstance(o, tuple) else o))
+    with torch.no_grad():
+        out = m(input_ids=torch.tensor(toks)[None], position_ids=torch.arange(P, P + T)[None],
+                past_key_values=cache, use_cache=True, cache_position=torch.arange(P, P + T))
+    hk.remove()
+    r = oprefill.prefill(cfg, w, toks, P, kc.copy(), vc.copy(), kv_round=False)
+    ref_x = resid["x"][0].numpy()
+    np.testing.assert_allclose(r["hidden"], ref_x, rtol=0, atol=2e-6 * np.abs(ref_x).max())
+    ref_logits = out.logits[0, -1].numpy()
+    np.testing.assert_allclose(r["logits"], ref_logits, rtol=0, atol=2e-6 * np.abs(ref_logits).max())
+
+
+def test_prefill_chunks_compose():
+    # a prompt prefilled in two calls (the second continuing at pos0 = T1) equals one call
+    cfg = synth.configs.TINY
+    w, kc, vc, toks = _prefill_case(cfg, 23, 0, 32, seed=5)
+    k1, v1 = kc.copy(), vc.copy()
+    r = oprefill.prefill(cfg, w, toks, 0, k1, v1)
+    k2, v2 = kc.copy(), vc.copy()
+    oprefill.prefill(cfg, w, toks[:9], 0, k2, v2)
+    r2 = oprefill.prefill(cfg, w, toks[9:], 9, k2, v2)
+    np.testing.assert_array_equal(k1, k2)
+    np.testing.assert_array_equal(v1, v2)
+    np.testing.assert_allclose(r2["hidden"], r["hidden"][9:], rtol=1e-10, atol=1e-12)
+    assert r2["next"] == r["next"]
