@@ -133,6 +133,48 @@ mk_status mk_build_graph(const mk_model_desc *desc, int32_t batch, int32_t max_c
 mk_status mk_plan_graph(const mk_model_desc *desc, int32_t batch, int32_t max_ctx, const mk_options *opt,
                         int32_t n_workgroups, void *buf, size_t cap, size_t *need);
 
+/* ---- The prompt (prefill) megakernel ------------------------------------------
+ * The pass that runs once per request over the whole prompt before decoding starts,
+ * as its own persistent megakernel (knowledge-base digest "megakernel boundary
+ * selection": prefill in its list of first-used concepts; its planner gives Llama-1B
+ * a second megakernel, Figure 4, Table IV).  The same interpreter, queues and events
+ * as the decode step; the tasks are RMSNorm tiles of 16 tokens, matrix-core GEMM tiles
+ * (rows x 64 or 128 tokens) of the Q/K/V, O, gate/up and down projections, causal
+ * attention tiles of 16 query tokens x one KV group, and LM-head tiles for the last
+ * token.  Dense models with head_dim 64, hidden a multiple of 512 up to 2048, ffn_dim
+ * and n_q*head_dim multiples of 128.
+ *
+ * Builds a prompt handle for prompts of exactly n_tokens tokens (>= 1) of one sequence
+ * whose KV cache holds max_ctx >= n_tokens positions (the cache layout of a batch-1
+ * decode handle with the same max_ctx, so a decode handle continues from it).
+ * Options as mk_build_graph (attn_splits is ignored).  Errors: MK_E_INVALID (NULL
+ * pointers, n_tokens < 1 or > max_ctx, bad options), MK_E_UNSUPPORTED (a mixture of
+ * experts, head_dim other than 64, hidden above 2048 or not a multiple of 512, ffn_dim
+ * or n_q*head_dim not a multiple of 128), MK_E_NO_DEVICE, MK_E_NOMEM, MK_E_HIP.
+ * mk_decode_step and mk_decode_step_noalloc refuse the handle (MK_E_INVALID); the
+ * other handle functions apply: mk_next_tokens gives 1 token, mk_hidden_out
+ * [n_tokens rounded up to 16][hidden] (the first n_tokens rows: every prompt token's
+ * final residual), mk_kv_cache_bytes the cache size, mk_export_graph the graph. */
+mk_status mk_build_prefill(const mk_model_desc *desc, int32_t n_tokens, int32_t max_ctx, const mk_options *opt,
+                           mk_handle **out);
+
+/* Host-only planning of a prompt graph for `n_workgroups` workgroups, exported as
+ * mk_plan_graph does (touches no GPU; weight pointers may be NULL). */
+mk_status mk_plan_prefill(const mk_model_desc *desc, int32_t n_tokens, int32_t max_ctx, const mk_options *opt,
+                          int32_t n_workgroups, void *buf, size_t cap, size_t *need);
+
+/* One prompt, asynchronous on `stream`; enqueues exactly one kernel.  tokens (dev)
+ * int32 [n_tokens]: the prompt, at positions pos0 .. pos0 + n_tokens - 1 (host int;
+ * 0 <= pos0 <= max_ctx - n_tokens, else MK_E_INVALID); cache slots 0 .. pos0 - 1 of
+ * kv_cache (dev) hold the earlier context (a longer prompt in chunks: pos0 advancing by
+ * n_tokens).  Writes K/V slots pos0 .. pos0 + n_tokens - 1 of every layer, the final
+ * residual of every prompt token (mk_hidden_out), the logits of the last token into
+ * logits (dev, float [vocab]) unless NULL, and its greedy next token (mk_next_tokens).
+ * A token outside [0, vocab) records a device error (mk_check_device_error).
+ * Errors: MK_E_INVALID (NULL handle/tokens/kv_cache, a decode handle, pos0 out of
+ * range), MK_E_HIP, MK_E_NOT_RESIDENT. */
+mk_status mk_prefill(mk_handle *h, const int32_t *tokens, int32_t pos0, void *kv_cache, float *logits, void *stream);
+
 /* Bytes of the KV cache the caller allocates for this handle: K then V, each
  * bf16 [n_layers][batch][n_kv][max_ctx][head_dim] (the model's attention cache;
  * the pages take the model as given). */

@@ -19,9 +19,14 @@ MK_OK, MK_E_INVALID, MK_E_UNSUPPORTED, MK_E_NOMEM, MK_E_HIP, MK_E_NOT_RESIDENT, 
 
 # opcodes of the interpreter (mirrors csrc/mk_internal.h)
 OP_END, OP_QKV, OP_ATTN, OP_OPROJ, OP_GATEUP, OP_DOWN, OP_LMHEAD, OP_ROUTE, OP_EGU, OP_EDOWN = range(10)
+# the prompt (prefill) graph's operations
+OP_PNORM, OP_PQKV, OP_PATTN, OP_POPROJ, OP_PGU, OP_PDOWN, OP_PLM = range(10, 17)
 OP_NAMES = {OP_QKV: "qkv_rope", OP_ATTN: "attention", OP_OPROJ: "oproj_residual", OP_GATEUP: "gateup_silu",
             OP_DOWN: "down_residual", OP_LMHEAD: "lmhead_argmax", OP_ROUTE: "router_topk",
-            OP_EGU: "expert_gateup_silu", OP_EDOWN: "expert_down_residual"}
+            OP_EGU: "expert_gateup_silu", OP_EDOWN: "expert_down_residual",
+            OP_PNORM: "prompt_rmsnorm", OP_PQKV: "prompt_qkv_rope", OP_PATTN: "prompt_attention",
+            OP_POPROJ: "prompt_oproj_residual", OP_PGU: "prompt_gateup_silu", OP_PDOWN: "prompt_down_residual",
+            OP_PLM: "prompt_lmhead_argmax"}
 NONE = 0xFFFFFFFF
 
 _P = ctypes.c_void_p
@@ -89,6 +94,16 @@ def load():
     lib.mk_plan_graph.argtypes = [ctypes.POINTER(ModelDesc), ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(Options),
                                   ctypes.c_int32, _P, ctypes.c_size_t, ctypes.POINTER(ctypes.c_size_t)]
     lib.mk_plan_graph.restype = ctypes.c_int
+    if hasattr(lib, "mk_prefill"):  # (older variant builds loaded through MK_LIBRARY lack it)
+        lib.mk_build_prefill.argtypes = [ctypes.POINTER(ModelDesc), ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.POINTER(Options), ctypes.POINTER(_P)]
+        lib.mk_build_prefill.restype = ctypes.c_int
+        lib.mk_plan_prefill.argtypes = [ctypes.POINTER(ModelDesc), ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.POINTER(Options), ctypes.c_int32, _P, ctypes.c_size_t,
+                                        ctypes.POINTER(ctypes.c_size_t)]
+        lib.mk_plan_prefill.restype = ctypes.c_int
+        lib.mk_prefill.argtypes = [_P, _P, ctypes.c_int32, _P, _P, _P]
+        lib.mk_prefill.restype = ctypes.c_int
     lib.mk_kv_cache_bytes.argtypes = [_P]
     lib.mk_kv_cache_bytes.restype = ctypes.c_size_t
     lib.mk_decode_step.argtypes = [_P, _P, _P, _P, _P, _P]
@@ -168,6 +183,32 @@ def mk_plan_graph(desc, batch, max_ctx, opt, n_workgroups):
     _check(lib.mk_plan_graph(ctypes.byref(desc), batch, max_ctx, o, n_workgroups, buf, need.value,
                              ctypes.byref(need)), "mk_plan_graph")
     return buf.raw
+
+
+def mk_build_prefill(desc, n_tokens, max_ctx, opt=None):
+    """A prompt (prefill) handle for prompts of n_tokens tokens of one sequence."""
+    h = _P()
+    st = load().mk_build_prefill(ctypes.byref(desc), n_tokens, max_ctx,
+                                 ctypes.byref(opt) if opt is not None else None, ctypes.byref(h))
+    _check(st, "mk_build_prefill")
+    return h
+
+
+def mk_plan_prefill(desc, n_tokens, max_ctx, opt, n_workgroups):
+    lib = load()
+    need = ctypes.c_size_t(0)
+    o = ctypes.byref(opt) if opt is not None else None
+    st = lib.mk_plan_prefill(ctypes.byref(desc), n_tokens, max_ctx, o, n_workgroups, None, 0, ctypes.byref(need))
+    if st not in (MK_OK, MK_E_INVALID) or need.value == 0:
+        _check(st, "mk_plan_prefill")
+    buf = ctypes.create_string_buffer(need.value)
+    _check(lib.mk_plan_prefill(ctypes.byref(desc), n_tokens, max_ctx, o, n_workgroups, buf, need.value,
+                               ctypes.byref(need)), "mk_plan_prefill")
+    return buf.raw
+
+
+def mk_prefill(h, tokens_ptr, pos0, kv_ptr, logits_ptr, stream_ptr):
+    _check(load().mk_prefill(h, tokens_ptr, pos0, kv_ptr, logits_ptr, stream_ptr), "mk_prefill")
 
 
 def mk_kv_cache_bytes(h):

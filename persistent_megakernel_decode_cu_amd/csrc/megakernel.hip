@@ -2628,6 +2628,8 @@ __device__ __noinline__ void finish_step(const Params* pp, uint32_t epoch, uint3
     }
 }
 
+#include "prefill_ops.h"
+
 #define MK_KT_DISPATCH(fn, kt, ...)                                      \
     ((kt) == 128    ? fn<128>(__VA_ARGS__)                               \
      : (kt) == 256  ? fn<256>(__VA_ARGS__)                               \
@@ -2644,6 +2646,8 @@ __device__ __noinline__ void finish_step(const Params* pp, uint32_t epoch, uint3
 
 // ---- compute-wave main loop ---------------------------------------------------------------
 
+// PF: the prompt megakernel's operations (else the decode step's)
+template <bool PF>
 __device__ __noinline__ void compute(const Params* pp, uint32_t epoch, int wave) {
     Ctx c;
     c.wave = (int)uni((uint32_t)wave);
@@ -2671,7 +2675,23 @@ __device__ __noinline__ void compute(const Params* pp, uint32_t epoch, int wave)
         bool ok = true;
         // single-sequence operations referenced first: their functions are emitted next
         // to the loader, ahead of the several-sequence GEMV instances
-        if (!batched) {
+        if constexpr (PF) {
+            const bool w2 = (k.flags & TF_NGW2) != 0, r128 = k.nrows == 128;
+#define MK_PF_GEMM(OPK)                                                                  \
+    (r128 ? (w2 ? op_pgemm<OPK, 8, 2>(pp, slot, page0, t, epoch) : op_pgemm<OPK, 8, 1>(pp, slot, page0, t, epoch)) \
+          : op_pgemm<OPK, 4, 1>(pp, slot, page0, t, epoch))
+            switch (k.op) {
+                case OP_PNORM: ok = op_pnorm(pp, slot, page0, t, epoch); break;
+                case OP_PQKV: ok = MK_PF_GEMM(OP_PQKV); break;
+                case OP_PATTN: ok = op_pattn(pp, slot, page0, t, epoch); break;
+                case OP_POPROJ: ok = MK_PF_GEMM(OP_POPROJ); break;
+                case OP_PGU: ok = MK_PF_GEMM(OP_PGU); break;
+                case OP_PDOWN: ok = MK_PF_GEMM(OP_PDOWN); break;
+                case OP_PLM: ok = MK_KT_DISPATCH_2K(op_plm, h, pp, slot, page0, t, epoch); break;
+                default: break;
+            }
+#undef MK_PF_GEMM
+        } else if (!batched) {
             switch (k.op) {
                 case OP_QKV: ok = MK_KT_DISPATCH(op_qkv, h, pp, slot, page0, t, epoch); break;
                 case OP_ATTN: ok = attn_kswizzle(p0.T.d, p0.T.grp) ? op_attn_mfma(pp, slot, page0, t, epoch)
@@ -2736,7 +2756,7 @@ __device__ __noinline__ void compute(const Params* pp, uint32_t epoch, int wave)
                 // post the event to its scheduler's activated-event queue
                 st_dev(&p.aeq_stamp[k.sig_ev + (uint32_t)c.lane], epoch);
             }
-            if (k.op == OP_LMHEAD) finish_step(pp, epoch, c.parity);
+            if (k.op == OP_LMHEAD || (PF && k.op == OP_PLM)) finish_step(pp, epoch, c.parity);
             if (task_count && c.lane == 0) addu_dev(&task_count[k.id], 1u);
             if (tracing && c.lane == 0) {
                 unsigned long long* tr = p.trace + (size_t)k.id * TRACE_WORDS;
@@ -2832,7 +2852,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) mk_step_kernel(const Params* pp, 
                 p.aticket[(parity ^ 1u) * nt + i] = 0u;
         }
         if (wave >= NCW) loader(pp, epoch, wave - NCW);
-        else compute(pp, epoch, wave);
+        else compute<false>(pp, epoch, wave);
     }
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -2849,6 +2869,67 @@ hipError_t launch_step(const Params* dparams, const StepArgs& a, uint32_t grid, 
         return hipLaunchCooperativeKernel((const void*)mk_step_kernel, dim3(grid), dim3(NTHREADS), args, 0, stream);
     }
     hipLaunchKernelGGL(mk_step_kernel, dim3(grid), dim3(NTHREADS), 0, stream, dparams, a);
+    return hipGetLastError();
+}
+
+// The prompt megakernel: the same interpreter (loader waves, LDS ring, queues, events) over a
+// prompt graph.  Input check: every prompt token in [0, vocab) (pos0 is checked on the host).
+__global__ void __launch_bounds__(NTHREADS, 1) mk_prefill_kernel(const Params* pp, StepArgs a) {
+    const int wave = threadIdx.x >> 6;
+    CParams& p = P(pp);
+    if (threadIdx.x < FIFO) {
+        S.fifo_ready[threadIdx.x] = 0;
+        S.fifo_free[threadIdx.x] = 0;
+    }
+    if (threadIdx.x < NPAGES) {
+        for (int lw = 0; lw < NLW; ++lw) S.page_ready[lw][threadIdx.x] = 0;
+        S.page_free[threadIdx.x] = 0;
+    }
+    if (threadIdx.x < NCW) S.cgen[threadIdx.x] = 0;
+    if (threadIdx.x == 0) {
+        S.go = 0;
+        S.cbar = 0;
+        S.done = 0;
+        S.abort = 0;
+        S.dyn_ready = 0;
+        S.dyn_ack = 0;
+        S.trace_on = p.trace != nullptr ? 1u : 0u;
+        S.adealt = 0;
+        S.tm[2] = 0;
+        S.tm[3] = 0;
+        S.args = a;
+    }
+    const uint32_t epoch = p.state[ST_EPOCH];
+    const uint32_t parity = epoch & 1u;
+    int bad = 0;
+    for (int t = threadIdx.x; t < p.T.pf_T; t += NTHREADS) {
+        const int32_t v = a.tokens[t];
+        if (v < 0 || v >= p.T.V) bad = 1;
+    }
+    bad = __syncthreads_or(bad);
+    if (bad) {
+        if (blockIdx.x == 0 && threadIdx.x == 0) raise_error(pp, ERR_INPUT, 0, 0, 0, 0);
+    } else {
+        // the other parity's argmax key, for the next launch (read only after this one)
+        if (blockIdx.x == 0 && threadIdx.x == 0) p.key[parity ^ 1u] = 0ull;
+        if (wave >= NCW) loader(pp, epoch, wave - NCW);
+        else compute<true>(pp, epoch, wave);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t old = addu_dev(&p.state[ST_EXIT], 1u);
+        if (old + 1u == epoch * gridDim.x) st_dev(&p.state[ST_EPOCH], epoch + 1u);
+    }
+}
+
+hipError_t launch_prefill(const Params* dparams, const StepArgs& a, uint32_t grid, hipStream_t stream, bool cooperative) {
+    if (cooperative) {
+        StepArgs ac = a;
+        const Params* pc = dparams;
+        void* args[] = {(void*)&pc, (void*)&ac};
+        return hipLaunchCooperativeKernel((const void*)mk_prefill_kernel, dim3(grid), dim3(NTHREADS), args, 0, stream);
+    }
+    hipLaunchKernelGGL(mk_prefill_kernel, dim3(grid), dim3(NTHREADS), 0, stream, dparams, a);
     return hipGetLastError();
 }
 
@@ -2918,6 +2999,12 @@ __global__ void __launch_bounds__(256) repack_tiles_kernel(const TileOp* ops, co
             const uint32_t half = w / (rgs * hb), w2 = w % (rgs * hb);
             row = (c * cr + w2 / hb) * 16 + l % 16;
             col = (half * hb + w2 % hb) * 32 + (l / 16) * 8;
+        } else if (op.blocked == 3) {  // prompt GEMM pages: page, then column block, then row group
+            const uint32_t b = e / 64, l = e % 64;
+            const uint32_t nrg = op.rows / 16, kbp = 16 / nrg;
+            const uint32_t pg = b / 16, w = b % 16;
+            row = (w % nrg) * 16 + l % 16;
+            col = (pg * kbp + w / nrg) * 32 + (l / 16) * 8;
         } else if (op.blocked) {  // row-group major: block b = (row group, column block)
             const uint32_t b = e / 64, l = e % 64;
             row = (b / nkb) * 16 + l % 16;
@@ -2948,5 +3035,6 @@ hipError_t launch_repack(const CopyOp* ops, uint32_t n_ops, uint8_t* dst, hipStr
 int step_threads() { return NTHREADS; }
 size_t step_lds_bytes() { return sizeof(Smem); }
 const void* step_kernel_ptr() { return (const void*)mk_step_kernel; }
+const void* prefill_kernel_ptr() { return (const void*)mk_prefill_kernel; }
 
 }  // namespace mk

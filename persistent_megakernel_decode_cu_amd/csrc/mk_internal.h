@@ -18,7 +18,15 @@ enum Op : uint8_t {
     OP_ROUTE = 7,     // RMSNorm + router GEMV rows: router logits of up to 16 experts
     OP_EGU = 8,       // RMSNorm + one expert's gate/up rows + SiLU * up
     OP_EDOWN = 9,     // routing weights (top-k + softmax) + one expert's down-proj rows, weighted, + residual (atomic)
-    OP_COUNT = 10
+    // the prompt (prefill) megakernel: the T tokens of one sequence's prompt per launch
+    OP_PNORM = 10,    // RMSNorm of 16 tokens' residual rows -> matrix-core operands (+ the residual carried on)
+    OP_PQKV = 11,     // Q/K/V rows x a token block + RoPE -> query operands and K/V cache rows
+    OP_PATTN = 12,    // causal attention of 16 query tokens for the heads of one KV group
+    OP_POPROJ = 13,   // O-proj rows x a token block over one K slice, added to the residual (atomic)
+    OP_PGU = 14,      // gate/up rows x a token block + SiLU * up -> down-projection operands
+    OP_PDOWN = 15,    // down-proj rows x a token block over one K slice, added to the residual (atomic)
+    OP_PLM = 16,      // final RMSNorm'd last token x LM-head rows + argmax
+    OP_COUNT = 17
 };
 
 constexpr uint32_t NONE = 0xFFFFFFFFu;
@@ -69,8 +77,15 @@ static_assert(sizeof(Task) == 48, "task record is 48 bytes");
 
 enum TaskFlags : uint8_t {
     TF_RESID = 1,    // OPROJ / DOWN: this tile also adds the residual input
-    TF_SIGRANGE = 2  // ROUTE: signals the E consecutive events sig_ev .. sig_ev + E - 1
+    TF_SIGRANGE = 2, // ROUTE: signals the E consecutive events sig_ev .. sig_ev + E - 1
+    TF_NGW2 = 4      // prompt GEMM tiles: two token groups of 16 per compute wave (128-token blocks), else one
 };
+
+// Prompt GEMM tiles: the tile's weights (rows x K slice) are stored page by page, each
+// 16 KiB page holding every row of the tile over a 16 / (rows / 16) x 32-column stretch
+// of K, as 16 x 32 matrix-core blocks in (column block, row group) order.
+constexpr int PF_GEMMS = 4;  // QKV, O-proj, gate/up, down
+constexpr int pf_kbp(int rows) { return 16 / (rows / 16); }  // 32-column blocks per page
 
 // Tiling of one model on W workgroups (computed once on the host).
 struct Tiling {
@@ -88,6 +103,11 @@ struct Tiling {
     // routing; expert gate/up tiles of r_gu rows of m (gate and up rows interleaved in
     // blocks of 32), expert down tiles of r_dn rows
     int32_t E, topk, fe, r_gu, r_dn;
+    // prompt graph (mk_build_prefill; pf_T = 0 for a decode graph): tokens per launch, then per
+    // GEMM (QKV, O-proj, gate/up, down): rows per tile (64 or 128; gate/up: half gate, half up
+    // rows), token groups of 16 per compute wave (tokens per task: 64 ngw), K slices
+    int32_t pf_T;
+    int32_t pf_rows[PF_GEMMS], pf_ngw[PF_GEMMS], pf_slices[PF_GEMMS];
 };
 
 // Byte layout of the handle-owned packed weight buffer.

@@ -20,6 +20,7 @@ struct mk_handle {
     int W = 0;
     bool cooperative = false;  // plain launch unless asked (mk_options.cooperative)
     bool poison = false;       // fill the step's scratch with NaN before every step (mk_options.poison)
+    int prompt = 0;            // a prompt (prefill) handle: tokens per launch (mk_build_prefill); 0: decode
     size_t xop_bytes = 0;
     // the allocation-free step: the same parameters with the step's scratch in the per-GPU static
     // array (null when this handle's scratch does not fit it)
@@ -99,6 +100,27 @@ mk_status plan(const mk_model_desc* desc, int32_t batch, int32_t max_ctx, const 
     return MK_OK;
 }
 
+mk_status plan_prefill(const mk_model_desc* desc, int32_t n_tokens, int32_t max_ctx, const mk_options* opt, int W,
+                       Graph* g, bool* tied) {
+    if (!desc) return MK_E_INVALID;
+    mk_options o;
+    memset(&o, 0, sizeof(o));
+    if (opt) o = *opt;
+    if (o.sched < 0 || o.sched > 3 || o.policy < 0 || o.policy > 1) return MK_E_INVALID;
+    if (o.page_kib != 0 && o.page_kib != 16) return MK_E_INVALID;
+    if (o.poison < 0 || o.poison > 1 || o.attn_splits < 0 || o.attn_splits > 16) return MK_E_INVALID;
+    Tiling T;
+    std::string err;
+    bool unsup = false;
+    if (plan_prefill_tiling(dims_of(desc), n_tokens, max_ctx, W, &T, &err, &unsup) != 0)
+        return unsup ? MK_E_UNSUPPORTED : MK_E_INVALID;
+    Layout Ly;
+    *tied = desc->tied_lm_head != 0;
+    plan_layout(T, *tied, &Ly);
+    build_prefill_graph(T, Ly, o.sched, o.policy, g);
+    return MK_OK;
+}
+
 // Copy the caller's weights into the packed layout: gains and embedding row by
 // row (CopyOp), then every GEMV tile in task order (TileOp): rows of the tile
 // come from a host-built table of row addresses (null = a zero row of padding),
@@ -133,7 +155,7 @@ mk_status repack(mk_handle* h, const mk_model_desc* d, uint8_t* wd) {
     const int half = T.d / 2, P = T.qkv_pairs;
     const uint8_t* lm = (const uint8_t*)(h->tied ? d->tok_embed : d->lm_head);
     for (const Task& k : h->g.tasks) {
-        if (k.op == OP_ATTN || k.wbytes == 0 || k.seq != 0) continue;  // column groups share the tiles
+        if (k.op == OP_ATTN || k.wbytes == 0 || k.seq != 0) continue;  // column groups (token blocks) share the tiles
         const mk_layer_weights& lw = d->layers[k.layer < T.L ? k.layer : 0];
         TileOp t;
         t.dst_off = k.wofs;
@@ -178,6 +200,28 @@ mk_status repack(mk_handle* h, const mk_model_desc* d, uint8_t* wd) {
                 for (uint32_t i = 0; i < 32; ++i) rows.push_back((const uint8_t*)lw.exp_gate + (e0 + k.row0 + q + i) * rowb);
                 for (uint32_t i = 0; i < 32; ++i) rows.push_back((const uint8_t*)lw.exp_up + (e0 + k.row0 + q + i) * rowb);
             }
+        } else if (k.op == OP_PQKV) {
+            // rows row0 .. of the stacked [Wq; Wk; Wv]
+            const uint32_t nqd = (uint32_t)(T.nq * T.d), nkd = (uint32_t)(T.nkv * T.d);
+            for (uint32_t i = 0; i < k.nrows; ++i) {
+                const uint32_t r = k.row0 + i;
+                rows.push_back(r < nqd         ? (const uint8_t*)lw.wq + (uint64_t)r * rowb
+                               : r < nqd + nkd ? (const uint8_t*)lw.wk + (uint64_t)(r - nqd) * rowb
+                                               : (const uint8_t*)lw.wv + (uint64_t)(r - nqd - nkd) * rowb);
+            }
+        } else if (k.op == OP_POPROJ || k.op == OP_PDOWN) {
+            // rows row0 .. of W_o or W_d over K slice `part`
+            const uint64_t kfull = k.op == OP_POPROJ ? (uint64_t)T.nq * T.d : (uint64_t)T.f;
+            kt = (uint32_t)(kfull / (uint64_t)T.pf_slices[k.op == OP_POPROJ ? 1 : 3]);
+            const uint8_t* src = (const uint8_t*)(k.op == OP_POPROJ ? lw.wo : lw.w_down);
+            for (uint32_t i = 0; i < k.nrows; ++i)
+                rows.push_back(src + (uint64_t)(k.row0 + i) * kfull * 2 + (uint64_t)k.part * kt * 2);
+        } else if (k.op == OP_PGU) {
+            // m rows row0 .. row0 + nrows/2: their gate rows, then their up rows
+            for (uint32_t i = 0; i < k.nrows / 2; ++i) rows.push_back((const uint8_t*)lw.w_gate + (uint64_t)(k.row0 + i) * rowb);
+            for (uint32_t i = 0; i < k.nrows / 2; ++i) rows.push_back((const uint8_t*)lw.w_up + (uint64_t)(k.row0 + i) * rowb);
+        } else if (k.op == OP_PLM) {
+            for (uint32_t i = 0; i < k.nrows; ++i) rows.push_back(lm + (uint64_t)(k.row0 + i) * rowb);
         } else if (k.op == OP_EDOWN) {
             kt = (uint32_t)T.fe;
             const uint64_t pitch = (uint64_t)T.fe * 2;
@@ -188,6 +232,7 @@ mk_status repack(mk_handle* h, const mk_model_desc* d, uint8_t* wd) {
         t.rows = (uint32_t)(k.wbytes / (kt * 2));
         while (rows.size() < (size_t)t.row_base + t.rows) rows.push_back(nullptr);
         t.blocked = kt <= 2048 ? 1u : 0u;
+        if (k.op == OP_PQKV || k.op == OP_POPROJ || k.op == OP_PGU || k.op == OP_PDOWN) t.blocked = 3u;
         t.chunk_rows = 0;
         if (halves_packed(batched_path(T.B, T.E), k.op, (int)kt)) {
             t.blocked = 2u;
@@ -278,8 +323,13 @@ mk_status mk_plan_graph(const mk_model_desc* desc, int32_t batch, int32_t max_ct
     return MK_OK;
 }
 
-mk_status mk_build_graph(const mk_model_desc* desc, int32_t batch, int32_t max_ctx, const mk_options* opt,
-                         mk_handle** out) {
+}  // extern "C"
+
+namespace {
+
+// A decode handle (prompt = 0) or a prompt handle (prompt = tokens per launch, batch 1).
+mk_status build_handle(const mk_model_desc* desc, int32_t batch, int32_t max_ctx, const mk_options* opt, int32_t prompt,
+                       mk_handle** out) {
     if (!out) return MK_E_INVALID;
     *out = nullptr;
     if (!desc_ok(desc)) return MK_E_INVALID;
@@ -295,14 +345,17 @@ mk_status mk_build_graph(const mk_model_desc* desc, int32_t batch, int32_t max_c
     hipDeviceProp_t prop;
     HIPCHK(hipGetDeviceProperties(&prop, h->device));
     int per_cu = 0;
-    HIPCHK(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, step_kernel_ptr(), step_threads(), 0));
+    HIPCHK(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, prompt ? prefill_kernel_ptr() : step_kernel_ptr(),
+                                                         step_threads(), 0));
     const int max_resident = per_cu * prop.multiProcessorCount;
     h->W = o.n_workgroups > 0 ? o.n_workgroups : prop.multiProcessorCount;
     if (h->W > max_resident) {
         delete h;
         return MK_E_NOT_RESIDENT;
     }
-    mk_status st = plan(desc, batch, max_ctx, &o, h->W, &h->g, &h->tied);
+    h->prompt = prompt;
+    mk_status st = prompt ? plan_prefill(desc, prompt, max_ctx, &o, h->W, &h->g, &h->tied)
+                          : plan(desc, batch, max_ctx, &o, h->W, &h->g, &h->tied);
     if (st != MK_OK) {
         delete h;
         return st;
@@ -374,12 +427,27 @@ mk_status mk_build_graph(const mk_model_desc* desc, int32_t batch, int32_t max_c
     const int half = T.d / 2;
     ALLOC(rope, (size_t)T.C * half * sizeof(float2), false);
     p.rope = rope;
+    if (prompt) {
+        // prompt buffers: query operands, residual rows after attention and after the FFN, and the
+        // matrix-core operand regions (normalised inputs, attention output, SiLU(gate) * up, final
+        // normalised last token), all zero at first (the columns of the tokens past the prompt in its
+        // last group of 16 stay zero or finite)
+        const size_t ntg = (size_t)(T.pf_T + 15) / 16;
+        ALLOC(p.q, ntg * T.nq * (T.d / 32) * 2048, true);
+        ALLOC(p.part, 256, true);
+        ALLOC(p.m, 256, true);
+        h->acc_bytes = 2 * ntg * 16 * T.h * 4;
+        ALLOC(p.acc, h->acc_bytes, true);
+        h->xop_bytes = (ntg * ((size_t)T.h + (size_t)T.nq * T.d + (size_t)T.f) + T.h) / 32 * 2048;
+        ALLOC(p.xop, h->xop_bytes, true);
+    } else {
     ALLOC(p.q, (size_t)T.B * T.nq * T.d * 4, true);
     ALLOC(p.part, (size_t)T.B * T.nkv * part_chunks(batched_path(T.B, T.E), T.attn_splits) * T.grp * (T.d + 2) * 4, true);
     ALLOC(p.m, (size_t)T.B * T.f * 4, true);
     h->acc_bytes = (size_t)2 * (2 * T.L + 1) * T.B * T.h * 4;
     ALLOC(p.acc, h->acc_bytes, true);
-    if (batched_path(T.B, T.E)) {
+    }
+    if (!prompt && batched_path(T.B, T.E)) {
         // matrix-core operands of the O- and down-projection inputs: 2 bf16 parts x 16
         // sequences per column (columns of absent sequences stay zero for the handle's life)
         const size_t n_sg = (size_t)(T.B + GROUP_SEQS - 1) / GROUP_SEQS;
@@ -394,7 +462,8 @@ mk_status mk_build_graph(const mk_model_desc* desc, int32_t batch, int32_t max_c
             ALLOC(p.eids, (size_t)T.L * T.B * T.topk * 4, true);
         }
     }
-    ALLOC(p.hidden, (size_t)T.B * T.h * 4, true);
+    if (prompt) p.hidden = p.acc + (size_t)(T.pf_T + 15) / 16 * 16 * T.h;  // the residual after the last layer
+    else ALLOC(p.hidden, (size_t)T.B * T.h * 4, true);
     ALLOC(p.key, sizeof(unsigned long long) * 2 * T.B, true);
     ALLOC(p.ticket, 4 * T.B, true);
     ALLOC(p.next, 4 * T.B, true);
@@ -420,7 +489,7 @@ mk_status mk_build_graph(const mk_model_desc* desc, int32_t batch, int32_t max_c
         mk_destroy(h);
         return MK_E_HIP;
     }
-    {
+    if (!prompt) {
         // the allocation-free step: the same buffers laid out in this GPU's static scratch array
         // (tasks, queues, weights, RoPE table, outputs and the event-driven lists stay the handle's)
         size_t at = 0;
@@ -489,6 +558,58 @@ mk_status mk_build_graph(const mk_model_desc* desc, int32_t batch, int32_t max_c
 #undef ALLOC
 }
 
+}  // namespace
+
+extern "C" {
+
+mk_status mk_build_graph(const mk_model_desc* desc, int32_t batch, int32_t max_ctx, const mk_options* opt,
+                         mk_handle** out) {
+    return build_handle(desc, batch, max_ctx, opt, 0, out);
+}
+
+mk_status mk_build_prefill(const mk_model_desc* desc, int32_t n_tokens, int32_t max_ctx, const mk_options* opt,
+                           mk_handle** out) {
+    if (n_tokens < 1) {
+        if (out) *out = nullptr;
+        return MK_E_INVALID;
+    }
+    return build_handle(desc, 1, max_ctx, opt, n_tokens, out);
+}
+
+mk_status mk_plan_prefill(const mk_model_desc* desc, int32_t n_tokens, int32_t max_ctx, const mk_options* opt,
+                          int32_t n_workgroups, void* buf, size_t cap, size_t* need) {
+    if (!desc || n_workgroups < 1 || n_tokens < 1) return MK_E_INVALID;
+    Graph g;
+    bool tied;
+    mk_status st = plan_prefill(desc, n_tokens, max_ctx, opt, n_workgroups, &g, &tied);
+    if (st != MK_OK) return st;
+    size_t n = export_size(g);
+    if (need) *need = n;
+    if (!buf || cap < n) return MK_E_INVALID;
+    export_graph(g, buf, cap);
+    return MK_OK;
+}
+
+mk_status mk_prefill(mk_handle* h, const int32_t* tokens, int32_t pos0, void* kv_cache, float* logits, void* stream) {
+    if (!h || !h->prompt || !tokens || !kv_cache) return MK_E_INVALID;
+    const Tiling& T = h->g.T;
+    if (pos0 < 0 || pos0 > T.C - T.pf_T) return MK_E_INVALID;
+    StepArgs a;
+    a.tokens = tokens;
+    a.positions = nullptr;
+    a.kc = (uint16_t*)kv_cache;
+    a.vc = (uint16_t*)kv_cache + (size_t)T.L * T.B * T.nkv * (size_t)T.C * T.d;
+    a.logits = logits;
+    a.pos0 = pos0;
+    if (h->poison) {
+        const mk_status st = enqueue_poison(h, h->p, logits, (hipStream_t)stream);
+        if (st != MK_OK) return st;
+    }
+    hipError_t e = launch_prefill(h->dparams, a, (uint32_t)h->W, (hipStream_t)stream, h->cooperative);
+    if (e == hipErrorCooperativeLaunchTooLarge) return MK_E_NOT_RESIDENT;
+    return e == hipSuccess ? MK_OK : MK_E_HIP;
+}
+
 size_t mk_kv_cache_bytes(const mk_handle* h) {
     if (!h) return 0;
     const Tiling& T = h->g.T;
@@ -497,7 +618,7 @@ size_t mk_kv_cache_bytes(const mk_handle* h) {
 
 mk_status mk_decode_step(mk_handle* h, const int32_t* tokens, const int32_t* positions, void* kv_cache, float* logits,
                          void* stream) {
-    if (!h || !tokens || !positions || (!kv_cache && h->g.T.L > 0)) return MK_E_INVALID;
+    if (!h || h->prompt || !tokens || !positions || (!kv_cache && h->g.T.L > 0)) return MK_E_INVALID;
     const Tiling& T = h->g.T;
     StepArgs a;
     a.tokens = tokens;
@@ -505,6 +626,7 @@ mk_status mk_decode_step(mk_handle* h, const int32_t* tokens, const int32_t* pos
     a.kc = (uint16_t*)kv_cache;
     a.vc = (uint16_t*)kv_cache + (size_t)T.L * T.B * T.nkv * (size_t)T.C * T.d;
     a.logits = logits;
+    a.pos0 = 0;
     if (h->poison) {
         const mk_status st = enqueue_poison(h, h->p, logits, (hipStream_t)stream);
         if (st != MK_OK) return st;
@@ -516,7 +638,7 @@ mk_status mk_decode_step(mk_handle* h, const int32_t* tokens, const int32_t* pos
 
 mk_status mk_decode_step_noalloc(mk_handle* h, const int32_t* tokens, const int32_t* positions, void* kv_cache,
                                  float* logits, void* stream) {
-    if (!h || !tokens || !positions || (!kv_cache && h->g.T.L > 0)) return MK_E_INVALID;
+    if (!h || h->prompt || !tokens || !positions || (!kv_cache && h->g.T.L > 0)) return MK_E_INVALID;
     if (!h->dparams_na) return MK_E_UNSUPPORTED;  // this handle's scratch exceeds the static array
     const Tiling& T = h->g.T;
     const Params& p = h->p_na;
@@ -559,6 +681,7 @@ mk_status mk_decode_step_noalloc(mk_handle* h, const int32_t* tokens, const int3
     a.kc = (uint16_t*)kv_cache;
     a.vc = (uint16_t*)kv_cache + (size_t)T.L * T.B * T.nkv * (size_t)T.C * T.d;
     a.logits = logits;
+    a.pos0 = 0;
     e = launch_step(h->dparams_na, a, (uint32_t)h->W, (hipStream_t)stream, h->cooperative);
     if (e == hipErrorCooperativeLaunchTooLarge) return MK_E_NOT_RESIDENT;
     return e == hipSuccess ? MK_OK : MK_E_HIP;
@@ -581,6 +704,16 @@ mk_status enqueue_poison(mk_handle* h, const Params& p, float* logits, hipStream
             ++ps.n;
         };
         const uint32_t fnan = 0x7fc00000u, bnan2 = 0x7fc07fc0u, neg1 = 0xffffffffu;
+        if (h->prompt) {
+            // query operands, operand regions, residual rows and logits (each written before it is read;
+            // columns of tokens past the prompt only ever meet other such columns)
+            span(p.q, (size_t)(T.pf_T + 15) / 16 * T.nq * (T.d / 32) * 2048, fnan);
+            span(p.xop, h->xop_bytes, bnan2);
+            span(p.acc, h->acc_bytes, fnan);
+            span(logits, (size_t)T.V * 4, fnan);
+            hipError_t e = launch_poison(ps, stream);
+            return e == hipSuccess ? MK_OK : MK_E_HIP;
+        }
         span(p.q, (size_t)T.B * T.nq * T.d * 4, fnan);
         span(p.part, (size_t)T.B * T.nkv * part_chunks(batched_path(T.B, T.E), T.attn_splits) * T.grp * (T.d + 2) * 4, fnan);
         span(p.m, (size_t)T.B * T.f * 4, fnan);

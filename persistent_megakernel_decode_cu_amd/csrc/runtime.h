@@ -30,7 +30,8 @@ struct StepArgs {
     const int32_t* positions; // [B]
     uint16_t* kc;             // K cache [L][B][n_kv][C][d]
     uint16_t* vc;             // V cache
-    float* logits;            // [B][V] or null
+    float* logits;            // [B][V] or null (prompt launch: [V] of the last token)
+    int32_t pos0;             // prompt launch: position of the first prompt token (tokens: [T])
 };
 
 // Everything else the kernel reads, resident in device memory for the life of the handle.
@@ -99,13 +100,16 @@ hipError_t launch_repack(const CopyOp* ops, uint32_t n_ops, uint8_t* dst, hipStr
 // lane l of a block holds row 16*rg + l%16, columns 32*kb + 8*(l/16) .. +7).
 struct TileOp {
     uint64_t dst_off;
-    uint32_t row_base, rows, kt, blocked;  // blocked: 0 row-major, 1 matrix-core blocks, 2 the same in K halves
+    uint32_t row_base, rows, kt, blocked;  // blocked: 0 row-major, 1 matrix-core blocks, 2 the same in K halves,
+                                           // 3 prompt GEMM pages (page, then column block, then row group)
     uint32_t chunk_rows;                   // blocked == 2: rows per chunk
 };
 hipError_t launch_repack_tiles(const TileOp* ops, uint32_t n_ops, const uint8_t* const* rowsrc, uint8_t* dst,
                                hipStream_t stream);
 
 hipError_t launch_step(const Params* dparams, const StepArgs& a, uint32_t grid, hipStream_t stream, bool cooperative);
+// the prompt megakernel: same interpreter, prompt operations
+hipError_t launch_prefill(const Params* dparams, const StepArgs& a, uint32_t grid, hipStream_t stream, bool cooperative);
 
 // Fill spans (poison mode, and the allocation-free step's clears): up to MAX_SPANS spans of
 // 32-bit words, each filled with a pattern before a step.
@@ -127,5 +131,6 @@ hipError_t noalloc_scratch_base(int device, uint8_t** out);
 int step_threads();
 size_t step_lds_bytes();
 const void* step_kernel_ptr();
+const void* prefill_kernel_ptr();
 
 }  // namespace mk

@@ -136,6 +136,11 @@ def make_tokens(cfg, batch, seed=SEED_TOKENS):
     return uniform_int(seed, "tokens", 0, cfg.vocab - 1, batch)
 
 
+def make_prompt(cfg, n, seed=SEED_TOKENS):
+    """n prompt token ids, uniform over the vocabulary (a stream of their own)."""
+    return uniform_int(seed, "prompt", 0, cfg.vocab - 1, n)
+
+
 def make_positions(batch, lo, hi, seed=SEED_TOKENS):
     """Per-sequence context lengths, uniform in [lo, hi]."""
     if lo == hi:

@@ -42,4 +42,8 @@ MOE_1B = ModelConfig("moe-16l-64e-top8", 16, 2048, 32, 8, 64, 0, 128256, True, 5
 # Tiny sparse MoE for the GPU tests: the tiny attention shape, 8 experts of SwiGLU 256, top-2.
 TINY_MOE = ModelConfig("tiny-moe", 2, 256, 4, 2, 64, 0, 4096, True, 10000.0, n_experts=8, top_k=2, expert_ffn=256)
 
-CONFIGS = {c.name: c for c in (TINY, LLAMA_1B, LLAMA_8B, MOE_1B, TINY_MOE)}
+# Small dense decoder within the prompt megakernel's shape limits (hidden a multiple of 512, head_dim 64):
+# 2 layers, hidden 512, 8 Q / 2 KV heads of 64, SwiGLU 1024, vocab 4096.
+TINY_PF = ModelConfig("tiny-prompt", 2, 512, 8, 2, 64, 1024, 4096, True, 10000.0)
+
+CONFIGS = {c.name: c for c in (TINY, LLAMA_1B, LLAMA_8B, MOE_1B, TINY_MOE, TINY_PF)}
