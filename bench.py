@@ -18,6 +18,8 @@ baseline on the same inputs, and the oracle's CPU time on a bounded sample.
   python bench.py --batch 16    (mixed-context batch workload, tokens/s, with the one-kernel-per-op baseline
                                 on the same inputs beside it; not the headline line)
   python bench.py --model moe   (64-expert top-8 MoE on the 1B attention shape, batch 16, context 2048)
+  python bench.py --prefill 1024 (the prompt megakernel on a 1024-token prompt: tokens/s, TFLOP/s vs the
+                                matrix-core peak, beside the same prompt as 1024 decode steps)
 """
 import argparse
 import json
@@ -229,7 +231,9 @@ def baseline_leg(mk, torch, cfg, desc, kv, tok, P0, C, K, W, mk_ms):
 
 
 TRACE_OPS = {1: "QKV+RoPE", 2: "attention", 3: "O-proj", 4: "gate/up", 5: "down", 6: "LM head", 7: "router",
-             8: "expert gate/up", 9: "expert down"}
+             8: "expert gate/up", 9: "expert down", 10: "RMSNorm (prompt)", 11: "QKV+RoPE (prompt)",
+             12: "attention (prompt)", 13: "O-proj (prompt)", 14: "gate/up (prompt)", 15: "down (prompt)",
+             16: "LM head (prompt)"}
 
 
 def trace_summary(tr, ex, title, command):
@@ -283,7 +287,7 @@ def trace_summary(tr, ex, title, command):
     # per layer: when each phase's last task ended (from the step's first fetch)
     layers = tasks["layer"]
     L = ex["header"]["L"]
-    phase_ops = [o for o in (1, 2, 3, 4, 5, 7, 8, 9) if (ops == o).any()]
+    phase_ops = [o for o in (1, 2, 3, 4, 5, 7, 8, 9, 10, 11, 12, 13, 14, 15) if (ops == o).any()]
     lines += ["", "## Layer phases (µs from the step's first fetch: the end of each phase's last task)", "",
               "| layer | " + " | ".join(TRACE_OPS[o] for o in phase_ops) + " | layer time |",
               "|---|" + "---|" * (len(phase_ops) + 1)]
@@ -302,7 +306,7 @@ def trace_summary(tr, ex, title, command):
             lines.append(f"| {l} | " + " | ".join(f"{r:.1f}" for r in row) + f" | {lt:.1f} |")
         elif l == 3:
             lines.append("| … |" + " |" * (len(phase_ops) + 1))
-    s = ops == 6
+    s = (ops == 6) | (ops == 16)
     if s.any():
         lm_end = (int(end[s].max()) - t0) * us
         lines += ["", f"Median layer time {np.median(layer_times[1:] or layer_times):.1f} µs; LM head phase "
@@ -486,6 +490,123 @@ def bench_batch(args, torch, synth, mk):
     print(json.dumps(out), flush=True)
 
 
+def prefill_flops(cfg, T, pos0=0):
+    """Algorithmic flops of one prompt: the projections of every token (2 per weight), causal attention
+    (QK^T and PV, 2 d flops each per query head and visible key) and the LM head of the last token."""
+    h, d = cfg.hidden, cfg.head_dim
+    proj = cfg.n_layers * (h * (cfg.n_q + 2 * cfg.n_kv) * d + cfg.n_q * d * h + 3 * h * cfg.ffn)
+    keys = sum(pos0 + t + 1 for t in range(T))
+    attn = cfg.n_layers * cfg.n_q * 4 * d * keys
+    return 2 * proj * T + attn + 2 * cfg.vocab * h
+
+
+def bench_prefill(args, torch, synth, mk):
+    """The prompt (prefill) megakernel: one launch runs a prompt of T tokens at positions 0 .. T-1 through
+    the Llama-1B shape (K/V of every layer written, last token's logits and next token).  Synthetic prompt
+    tokens uniform over the vocabulary, the same prompt every launch."""
+    cfg = synth.configs.LLAMA_1B
+    T, K, W = args.prefill, args.steps, args.warmup
+    C = max(2048, (T + 63) // 64 * 64)
+    t_gen = time.perf_counter()
+    w = synth.make_weights(cfg)
+    kc, vc = synth.make_kv(cfg, 1, C)
+    toks = synth.make_prompt(cfg, T)
+    t_gen = time.perf_counter() - t_gen
+    dev = {k: torch.from_numpy(v.view(np.int16)).cuda() for k, v in w.items()}
+    model = mk.Model(cfg, dev)
+    opt_kw = dict(sched=SCHEDS[args.sched], policy=0 if args.policy == "rr" else 1,
+                  cooperative=1 if args.cooperative else 0)
+    h = mk.mk_build_prefill(model.desc, T, C, mk.options(**opt_kw))
+    graph = mk.parse_export(mk.mk_export_graph(h))
+    kv = torch.from_numpy(np.concatenate([kc.reshape(-1), vc.reshape(-1)]).view(np.int16)).cuda()
+    logits = torch.empty(cfg.vocab, dtype=torch.float32, device="cuda")
+    tok = torch.tensor(toks, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    for _ in range(W):
+        mk.mk_prefill(h, tok.data_ptr(), 0, kv.data_ptr(), logits.data_ptr(), sp)
+    torch.cuda.synchronize()
+    err = mk.mk_check_device_error(h)
+    if err:
+        raise SystemExit(f"device error: {err}")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    t0 = time.perf_counter()
+    for s_ in range(K):
+        ev[s_][0].record(stream)
+        mk.mk_prefill(h, tok.data_ptr(), 0, kv.data_ptr(), logits.data_ptr(), sp)
+        ev[s_][1].record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1000.0 / K
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    err = mk.mk_check_device_error(h)
+    if err:
+        raise SystemExit(f"device error: {err}")
+    mk.mk_destroy(h)
+    flops = prefill_flops(cfg, T)
+    tflops = flops / (ms * 1e-3) / 1e12
+    wbytes = cfg.weight_bytes()
+    # the same prompt as T decode steps of the decode megakernel (batch 1, one launch per token): the
+    # per-step time at the prompt's mid context, times T
+    hd = mk.mk_build_graph(model.desc, 1, C, mk.options())
+    kvd = kv.clone()
+    pos = torch.arange(T // 2, T // 2 + 16, dtype=torch.int32, device="cuda")
+    for s_ in range(4):
+        mk.mk_decode_step(hd, tok.data_ptr(), pos[s_].data_ptr(), kvd.data_ptr(), 0, sp)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for s_ in range(16):
+        mk.mk_decode_step(hd, tok.data_ptr() + 4 * s_, pos[s_].data_ptr(), kvd.data_ptr(), 0, sp)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    dec_us = e0.elapsed_time(e1) * 1000.0 / 16
+    mk.mk_destroy(hd)
+    del kvd
+    out = {
+        "metric": f"prompt (prefill) tokens/s, Llama-1B shape, {T}-token prompt, one launch; achieved TFLOP/s vs "
+                  "the bf16 matrix-core peak",
+        "value": round(T * 1000.0 / ms, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms, 4), "wall_ms_per_prompt": round(wall_ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{cfg.name} prompt of {T} tokens at positions 0..{T - 1}, bf16 weights and KV "
+                               "cache, one kernel launch per prompt",
+                   "prompt_tokens": T, "max_ctx": C, "sched": args.sched, "workgroups": int(graph["header"]["W"]),
+                   "tasks_per_prompt": int(graph["header"]["n_tasks"])},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": 2500.0, "unit": "TFLOP/s",
+                     "frac": round(tflops / 2500.0, 4), "traffic": None,
+                     "algorithmic_flops_per_prompt": int(flops), "kernel_us_per_launch": round(ms * 1000, 2),
+                     "weight_bytes": int(wbytes), "weights_gbs": round(wbytes / (ms * 1e-3) / 1e9, 1)},
+        "as_decode_steps": {"us_per_step": round(dec_us, 1), "ms_for_prompt": round(dec_us * T / 1000.0, 2),
+                            "speedup": round(dec_us * T / 1000.0 / ms, 2)},
+        "input_generation_s": round(t_gen, 1),
+    }
+    if args.trace:
+        ht = mk.mk_build_prefill(model.desc, T, C, mk.options(trace=1, **opt_kw))
+        ex = mk.parse_export(mk.mk_export_graph(ht))
+        for _ in range(2):
+            mk.mk_prefill(ht, tok.data_ptr(), 0, kv.data_ptr(), logits.data_ptr(), sp)
+        torch.cuda.synchronize()
+        err = mk.mk_check_device_error(ht)
+        if err:
+            raise SystemExit(f"device error: {err}")
+        tr = mk.mk_read_trace(ht, int(ex["header"]["n_tasks"]))
+        mk.mk_destroy(ht)
+        with open(args.trace, "w") as f:
+            f.write(trace_summary(tr, ex, f"Trace of one prompt launch: {out['config']['workload']}",
+                                  " ".join(["python"] + sys.argv)))
+        out["trace_summary"] = args.trace
+    if not args.no_cpu_baseline:
+        from oracle import prefill as oprefill
+        n = min(T, 128)
+        t0 = time.perf_counter()
+        oprefill.prefill(cfg, w, toks[:n], 0, kc.copy(), vc.copy())
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": round(n / dt, 2), "unit": "tokens/s", "cores": os.cpu_count(),
+                               "kind": "oracle", "sample": f"the oracle's double-precision prefill of the first "
+                                                           f"{n} prompt tokens (numpy matrix products)"}
+    del dev, model
+    print(json.dumps(out), flush=True)
+
+
 def bench_micro(mk):
     """The costs the megakernel trades against each other, measured on this GPU."""
     us_stream, us_graph = mk.mkm_launch_latency(2000)
@@ -527,6 +648,8 @@ def main():
     ap.add_argument("--batch", type=int, default=1,
                     help="sequences per step; above 1: the mixed-context batch workload (contexts uniform in "
                          "[256, 4096], room for 4352), reported in tokens/s")
+    ap.add_argument("--prefill", type=int, default=0, metavar="T",
+                    help="the prompt (prefill) megakernel on a T-token prompt instead of the decode step")
     ap.add_argument("--micro", action="store_true",
                     help="run the measurement microbenchmarks (launch latency, dependency hop, barrier, LDS fill, "
                          "streaming read) and print their JSON line instead of the step benchmark")
@@ -554,6 +677,8 @@ def main():
     import synth
     import persistent_megakernel_decode_cu_amd as mk
 
+    if args.prefill:
+        return bench_prefill(args, torch, synth, mk)
     if args.micro:
         return bench_micro(mk)
     if args.model == "8b" and args.batch > 1:

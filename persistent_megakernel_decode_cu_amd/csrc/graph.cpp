@@ -493,7 +493,7 @@ int plan_prefill_tiling(const Dims& dm, int Tn, int C, int W, Tiling* t, std::st
             if (N[op] % rows) continue;
             if (op == 2 && dm.f % (rows / 2)) continue;
             const int64_t page_cols = 32ll * pf_kbp(rows);
-            for (int S = 1; S <= (op == 1 || op == 3 ? 8 : 1); S *= 2) {
+            for (int S = 1; S <= (op == 1 || op == 3 ? PF_MAX_SLICES : 1); S *= 2) {
                 if (K[op] % (S * page_cols) || K[op] / S < 256) continue;
                 const int64_t tasks = N[op] / rows * ((Tn + 64 * ngw - 1) / (64 * ngw)) * S;
                 const int64_t pages = rows * (K[op] / S) * 2 / 16384;
@@ -541,12 +541,14 @@ int build_prefill_graph(const Tiling& T, const Layout& Ly, int sched, int policy
         k.sig_nsub = 1;
         return k;
     };
-    // RMSNorm tasks (kind 0: attention input, 1: FFN input) over every token group
+    // RMSNorm tasks of 4 tokens each (kind 0: attention input, 1: FFN input, 2: the final residual),
+    // which also add the previous projection's K-slice partials to the residual
+    const int nquads = (T.pf_T + 3) / 4;
     auto norms = [&](int l, int kind, uint32_t wait, uint32_t sig) {
-        for (int tg = 0; tg < ntg; ++tg) {
+        for (int q = 0; q < nquads; ++q) {
             Task k = blank(OP_PNORM, l, wait, sig);
             k.part = (uint16_t)kind;
-            k.seq = (uint32_t)tg;
+            k.seq = (uint32_t)q;
             add(k);
         }
     };
@@ -596,14 +598,9 @@ int build_prefill_graph(const Tiling& T, const Layout& Ly, int sched, int policy
         gemms(l, 3, Ly.down, ev_g, ev_d);
         ev_x = ev_d;
     }
-    // final RMSNorm of the last token, LM head + argmax
+    // the final residual of every token (the last one also normalised for the LM head), LM head + argmax
     const uint32_t ev_f = g.new_event();
-    {
-        Task k = blank(OP_PNORM, L, ev_x, ev_f);
-        k.part = 2;
-        k.seq = (uint32_t)((T.pf_T - 1) / 16);
-        add(k);
-    }
+    norms(L, 2, ev_x, ev_f);
     for (int t = 0; t < T.n_lm_tiles; ++t) {
         Task k = blank(OP_PLM, L, ev_f, NONE);
         k.row0 = (uint32_t)(t * T.lm_rows);

@@ -60,6 +60,11 @@ constexpr int MAX_INFLIGHT = MK_MAX_INFLIGHT;
 #define MK_ATTN_INFLIGHT MK_MAX_INFLIGHT
 #endif
 constexpr int ATTN_INFLIGHT = MK_ATTN_INFLIGHT;
+#ifndef MK_PF_INFLIGHT
+#define MK_PF_INFLIGHT 4
+#endif
+constexpr int PF_INFLIGHT = MK_PF_INFLIGHT;  // the prompt megakernel's loader depth
+static_assert(PF_INFLIGHT >= 1 && PF_INFLIGHT < NPAGES && LPP * PF_INFLIGHT <= 63, "vmcnt range");
 static_assert(ATTN_INFLIGHT >= 1 && ATTN_INFLIGHT <= NPAGES && LPP * ATTN_INFLIGHT <= 63, "vmcnt range");
 constexpr int DYNQ = 64;               // popped task ids shared between the loader waves (dynamic queue)
 constexpr int MAXB = 64;               // sequences per step held in LDS
@@ -663,6 +668,9 @@ typedef const __attribute__((address_space(4))) Task c_task;
 // dynamic queue, pops task ids and hands them to the other loader waves.  Every
 // wait first drains and publishes the loads in flight, so a page a consumer
 // waits for is never held back by a waiting loader.
+// INFL: pages in flight per loader wave before it waits for the oldest (the decode step: MAX_INFLIGHT;
+// the prompt megakernel's GEMM tiles consume pages faster and keep more in flight)
+template <int INFL>
 __device__ __noinline__ void loader(const Params* pp, uint32_t epoch, int lw) {
     CParams& p = P(pp);
     lw = (int)uni((uint32_t)lw);
@@ -795,9 +803,9 @@ __device__ __noinline__ void loader(const Params* pp, uint32_t epoch, int lw) {
                 lds_st(S.tl_issue1[fs], now);
             }
             ++pseq;
-            if constexpr (ATTN_INFLIGHT == MAX_INFLIGHT) {
-                if (pseq - pub == MAX_INFLIGHT) {
-                    vm_wait<LPP * (MAX_INFLIGHT - 1)>();
+            if constexpr (ATTN_INFLIGHT == INFL) {
+                if (pseq - pub == INFL) {
+                    vm_wait<LPP * (INFL - 1)>();
                     publish_one();
                 }
             } else if (k.op == OP_ATTN) {
@@ -805,10 +813,10 @@ __device__ __noinline__ void loader(const Params* pp, uint32_t epoch, int lw) {
                     vm_wait<LPP * (ATTN_INFLIGHT - 1)>();
                     while (pseq - pub > (uint32_t)ATTN_INFLIGHT - 1u) publish_one();
                 }
-            } else if (pseq - pub >= (uint32_t)MAX_INFLIGHT) {
-                // (after an attention task's deeper queue: every page but the newest MAX_INFLIGHT - 1)
-                vm_wait<LPP * (MAX_INFLIGHT - 1)>();
-                while (pseq - pub > (uint32_t)MAX_INFLIGHT - 1u) publish_one();
+            } else if (pseq - pub >= (uint32_t)INFL) {
+                // (after an attention task's deeper queue: every page but the newest INFL - 1)
+                vm_wait<LPP * (INFL - 1)>();
+                while (pseq - pub > (uint32_t)INFL - 1u) publish_one();
             }
         }
     }
@@ -2851,7 +2859,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) mk_step_kernel(const Params* pp, 
             for (size_t i = (size_t)blockIdx.x * NTHREADS + threadIdx.x; i < nt; i += (size_t)gridDim.x * NTHREADS)
                 p.aticket[(parity ^ 1u) * nt + i] = 0u;
         }
-        if (wave >= NCW) loader(pp, epoch, wave - NCW);
+        if (wave >= NCW) loader<MAX_INFLIGHT>(pp, epoch, wave - NCW);
         else compute<false>(pp, epoch, wave);
     }
     __syncthreads();
@@ -2912,7 +2920,7 @@ __global__ void __launch_bounds__(NTHREADS, 1) mk_prefill_kernel(const Params* p
     } else {
         // the other parity's argmax key, for the next launch (read only after this one)
         if (blockIdx.x == 0 && threadIdx.x == 0) p.key[parity ^ 1u] = 0ull;
-        if (wave >= NCW) loader(pp, epoch, wave - NCW);
+        if (wave >= NCW) loader<PF_INFLIGHT>(pp, epoch, wave - NCW);
         else compute<true>(pp, epoch, wave);
     }
     __syncthreads();

@@ -85,6 +85,7 @@ enum TaskFlags : uint8_t {
 // 16 KiB page holding every row of the tile over a 16 / (rows / 16) x 32-column stretch
 // of K, as 16 x 32 matrix-core blocks in (column block, row group) order.
 constexpr int PF_GEMMS = 4;  // QKV, O-proj, gate/up, down
+constexpr int PF_MAX_SLICES = 4;  // K slices of the O- and down projections (their partials meet in the RMSNorm tasks)
 constexpr int pf_kbp(int rows) { return 16 / (rows / 16); }  // 32-column blocks per page
 
 // Tiling of one model on W workgroups (computed once on the host).

@@ -10,8 +10,10 @@
 // of 64 or 128 tokens, streams its weight tile through the LDS pages once, and reads the
 // token operands (two bf16 parts per fp32 input, as the several-sequence decode path)
 // from L2.  Buffers of a prompt handle:
-//   p.acc  residual rows R_a [Tp][h] (after attention) and R_b [Tp][h] (after the FFN),
-//          fp32, Tp = T rounded up to 16; R_b after the last layer is the hidden output
+//   p.acc  residual rows, fp32 [Tp][h] each (Tp = T rounded up to 16): R_b the input of a layer
+//          (after the last layer: the hidden output), R_a after its attention; then the K-slice
+//          partial outputs of the O-projection [S_o][Tp][h] and of the down projection [S_d][Tp][h],
+//          which the next RMSNorm tasks add to the residual (no atomics)
 //   p.xop  matrix-core B operands in units of (token group of 16, 32-column block):
 //          [part][64 lanes][8 bf16] = 2 KiB, lane = token % 16 + 16 ((column % 32) / 8);
 //          X [ntg][h/32] normalised input of QKV or gate/up, O [ntg][nq d/32] attention
@@ -28,8 +30,14 @@ __device__ __forceinline__ uint16_t* pf_m(CParams& p) {
     return pf_o(p) + (size_t)pf_ntg(p) * (p.T.nq * p.T.d / 32) * 1024;
 }
 __device__ __forceinline__ uint16_t* pf_lm(CParams& p) { return pf_m(p) + (size_t)pf_ntg(p) * (p.T.f / 32) * 1024; }
+__device__ __forceinline__ size_t pf_rows(CParams& p) { return (size_t)pf_ntg(p) * 16 * p.T.h; }  // floats per [Tp][h]
 __device__ __forceinline__ float* pf_ra(CParams& p) { return p.acc; }
-__device__ __forceinline__ float* pf_rb(CParams& p) { return p.acc + (size_t)pf_ntg(p) * 16 * p.T.h; }
+__device__ __forceinline__ float* pf_rb(CParams& p) { return p.acc + pf_rows(p); }
+// K-slice partial outputs of the O-projection (slice s) and of the down projection
+__device__ __forceinline__ float* pf_po(CParams& p, int s) { return p.acc + (2 + (size_t)s) * pf_rows(p); }
+__device__ __forceinline__ float* pf_pd(CParams& p, int s) {
+    return p.acc + (2 + (size_t)p.T.pf_slices[1] + (size_t)s) * pf_rows(p);
+}
 
 // byte offset of (token group tg, column block kb, part pt, lane) in a region of nkb column blocks
 __device__ __forceinline__ uint32_t pf_unit(uint32_t tg, uint32_t nkb, uint32_t kb, uint32_t pt, uint32_t lane) {
@@ -47,12 +55,12 @@ __device__ __forceinline__ void st8_dev(__amdgpu_buffer_rsrc_t r, uint32_t off, 
     __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 16);
 }
 
-// RMSNorm of 16 tokens (kind 0: the attention input of layer l, 1: its FFN input, 2: the
-// final norm, of the last prompt token only).  Compute wave w takes tokens 16 tg + 4 w ..
-// + 3; a lane holds columns 512 j + 8 lane .. + 7.  Kind 0 carries the residual into R_a
-// (layer 0: the embedding rows), kind 1 into R_b, where the O-projection and down tiles
-// then add their outputs; the normalised rows go to the X (LM) operands.  Tokens past the
-// prompt write zero operands.
+// RMSNorm tasks of 4 tokens (compute wave w: token 4 q + w; a lane holds columns 512 j + 8 lane
+// .. + 7).  Each first completes the residual: kind 0 (the attention input of layer l) x = R_a +
+// the previous layer's down partials (layer 0: the embedding row) -> R_b; kind 1 (the FFN input)
+// x = R_b + this layer's O-projection partials -> R_a; kind 2 (after the last layer) x = R_a + the
+// down partials -> R_b, the hidden output.  Then x is normalised into the X operands (kind 2: of
+// the last prompt token only, into the LM operands).  Tokens past the prompt write zero operands.
 __device__ __noinline__ bool op_pnorm(const Params* pp, uint32_t slot_, uint32_t page0, uint32_t t_, uint32_t epoch_) {
     const Task k = fifo_task(slot_);
     Ctx c = make_ctx(t_, epoch_);
@@ -61,95 +69,123 @@ __device__ __noinline__ bool op_pnorm(const Params* pp, uint32_t slot_, uint32_t
     const int lane = c.lane, wave = c.wave;
     const int h = p.T.h, L = p.T.L, Tn = p.T.pf_T, l = k.layer, kind = k.part;
     const int nkb = h / 32, NJ = h / 512;
+    const int tok = (int)k.seq * 4 + wave;
+    const bool valid = tok < Tn;
     const uint16_t* gp = gains(p, kind == 0 ? 2 * l : kind == 1 ? 2 * l + 1 : 2 * L);
     uint4 gw[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
         if (j < NJ) gw[j] = gld_u4(gp + j * 512 + lane * 8);
     if (!await_inputs(pp, k, c)) return false;
-    const size_t rbytes = (size_t)pf_ntg(p) * 16 * h * 4;
+    const uint32_t rbytes = (uint32_t)(pf_rows(p) * 4);
+    // the residual so far and the partials to add (nsl of them, all [Tp][h])
+    const float* base = kind == 1 ? pf_rb(p) : pf_ra(p);
+    const int nsl = kind == 1 ? p.T.pf_slices[1] : p.T.pf_slices[3];
+    const float* part0 = kind == 1 ? pf_po(p, 0) : pf_pd(p, 0);
     const bool from_emb = kind == 0 && l == 0;
-    const __amdgpu_buffer_rsrc_t src = dev_rsrc(kind == 1 ? pf_ra(p) : pf_rb(p), (uint32_t)rbytes);
-    const __amdgpu_buffer_rsrc_t dst = dev_rsrc(kind == 0 ? pf_ra(p) : pf_rb(p), (uint32_t)rbytes);
-    const __amdgpu_buffer_rsrc_t reg =
-        dev_rsrc(kind == 2 ? pf_lm(p) : pf_x(p), (uint32_t)(kind == 2 ? 1 : pf_ntg(p)) * nkb * 2048u);
-    const uint16_t* emb = (const uint16_t*)(p.w + p.lay.embed);
-    for (int u = 0; u < 4; ++u) {
-        if (kind == 2 && (wave != 0 || u != 0)) break;
-        const int tok = kind == 2 ? Tn - 1 : (int)k.seq * 16 + 4 * wave + u;
-        const bool valid = tok < Tn;
-        float x[4][8];
+    float x[4][8];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[j][e] = 0.f;
-        if (valid) {
-            if (from_emb) {
-                const int id = gld(S.args.tokens + tok);
+        for (int e = 0; e < 8; ++e) x[j][e] = 0.f;
+    if (valid) {
+        if (from_emb) {
+            const int id = gld(S.args.tokens + tok);
+            const uint16_t* emb = (const uint16_t*)(p.w + p.lay.embed) + (size_t)id * h;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    if (j >= NJ) break;
-                    const uint4 v = gld_u4(emb + (size_t)id * h + j * 512 + lane * 8);
-                    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+            for (int j = 0; j < 4; ++j) {
+                if (j >= NJ) break;
+                const uint4 v = gld_u4(emb + j * 512 + lane * 8);
+                const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        x[j][2 * e] = bf16lo(w4[e]);
-                        x[j][2 * e + 1] = bf16hi(w4[e]);
+                for (int e = 0; e < 4; ++e) {
+                    x[j][2 * e] = bf16lo(w4[e]);
+                    x[j][2 * e + 1] = bf16hi(w4[e]);
+                }
+            }
+        } else {
+            // the residual and up to PF_MAX_SLICES partials, added in slice order; each half of the
+            // row's columns with all of its loads in flight at once
+#pragma unroll
+            for (int jh = 0; jh < 2; ++jh) {
+                if (2 * jh >= NJ) break;
+                u32x4 a[PF_MAX_SLICES + 1][2], b[PF_MAX_SLICES + 1][2];
+#pragma unroll
+                for (int q = 0; q <= PF_MAX_SLICES; ++q) {
+                    if (q > nsl) break;
+                    const __amdgpu_buffer_rsrc_t r =
+                        dev_rsrc(q == 0 ? base : part0 + (size_t)(q - 1) * pf_rows(p), rbytes);
+#pragma unroll
+                    for (int jj = 0; jj < 2; ++jj) {
+                        const int j = 2 * jh + jj;
+                        if (j >= NJ) break;
+                        const uint32_t off = (uint32_t)(tok * h + j * 512 + lane * 8) * 4u;
+                        a[q][jj] = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 16);
+                        b[q][jj] = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 16);
                     }
                 }
-            } else {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    if (j >= NJ) break;
-                    const uint32_t off = (uint32_t)(tok * h + j * 512 + lane * 8) * 4u;
-                    const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(src, off, 0, 16);
-                    const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(src, off + 16, 0, 16);
+                for (int q = 0; q <= PF_MAX_SLICES; ++q) {
+                    if (q > nsl) break;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        x[j][e] = __uint_as_float(a[e]);
-                        x[j][4 + e] = __uint_as_float(b[e]);
+                    for (int jj = 0; jj < 2; ++jj) {
+                        const int j = 2 * jh + jj;
+                        if (j >= NJ) break;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            x[j][e] += __uint_as_float(a[q][jj][e]);
+                            x[j][4 + e] += __uint_as_float(b[q][jj][e]);
+                        }
                     }
                 }
             }
         }
-        float ss = 0.f;
+    }
+    float ss = 0.f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) ss = fmaf(x[j][e], x[j][e], ss);
-        ss = wave_sum(ss);
-        const float rs = 1.0f / sqrtf(ss / (float)h + p.eps);
-        const int tg = kind == 2 ? 0 : tok / 16, n = kind == 2 ? 0 : tok % 16;
+        for (int e = 0; e < 8; ++e) ss = fmaf(x[j][e], x[j][e], ss);
+    ss = wave_sum(ss);
+    const float rs = 1.0f / sqrtf(ss / (float)h + p.eps);
+    // the completed residual
+    const __amdgpu_buffer_rsrc_t dst = dev_rsrc(kind == 1 ? pf_ra(p) : pf_rb(p), rbytes);
+    if (valid) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             if (j >= NJ) break;
-            const int c0 = j * 512 + lane * 8;
-            if (valid && kind != 2) {
-                const uint32_t off = (uint32_t)(tok * h + c0) * 4u;
-                __builtin_amdgcn_raw_buffer_store_b128(
-                    u32x4{__float_as_uint(x[j][0]), __float_as_uint(x[j][1]), __float_as_uint(x[j][2]),
-                          __float_as_uint(x[j][3])},
-                    dst, off, 0, 16);
-                __builtin_amdgcn_raw_buffer_store_b128(
-                    u32x4{__float_as_uint(x[j][4]), __float_as_uint(x[j][5]), __float_as_uint(x[j][6]),
-                          __float_as_uint(x[j][7])},
-                    dst, off + 16, 0, 16);
-            }
-            const uint32_t g4[4] = {gw[j].x, gw[j].y, gw[j].z, gw[j].w};
-            float y[8];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                y[2 * e] = x[j][2 * e] * rs * bf16lo(g4[e]);
-                y[2 * e + 1] = x[j][2 * e + 1] * rs * bf16hi(g4[e]);
-            }
-            u32x4v hi, lo;
-            split8(y, hi, lo);
-            const uint32_t ln = (uint32_t)(n + 16 * ((c0 % 32) / 8));
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, hi), reg,
-                                                   pf_unit((uint32_t)tg, (uint32_t)nkb, (uint32_t)(c0 / 32), 0, ln), 0, 16);
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, lo), reg,
-                                                   pf_unit((uint32_t)tg, (uint32_t)nkb, (uint32_t)(c0 / 32), 1, ln), 0, 16);
+            const uint32_t off = (uint32_t)(tok * h + j * 512 + lane * 8) * 4u;
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4{__float_as_uint(x[j][0]), __float_as_uint(x[j][1]),
+                                                         __float_as_uint(x[j][2]), __float_as_uint(x[j][3])},
+                                                   dst, off, 0, 16);
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4{__float_as_uint(x[j][4]), __float_as_uint(x[j][5]),
+                                                         __float_as_uint(x[j][6]), __float_as_uint(x[j][7])},
+                                                   dst, off + 16, 0, 16);
         }
+    }
+    // the normalised row as matrix-core operands
+    if (kind == 2 && tok != Tn - 1) return true;
+    const int tg = kind == 2 ? 0 : tok / 16, n = kind == 2 ? 0 : tok % 16;
+    const __amdgpu_buffer_rsrc_t reg =
+        dev_rsrc(kind == 2 ? pf_lm(p) : pf_x(p), (uint32_t)(kind == 2 ? 1 : pf_ntg(p)) * nkb * 2048u);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        if (j >= NJ) break;
+        const int c0 = j * 512 + lane * 8;
+        const uint32_t g4[4] = {gw[j].x, gw[j].y, gw[j].z, gw[j].w};
+        float y[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            y[2 * e] = x[j][2 * e] * rs * bf16lo(g4[e]);
+            y[2 * e + 1] = x[j][2 * e + 1] * rs * bf16hi(g4[e]);
+        }
+        u32x4v hi, lo;
+        split8(y, hi, lo);
+        const uint32_t ln = (uint32_t)(n + 16 * ((c0 % 32) / 8));
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, hi), reg,
+                                               pf_unit((uint32_t)tg, (uint32_t)nkb, (uint32_t)(c0 / 32), 0, ln), 0, 16);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, lo), reg,
+                                               pf_unit((uint32_t)tg, (uint32_t)nkb, (uint32_t)(c0 / 32), 1, ln), 0, 16);
     }
     return true;
 }
@@ -196,10 +232,10 @@ __device__ __noinline__ bool op_pgemm(const Params* pp, uint32_t slot_, uint32_t
                                             (uint32_t)pt, (uint32_t)lane),
                                     0, 16));
     };
-    // one page: the next page's B operands are issued first (in flight during the products);
-    // the page's A blocks are read one column block at a time
+    // one page: the B operands of the page after next are issued first (two pages of loads stay in
+    // flight during the products); the page's A blocks are read one column block at a time
     auto page = [&](uint32_t s, const u32x4v (&bc)[NGW][KBP][NPART], u32x4v (&bn)[NGW][KBP][NPART]) -> bool {
-        if (s + 1 < npages) load_b(bn, s + 1);
+        if (s + 2 < npages) load_b(bn, s + 2);
         if (!page_acquire(pp, page0 + s, k.id)) return false;
         const uint32_t slot = (page0 + s) % NPAGES;
 #pragma unroll
@@ -220,11 +256,13 @@ __device__ __noinline__ bool op_pgemm(const Params* pp, uint32_t slot_, uint32_t
         page_release(page0 + s, lane);
         return true;
     };
-    u32x4v b0[NGW][KBP][NPART], b1[NGW][KBP][NPART];
+    u32x4v b0[NGW][KBP][NPART], b1[NGW][KBP][NPART], b2[NGW][KBP][NPART];
     load_b(b0, 0);
-    for (uint32_t s = 0; s < npages; s += 2) {
-        if (!page(s, b0, b1)) return false;
+    if (npages > 1) load_b(b1, 1);
+    for (uint32_t s = 0; s < npages; s += 3) {
+        if (!page(s, b0, b2)) return false;
         if (s + 1 < npages && !page(s + 1, b1, b0)) return false;
+        if (s + 2 < npages && !page(s + 2, b2, b1)) return false;
     }
     tmark(c, 1);
     const int32_t pos0 = (int32_t)uni((uint32_t)S.args.pos0);
@@ -303,13 +341,16 @@ __device__ __noinline__ bool op_pgemm(const Params* pp, uint32_t slot_, uint32_t
                 st8_dev(mr, pf_unit((uint32_t)tg, (uint32_t)nkm, (uint32_t)(mrow / 32), 1, ln) + e0, ml);
             }
         } else {
-            // O-projection / down: add to the residual rows (R_a / R_b) of the prompt's tokens
+            // O-projection / down: this K slice's partial rows of the prompt's tokens (the next RMSNorm
+            // tasks add the slices to the residual)
             if (tok >= Tn) continue;
-            float* dst = (OPK == OP_POPROJ ? pf_ra(p) : pf_rb(p)) + (size_t)tok * h + k.row0;
+            const __amdgpu_buffer_rsrc_t pr =
+                dev_rsrc(OPK == OP_POPROJ ? pf_po(p, k.part) : pf_pd(p, k.part), (uint32_t)(pf_rows(p) * 4));
 #pragma unroll
             for (int rg = 0; rg < RG; ++rg)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) addf_dev(dst + 16 * rg + 4 * kq + i, acc[rg][j][i]);
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    __builtin_bit_cast(u32x4, acc[rg][j]), pr,
+                    (uint32_t)((size_t)tok * h + k.row0 + 16 * rg + 4 * kq) * 4u, 0, 16);
         }
     }
     return true;

@@ -428,15 +428,15 @@ mk_status build_handle(const mk_model_desc* desc, int32_t batch, int32_t max_ctx
     ALLOC(rope, (size_t)T.C * half * sizeof(float2), false);
     p.rope = rope;
     if (prompt) {
-        // prompt buffers: query operands, residual rows after attention and after the FFN, and the
-        // matrix-core operand regions (normalised inputs, attention output, SiLU(gate) * up, final
+        // prompt buffers: query operands, the residual rows (input of a layer, after its attention) and
+        // the K-slice partial outputs of the O- and down projections, and the matrix-core operand regions (normalised inputs, attention output, SiLU(gate) * up, final
         // normalised last token), all zero at first (the columns of the tokens past the prompt in its
         // last group of 16 stay zero or finite)
         const size_t ntg = (size_t)(T.pf_T + 15) / 16;
         ALLOC(p.q, ntg * T.nq * (T.d / 32) * 2048, true);
         ALLOC(p.part, 256, true);
         ALLOC(p.m, 256, true);
-        h->acc_bytes = 2 * ntg * 16 * T.h * 4;
+        h->acc_bytes = (2 + (size_t)T.pf_slices[1] + (size_t)T.pf_slices[3]) * ntg * 16 * T.h * 4;
         ALLOC(p.acc, h->acc_bytes, true);
         h->xop_bytes = (ntg * ((size_t)T.h + (size_t)T.nq * T.d + (size_t)T.f) + T.h) / 32 * 2048;
         ALLOC(p.xop, h->xop_bytes, true);

@@ -18,29 +18,38 @@ from oracle import prefill as oprefill
 pytestmark = pytest.mark.gpu
 
 CFG = synth.configs.TINY_PF
-# K/V bar, as for the decode step's batched path (tests/test_gpu_batch.py): the projections carry
-# each fp32 input as two bf16 parts, so a projected value is off by up to about 2^-16 sum_i
-# |w_i x_i| before its bf16 rounding; allowed: one bf16 ulp of the oracle's value plus 2^-10 of
-# the head vector's largest magnitude.  A slot whose context is shorter than SHORT_CONTEXT
-# positions passes its V through attention almost unaveraged, so a rounding the device takes
-# the other way moves the next layers by up to an ulp; such slots are held to the bound at
-# layer 0 only.
+# K/V bar.  Layer 0 (whose K/V depend on the token and the layer's weights only): as for the decode
+# step's batched path (tests/test_gpu_batch.py), one bf16 ulp of the oracle's value plus 2^-10 of the
+# head vector's largest magnitude (the projections carry each fp32 input as two bf16 parts, so a
+# projected value is off by up to about 2^-16 sum_i |w_i x_i| before its rounding).  Deeper layers:
+# a prompt's contexts are short, so each K/V rounding that the device takes the other way from the
+# oracle passes almost unaveraged into the next layers, and the prompt amplifies it: the oracle itself,
+# run with the prompt's K/V unrounded instead of rounded (a perturbation of at most half an ulp), keeps
+# only 23-42 % of the deeper layers' K bit-exact and moves the final residual by 0.75 % (median) at the
+# Llama-1B shape with 128 tokens.  There the K/V of each layer are held, as a whole, to the relative
+# error of the residual (TOL_HIDDEN_REL), and every token's residual and the logits to the decode bars.
 KV_HEAD_REL = 2.0 ** -10
-SHORT_CONTEXT = 16
 
 
-def check_kv_slots(got, want, positions, label):
-    """got/want: uint16 [L][1][nkv][C][d]; every listed slot within the bound above."""
-    for P in positions:
-        nl = 1 if P + 1 < SHORT_CONTEXT else want.shape[0]
-        r = oracle.bf16_to_f64(want[:nl, 0, :, P])
-        g = oracle.bf16_to_f64(got[:nl, 0, :, P])
-        head_max = np.abs(r).max(axis=2, keepdims=True)
-        bad = np.argwhere(np.abs(g - r) > np.abs(r) * 2.0 ** -7 + KV_HEAD_REL * head_max + 1e-30)
-        for i in bad[:4]:
-            t = tuple(i)
-            print(f"{label} pos {P} (layer, group, dim) {t}: oracle {r[t]!r} gpu {g[t]!r}", flush=True)
-        assert len(bad) == 0, (label, P, len(bad))
+def check_kv_slots(got, want, positions, label, layers=1):
+    """got/want: uint16 [L][1][nkv][C][d].  Layer 0 of every listed slot within the tight bound; each
+    of the first `layers` layers within TOL_HIDDEN_REL relative error (L2 over the listed slots)."""
+    pos = np.asarray(list(positions))
+    r = oracle.bf16_to_f64(want[:1, 0][:, :, pos])
+    g = oracle.bf16_to_f64(got[:1, 0][:, :, pos])
+    head_max = np.abs(r).max(axis=3, keepdims=True)
+    bad = np.argwhere(np.abs(g - r) > np.abs(r) * 2.0 ** -7 + KV_HEAD_REL * head_max + 1e-30)
+    for i in bad[:4]:
+        t = tuple(i)
+        print(f"{label} layer 0 (group, slot, dim) {t[1:]}: oracle {r[t]!r} gpu {g[t]!r}", flush=True)
+    assert len(bad) == 0, (label, len(bad))
+    for l in range(layers):
+        r = oracle.bf16_to_f64(want[l, 0][:, pos])
+        g = oracle.bf16_to_f64(got[l, 0][:, pos])
+        rel = float(np.linalg.norm(g - r) / np.linalg.norm(r))
+        if l in (0, layers - 1):
+            print(f"{label} layer {l}: relative error {rel:.3g}, bit-exact {float((g == r).mean()):.4f}", flush=True)
+        assert rel <= TOL_HIDDEN_REL, (label, l, rel)
 
 
 class Prompt:
@@ -89,9 +98,7 @@ def check_prompt(cfg, run, toks, pos0, kc, vc, ref, kk, vv, label):
     gk, gv = kv_to_host(run.kv, run.shape)
     sl = slice(pos0, pos0 + T)
     for name, got, want, orig in (("K", gk, kk, kc), ("V", gv, vv, vc)):
-        exact = float((got[:, :, :, sl] == want[:, :, :, sl]).mean())
-        print(f"{label} {name}: bit-exact fraction {exact:.4f}", flush=True)
-        check_kv_slots(got, want, range(pos0, pos0 + T), f"{label} {name}")
+        check_kv_slots(got, want, range(pos0, pos0 + T), f"{label} {name}", layers=cfg.n_layers)
         # slots outside the prompt untouched
         mask = np.ones(got.shape[3], bool)
         mask[sl] = False
@@ -268,7 +275,7 @@ def test_llama1b_prompt_1024_against_sampled_outputs(weights1b):
     kk, vv = kc.copy(), vc.copy()
     ref = oprefill.prefill(CFG1B, weights1b, toks[:128], 0, kk, vv)
     for name, got, want in (("K", gk, kk), ("V", gv, vv)):
-        check_kv_slots(got, want, range(128), f"first 128 {name}")
+        check_kv_slots(got, want, range(128), f"first 128 {name}", layers=CFG1B.n_layers)
     rel = np.linalg.norm(hid[:128] - ref["hidden"], axis=1) / np.linalg.norm(ref["hidden"], axis=1)
     print(f"first 128 hidden rel max {rel.max():.3g}", flush=True)
     assert rel.max() <= TOL_HIDDEN_REL
