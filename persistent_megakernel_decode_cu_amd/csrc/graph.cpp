@@ -463,11 +463,11 @@ int plan_prefill_tiling(const Dims& dm, int Tn, int C, int W, Tiling* t, std::st
         if (unsupported) *unsupported = unsup;
         return -1;
     };
+    if (dm.n_experts) return fail("the prompt megakernel covers dense models", true);
     if (dm.L < 1 || dm.h <= 0 || dm.nq <= 0 || dm.nkv <= 0 || dm.d <= 0 || dm.V <= 0 || dm.f <= 0)
         return fail("non-positive model dimension");
     if (Tn < 1 || C < Tn || W < 1) return fail("1 <= prompt tokens <= max_ctx and workgroups >= 1");
     if (dm.nq % dm.nkv) return fail("n_q_heads must be a multiple of n_kv_heads");
-    if (dm.n_experts) return fail("the prompt megakernel covers dense models", true);
     if (dm.d != 64) return fail("the prompt attention tiles are written for head_dim 64", true);
     if (dm.h % 512 || dm.h > 2048) return fail("the prompt graph needs hidden a multiple of 512, at most 2048", true);
     if (dm.f % 128 || (dm.nq * dm.d) % 128) return fail("ffn_dim and n_q*head_dim must be multiples of 128", true);
@@ -490,6 +490,9 @@ int plan_prefill_tiling(const Dims& dm, int Tn, int C, int W, Tiling* t, std::st
         const int shapes[3][2] = {{128, 2}, {128, 1}, {64, 1}};
         for (const auto& sh : shapes) {
             const int rows = sh[0], ngw = sh[1];
+#ifdef MK_PF_ONLY_SHAPE  // (tuning builds: one tile shape only, 0, 1 or 2 of the list)
+            if (&sh != &shapes[MK_PF_ONLY_SHAPE]) continue;
+#endif
             if (N[op] % rows) continue;
             if (op == 2 && dm.f % (rows / 2)) continue;
             const int64_t page_cols = 32ll * pf_kbp(rows);
@@ -552,9 +555,10 @@ int build_prefill_graph(const Tiling& T, const Layout& Ly, int sched, int policy
             add(k);
         }
     };
-    // GEMM tiles of projection `op`: token blocks outermost, so that a tile's token blocks
-    // land on workgroups a multiple of 8 apart (the same XCD, when the row tiles number a
-    // multiple of 8) and read its weights through one L2
+    // GEMM tiles of projection `op`, listed tile by tile (a tile's K slices and token blocks together)
+    // and placed so that, under round-robin queues, each run of W/8 consecutive tiles-and-blocks falls
+    // on the workgroups of one XCD in the same round (workgroup w runs on XCD w mod 8): the token
+    // blocks of one weight tile run at the same time on one XCD and read its weights through one L2
     const uint8_t opc[PF_GEMMS] = {OP_PQKV, OP_POPROJ, OP_PGU, OP_PDOWN};
     const int64_t N[PF_GEMMS] = {(int64_t)(T.nq + 2 * T.nkv) * T.d, T.h, 2ll * T.f, T.h};
     const int64_t K[PF_GEMMS] = {T.h, (int64_t)T.nq * T.d, T.h, T.f};
@@ -563,9 +567,10 @@ int build_prefill_graph(const Tiling& T, const Layout& Ly, int sched, int policy
         const int ntb = (T.pf_T + 64 * ngw - 1) / (64 * ngw);
         const int64_t nrt = N[op] / rows;
         const uint32_t wbytes = (uint32_t)(rows * (K[op] / S) * 2);
-        for (int tb = 0; tb < ntb; ++tb)
+        std::vector<Task> list;
+        for (int64_t r = 0; r < nrt; ++r)
             for (int s = 0; s < S; ++s)
-                for (int64_t r = 0; r < nrt; ++r) {
+                for (int tb = 0; tb < ntb; ++tb) {
                     Task k = blank(opc[op], l, wait, sig);
                     k.part = (uint16_t)s;
                     k.row0 = (uint32_t)(op == 2 ? r * rows / 2 : r * rows);  // gate/up: the first m row
@@ -574,8 +579,21 @@ int build_prefill_graph(const Tiling& T, const Layout& Ly, int sched, int policy
                     k.flags = ngw == 2 ? TF_NGW2 : 0;
                     k.wbytes = wbytes;
                     k.wofs = Ly.layer0 + (uint64_t)l * Ly.layer_bytes + region + ((uint64_t)s * nrt + r) * wbytes;
-                    add(k);
+                    list.push_back(k);
                 }
+        const size_t n = list.size(), Wn = (size_t)T.W;
+        if (Wn % 8 == 0) {
+            // round r holds m = min(W, n - r W) tasks; when m is a multiple of 8, its i-th task goes to
+            // XCD i / (m / 8), slot i mod (m / 8), i.e. position 8 slot + XCD of the round
+            std::vector<Task> placed(list);
+            for (size_t r0 = 0; r0 < n; r0 += Wn) {
+                const size_t m = std::min(Wn, n - r0), G = m / 8;
+                if (m % 8) continue;
+                for (size_t i = 0; i < m; ++i) placed[r0 + 8 * (i % G) + i / G] = list[r0 + i];
+            }
+            list.swap(placed);
+        }
+        for (const Task& k : list) add(k);
     };
     uint32_t ev_x = NONE;
     for (int l = 0; l < L; ++l) {

@@ -61,7 +61,7 @@ constexpr int MAX_INFLIGHT = MK_MAX_INFLIGHT;
 #endif
 constexpr int ATTN_INFLIGHT = MK_ATTN_INFLIGHT;
 #ifndef MK_PF_INFLIGHT
-#define MK_PF_INFLIGHT 4
+#define MK_PF_INFLIGHT 6
 #endif
 constexpr int PF_INFLIGHT = MK_PF_INFLIGHT;  // the prompt megakernel's loader depth
 static_assert(PF_INFLIGHT >= 1 && PF_INFLIGHT < NPAGES && LPP * PF_INFLIGHT <= 63, "vmcnt range");

@@ -77,6 +77,7 @@ __device__ __noinline__ bool op_pnorm(const Params* pp, uint32_t slot_, uint32_t
     for (int j = 0; j < 4; ++j)
         if (j < NJ) gw[j] = gld_u4(gp + j * 512 + lane * 8);
     if (!await_inputs(pp, k, c)) return false;
+    tmark(c, 0);
     const uint32_t rbytes = (uint32_t)(pf_rows(p) * 4);
     // the residual so far and the partials to add (nsl of them, all [Tp][h])
     const float* base = kind == 1 ? pf_rb(p) : pf_ra(p);
@@ -147,6 +148,7 @@ __device__ __noinline__ bool op_pnorm(const Params* pp, uint32_t slot_, uint32_t
 #pragma unroll
         for (int e = 0; e < 8; ++e) ss = fmaf(x[j][e], x[j][e], ss);
     ss = wave_sum(ss);
+    tmark(c, 1);
     const float rs = 1.0f / sqrtf(ss / (float)h + p.eps);
     // the completed residual
     const __amdgpu_buffer_rsrc_t dst = dev_rsrc(kind == 1 ? pf_ra(p) : pf_rb(p), rbytes);
@@ -212,6 +214,8 @@ __device__ __noinline__ bool op_pgemm(const Params* pp, uint32_t slot_, uint32_t
     const uint32_t kb0 = k.part * npages * KBP;  // first column block of this K slice
     const int tgw = (int)k.seq * 4 * NGW + wave;  // this wave's first token group (then + 4)
     if (!await_inputs(pp, k, c)) return false;
+    tmark(c, 0);
+    const bool trace_pages = wave == 0 && c.tr;
     f32x4v acc[RG][NGW];
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg)
@@ -233,22 +237,26 @@ __device__ __noinline__ bool op_pgemm(const Params* pp, uint32_t slot_, uint32_t
                                     0, 16));
     };
     // one page: the B operands of the page after next are issued first (two pages of loads stay in
-    // flight during the products); the page's A blocks are read one column block at a time
+    // flight during the products); the page's A blocks are read one column block at a time.  The
+    // prefetch is unconditional (past the last page it reads other columns of the region, or zeros
+    // past its end, never used): a conditional one would make the compiler wait for every load.
     auto page = [&](uint32_t s, const u32x4v (&bc)[NGW][KBP][NPART], u32x4v (&bn)[NGW][KBP][NPART]) -> bool {
-        if (s + 2 < npages) load_b(bn, s + 2);
-        if (!page_acquire(pp, page0 + s, k.id)) return false;
+        load_b(bn, s + 2);
+        if (!page_acquire_tr(pp, page0 + s, k.id, trace_pages, lane)) return false;
+        if (trace_pages && lane == 0) lds_st(S.tm[2], (uint32_t)rtc());
         const uint32_t slot = (page0 + s) % NPAGES;
 #pragma unroll
         for (int kb = 0; kb < KBP; ++kb) {
             u32x4v a[RG];
 #pragma unroll
             for (int rg = 0; rg < RG; ++rg) a[rg] = *(const u32x4v*)&ring[slot][(kb * RG + rg) * 1024 + lane * 16];
+            // parts outermost: an accumulator's consecutive products are RG * NGW issues apart
 #pragma unroll
-            for (int rg = 0; rg < RG; ++rg)
+            for (int pt = 0; pt < NPART; ++pt)
 #pragma unroll
-                for (int j = 0; j < NGW; ++j)
+                for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
-                    for (int pt = 0; pt < NPART; ++pt)
+                    for (int j = 0; j < NGW; ++j)
                         acc[rg][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                             __builtin_bit_cast(bf16x8v, a[rg]), __builtin_bit_cast(bf16x8v, bc[j][kb][pt]),
                             acc[rg][j], 0, 0, 0);
@@ -258,7 +266,7 @@ __device__ __noinline__ bool op_pgemm(const Params* pp, uint32_t slot_, uint32_t
     };
     u32x4v b0[NGW][KBP][NPART], b1[NGW][KBP][NPART], b2[NGW][KBP][NPART];
     load_b(b0, 0);
-    if (npages > 1) load_b(b1, 1);
+    load_b(b1, 1);
     for (uint32_t s = 0; s < npages; s += 3) {
         if (!page(s, b0, b2)) return false;
         if (s + 1 < npages && !page(s + 1, b1, b0)) return false;
@@ -374,6 +382,7 @@ __device__ __noinline__ bool op_pattn(const Params* pp, uint32_t slot_, uint32_t
     const int ntg = pf_ntg(p);
     const int32_t pos0 = (int32_t)uni((uint32_t)S.args.pos0);
     if (!await_inputs(pp, k, c)) return false;
+    tmark(c, 0);
     const int32_t kmax = pos0 + min(16 * qg + 15, Tn - 1);  // the last key any query of the group sees
     const int nblk = kmax / 16 + 1;
     const int32_t qpos = pos0 + 16 * qg + n;  // this lane's query position
@@ -398,21 +407,28 @@ __device__ __noinline__ bool op_pattn(const Params* pp, uint32_t slot_, uint32_t
 #pragma unroll
         for (int t = 0; t < 4; ++t) oacc[t] = f32x4v{0.f, 0.f, 0.f, 0.f};
         float M = -INFINITY, Lp = 0.f;
-        for (int kb = 0; kb < nblk; ++kb) {
-            // K rows 16 kb + n (A operand: dimensions 32 ks + 8 kq ..), V words of keys 16 kb + 4 kq + jj,
-            // dimensions 4 n .. 4 n + 3; rows past kmax are read as row kmax (masked below)
+        // K rows 16 kb + n (A operand: dimensions 32 ks + 8 kq ..), V words of keys 16 kb + 4 kq + jj,
+        // dimensions 4 n .. 4 n + 3; rows past kmax are read as row kmax (masked below).  The next key
+        // block's loads are issued before the current one's products.
+        auto load_kv = [&](int kb, u32x4v (&ka)[2], u32x2v (&vw)[4]) {
             const uint32_t krow = (uint32_t)min(16 * kb + n, kmax);
-            u32x4v ka[2];
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
                 ka[ks] = __builtin_bit_cast(
                     u32x4v, __builtin_amdgcn_raw_buffer_load_b128(kr, (krow * D + 32 * ks + 8 * kq) * 2u, 0, 16));
-            u32x2v vw[4];
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
                 const uint32_t vrow = (uint32_t)min(16 * kb + 4 * kq + jj, kmax);
                 vw[jj] = __builtin_amdgcn_raw_buffer_load_b64(vr, (vrow * D + 4 * n) * 2u, 0, 16);
             }
+        };
+        u32x4v kan[2];
+        u32x2v vwn[4];
+        load_kv(0, kan, vwn);
+        for (int kb = 0; kb < nblk; ++kb) {
+            u32x4v ka[2] = {kan[0], kan[1]};
+            u32x2v vw[4] = {vwn[0], vwn[1], vwn[2], vwn[3]};
+            load_kv(kb + 1, kan, vwn);  // (unconditional: rows past kmax read row kmax, unused)
             f32x4v s = f32x4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
@@ -457,6 +473,7 @@ __device__ __noinline__ bool op_pattn(const Params* pp, uint32_t slot_, uint32_t
                 oacc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, __builtin_bit_cast(s16x4v, pl), oacc[t], 0, 0, 0);
             }
         }
+        if (hh == wave) tmark(c, 1);
         float Lt = Lp + __shfl_xor(Lp, 16, 64);
         Lt += __shfl_xor(Lt, 32, 64);
         const float inv = 1.0f / Lt;
