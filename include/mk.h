@@ -109,11 +109,11 @@ typedef struct {
 /* Validates the description, copies the weights into a handle-owned packed
  * layout (the caller may free its copies afterwards), builds the task graph,
  * the event targets and the queues, and uploads them to the current device.
- * 1 <= batch <= 32 sequences (batch > 1 also needs hidden <= 2048; the
+ * 1 <= batch <= 64 sequences (batch > 1 also needs hidden <= 2048; the
  * projections of up to 16 sequences share one pass over the weights, so
- * 17..32 sequences take two); max_ctx >= 1 positions per sequence in the KV
+ * 17..32 sequences take two, 33..64 up to four); max_ctx >= 1 positions per sequence in the KV
  * cache.  Errors: MK_E_INVALID (NULL pointers, unsupported shapes, bad options),
- * MK_E_UNSUPPORTED (batch > 32; batch > 1, or a mixture of experts, with
+ * MK_E_UNSUPPORTED (batch > 64; batch > 1, or a mixture of experts, with
  * hidden > 2048), MK_E_NO_DEVICE, MK_E_NOMEM, MK_E_HIP.  On success *out
  * receives the handle.  Defined by: the task graph built once on the host and
  * reused for every forward (Hazy Research megakernel news page, section 4,
@@ -292,7 +292,7 @@ const char *mk_status_str(mk_status s);
  * RMSNorm, LM head, argmax), for comparison: the execution model the Hazy
  * Research megakernel news page (section 3) contrasts the megakernel with.
  * Same inputs, layouts and arithmetic as the megakernel; reads the caller's
- * weights in place (no copy), so they must outlive the handle.  batch 1..32,
+ * weights in place (no copy), so they must outlive the handle.  batch 1..64,
  * dense models only, n_q_heads / n_kv_heads <= 8.  batch 1: hidden,
  * n_q*head_dim and ffn_dim must be powers of two in [512, 8192] (vector-ALU
  * GEMVs).  batch > 1: the projections run on the matrix cores with each fp32
@@ -304,7 +304,7 @@ const char *mk_status_str(mk_status s);
 typedef struct mkb_handle mkb_handle;
 
 /* Validates the description against the limits above and allocates the baseline's activation buffers
- * (the weights are read in place).  Errors: MK_E_INVALID (NULL pointers, batch outside 1..32, a mixture
+ * (the weights are read in place).  Errors: MK_E_INVALID (NULL pointers, batch outside 1..64, a mixture
  * of experts, head_dim other than 64 or 128), MK_E_UNSUPPORTED (projection shapes outside the limits
  * above), MK_E_NOMEM, MK_E_HIP.  (One kernel per
  * operator, a launch boundary as the only synchronisation: Hazy Research megakernel news page, section 3.) */

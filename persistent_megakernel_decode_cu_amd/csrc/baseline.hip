@@ -559,12 +559,16 @@ static int project_b(mkb_handle* hb, const uint16_t* const* W, const int* rows, 
     a.X = X;
     a.out = out;
     const dim3 grid((p.waves + 3) / 4), blk(256);
-    const bool two = hb->B > 16;
+    // column groups of 16 sequences per wave: 1, 2 or 4 (33..64 sequences; a third group's
+    // columns past the last sequence read a valid row and are not stored)
+    const int ng = hb->B > 32 ? 4 : hb->B > 16 ? 2 : 1;
     if (p.RG == 4) {
-        if (two) hipLaunchKernelGGL((k_gemm_b<4, 2, 2>), grid, blk, 0, s, a);
+        if (ng == 4) hipLaunchKernelGGL((k_gemm_b<4, 4, 1>), grid, blk, 0, s, a);
+        else if (ng == 2) hipLaunchKernelGGL((k_gemm_b<4, 2, 2>), grid, blk, 0, s, a);
         else hipLaunchKernelGGL((k_gemm_b<4, 1, 4>), grid, blk, 0, s, a);
     } else {
-        if (two) hipLaunchKernelGGL((k_gemm_b<1, 2, 4>), grid, blk, 0, s, a);
+        if (ng == 4) hipLaunchKernelGGL((k_gemm_b<1, 4, 2>), grid, blk, 0, s, a);
+        else if (ng == 2) hipLaunchKernelGGL((k_gemm_b<1, 2, 4>), grid, blk, 0, s, a);
         else hipLaunchKernelGGL((k_gemm_b<1, 1, 8>), grid, blk, 0, s, a);
     }
     hb->launches += 1;
@@ -574,7 +578,7 @@ static int project_b(mkb_handle* hb, const uint16_t* const* W, const int* rows, 
 extern "C" {
 
 mk_status mkb_create(const mk_model_desc* d, int32_t batch, int32_t max_ctx, mkb_handle** out) {
-    if (!d || !out || batch < 1 || batch > 32 || max_ctx < 1 || d->n_experts != 0 || !d->layers) return MK_E_INVALID;
+    if (!d || !out || batch < 1 || batch > 64 || max_ctx < 1 || d->n_experts != 0 || !d->layers) return MK_E_INVALID;
     if (d->head_dim != 64 && d->head_dim != 128) return MK_E_INVALID;
     if (d->n_kv_heads < 1 || d->n_q_heads % d->n_kv_heads || d->n_q_heads / d->n_kv_heads > 8) return MK_E_UNSUPPORTED;
     const int h = d->hidden, qd = d->n_q_heads * d->head_dim, kvd = d->n_kv_heads * d->head_dim, f = d->ffn_dim;

@@ -63,7 +63,7 @@ int plan_tiling(const Dims& dm, int B, int C, int W, const PlanOptions& o, Tilin
     if (dm.d != 64 && dm.d != 128) return fail("head_dim must be 64 or 128");
     if (dm.nq % dm.nkv) return fail("n_q_heads must be a multiple of n_kv_heads");
     const bool moe = dm.n_experts != 0;
-    if (B > MAX_BATCH) return fail("batch is limited to 32 sequences per step");
+    if (B > MAX_BATCH) return fail("batch is limited to 64 sequences per step");
     const bool batched = batched_path(B, dm.n_experts);
     if (batched && dm.h > 2048) return fail("batch > 1 and experts need hidden <= 2048");
     if (moe) {

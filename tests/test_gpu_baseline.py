@@ -73,10 +73,10 @@ def test_baseline_one_step(cfg, C, P):
     assert r["launches"] == 11 * cfg.n_layers + 5
 
 
-@pytest.mark.parametrize("B", [3, 20])
+@pytest.mark.parametrize("B", [3, 20, 50])
 def test_baseline_batch_small(B):
-    # ragged batches: one column group with padding, two groups with the second ragged;
-    # contexts from 1 to the last slot
+    # ragged batches: one column group with padding, two groups with the second ragged, four
+    # groups (50 sequences: the fourth holds 2); contexts from 1 to the last slot
     pos = synth.make_positions(B, 0, 511)
     pos[0], pos[-1] = 0, 511
     _check_one_step(SMALL, 512, pos)

@@ -80,7 +80,7 @@ def _one_step(cfg, B, C, positions, check_kv=True, **opt):
         _check_kv((kc, vc), (k2, v2), (kg, vg), pos)
 
 
-@pytest.mark.parametrize("B", [2, 3, 16, 20, 32])
+@pytest.mark.parametrize("B", [2, 3, 16, 20, 32, 50, 64])
 def test_tiny_batch_one_step(B):
     # mixed context lengths, including position 0 and the last slot
     pos = synth.make_positions(B, 0, 511)

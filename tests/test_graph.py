@@ -250,7 +250,7 @@ def test_batched_checker_catches_an_oproj_that_skips_attention():
 def test_planner_rejects_what_it_does_not_implement():
     cfg = synth.configs.TINY
     with pytest.raises(mk.MkError):
-        plan(cfg, 4, B=33)
+        plan(cfg, 4, B=65)
     with pytest.raises(mk.MkError):
         plan(synth.configs.LLAMA_8B, 256, B=2)
     with pytest.raises(mk.MkError):
