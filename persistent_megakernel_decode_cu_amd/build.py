@@ -8,7 +8,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmk.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["graph.cpp", "runtime.cpp", "megakernel.hip", "baseline.hip", "micro.hip"]
+SOURCES = ["graph.cpp", "prefill_graph.cpp", "runtime.cpp", "megakernel.hip", "baseline.hip", "micro.hip"]
 
 # Packed-FP32 instructions are kept out of every kernel of this library.
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

@@ -33,7 +33,10 @@ struct Graph {
 int plan_tiling(const Dims& dm, int B, int C, int W, const PlanOptions& o, Tiling* t, std::string* err);
 void plan_layout(const Tiling& T, bool tied, Layout* out);
 int build_graph(const Tiling& T, const Layout& Ly, int sched, int policy, Graph* g);
-// the prompt graph: T tokens of one sequence per launch (dense models, head_dim 64, hidden <= 2048);
+// sub-counters, each event's dependents and the queues of a graph whose tasks and targets are built
+void finish_graph(Graph& g, int sched, int policy);
+// the prompt graph (prefill_graph.cpp): T tokens of one sequence per launch (dense models, head_dim 64,
+// hidden <= 2048);
 // *unsupported tells a valid shape this graph does not implement from a bad argument
 int plan_prefill_tiling(const Dims& dm, int T, int C, int W, Tiling* t, std::string* err, bool* unsupported);
 int build_prefill_graph(const Tiling& T, const Layout& Ly, int sched, int policy, Graph* g);
