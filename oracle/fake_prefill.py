@@ -16,7 +16,7 @@ needs a value its event does not guarantee: every buffer a task writes starts as
 
 Tile semantics, as the prompt graph defines them (the knowledge-base digest "megakernel
 boundary selection" defines prefill as the pass over the whole prompt, once per request):
-  RMSNorm (part = kind, seq = q): tokens 4q .. 4q+3; kind 0 of layer l: x = R_a + the down
+  RMSNorm (part = kind, seq = q, nrows = n tokens, 1 or 4): tokens nq .. nq+n-1; kind 0 of layer l: x = R_a + the down
     partials (layer 0: the embedding row) -> R_b, normalised -> X; kind 1: x = R_b + the
     O-projection partials -> R_a, normalised -> X; kind 2: x = R_a + the down partials -> R_b
     (the hidden output), the last token normalised with the final gains -> LM.
@@ -71,8 +71,9 @@ class PromptDevice:
         return range(n * k["seq"], min(n * k["seq"] + n, self.T))
 
     def _pnorm(self, k):
-        cfg, l, kind = self.cfg, k["layer"], k["part"]
-        for t in range(4 * k["seq"], min(4 * k["seq"] + 4, self.T)):
+        cfg, l, kind, n = self.cfg, k["layer"], k["part"], k["nrows"]
+        assert n in (1, 4), "an RMSNorm task covers one or four tokens"
+        for t in range(n * k["seq"], min(n * k["seq"] + n, self.T)):
             if kind == 0:
                 x = self.W["tok_embed"][self.tok[t]] if l == 0 else self.Ra[t] + self.Pd[:, t].sum(axis=0)
                 self.Rb[t] = x

@@ -109,12 +109,15 @@ int build_prefill_graph(const Tiling& T, const Layout& Ly, int sched, int policy
     };
     // RMSNorm tasks of 4 tokens each (kind 0: attention input, 1: FFN input, 2: the final residual),
     // which also add the previous projection's K-slice partials to the residual
-    const int nquads = (T.pf_T + 3) / 4;
+    // RMSNorm tasks: of one token while the prompt has no more tokens than there are workgroups
+    // (a phase of one round, each task's loads a quarter of a four-token task's), else of four
+    const int tpn = T.pf_T <= T.W ? 1 : 4, nnorm = (T.pf_T + tpn - 1) / tpn;
     auto norms = [&](int l, int kind, uint32_t wait, uint32_t sig) {
-        for (int q = 0; q < nquads; ++q) {
+        for (int q = 0; q < nnorm; ++q) {
             Task k = blank(OP_PNORM, l, wait, sig);
             k.part = (uint16_t)kind;
             k.seq = (uint32_t)q;
+            k.nrows = (uint32_t)tpn;  // tokens tpn q .. tpn q + tpn - 1
             add(k);
         }
     };

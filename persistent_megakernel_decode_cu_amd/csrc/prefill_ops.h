@@ -55,8 +55,100 @@ __device__ __forceinline__ void st8_dev(__amdgpu_buffer_rsrc_t r, uint32_t off, 
     __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 16);
 }
 
+// RMSNorm task of one token (short prompts: one task per token spreads the phase over as many
+// workgroups as there are tokens): compute wave w takes columns w h/4 .. (w + 1) h/4 - 1, eight
+// per lane; the four waves' sums of squares meet in LDS.  Same arithmetic and summation order as
+// the four-token task.
+__device__ __forceinline__ bool pnorm_token(const Params* pp, const Task& k, Ctx& c, const uint16_t* gp) {
+    CParams& p = P(pp);
+    const int lane = c.lane, wave = c.wave;
+    const int h = p.T.h, Tn = p.T.pf_T, l = k.layer, kind = k.part, nkb = h / 32;
+    const int tok = (int)k.seq, cw = h / NCW, c0 = wave * cw + lane * 8;
+    const bool act = lane * 8 < cw && tok < Tn;
+    const uint4 gw = act ? gld_u4(gp + c0) : make_uint4(0, 0, 0, 0);
+    if (!await_inputs(pp, k, c)) return false;
+    tmark(c, 0);
+    const uint32_t rbytes = (uint32_t)(pf_rows(p) * 4);
+    const float* base = kind == 1 ? pf_rb(p) : pf_ra(p);
+    const int nsl = kind == 1 ? p.T.pf_slices[1] : p.T.pf_slices[3];
+    const float* part0 = kind == 1 ? pf_po(p, 0) : pf_pd(p, 0);
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = 0.f;
+    if (act) {
+        if (kind == 0 && l == 0) {
+            const int id = gld(S.args.tokens + tok);
+            const uint4 v = gld_u4((const uint16_t*)(p.w + p.lay.embed) + (size_t)id * h + c0);
+            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                x[2 * e] = bf16lo(w4[e]);
+                x[2 * e + 1] = bf16hi(w4[e]);
+            }
+        } else {
+            // the residual and the partials, all loads in flight at once, added in slice order
+            u32x4 a[PF_MAX_SLICES + 1], b[PF_MAX_SLICES + 1];
+            const uint32_t off = (uint32_t)(tok * h + c0) * 4u;
+#pragma unroll
+            for (int q = 0; q <= PF_MAX_SLICES; ++q) {
+                if (q > nsl) break;
+                const __amdgpu_buffer_rsrc_t r = dev_rsrc(q == 0 ? base : part0 + (size_t)(q - 1) * pf_rows(p), rbytes);
+                a[q] = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 16);
+                b[q] = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 16);
+            }
+#pragma unroll
+            for (int q = 0; q <= PF_MAX_SLICES; ++q) {
+                if (q > nsl) break;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    x[e] += __uint_as_float(a[q][e]);
+                    x[4 + e] += __uint_as_float(b[q][e]);
+                }
+            }
+        }
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
+    ss = wave_sum(ss);
+    // the four waves' sums (a slot per task parity: a wave a task ahead cannot overwrite them)
+    if (lane == 0) S.ssqb[wave][c.t & 1u] = ss;
+    if (!cbarrier(pp, c, k.id)) return false;
+    ss = (S.ssqb[0][c.t & 1u] + S.ssqb[1][c.t & 1u]) + (S.ssqb[2][c.t & 1u] + S.ssqb[3][c.t & 1u]);
+    tmark(c, 1);
+    if (!act) return true;
+    const float rs = 1.0f / sqrtf(ss / (float)h + p.eps);
+    const __amdgpu_buffer_rsrc_t dst = dev_rsrc(kind == 1 ? pf_ra(p) : pf_rb(p), rbytes);
+    const uint32_t off = (uint32_t)(tok * h + c0) * 4u;
+    __builtin_amdgcn_raw_buffer_store_b128(
+        u32x4{__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3])}, dst, off, 0,
+        16);
+    __builtin_amdgcn_raw_buffer_store_b128(
+        u32x4{__float_as_uint(x[4]), __float_as_uint(x[5]), __float_as_uint(x[6]), __float_as_uint(x[7])}, dst,
+        off + 16, 0, 16);
+    if (kind == 2 && tok != Tn - 1) return true;
+    const int tg = kind == 2 ? 0 : tok / 16, n = kind == 2 ? 0 : tok % 16;
+    const __amdgpu_buffer_rsrc_t reg =
+        dev_rsrc(kind == 2 ? pf_lm(p) : pf_x(p), (uint32_t)(kind == 2 ? 1 : pf_ntg(p)) * nkb * 2048u);
+    const uint32_t g4[4] = {gw.x, gw.y, gw.z, gw.w};
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        y[2 * e] = x[2 * e] * rs * bf16lo(g4[e]);
+        y[2 * e + 1] = x[2 * e + 1] * rs * bf16hi(g4[e]);
+    }
+    u32x4v hi, lo;
+    split8(y, hi, lo);
+    const uint32_t ln = (uint32_t)(n + 16 * ((c0 % 32) / 8));
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, hi), reg,
+                                           pf_unit((uint32_t)tg, (uint32_t)nkb, (uint32_t)(c0 / 32), 0, ln), 0, 16);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, lo), reg,
+                                           pf_unit((uint32_t)tg, (uint32_t)nkb, (uint32_t)(c0 / 32), 1, ln), 0, 16);
+    return true;
+}
+
 // RMSNorm tasks of 4 tokens (compute wave w: token 4 q + w; a lane holds columns 512 j + 8 lane
-// .. + 7).  Each first completes the residual: kind 0 (the attention input of layer l) x = R_a +
+// .. + 7), or of one (nrows = 1: pnorm_token).  Each first completes the residual: kind 0 (the attention input of layer l) x = R_a +
 // the previous layer's down partials (layer 0: the embedding row) -> R_b; kind 1 (the FFN input)
 // x = R_b + this layer's O-projection partials -> R_a; kind 2 (after the last layer) x = R_a + the
 // down partials -> R_b, the hidden output.  Then x is normalised into the X operands (kind 2: of
@@ -69,9 +161,10 @@ __device__ __noinline__ bool op_pnorm(const Params* pp, uint32_t slot_, uint32_t
     const int lane = c.lane, wave = c.wave;
     const int h = p.T.h, L = p.T.L, Tn = p.T.pf_T, l = k.layer, kind = k.part;
     const int nkb = h / 32, NJ = h / 512;
+    const uint16_t* gp = gains(p, kind == 0 ? 2 * l : kind == 1 ? 2 * l + 1 : 2 * L);
+    if (k.nrows == 1) return pnorm_token(pp, k, c, gp);
     const int tok = (int)k.seq * 4 + wave;
     const bool valid = tok < Tn;
-    const uint16_t* gp = gains(p, kind == 0 ? 2 * l : kind == 1 ? 2 * l + 1 : 2 * L);
     uint4 gw[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j)

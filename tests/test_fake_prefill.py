@@ -51,8 +51,9 @@ def _agrees(out, kk, vv, want):
             np.array_equal(kk, wk) and np.array_equal(vv, wv))
 
 
-# (prompt tokens, pos0, max ctx, workgroups): ragged prompts, earlier context, the three tile shapes
-CASES = [(40, 0, 64, 16), (77, 13, 128, 16), (150, 0, 256, 4), (1, 5, 32, 7)]
+# (prompt tokens, pos0, max ctx, workgroups): ragged prompts, earlier context, the three tile shapes,
+# RMSNorm tasks of four tokens and of one (prompts no longer than the workgroup count)
+CASES = [(40, 0, 64, 16), (77, 13, 128, 16), (150, 0, 256, 4), (1, 5, 32, 7), (20, 3, 64, 32)]
 
 
 @pytest.mark.parametrize("T,pos0,C,W", CASES)
