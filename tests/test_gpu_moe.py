@@ -74,7 +74,7 @@ def _one_step(cfg, B, C, pos, exact_experts=True, **opt):
     assert res["argmax_equal"]
 
 
-@pytest.mark.parametrize("B", [1, 2, 5, 20])
+@pytest.mark.parametrize("B", [1, 2, 5, 20, 37, 64])
 def test_tiny_moe_one_step(B):
     pos = synth.make_positions(B, 0, 511)
     pos[0] = 0

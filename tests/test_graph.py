@@ -218,6 +218,10 @@ BATCH_CASES = [
     (synth.configs.MOE_1B, 1, 256, 2048, 0),
     (synth.configs.TINY_MOE, 20, 64, 512, 1),
     (synth.configs.MOE_1B, 16, 256, 2048, 0),
+    # three and four column groups of 16 sequences (the largest batch), with and without experts
+    (synth.configs.TINY, 64, 64, 512, 0),
+    (synth.configs.TINY_MOE, 37, 64, 512, 0),
+    (synth.configs.TINY_MOE, 64, 128, 512, 1),
 ]
 
 
