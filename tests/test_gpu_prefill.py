@@ -127,6 +127,9 @@ CASES = [
     (40, 7, 128, 0, 1),
     (40, 7, 128, 0, 2),
     (40, 7, 128, 0, 3),
+    (64, 64, 128, 0, 0),    # the prompt ends at the cache's last slot
+    (96, 0, 96, 0, 0),      # the prompt is the whole cache
+    (300, 0, 512, 0, 0),    # more tokens than workgroups: RMSNorm tasks of four tokens
 ]
 
 
