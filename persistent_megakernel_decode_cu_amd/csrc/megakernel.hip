@@ -2165,7 +2165,8 @@ __device__ __noinline__ bool op_lmhead(const Params* pp, uint32_t slot_, uint32_
         key = other > key ? other : key;
     }
     if (lane == 0 && key)
-        __hip_atomic_fetch_max((g_u64*)&p.key[c.parity * p.T.B + 0], key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_max((g_u64*)&p.key[(c.parity * KEY_SLOTS + k.row0 / (uint32_t)p.T.lm_rows % KEY_SLOTS) * p.T.B],
+                               key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     copy_hidden_share(p, k, c.parity, tid);
     return true;
 }
@@ -2586,8 +2587,9 @@ __device__ __noinline__ bool op_gemv_b(const Params* pp, uint32_t slot_, uint32_
                 key = other > key ? other : key;
             }
             if (lane == 0 && key)
-                __hip_atomic_fetch_max((g_u64*)&p.key[c.parity * Btot + gb0 + b], key, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_fetch_max(
+                    (g_u64*)&p.key[(c.parity * KEY_SLOTS + k.row0 / (uint32_t)p.T.lm_rows % KEY_SLOTS) * Btot + gb0 + b],
+                    key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         if (k.seq == 0) copy_hidden_share(p, k, c.parity, tid);  // once, by the first column group's tiles
     } else if (k.op == OP_OPROJ || k.op == OP_DOWN) {  // residual accumulation (expert tiles did theirs per chunk)
@@ -2630,8 +2632,13 @@ __device__ __noinline__ void finish_step(const Params* pp, uint32_t epoch, uint3
     acquire_fence();
     const int B = p.T.B;
     for (int b = lane; b < B; b += 64) {
-        const unsigned long long key =
-            __hip_atomic_load((g_u64*)&p.key[parity * B + b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        unsigned long long key = 0ull;
+#pragma unroll
+        for (int s = 0; s < KEY_SLOTS; ++s) {
+            const unsigned long long ks = __hip_atomic_load((g_u64*)&p.key[(parity * KEY_SLOTS + s) * B + b],
+                                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            key = ks > key ? ks : key;
+        }
         gst(p.next + b, (int32_t)(0xffffffffu - (uint32_t)(key & 0xffffffffu)));
     }
 }
@@ -2853,7 +2860,8 @@ __global__ void __launch_bounds__(NTHREADS, 1) mk_step_kernel(const Params* pp, 
         float* other = p.acc + (size_t)(parity ^ 1u) * nacc;
         for (size_t i = (size_t)blockIdx.x * NTHREADS + threadIdx.x; i < nacc; i += (size_t)gridDim.x * NTHREADS)
             other[i] = 0.f;
-        if (blockIdx.x == 0 && (int)threadIdx.x < B) p.key[(parity ^ 1u) * B + threadIdx.x] = 0ull;
+        if (blockIdx.x == 0)
+            for (int i = threadIdx.x; i < KEY_SLOTS * B; i += NTHREADS) p.key[(parity ^ 1u) * KEY_SLOTS * B + i] = 0ull;
         if (p.aticket) {
             const size_t nt = (size_t)p.T.L * B * p.T.nkv;
             for (size_t i = (size_t)blockIdx.x * NTHREADS + threadIdx.x; i < nt; i += (size_t)gridDim.x * NTHREADS)
@@ -2919,7 +2927,8 @@ __global__ void __launch_bounds__(NTHREADS, 1) mk_prefill_kernel(const Params* p
         if (blockIdx.x == 0 && threadIdx.x == 0) raise_error(pp, ERR_INPUT, 0, 0, 0, 0);
     } else {
         // the other parity's argmax key, for the next launch (read only after this one)
-        if (blockIdx.x == 0 && threadIdx.x == 0) p.key[parity ^ 1u] = 0ull;
+        if (blockIdx.x == 0)
+            for (int i = threadIdx.x; i < KEY_SLOTS * p.T.B; i += NTHREADS) p.key[(parity ^ 1u) * KEY_SLOTS * p.T.B + i] = 0ull;
         if (wave >= NCW) loader<PF_INFLIGHT>(pp, epoch, wave - NCW);
         else compute<true>(pp, epoch, wave);
     }

@@ -34,7 +34,11 @@ constexpr uint32_t NONE = 0xFFFFFFFFu;
 // Device-side capacities the tiling must respect.
 constexpr int MAX_TILE_ROWS = 1024;  // rows x sequences of one GEMV tile (LDS row-result buffer)
 constexpr int GROUP_SEQS = 16;       // sequences per column group (columns of one matrix-core operand)
-constexpr int MAX_BATCH = 64;        // sequences per step: GEMV tiles run once per column group
+constexpr int MAX_BATCH = 64;
+// Argmax keys per sequence and step parity: LM-head tile i folds its maximum into slot i % KEY_SLOTS
+// (one 64-bit atomic max per tile and sequence; spreading them keeps the tiles that finish together
+// from queueing on one word), and the step's last tile reduces the slots.
+constexpr int KEY_SLOTS = 16;        // sequences per step: GEMV tiles run once per column group
 constexpr int MAX_ACT = 4096;        // floats of one staged activation vector (LDS)
 
 // Several-sequence QKV and gate/up tiles with K = 2048 are packed in two halves of K

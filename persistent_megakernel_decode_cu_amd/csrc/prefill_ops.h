@@ -635,6 +635,6 @@ __device__ __noinline__ bool op_plm(const Params* pp, uint32_t slot_, uint32_t p
         key = other > key ? other : key;
     }
     if (lane == 0 && key)
-        __hip_atomic_fetch_max((g_u64*)&p.key[c.parity], key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_max((g_u64*)&p.key[c.parity * KEY_SLOTS * p.T.B], key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return true;
 }

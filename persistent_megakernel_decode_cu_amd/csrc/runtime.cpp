@@ -271,7 +271,7 @@ mk_status rearm(mk_handle* h) {
     if (p.aticket) HIPCHK(hipMemset(p.aticket, 0, (size_t)2 * T.L * T.B * T.nkv * 4));
     if (p.rq_stamp) HIPCHK(hipMemset(p.rq_stamp, 0, h->g.tasks.size() * 4));
     if (p.aeq_stamp) HIPCHK(hipMemset(p.aeq_stamp, 0, h->n_events * 4));
-    HIPCHK(hipMemset(p.key, 0, sizeof(unsigned long long) * 2 * T.B));
+    HIPCHK(hipMemset(p.key, 0, sizeof(unsigned long long) * 2 * KEY_SLOTS * T.B));
     HIPCHK(hipMemset(p.ticket, 0, 4 * T.B));
     HIPCHK(hipDeviceSynchronize());
     return MK_OK;
@@ -464,7 +464,7 @@ mk_status build_handle(const mk_model_desc* desc, int32_t batch, int32_t max_ctx
     }
     if (prompt) p.hidden = p.acc + (size_t)(T.pf_T + 15) / 16 * 16 * T.h;  // the residual after the last layer
     else ALLOC(p.hidden, (size_t)T.B * T.h * 4, true);
-    ALLOC(p.key, sizeof(unsigned long long) * 2 * T.B, true);
+    ALLOC(p.key, sizeof(unsigned long long) * 2 * KEY_SLOTS * T.B, true);
     ALLOC(p.ticket, 4 * T.B, true);
     ALLOC(p.next, 4 * T.B, true);
     if (o.trace) {
@@ -505,7 +505,7 @@ mk_status build_handle(const mk_model_desc* desc, int32_t batch, int32_t max_ctx
         const size_t o_xop = batched_path(T.B, T.E) ? take(h->xop_bytes) : 0;
         const size_t o_at = batched_path(T.B, T.E) ? take((size_t)2 * T.L * T.B * T.nkv * 4) : 0;
         const size_t o_rl = T.E ? take((size_t)T.L * T.B * T.E * 4) : 0;
-        const size_t o_key = take(sizeof(unsigned long long) * 2 * T.B), o_ticket = take(4 * (size_t)T.B);
+        const size_t o_key = take(sizeof(unsigned long long) * 2 * KEY_SLOTS * T.B), o_ticket = take(4 * (size_t)T.B);
         const size_t o_rqs = o.sched >= 2 ? take(h->g.tasks.size() * 4) : 0;
         const size_t o_aeq = o.sched == 3 ? take(h->n_events * 4) : 0;
         h->na_bytes = at;
@@ -663,7 +663,7 @@ mk_status mk_decode_step_noalloc(mk_handle* h, const int32_t* tokens, const int3
     span(p.state + 1, (ST_WORDS - 1) * 4, 0u);
     span(p.state + ST_EPOCH, 4, 1u);  // ST_EPOCH is word 0
     span(p.acc + nacc, nacc * 4, 0u);  // parity 1
-    span(p.key + T.B, (size_t)T.B * 8, 0u);
+    span(p.key + (size_t)KEY_SLOTS * T.B, (size_t)KEY_SLOTS * T.B * 8, 0u);
     span(p.ticket, (size_t)T.B * 4, 0u);
     span(p.aticket ? p.aticket + nat : nullptr, nat * 4, 0u);
     span(p.rq_stamp, h->g.tasks.size() * 4, 0u);

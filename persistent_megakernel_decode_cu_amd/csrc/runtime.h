@@ -71,7 +71,7 @@ struct Params {
     float* rlogit;            // MoE: [L][B][E] router logits
     int32_t* eids;            // MoE: [L][B][top_k] selected experts, in selection order
     float* hidden;            // [B][h]
-    unsigned long long* key;  // [2][B] packed argmax keys
+    unsigned long long* key;  // [2][KEY_SLOTS][B] packed argmax keys
     uint32_t* ticket;         // [B]
     int32_t* next;            // [B]
     uint32_t* task_count;     // [n_tasks] or null
