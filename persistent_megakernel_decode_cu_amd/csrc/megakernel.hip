@@ -290,7 +290,16 @@ __device__ __forceinline__ float seg_sum(float v) {
     return v;
 }
 
-__device__ __forceinline__ uint32_t ctr_index(uint32_t ev, uint32_t sub) { return (ev * 8u + sub) * 32u; }
+__device__ __forceinline__ uint32_t ctr_index(uint32_t ev, uint32_t sub) { return (ev * CTR_SUBS + sub) * CTR_LINE; }
+// The counter words a consumer sums (a task record's nsub is 1 or 8)
+__device__ __forceinline__ uint32_t ctr_words(uint32_t nsub) { return nsub == 8u ? (uint32_t)CTR_SUBS : 1u; }
+// One poll: lane i < ctr_words(nsub) reads word i, the wave sums them
+__device__ __forceinline__ uint32_t ctr_sum(const uint32_t* ctr, uint32_t ev, uint32_t nsub, int lane) {
+    uint32_t v = (uint32_t)lane < ctr_words(nsub) ? ld_dev(&ctr[ctr_index(ev, lane)]) : 0u;
+#pragma unroll
+    for (int o = 1; o < CTR_SUBS; o <<= 1) v += __shfl_xor(v, o, 64);
+    return __builtin_amdgcn_readfirstlane(v);
+}
 
 // ---- error path -------------------------------------------------------------------
 
@@ -349,11 +358,7 @@ __device__ __noinline__ bool wait_event(const Params* pp, uint32_t ev, uint32_t 
     uint32_t it = 0;
     const uint32_t* ctr = p.ctr;
     for (;;) {
-        uint32_t v = (uint32_t)lane < nsub ? ld_dev(&ctr[ctr_index(ev, lane)]) : 0u;
-        v += __shfl_xor(v, 1, 64);
-        v += __shfl_xor(v, 2, 64);
-        v += __shfl_xor(v, 4, 64);
-        const uint32_t sum = uni(v);
+        const uint32_t sum = ctr_sum(ctr, ev, nsub, lane);
         if (sum >= want) return true;
         if (lds_ld(S.abort)) return false;
         if ((++it & 63u) == 0u) {
@@ -899,11 +904,7 @@ __device__ __forceinline__ void tmark(const Ctx& c, int i) {
 
 // One poll of an event: do its sub-counters sum to `want`?
 __device__ __forceinline__ bool event_ready(CParams& p, uint32_t ev, uint32_t nsub, uint32_t want, int lane) {
-    uint32_t v = (uint32_t)lane < nsub ? ld_dev(&p.ctr[ctr_index(ev, lane)]) : 0u;
-    v += __shfl_xor(v, 1, 64);
-    v += __shfl_xor(v, 2, 64);
-    v += __shfl_xor(v, 4, 64);
-    return uni(v) >= want;
+    return ctr_sum(p.ctr, ev, nsub, lane) >= want;
 }
 
 // Compute wave 0 waits for the task's event and releases the other compute waves.
@@ -2755,7 +2756,7 @@ __device__ __noinline__ void compute(const Params* pp, uint32_t epoch, int wave)
             bool activated = false;
             if (k.sig_ev != NONE && k.id != drop_task && (uint32_t)c.lane < n_sig) {
                 const uint32_t ev = k.sig_ev + (uint32_t)c.lane;
-                const uint32_t sub = k.sig_nsub == 8 ? xcc_id() : 0u;
+                const uint32_t sub = k.sig_nsub == 8 ? xcc_id() + 8u * ((blockIdx.x >> 3) % (uint32_t)(CTR_SUBS / 8)) : 0u;
                 const uint32_t old = addu_dev(&ctr[ctr_index(ev, sub)], 1u);
                 // event-driven dispatch: the count that reaches the event's threshold activates it
                 activated = sched >= 2 && old + 1u == epoch * p.ev_target[ev];

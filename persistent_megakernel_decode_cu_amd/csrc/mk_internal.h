@@ -38,7 +38,18 @@ constexpr int MAX_BATCH = 64;
 // Argmax keys per sequence and step parity: LM-head tile i folds its maximum into slot i % KEY_SLOTS
 // (one 64-bit atomic max per tile and sequence; spreading them keeps the tiles that finish together
 // from queueing on one word), and the step's last tile reduces the slots.
-constexpr int KEY_SLOTS = 16;        // sequences per step: GEMV tiles run once per column group
+constexpr int KEY_SLOTS = 16;
+// Counter words per event with many producers (a task record's nsub of 8): producers add to one of
+// CTR_SUBS words (by their XCD, then by workgroup), each on its own 128-byte line, and consumers sum
+// them; events with few producers use word 0 alone.  (Measured on the 1B shape: 16 words against 8,
+// 807.0 -> 800.3 us per step at batch 1 and 1530.3 -> 1518.3 us at batch 16; 32 words no better:
+// the increments that end a phase arrive together and queue on their word.)
+#ifndef MK_CTR_SUBS
+#define MK_CTR_SUBS 16
+#endif
+constexpr int CTR_SUBS = MK_CTR_SUBS;
+constexpr int CTR_LINE = 32;  // 32-bit words per counter line
+static_assert(CTR_SUBS == 8 || CTR_SUBS == 16 || CTR_SUBS == 32 || CTR_SUBS == 64, "8..64 counter words per event");        // sequences per step: GEMV tiles run once per column group
 constexpr int MAX_ACT = 4096;        // floats of one staged activation vector (LDS)
 
 // Several-sequence QKV and gate/up tiles with K = 2048 are packed in two halves of K
@@ -62,8 +73,8 @@ constexpr int part_chunks(bool batched, int splits) { return batched ? ATTN_MAX_
 // One instruction of the interpreter: 48 bytes, read by the loader wave into LDS.
 struct Task {
     uint8_t op;
-    uint8_t wait_nsub;     // sub-counters of the awaited event (1 or 8)
-    uint8_t sig_nsub;      // sub-counters of the signalled event (1 or 8)
+    uint8_t wait_nsub;     // counter words of the awaited event: 1, or 8 for CTR_SUBS words
+    uint8_t sig_nsub;      // counter words of the signalled event: 1, or 8 for CTR_SUBS words
     uint8_t flags;         // TaskFlags
     uint16_t layer;
     uint16_t part;         // QKV: head slot; ATTN/OPROJ: KV group; DOWN: K block; EGU/EDOWN: expert

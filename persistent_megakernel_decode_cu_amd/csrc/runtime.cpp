@@ -263,7 +263,7 @@ mk_status repack(mk_handle* h, const mk_model_desc* d, uint8_t* wd) {
 mk_status rearm(mk_handle* h) {
     const Tiling& T = h->g.T;
     Params& p = h->p;
-    HIPCHK(hipMemset(p.ctr, 0, h->n_events * 8 * 32 * 4));
+    HIPCHK(hipMemset(p.ctr, 0, h->n_events * CTR_SUBS * CTR_LINE * 4));
     std::vector<uint32_t> st(ST_WORDS, 0);
     st[ST_EPOCH] = 1;
     HIPCHK(hipMemcpy(p.state, st.data(), ST_WORDS * 4, hipMemcpyHostToDevice));
@@ -398,7 +398,7 @@ mk_status build_handle(const mk_model_desc* desc, int32_t batch, int32_t max_ctx
     ALLOC(qq, h->g.queue.size() * 4, false);
     p.queue_off = qo;
     p.queue = qq;
-    ALLOC(p.ctr, h->n_events * 8 * 32 * 4, true);
+    ALLOC(p.ctr, h->n_events * CTR_SUBS * CTR_LINE * 4, true);
     if (o.sched >= 2) {
         uint32_t *evt, *co, *cs, *rq;
         ALLOC(evt, h->n_events * 4, false);
@@ -498,7 +498,7 @@ mk_status build_handle(const mk_model_desc* desc, int32_t batch, int32_t max_ctx
             at += std::max<size_t>(256, (bytes + 255) / 256 * 256);
             return o;
         };
-        const size_t o_ctr = take(h->n_events * 8 * 32 * 4), o_state = take(ST_WORDS * 4);
+        const size_t o_ctr = take(h->n_events * CTR_SUBS * CTR_LINE * 4), o_state = take(ST_WORDS * 4);
         const size_t o_q = take((size_t)T.B * T.nq * T.d * 4);
         const size_t o_part = take((size_t)T.B * T.nkv * part_chunks(batched_path(T.B, T.E), T.attn_splits) * T.grp * (T.d + 2) * 4);
         const size_t o_m = take((size_t)T.B * T.f * 4), o_acc = take(h->acc_bytes);
@@ -659,7 +659,7 @@ mk_status mk_decode_step_noalloc(mk_handle* h, const int32_t* tokens, const int3
         ++cs.n;
     };
     const size_t nacc = (size_t)(2 * T.L + 1) * T.B * T.h, nat = (size_t)T.L * T.B * T.nkv;
-    span(p.ctr, h->n_events * 8 * 32 * 4, 0u);
+    span(p.ctr, h->n_events * CTR_SUBS * CTR_LINE * 4, 0u);
     span(p.state + 1, (ST_WORDS - 1) * 4, 0u);
     span(p.state + ST_EPOCH, 4, 1u);  // ST_EPOCH is word 0
     span(p.acc + nacc, nacc * 4, 0u);  // parity 1
@@ -773,11 +773,11 @@ mk_status mk_export_graph(const mk_handle* h, void* buf, size_t cap, size_t* nee
 mk_status mk_read_counters(mk_handle* h, uint32_t* host, size_t n, uint32_t* epoch) {
     if (!h || (!host && n)) return MK_E_INVALID;
     HIPCHK(hipDeviceSynchronize());
-    std::vector<uint32_t> raw(h->n_events * 8 * 32);
+    std::vector<uint32_t> raw(h->n_events * CTR_SUBS * CTR_LINE);
     HIPCHK(hipMemcpy(raw.data(), h->p.ctr, raw.size() * 4, hipMemcpyDeviceToHost));
     for (size_t e = 0; e < n && e < h->n_events; ++e) {
         uint32_t s = 0;
-        for (int k = 0; k < 8; ++k) s += raw[(e * 8 + k) * 32];
+        for (int k = 0; k < CTR_SUBS; ++k) s += raw[(e * CTR_SUBS + k) * CTR_LINE];
         host[e] = s;
     }
     if (epoch) {
