@@ -213,7 +213,8 @@ mk_status mk_decode_step(mk_handle *h, const int32_t *tokens, const int32_t *pos
  * by mk_build_graph) still owns the weights, task graph and outputs.  MK_E_UNSUPPORTED
  * when the handle's scratch exceeds the array (about 1.1 MiB at the 1B shape with one
  * sequence, 20 MiB with 16 sequences, 40 MiB with 32: refused).  mk_check_device_error
- * reports a device error of such a step until the next one on that GPU. */
+ * reports a device error of such a step while it is the handle's last step and no other
+ * allocation-free step has run on that GPU since. */
 mk_status mk_decode_step_noalloc(mk_handle *h, const int32_t *tokens, const int32_t *positions, void *kv_cache,
                                  float *logits, void *stream);
 

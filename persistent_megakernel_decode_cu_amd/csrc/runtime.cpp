@@ -27,6 +27,9 @@ struct mk_handle {
     Params p_na;
     Params* dparams_na = nullptr;
     size_t na_bytes = 0;  // scratch this handle's steps need
+    // the handle's last step was an allocation-free one: only then is the error record in the
+    // per-GPU array its own (the array holds another handle's scratch after that one's steps)
+    bool na_last = false;
     bool tied = true;
     Graph g;
     Params p;           // host copy
@@ -605,6 +608,7 @@ mk_status mk_prefill(mk_handle* h, const int32_t* tokens, int32_t pos0, void* kv
         const mk_status st = enqueue_poison(h, h->p, logits, (hipStream_t)stream);
         if (st != MK_OK) return st;
     }
+    h->na_last = false;
     hipError_t e = launch_prefill(h->dparams, a, (uint32_t)h->W, (hipStream_t)stream, h->cooperative);
     if (e == hipErrorCooperativeLaunchTooLarge) return MK_E_NOT_RESIDENT;
     return e == hipSuccess ? MK_OK : MK_E_HIP;
@@ -631,6 +635,7 @@ mk_status mk_decode_step(mk_handle* h, const int32_t* tokens, const int32_t* pos
         const mk_status st = enqueue_poison(h, h->p, logits, (hipStream_t)stream);
         if (st != MK_OK) return st;
     }
+    h->na_last = false;
     hipError_t e = launch_step(h->dparams, a, (uint32_t)h->W, (hipStream_t)stream, h->cooperative);
     if (e == hipErrorCooperativeLaunchTooLarge) return MK_E_NOT_RESIDENT;
     return e == hipSuccess ? MK_OK : MK_E_HIP;
@@ -682,6 +687,7 @@ mk_status mk_decode_step_noalloc(mk_handle* h, const int32_t* tokens, const int3
     a.vc = (uint16_t*)kv_cache + (size_t)T.L * T.B * T.nkv * (size_t)T.C * T.d;
     a.logits = logits;
     a.pos0 = 0;
+    h->na_last = true;
     e = launch_step(h->dparams_na, a, (uint32_t)h->W, (hipStream_t)stream, h->cooperative);
     if (e == hipErrorCooperativeLaunchTooLarge) return MK_E_NOT_RESIDENT;
     return e == hipSuccess ? MK_OK : MK_E_HIP;
@@ -740,8 +746,9 @@ mk_status mk_check_device_error(mk_handle* h, char* msg, size_t cap) {
     HIPCHK(hipDeviceSynchronize());
     uint32_t rec[8];
     HIPCHK(hipMemcpy(rec, h->p.state + ST_ERR, sizeof(rec), hipMemcpyDeviceToHost));
-    if (rec[0] == ERR_NONE && h->dparams_na) {
-        // the last allocation-free step's record (kept until the next such step on this GPU clears it)
+    if (rec[0] == ERR_NONE && h->dparams_na && h->na_last) {
+        // this handle's last step was allocation-free: its record is in the per-GPU array (kept
+        // until the next allocation-free step on this GPU clears it)
         HIPCHK(hipMemcpy(rec, h->p_na.state + ST_ERR, sizeof(rec), hipMemcpyDeviceToHost));
         if (rec[0] != ERR_NONE) {
             const uint32_t zero[8] = {0, 0, 0, 0, 0, 0, 0, 0};

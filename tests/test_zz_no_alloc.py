@@ -18,6 +18,7 @@ pytestmark = pytest.mark.gpu
 
 TINY = synth.configs.TINY
 LLAMA_1B = synth.configs.LLAMA_1B
+TINY_MOE = synth.configs.TINY_MOE
 
 
 class Case:
@@ -145,3 +146,21 @@ def test_noalloc_refuses_a_handle_whose_scratch_exceeds_the_array():
                                   torch.cuda.current_stream().cuda_stream)
     assert ei.value.status == mk.MK_E_UNSUPPORTED
     run.close()
+
+
+def test_error_check_after_another_handles_allocation_free_steps():
+    """A handle whose steps were all ordinary reports no device error after another handle's
+    allocation-free steps have left that handle's counters in the per-GPU array (the check
+    consults the array's error record only when the handle's own last step used it)."""
+    case = Case(LLAMA_1B, 1, 2048, [1024])
+    print("case 1B B=1: 3 allocation-free steps, then a tiny MoE handle's ordinary step", flush=True)
+    for _ in range(3):
+        case.step(True)
+    torch.cuda.synchronize()
+    assert mk.mk_check_device_error(case.run.h) is None
+    other = Case(TINY_MOE, 1, 512, [100])
+    other.step(False)
+    torch.cuda.synchronize()
+    assert mk.mk_check_device_error(other.run.h) is None
+    other.run.close()
+    case.run.close()
