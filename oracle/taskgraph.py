@@ -267,10 +267,10 @@ def build(cfg, B, C, W, policy=0, attn_splits=0, sched=0):
             rows = min(t["lm_rows"], cfg.vocab - i * t["lm_rows"])
             task(op=OP_LMHEAD, layer=L, row0=i * t["lm_rows"], nrows=rows, seq=sg, wait_ev=ev_x,
                  wbytes=_round16(rows) * h * 2, wofs=lay["lm"] + i * t["lm_rows"] * h * 2)
-    # events with more than 16 producers spread their counts over the device's counter words
+    # events with more than 4 producers spread their counts over the device's counter words
     # (recorded as nsub 8), except under event-driven dispatch, where one counter per event
     # tells its last producer
-    nsub = [8 if n > 16 and sched < 2 else 1 for n in target]
+    nsub = [8 if n > 4 and sched < 2 else 1 for n in target]
     for k in tasks:
         k["wait_target"] = target[k["wait_ev"]] if k["wait_ev"] != NONE else 0
         k["wait_nsub"] = nsub[k["wait_ev"]] if k["wait_ev"] != NONE else 1

@@ -183,10 +183,10 @@ static uint64_t task_cost(const Task& k) { return (uint64_t)k.wbytes + 8192; }
 
 // Sub-counters, event dependents and the queues of a graph whose tasks and targets are built.
 void finish_graph(Graph& g, int sched, int policy) {
-    // counter words: events with more than 16 producers spread their increments over the device's
-    // CTR_SUBS words (nsub 8); measured on the 1B shape at batch 1 against more than 32: 799 -> 785 us
-    // per step (event-driven dispatch: one counter per event, which tells its last producer)
-    for (size_t e = 0; e < g.target.size(); ++e) g.nsub[e] = sched < 2 && g.target[e] > 16 ? 8 : 1;
+    // counter words: events with more than 4 producers spread their increments over the device's
+    // CTR_SUBS words (nsub 8); measured on the 1B shape at batch 1 against more than 32 / 16: 799 / 786
+    // -> 780 us per step (event-driven dispatch: one counter per event, which tells its last producer)
+    for (size_t e = 0; e < g.target.size(); ++e) g.nsub[e] = sched < 2 && g.target[e] > 4 ? 8 : 1;
     // dependents of every event, and the tasks that wait on none
     g.cons_off.assign(g.target.size() + 1, 0);
     g.cons.clear();
