@@ -63,13 +63,14 @@ def measured_traffic(batch=1):
     return int(rec["traffic_bytes_per_launch"])
 
 
-# every source the kernel's memory traffic depends on: the kernel, the planner (tiles, queues) and the
-# runtime's weight packing (tile order in HBM)
+# every source the kernel's memory traffic depends on: the kernel, the planner (tiles, queues), the
+# runtime's weight packing (tile order in HBM) and the compiler flags the library is built with
 TRAFFIC_SOURCES = ["persistent_megakernel_decode_cu_amd/csrc/megakernel.hip",
                    "persistent_megakernel_decode_cu_amd/csrc/graph.cpp",
                    "persistent_megakernel_decode_cu_amd/csrc/runtime.cpp",
                    "persistent_megakernel_decode_cu_amd/csrc/runtime.h",
-                   "persistent_megakernel_decode_cu_amd/csrc/mk_internal.h"]
+                   "persistent_megakernel_decode_cu_amd/csrc/mk_internal.h",
+                   "persistent_megakernel_decode_cu_amd/build.py"]
 
 
 def traffic_from_counters(fetch_csv, write_csv, kernel="mk::mk_step_kernel", copy_bytes=256 << 20,
